@@ -1,0 +1,123 @@
+"""Oracle: dense per-token SwiGLU expert FFN and its gradients, fp64 --
+TEST INFRASTRUCTURE ONLY.
+
+MegaFlux summary (picx.dev/p/e4jAzZ), "Backward" section:
+* expert computation: Z_e = X_e W_1,e ; Z_e = [G_e, U_e] ;
+  A_e = SiLU(G_e) * U_e ; O_e = A_e W_2,e ; y_t = sum_{e in S_t} p_te O_e[t];
+* gradients: dA_e = D_e W_2,e^T ; dX_e = dZ_e W_1,e^T ; dW_2,e = A_e^T D_e ;
+  dW_1,e = X_e^T dZ_e.
+
+Storage convention (matches the library): w1 is [E, 2*d_ff, d] with rows
+0..d_ff-1 producing G and rows d_ff..2*d_ff-1 producing U, i.e. it holds
+W_1,e transposed; w2 is [E, d, d_ff], i.e. W_2,e transposed.  So for one row
+x (length d): z = w1[e] @ x, o = w2[e] @ a.
+
+Readings (the pages are silent): D_e = dL/dO_e, which through
+y_t = sum p O carries the gate, D[t] = p_te * dy_t; SiLU(g) = g * sigmoid(g);
+expert slots with id < 0 contribute nothing.  There are no blocks and no
+plan here: every routed (token, slot) pair is computed on its own and the k
+contributions of a token are added in slot order.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def sigmoid(g):
+    return 1.0 / (1.0 + np.exp(-g))
+
+
+def silu(g):
+    return g * sigmoid(g)
+
+
+def _pairs_by_expert(ids, tokens):
+    """{e: (positions into `tokens`, slot j)} for every routed pair."""
+    sub = ids[tokens]
+    out = {}
+    for e in np.unique(sub[sub >= 0]):
+        ti, j = np.nonzero(sub == e)
+        out[int(e)] = (ti, j)
+    return out
+
+
+def forward(x, w1, w2, topk_ids, gates, tokens=None, return_z=False):
+    """y [n, d] for the given token subset (default: all tokens), fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    ids = np.asarray(topk_ids)
+    p = np.asarray(gates, dtype=np.float64)
+    T, k = ids.shape
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    F = w1.shape[1] // 2
+    contrib = np.zeros((len(tokens), k, x.shape[1]))
+    zs = {}
+    for e, (ti, j) in _pairs_by_expert(ids, tokens).items():
+        xe = x[tokens[ti]]
+        w1e = np.asarray(w1[e], dtype=np.float64)
+        w2e = np.asarray(w2[e], dtype=np.float64)
+        z = xe @ w1e.T
+        a = silu(z[:, :F]) * z[:, F:]
+        o = a @ w2e.T
+        contrib[ti, j] = p[tokens[ti], j][:, None] * o
+        if return_z:
+            zs[e] = (tokens[ti], j, z)
+    y = np.zeros((len(tokens), x.shape[1]))
+    for j in range(k):
+        y += contrib[:, j]
+    return (y, zs) if return_z else y
+
+
+def backward(x, w1, w2, topk_ids, gates, dy, tokens=None, experts=None):
+    """Gradients of L = sum_t dy_t . y_t.
+
+    Returns dict with dx [n, d] for the token subset `tokens` (default all) and,
+    for each expert in `experts` (default all), dw1 [2*d_ff, d] and dw2 [d, d_ff]
+    in the library's storage layout (gradient of w1/w2 as stored).  dW of an
+    expert sums over *all* of its routed rows, whatever `tokens` is.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    ids = np.asarray(topk_ids)
+    p = np.asarray(gates, dtype=np.float64)
+    T, k = ids.shape
+    d = x.shape[1]
+    E = w1.shape[0]
+    F = w1.shape[1] // 2
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    experts = range(E) if experts is None else experts
+    tok_pos = {int(t): i for i, t in enumerate(tokens)}
+    all_pairs = _pairs_by_expert(ids, np.arange(T))
+
+    dx_contrib = np.zeros((len(tokens), k, d))
+    dw1, dw2 = {}, {}
+    want_w = set(int(e) for e in experts)
+    for e in range(E):
+        need_rows = e in want_w
+        ti, j = all_pairs.get(e, (np.zeros(0, int), np.zeros(0, int)))
+        if not need_rows:
+            keep = np.array([t in tok_pos for t in ti], dtype=bool)
+            ti, j = ti[keep], j[keep]
+        w1e = np.asarray(w1[e], dtype=np.float64)
+        w2e = np.asarray(w2[e], dtype=np.float64)
+        xe = x[ti]
+        D = p[ti, j][:, None] * dy[ti]                 # dL/dO_e
+        z = xe @ w1e.T
+        g, u = z[:, :F], z[:, F:]
+        sg = sigmoid(g)
+        a = g * sg * u
+        dA = D @ w2e                                  # D_e W_2,e^T in math layout
+        dG = dA * u * sg * (1.0 + g * (1.0 - sg))
+        dU = dA * g * sg
+        dZ = np.concatenate([dG, dU], axis=1)
+        dX = dZ @ w1e                                 # dZ_e W_1,e^T
+        for r in range(len(ti)):
+            pos = tok_pos.get(int(ti[r]))
+            if pos is not None:
+                dx_contrib[pos, j[r]] = dX[r]
+        if need_rows:
+            dw2[e] = D.T @ a                          # [d, d_ff] = (A^T D)^T
+            dw1[e] = dZ.T @ xe                        # [2 d_ff, d] = (X^T dZ)^T
+    dx = np.zeros((len(tokens), d))
+    for jj in range(k):
+        dx += dx_contrib[:, jj]
+    return {"dx": dx, "dw1": dw1, "dw2": dw2}
