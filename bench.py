@@ -1,0 +1,231 @@
+"""Benchmark of the skew-aware MoE expert layer on one MI355X.
+
+One step = the whole path over one batch of synthetic routed tokens:
+route statistics -> forward plan -> forward (FC1+SwiGLU, FC2, combine) ->
+backward plan (reduction-aware) -> backward (dA, dX, combine, weight
+gradients, replica reduction).  Inputs and weights are resident in HBM before
+timing starts.  The workload is the Qwen3-30B-A3B-shaped layer (T=8192,
+d=2048, d_ff=768, E=128, top-8, beta=128, P=8 CU partitions, s=4) at skew
+kappa=1 by default.
+
+Prints one JSON line.  `value` is useful TFLOP/s: (6 + 12) * d * d_ff * R per
+step (R = routed rows; padding rows, SwiGLU, combine not counted), divided by
+the measured step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer useful TFLOP/s (fwd,bwd) at κ=1/2/4/8; % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PEAK_FP8_TFLOPS = 5033.2
+PEAK_HBM_GBS = 8000.0
+
+FWD_STAGES = ["sched", "fc1", "fc2", "combine"]
+BWD_STAGES = ["sched", "dA", "dX", "combine", "dW", "reduce"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_bf16_fwdbwd")
+    ap.add_argument("--kappa", type=float, default=1)
+    ap.add_argument("--fixed", action="store_true", help="fixed placement (s = 0)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time every kappa of the workload, fixed and planned")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=512)
+    return ap.parse_args()
+
+
+def flops_per_row(w):
+    return 6 * w.d * w.d_ff, 12 * w.d * w.d_ff
+
+
+def build_case(w, kappa, fixed, dev):
+    import torch
+
+    from moe_expert_ffn_amd.inputs import contiguous_owners, make_dy, make_layer, make_routing, make_x
+    from moe_expert_ffn_amd.runner import LayerRunner
+    ids, gates = make_routing(w, kappa)
+    T = ids.shape[0]
+    lay = make_layer(w, dev)
+    x = lay["x"] if "x" in lay and lay["x"].shape[0] == T else make_x(w, T, dev)
+    act = torch.float32 if w.act == "f32" else torch.bfloat16
+    dy = make_dy(w, T, dev) if w.backward else None
+    r = LayerRunner(lay["w1"], lay["w2"], lay.get("w1_scale"), lay.get("w2_scale"), act_dtype=act,
+                    T=T, k=w.k, beta=w.beta, P=w.P, s=0 if fixed else w.s,
+                    owner=torch.from_numpy(contiguous_owners(w.E, w.P)), with_backward=w.backward)
+    return dict(runner=r, x=x, gates=torch.from_numpy(gates).to(dev), ids=torch.from_numpy(ids).to(dev),
+                dy=dy, ids_np=ids, gates_np=gates, lay=lay, T=T)
+
+
+def time_steps(case, steps, warmup, with_events=True):
+    """Times `steps` full steps; returns wall ms/step and per-stage mean ms."""
+    import torch
+
+    from moe_expert_ffn_amd import binding as B
+    r = case["runner"]
+    bwd = case["dy"] is not None
+
+    def one(evf=None, evb=None):
+        r.route(case["ids"])
+        r.make_plan(B.PLAN_FWD)
+        r.forward(case["x"], case["gates"], case["ids"], events=evf)
+        if bwd:
+            r.make_plan(B.PLAN_BWD, out=r.plan_b)
+            r.backward(case["x"], case["gates"], case["dy"], case["ids"], events=evb)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    evs = []
+    if with_events:
+        for _ in range(steps):
+            evs.append((B.Events(5), B.Events(7) if bwd else None, B.Events(2)))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if with_events:
+            ef, eb, es = evs[i]
+            es.record(0)
+            one(ef.ev, eb.ev if eb else None)
+            es.record(1)
+        else:
+            one()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    stages = {}
+    if with_events:
+        acc = {}
+        for ef, eb, es in evs:
+            for j, nm in enumerate(FWD_STAGES):
+                acc.setdefault("fwd." + nm, []).append(ef.elapsed_ms(j, j + 1))
+            if eb:
+                for j, nm in enumerate(BWD_STAGES):
+                    acc.setdefault("bwd." + nm, []).append(eb.elapsed_ms(j, j + 1))
+            acc.setdefault("step", []).append(es.elapsed_ms(0, 1))
+        stages = {k: sum(v) / len(v) for k, v in acc.items()}
+    assert int(r.status.item()) == 0, "device status word set"
+    return wall_ms, stages
+
+
+def kernel_flops(w, R):
+    dd = w.d * w.d_ff
+    return {"fwd.fc1": 4 * dd * R, "fwd.fc2": 2 * dd * R, "bwd.dA": 2 * dd * R,
+            "bwd.dX": 4 * dd * R, "bwd.dW": 6 * dd * R}
+
+
+def cpu_baseline(case, w, tokens):
+    """The oracle, untuned, on the first `tokens` tokens of the same workload:
+    forward of those tokens plus their dx, and dW of every expert over their
+    rows.  Useful TFLOP/s of that sample."""
+    import numpy as np
+
+    from oracle import ffn as offn
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    n = min(tokens, case["T"])
+    ids = case["ids_np"][:n]
+    gates = case["gates_np"][:n].astype(np.float64)
+    lay = case["lay"]
+    x = case["x"][:n].double().cpu().numpy()
+    w1 = lay["w1"].double().cpu().numpy()
+    w2 = lay["w2"].double().cpu().numpy()
+    rows = int((ids >= 0).sum())
+    f_fwd, f_bwd = flops_per_row(w)
+    t0 = time.perf_counter()
+    offn.forward(x, w1, w2, ids, gates)
+    flops = f_fwd * rows
+    if case["dy"] is not None:
+        dy = case["dy"][:n].double().cpu().numpy()
+        offn.backward(x, w1, w2, ids, gates, dy)
+        flops += f_bwd * rows
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n} of {case['T']} tokens ({rows} routed rows): dense fp64 forward"
+                      f"{' + backward (dx, dW)' if case['dy'] is not None else ''}, numpy",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the layer's P workers are CU partitions of a single "
+              f"MI355X; --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from moe_expert_ffn_amd import binding as B
+    from moe_expert_ffn_amd.inputs import WORKLOADS, realised_kappa
+    B.load()
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[args.workload]
+    case = build_case(w, args.kappa, args.fixed, dev)
+    R = int((case["ids_np"] >= 0).sum())
+    ms, stages = time_steps(case, args.steps, args.warmup)
+    f_fwd, f_bwd = flops_per_row(w)
+    useful = (f_fwd + (f_bwd if w.backward else 0)) * R
+    value = useful / (ms * 1e-3) / 1e12
+
+    kf = kernel_flops(w, R)
+    cand = {k: v for k, v in stages.items() if k in kf}
+    dom = max(cand, key=cand.get)
+    dur_s = cand[dom] * 1e-3
+    achieved = kf[dom] / dur_s / 1e12
+    peak = PEAK_BF16_TFLOPS
+    roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+            "launch_us": round(cand[dom] * 1e3, 2), "flops_per_launch": kf[dom]}
+
+    plan_f = case["runner"].plan_f["plan_info"].cpu().tolist()
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded routing, random-init weights)",
+        "config": {"workload": f"{w.name}: T={case['T']} d={w.d} d_ff={w.d_ff} E={w.E} top-{w.k} "
+                               f"beta={w.beta} P={w.P} s={0 if args.fixed else w.s} "
+                               f"kappa={args.kappa:g} ({'fwd+bwd' if w.backward else 'fwd'})",
+                   "kappa_realised": round(realised_kappa(case["ids_np"], w.E), 4),
+                   "routed_rows": R, "placement": "fixed" if args.fixed else "planned",
+                   "plan_info_fwd": plan_f},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "stages_us": {k: round(v * 1e3, 2) for k, v in stages.items()},
+        "roofline": roof,
+    }
+    if args.sweep:
+        sweep = []
+        for kap in w.kappas:
+            for fixed in (True, False):
+                c = build_case(w, kap, fixed, dev)
+                Rk = int((c["ids_np"] >= 0).sum())
+                msk, st = time_steps(c, max(5, args.steps // 2), 2)
+                uk = (f_fwd + (f_bwd if w.backward else 0)) * Rk
+                sweep.append({"kappa": kap, "placement": "fixed" if fixed else "planned",
+                              "ms": round(msk, 4), "tflops": round(uk / (msk * 1e-3) / 1e12, 2),
+                              "fwd_us": round(sum(v for k_, v in st.items() if k_.startswith("fwd.")) * 1e3, 1),
+                              "bwd_us": round(sum(v for k_, v in st.items() if k_.startswith("bwd.")) * 1e3, 1)})
+                del c
+                torch.cuda.empty_cache()
+        out["kappa_sweep"] = sweep
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(case, w, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

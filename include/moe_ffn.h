@@ -1,0 +1,197 @@
+/*
+ * moe_ffn.h -- C ABI of the skew-aware MoE expert layer for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operations follow the MegaFlux summary (picx.dev/p/e4jAzZ):
+ *   - routing statistics: per-expert counts c_e and the skew
+ *     kappa = E * sum_e (c_e / sum_j c_j)^2  ("Routing Skew Problem");
+ *   - token blocks of at most beta rows, b_e = ceil(c_e / beta), and the
+ *     min-max block placement q (E x P) under a per-worker replica budget s
+ *     ("Problem Formulation");
+ *   - the bounded greedy planner with four searches and the
+ *     reduction-aware backward variant C_lambda = max_r (l_r + lambda n_r)
+ *     ("Bounded Greedy Search");
+ *   - the SwiGLU expert computation and gated combine, and the gradients
+ *     dA = D W2^T, dX = dZ W1^T, dW2 = A^T D, dW1 = X^T dZ, with replica
+ *     partial weight gradients reduced into the owner in fp32 in a fixed
+ *     order ("Forward" / "Backward" and their equations).
+ *
+ * The P workers of the pages are CU partitions of one GPU: worker r runs on
+ * the XCDs {x : x * P / 8 == r} (P in {1, 2, 4, 8}).
+ *
+ * Conventions for every entry point:
+ *   - pointers are DEVICE pointers unless marked (host);
+ *   - every call only enqueues work on `stream` (a hipStream_t; NULL = the
+ *     default stream) and returns; it never synchronises the host, never
+ *     allocates device memory and keeps no state between calls;
+ *   - the caller owns every buffer; outputs are overwritten, never
+ *     accumulated into;
+ *   - the return value is a moe_status, decided on the host from the
+ *     arguments alone (nothing is launched when it is not MOE_OK);
+ *   - problems only visible on the device (an expert id >= E, a plan that
+ *     breaks its constraints) are OR-ed into *status_dev as MOE_DEV_* bits;
+ *     the caller zeroes it beforehand and reads it after its own sync;
+ *   - `ws` is a caller-provided device workspace of at least
+ *     moe_workspace_size(...) bytes, 256-byte aligned.  Calls that share a
+ *     workspace must not overlap in time (use one stream per workspace).
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = -1,          /* argument out of range, or a required pointer is NULL */
+  MOE_ERR_UNSUPPORTED = -2,  /* valid in principle, not implemented (see each call) */
+  MOE_ERR_WORKSPACE = -3,    /* ws is NULL, misaligned or smaller than required */
+  MOE_ERR_HIP = -4           /* the HIP runtime refused a launch */
+} moe_status;
+
+/* bits OR-ed into *status_dev by device code */
+#define MOE_DEV_BAD_EXPERT 1   /* a top-k id >= E (that row is skipped) */
+#define MOE_DEV_BAD_PLAN   2   /* block_worker outside [0,P), or a worker with more
+                                  than s non-home experts (those blocks are skipped) */
+#define MOE_DEV_BAD_OWNER  4   /* owner[e] outside [0,P) */
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+typedef enum { MOE_PLAN_FWD = 0, MOE_PLAN_BWD = 1 } moe_plan_mode;
+
+/* One expert layer.  The weights are stored transposed with respect to the
+ * pages' X W notation, so that both operands of every forward product are
+ * contiguous along the reduction dimension:
+ *   w1 [E][2*d_ff][d]: rows 0..d_ff-1 produce G, rows d_ff..2*d_ff-1 produce U;
+ *   w2 [E][d][d_ff].
+ * act_dtype (MOE_F32 or MOE_BF16) is the dtype of x, y, dy, dx and z_save.
+ * w_dtype is MOE_F32 (with act MOE_F32), MOE_BF16 (with act MOE_BF16) or
+ * MOE_FP8_E4M3 (OCP e4m3fn codes, act MOE_BF16, forward only); fp8 weights
+ * carry one fp32 scale per 128x128 block:
+ *   w1_scale [E][2*d_ff/128][d/128], w2_scale [E][d/128][d_ff/128].
+ * Requires d % 128 == 0 and d_ff % 64 == 0 (fp8: d_ff % 128 == 0). */
+typedef struct {
+  int E, d, d_ff;
+  int act_dtype;
+  int w_dtype;
+  const void* w1;
+  const void* w2;
+  const float* w1_scale;
+  const float* w2_scale;
+} moe_layer;
+
+int moe_abi_version(void);
+const char* moe_status_str(int status);
+
+/* Upper bound of the padded slot count: T*k + E*(beta-1). */
+size_t moe_max_slots(int T, int k, int E, int beta);
+/* Upper bound of sum_e b_e: (T*k + E*(beta-1)) / beta. */
+size_t moe_max_blocks(int T, int k, int E, int beta);
+
+/* Workspace needed by moe_route_stats, moe_plan, moe_forward and (when
+ * with_backward != 0) moe_backward for these sizes; one workspace serves all
+ * of them.  `L` (host) must be valid; returns 0 for invalid arguments. */
+size_t moe_workspace_size(const moe_layer* L, int T, int k, int beta, int P, int s,
+                          int with_backward);
+
+/* Routing statistics ("Routing Skew Problem" kappa equation; block
+ * definition of "Problem Formulation").
+ *   topk_ids [T][k] int32: expert of each (token, slot); id < 0 = no expert.
+ *   counts [E]: c_e.  offsets [E+1]: exclusive prefix sum of c.
+ *   block_counts [E]: b_e = ceil(c_e/beta).  block_offsets [E+1]: prefix sum of b.
+ *   row_to_slot [T*k]: padded slot of routed row i = t*k + j, -1 when id < 0.
+ *     Rows of expert e occupy slots beta*block_offsets[e] ... in increasing i.
+ *   slot_to_row [moe_max_slots]: inverse map, -1 for padding slots.
+ *   kappa [1] (double): E * sum c^2 / (sum c)^2 computed from exact integers
+ *     with one IEEE division; 1.0 when nothing is routed.
+ * Limits: 1 <= E <= 1024, 1 <= k, 1 <= beta, T >= 0, T*k < 2^31. */
+int moe_route_stats(const int32_t* topk_ids, int T, int k, int E, int beta,
+                    int32_t* counts, int32_t* offsets, int32_t* block_counts,
+                    int32_t* block_offsets, int32_t* row_to_slot, int32_t* slot_to_row,
+                    double* kappa, int32_t* status_dev, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* Replica placement and block assignment ("Problem Formulation", "Bounded
+ * Greedy Search").  Runs entirely on the device (no host round trip), one
+ * workgroup; integer-only, so the result is deterministic.
+ *   block_counts [E], block_offsets [E+1]: from moe_route_stats.
+ *   owner [E]: h(e) in [0, P), the home worker of each expert.
+ *   mode MOE_PLAN_FWD minimises max_r l_r; MOE_PLAN_BWD minimises
+ *   max_r (l_r + lambda * n_r), n_r = remote copies of r's experts.
+ *   s = 0 gives fixed placement.
+ * Outputs: q [E][P] blocks of e on r; load [P] = l_r; block_worker
+ *   [moe_max_blocks]: worker of each block (expert e's blocks go to its owner
+ *   first, then to ascending workers; entries past sum b are untouched);
+ *   plan_info [4] = {objective, chosen search 0..3, replica count, tau}.
+ * Limits: 1 <= E <= 512, P in {1,2,4,8}, s >= 0, lambda >= 0. */
+int moe_plan(const int32_t* block_counts, const int32_t* block_offsets,
+             const int32_t* owner, int E, int P, int s, int mode, int lambda,
+             int32_t* q, int32_t* load, int32_t* block_worker, int32_t* plan_info,
+             int32_t* status_dev, void* ws, size_t ws_bytes, void* stream);
+
+/* Forward expert layer ("Backward" section, expert-computation equation):
+ *   y_t = sum_{j: id_tj >= 0} p_tj * W2_e (SiLU(G) * U),  [G; U] = W1_e x_t,
+ * executed over the planned blocks: worker r's CU partition runs the blocks
+ * with block_worker == r.  The result does not depend on the plan: every
+ * routed row is computed by the same code whatever worker runs it, and the k
+ * contributions of a token are added in slot order in fp32, rounded once.
+ *   x [T][d] act dtype; gates [T][k] fp32 (p_tj);
+ *   counts/block_offsets/row_to_slot/slot_to_row from moe_route_stats;
+ *   block_worker from moe_plan (or any assignment of blocks to [0,P)).
+ *   y [T][d] act dtype.
+ *   z_save (nullable) [moe_max_slots][2*d_ff] act dtype: receives [G, U] of
+ *     every routed row, as needed by moe_backward.
+ *   stage_events (host, nullable): 5 hipEvent_t recorded on `stream` at
+ *     start / after scheduling / after FC1 / after FC2 / after combine. */
+int moe_forward(const moe_layer* L, const void* x, const float* gates,
+                const int32_t* topk_ids, int T, int k, int beta, int P,
+                const int32_t* counts, const int32_t* block_offsets,
+                const int32_t* row_to_slot, const int32_t* slot_to_row,
+                const int32_t* block_worker, void* y, void* z_save,
+                int32_t* status_dev, void* ws, size_t ws_bytes,
+                void* const* stage_events, void* stream);
+
+/* Backward expert layer (gradient equations of the "Backward" section), with
+ * D_t = p_tj * dy_t:
+ *   dx_t = sum_j W1_e^T [dG; dU],  dG = dA * U * s(G)(1 + G(1 - s(G))),
+ *   dU = dA * SiLU(G),  dA = W2_e^T D;
+ *   dw2[e] = sum_rows D A^T,  dw1[e] = sum_rows [dG; dU] x^T   (fp32).
+ * Worker r computes the weight-gradient partial of every expert it holds
+ * blocks of; a non-owner's partial goes to one of its s replica slots in
+ * `ws`, and each owner slot dw*[e] = owner partial + replica partials in
+ * ascending worker order, in fp32 (early fixed-order owner reduction).
+ *   dy [T][d], z_save from moe_forward on the same routing, owner [E] = h(e);
+ *   dx [T][d] act dtype; dw1 [E][2*d_ff][d] fp32; dw2 [E][d][d_ff] fp32.
+ *   stage_events (host, nullable): 7 events: start / after scheduling /
+ *     after dA / after dX / after dx combine / after weight gradients /
+ *     after replica reduction.
+ * MOE_ERR_UNSUPPORTED for fp8 weights. */
+int moe_backward(const moe_layer* L, const void* x, const float* gates, const void* dy,
+                 const void* z_save, const int32_t* topk_ids, int T, int k, int beta,
+                 int P, int s, const int32_t* counts, const int32_t* block_offsets,
+                 const int32_t* row_to_slot, const int32_t* slot_to_row,
+                 const int32_t* owner, const int32_t* block_worker, void* dx, float* dw1,
+                 float* dw2, int32_t* status_dev, void* ws, size_t ws_bytes,
+                 void* const* stage_events, void* stream);
+
+/* Timing helpers so a caller without a HIP binding can time the stages:
+ * create / destroy a hipEvent_t, and the milliseconds between two recorded
+ * events (waits for `b`). */
+int moe_event_create(void** ev);
+int moe_event_destroy(void* ev);
+int moe_event_record(void* ev, void* stream);
+int moe_event_elapsed_ms(void* a, void* b, float* ms);
+
+/* Number of CUs and XCDs of the current device (host; for reporting). */
+int moe_device_info(int* num_cus, int* num_xcds, int* wg_per_cu_gemm);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FFN_H */

@@ -1,0 +1,240 @@
+"""Thin ctypes binding of libmoe_ffn.so (C ABI in include/moe_ffn.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  torch provides device memory and the current HIP stream.  The
+library must have been built (``python moe_expert_ffn_amd/build.py`` or
+``__graft_entry__.build()``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_ffn.so")
+
+MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+PLAN_FWD, PLAN_BWD = 0, 1
+DEV_BAD_EXPERT, DEV_BAD_PLAN, DEV_BAD_OWNER = 1, 2, 4
+
+EXPORTS = ["moe_abi_version", "moe_status_str", "moe_max_slots", "moe_max_blocks",
+           "moe_workspace_size", "moe_route_stats", "moe_plan", "moe_forward", "moe_backward",
+           "moe_event_create", "moe_event_destroy", "moe_event_record", "moe_event_elapsed_ms",
+           "moe_device_info"]
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("E", ctypes.c_int), ("d", ctypes.c_int), ("d_ff", ctypes.c_int),
+                ("act_dtype", ctypes.c_int), ("w_dtype", ctypes.c_int),
+                ("w1", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("w1_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+
+def load():
+    """Load the built library (raises MoeError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise MoeError(f"{LIB_PATH} is missing: build it with moe_expert_ffn_amd/build.py")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.moe_abi_version.restype = _I
+    lib.moe_status_str.restype = ctypes.c_char_p
+    lib.moe_status_str.argtypes = [_I]
+    lib.moe_max_slots.restype = _SZ
+    lib.moe_max_slots.argtypes = [_I, _I, _I, _I]
+    lib.moe_max_blocks.restype = _SZ
+    lib.moe_max_blocks.argtypes = [_I, _I, _I, _I]
+    lib.moe_workspace_size.restype = _SZ
+    lib.moe_workspace_size.argtypes = [ctypes.POINTER(Layer), _I, _I, _I, _I, _I, _I]
+    lib.moe_route_stats.restype = _I
+    lib.moe_route_stats.argtypes = [_P, _I, _I, _I, _I] + [_P] * 8 + [_P, _SZ, _P]
+    lib.moe_plan.restype = _I
+    lib.moe_plan.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I] + [_P] * 5 + [_P, _SZ, _P]
+    lib.moe_forward.restype = _I
+    lib.moe_forward.argtypes = ([ctypes.POINTER(Layer), _P, _P, _P, _I, _I, _I, _I]
+                                + [_P] * 8 + [_P, _SZ, _P, _P])
+    lib.moe_backward.restype = _I
+    lib.moe_backward.argtypes = ([ctypes.POINTER(Layer), _P, _P, _P, _P, _P, _I, _I, _I, _I, _I]
+                                 + [_P] * 10 + [_P, _SZ, _P, _P])
+    lib.moe_event_create.argtypes = [ctypes.POINTER(_P)]
+    lib.moe_event_destroy.argtypes = [_P]
+    lib.moe_event_record.argtypes = [_P, _P]
+    lib.moe_event_elapsed_ms.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_float)]
+    lib.moe_device_info.argtypes = [ctypes.POINTER(_I)] * 3
+    _lib = lib
+    return lib
+
+
+def _check(rc):
+    if rc != MOE_OK:
+        raise MoeError(f"libmoe_ffn: {load().moe_status_str(rc).decode()} ({rc})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _require_device(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise MoeError("all buffers must be contiguous device tensors")
+
+
+def act_code(dtype) -> int:
+    return MOE_F32 if dtype == torch.float32 else MOE_BF16
+
+
+def make_layer(w1, w2, w1_scale=None, w2_scale=None, act_dtype=torch.bfloat16) -> Layer:
+    _require_device(w1, w2, w1_scale, w2_scale)
+    E, two_dff, d = w1.shape
+    if w1.dtype == torch.uint8:
+        wcode = MOE_FP8_E4M3
+    elif w1.dtype == torch.float32:
+        wcode = MOE_F32
+    else:
+        wcode = MOE_BF16
+    return Layer(E, d, two_dff // 2, act_code(act_dtype), wcode, w1.data_ptr(), w2.data_ptr(),
+                 w1_scale.data_ptr() if w1_scale is not None else None,
+                 w2_scale.data_ptr() if w2_scale is not None else None)
+
+
+def max_slots(T, k, E, beta) -> int:
+    return int(load().moe_max_slots(T, k, E, beta))
+
+
+def max_blocks(T, k, E, beta) -> int:
+    return int(load().moe_max_blocks(T, k, E, beta))
+
+
+def workspace(layer: Layer, T, k, beta, P, s, with_backward, device) -> torch.Tensor:
+    n = int(load().moe_workspace_size(ctypes.byref(layer), T, k, beta, P, s, int(with_backward)))
+    if n == 0:
+        raise MoeError("moe_workspace_size rejected the sizes")
+    return torch.empty(n + 256, dtype=torch.uint8, device=device)
+
+
+def _aligned(ws: torch.Tensor):
+    p = ws.data_ptr()
+    off = (-p) % 256
+    return ctypes.c_void_p(p + off), ws.numel() - off
+
+
+def alloc_route(T, k, E, beta, device):
+    i32 = dict(dtype=torch.int32, device=device)
+    return {
+        "counts": torch.empty(E, **i32), "offsets": torch.empty(E + 1, **i32),
+        "block_counts": torch.empty(E, **i32), "block_offsets": torch.empty(E + 1, **i32),
+        "row_to_slot": torch.empty(max(T * k, 1), **i32),
+        "slot_to_row": torch.empty(max(max_slots(T, k, E, beta), 1), **i32),
+        "kappa": torch.empty(1, dtype=torch.float64, device=device),
+    }
+
+
+def route_stats(topk_ids: torch.Tensor, E: int, beta: int, out: dict, ws: torch.Tensor,
+                status: torch.Tensor):
+    _require_device(topk_ids, ws, status, *out.values())
+    T, k = topk_ids.shape
+    wsp, wsn = _aligned(ws)
+    _check(load().moe_route_stats(_ptr(topk_ids), T, k, E, beta, _ptr(out["counts"]),
+                                  _ptr(out["offsets"]), _ptr(out["block_counts"]),
+                                  _ptr(out["block_offsets"]), _ptr(out["row_to_slot"]),
+                                  _ptr(out["slot_to_row"]), _ptr(out["kappa"]), _ptr(status),
+                                  wsp, wsn, _stream()))
+    return out
+
+
+def alloc_plan(E, P, nblocks_cap, device):
+    i32 = dict(dtype=torch.int32, device=device)
+    return {"q": torch.empty((E, P), **i32), "load": torch.empty(P, **i32),
+            "block_worker": torch.full((max(nblocks_cap, 1),), -1, **i32),
+            "plan_info": torch.empty(4, **i32)}
+
+
+def plan(block_counts, block_offsets, owner, P, s, mode, lam, out, ws, status):
+    _require_device(block_counts, block_offsets, owner, ws, status, *out.values())
+    E = block_counts.numel()
+    wsp, wsn = _aligned(ws)
+    _check(load().moe_plan(_ptr(block_counts), _ptr(block_offsets), _ptr(owner), E, P, s, mode,
+                           lam, _ptr(out["q"]), _ptr(out["load"]), _ptr(out["block_worker"]),
+                           _ptr(out["plan_info"]), _ptr(status), wsp, wsn, _stream()))
+    return out
+
+
+def forward(layer: Layer, x, gates, topk_ids, beta, P, rs, block_worker, y, z_save, ws, status,
+            events=None):
+    _require_device(x, gates, topk_ids, y, z_save, ws, status, block_worker)
+    T, k = topk_ids.shape
+    wsp, wsn = _aligned(ws)
+    ev = None if events is None else (ctypes.c_void_p * len(events))(*events)
+    _check(load().moe_forward(ctypes.byref(layer), _ptr(x), _ptr(gates), _ptr(topk_ids), T, k,
+                              beta, P, _ptr(rs["counts"]), _ptr(rs["block_offsets"]),
+                              _ptr(rs["row_to_slot"]), _ptr(rs["slot_to_row"]),
+                              _ptr(block_worker), _ptr(y), _ptr(z_save), _ptr(status), wsp, wsn,
+                              ev, _stream()))
+
+
+def backward(layer: Layer, x, gates, dy, z_save, topk_ids, beta, P, s, rs, owner, block_worker,
+             dx, dw1, dw2, ws, status, events=None):
+    _require_device(x, gates, dy, z_save, topk_ids, owner, block_worker, dx, dw1, dw2, ws, status)
+    T, k = topk_ids.shape
+    wsp, wsn = _aligned(ws)
+    ev = None if events is None else (ctypes.c_void_p * len(events))(*events)
+    _check(load().moe_backward(ctypes.byref(layer), _ptr(x), _ptr(gates), _ptr(dy), _ptr(z_save),
+                               _ptr(topk_ids), T, k, beta, P, s, _ptr(rs["counts"]),
+                               _ptr(rs["block_offsets"]), _ptr(rs["row_to_slot"]),
+                               _ptr(rs["slot_to_row"]), _ptr(owner), _ptr(block_worker), _ptr(dx),
+                               _ptr(dw1), _ptr(dw2), _ptr(status), wsp, wsn, ev, _stream()))
+
+
+class Events:
+    """n hipEvent_t created through the library, for stage timing on the
+    stream the kernels run on."""
+
+    def __init__(self, n):
+        lib = load()
+        self.ev = []
+        for _ in range(n):
+            p = ctypes.c_void_p()
+            _check(lib.moe_event_create(ctypes.byref(p)))
+            self.ev.append(p.value)
+
+    def elapsed_ms(self, i, j) -> float:
+        ms = ctypes.c_float()
+        _check(load().moe_event_elapsed_ms(ctypes.c_void_p(self.ev[i]), ctypes.c_void_p(self.ev[j]),
+                                          ctypes.byref(ms)))
+        return float(ms.value)
+
+    def record(self, i):
+        _check(load().moe_event_record(ctypes.c_void_p(self.ev[i]), _stream()))
+
+    def __del__(self):
+        try:
+            lib = load()
+            for e in self.ev:
+                lib.moe_event_destroy(ctypes.c_void_p(e))
+        except Exception:
+            pass
+
+
+def device_info():
+    a, b, c = _I(), _I(), _I()
+    _check(load().moe_device_info(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return {"num_cus": a.value, "num_xcds": b.value, "gemm_wg_per_cu": c.value}

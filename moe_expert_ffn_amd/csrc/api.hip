@@ -1,0 +1,206 @@
+// C ABI of the MoE expert layer: argument checks on the host, workspace
+// carving and kernel launches.  No allocation, no host synchronisation.
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+#include "moe_ffn.h"
+
+using namespace moe;
+
+namespace {
+
+bool valid_P(int P) { return P == 1 || P == 2 || P == 4 || P == 8; }
+
+bool ws_ok(const void* ws, size_t have, size_t need) {
+  if (need == 0) return true;
+  if (!ws) return false;
+  if (((uintptr_t)ws) & 255u) return false;
+  return have >= need;
+}
+
+// Shared validation of the layer description; returns MOE_OK or an error.
+int check_layer(const moe_layer* L, bool backward) {
+  if (!L) return MOE_ERR_ARG;
+  if (L->E < 1 || L->d < 1 || L->d_ff < 1) return MOE_ERR_ARG;
+  if (!L->w1 || !L->w2) return MOE_ERR_ARG;
+  if (L->E > kMaxPlanExperts) return MOE_ERR_UNSUPPORTED;
+  if (L->d % 128 != 0 || L->d_ff % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  const bool f32 = L->act_dtype == MOE_F32 && L->w_dtype == MOE_F32;
+  const bool bf = L->act_dtype == MOE_BF16 && L->w_dtype == MOE_BF16;
+  const bool f8 = L->act_dtype == MOE_BF16 && L->w_dtype == MOE_FP8_E4M3;
+  if (!f32 && !bf && !f8) return L->act_dtype > MOE_BF16 || L->w_dtype > MOE_FP8_E4M3
+                                     ? MOE_ERR_ARG : MOE_ERR_UNSUPPORTED;
+  if (f8) {
+    if (backward) return MOE_ERR_UNSUPPORTED;
+    if (L->d_ff % 128 != 0) return MOE_ERR_UNSUPPORTED;
+    if (!L->w1_scale || !L->w2_scale) return MOE_ERR_ARG;
+  }
+  return MOE_OK;
+}
+
+Sizes make_sizes(const moe_layer* L, int T, int k, int beta, int P, int s) {
+  Sizes z{};
+  z.T = T; z.k = k; z.E = L->E; z.d = L->d; z.dff = L->d_ff; z.beta = beta; z.P = P; z.s = s;
+  z.act_bytes = L->act_dtype == MOE_F32 ? 4 : 2;
+  z.max_slots = moe_max_slots(T, k, L->E, beta);
+  z.max_blocks = moe_max_blocks(T, k, L->E, beta);
+  const size_t per_block = beta > kBM ? (size_t)(beta + kBM - 1) / kBM : 1;
+  z.max_mt = z.max_blocks * per_block;
+  return z;
+}
+
+bool sizes_ok(int T, int k, int E, int beta) {
+  if (T < 0 || k < 1 || E < 1 || beta < 1) return false;
+  const long long slots = (long long)T * k + (long long)E * (beta - 1);
+  return slots < (1ll << 31);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_max_slots(int T, int k, int E, int beta) {
+  if (!sizes_ok(T, k, E, beta)) return 0;
+  return (size_t)T * k + (size_t)E * (beta - 1);
+}
+
+size_t moe_max_blocks(int T, int k, int E, int beta) {
+  if (!sizes_ok(T, k, E, beta)) return 0;
+  return ((size_t)T * k + (size_t)E * (beta - 1)) / beta;
+}
+
+size_t moe_workspace_size(const moe_layer* L, int T, int k, int beta, int P, int s,
+                          int with_backward) {
+  if (!L || !sizes_ok(T, k, L->E, beta) || !valid_P(P) || s < 0) return 0;
+  if (L->E > kMaxExperts) return 0;
+  size_t need = route_ws_bytes(T, k, L->E);
+  if (L->E <= kMaxPlanExperts && L->d > 0 && L->d_ff > 0) {
+    const Sizes z = make_sizes(L, T, k, beta, P, s);
+    const size_t f = exec_layout(z, false).total;
+    if (f > need) need = f;
+    if (with_backward) {
+      const size_t b = exec_layout(z, true).total;
+      if (b > need) need = b;
+    }
+  }
+  return need;
+}
+
+int moe_route_stats(const int32_t* topk_ids, int T, int k, int E, int beta, int32_t* counts,
+                    int32_t* offsets, int32_t* block_counts, int32_t* block_offsets,
+                    int32_t* row_to_slot, int32_t* slot_to_row, double* kappa,
+                    int32_t* status_dev, void* ws, size_t ws_bytes, void* stream) {
+  if (!sizes_ok(T, k, E, beta)) return MOE_ERR_ARG;
+  if (E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if ((T > 0 && (!topk_ids || !row_to_slot)) || !counts || !offsets || !block_counts ||
+      !block_offsets || !slot_to_row || !kappa || !status_dev)
+    return MOE_ERR_ARG;
+  if (!ws_ok(ws, ws_bytes, route_ws_bytes(T, k, E))) return MOE_ERR_WORKSPACE;
+  return launch_route_stats(topk_ids, T, k, E, beta, counts, offsets, block_counts,
+                            block_offsets, row_to_slot, slot_to_row, kappa, status_dev, ws,
+                            (hipStream_t)stream);
+}
+
+int moe_plan(const int32_t* block_counts, const int32_t* block_offsets, const int32_t* owner,
+             int E, int P, int s, int mode, int lambda, int32_t* q, int32_t* load,
+             int32_t* block_worker, int32_t* plan_info, int32_t* status_dev, void* ws,
+             size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (E < 1 || s < 0 || lambda < 0 || (mode != MOE_PLAN_FWD && mode != MOE_PLAN_BWD))
+    return MOE_ERR_ARG;
+  if (!valid_P(P) || E > kMaxPlanExperts) return MOE_ERR_UNSUPPORTED;
+  if (!block_counts || !block_offsets || !owner || !q || !load || !block_worker ||
+      !plan_info || !status_dev)
+    return MOE_ERR_ARG;
+  return launch_plan(block_counts, block_offsets, owner, E, P, s, mode, lambda, q, load,
+                     block_worker, plan_info, status_dev, (hipStream_t)stream);
+}
+
+int moe_forward(const moe_layer* L, const void* x, const float* gates, const int32_t* topk_ids,
+                int T, int k, int beta, int P, const int32_t* counts,
+                const int32_t* block_offsets, const int32_t* row_to_slot,
+                const int32_t* slot_to_row, const int32_t* block_worker, void* y, void* z_save,
+                int32_t* status_dev, void* ws, size_t ws_bytes, void* const* stage_events,
+                void* stream) {
+  (void)topk_ids;
+  const int lc = check_layer(L, false);
+  if (lc != MOE_OK) return lc;
+  if (!sizes_ok(T, k, L->E, beta)) return MOE_ERR_ARG;
+  if (!valid_P(P)) return MOE_ERR_UNSUPPORTED;
+  if ((T > 0 && (!x || !gates || !row_to_slot || !y)) || !counts || !block_offsets ||
+      !slot_to_row || !block_worker || !status_dev)
+    return MOE_ERR_ARG;
+  const Sizes z = make_sizes(L, T, k, beta, P, 0);
+  if (!ws_ok(ws, ws_bytes, exec_layout(z, false).total)) return MOE_ERR_WORKSPACE;
+  LayerPtrs Lp{L->w1, L->w2, L->w1_scale, L->w2_scale, L->act_dtype, L->w_dtype};
+  return launch_forward(z, Lp, x, gates, counts, block_offsets, row_to_slot, slot_to_row,
+                        block_worker, y, z_save, status_dev, (char*)ws, stage_events,
+                        (hipStream_t)stream);
+}
+
+int moe_backward(const moe_layer* L, const void* x, const float* gates, const void* dy,
+                 const void* z_save, const int32_t* topk_ids, int T, int k, int beta, int P,
+                 int s, const int32_t* counts, const int32_t* block_offsets,
+                 const int32_t* row_to_slot, const int32_t* slot_to_row, const int32_t* owner,
+                 const int32_t* block_worker, void* dx, float* dw1, float* dw2,
+                 int32_t* status_dev, void* ws, size_t ws_bytes, void* const* stage_events,
+                 void* stream) {
+  (void)topk_ids;
+  const int lc = check_layer(L, true);
+  if (lc != MOE_OK) return lc;
+  if (!sizes_ok(T, k, L->E, beta) || s < 0) return MOE_ERR_ARG;
+  if (!valid_P(P)) return MOE_ERR_UNSUPPORTED;
+  if ((T > 0 && (!x || !gates || !dy || !z_save || !row_to_slot || !dx)) || !counts ||
+      !block_offsets || !slot_to_row || !owner || !block_worker || !dw1 || !dw2 || !status_dev)
+    return MOE_ERR_ARG;
+  const Sizes z = make_sizes(L, T, k, beta, P, s);
+  if (!ws_ok(ws, ws_bytes, exec_layout(z, true).total)) return MOE_ERR_WORKSPACE;
+  LayerPtrs Lp{L->w1, L->w2, L->w1_scale, L->w2_scale, L->act_dtype, L->w_dtype};
+  return launch_backward(z, Lp, x, gates, dy, z_save, counts, block_offsets, row_to_slot,
+                         slot_to_row, owner, block_worker, dx, dw1, dw2, status_dev, (char*)ws,
+                         stage_events, (hipStream_t)stream);
+}
+
+int moe_event_create(void** ev) {
+  if (!ev) return MOE_ERR_ARG;
+  return hipEventCreate((hipEvent_t*)ev) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+int moe_event_destroy(void* ev) {
+  return hipEventDestroy((hipEvent_t)ev) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+int moe_event_record(void* ev, void* stream) {
+  return hipEventRecord((hipEvent_t)ev, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+int moe_event_elapsed_ms(void* a, void* b, float* ms) {
+  if (!ms) return MOE_ERR_ARG;
+  if (hipEventSynchronize((hipEvent_t)b) != hipSuccess) return MOE_ERR_HIP;
+  return hipEventElapsedTime(ms, (hipEvent_t)a, (hipEvent_t)b) == hipSuccess ? MOE_OK
+                                                                              : MOE_ERR_HIP;
+}
+
+int moe_device_info(int* num_cus, int* num_xcds, int* wg_per_cu_gemm) {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (num_cus) *num_cus = n;
+  if (num_xcds) *num_xcds = 8;
+  if (wg_per_cu_gemm) *wg_per_cu_gemm = gemm_wg_per_cu();
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Device helpers shared by the MoE expert-layer kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_DEV __device__ __forceinline__
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies
+constexpr int kMaxP = 8;
+
+// bf16 is carried as raw 16-bit words; conversions are exact (widen) or
+// round-to-nearest-even (narrow, NaN kept quiet).
+MOE_DEV float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+MOE_DEV uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// OCP e4m3fn -> float, from the format's definition: sign, 4-bit exponent with
+// bias 7, 3-bit mantissa, subnormals at exponent 0.  (S.1111.111 = NaN is never
+// produced by the weight quantiser and decodes as 480 here.)
+MOE_DEV float e4m3_to_f32(uint32_t c) {
+  uint32_t ex = (c >> 3) & 0xfu, man = c & 7u;
+  float mag = ex ? __uint_as_float(((ex + 120u) << 23) | (man << 20))
+                 : (float)man * (1.0f / 512.0f);
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// Worker (CU partition) of a workgroup.  Workgroups of one dispatch are handed
+// to the XCDs round-robin, so blockIdx % 8 is the XCD; worker r owns the XCDs
+// x with x * P / 8 == r.  Correctness never depends on the mapping being
+// physical: every worker always receives gridDim/ P workgroups.
+MOE_DEV int worker_of_block(int P) { return (int)(blockIdx.x % kXcds) * P / kXcds; }
+
+// Wave-wide inclusive prefix sum (64 lanes).
+MOE_DEV int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+MOE_DEV int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+MOE_DEV long long wave_sum64(long long v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Lanes of this wave holding the same value as this lane (value < 2^nbits).
+MOE_DEV uint64_t wave_match(uint32_t v, int nbits, bool active) {
+  uint64_t m = __ballot(active);
+  for (int b = 0; b < nbits; ++b) {
+    uint64_t bal = __ballot(active && ((v >> b) & 1u));
+    m &= ((v >> b) & 1u) ? bal : ~bal;
+  }
+  return active ? m : 0ull;
+}
+
+MOE_DEV uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & 63;
+  return lane ? (~0ull >> (64 - lane)) : 0ull;
+}
+
+}  // namespace moe

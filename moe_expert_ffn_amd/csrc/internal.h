@@ -1,0 +1,65 @@
+// Library-internal declarations: limits, workspace layout and the launchers
+// behind the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxExperts = 1024;      // routing statistics
+constexpr int kMaxPlanExperts = 512;   // planner and executors (LDS-resident tables)
+constexpr int kBM = 128;               // rows of one GEMM tile (= one M-tile)
+constexpr int kBN = 128;               // columns of one GEMM tile
+constexpr int kNumCounters = 64;       // per-(phase, worker) work counters
+
+inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Per-worker M-tile descriptor: expert, first slot, valid rows (<= kBM).
+// Per-worker weight-gradient segment: expert, first slot, valid rows,
+// destination (-1 = the owner's slot dw*[e], else a replica slot index).
+struct Sizes {
+  int T, k, E, d, dff, beta, P, s;
+  int act_bytes;
+  size_t max_slots, max_blocks, max_mt;
+};
+
+struct WsLayout {
+  size_t ctr, mt_cnt, mt, seg_cnt, seg, rep_slot, owner_has, bufA, bufO, rslots, total;
+};
+
+WsLayout exec_layout(const Sizes& z, bool backward);
+size_t route_ws_bytes(int T, int k, int E);
+
+int launch_route_stats(const int32_t* ids, int T, int k, int E, int beta, int32_t* counts,
+                       int32_t* offsets, int32_t* block_counts, int32_t* block_offsets,
+                       int32_t* row_to_slot, int32_t* slot_to_row, double* kappa,
+                       int32_t* status, void* ws, hipStream_t st);
+int launch_plan(const int32_t* bcnt, const int32_t* boff, const int32_t* owner, int E, int P,
+                int s, int mode, int lam, int32_t* q, int32_t* load, int32_t* bw,
+                int32_t* info, int32_t* status, hipStream_t st);
+
+struct LayerPtrs {
+  const void* w1;
+  const void* w2;
+  const float* w1s;
+  const float* w2s;
+  int act_dtype, w_dtype;
+};
+
+int launch_forward(const Sizes& z, const LayerPtrs& L, const void* x, const float* gates,
+                   const int32_t* counts, const int32_t* boff, const int32_t* row_to_slot,
+                   const int32_t* slot_to_row, const int32_t* block_worker, void* y,
+                   void* z_save, int32_t* status, char* ws, void* const* ev, hipStream_t st);
+
+int launch_backward(const Sizes& z, const LayerPtrs& L, const void* x, const float* gates,
+                    const void* dy, const void* z_save, const int32_t* counts,
+                    const int32_t* boff, const int32_t* row_to_slot,
+                    const int32_t* slot_to_row, const int32_t* owner,
+                    const int32_t* block_worker, void* dx, float* dw1, float* dw2,
+                    int32_t* status, char* ws, void* const* ev, hipStream_t st);
+
+int gemm_wg_per_cu();
+
+}  // namespace moe

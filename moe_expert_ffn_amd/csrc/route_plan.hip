@@ -1,0 +1,356 @@
+// Routing statistics and the on-device planner.
+//
+// Routing statistics (MegaFlux summary, "Routing Skew Problem" kappa equation
+// and the block definition of "Problem Formulation"):
+//   c_e, exclusive prefix sums, b_e = ceil(c_e / beta), kappa, and a stable
+//   padded slotting in which expert e's rows occupy slots beta * sum_{e'<e} b_e'
+//   onward in increasing flat index t*k + j.
+// Three launches: per-chunk histograms (LDS atomics; order-free), one
+// workgroup that scans them per expert and across experts, and a slotting pass
+// in which each wave ranks equal ids with a ballot-based match, so the slot of
+// a row depends only on the rows before it.
+//
+// Planner ("Problem Formulation", "Bounded Greedy Search"): one workgroup of
+// four waves; wave w runs greedy search w (donor priority x fan-out), lane r of
+// a wave holds worker r's load, replica count and remote-copy count, and the
+// search state q lives in LDS.  Every quantity is an integer, so the plan is
+// bit-identical on every run and to any other implementation of the same
+// reading (owner-first contiguous expansion, smallest index on every tie).
+#include "common.h"
+#include "moe_ffn.h"
+#include "internal.h"
+
+namespace moe {
+
+constexpr int kChunk = 256;
+
+__global__ __launch_bounds__(256) void k_route_count(const int32_t* __restrict__ ids, int N,
+                                                     int E, int32_t* __restrict__ chunk_cnt,
+                                                     int32_t* __restrict__ slot_to_row, int cap,
+                                                     int32_t* status) {
+  __shared__ int cnt[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  __syncthreads();
+  const int i = blockIdx.x * kChunk + threadIdx.x;
+  if (i < N) {
+    const int v = ids[i];
+    if (v >= E) atomicOr(status, MOE_DEV_BAD_EXPERT);
+    else if (v >= 0) atomicAdd(&cnt[v], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) chunk_cnt[(size_t)blockIdx.x * E + e] = cnt[e];
+  for (int sidx = blockIdx.x * kChunk + threadIdx.x; sidx < cap; sidx += gridDim.x * kChunk)
+    slot_to_row[sidx] = -1;
+}
+
+// One workgroup of 1024 threads; thread e owns expert e.
+__global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk_cnt, int nchunks,
+                                                     int E, int beta, int32_t* counts,
+                                                     int32_t* offsets, int32_t* block_counts,
+                                                     int32_t* block_offsets, double* kappa) {
+  __shared__ int wtot_c[16], wtot_b[16];
+  __shared__ long long red_s[16], red_s2[16];
+  const int e = threadIdx.x, lane = e & 63, wv = e >> 6;
+  int c = 0;
+  if (e < E)
+    for (int ch = 0; ch < nchunks; ++ch) c += chunk_cnt[(size_t)ch * E + e];
+  const int b = (c + beta - 1) / beta;
+  const int ic = wave_incl_scan(c), ib = wave_incl_scan(b);
+  if (lane == 63) { wtot_c[wv] = ic; wtot_b[wv] = ib; }
+  long long s1 = wave_sum64((long long)c), s2 = wave_sum64((long long)c * c);
+  if (lane == 0) { red_s[wv] = s1; red_s2[wv] = s2; }
+  __syncthreads();
+  int pc = 0, pb = 0;
+  for (int w = 0; w < wv; ++w) { pc += wtot_c[w]; pb += wtot_b[w]; }
+  const int exc_c = pc + ic - c, exc_b = pb + ib - b;
+  if (e < E) {
+    counts[e] = c;
+    offsets[e] = exc_c;
+    block_counts[e] = b;
+    block_offsets[e] = exc_b;
+    if (e == E - 1) { offsets[E] = exc_c + c; block_offsets[E] = exc_b + b; }
+    int run = beta * exc_b;
+    for (int ch = 0; ch < nchunks; ++ch) {
+      const size_t at = (size_t)ch * E + e;
+      const int t = chunk_cnt[at];
+      chunk_cnt[at] = run;
+      run += t;
+    }
+  }
+  if (e == 0) {
+    long long S = 0, S2 = 0;
+    for (int w = 0; w < 16; ++w) { S += red_s[w]; S2 += red_s2[w]; }
+    // exact integers, then one correctly rounded IEEE division
+    *kappa = (S == 0) ? 1.0 : (double)((long long)E * S2) / (double)(S * S);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_route_slot(const int32_t* __restrict__ ids, int N, int E,
+                                                    const int32_t* __restrict__ chunk_base,
+                                                    int32_t* __restrict__ row_to_slot,
+                                                    int32_t* __restrict__ slot_to_row) {
+  __shared__ int wcnt[4][kMaxExperts];
+  for (int i = threadIdx.x; i < 4 * E; i += blockDim.x) wcnt[i / E][i % E] = 0;
+  __syncthreads();
+  const int i = blockIdx.x * kChunk + threadIdx.x;
+  const int wv = threadIdx.x >> 6;
+  const int v = (i < N) ? ids[i] : -1;
+  const bool act = (v >= 0) && (v < E);
+  const uint64_t m = wave_match((uint32_t)(act ? v : 0), 10, act);
+  const uint64_t below = m & lanemask_lt();
+  const int rank = __popcll(below);
+  if (act && below == 0) wcnt[wv][v] = __popcll(m);
+  __syncthreads();
+  if (i < N) {
+    int slot = -1;
+    if (act) {
+      slot = chunk_base[(size_t)blockIdx.x * E + v] + rank;
+      for (int w = 0; w < wv; ++w) slot += wcnt[w][v];
+      slot_to_row[slot] = i;
+    }
+    row_to_slot[i] = slot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Planner
+// ---------------------------------------------------------------------------
+MOE_DEV long long wave_max64(long long v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    long long o = __shfl_xor(v, off, 64);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+MOE_DEV int wave_max32(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    int o = __shfl_xor(v, off, 64);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(256) void k_plan(const int32_t* __restrict__ bcnt,
+                                              const int32_t* __restrict__ boff,
+                                              const int32_t* __restrict__ owner, int E, int P,
+                                              int s, int mode, int lam, int32_t* q_out,
+                                              int32_t* load_out, int32_t* bw_out,
+                                              int32_t* info_out, int32_t* status) {
+  extern __shared__ int sm[];
+  int* b_s = sm;                     // [E]
+  int* h_s = b_s + E;                // [E]
+  int* boff_s = h_s + E;             // [E+1]
+  int* qh_s = boff_s + E + 1;        // [4][E]   q[e][h(e)] per search
+  int* qn_s = qh_s + 4 * E;          // [4][E][8] q[e][t], t != h(e)
+  __shared__ int res_obj[4], res_rep[4], res_ell[4][kMaxP], best_w;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int e = tid; e < E; e += 256) {
+    b_s[e] = bcnt[e];
+    int h = owner[e];
+    if (h < 0 || h >= P) { atomicOr(status, MOE_DEV_BAD_OWNER); h = 0; }
+    h_s[e] = h;
+  }
+  for (int e = tid; e <= E; e += 256) boff_s[e] = boff[e];
+  for (int i = tid; i < 4 * E * 8; i += 256) qn_s[i] = 0;
+  __syncthreads();
+
+  const bool bwd = (mode == MOE_PLAN_BWD);
+  const bool homeload_key = (w >= 2);
+  const bool fan_one = (w % 2) == 0;
+  int* qh = qh_s + w * E;
+  int* qn = qn_s + w * E * 8;
+
+  long long Bp = 0;
+  for (int e = lane; e < E; e += 64) Bp += b_s[e];
+  const long long B = wave_sum64(Bp);
+  const int tau = (int)((B + P - 1) / P);
+
+  // worker state lives on lane r < P
+  int ell = 0, rep = 0, nrem = 0;
+  for (int e = lane; e < E; e += 64) qh[e] = b_s[e];
+  for (int r = 0; r < P; ++r) {
+    int part = 0;
+    for (int e = lane; e < E; e += 64)
+      if (h_s[e] == r) part += b_s[e];
+    const int tot = wave_sum(part);
+    if (lane == r) ell = tot;
+  }
+
+  for (int round = 0; round < P; ++round) {
+    bool moved = false;
+    const int myL0 = ell + (bwd ? lam * nrem : 0);
+    int key = myL0 - tau;
+    if (homeload_key) {
+      key = 0;
+      for (int r = 0; r < P; ++r) {
+        int m = 0;
+        for (int e = lane; e < E; e += 64)
+          if (h_s[e] == r && qh[e] > m) m = qh[e];
+        m = wave_max32(m);
+        if (lane == r) key = m;
+      }
+    }
+    const bool isdon = (lane < P) && (myL0 > tau);
+    int rank = 0;
+    for (int r2 = 0; r2 < P; ++r2) {
+      const int k2 = __shfl(key, r2, 64);
+      const int d2 = __shfl((int)isdon, r2, 64);
+      if (d2 && (k2 > key || (k2 == key && r2 < lane))) ++rank;
+    }
+    const int ndon = __popcll(__ballot(isdon));
+    for (int j = 0; j < ndon; ++j) {
+      const int r = __ffsll((unsigned long long)__ballot(isdon && rank == j)) - 1;
+      uint32_t done = 0;
+      // Each pass marks one expert done, so E passes suffice; the cap only
+      // guards against a logic error ever spinning forever on the device.
+      for (int guard_e = 0; guard_e <= E; ++guard_e) {
+        const int Lr0 = __shfl(ell, r, 64) + (bwd ? lam * __shfl(nrem, r, 64) : 0);
+        if (Lr0 <= tau) break;
+        long long bk = 0;
+        for (int i = 0, e = lane; e < E; ++i, e += 64)
+          if (h_s[e] == r && !((done >> i) & 1u) && qh[e] > 0) {
+            const long long kk = ((long long)qh[e] << 32) | (long long)(0xFFFFFFFFu - (uint32_t)e);
+            if (kk > bk) bk = kk;
+          }
+        bk = wave_max64(bk);
+        if (bk == 0) break;
+        const int e = (int)(0xFFFFFFFFu - (uint32_t)(bk & 0xFFFFFFFFll));
+        int qer = (int)(bk >> 32);
+        if (lane == (e & 63)) done |= 1u << (e >> 6);
+        bool nc = false;
+        // every move strictly lowers the donor's effective load (delta >= 1,
+        // and a backward copy needs delta > lambda), so moves are bounded by it
+        for (int guard_m = 0; guard_m <= Lr0 + 1; ++guard_m) {
+          const int Lr = __shfl(ell, r, 64) + (bwd ? lam * __shfl(nrem, r, 64) : 0);
+          if (Lr <= tau || qer <= 0) break;
+          long long cand = -1;
+          int dl = 0, isnew = 0;
+          if (lane < P && lane != r) {
+            const int Lt = ell + (bwd ? lam * nrem : 0);
+            if (Lt < tau) {
+              const int qet = qn[e * 8 + lane];
+              bool ok = true;
+              int delta = 0;
+              if (qet > 0) {
+                delta = min(min(Lr - tau, tau - Lt), qer);
+              } else if (rep >= s || (fan_one && nc)) {
+                ok = false;
+              } else if (bwd) {
+                delta = min(min(Lr - tau + lam, tau - Lt), qer);
+                ok = delta > lam;
+                isnew = 1;
+              } else {
+                delta = min(min(Lr - tau, tau - Lt), qer);
+                isnew = 1;
+              }
+              if (ok) {
+                cand = ((long long)(tau - Lt) << 8) | (long long)(255 - lane);
+                dl = delta;
+              }
+            }
+          }
+          const long long bc = wave_max64(cand);
+          if (bc < 0) break;
+          const int t = 255 - (int)(bc & 255);
+          const int delta = __shfl(dl, t, 64);
+          const int nw = __shfl(isnew, t, 64);
+          if (lane == r) { ell -= delta; nrem += nw; }
+          if (lane == t) { ell += delta; rep += nw; qn[e * 8 + t] += delta; }
+          qer -= delta;
+          if (nw) nc = true;
+          moved = true;
+        }
+        if (lane == (e & 63)) qh[e] = qer;
+      }
+    }
+    const int maxL = wave_max32(lane < P ? ell + (bwd ? lam * nrem : 0) : INT_MIN);
+    if (!moved || maxL <= tau) break;
+  }
+  const int obj = wave_max32(lane < P ? ell + (bwd ? lam * nrem : 0) : INT_MIN);
+  const int reps = wave_sum(lane < P ? rep : 0);
+  if (lane == 0) { res_obj[w] = obj; res_rep[w] = reps; }
+  if (lane < P) res_ell[w][lane] = ell;
+  __syncthreads();
+  if (tid == 0) {
+    int bw = 0;
+    for (int c = 1; c < 4; ++c)
+      if (res_obj[c] < res_obj[bw] || (res_obj[c] == res_obj[bw] && res_rep[c] < res_rep[bw]))
+        bw = c;
+    best_w = bw;
+    info_out[0] = res_obj[bw];
+    info_out[1] = bw;
+    info_out[2] = res_rep[bw];
+    info_out[3] = tau;
+  }
+  __syncthreads();
+  const int W = best_w;
+  const int* qhb = qh_s + W * E;
+  const int* qnb = qn_s + W * E * 8;
+  if (tid < P) load_out[tid] = res_ell[W][tid];
+  for (int i = tid; i < E * P; i += 256) {
+    const int e = i / P, t = i % P;
+    q_out[i] = (t == h_s[e]) ? qhb[e] : qnb[e * 8 + t];
+  }
+  const int nb = boff_s[E];
+  for (int g = tid; g < nb; g += 256) {
+    int lo = 0, hi = E;  // largest e with boff_s[e] <= g
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (boff_s[mid] <= g) lo = mid; else hi = mid;
+    }
+    const int e = lo, h = h_s[e];
+    int i = g - boff_s[e];
+    int wk = h;
+    if (i >= qhb[e]) {
+      i -= qhb[e];
+      for (int t = 0; t < P; ++t) {
+        if (t == h) continue;
+        const int qt = qnb[e * 8 + t];
+        if (i < qt) { wk = t; break; }
+        i -= qt;
+      }
+    }
+    bw_out[g] = wk;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+size_t route_ws_bytes(int T, int k, int E) {
+  const long long N = (long long)T * k;
+  const long long nch = N > 0 ? (N + kChunk - 1) / kChunk : 1;
+  return align_up((size_t)nch * E * sizeof(int32_t));
+}
+
+int launch_route_stats(const int32_t* ids, int T, int k, int E, int beta, int32_t* counts,
+                       int32_t* offsets, int32_t* block_counts, int32_t* block_offsets,
+                       int32_t* row_to_slot, int32_t* slot_to_row, double* kappa,
+                       int32_t* status, void* ws, hipStream_t st) {
+  const int N = T * k;
+  const int nch = N > 0 ? (N + kChunk - 1) / kChunk : 1;
+  const int cap = N + E * (beta - 1);
+  int32_t* chunk = (int32_t*)ws;
+  hipLaunchKernelGGL(k_route_count, dim3(nch), dim3(kChunk), 0, st, ids, N, E, chunk,
+                     slot_to_row, cap, status);
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, st, chunk, nch, E, beta, counts,
+                     offsets, block_counts, block_offsets, kappa);
+  if (N > 0)
+    hipLaunchKernelGGL(k_route_slot, dim3(nch), dim3(kChunk), 0, st, ids, N, E, chunk,
+                       row_to_slot, slot_to_row);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int launch_plan(const int32_t* bcnt, const int32_t* boff, const int32_t* owner, int E, int P,
+                int s, int mode, int lam, int32_t* q, int32_t* load, int32_t* bw,
+                int32_t* info, int32_t* status, hipStream_t st) {
+  const size_t lds = sizeof(int) * (size_t)(3 * E + 1 + 4 * E + 4 * E * 8);
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(256), lds, st, bcnt, boff, owner, E, P, s, mode,
+                     lam, q, load, bw, info, status);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace moe

@@ -148,7 +148,7 @@ def make_routing(w: Workload, kappa: float, salt: int = 0):
     """Top-k expert ids int32 [T, k] (-1 = no local expert) and gates fp32 [T, k]."""
     rng = np.random.default_rng(seed_for(w, kappa, STREAM_LOGITS, salt))
     T, k, E = w.T, w.k, w.E
-    if w.name == "tiny_f32":
+    if w.name == "tiny_f32" or kappa == 0:
         bias = -1.0 * np.log(np.arange(E) + 1.0)       # Zipf(1.0) per-expert bias
         logits = rng.standard_normal((T, E)) + bias[None, :]
         return _route_from_logits(logits, k)

@@ -1,0 +1,68 @@
+"""Chains the library's calls for one expert layer over preallocated buffers:
+route statistics -> plan -> forward (-> backward plan -> backward).
+
+Buffers come from torch (device memory); every computation is a library call.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+
+
+class LayerRunner:
+    def __init__(self, w1, w2, w1_scale=None, w2_scale=None, *, act_dtype, T, k, beta, P, s,
+                 owner, lam=12, with_backward=False, save_z=None):
+        dev = w1.device
+        self.dev = dev
+        self.layer = B.make_layer(w1, w2, w1_scale, w2_scale, act_dtype)
+        self.keep = (w1, w2, w1_scale, w2_scale)
+        self.E, self.d, self.dff = self.layer.E, self.layer.d, self.layer.d_ff
+        self.T, self.k, self.beta, self.P, self.s, self.lam = T, k, beta, P, s, lam
+        self.act_dtype = act_dtype
+        self.owner = owner.to(device=dev, dtype=torch.int32).contiguous()
+        self.with_backward = with_backward
+        self.ws = B.workspace(self.layer, T, k, beta, P, s, with_backward, dev)
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.rs = B.alloc_route(T, k, self.E, beta, dev)
+        nbc = B.max_blocks(T, k, self.E, beta)
+        self.plan_f = B.alloc_plan(self.E, P, nbc, dev)
+        self.plan_b = B.alloc_plan(self.E, P, nbc, dev) if with_backward else None
+        self.y = torch.empty((T, self.d), dtype=act_dtype, device=dev)
+        need_z = with_backward if save_z is None else save_z
+        ms = max(B.max_slots(T, k, self.E, beta), 1)
+        self.z = torch.empty((ms, 2 * self.dff), dtype=act_dtype, device=dev) if need_z else None
+        if with_backward:
+            self.dx = torch.empty((T, self.d), dtype=act_dtype, device=dev)
+            self.dw1 = torch.empty((self.E, 2 * self.dff, self.d), dtype=torch.float32, device=dev)
+            self.dw2 = torch.empty((self.E, self.d, self.dff), dtype=torch.float32, device=dev)
+
+    def route(self, topk_ids):
+        return B.route_stats(topk_ids, self.E, self.beta, self.rs, self.ws, self.status)
+
+    def make_plan(self, mode=B.PLAN_FWD, s=None, out=None):
+        out = self.plan_f if out is None else out
+        return B.plan(self.rs["block_counts"], self.rs["block_offsets"], self.owner, self.P,
+                      self.s if s is None else s, mode, self.lam, out, self.ws, self.status)
+
+    def forward(self, x, gates, topk_ids, block_worker=None, events=None):
+        bw = self.plan_f["block_worker"] if block_worker is None else block_worker
+        B.forward(self.layer, x, gates, topk_ids, self.beta, self.P, self.rs, bw, self.y, self.z,
+                  self.ws, self.status, events)
+        return self.y
+
+    def backward(self, x, gates, dy, topk_ids, block_worker=None, events=None):
+        bw = self.plan_b["block_worker"] if block_worker is None else block_worker
+        B.backward(self.layer, x, gates, dy, self.z, topk_ids, self.beta, self.P, self.s, self.rs,
+                   self.owner, bw, self.dx, self.dw1, self.dw2, self.ws, self.status, events)
+        return self.dx, self.dw1, self.dw2
+
+    def step(self, x, gates, topk_ids, dy=None, s=None):
+        """One pass of the whole path: route -> plan -> forward [-> plan(bwd) -> backward]."""
+        self.route(topk_ids)
+        self.make_plan(B.PLAN_FWD, s)
+        self.forward(x, gates, topk_ids)
+        if dy is not None:
+            self.make_plan(B.PLAN_BWD, s, self.plan_b)
+            self.backward(x, gates, dy, topk_ids)
+        return self.y

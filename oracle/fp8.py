@@ -26,9 +26,15 @@ def decode_e4m3(codes) -> np.ndarray:
     return np.where((c & 0x7F) == 0x7F, np.nan, out)
 
 
+_TABLE = None
+
+
 def dequant_blocks(codes, scales) -> np.ndarray:
     """codes uint8 [..., N, K], scales fp32 [..., N/128, K/128] -> fp64 [..., N, K]."""
-    v = decode_e4m3(codes)
+    global _TABLE
+    if _TABLE is None:
+        _TABLE = decode_e4m3(np.arange(256, dtype=np.uint8))   # every code, decoded once
+    v = _TABLE[np.asarray(codes, dtype=np.uint8)]
     s = np.asarray(scales, dtype=np.float64)
     s = np.repeat(np.repeat(s, 128, axis=-2), 128, axis=-1)
     return v * s

@@ -1,0 +1,87 @@
+"""The C-ABI library loads and exports every entry point include/moe_ffn.h
+declares; host-side argument validation (which returns before any device
+work, so it runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from moe_expert_ffn_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moe_ffn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = B.load()
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B.EXPORTS)
+
+
+def test_version_and_status_strings():
+    lib = B.load()
+    assert lib.moe_abi_version() == 1
+    assert lib.moe_status_str(0) == b"ok"
+    assert b"workspace" in lib.moe_status_str(-3)
+
+
+def test_size_helpers():
+    assert B.max_slots(8192, 8, 128, 128) == 65536 + 128 * 127
+    assert B.max_blocks(8192, 8, 128, 128) == (65536 + 128 * 127) // 128
+    assert B.max_slots(-1, 8, 128, 128) == 0
+
+
+def _layer(E=8, d=128, dff=64, act=B.MOE_F32, w=B.MOE_F32):
+    return B.Layer(E, d, dff, act, w, 16, 32, None, None)
+
+
+def test_workspace_size_and_rejections():
+    lib = B.load()
+    L = _layer()
+    f = lib.moe_workspace_size(ctypes.byref(L), 256, 2, 16, 4, 1, 0)
+    b = lib.moe_workspace_size(ctypes.byref(L), 256, 2, 16, 4, 1, 1)
+    assert 0 < f <= b
+    assert lib.moe_workspace_size(ctypes.byref(L), 256, 2, 16, 3, 1, 0) == 0    # P not in {1,2,4,8}
+    assert lib.moe_workspace_size(ctypes.byref(L), 256, 2, 0, 4, 1, 0) == 0     # beta < 1
+
+
+def test_host_validation_errors():
+    lib = B.load()
+    P = ctypes.c_void_p(16)
+    # route stats: bad sizes / null pointers / missing workspace
+    assert lib.moe_route_stats(P, 4, 2, 0, 16, *([P] * 8), P, 1 << 20, None) == B.MOE_ERR_ARG
+    assert lib.moe_route_stats(P, 4, 2, 2000, 16, *([P] * 8), P, 1 << 20, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_stats(None, 4, 2, 8, 16, *([P] * 8), P, 1 << 20, None) == B.MOE_ERR_ARG
+    assert lib.moe_route_stats(P, 4, 2, 8, 16, *([P] * 8), None, 0, None) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_route_stats(P, 4, 2, 8, 16, *([P] * 8), ctypes.c_void_p(17), 1 << 20,
+                               None) == B.MOE_ERR_WORKSPACE
+    # planner
+    assert lib.moe_plan(P, P, P, 8, 3, 1, 0, 12, *([P] * 5), P, 0, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_plan(P, P, P, 8, 4, -1, 0, 12, *([P] * 5), P, 0, None) == B.MOE_ERR_ARG
+    assert lib.moe_plan(P, P, P, 8, 4, 1, 2, 12, *([P] * 5), P, 0, None) == B.MOE_ERR_ARG
+    assert lib.moe_plan(P, P, P, 8, 4, 1, 0, -1, *([P] * 5), P, 0, None) == B.MOE_ERR_ARG
+    assert lib.moe_plan(P, P, P, 600, 4, 1, 0, 12, *([P] * 5), P, 0, None) == B.MOE_ERR_UNSUPPORTED
+    # forward / backward layer checks
+    bad_d = _layer(d=96)
+    assert lib.moe_forward(ctypes.byref(bad_d), P, P, P, 4, 2, 16, 4, *([P] * 8), P, 1 << 30,
+                           None, None) == B.MOE_ERR_UNSUPPORTED
+    mixed = _layer(act=B.MOE_F32, w=B.MOE_BF16)
+    assert lib.moe_forward(ctypes.byref(mixed), P, P, P, 4, 2, 16, 4, *([P] * 8), P, 1 << 30,
+                           None, None) == B.MOE_ERR_UNSUPPORTED
+    fp8 = B.Layer(8, 128, 128, B.MOE_BF16, B.MOE_FP8_E4M3, 16, 32, 64, 64)
+    assert lib.moe_backward(ctypes.byref(fp8), P, P, P, P, P, 4, 2, 16, 4, 1, *([P] * 10), P,
+                            1 << 30, None, None) == B.MOE_ERR_UNSUPPORTED
+    ok = _layer()
+    assert lib.moe_forward(ctypes.byref(ok), P, P, P, 4, 2, 16, 4, *([P] * 8), P, 16, None,
+                           None) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_forward(ctypes.byref(ok), P, P, P, 4, 2, 16, 5, *([P] * 8), P, 1 << 30, None,
+                           None) == B.MOE_ERR_UNSUPPORTED
