@@ -44,8 +44,7 @@ Sizes make_sizes(const moe_layer* L, int T, int k, int beta, int P, int s) {
   z.act_bytes = L->act_dtype == MOE_F32 ? 4 : 2;
   z.max_slots = moe_max_slots(T, k, L->E, beta);
   z.max_blocks = moe_max_blocks(T, k, L->E, beta);
-  const size_t per_block = beta > kBM ? (size_t)(beta + kBM - 1) / kBM : 1;
-  z.max_mt = z.max_blocks * per_block;
+  z.max_mt = max_tiles(z);
   return z;
 }
 

@@ -17,14 +17,28 @@ constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies
 constexpr int kMaxP = 8;
 
 // bf16 is carried as raw 16-bit words; conversions are exact (widen) or
-// round-to-nearest-even (narrow, NaN kept quiet).
+// round-to-nearest-even in hardware (narrow).
 MOE_DEV float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
-MOE_DEV uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+MOE_DEV uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }  // v_cvt_pk_bf16_f32
+
+// Explicit address spaces: LDS (3) and global (1).  Without them a pointer
+// that passes through a select or an array decays to a generic pointer and
+// every access becomes a flat load that waits on both memory counters.
+#define MOE_LDS __attribute__((address_space(3)))
+#define MOE_GLB __attribute__((address_space(1)))
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+MOE_DEV uint4 ldg16(const void* p) {
+  const u32x4_t v = *(const MOE_GLB u32x4_t*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
+MOE_DEV void stg16(void* p, uint4 v) { *(MOE_GLB u32x4_t*)p = u32x4_t{v.x, v.y, v.z, v.w}; }
+MOE_DEV uint4 lds_ld16(const MOE_LDS void* p) {
+  const u32x4_t v = *(const MOE_LDS u32x4_t*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+MOE_DEV void lds_st16(MOE_LDS void* p, uint4 v) { *(MOE_LDS u32x4_t*)p = u32x4_t{v.x, v.y, v.z, v.w}; }
+MOE_DEV void lds_st8(MOE_LDS void* p, uint2 v) { *(MOE_LDS u32x2_t*)p = u32x2_t{v.x, v.y}; }
 
 // OCP e4m3fn -> float, from the format's definition: sign, 4-bit exponent with
 // bias 7, 3-bit mantissa, subnormals at exponent 0.  (S.1111.111 = NaN is never

@@ -25,7 +25,7 @@ struct SchedArgs {
   const int32_t* boff;
   const int32_t* bw;
   const int32_t* owner;
-  int E, P, s, beta, backward;
+  int E, P, s, beta, backward, bm;
   int32_t* ctr;
   int32_t* mt_cnt;
   int4* mt;
@@ -46,12 +46,19 @@ MOE_DEV int expert_of(int g, const int* boff_s, int E) {
   return lo;
 }
 
-// One workgroup.  M-tiles: every block of beta slots spawns ceil(valid/128)
-// tiles on its worker, listed per worker in block order (one exclusive scan
-// per worker).  Segments (backward): the blocks of one (expert, worker) pair
-// must form one contiguous run; its slot range and valid-row count become one
-// weight-gradient segment, with a replica slot when the worker is not the
-// owner (rank among that worker's non-home experts, in expert order).
+// One workgroup.  M-tiles: a tile holds up to `bm` consecutive slots of one
+// (expert, worker) run of blocks.  When bm is a multiple of beta, tiles start
+// every bm/beta blocks from the start of each run; otherwise every block is cut
+// into ceil(valid rows / bm) tiles of its own.  Tiles are listed per worker in
+// block order (one exclusive scan per worker).  Segments (backward): the
+// blocks of one (expert, worker) pair must form one contiguous run; its slot
+// range and valid-row count become one weight-gradient segment, with a replica
+// slot when the worker is not the owner (rank among that worker's non-home
+// experts, in expert order).
+MOE_DEV int block_rows(int g, int e, int beta, const int* boff_s, const int* cnt_s) {
+  return min(beta, beta * boff_s[e] + cnt_s[e] - beta * g);
+}
+
 __global__ __launch_bounds__(256) void k_sched(SchedArgs a) {
   extern __shared__ int sm[];
   const int E = a.E, P = a.P;
@@ -72,22 +79,46 @@ __global__ __launch_bounds__(256) void k_sched(SchedArgs a) {
     const int w = a.bw[g];
     if (w < 0 || w >= P) atomicOr(a.status, MOE_DEV_BAD_PLAN);
   }
+  const bool grouped = (a.bm % a.beta) == 0;
+  const int f = grouped ? a.bm / a.beta : 1;
+  const uint64_t le_mask = (lane == 63) ? ~0ull : ((1ull << (lane + 1)) - 1);
   for (int r = wv; r < P; r += 4) {
-    int run = 0;
+    int run = 0, carry = 0;
     for (int base = 0; base < nb; base += 64) {
       const int g = base + lane;
-      int nt = 0, e = 0, bstart = 0, vrows = 0;
-      if (g < nb && a.bw[g] == r) {
+      const bool mine = g < nb && a.bw[g] == r;
+      int e = 0, bstart = 0, vrows = 0;
+      bool start = false;
+      if (mine) {
         e = expert_of(g, boff_s, E);
         bstart = a.beta * g;
-        vrows = min(a.beta, a.beta * boff_s[e] + cnt_s[e] - bstart);
-        nt = (vrows + kBM - 1) / kBM;
+        vrows = block_rows(g, e, a.beta, boff_s, cnt_s);
+        start = (g == boff_s[e]) || a.bw[g - 1] != r;
+      }
+      const uint64_t sm_ = __ballot(start) & le_mask;
+      const int rs = sm_ ? base + 63 - __clzll(sm_) : carry;
+      carry = __shfl(rs, 63, 64);
+      int nt = 0, trows = 0;
+      if (mine) {
+        if (grouped) {
+          if ((g - rs) % f == 0) {
+            nt = 1;
+            for (int i = 0; i < f; ++i) {
+              const int gi = g + i;
+              if (gi >= boff_s[e + 1] || (i > 0 && a.bw[gi] != r)) break;
+              trows += block_rows(gi, e, a.beta, boff_s, cnt_s);
+            }
+          }
+        } else {
+          nt = (vrows + a.bm - 1) / a.bm;
+        }
       }
       const int inc = wave_incl_scan(nt);
       const int pos = run + inc - nt;
-      for (int i = 0; i < nt; ++i)
-        a.mt[(size_t)r * a.max_mt + pos + i] =
-            make_int4(e, bstart + i * kBM, min(kBM, vrows - i * kBM), 0);
+      for (int i = 0; i < nt; ++i) {
+        const int rows = grouped ? trows : min(a.bm, vrows - i * a.bm);
+        a.mt[(size_t)r * a.max_mt + pos + i] = make_int4(e, bstart + i * a.bm, rows, 0);
+      }
       run += __shfl(inc, 63, 64);
     }
     if (lane == 0) a.mt_cnt[r] = run;
@@ -181,20 +212,36 @@ struct ExecArgs {
 
 enum { PH_FC1 = 0, PH_FC2 = 1, PH_DA = 2, PH_DX = 3, PH_DW = 4 };
 
+// bf16 operands on the big tile go through the direct-to-LDS pipeline.
+template <typename T, bool FP8, class C>
+constexpr bool kUseDma = sizeof(T) == 2 && !FP8 && C::BM == 256 && C::BN == 256;
+
+// Dynamic LDS of a GEMM kernel: operand staging or the largest epilogue tile
+// (FC1 with [G, U] saved: two bf16 tiles of BM x (BN/2 + 8)).
+template <typename T, class C> constexpr size_t gemm_lds_bytes() {
+  const size_t reg = TileLds<T, C>::BYTES;
+  const size_t dma = DmaCfg<C>::BYTES;
+  const size_t epi = (size_t)2 * C::BM * (C::BN / 2 + 16 / sizeof(T)) * sizeof(T);
+  size_t m = reg > dma ? reg : dma;
+  return m > epi ? m : epi;
+}
+
 // ---- forward: FC1 + SwiGLU ------------------------------------------------
-// N-tile nj covers A columns [64 nj, 64 nj + 64); its 128 weight rows
-// interleave 32 G rows and the matching 32 U rows, so each wave holds G and U
-// of the same (row, column) in two accumulators and applies SwiGLU in
+// N-tile nj covers A columns [nj*BN/2, (nj+1)*BN/2); its BN weight rows
+// alternate 32 G rows and the matching 32 U rows, so a wave holds G and U of
+// the same (row, column) in neighbouring accumulators and applies SwiGLU in
 // registers.
-template <typename T, bool FP8>
-__global__ __launch_bounds__(256) void k_fc1(ExecArgs a) {
+template <typename T, bool FP8, class C>
+__global__ __launch_bounds__(C::NT) void k_fc1(ExecArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int tslot;
-  T* smem = (T*)smem_raw;
+  MOE_LDS T* smem = (MOE_LDS T*)smem_raw;
+  constexpr int HALF = C::BN / 2;
   const int r = worker_of_block(a.P);
-  const int nnt = a.dff / 64;
+  const int nnt = a.dff / HALF;
   const int total = a.mt_cnt[r] * nnt;
   const int lane = threadIdx.x & 63;
+  const int wn = wave_id() % C::WAVES_N;
   const T* X = (const T*)a.x;
   T* Ab = (T*)a.bufA;
   T* Z = (T*)a.z_save;
@@ -204,59 +251,84 @@ __global__ __launch_bounds__(256) void k_fc1(ExecArgs a) {
     const int4 m = a.mt[(size_t)r * a.max_mt + tile / nnt];
     const int nj = tile % nnt;
     const int e = m.x, slot0 = m.y, nrows = m.z;
-    RowLoad<T, kBM> la;
-    la.init([&](int row) -> const T* {
-      if (row >= nrows) return nullptr;
-      return X + (size_t)(a.slot_to_row[slot0 + row] / a.k) * a.d;
-    });
+    RowLoad<T, C::BM, C::NT> la;
+    if constexpr (!kUseDma<T, FP8, C>)
+      la.init(X, [&](int row) { return row < nrows ? (a.slot_to_row[slot0 + row] / a.k) * a.d : -1; });
     auto w1row = [&](int rho) {
       const int q = rho >> 5;
-      return (q & 1) * a.dff + nj * 64 + (q >> 1) * 32 + (rho & 31);
+      return (q & 1) * a.dff + nj * HALF + (q >> 1) * 32 + (rho & 31);
     };
-    f32x16_t acc[2][2];
+    f32x16_t acc[C::MB][C::NB];
     const int nk = a.d / Elem<T>::BK;
-    if constexpr (FP8) {
-      RowLoadFp8<kBN> lb;
+    if constexpr (kUseDma<T, FP8, C>) {
+      RowDma<C::BM, C::NT / 64> da;
+      da.init(X, [&](int row) { return row < nrows ? (a.slot_to_row[slot0 + row] / a.k) * a.d : -1; });
+      RowDma<C::BN, C::NT / 64> db;
+      db.init((const uint16_t*)a.w1 + (size_t)e * 2 * a.dff * a.d, [&](int rho) { return w1row(rho) * a.d; });
+      gemm_tile_dma<C>(da, db, a.d / kDmaBK, smem, acc);
+    } else if constexpr (FP8) {
+      RowLoadFp8<C::BN, C::NT> lb;
       const uint8_t* W = (const uint8_t*)a.w1 + (size_t)e * 2 * a.dff * a.d;
       const float* S = a.w1s + (size_t)e * (2 * a.dff / 128) * (a.d / 128);
       lb.init([&](int rho) { return W + (size_t)w1row(rho) * a.d; },
               [&](int rho) { return S + (size_t)(w1row(rho) >> 7) * (a.d >> 7); });
-      gemm_tile<T>(PlainLd<RowLoad<T, kBM>>{la}, PlainLd<RowLoadFp8<kBN>>{lb}, nk, smem, acc);
+      gemm_tile<T, C>(PlainLd<decltype(la)>{la}, PlainLd<decltype(lb)>{lb}, nk, smem, acc);
     } else {
-      RowLoad<T, kBN> lb;
-      const T* W = (const T*)a.w1 + (size_t)e * 2 * a.dff * a.d;
-      lb.init([&](int rho) -> const T* { return W + (size_t)w1row(rho) * a.d; });
-      gemm_tile<T>(PlainLd<RowLoad<T, kBM>>{la}, PlainLd<RowLoad<T, kBN>>{lb}, nk, smem, acc);
+      RowLoad<T, C::BN, C::NT> lb;
+      lb.init((const T*)a.w1 + (size_t)e * 2 * a.dff * a.d, [&](int rho) { return w1row(rho) * a.d; });
+      gemm_tile<T, C>(PlainLd<decltype(la)>{la}, PlainLd<decltype(lb)>{lb}, nk, smem, acc);
     }
-    const int c = nj * 64 + ((threadIdx.x >> 6) & 1) * 32 + (lane & 31);
+    // SwiGLU in registers, then A (and [G, U] when saved) through LDS
+    constexpr int LDA = HALF + 16 / (int)sizeof(T);
+    const size_t abase = (size_t)slot0 * a.dff + nj * HALF;
+    auto pairs = [&](auto&& put) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int p = 0; p < C::NB / 2; ++p) {
+        const int lc = (wn * C::NB / 2 + p) * 32 + (lane & 31);
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int row = acc_row(i, rr, lane);
-        if (row < nrows) {
-          const float g = acc[i][0][rr], u = acc[i][1][rr];
-          const float av = g / (1.f + expf(-g)) * u;
-          const size_t slot = (size_t)slot0 + row;
-          Ab[slot * a.dff + c] = to_act<T>(av);
-          if (Z) {
-            Z[slot * 2 * a.dff + c] = to_act<T>(g);
-            Z[slot * 2 * a.dff + a.dff + c] = to_act<T>(u);
-          }
-        }
+        for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr)
+            put(acc_row<C>(i, rr, lane), lc, acc[i][2 * p][rr], acc[i][2 * p + 1][rr]);
       }
+    };
+    MOE_LDS T* sa = smem;
+    pairs([&](int row, int lc, float g, float u) {
+      sa[row * LDA + lc] = to_act<T>(g / (1.f + expf(-g)) * u);
+    });
+    __syncthreads();
+    lds_to_global<T, C::NT>(sa, C::BM, HALF, LDA, [&](int row, int col, const V16& v) {
+      if (row < nrows) stg16(Ab + abase + (size_t)row * a.dff + col, v.u);
+    });
+    if (Z) {
+      __syncthreads();
+      MOE_LDS T* sg = smem;
+      MOE_LDS T* su = smem + C::BM * LDA;
+      pairs([&](int row, int lc, float g, float u) {
+        sg[row * LDA + lc] = to_act<T>(g);
+        su[row * LDA + lc] = to_act<T>(u);
+      });
+      __syncthreads();
+      const size_t zbase = (size_t)slot0 * 2 * a.dff + nj * HALF;
+      lds_to_global<T, C::NT>(sg, C::BM, HALF, LDA, [&](int row, int col, const V16& v) {
+        if (row < nrows) stg16(Z + zbase + (size_t)row * 2 * a.dff + col, v.u);
+      });
+      lds_to_global<T, C::NT>(su, C::BM, HALF, LDA, [&](int row, int col, const V16& v) {
+        if (row < nrows) stg16(Z + zbase + (size_t)row * 2 * a.dff + a.dff + col, v.u);
+      });
+    }
   }
 }
 
 // ---- forward: FC2 + gate ----------------------------------------------------
-template <typename T, bool FP8>
-__global__ __launch_bounds__(256) void k_fc2(ExecArgs a) {
+template <typename T, bool FP8, class C>
+__global__ __launch_bounds__(C::NT) void k_fc2(ExecArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int tslot;
-  __shared__ float pg[kBM];
-  T* smem = (T*)smem_raw;
+  __shared__ float pg[C::BM];
+  MOE_LDS T* smem = (MOE_LDS T*)smem_raw;
   const int r = worker_of_block(a.P);
-  const int nnt = a.d / kBN;
+  const int nnt = a.d / C::BN;
   const int total = a.mt_cnt[r] * nnt;
   const int lane = threadIdx.x & 63;
   const T* Ab = (const T*)a.bufA;
@@ -267,39 +339,41 @@ __global__ __launch_bounds__(256) void k_fc2(ExecArgs a) {
     const int4 m = a.mt[(size_t)r * a.max_mt + tile / nnt];
     const int nj = tile % nnt;
     const int e = m.x, slot0 = m.y, nrows = m.z;
-    if (threadIdx.x < kBM)
-      pg[threadIdx.x] = threadIdx.x < nrows ? a.gates[a.slot_to_row[slot0 + threadIdx.x]] : 0.f;
-    RowLoad<T, kBM> la;
-    la.init([&](int row) -> const T* {
-      return row < nrows ? Ab + ((size_t)slot0 + row) * a.dff : nullptr;
-    });
-    f32x16_t acc[2][2];
+    for (int i = threadIdx.x; i < C::BM; i += C::NT)
+      pg[i] = i < nrows ? a.gates[a.slot_to_row[slot0 + i]] : 0.f;
+    RowLoad<T, C::BM, C::NT> la;
+    if constexpr (!kUseDma<T, FP8, C>)
+      la.init(Ab + (size_t)slot0 * a.dff, [&](int row) { return row < nrows ? row * a.dff : -1; });
+    f32x16_t acc[C::MB][C::NB];
     const int nk = a.dff / Elem<T>::BK;
-    if constexpr (FP8) {
-      RowLoadFp8<kBN> lb;
+    if constexpr (kUseDma<T, FP8, C>) {
+      RowDma<C::BM, C::NT / 64> da;
+      da.init((const uint16_t*)Ab + (size_t)slot0 * a.dff, [&](int row) { return row < nrows ? row * a.dff : -1; });
+      RowDma<C::BN, C::NT / 64> db;
+      db.init((const uint16_t*)a.w2 + (size_t)e * a.d * a.dff + (size_t)nj * C::BN * a.dff,
+              [&](int rho) { return rho * a.dff; });
+      gemm_tile_dma<C>(da, db, a.dff / kDmaBK, smem, acc);
+    } else if constexpr (FP8) {
+      RowLoadFp8<C::BN, C::NT> lb;
       const uint8_t* W = (const uint8_t*)a.w2 + (size_t)e * a.d * a.dff;
       const float* S = a.w2s + (size_t)e * (a.d / 128) * (a.dff / 128);
-      lb.init([&](int rho) { return W + (size_t)(nj * kBN + rho) * a.dff; },
-              [&](int rho) { return S + (size_t)((nj * kBN + rho) >> 7) * (a.dff >> 7); });
-      gemm_tile<T>(PlainLd<RowLoad<T, kBM>>{la}, PlainLd<RowLoadFp8<kBN>>{lb}, nk, smem, acc);
+      lb.init([&](int rho) { return W + (size_t)(nj * C::BN + rho) * a.dff; },
+              [&](int rho) { return S + (size_t)((nj * C::BN + rho) >> 7) * (a.dff >> 7); });
+      gemm_tile<T, C>(PlainLd<decltype(la)>{la}, PlainLd<decltype(lb)>{lb}, nk, smem, acc);
     } else {
-      RowLoad<T, kBN> lb;
-      const T* W = (const T*)a.w2 + (size_t)e * a.d * a.dff;
-      lb.init([&](int rho) -> const T* { return W + (size_t)(nj * kBN + rho) * a.dff; });
-      gemm_tile<T>(PlainLd<RowLoad<T, kBM>>{la}, PlainLd<RowLoad<T, kBN>>{lb}, nk, smem, acc);
+      RowLoad<T, C::BN, C::NT> lb;
+      lb.init((const T*)a.w2 + (size_t)e * a.d * a.dff + (size_t)nj * C::BN * a.dff,
+              [&](int rho) { return rho * a.dff; });
+      gemm_tile<T, C>(PlainLd<decltype(la)>{la}, PlainLd<decltype(lb)>{lb}, nk, smem, acc);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int row = acc_row(i, rr, lane);
-        if (row < nrows) {
-          const float p = pg[row];
-          const size_t base = ((size_t)slot0 + row) * a.d + nj * kBN;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) O[base + acc_col(j, lane)] = to_act<T>(p * acc[i][j][rr]);
-        }
-      }
+    constexpr int LDO = C::BN + 16 / (int)sizeof(T);
+    acc_to_lds<C>(acc, smem, LDO, 0, C::BM,
+                  [&](float v, int row, int) { return to_act<T>(pg[row] * v); });
+    __syncthreads();
+    const size_t obase = (size_t)slot0 * a.d + nj * C::BN;
+    lds_to_global<T, C::NT>(smem, C::BM, C::BN, LDO, [&](int row, int col, const V16& v) {
+      if (row < nrows) stg16(O + obase + (size_t)row * a.d + col, v.u);
+    });
   }
 }
 
@@ -320,7 +394,7 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ src,
     const int s = row_to_slot[(size_t)t * k + j];
     if (s < 0) continue;
     V16 in;
-    in.u = *(const uint4*)(src + (size_t)s * d + c);
+    in.u = ldg16(src + (size_t)s * d + c);
 #pragma unroll
     for (int v = 0; v < VE; ++v) {
       if constexpr (sizeof(T) == 2) acc[v] += bf2f(in.h[v]);
@@ -333,7 +407,7 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ src,
     if constexpr (sizeof(T) == 2) o.h[v] = f2bf(acc[v]);
     else o.f[v] = acc[v];
   }
-  *(uint4*)(out + (size_t)t * d + c) = o.u;
+  stg16(out + (size_t)t * d + c, o.u);
 }
 
 // ---- backward: dA -> dZ -------------------------------------------------------
@@ -344,18 +418,35 @@ template <typename T> struct SrcRowsMN {       // element (k, n) = base[k * ld +
   int ld, n0, nlim;
   MOE_DEV uint4 operator()(int kk, int mn) const {
     const int n = n0 + mn;
-    return n < nlim ? *(const uint4*)(base + (size_t)kk * ld + n) : zero4();
+    return n < nlim ? ldg16(base + (size_t)kk * ld + n) : zero4();
   }
 };
 
-template <typename T>
-__global__ __launch_bounds__(256) void k_bwd_da(ExecArgs a) {
+MOE_DEV void load4(const uint16_t* p, float* v) {
+  const uint2 q = *(const uint2*)p;
+  v[0] = bf2f((uint16_t)(q.x & 0xffff)); v[1] = bf2f((uint16_t)(q.x >> 16));
+  v[2] = bf2f((uint16_t)(q.y & 0xffff)); v[3] = bf2f((uint16_t)(q.y >> 16));
+}
+MOE_DEV void load4(const float* p, float* v) {
+  const float4 q = *(const float4*)p;
+  v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+}
+MOE_DEV void store4(uint16_t* p, const float* v) {
+  uint2 q;
+  q.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  q.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  *(uint2*)p = q;
+}
+MOE_DEV void store4(float* p, const float* v) { *(float4*)p = make_float4(v[0], v[1], v[2], v[3]); }
+
+template <typename T, class C>
+__global__ __launch_bounds__(C::NT) void k_bwd_da(ExecArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int tslot;
-  __shared__ float pg[kBM];
-  T* smem = (T*)smem_raw;
+  __shared__ float pg[C::BM];
+  MOE_LDS T* smem = (MOE_LDS T*)smem_raw;
   const int r = worker_of_block(a.P);
-  const int nnt = (a.dff + kBN - 1) / kBN;
+  const int nnt = (a.dff + C::BN - 1) / C::BN;
   const int total = a.mt_cnt[r] * nnt;
   const int lane = threadIdx.x & 63;
   const T* DY = (const T*)a.dy;
@@ -367,49 +458,52 @@ __global__ __launch_bounds__(256) void k_bwd_da(ExecArgs a) {
     const int4 m = a.mt[(size_t)r * a.max_mt + tile / nnt];
     const int nj = tile % nnt;
     const int e = m.x, slot0 = m.y, nrows = m.z;
-    if (threadIdx.x < kBM)
-      pg[threadIdx.x] = threadIdx.x < nrows ? a.gates[a.slot_to_row[slot0 + threadIdx.x]] : 0.f;
-    RowLoad<T, kBM> la;
-    la.init([&](int row) -> const T* {
-      if (row >= nrows) return nullptr;
-      return DY + (size_t)(a.slot_to_row[slot0 + row] / a.k) * a.d;
-    });
-    TransLoad<T, kBN> lb;
+    for (int i = threadIdx.x; i < C::BM; i += C::NT)
+      pg[i] = i < nrows ? a.gates[a.slot_to_row[slot0 + i]] : 0.f;
+    RowLoad<T, C::BM, C::NT> la;
+    la.init(DY, [&](int row) { return row < nrows ? (a.slot_to_row[slot0 + row] / a.k) * a.d : -1; });
+    TransLoad<T, C::BN, C::NT> lb;
     lb.init();
-    SrcRowsMN<T> src{(const T*)a.w2 + (size_t)e * a.d * a.dff, a.dff, nj * kBN, a.dff};
-    f32x16_t acc[2][2];
-    gemm_tile<T>(PlainLd<RowLoad<T, kBM>>{la}, TransLd<TransLoad<T, kBN>, SrcRowsMN<T>>{lb, src},
-                 a.d / Elem<T>::BK, smem, acc);
+    SrcRowsMN<T> src{(const T*)a.w2 + (size_t)e * a.d * a.dff, a.dff, nj * C::BN, a.dff};
+    f32x16_t acc[C::MB][C::NB];
+    gemm_tile<T, C>(PlainLd<decltype(la)>{la}, TransLd<decltype(lb), SrcRowsMN<T>>{lb, src},
+                    a.d / Elem<T>::BK, smem, acc);
+    // p * dA in fp32 through LDS, 128 rows at a time; the SwiGLU gradient is
+    // applied on the way out with 4-wide coalesced reads of the saved [G, U]
+    constexpr int PASS = 128, LDD = C::BN + 4;
+    MOE_LDS float* sd = (MOE_LDS float*)smem;
+    for (int p0 = 0; p0 < C::BM; p0 += PASS) {
+      if (p0) __syncthreads();
+      acc_to_lds<C>(acc, sd, LDD, p0, PASS, [&](float v, int row, int) { return pg[row] * v; });
+      __syncthreads();
+      lds_to_global<float, C::NT>(sd, PASS, C::BN, LDD, [&](int rl, int col, const V16& v) {
+        const int row = p0 + rl, n = nj * C::BN + col;
+        if (row >= nrows || n >= a.dff) return;
+        const size_t zb = ((size_t)slot0 + row) * 2 * a.dff + n;
+        float g[4], u[4], dg[4], du[4];
+        load4(Z + zb, g);
+        load4(Z + zb + a.dff, u);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int row = acc_row(i, rr, lane);
-        if (row >= nrows) continue;
-        const float p = pg[row];
-        const size_t zb = ((size_t)slot0 + row) * 2 * a.dff;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = nj * kBN + acc_col(j, lane);
-          if (n >= a.dff) continue;
-          const float dA = p * acc[i][j][rr];
-          const float g = from_act(Z[zb + n]), u = from_act(Z[zb + a.dff + n]);
-          const float sg = 1.f / (1.f + expf(-g));
-          dZ[zb + n] = to_act<T>(dA * u * sg * (1.f + g * (1.f - sg)));
-          dZ[zb + a.dff + n] = to_act<T>(dA * g * sg);
+        for (int q = 0; q < 4; ++q) {
+          const float sg = 1.f / (1.f + expf(-g[q]));
+          dg[q] = v.f[q] * u[q] * sg * (1.f + g[q] * (1.f - sg));
+          du[q] = v.f[q] * g[q] * sg;
         }
-      }
+        store4(dZ + zb, dg);
+        store4(dZ + zb + a.dff, du);
+      });
+    }
   }
 }
 
 // ---- backward: dX per routed row ----------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void k_bwd_dx(ExecArgs a) {
+template <typename T, class C>
+__global__ __launch_bounds__(C::NT) void k_bwd_dx(ExecArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int tslot;
-  T* smem = (T*)smem_raw;
+  MOE_LDS T* smem = (MOE_LDS T*)smem_raw;
   const int r = worker_of_block(a.P);
-  const int nnt = a.d / kBN;
+  const int nnt = a.d / C::BN;
   const int total = a.mt_cnt[r] * nnt;
   const int lane = threadIdx.x & 63;
   const T* dZ = (const T*)a.bufA;
@@ -420,26 +514,21 @@ __global__ __launch_bounds__(256) void k_bwd_dx(ExecArgs a) {
     const int4 m = a.mt[(size_t)r * a.max_mt + tile / nnt];
     const int nj = tile % nnt;
     const int e = m.x, slot0 = m.y, nrows = m.z;
-    RowLoad<T, kBM> la;
-    la.init([&](int row) -> const T* {
-      return row < nrows ? dZ + ((size_t)slot0 + row) * 2 * a.dff : nullptr;
-    });
-    TransLoad<T, kBN> lb;
+    RowLoad<T, C::BM, C::NT> la;
+    la.init(dZ + (size_t)slot0 * 2 * a.dff, [&](int row) { return row < nrows ? row * 2 * a.dff : -1; });
+    TransLoad<T, C::BN, C::NT> lb;
     lb.init();
-    SrcRowsMN<T> src{(const T*)a.w1 + (size_t)e * 2 * a.dff * a.d, a.d, nj * kBN, a.d};
-    f32x16_t acc[2][2];
-    gemm_tile<T>(PlainLd<RowLoad<T, kBM>>{la}, TransLd<TransLoad<T, kBN>, SrcRowsMN<T>>{lb, src},
-                 2 * a.dff / Elem<T>::BK, smem, acc);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int row = acc_row(i, rr, lane);
-        if (row >= nrows) continue;
-        const size_t base = ((size_t)slot0 + row) * a.d + nj * kBN;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) dXp[base + acc_col(j, lane)] = to_act<T>(acc[i][j][rr]);
-      }
+    SrcRowsMN<T> src{(const T*)a.w1 + (size_t)e * 2 * a.dff * a.d, a.d, nj * C::BN, a.d};
+    f32x16_t acc[C::MB][C::NB];
+    gemm_tile<T, C>(PlainLd<decltype(la)>{la}, TransLd<decltype(lb), SrcRowsMN<T>>{lb, src},
+                    2 * a.dff / Elem<T>::BK, smem, acc);
+    constexpr int LDO = C::BN + 16 / (int)sizeof(T);
+    acc_to_lds<C>(acc, smem, LDO, 0, C::BM, [&](float v, int, int) { return to_act<T>(v); });
+    __syncthreads();
+    const size_t obase = (size_t)slot0 * a.d + nj * C::BN;
+    lds_to_global<T, C::NT>(smem, C::BM, C::BN, LDO, [&](int row, int col, const V16& v) {
+      if (row < nrows) stg16(dXp + obase + (size_t)row * a.d + col, v.u);
+    });
   }
 }
 
@@ -455,7 +544,7 @@ template <typename T> struct SrcGatherRow {    // element (k, m) = base[t(slot0 
     const int m = m0 + mn;
     if (kk >= nrows || m >= mlim) return zero4();
     const int t = slot_to_row[slot0 + kk] / topk;
-    return *(const uint4*)(base + (size_t)t * ld + m);
+    return ldg16(base + (size_t)t * ld + m);
   }
 };
 template <typename T> struct SrcSlotRow {      // element (k, m) = base[(slot0 + k) * ld + m0 + m]
@@ -464,7 +553,7 @@ template <typename T> struct SrcSlotRow {      // element (k, m) = base[(slot0 +
   MOE_DEV uint4 operator()(int kk, int mn) const {
     const int m = m0 + mn;
     if (kk >= nrows || m >= mlim) return zero4();
-    return *(const uint4*)(base + ((size_t)slot0 + kk) * ld + m);
+    return ldg16(base + ((size_t)slot0 + kk) * ld + m);
   }
 };
 template <typename T> struct SrcGatedAct {     // element (k, n) = p * SiLU(G) * U at slot0 + k
@@ -479,8 +568,8 @@ template <typename T> struct SrcGatedAct {     // element (k, n) = p * SiLU(G) *
     const size_t zb = ((size_t)slot0 + kk) * 2 * dff;
     const float p = gates[slot_to_row[slot0 + kk]];
     V16 g, u, o;
-    g.u = *(const uint4*)(z + zb + n);
-    u.u = *(const uint4*)(z + zb + dff + n);
+    g.u = ldg16(z + zb + n);
+    u.u = ldg16(z + zb + dff + n);
 #pragma unroll
     for (int v = 0; v < VE; ++v) {
       float gv, uv;
@@ -494,14 +583,14 @@ template <typename T> struct SrcGatedAct {     // element (k, n) = p * SiLU(G) *
   }
 };
 
-template <typename T>
-__global__ __launch_bounds__(256) void k_bwd_dw(ExecArgs a) {
+template <typename T, class C>
+__global__ __launch_bounds__(C::NT) void k_bwd_dw(ExecArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int tslot;
-  T* smem = (T*)smem_raw;
+  MOE_LDS T* smem = (MOE_LDS T*)smem_raw;
   const int r = worker_of_block(a.P);
-  const int n2m = a.d / kBM, n2n = (a.dff + kBN - 1) / kBN;   // dW2 [d][dff]
-  const int n1m = 2 * a.dff / kBM, n1n = a.d / kBN;          // dW1 [2dff][d]
+  const int n2m = a.d / C::BM, n2n = (a.dff + C::BN - 1) / C::BN;   // dW2 [d][dff]
+  const int n1m = 2 * a.dff / C::BM, n1n = a.d / C::BN;            // dW1 [2dff][d]
   const int per_seg = n2m * n2n + n1m * n1n;
   const int total = a.seg_cnt[r] * per_seg;
   const int lane = threadIdx.x & 63;
@@ -514,9 +603,9 @@ __global__ __launch_bounds__(256) void k_bwd_dw(ExecArgs a) {
     if (e < 0) continue;
     int loc = tile % per_seg;
     const int nk = (nrows + Elem<T>::BK - 1) / Elem<T>::BK;
-    f32x16_t acc[2][2];
-    TransLoad<T, kBM> la;
-    TransLoad<T, kBN> lb;
+    f32x16_t acc[C::MB][C::NB];
+    TransLoad<T, C::BM, C::NT> la;
+    TransLoad<T, C::BN, C::NT> lb;
     la.init();
     lb.init();
     float* out;
@@ -524,10 +613,11 @@ __global__ __launch_bounds__(256) void k_bwd_dw(ExecArgs a) {
     if (loc < n2m * n2n) {
       mi = loc / n2n;
       nj = loc % n2n;
-      SrcGatherRow<T> sa{(const T*)a.dy, a.slot_to_row, slot0, nrows, a.k, a.d, mi * kBM, a.d};
-      SrcGatedAct<T> sb{(const T*)a.z_save, a.gates, a.slot_to_row, slot0, nrows, a.dff, nj * kBN};
-      gemm_tile<T>(TransLd<TransLoad<T, kBM>, SrcGatherRow<T>>{la, sa},
-                   TransLd<TransLoad<T, kBN>, SrcGatedAct<T>>{lb, sb}, nk, smem, acc);
+      SrcGatherRow<T> sa{(const T*)a.dy, a.slot_to_row, slot0, nrows, a.k, a.d, mi * C::BM, a.d};
+      SrcGatedAct<T> sb{(const T*)a.z_save, a.gates, a.slot_to_row, slot0, nrows, a.dff,
+                        nj * C::BN};
+      gemm_tile<T, C>(TransLd<decltype(la), SrcGatherRow<T>>{la, sa},
+                      TransLd<decltype(lb), SrcGatedAct<T>>{lb, sb}, nk, smem, acc);
       out = (dst < 0 ? a.dw2 + (size_t)e * a.d * a.dff
                      : a.rslots + (size_t)dst * w_elems + (size_t)2 * a.dff * a.d);
       ldo = a.dff;
@@ -536,50 +626,65 @@ __global__ __launch_bounds__(256) void k_bwd_dw(ExecArgs a) {
       loc -= n2m * n2n;
       mi = loc / n1n;
       nj = loc % n1n;
-      SrcSlotRow<T> sa{(const T*)a.bufA, slot0, nrows, 2 * a.dff, mi * kBM, 2 * a.dff};
-      SrcGatherRow<T> sb{(const T*)a.x, a.slot_to_row, slot0, nrows, a.k, a.d, nj * kBN, a.d};
-      gemm_tile<T>(TransLd<TransLoad<T, kBM>, SrcSlotRow<T>>{la, sa},
-                   TransLd<TransLoad<T, kBN>, SrcGatherRow<T>>{lb, sb}, nk, smem, acc);
+      SrcSlotRow<T> sa{(const T*)a.bufA, slot0, nrows, 2 * a.dff, mi * C::BM, 2 * a.dff};
+      SrcGatherRow<T> sb{(const T*)a.x, a.slot_to_row, slot0, nrows, a.k, a.d, nj * C::BN, a.d};
+      gemm_tile<T, C>(TransLd<decltype(la), SrcSlotRow<T>>{la, sa},
+                      TransLd<decltype(lb), SrcGatherRow<T>>{lb, sb}, nk, smem, acc);
       out = (dst < 0 ? a.dw1 + (size_t)e * 2 * a.dff * a.d : a.rslots + (size_t)dst * w_elems);
       ldo = a.d;
       nlim = a.d;
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const size_t row = (size_t)mi * kBM + acc_row(i, rr, lane);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = nj * kBN + acc_col(j, lane);
-          if (n < nlim) out[row * ldo + n] = acc[i][j][rr];
-        }
-      }
+    constexpr int PASS = 128, LDD = C::BN + 4;
+    MOE_LDS float* sd = (MOE_LDS float*)smem;
+    for (int p0 = 0; p0 < C::BM; p0 += PASS) {
+      if (p0) __syncthreads();
+      acc_to_lds<C>(acc, sd, LDD, p0, PASS, [](float v, int, int) { return v; });
+      __syncthreads();
+      lds_to_global<float, C::NT>(sd, PASS, C::BN, LDD, [&](int rl, int col, const V16& v) {
+        const int n = nj * C::BN + col;
+        if (n < nlim) stg16(out + ((size_t)mi * C::BM + p0 + rl) * ldo + n, v.u);
+      });
+    }
   }
 }
 
 // Owner slot <- (owner partial or 0) + replica partials in ascending worker
 // order, fp32.  Experts with an owner partial and no replica are untouched.
+// The per-expert table is staged in LDS once per workgroup.
 __global__ __launch_bounds__(256) void k_bwd_reduce(const int32_t* __restrict__ rep_slot,
                                                     const int32_t* __restrict__ owner_has,
                                                     const float* __restrict__ rslots, int E,
                                                     int P, int d, int dff, float* dw1,
                                                     float* dw2) {
+  __shared__ int tab[kMaxPlanExperts][kMaxP];
+  __shared__ int own[kMaxPlanExperts];
+  __shared__ int work[kMaxPlanExperts];
+  __shared__ int nwork;
+  if (threadIdx.x == 0) nwork = 0;
+  for (int i = threadIdx.x; i < E * P; i += 256) tab[i / P][i % P] = rep_slot[i];
+  for (int e = threadIdx.x; e < E; e += 256) own[e] = owner_has[e];
+  __syncthreads();
+  // experts with something to do: a replica partial, or no owner partial
+  for (int e = threadIdx.x; e < E; e += 256) {
+    bool rep = false;
+    for (int w = 0; w < P; ++w) rep |= tab[e][w] >= 0;
+    if (rep || !own[e]) work[atomicAdd(&nwork, 1)] = e;
+  }
+  __syncthreads();
   const size_t n1 = (size_t)2 * dff * d, n2 = (size_t)d * dff, w_elems = n1 + n2;
   const size_t nvec = w_elems / 4;
-  for (int e = 0; e < E; ++e) {
+  for (int q0 = 0; q0 < nwork; ++q0) {
+    const int e = work[q0];
     int slots[kMaxP];
     int nrep = 0;
-    for (int w = 0; w < P; ++w) {
-      const int sl = rep_slot[e * P + w];
-      if (sl >= 0) slots[nrep++] = sl;
-    }
-    const bool own = owner_has[e] != 0;
-    if (own && nrep == 0) continue;
+#pragma unroll
+    for (int w = 0; w < kMaxP; ++w)
+      if (w < P && tab[e][w] >= 0) slots[nrep++] = tab[e][w];
+    const bool ownp = own[e] != 0;
     for (size_t v = (size_t)blockIdx.x * 256 + threadIdx.x; v < nvec; v += (size_t)gridDim.x * 256) {
       const size_t i = v * 4;
       float* dst = (i < n1) ? dw1 + (size_t)e * n1 + i : dw2 + (size_t)e * n2 + (i - n1);
-      float4 accv = own ? *(const float4*)dst : make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 accv = ownp ? *(const float4*)dst : make_float4(0.f, 0.f, 0.f, 0.f);
       for (int q = 0; q < nrep; ++q) {
         const float4 p = *(const float4*)(rslots + (size_t)slots[q] * w_elems + i);
         accv.x += p.x; accv.y += p.y; accv.z += p.z; accv.w += p.w;
@@ -610,6 +715,17 @@ WsLayout exec_layout(const Sizes& z, bool backward) {
   return L;
 }
 
+// The big tile needs every M/N extent it touches to be a multiple of 256.
+bool use_big_tiles(const Sizes& z) {
+  return z.act_bytes == 2 && z.d % 256 == 0 && z.dff % 128 == 0;
+}
+
+size_t max_tiles(const Sizes& z) {
+  const int bm = use_big_tiles(z) ? BigCfg::BM : SmallCfg::BM;
+  const size_t per_block = z.beta > bm ? (size_t)(z.beta + bm - 1) / bm : 1;
+  return z.max_blocks * per_block;
+}
+
 static int num_cus() {
   static int n = 0;
   if (!n) {
@@ -621,12 +737,11 @@ static int num_cus() {
   return n;
 }
 
-template <typename K> static int persistent_grid(K kernel, size_t lds) {
-  static_assert(sizeof(K) > 0, "");
+template <typename K> static int persistent_grid(K kernel, int threads, size_t lds) {
   (void)hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds);
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess ||
       per_cu <= 0)
     per_cu = 1;
   int g = num_cus() * per_cu;
@@ -635,8 +750,8 @@ template <typename K> static int persistent_grid(K kernel, size_t lds) {
 }
 
 int gemm_wg_per_cu() {
-  const size_t lds = TileCfg<uint16_t>::LDS_BYTES;
-  return persistent_grid(k_fc1<uint16_t, false>, lds) / num_cus();
+  return persistent_grid(k_fc1<uint16_t, false, BigCfg>, BigCfg::NT,
+                         TileLds<uint16_t, BigCfg>::BYTES) / num_cus();
 }
 
 static void rec(void* const* ev, int i, hipStream_t st) {
@@ -647,12 +762,13 @@ static size_t sched_lds(const Sizes& z, bool bwd) {
   return sizeof(int) * ((size_t)2 * z.E + 1 + (bwd ? (size_t)3 * z.E * z.P : 0));
 }
 
-static SchedArgs make_sched(const Sizes& z, const int32_t* counts, const int32_t* boff,
-                            const int32_t* bw, const int32_t* owner, bool bwd, char* ws,
-                            const WsLayout& L, int32_t* status) {
+static void launch_sched(const Sizes& z, const int32_t* counts, const int32_t* boff,
+                         const int32_t* bw, const int32_t* owner, bool bwd, char* ws,
+                         const WsLayout& L, int32_t* status, hipStream_t st) {
   SchedArgs s{};
   s.counts = counts; s.boff = boff; s.bw = bw; s.owner = owner;
   s.E = z.E; s.P = z.P; s.s = z.s; s.beta = z.beta; s.backward = bwd ? 1 : 0;
+  s.bm = use_big_tiles(z) ? BigCfg::BM : SmallCfg::BM;
   s.ctr = (int32_t*)(ws + L.ctr);
   s.mt_cnt = (int32_t*)(ws + L.mt_cnt);
   s.mt = (int4*)(ws + L.mt);
@@ -662,7 +778,10 @@ static SchedArgs make_sched(const Sizes& z, const int32_t* counts, const int32_t
   s.rep_slot = (int32_t*)(ws + L.rep_slot);
   s.owner_has = (int32_t*)(ws + L.owner_has);
   s.status = status;
-  return s;
+  const size_t lds = sched_lds(z, bwd);
+  (void)hipFuncSetAttribute((const void*)k_sched, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sched_lds(z, true));
+  hipLaunchKernelGGL(k_sched, dim3(1), dim3(256), lds, st, s);
 }
 
 static ExecArgs make_exec(const Sizes& z, const LayerPtrs& Lp, char* ws, const WsLayout& L) {
@@ -683,15 +802,15 @@ static ExecArgs make_exec(const Sizes& z, const LayerPtrs& Lp, char* ws, const W
   return a;
 }
 
-template <typename T, bool FP8>
+template <typename T, bool FP8, class C>
 static void run_forward(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* y,
                         void* const* ev, hipStream_t st) {
-  const size_t lds = TileCfg<T>::LDS_BYTES;
-  static int g1 = persistent_grid(k_fc1<T, FP8>, lds);
-  static int g2 = persistent_grid(k_fc2<T, FP8>, lds);
-  hipLaunchKernelGGL((k_fc1<T, FP8>), dim3(g1), dim3(256), lds, st, a);
+  const size_t lds = gemm_lds_bytes<T, C>();
+  static int g1 = persistent_grid(k_fc1<T, FP8, C>, C::NT, lds);
+  static int g2 = persistent_grid(k_fc2<T, FP8, C>, C::NT, lds);
+  hipLaunchKernelGGL((k_fc1<T, FP8, C>), dim3(g1), dim3(C::NT), lds, st, a);
   rec(ev, 2, st);
-  hipLaunchKernelGGL((k_fc2<T, FP8>), dim3(g2), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((k_fc2<T, FP8, C>), dim3(g2), dim3(C::NT), lds, st, a);
   rec(ev, 3, st);
   const long long nth = (long long)z.T * (z.d / Elem<T>::VE);
   if (nth > 0)
@@ -706,38 +825,40 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
                    void* z_save, int32_t* status, char* ws, void* const* ev, hipStream_t st) {
   const WsLayout L = exec_layout(z, false);
   rec(ev, 0, st);
-  SchedArgs sa = make_sched(z, counts, boff, block_worker, nullptr, false, ws, L, status);
-  const size_t slds = sched_lds(z, false);
-  (void)hipFuncSetAttribute((const void*)k_sched, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)sched_lds(z, true));
-  hipLaunchKernelGGL(k_sched, dim3(1), dim3(256), slds, st, sa);
+  launch_sched(z, counts, boff, block_worker, nullptr, false, ws, L, status, st);
   rec(ev, 1, st);
   ExecArgs a = make_exec(z, Lp, ws, L);
   a.x = x; a.gates = gates; a.slot_to_row = slot_to_row; a.row_to_slot = row_to_slot;
   a.z_save = z_save;
-  if (Lp.act_dtype == MOE_F32) run_forward<float, false>(z, a, row_to_slot, y, ev, st);
-  else if (Lp.w_dtype == MOE_FP8_E4M3) run_forward<uint16_t, true>(z, a, row_to_slot, y, ev, st);
-  else run_forward<uint16_t, false>(z, a, row_to_slot, y, ev, st);
+  const bool big = use_big_tiles(z);
+  if (Lp.act_dtype == MOE_F32) run_forward<float, false, SmallCfg>(z, a, row_to_slot, y, ev, st);
+  else if (Lp.w_dtype == MOE_FP8_E4M3) {
+    if (big) run_forward<uint16_t, true, BigCfg>(z, a, row_to_slot, y, ev, st);
+    else run_forward<uint16_t, true, SmallCfg>(z, a, row_to_slot, y, ev, st);
+  } else {
+    if (big) run_forward<uint16_t, false, BigCfg>(z, a, row_to_slot, y, ev, st);
+    else run_forward<uint16_t, false, SmallCfg>(z, a, row_to_slot, y, ev, st);
+  }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
-template <typename T>
+template <typename T, class C>
 static void run_backward(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* dx,
                          float* dw1, float* dw2, void* const* ev, hipStream_t st) {
-  const size_t lds = TileCfg<T>::LDS_BYTES;
-  static int ga = persistent_grid(k_bwd_da<T>, lds);
-  static int gx = persistent_grid(k_bwd_dx<T>, lds);
-  static int gw = persistent_grid(k_bwd_dw<T>, lds);
-  hipLaunchKernelGGL(k_bwd_da<T>, dim3(ga), dim3(256), lds, st, a);
+  const size_t lds = TileLds<T, C>::BYTES;
+  static int ga = persistent_grid(k_bwd_da<T, C>, C::NT, lds);
+  static int gx = persistent_grid(k_bwd_dx<T, C>, C::NT, lds);
+  static int gw = persistent_grid(k_bwd_dw<T, C>, C::NT, lds);
+  hipLaunchKernelGGL((k_bwd_da<T, C>), dim3(ga), dim3(C::NT), lds, st, a);
   rec(ev, 2, st);
-  hipLaunchKernelGGL(k_bwd_dx<T>, dim3(gx), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((k_bwd_dx<T, C>), dim3(gx), dim3(C::NT), lds, st, a);
   rec(ev, 3, st);
   const long long nth = (long long)z.T * (z.d / Elem<T>::VE);
   if (nth > 0)
     hipLaunchKernelGGL(k_combine<T>, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, st,
                        (const T*)a.bufO, row_to_slot, z.T, z.k, z.d, (T*)dx);
   rec(ev, 4, st);
-  hipLaunchKernelGGL(k_bwd_dw<T>, dim3(gw), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((k_bwd_dw<T, C>), dim3(gw), dim3(C::NT), lds, st, a);
   rec(ev, 5, st);
   hipLaunchKernelGGL(k_bwd_reduce, dim3(num_cus() * 4), dim3(256), 0, st, a.rep_slot,
                      a.owner_has, (const float*)a.rslots, z.E, z.P, z.d, z.dff, dw1, dw2);
@@ -752,18 +873,15 @@ int launch_backward(const Sizes& z, const LayerPtrs& Lp, const void* x, const fl
                     int32_t* status, char* ws, void* const* ev, hipStream_t st) {
   const WsLayout L = exec_layout(z, true);
   rec(ev, 0, st);
-  SchedArgs sa = make_sched(z, counts, boff, block_worker, owner, true, ws, L, status);
-  const size_t slds = sched_lds(z, true);
-  (void)hipFuncSetAttribute((const void*)k_sched, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)slds);
-  hipLaunchKernelGGL(k_sched, dim3(1), dim3(256), slds, st, sa);
+  launch_sched(z, counts, boff, block_worker, owner, true, ws, L, status, st);
   rec(ev, 1, st);
   ExecArgs a = make_exec(z, Lp, ws, L);
   a.x = x; a.gates = gates; a.slot_to_row = slot_to_row; a.row_to_slot = row_to_slot;
   a.z_save = const_cast<void*>(z_save);
   a.dy = dy; a.dw1 = dw1; a.dw2 = dw2;
-  if (Lp.act_dtype == MOE_F32) run_backward<float>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
-  else run_backward<uint16_t>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
+  if (Lp.act_dtype == MOE_F32) run_backward<float, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
+  else if (use_big_tiles(z)) run_backward<uint16_t, BigCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
+  else run_backward<uint16_t, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -1,18 +1,25 @@
-// One 128x128 output tile of C = A * B on CDNA4 matrix cores.
+// One BM x BN output tile of C = A * B on CDNA4 matrix cores.
 //
-// 256 threads = 4 waves in a 2x2 grid, each wave owning a 64x64 sub-tile as
-// 2x2 blocks of 32x32 MFMA accumulators (16 fp32 per lane each).  Operands are
-// staged through LDS in a K-contiguous layout, [row][BK + pad], double
-// buffered: the global loads of K-tile kt+1 are in flight while the waves run
-// the MFMAs of K-tile kt, and one barrier per K-tile separates the two
-// buffers.  Row stride is BK*size + 16 bytes, so the 16-byte fragment reads of
-// the 32 lanes of one half-wave land on distinct bank groups.
+// Two shapes:
+//   Big   -- 256 x 256, 4 waves (2 x 2, each a 128 x 128 sub-tile = 4 x 4
+//            blocks of 32x32 MFMA accumulators, 256 accumulator registers per
+//            lane); 256 threads, one workgroup per CU, one wave per SIMD with
+//            the full 512-register file.  Each 64-wide K step loads 64 KB from
+//            L2/HBM for 8.4 MFLOP, twice the reuse of a 128 x 128 tile, and
+//            each wave reads 8 KB of LDS per 16 MFMAs.
+//   Small -- 128 x 128, 4 waves (2 x 2, each 64 x 64); 256 threads; used when a
+//            dimension is not a multiple of 256 or for fp32.
+// Operands are staged through LDS in a K-contiguous layout, [row][BK + pad],
+// double buffered: the global loads of K step kt+1 are in flight while the
+// waves run the MFMAs of step kt; one barrier per step separates the buffers.
+// The row stride is BK*size + 16 bytes, so the 16-byte fragment reads of the
+// 32 lanes of one half-wave land on distinct bank groups.
 //
 // Element types: bf16 (raw uint16_t) uses v_mfma_f32_32x32x16_bf16 (8 values
 // per lane per operand, BK = 64); fp32 uses v_mfma_f32_32x32x2_f32 (BK = 32).
 // Each lane of an MFMA operand holds a run of consecutive K values; both
-// operands use the same K assignment, so the contraction is exact in order of
-// the hardware's accumulation.
+// operands use the same K assignment, so the contraction is exact up to the
+// hardware's accumulation order.
 //
 // Operand loaders come in two shapes:
 //   RowLoad   -- the tile's rows are contiguous along K in memory (activation
@@ -28,17 +35,26 @@
 
 namespace moe {
 
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_> struct GemmCfg {
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int NT = 64 * WAVES_M * WAVES_N;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int MB = WM / 32, NB = WN / 32;
+};
+using BigCfg = GemmCfg<256, 256, 2, 2>;
+using SmallCfg = GemmCfg<128, 128, 2, 2>;
+
 template <typename T> struct Elem;
 template <> struct Elem<uint16_t> { static constexpr int VE = 8, BK = 64; };
 template <> struct Elem<float> { static constexpr int VE = 4, BK = 32; };
 
-template <typename T> struct TileCfg {
+template <typename T, class C> struct TileLds {
   static constexpr int VE = Elem<T>::VE, BK = Elem<T>::BK;
   static constexpr int LDK = BK + VE;               // +16 bytes
   static constexpr int KC = 2 * VE;                 // K per MFMA chunk
   static constexpr int NKC = BK / KC;
-  static constexpr int A_ELEMS = kBM * LDK, B_ELEMS = kBN * LDK;
-  static constexpr size_t LDS_BYTES = 2 * (size_t)(A_ELEMS + B_ELEMS) * sizeof(T);
+  static constexpr int A_ELEMS = C::BM * LDK, B_ELEMS = C::BN * LDK;
+  static constexpr size_t BYTES = 2 * (size_t)(A_ELEMS + B_ELEMS) * sizeof(T);
 };
 
 union V16 {
@@ -50,80 +66,96 @@ union V16 {
 
 MOE_DEV uint4 zero4() { return make_uint4(0, 0, 0, 0); }
 
+MOE_DEV int wave_id() { return threadIdx.x >> 6; }
+
 // ---- MFMA on one K chunk of the staged tile -------------------------------
-MOE_DEV void mma_chunk(f32x16_t (&acc)[2][2], const uint16_t* sA, const uint16_t* sB, int wm,
-                       int wn, int kc, int lane) {
-  constexpr int LDK = TileCfg<uint16_t>::LDK;
+template <class C>
+MOE_DEV void mma_chunk(f32x16_t (&acc)[C::MB][C::NB], const MOE_LDS uint16_t* sA,
+                       const MOE_LDS uint16_t* sB,
+                       int kc, int lane) {
+  constexpr int LDK = TileLds<uint16_t, C>::LDK;
+  const int wm = wave_id() / C::WAVES_N, wn = wave_id() % C::WAVES_N;
   const int ko = kc * 16 + (lane >> 5) * 8;
-  bf16x8_t a[2], b[2];
+  bf16x8_t a[C::MB], b[C::NB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    a[i] = *(const bf16x8_t*)(sA + (wm * 64 + i * 32 + (lane & 31)) * LDK + ko);
-    b[i] = *(const bf16x8_t*)(sB + (wn * 64 + i * 32 + (lane & 31)) * LDK + ko);
-  }
+  for (int i = 0; i < C::MB; ++i)
+    a[i] = *(const MOE_LDS bf16x8_t*)(sA + (wm * C::WM + i * 32 + (lane & 31)) * LDK + ko);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < C::NB; ++j)
+    b[j] = *(const MOE_LDS bf16x8_t*)(sB + (wn * C::WN + j * 32 + (lane & 31)) * LDK + ko);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+  for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NB; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
-MOE_DEV void mma_chunk(f32x16_t (&acc)[2][2], const float* sA, const float* sB, int wm, int wn,
-                       int kc, int lane) {
-  constexpr int LDK = TileCfg<float>::LDK;
+template <class C>
+MOE_DEV void mma_chunk(f32x16_t (&acc)[C::MB][C::NB], const MOE_LDS float* sA,
+                       const MOE_LDS float* sB, int kc,
+                       int lane) {
+  constexpr int LDK = TileLds<float, C>::LDK;
+  const int wm = wave_id() / C::WAVES_N, wn = wave_id() % C::WAVES_N;
   const int ko = kc * 8 + (lane >> 5) * 4;
-  f32x4_t a[2], b[2];
+  f32x4_t a[C::MB], b[C::NB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    a[i] = *(const f32x4_t*)(sA + (wm * 64 + i * 32 + (lane & 31)) * LDK + ko);
-    b[i] = *(const f32x4_t*)(sB + (wn * 64 + i * 32 + (lane & 31)) * LDK + ko);
-  }
+  for (int i = 0; i < C::MB; ++i)
+    a[i] = *(const MOE_LDS f32x4_t*)(sA + (wm * C::WM + i * 32 + (lane & 31)) * LDK + ko);
+#pragma unroll
+  for (int j = 0; j < C::NB; ++j)
+    b[j] = *(const MOE_LDS f32x4_t*)(sB + (wn * C::WN + j * 32 + (lane & 31)) * LDK + ko);
 #pragma unroll
   for (int v = 0; v < 4; ++v)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < C::MB; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < C::NB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][v], b[j][v], acc[i][j], 0, 0, 0);
 }
 
 // ---- loaders ---------------------------------------------------------------
-// K-contiguous rows.  rowptr(row) returns the row's first element (K index 0)
-// or nullptr for a row that reads as zeros.
-template <typename T, int ROWS> struct RowLoad {
-  static constexpr int VE = Elem<T>::VE, BK = Elem<T>::BK, LDK = TileCfg<T>::LDK;
+// K-contiguous rows.  rowoff(row) returns the element offset of the row's
+// first element (K index 0) from `base`, or -1 for a row that reads as zeros.
+// Offsets are 32-bit (every operand here is < 2^31 elements) and the LDS
+// position of chunk i is a compile-time step from chunk 0, which keeps the
+// loader at one register per chunk plus its data.
+template <typename T, int ROWS, int NT> struct RowLoad {
+  static constexpr int VE = Elem<T>::VE, BK = Elem<T>::BK, LDK = BK + VE;
   static constexpr int CPR = BK / VE;               // 16-byte chunks per row
-  static constexpr int NCH = ROWS * CPR / 256;
-  const T* ptr[NCH];
-  int soff[NCH];
+  static constexpr int NCH = ROWS * CPR / NT;
+  static_assert(NT % CPR == 0, "rows per pass");
+  const T* base;
+  int off[NCH];
   uint4 v[NCH];
-  template <class F> MOE_DEV void init(F rowptr) {
+  template <class F> MOE_DEV void init(const T* b, F rowoff) {
+    base = b;
+    const int col = (threadIdx.x % CPR) * VE;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      const int row = c / CPR, col = (c % CPR) * VE;
-      const T* p = rowptr(row);
-      ptr[i] = p ? p + col : nullptr;
-      soff[i] = row * LDK + col;
+      const int row = threadIdx.x / CPR + i * (NT / CPR);
+      const int o = rowoff(row);
+      off[i] = o < 0 ? -1 : o + col;
     }
   }
   MOE_DEV void load(int kt) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) v[i] = ptr[i] ? *(const uint4*)(ptr[i] + (size_t)kt * BK) : zero4();
+    for (int i = 0; i < NCH; ++i)
+      v[i] = off[i] >= 0 ? ldg16(base + (size_t)(unsigned)off[i] + (size_t)kt * BK) : zero4();
   }
-  MOE_DEV void store(T* s) {
+  MOE_DEV void store(MOE_LDS T* s) {
+    MOE_LDS T* p = s + (threadIdx.x / CPR) * LDK + (threadIdx.x % CPR) * VE;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) *(uint4*)(s + soff[i]) = v[i];
+    for (int i = 0; i < NCH; ++i) lds_st16(p + i * (NT / CPR) * LDK, v[i]);
   }
 };
 
 // e4m3 weight rows with one fp32 scale per 128x128 block, widened to bf16 on
 // the way into LDS.  rowptr(row) gives the row's codes, rowscale(row) the
 // scale row of its 128-row block (indexed by K/128).
-template <int ROWS> struct RowLoadFp8 {
-  static constexpr int BK = 64, LDK = TileCfg<uint16_t>::LDK;
+template <int ROWS, int NT> struct RowLoadFp8 {
+  static constexpr int BK = 64, LDK = BK + 8;
   static constexpr int CPR = BK / 16;               // 16 codes per 16-byte chunk
-  static constexpr int NCH = ROWS * CPR / 256;
+  static constexpr int NCH = ROWS * CPR / NT;
   const uint8_t* ptr[NCH];
   const float* sc[NCH];
   int soff[NCH];
@@ -132,7 +164,7 @@ template <int ROWS> struct RowLoadFp8 {
   template <class F, class G> MOE_DEV void init(F rowptr, G rowscale) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int c = threadIdx.x + 256 * i;
+      const int c = threadIdx.x + NT * i;
       const int row = c / CPR, col = (c % CPR) * 16;
       const uint8_t* p = rowptr(row);
       ptr[i] = p ? p + col : nullptr;
@@ -143,11 +175,11 @@ template <int ROWS> struct RowLoadFp8 {
   MOE_DEV void load(int kt) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      v[i] = ptr[i] ? *(const uint4*)(ptr[i] + (size_t)kt * BK) : zero4();
-      s[i] = ptr[i] ? sc[i][(kt * BK) >> 7] : 0.f;
+      v[i] = ptr[i] ? ldg16(ptr[i] + (size_t)kt * BK) : zero4();
+      s[i] = ptr[i] ? *(const MOE_GLB float*)(sc[i] + ((kt * BK) >> 7)) : 0.f;
     }
   }
-  MOE_DEV void store(uint16_t* sm) {
+  MOE_DEV void store(MOE_LDS uint16_t* sm) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       V16 in, o0, o1;
@@ -157,8 +189,8 @@ template <int ROWS> struct RowLoadFp8 {
         o0.h[j] = f2bf(e4m3_to_f32(in.b[j]) * s[i]);
         o1.h[j] = f2bf(e4m3_to_f32(in.b[8 + j]) * s[i]);
       }
-      *(uint4*)(sm + soff[i]) = o0.u;
-      *(uint4*)(sm + soff[i] + 8) = o1.u;
+      lds_st16(sm + soff[i], o0.u);
+      lds_st16(sm + soff[i] + 8, o1.u);
     }
   }
 };
@@ -166,43 +198,49 @@ template <int ROWS> struct RowLoadFp8 {
 // Source contiguous along the tile's ROWS axis (M or N); K walks source rows.
 // src(k, mn) returns 16 bytes = VE elements at (k, mn..mn+VE-1), zeros when
 // out of range.  Thread t covers K rows k0..k0+3 and MN columns mn0..mn0+VE-1.
-template <typename T, int ROWS> struct TransLoad {
-  static constexpr int VE = Elem<T>::VE, BK = Elem<T>::BK, LDK = TileCfg<T>::LDK;
+template <typename T, int ROWS, int NT> struct TransLoad {
+  static constexpr int VE = Elem<T>::VE, BK = Elem<T>::BK, LDK = BK + VE;
   static constexpr int MNG = ROWS / VE;
   static constexpr int KSUB = 4;
-  static_assert(MNG * (BK / KSUB) == 256, "one 4 x VE block per thread");
-  int mn0, k0;
-  uint4 v[KSUB];
-  MOE_DEV void init() {
-    mn0 = (threadIdx.x % MNG) * VE;
-    k0 = (threadIdx.x / MNG) * KSUB;
-  }
+  static constexpr int NSUB = MNG * (BK / KSUB) / NT;   // 4 x VE blocks per thread
+  static_assert(NSUB * NT == MNG * (BK / KSUB), "blocks must tile the threads");
+  uint4 v[NSUB][KSUB];
+  MOE_DEV void init() {}
+  // K groups vary fastest across lanes: the 16 (bf16) lanes of one MN group
+  // write one LDS row's K range as a contiguous run, and the next 16 lanes the
+  // row VE further on, so a wave's transposed stores cover every bank once.
+  static constexpr int KG = BK / KSUB;
+  MOE_DEV int mn0(int i) const { return ((threadIdx.x + NT * i) / KG) * VE; }
+  MOE_DEV int k0(int i) const { return ((threadIdx.x + NT * i) % KG) * KSUB; }
   template <class S> MOE_DEV void load(int kt, S& src) {
 #pragma unroll
-    for (int kk = 0; kk < KSUB; ++kk) v[kk] = src(kt * BK + k0 + kk, mn0);
+    for (int i = 0; i < NSUB; ++i)
+#pragma unroll
+      for (int kk = 0; kk < KSUB; ++kk) v[i][kk] = src(kt * BK + k0(i) + kk, mn0(i));
   }
-  MOE_DEV void store(T* s) {
-    if constexpr (sizeof(T) == 2) {
+  MOE_DEV void store(MOE_LDS T* s) {
+#pragma unroll
+    for (int i = 0; i < NSUB; ++i) {
       V16 in[KSUB];
 #pragma unroll
-      for (int kk = 0; kk < KSUB; ++kk) in[kk].u = v[kk];
+      for (int kk = 0; kk < KSUB; ++kk) in[kk].u = v[i][kk];
+      const int m0 = mn0(i), kb = k0(i);
+      if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        uint2 o;
-        o.x = (uint32_t)in[0].h[e] | ((uint32_t)in[1].h[e] << 16);
-        o.y = (uint32_t)in[2].h[e] | ((uint32_t)in[3].h[e] << 16);
-        *(uint2*)(s + (mn0 + e) * LDK + k0) = o;
-      }
-    } else {
-      V16 in[KSUB];
+        for (int e = 0; e < VE; ++e) {
+          uint2 o;
+          o.x = (uint32_t)in[0].h[e] | ((uint32_t)in[1].h[e] << 16);
+          o.y = (uint32_t)in[2].h[e] | ((uint32_t)in[3].h[e] << 16);
+          lds_st8(s + (m0 + e) * LDK + kb, o);
+        }
+      } else {
 #pragma unroll
-      for (int kk = 0; kk < KSUB; ++kk) in[kk].u = v[kk];
+        for (int e = 0; e < VE; ++e) {
+          V16 o;
 #pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        V16 o;
-#pragma unroll
-        for (int kk = 0; kk < KSUB; ++kk) o.f[kk] = in[kk].f[e];
-        *(uint4*)(s + (mn0 + e) * LDK + k0) = o.u;
+          for (int kk = 0; kk < KSUB; ++kk) o.f[kk] = in[kk].f[e];
+          lds_st16(s + (m0 + e) * LDK + kb, o.u);
+        }
       }
     }
   }
@@ -212,34 +250,34 @@ template <typename T, int ROWS> struct TransLoad {
 template <class L> struct PlainLd {
   L& l;
   MOE_DEV void load(int kt) { l.load(kt); }
-  template <typename T> MOE_DEV void store(T* s) { l.store(s); }
+  template <typename P> MOE_DEV void store(P s) { l.store(s); }
 };
 template <class L, class S> struct TransLd {
   L& l;
   S& src;
   MOE_DEV void load(int kt) { l.load(kt, src); }
-  template <typename T> MOE_DEV void store(T* s) { l.store(s); }
+  template <typename P> MOE_DEV void store(P s) { l.store(s); }
 };
 
 // ---- main loop ----------------------------------------------------------------
-template <typename T, class LA, class LB>
-MOE_DEV void gemm_tile(LA la, LB lb, int nk, T* smem, f32x16_t (&acc)[2][2]) {
-  using C = TileCfg<T>;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
+// Every wave runs every MFMA: a data-dependent skip would make the compiler
+// copy the accumulators, which costs far more than the padding rows it saves.
+template <typename T, class C, class LA, class LB>
+MOE_DEV void gemm_tile(LA la, LB lb, int nk, MOE_LDS T* smem, f32x16_t (&acc)[C::MB][C::NB]) {
+  using L = TileLds<T, C>;
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < C::MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < C::NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   if (nk <= 0) return;
-  T* sA[2] = {smem, smem + C::A_ELEMS + C::B_ELEMS};
-  T* sB[2] = {smem + C::A_ELEMS, smem + 2 * C::A_ELEMS + C::B_ELEMS};
+  constexpr int STAGE = L::A_ELEMS + L::B_ELEMS;
   la.load(0);
   lb.load(0);
-  la.store(sA[0]);
-  lb.store(sB[0]);
+  la.store(smem);
+  lb.store(smem + L::A_ELEMS);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
@@ -249,23 +287,282 @@ MOE_DEV void gemm_tile(LA la, LB lb, int nk, T* smem, f32x16_t (&acc)[2][2]) {
       lb.load(kt + 1);
     }
 #pragma unroll
-    for (int kc = 0; kc < C::NKC; ++kc) mma_chunk(acc, sA[cur], sB[cur], wm, wn, kc, lane);
+    for (int kc = 0; kc < L::NKC; ++kc)
+      mma_chunk<C>(acc, smem + cur * STAGE, smem + cur * STAGE + L::A_ELEMS, kc, lane);
     if (more) {
-      la.store(sA[cur ^ 1]);
-      lb.store(sB[cur ^ 1]);
+      la.store(smem + (cur ^ 1) * STAGE);
+      lb.store(smem + (cur ^ 1) * STAGE + L::A_ELEMS);
     }
     __syncthreads();
   }
 }
 
-// Coordinates of accumulator register r of block (i, j) for this lane.
-MOE_DEV int acc_row(int i, int r, int lane) {
-  const int wm = (threadIdx.x >> 6) >> 1;
-  return wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+// Deeper pipeline: two register sets of global prefetch, so the loads of K step
+// kt+2 are in flight while step kt computes; the LDS stores of step kt+1 (whose
+// loads were issued a full step earlier) are made between the MFMA chunks of
+// step kt; and the operand fragments of chunk kc+1 are read while chunk kc's
+// MFMAs run.  One barrier per step.  LA/LB are copyable loader values.
+template <class C, typename T> struct Frags;
+template <class C> struct Frags<C, uint16_t> {
+  bf16x8_t a[C::MB], b[C::NB];
+  MOE_DEV void read(const MOE_LDS uint16_t* sA, const MOE_LDS uint16_t* sB, int kc, int lane) {
+    constexpr int LDK = TileLds<uint16_t, C>::LDK;
+    const int wm = wave_id() / C::WAVES_N, wn = wave_id() % C::WAVES_N;
+    const int ko = kc * 16 + (lane >> 5) * 8;
+#pragma unroll
+    for (int i = 0; i < C::MB; ++i)
+      a[i] = *(const MOE_LDS bf16x8_t*)(sA + (wm * C::WM + i * 32 + (lane & 31)) * LDK + ko);
+#pragma unroll
+    for (int j = 0; j < C::NB; ++j)
+      b[j] = *(const MOE_LDS bf16x8_t*)(sB + (wn * C::WN + j * 32 + (lane & 31)) * LDK + ko);
+  }
+  MOE_DEV void mma(f32x16_t (&acc)[C::MB][C::NB]) const {
+#pragma unroll
+    for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+};
+
+template <typename T, class C, class LA, class LB>
+MOE_DEV void gemm_tile_deep(LA la0, LB lb0, int nk, MOE_LDS T* smem, f32x16_t (&acc)[C::MB][C::NB]) {
+  using L = TileLds<T, C>;
+  constexpr int STAGE = L::A_ELEMS + L::B_ELEMS;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  if (nk <= 0) return;
+  LA la1 = la0;
+  LB lb1 = lb0;
+  // prologue: step 0 -> LDS stage 0; step 1 in flight in set 1
+  la0.load(0);
+  lb0.load(0);
+  if (nk > 1) { la1.load(1); lb1.load(1); }
+  la0.store(smem);
+  lb0.store(smem + L::A_ELEMS);
+  __syncthreads();
+  Frags<C, T> f0, f1;
+  auto step = [&](int kt, LA& lan, LB& lbn, LA& las, LB& lbs) {
+    // lan/lbn: set to load step kt+2 into; las/lbs: set holding step kt+1
+    const MOE_LDS T* sA = smem + (kt & 1) * STAGE;
+    const MOE_LDS T* sB = sA + L::A_ELEMS;
+    MOE_LDS T* nA = smem + ((kt + 1) & 1) * STAGE;
+    if (kt + 2 < nk) { lan.load(kt + 2); lbn.load(kt + 2); }
+    f0.read(sA, sB, 0, lane);
+#pragma unroll
+    for (int kc = 0; kc < L::NKC; kc += 2) {
+      f1.read(sA, sB, kc + 1, lane);
+      f0.mma(acc);
+      if (kc == 0 && kt + 1 < nk) las.store(nA);
+      if (kc + 2 < L::NKC) f0.read(sA, sB, kc + 2, lane);
+      f1.mma(acc);
+      if (kc == 0 && kt + 1 < nk) lbs.store(nA + L::A_ELEMS);
+    }
+    __syncthreads();
+  };
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, la0, lb0, la1, lb1);
+    step(kt + 1, la1, lb1, la0, lb0);
+  }
+  if (kt < nk) step(kt, la0, lb0, la1, lb1);
 }
-MOE_DEV int acc_col(int j, int lane) {
-  const int wn = (threadIdx.x >> 6) & 1;
-  return wn * 64 + j * 32 + (lane & 31);
+
+// ---- direct-to-LDS pipeline (bf16, K-contiguous operands) ---------------------
+// global_load_lds_dwordx4 moves 16 bytes per lane from global memory straight
+// into LDS (lane i of a wave writes LDS bytes [16 i, 16 i + 16) after the
+// wave-uniform base), so staging costs no registers and four stages fit:
+// the loads of K step kt+3 are in flight while step kt computes.
+// Stage layout: [rows][32 bf16 = 64 bytes], the four 16-byte chunks of a row
+// XOR-swizzled by ((row >> 1) ^ (row >> 3)) & 3, so any 8 (or 16) lanes that
+// read one chunk of 8 (16) consecutive rows hit distinct LDS bank groups.  A wave load instruction
+// covers 16 rows; the 256 rows of a tile operand are 16 instructions, 4 per
+// wave.  Completion is tracked with explicit vmcnt waits and a bare s_barrier
+// (__syncthreads would wait for every load in flight).
+constexpr int kDmaStages = 4, kDmaBK = 32, kDmaRowBytes = 64;
+
+MOE_DEV int dma_swz(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row >> 3)) & 3); }
+
+template <int ROWS, int NWAVES> struct RowDma {
+  static constexpr int NI = ROWS / 16 / NWAVES;     // load instructions per wave per step
+  const uint16_t* base;
+  int off[NI];                                      // element offset of this lane's chunk
+  template <class F> MOE_DEV void init(const uint16_t* b, F rowoff) {
+    base = b;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = (w + NWAVES * i) * 16 + (lane >> 2);
+      const int o = rowoff(row);
+      off[i] = (o < 0 ? 0 : o) + dma_swz(row, lane & 3) * 8;
+    }
+  }
+  // issue this wave's loads of K step kt into the stage at `st` (LDS)
+  MOE_DEV void issue(int kt, MOE_LDS uint16_t* st) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const MOE_GLB void*)(base + (size_t)(unsigned)off[i] + (size_t)kt * kDmaBK),
+          (MOE_LDS void*)(st + (w + NWAVES * i) * 16 * (kDmaRowBytes / 2)), 16, 0, 0);
+  }
+};
+
+template <int N> MOE_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <class C> struct DmaFrags {
+  bf16x8_t a[C::MB], b[C::NB];
+  MOE_DEV void read(const MOE_LDS uint16_t* sA, const MOE_LDS uint16_t* sB, int kc, int lane) {
+    const int wm = wave_id() / C::WAVES_N, wn = wave_id() % C::WAVES_N;
+    const int ch = kc * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < C::MB; ++i) {
+      const int row = wm * C::WM + i * 32 + (lane & 31);
+      a[i] = *(const MOE_LDS bf16x8_t*)(sA + row * 32 + dma_swz(row, ch) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < C::NB; ++j) {
+      const int row = wn * C::WN + j * 32 + (lane & 31);
+      b[j] = *(const MOE_LDS bf16x8_t*)(sB + row * 32 + dma_swz(row, ch) * 8);
+    }
+  }
+  MOE_DEV void mma(f32x16_t (&acc)[C::MB][C::NB]) const {
+#pragma unroll
+    for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+};
+
+template <class C> struct DmaCfg {
+  static constexpr int STAGE_A = C::BM * 32, STAGE_B = C::BN * 32;   // elements
+  static constexpr int STAGE = STAGE_A + STAGE_B;
+  static constexpr size_t BYTES = (size_t)kDmaStages * STAGE * 2;
+  static constexpr int LPS = C::BM / 16 / (C::NT / 64) + C::BN / 16 / (C::NT / 64);
+};
+
+template <int N> MOE_DEV void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));   // lgkmcnt(0)
+}
+
+// nk = K / 32 steps.  Schedule of step kt (stage kt % 4 holds its operands):
+//   read chunk-1 fragments of kt | MFMAs of chunk 0
+//   wait until this wave's loads of step kt+1 landed and its LDS reads are
+//   done; barrier (now every wave's part of step kt+1 is in LDS and nobody
+//   still reads stage kt % 4); issue the loads of step kt+4 into stage kt % 4;
+//   read chunk-0 fragments of kt+1 | MFMAs of chunk 1 of kt.
+// Loads past the last step re-read step nk-1 into stages nobody reads again,
+// so every step has the same shape and the same wait counts.
+// sched_barrier pins each fragment read ahead of the 16 MFMAs that hide it.
+template <class C>
+MOE_DEV void gemm_tile_dma(const RowDma<C::BM, C::NT / 64>& la, const RowDma<C::BN, C::NT / 64>& lb,
+                           int nk, MOE_LDS uint16_t* smem, f32x16_t (&acc)[C::MB][C::NB]) {
+  using D = DmaCfg<C>;
+  constexpr int LPS = D::LPS;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  if (nk <= 0) return;
+  __syncthreads();                      // the previous tile's epilogue is done with the LDS
+  auto issue = [&](int step, MOE_LDS uint16_t* st) {
+    const int kk = step < nk ? step : nk - 1;
+    la.issue(kk, st);
+    lb.issue(kk, st + D::STAGE_A);
+  };
+#pragma unroll
+  for (int s = 0; s < kDmaStages; ++s) issue(s, smem + s * D::STAGE);
+  wait_vm_lgkm0<3 * LPS>();
+  __builtin_amdgcn_s_barrier();
+  DmaFrags<C> f0, f1;
+  f0.read(smem, smem + D::STAGE_A, 0, lane);
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    const MOE_LDS uint16_t* sA = smem + (kt % kDmaStages) * D::STAGE;
+    const MOE_LDS uint16_t* nA = smem + ((kt + 1) % kDmaStages) * D::STAGE;
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): chunk-0 fragments are in
+    __builtin_amdgcn_sched_barrier(0);
+    f1.read(sA, sA + D::STAGE_A, 1, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    f0.mma(acc);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm_lgkm0<2 * LPS>();
+    __builtin_amdgcn_s_barrier();
+    issue(kt + kDmaStages, smem + (kt % kDmaStages) * D::STAGE);
+    f0.read(nA, nA + D::STAGE_A, 0, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    f1.mma(acc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  {
+    const MOE_LDS uint16_t* sA = smem + ((nk - 1) % kDmaStages) * D::STAGE;
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    f1.read(sA, sA + D::STAGE_A, 1, lane);
+    f0.mma(acc);
+    f1.mma(acc);
+  }
+  wait_vm_lgkm0<0>();
+  __syncthreads();                      // all loads landed, all waves done with the stages
+}
+
+// Coordinates of accumulator register r of block (i, j) for this lane, within
+// the tile.
+template <class C> MOE_DEV int acc_row(int i, int r, int lane) {
+  const int wm = wave_id() / C::WAVES_N;
+  return wm * C::WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+}
+template <class C> MOE_DEV int acc_col(int j, int lane) {
+  const int wn = wave_id() % C::WAVES_N;
+  return wn * C::WN + j * 32 + (lane & 31);
+}
+
+// ---- epilogue through LDS ----------------------------------------------------
+// The accumulators are written unconditionally into an LDS tile (row-major,
+// `ldn` elements per row), then the workgroup reads it back in 16-byte chunks
+// along rows and calls emit(row, col, chunk) for global stores that are
+// coalesced and can be masked by row.  Callers bracket the two phases with
+// __syncthreads().
+template <class C, typename LdsT, class XF>
+MOE_DEV void acc_to_lds(const f32x16_t (&acc)[C::MB][C::NB], MOE_LDS LdsT* s, int ldn, int row0,
+                        int rows, XF xf) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < C::MB; ++i) {
+    const int rbase = (wave_id() / C::WAVES_N) * C::WM + i * 32;
+    if (rbase < row0 || rbase >= row0 + rows) continue;   // whole 32-row block in or out
+#pragma unroll
+    for (int j = 0; j < C::NB; ++j)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int row = rbase + (rr >> 2) * 8 + (lane >> 5) * 4 + (rr & 3);
+        const int col = (wave_id() % C::WAVES_N) * C::WN + j * 32 + (lane & 31);
+        s[(row - row0) * ldn + col] = xf(acc[i][j][rr], row, col);
+      }
+  }
+}
+
+template <typename LdsT, int NT, class EMIT>
+MOE_DEV void lds_to_global(const MOE_LDS LdsT* s, int rows, int cols, int ldn, EMIT emit) {
+  constexpr int V = 16 / sizeof(LdsT);
+  const int cpr = cols / V;
+  for (int c = threadIdx.x; c < rows * cpr; c += NT) {
+    const int row = c / cpr, col = (c % cpr) * V;
+    V16 v;
+    v.u = lds_ld16(s + row * ldn + col);
+    emit(row, col, v);
+  }
 }
 
 template <typename T> MOE_DEV T to_act(float f);

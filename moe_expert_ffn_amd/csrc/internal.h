@@ -10,13 +10,11 @@ namespace moe {
 
 constexpr int kMaxExperts = 1024;      // routing statistics
 constexpr int kMaxPlanExperts = 512;   // planner and executors (LDS-resident tables)
-constexpr int kBM = 128;               // rows of one GEMM tile (= one M-tile)
-constexpr int kBN = 128;               // columns of one GEMM tile
 constexpr int kNumCounters = 64;       // per-(phase, worker) work counters
 
 inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Per-worker M-tile descriptor: expert, first slot, valid rows (<= kBM).
+// Per-worker M-tile descriptor: expert, first slot, valid rows (<= tile rows).
 // Per-worker weight-gradient segment: expert, first slot, valid rows,
 // destination (-1 = the owner's slot dw*[e], else a replica slot index).
 struct Sizes {
@@ -30,6 +28,8 @@ struct WsLayout {
 };
 
 WsLayout exec_layout(const Sizes& z, bool backward);
+bool use_big_tiles(const Sizes& z);
+size_t max_tiles(const Sizes& z);
 size_t route_ws_bytes(int T, int k, int E);
 
 int launch_route_stats(const int32_t* ids, int T, int k, int E, int beta, int32_t* counts,

@@ -43,17 +43,33 @@ __global__ __launch_bounds__(256) void k_route_count(const int32_t* __restrict__
     slot_to_row[sidx] = -1;
 }
 
-// One workgroup of 1024 threads; thread e owns expert e.
+// One workgroup of 1024 threads.  Thread (e, g), g < G = 1024 / E, owns expert
+// e's chunks [g*nch/G, (g+1)*nch/G): it sums them, the partial sums meet in
+// LDS, threads e < E scan across experts, and each (e, g) then rewrites its
+// chunks as exclusive prefixes offset by beta * block_offset(e).
 __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk_cnt, int nchunks,
                                                      int E, int beta, int32_t* counts,
                                                      int32_t* offsets, int32_t* block_counts,
                                                      int32_t* block_offsets, double* kappa) {
   __shared__ int wtot_c[16], wtot_b[16];
   __shared__ long long red_s[16], red_s2[16];
-  const int e = threadIdx.x, lane = e & 63, wv = e >> 6;
+  __shared__ int part[1024];           // [g][e] partial sums
+  __shared__ int bbase[kMaxExperts];   // beta * block_offset(e)
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int G = 1024 / E;
+  const int e_own = tid % E, g = tid / E;
+  const bool worker = g < G;
+  const int c0 = worker ? (int)((long long)g * nchunks / G) : 0;
+  const int c1 = worker ? (int)((long long)(g + 1) * nchunks / G) : 0;
+  int ps = 0;
+#pragma unroll 8
+  for (int ch = c0; ch < c1; ++ch) ps += chunk_cnt[(size_t)ch * E + e_own];
+  if (worker) part[g * E + e_own] = ps;
+  __syncthreads();
+  const int e = tid;
   int c = 0;
   if (e < E)
-    for (int ch = 0; ch < nchunks; ++ch) c += chunk_cnt[(size_t)ch * E + e];
+    for (int q = 0; q < G; ++q) c += part[q * E + e];
   const int b = (c + beta - 1) / beta;
   const int ic = wave_incl_scan(c), ib = wave_incl_scan(b);
   if (lane == 63) { wtot_c[wv] = ic; wtot_b[wv] = ib; }
@@ -68,20 +84,25 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
     offsets[e] = exc_c;
     block_counts[e] = b;
     block_offsets[e] = exc_b;
+    bbase[e] = beta * exc_b;
     if (e == E - 1) { offsets[E] = exc_c + c; block_offsets[E] = exc_b + b; }
-    int run = beta * exc_b;
-    for (int ch = 0; ch < nchunks; ++ch) {
-      const size_t at = (size_t)ch * E + e;
-      const int t = chunk_cnt[at];
-      chunk_cnt[at] = run;
-      run += t;
-    }
   }
   if (e == 0) {
     long long S = 0, S2 = 0;
     for (int w = 0; w < 16; ++w) { S += red_s[w]; S2 += red_s2[w]; }
     // exact integers, then one correctly rounded IEEE division
     *kappa = (S == 0) ? 1.0 : (double)((long long)E * S2) / (double)(S * S);
+  }
+  __syncthreads();
+  if (worker) {
+    int run = bbase[e_own];
+    for (int q = 0; q < g; ++q) run += part[q * E + e_own];
+    for (int ch = c0; ch < c1; ++ch) {
+      const size_t at = (size_t)ch * E + e_own;
+      const int t = chunk_cnt[at];
+      chunk_cnt[at] = run;
+      run += t;
+    }
   }
 }
 

@@ -74,7 +74,7 @@ def test_forward_plan_invariance(name):
 
 def test_forward_saves_z():
     w = SMALL["small_bf16"]
-    c = Case(w, 0)
+    c = Case(w, 0, backward=True)       # a backward-capable runner keeps [G, U]
     _run(c)
     x, w1, w2, ids, gates = c.oracle_inputs()
     _, zs = offn.forward(x, w1, w2, ids, gates, return_z=True)
