@@ -35,6 +35,7 @@ struct SchedArgs {
   int32_t* rep_slot;
   int32_t* owner_has;
   int32_t* status;
+  int32_t* zero;
 };
 
 MOE_DEV int expert_of(int g, const int* boff_s, int E) {
@@ -71,6 +72,7 @@ __global__ __launch_bounds__(256) void k_sched(SchedArgs a) {
   for (int i = tid; i <= E; i += 256) boff_s[i] = a.boff[i];
   for (int i = tid; i < E; i += 256) cnt_s[i] = a.counts[i];
   if (tid < kNumCounters) a.ctr[tid] = 0;
+  if (tid < 64) a.zero[tid] = 0;
   if (a.backward)
     for (int i = tid; i < E * P; i += 256) { s0_s[i] = INT_MAX; rows_s[i] = 0; starts_s[i] = 0; }
   __syncthreads();
@@ -208,6 +210,8 @@ struct ExecArgs {
   float* dw1;
   float* dw2;
   float* rslots;
+  void* bufP;             // backward: P = p * SiLU(G) * U per routed row
+  const uint16_t* zero;   // 256 zero bytes in global memory
 };
 
 enum { PH_FC1 = 0, PH_FC2 = 1, PH_DA = 2, PH_DX = 3, PH_DW = 4 };
@@ -452,6 +456,7 @@ __global__ __launch_bounds__(C::NT) void k_bwd_da(ExecArgs a) {
   const T* DY = (const T*)a.dy;
   const T* Z = (const T*)a.z_save;
   T* dZ = (T*)a.bufA;
+  T* PA = (T*)a.bufP;    // P = p * SiLU(G) * U, written when a consumer needs it
   while (true) {
     const int tile = next_tile(&a.ctr[PH_DA * kMaxP + r], &tslot);
     if (tile >= total) break;
@@ -480,17 +485,20 @@ __global__ __launch_bounds__(C::NT) void k_bwd_da(ExecArgs a) {
         const int row = p0 + rl, n = nj * C::BN + col;
         if (row >= nrows || n >= a.dff) return;
         const size_t zb = ((size_t)slot0 + row) * 2 * a.dff + n;
-        float g[4], u[4], dg[4], du[4];
+        float g[4], u[4], dg[4], du[4], pa[4];
         load4(Z + zb, g);
         load4(Z + zb + a.dff, u);
+        const float p = pg[row];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float sg = 1.f / (1.f + expf(-g[q]));
           dg[q] = v.f[q] * u[q] * sg * (1.f + g[q] * (1.f - sg));
           du[q] = v.f[q] * g[q] * sg;
+          pa[q] = p * (g[q] * sg * u[q]);
         }
         store4(dZ + zb, dg);
         store4(dZ + zb + a.dff, du);
+        if (PA) store4(PA + ((size_t)slot0 + row) * a.dff + n, pa);
       });
     }
   }
@@ -648,6 +656,89 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dw(ExecArgs a) {
   }
 }
 
+// ---- weight gradients on the direct-to-LDS pipeline (bf16, d and d_ff multiples of 256) --
+// Weight gradients per (expert, worker) segment; K = the segment's routed rows,
+// in windows of up to kTokTab rows whose token indices sit in an LDS table.
+// dW2[c, n] = sum dy_t[c] * P[n];  dW1[j, c] = sum dZ[j] * x_t[c].
+// Every operand is read in its natural [row][feature] layout through transpose
+// reads; rows past the segment read the zero block.
+constexpr int kTokTab = 8192;
+template <class C>
+__global__ __launch_bounds__(C::NT) void k_bwd_dw_dma(ExecArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __shared__ int tslot;
+  MOE_LDS uint16_t* smem = (MOE_LDS uint16_t*)smem_raw;
+  MOE_LDS uint16_t* tok = smem + DmaPipe<C, MnOperand<MnDma<C::BM, C::NT / 64>, int>,
+                                         MnOperand<MnDma<C::BN, C::NT / 64>, int>>::BYTES / 2;
+  constexpr int NW = C::NT / 64;
+  const int r = worker_of_block(a.P);
+  const int n2m = a.d / C::BM, n2n = a.dff / C::BN;          // dW2 [d][dff]
+  const int n1m = 2 * a.dff / C::BM, n1n = a.d / C::BN;      // dW1 [2dff][d]
+  const int per_seg = n2m * n2n + n1m * n1n;
+  const int total = a.seg_cnt[r] * per_seg;
+  const size_t w_elems = (size_t)3 * a.d * a.dff;
+  const uint16_t* DY = (const uint16_t*)a.dy;
+  const uint16_t* X = (const uint16_t*)a.x;
+  const uint16_t* PA = (const uint16_t*)a.bufP;
+  const uint16_t* dZ = (const uint16_t*)a.bufA;
+  const MnDma<C::BM, NW> mna{a.zero};
+  const MnDma<C::BN, NW> mnb{a.zero};
+  while (true) {
+    const int tile = next_tile(&a.ctr[PH_DW * kMaxP + r], &tslot);
+    if (tile >= total) break;
+    const int4 sg = a.seg[(size_t)r * a.E + tile / per_seg];
+    const int e = sg.x, slot0 = sg.y, nrows = sg.z, dst = sg.w;
+    if (e < 0) continue;
+    const int loc = tile % per_seg;
+    const bool is2 = loc < n2m * n2n;
+    const int mi = is2 ? loc / n2n : (loc - n2m * n2n) / n1n;
+    const int nj = is2 ? loc % n2n : (loc - n2m * n2n) % n1n;
+    f32x16_t acc[C::MB][C::NB];
+    for (int w0 = 0; w0 < nrows; w0 += kTokTab) {
+      const int wrows = min(kTokTab, nrows - w0);
+      const int s0 = slot0 + w0;
+      __syncthreads();                       // previous users of the table are done
+      for (int i = threadIdx.x; i < wrows; i += C::NT) tok[i] = (uint16_t)(a.slot_to_row[s0 + i] / a.k);
+      __syncthreads();
+      const int nk = (wrows + kDmaBK - 1) / kDmaBK;
+      const bool more = w0 > 0;
+      if (is2) {
+        auto oa = mn_operand(mna, [&](int k) -> const uint16_t* {
+          return k < wrows ? DY + (size_t)tok[k] * a.d + mi * C::BM : nullptr; });
+        auto ob = mn_operand(mnb, [&](int k) -> const uint16_t* {
+          return k < wrows ? PA + ((size_t)s0 + k) * a.dff + nj * C::BN : nullptr; });
+        gemm_tile_dma<C>(oa, ob, nk, smem, acc, more);
+      } else {
+        auto oa = mn_operand(mna, [&](int k) -> const uint16_t* {
+          return k < wrows ? dZ + ((size_t)s0 + k) * 2 * a.dff + mi * C::BM : nullptr; });
+        auto ob = mn_operand(mnb, [&](int k) -> const uint16_t* {
+          return k < wrows ? X + (size_t)tok[k] * a.d + nj * C::BN : nullptr; });
+        gemm_tile_dma<C>(oa, ob, nk, smem, acc, more);
+      }
+    }
+    float* out;
+    int ldo;
+    if (is2) {
+      out = (dst < 0 ? a.dw2 + (size_t)e * a.d * a.dff
+                     : a.rslots + (size_t)dst * w_elems + (size_t)2 * a.dff * a.d);
+      ldo = a.dff;
+    } else {
+      out = (dst < 0 ? a.dw1 + (size_t)e * 2 * a.dff * a.d : a.rslots + (size_t)dst * w_elems);
+      ldo = a.d;
+    }
+    constexpr int PASS = 128, LDD = C::BN + 4;
+    MOE_LDS float* sd = (MOE_LDS float*)smem;
+    for (int p0 = 0; p0 < C::BM; p0 += PASS) {
+      if (p0) __syncthreads();
+      acc_to_lds<C>(acc, sd, LDD, p0, PASS, [](float v, int, int) { return v; });
+      __syncthreads();
+      lds_to_global<float, C::NT>(sd, PASS, C::BN, LDD, [&](int rl, int col, const V16& v) {
+        stg16(out + ((size_t)mi * C::BM + p0 + rl) * ldo + nj * C::BN + col, v.u);
+      });
+    }
+  }
+}
+
 // Owner slot <- (owner partial or 0) + replica partials in ascending worker
 // order, fp32.  Experts with an owner partial and no replica are untouched.
 // The per-expert table is staged in LDS once per workgroup.
@@ -711,6 +802,8 @@ WsLayout exec_layout(const Sizes& z, bool backward) {
   L.bufA = take((size_t)z.act_bytes * z.max_slots * (backward ? 2 : 1) * z.dff);
   L.bufO = take((size_t)z.act_bytes * z.max_slots * z.d);
   L.rslots = backward ? take(sizeof(float) * (size_t)z.P * z.s * 3 * z.d * z.dff) : o;
+  L.bufP = backward ? take((size_t)z.act_bytes * z.max_slots * z.dff) : o;
+  L.zero = take(256);
   L.total = o;
   return L;
 }
@@ -778,6 +871,7 @@ static void launch_sched(const Sizes& z, const int32_t* counts, const int32_t* b
   s.rep_slot = (int32_t*)(ws + L.rep_slot);
   s.owner_has = (int32_t*)(ws + L.owner_has);
   s.status = status;
+  s.zero = (int32_t*)(ws + L.zero);
   const size_t lds = sched_lds(z, bwd);
   (void)hipFuncSetAttribute((const void*)k_sched, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)sched_lds(z, true));
@@ -799,6 +893,8 @@ static ExecArgs make_exec(const Sizes& z, const LayerPtrs& Lp, char* ws, const W
   a.bufA = ws + L.bufA;
   a.bufO = ws + L.bufO;
   a.rslots = (float*)(ws + L.rslots);
+  a.bufP = ws + L.bufP;
+  a.zero = (const uint16_t*)(ws + L.zero);
   return a;
 }
 
@@ -842,10 +938,41 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+// The direct-to-LDS backward needs 256-multiples for d and d_ff (tile extents)
+// and token indices that fit the 16-bit LDS table.
+bool use_dma_backward(const Sizes& z) {
+  return use_big_tiles(z) && z.dff % 256 == 0 && z.T <= 65535;
+}
+
+template <class C>
+static void run_backward_dma(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* dx,
+                             float* dw1, float* dw2, void* const* ev, hipStream_t st) {
+  const size_t glds = gemm_lds_bytes<uint16_t, C>();
+  const size_t wlds = (size_t)kDmaStages * (32 * C::BM + 32 * C::BN) * 2 + (size_t)kTokTab * 2;
+  static int ga = persistent_grid(k_bwd_da<uint16_t, C>, C::NT, glds);
+  static int gx = persistent_grid(k_bwd_dx<uint16_t, C>, C::NT, glds);
+  static int gw = persistent_grid(k_bwd_dw_dma<C>, C::NT, wlds);
+  hipLaunchKernelGGL((k_bwd_da<uint16_t, C>), dim3(ga), dim3(C::NT), glds, st, a);
+  rec(ev, 2, st);
+  hipLaunchKernelGGL((k_bwd_dx<uint16_t, C>), dim3(gx), dim3(C::NT), glds, st, a);
+  rec(ev, 3, st);
+  const long long nth = (long long)z.T * (z.d / 8);
+  if (nth > 0)
+    hipLaunchKernelGGL(k_combine<uint16_t>, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, st,
+                       (const uint16_t*)a.bufO, row_to_slot, z.T, z.k, z.d, (uint16_t*)dx);
+  rec(ev, 4, st);
+  hipLaunchKernelGGL(k_bwd_dw_dma<C>, dim3(gw), dim3(C::NT), wlds, st, a);
+  rec(ev, 5, st);
+  hipLaunchKernelGGL(k_bwd_reduce, dim3(num_cus() * 4), dim3(256), 0, st, a.rep_slot,
+                     a.owner_has, (const float*)a.rslots, z.E, z.P, z.d, z.dff, dw1, dw2);
+  rec(ev, 6, st);
+}
+
 template <typename T, class C>
 static void run_backward(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* dx,
                          float* dw1, float* dw2, void* const* ev, hipStream_t st) {
-  const size_t lds = TileLds<T, C>::BYTES;
+  a.bufP = nullptr;
+  const size_t lds = gemm_lds_bytes<T, C>();
   static int ga = persistent_grid(k_bwd_da<T, C>, C::NT, lds);
   static int gx = persistent_grid(k_bwd_dx<T, C>, C::NT, lds);
   static int gw = persistent_grid(k_bwd_dw<T, C>, C::NT, lds);
@@ -880,6 +1007,7 @@ int launch_backward(const Sizes& z, const LayerPtrs& Lp, const void* x, const fl
   a.z_save = const_cast<void*>(z_save);
   a.dy = dy; a.dw1 = dw1; a.dw2 = dw2;
   if (Lp.act_dtype == MOE_F32) run_backward<float, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
+  else if (use_dma_backward(z)) run_backward_dma<BigCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else if (use_big_tiles(z)) run_backward<uint16_t, BigCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else run_backward<uint16_t, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;

@@ -390,6 +390,12 @@ MOE_DEV int dma_swz(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row >> 
 
 template <int ROWS, int NWAVES> struct RowDma {
   static constexpr int NI = ROWS / 16 / NWAVES;     // load instructions per wave per step
+  static constexpr int STAGE_ELEMS = ROWS * 32;
+  // MFMA operand fragment: rows row0 .. row0+31 (lane & 31), K chunk kc of the stage
+  static MOE_DEV bf16x8_t frag(const MOE_LDS uint16_t* st, int row0, int kc, int lane) {
+    const int row = row0 + (lane & 31);
+    return *(const MOE_LDS bf16x8_t*)(st + row * 32 + dma_swz(row, kc * 2 + (lane >> 5)) * 8);
+  }
   const uint16_t* base;
   int off[NI];                                      // element offset of this lane's chunk
   template <class F> MOE_DEV void init(const uint16_t* b, F rowoff) {
@@ -413,35 +419,71 @@ template <int ROWS, int NWAVES> struct RowDma {
   }
 };
 
+// MN-contiguous operand (the K index walks source rows, M or N is contiguous):
+// a stage holds 32 K rows x MN elements in their natural layout, [k][mn], 16-byte
+// chunks XOR-swizzled by 2 * (k % 8).  MFMA fragments come from
+// ds_read_b64_tr_b16: inside each 16-lane group, lane j supplies the address of
+// row k0 + j/4, columns m0 + 4 (j % 4) .. +3 and receives column m0 + j of rows
+// k0 .. k0+3, i.e. four consecutive K values of one M/N index; two such reads
+// give the eight K values an MFMA lane needs.
+// rowptr(k) returns the element pointer of (source row of stage row k, mn0) or
+// nullptr for a row that must read as zeros (it then reads `zero`, a zeroed
+// 16-byte-aligned block in global memory).
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+MOE_DEV int mn_swz(int row) { return (row & 7) << 1; }
+
+template <int MN, int NWAVES> struct MnDma {
+  static constexpr int ROWB = MN * 2;               // bytes per stage row
+  static constexpr int RPI = 1024 / ROWB;           // rows per wave load instruction
+  static constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
+  static constexpr int NI = 32 / RPI / NWAVES;      // load instructions per wave per step
+  static constexpr int STAGE_ELEMS = 32 * MN;
+  static_assert(NI * RPI * NWAVES == 32, "32 K rows per stage");
+  const uint16_t* zero;
+  template <class F> MOE_DEV void issue_rows(int kt, MOE_LDS uint16_t* st, F rowptr) const {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int q = w + NWAVES * i;
+      const int r = q * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ mn_swz(r);
+      const uint16_t* src = rowptr(kt * 32 + r);
+      const uint16_t* g = src ? src + c * 8 : zero;
+      __builtin_amdgcn_global_load_lds((const MOE_GLB void*)g,
+                                       (MOE_LDS void*)(st + q * RPI * MN), 16, 0, 0);
+    }
+  }
+  static MOE_DEV bf16x8_t frag(const MOE_LDS uint16_t* st, int mn_base, int kc, int lane) {
+    const int G = lane >> 4, j = lane & 15;
+    const int row = kc * 16 + 8 * (G >> 1) + (j >> 2);
+    const int m = mn_base + 16 * (G & 1) + 4 * (j & 3);
+    const int c = m >> 3, within = m & 7;
+    const MOE_LDS uint16_t* p0 = st + row * MN + ((c ^ mn_swz(row)) << 3) + within;
+    const MOE_LDS uint16_t* p1 = st + (row + 4) * MN + ((c ^ mn_swz(row + 4)) << 3) + within;
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS s16x4_t*)p0);
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS s16x4_t*)p1);
+    typedef short s16x8_t __attribute__((ext_vector_type(8)));
+    const s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
+};
+
+// A loader bound to its row function, with the interface the pipeline uses.
+template <class OP, class F> struct MnOperand {
+  const OP& op;
+  F rowptr;
+  static constexpr int NI = OP::NI, STAGE_ELEMS = OP::STAGE_ELEMS;
+  MOE_DEV void issue(int kt, MOE_LDS uint16_t* st) const { op.issue_rows(kt, st, rowptr); }
+  static MOE_DEV bf16x8_t frag(const MOE_LDS uint16_t* st, int b, int kc, int lane) {
+    return OP::frag(st, b, kc, lane);
+  }
+};
+template <class OP, class F> MOE_DEV MnOperand<OP, F> mn_operand(const OP& op, F f) { return {op, f}; }
+
 template <int N> MOE_DEV void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
-
-template <class C> struct DmaFrags {
-  bf16x8_t a[C::MB], b[C::NB];
-  MOE_DEV void read(const MOE_LDS uint16_t* sA, const MOE_LDS uint16_t* sB, int kc, int lane) {
-    const int wm = wave_id() / C::WAVES_N, wn = wave_id() % C::WAVES_N;
-    const int ch = kc * 2 + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < C::MB; ++i) {
-      const int row = wm * C::WM + i * 32 + (lane & 31);
-      a[i] = *(const MOE_LDS bf16x8_t*)(sA + row * 32 + dma_swz(row, ch) * 8);
-    }
-#pragma unroll
-    for (int j = 0; j < C::NB; ++j) {
-      const int row = wn * C::WN + j * 32 + (lane & 31);
-      b[j] = *(const MOE_LDS bf16x8_t*)(sB + row * 32 + dma_swz(row, ch) * 8);
-    }
-  }
-  MOE_DEV void mma(f32x16_t (&acc)[C::MB][C::NB]) const {
-#pragma unroll
-    for (int i = 0; i < C::MB; ++i)
-#pragma unroll
-      for (int j = 0; j < C::NB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
-};
 
 template <class C> struct DmaCfg {
   static constexpr int STAGE_A = C::BM * 32, STAGE_B = C::BN * 32;   // elements
@@ -464,57 +506,86 @@ template <int N> MOE_DEV void wait_vm_lgkm0() {
 // Loads past the last step re-read step nk-1 into stages nobody reads again,
 // so every step has the same shape and the same wait counts.
 // sched_barrier pins each fragment read ahead of the 16 MFMAs that hide it.
-template <class C>
-MOE_DEV void gemm_tile_dma(const RowDma<C::BM, C::NT / 64>& la, const RowDma<C::BN, C::NT / 64>& lb,
-                           int nk, MOE_LDS uint16_t* smem, f32x16_t (&acc)[C::MB][C::NB]) {
-  using D = DmaCfg<C>;
-  constexpr int LPS = D::LPS;
-  const int lane = threadIdx.x & 63;
+// OA / OB: operand objects with issue(step, stage) and a static
+// frag(stage, row0, kc, lane) (RowDma, or an MnOperand).
+template <class C, class OA, class OB> struct DmaPipe {
+  static constexpr int STAGE_A = OA::STAGE_ELEMS, STAGE = OA::STAGE_ELEMS + OB::STAGE_ELEMS;
+  static constexpr int LPS = OA::NI + OB::NI;
+  static constexpr size_t BYTES = (size_t)kDmaStages * STAGE * 2;
+  bf16x8_t a0[C::MB], b0[C::NB], a1[C::MB], b1[C::NB];
+  MOE_DEV void read(bf16x8_t (&a)[C::MB], bf16x8_t (&b)[C::NB], const MOE_LDS uint16_t* st, int kc,
+                    int lane) {
+    const int wm = wave_id() / C::WAVES_N, wn = wave_id() % C::WAVES_N;
 #pragma unroll
-  for (int i = 0; i < C::MB; ++i)
+    for (int i = 0; i < C::MB; ++i) a[i] = OA::frag(st, wm * C::WM + i * 32, kc, lane);
 #pragma unroll
-    for (int j = 0; j < C::NB; ++j)
+    for (int j = 0; j < C::NB; ++j) b[j] = OB::frag(st + STAGE_A, wn * C::WN + j * 32, kc, lane);
+  }
+  static MOE_DEV void mma(f32x16_t (&acc)[C::MB][C::NB], const bf16x8_t (&a)[C::MB],
+                          const bf16x8_t (&b)[C::NB]) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  if (nk <= 0) return;
-  __syncthreads();                      // the previous tile's epilogue is done with the LDS
-  auto issue = [&](int step, MOE_LDS uint16_t* st) {
-    const int kk = step < nk ? step : nk - 1;
-    la.issue(kk, st);
-    lb.issue(kk, st + D::STAGE_A);
-  };
+    for (int i = 0; i < C::MB; ++i)
 #pragma unroll
-  for (int s = 0; s < kDmaStages; ++s) issue(s, smem + s * D::STAGE);
-  wait_vm_lgkm0<3 * LPS>();
-  __builtin_amdgcn_s_barrier();
-  DmaFrags<C> f0, f1;
-  f0.read(smem, smem + D::STAGE_A, 0, lane);
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    const MOE_LDS uint16_t* sA = smem + (kt % kDmaStages) * D::STAGE;
-    const MOE_LDS uint16_t* nA = smem + ((kt + 1) % kDmaStages) * D::STAGE;
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): chunk-0 fragments are in
-    __builtin_amdgcn_sched_barrier(0);
-    f1.read(sA, sA + D::STAGE_A, 1, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    f0.mma(acc);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vm_lgkm0<2 * LPS>();
+      for (int j = 0; j < C::NB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+  MOE_DEV void run(const OA& oa, const OB& ob, int nk, MOE_LDS uint16_t* smem,
+                   f32x16_t (&acc)[C::MB][C::NB], bool accumulate = false) {
+    const int lane = threadIdx.x & 63;
+    if (!accumulate) {
+#pragma unroll
+      for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NB; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    }
+    if (nk <= 0) return;
+    __syncthreads();                      // the previous tile's epilogue is done with the LDS
+    auto issue = [&](int step, MOE_LDS uint16_t* st) {
+      const int kk = step < nk ? step : nk - 1;
+      oa.issue(kk, st);
+      ob.issue(kk, st + STAGE_A);
+    };
+#pragma unroll
+    for (int s = 0; s < kDmaStages; ++s) issue(s, smem + s * STAGE);
+    wait_vm_lgkm0<3 * LPS>();
     __builtin_amdgcn_s_barrier();
-    issue(kt + kDmaStages, smem + (kt % kDmaStages) * D::STAGE);
-    f0.read(nA, nA + D::STAGE_A, 0, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    f1.mma(acc);
-    __builtin_amdgcn_sched_barrier(0);
+    read(a0, b0, smem, 0, lane);
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      const MOE_LDS uint16_t* sA = smem + (kt % kDmaStages) * STAGE;
+      const MOE_LDS uint16_t* nA = smem + ((kt + 1) % kDmaStages) * STAGE;
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): chunk-0 fragments are in
+      __builtin_amdgcn_sched_barrier(0);
+      read(a1, b1, sA, 1, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(acc, a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm_lgkm0<2 * LPS>();
+      __builtin_amdgcn_s_barrier();
+      issue(kt + kDmaStages, smem + (kt % kDmaStages) * STAGE);
+      read(a0, b0, nA, 0, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(acc, a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    {
+      const MOE_LDS uint16_t* sA = smem + ((nk - 1) % kDmaStages) * STAGE;
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      read(a1, b1, sA, 1, lane);
+      mma(acc, a0, b0);
+      mma(acc, a1, b1);
+    }
+    wait_vm_lgkm0<0>();
+    __syncthreads();                      // all loads landed, all waves done with the stages
   }
-  {
-    const MOE_LDS uint16_t* sA = smem + ((nk - 1) % kDmaStages) * D::STAGE;
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    f1.read(sA, sA + D::STAGE_A, 1, lane);
-    f0.mma(acc);
-    f1.mma(acc);
-  }
-  wait_vm_lgkm0<0>();
-  __syncthreads();                      // all loads landed, all waves done with the stages
+};
+
+template <class C, class OA, class OB>
+MOE_DEV void gemm_tile_dma(const OA& oa, const OB& ob, int nk, MOE_LDS uint16_t* smem,
+                           f32x16_t (&acc)[C::MB][C::NB], bool accumulate = false) {
+  DmaPipe<C, OA, OB> p;
+  p.run(oa, ob, nk, smem, acc, accumulate);
 }
 
 // Coordinates of accumulator register r of block (i, j) for this lane, within
