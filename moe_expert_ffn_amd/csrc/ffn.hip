@@ -35,7 +35,6 @@ struct SchedArgs {
   int32_t* rep_slot;
   int32_t* owner_has;
   int32_t* status;
-  int32_t* zero;
 };
 
 MOE_DEV int expert_of(int g, const int* boff_s, int E) {
@@ -72,7 +71,6 @@ __global__ __launch_bounds__(256) void k_sched(SchedArgs a) {
   for (int i = tid; i <= E; i += 256) boff_s[i] = a.boff[i];
   for (int i = tid; i < E; i += 256) cnt_s[i] = a.counts[i];
   if (tid < kNumCounters) a.ctr[tid] = 0;
-  if (tid < 64) a.zero[tid] = 0;
   if (a.backward)
     for (int i = tid; i < E * P; i += 256) { s0_s[i] = INT_MAX; rows_s[i] = 0; starts_s[i] = 0; }
   __syncthreads();
@@ -211,7 +209,7 @@ struct ExecArgs {
   float* dw2;
   float* rslots;
   void* bufP;             // backward: P = p * SiLU(G) * U per routed row
-  const uint16_t* zero;   // 256 zero bytes in global memory
+  size_t slots;           // padded slot capacity (rows of bufA, bufO, bufP, z_save)
 };
 
 enum { PH_FC1 = 0, PH_FC2 = 1, PH_DA = 2, PH_DX = 3, PH_DW = 4 };
@@ -266,9 +264,11 @@ __global__ __launch_bounds__(C::NT) void k_fc1(ExecArgs a) {
     const int nk = a.d / Elem<T>::BK;
     if constexpr (kUseDma<T, FP8, C>) {
       RowDma<C::BM, C::NT / 64> da;
-      da.init(X, [&](int row) { return row < nrows ? (a.slot_to_row[slot0 + row] / a.k) * a.d : -1; });
+      da.init(X, (uint32_t)((size_t)a.T * a.d * 2),
+              [&](int row) { return row < nrows ? (a.slot_to_row[slot0 + row] / a.k) * a.d : -1; });
       RowDma<C::BN, C::NT / 64> db;
-      db.init((const uint16_t*)a.w1 + (size_t)e * 2 * a.dff * a.d, [&](int rho) { return w1row(rho) * a.d; });
+      db.init((const uint16_t*)a.w1 + (size_t)e * 2 * a.dff * a.d, (uint32_t)((size_t)4 * a.dff * a.d),
+              [&](int rho) { return w1row(rho) * a.d; });
       gemm_tile_dma<C>(da, db, a.d / kDmaBK, smem, acc);
     } else if constexpr (FP8) {
       RowLoadFp8<C::BN, C::NT> lb;
@@ -352,10 +352,11 @@ __global__ __launch_bounds__(C::NT) void k_fc2(ExecArgs a) {
     const int nk = a.dff / Elem<T>::BK;
     if constexpr (kUseDma<T, FP8, C>) {
       RowDma<C::BM, C::NT / 64> da;
-      da.init((const uint16_t*)Ab + (size_t)slot0 * a.dff, [&](int row) { return row < nrows ? row * a.dff : -1; });
+      da.init((const uint16_t*)Ab, (uint32_t)(a.slots * a.dff * 2),
+              [&](int row) { return row < nrows ? (slot0 + row) * a.dff : -1; });
       RowDma<C::BN, C::NT / 64> db;
-      db.init((const uint16_t*)a.w2 + (size_t)e * a.d * a.dff + (size_t)nj * C::BN * a.dff,
-              [&](int rho) { return rho * a.dff; });
+      db.init((const uint16_t*)a.w2 + (size_t)e * a.d * a.dff, (uint32_t)((size_t)2 * a.d * a.dff),
+              [&](int rho) { return (nj * C::BN + rho) * a.dff; });
       gemm_tile_dma<C>(da, db, a.dff / kDmaBK, smem, acc);
     } else if constexpr (FP8) {
       RowLoadFp8<C::BN, C::NT> lb;
@@ -656,20 +657,48 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dw(ExecArgs a) {
   }
 }
 
-// ---- weight gradients on the direct-to-LDS pipeline (bf16, d and d_ff multiples of 256) --
+// ---- weight gradients on the direct-to-LDS pipeline, two workgroups per CU ------
 // Weight gradients per (expert, worker) segment; K = the segment's routed rows,
-// in windows of up to kTokTab rows whose token indices sit in an LDS table.
+// in windows of up to kTokWin rows whose token indices sit in an LDS table.
 // dW2[c, n] = sum dy_t[c] * P[n];  dW1[j, c] = sum dZ[j] * x_t[c].
 // Every operand is read in its natural [row][feature] layout through transpose
-// reads; rows past the segment read the zero block.
-constexpr int kTokTab = 8192;
+// reads; rows past the segment read as zeros.  Tiles are 256 (M) x 128
+// (N) with transposed accumulators: each lane stores 16-byte runs of one fp32
+// output row directly, and the other workgroup on the CU computes meanwhile.
+constexpr int kTokWin = 2048;
+// Byte offset of (source row of K index k, col) in one operand: a gathered
+// token row (token index from the LDS table) or a slot row; kOob past the
+// window, which reads as zeros.
+// The table is read unconditionally and the row picked arithmetically
+// (g = 1: gathered, 0: slot row) so the reads of one step are all in flight
+// together instead of each behind a branch.
+struct DwRows {
+  const MOE_LDS uint16_t* tok;
+  int wrows, s0, ld, col;
+  uint32_t g;
+  MOE_DEV uint32_t operator()(int k) const {
+    const int kk = min(k, wrows - 1);
+    const uint32_t t = tok[kk];
+    const uint32_t row = t * g + (uint32_t)(s0 + kk) * (1u - g);
+    const uint32_t o = (row * (uint32_t)ld + (uint32_t)col) * 2u;
+    return k < wrows ? o : kOob;
+  }
+};
+template <class C> struct DwDual {
+  static constexpr int NW = C::NT / 64;
+  using OA = MnOperand<MnDma<C::BM, NW>, DwRows>;
+  using OB = MnOperand<MnDma<C::BN, NW>, DwRows>;
+  using Pipe = DmaPipe<C, OA, OB, kDualStages, true>;
+  static constexpr size_t STAGE_BYTES = Pipe::BYTES;
+  static constexpr size_t LDS_BYTES = STAGE_BYTES + (size_t)kTokWin * 2;
+};
+
 template <class C>
-__global__ __launch_bounds__(C::NT) void k_bwd_dw_dma(ExecArgs a) {
+__global__ __launch_bounds__(C::NT, 2) void k_bwd_dw_dual(ExecArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int tslot;
   MOE_LDS uint16_t* smem = (MOE_LDS uint16_t*)smem_raw;
-  MOE_LDS uint16_t* tok = smem + DmaPipe<C, MnOperand<MnDma<C::BM, C::NT / 64>, int>,
-                                         MnOperand<MnDma<C::BN, C::NT / 64>, int>>::BYTES / 2;
+  MOE_LDS uint16_t* tok = smem + DwDual<C>::STAGE_BYTES / 2;
   constexpr int NW = C::NT / 64;
   const int r = worker_of_block(a.P);
   const int n2m = a.d / C::BM, n2n = a.dff / C::BN;          // dW2 [d][dff]
@@ -677,12 +706,11 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dw_dma(ExecArgs a) {
   const int per_seg = n2m * n2n + n1m * n1n;
   const int total = a.seg_cnt[r] * per_seg;
   const size_t w_elems = (size_t)3 * a.d * a.dff;
-  const uint16_t* DY = (const uint16_t*)a.dy;
-  const uint16_t* X = (const uint16_t*)a.x;
-  const uint16_t* PA = (const uint16_t*)a.bufP;
-  const uint16_t* dZ = (const uint16_t*)a.bufA;
-  const MnDma<C::BM, NW> mna{a.zero};
-  const MnDma<C::BN, NW> mnb{a.zero};
+  const uint32_t bx = (uint32_t)((size_t)a.T * a.d * 2);
+  const BufRsrc r_dy = make_rsrc(a.dy, bx), r_x = make_rsrc(a.x, bx);
+  const BufRsrc r_dz = make_rsrc(a.bufA, (uint32_t)(a.slots * 4 * a.dff));
+  const BufRsrc r_p = make_rsrc(a.bufP, (uint32_t)(a.slots * 2 * a.dff));
+  const int lane = threadIdx.x & 63;
   while (true) {
     const int tile = next_tile(&a.ctr[PH_DW * kMaxP + r], &tslot);
     if (tile >= total) break;
@@ -693,28 +721,22 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dw_dma(ExecArgs a) {
     const bool is2 = loc < n2m * n2n;
     const int mi = is2 ? loc / n2n : (loc - n2m * n2n) / n1n;
     const int nj = is2 ? loc % n2n : (loc - n2m * n2n) % n1n;
+    // dW2 = dy^T P (A: gathered dy rows, B: P rows);  dW1 = dZ^T x (A: dZ rows, B: gathered x rows)
+    const MnDma<C::BM, NW> ma{is2 ? r_dy : r_dz};
+    const MnDma<C::BN, NW> mb{is2 ? r_p : r_x};
     f32x16_t acc[C::MB][C::NB];
-    for (int w0 = 0; w0 < nrows; w0 += kTokTab) {
-      const int wrows = min(kTokTab, nrows - w0);
+    for (int w0 = 0; w0 < nrows; w0 += kTokWin) {
+      const int wrows = min(kTokWin, nrows - w0);
       const int s0 = slot0 + w0;
       __syncthreads();                       // previous users of the table are done
       for (int i = threadIdx.x; i < wrows; i += C::NT) tok[i] = (uint16_t)(a.slot_to_row[s0 + i] / a.k);
       __syncthreads();
-      const int nk = (wrows + kDmaBK - 1) / kDmaBK;
-      const bool more = w0 > 0;
-      if (is2) {
-        auto oa = mn_operand(mna, [&](int k) -> const uint16_t* {
-          return k < wrows ? DY + (size_t)tok[k] * a.d + mi * C::BM : nullptr; });
-        auto ob = mn_operand(mnb, [&](int k) -> const uint16_t* {
-          return k < wrows ? PA + ((size_t)s0 + k) * a.dff + nj * C::BN : nullptr; });
-        gemm_tile_dma<C>(oa, ob, nk, smem, acc, more);
-      } else {
-        auto oa = mn_operand(mna, [&](int k) -> const uint16_t* {
-          return k < wrows ? dZ + ((size_t)s0 + k) * 2 * a.dff + mi * C::BM : nullptr; });
-        auto ob = mn_operand(mnb, [&](int k) -> const uint16_t* {
-          return k < wrows ? X + (size_t)tok[k] * a.d + nj * C::BN : nullptr; });
-        gemm_tile_dma<C>(oa, ob, nk, smem, acc, more);
-      }
+      uint32_t ga = __builtin_amdgcn_readfirstlane(is2 ? 1u : 0u);
+      asm volatile("" : "+s"(ga));           // opaque: keeps the select arithmetic
+      const DwRows ra{tok, wrows, s0, is2 ? a.d : 2 * a.dff, mi * C::BM, ga};
+      const DwRows rb{tok, wrows, s0, is2 ? a.dff : a.d, nj * C::BN, 1u - ga};
+      typename DwDual<C>::Pipe p;
+      p.run(mn_operand(ma, ra), mn_operand(mb, rb), (wrows + kDmaBK - 1) / kDmaBK, smem, acc, w0 > 0);
     }
     float* out;
     int ldo;
@@ -726,15 +748,17 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dw_dma(ExecArgs a) {
       out = (dst < 0 ? a.dw1 + (size_t)e * 2 * a.dff * a.d : a.rslots + (size_t)dst * w_elems);
       ldo = a.d;
     }
-    constexpr int PASS = 128, LDD = C::BN + 4;
-    MOE_LDS float* sd = (MOE_LDS float*)smem;
-    for (int p0 = 0; p0 < C::BM; p0 += PASS) {
-      if (p0) __syncthreads();
-      acc_to_lds<C>(acc, sd, LDD, p0, PASS, [](float v, int, int) { return v; });
-      __syncthreads();
-      lds_to_global<float, C::NT>(sd, PASS, C::BN, LDD, [&](int rl, int col, const V16& v) {
-        stg16(out + ((size_t)mi * C::BM + p0 + rl) * ldo + nj * C::BN + col, v.u);
-      });
+    out += (size_t)mi * C::BM * ldo + (size_t)nj * C::BN;
+#pragma unroll
+    for (int i = 0; i < C::MB; ++i) {
+      float* orow = out + (size_t)acc_row_t<C>(i, lane) * ldo;
+#pragma unroll
+      for (int j = 0; j < C::NB; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          stg16(orow + acc_col_t<C>(j, g, lane),
+                make_uint4(__float_as_uint(acc[i][j][4 * g]), __float_as_uint(acc[i][j][4 * g + 1]),
+                           __float_as_uint(acc[i][j][4 * g + 2]), __float_as_uint(acc[i][j][4 * g + 3])));
     }
   }
 }
@@ -803,7 +827,6 @@ WsLayout exec_layout(const Sizes& z, bool backward) {
   L.bufO = take((size_t)z.act_bytes * z.max_slots * z.d);
   L.rslots = backward ? take(sizeof(float) * (size_t)z.P * z.s * 3 * z.d * z.dff) : o;
   L.bufP = backward ? take((size_t)z.act_bytes * z.max_slots * z.dff) : o;
-  L.zero = take(256);
   L.total = o;
   return L;
 }
@@ -871,7 +894,6 @@ static void launch_sched(const Sizes& z, const int32_t* counts, const int32_t* b
   s.rep_slot = (int32_t*)(ws + L.rep_slot);
   s.owner_has = (int32_t*)(ws + L.owner_has);
   s.status = status;
-  s.zero = (int32_t*)(ws + L.zero);
   const size_t lds = sched_lds(z, bwd);
   (void)hipFuncSetAttribute((const void*)k_sched, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)sched_lds(z, true));
@@ -894,7 +916,7 @@ static ExecArgs make_exec(const Sizes& z, const LayerPtrs& Lp, char* ws, const W
   a.bufO = ws + L.bufO;
   a.rslots = (float*)(ws + L.rslots);
   a.bufP = ws + L.bufP;
-  a.zero = (const uint16_t*)(ws + L.zero);
+  a.slots = z.max_slots;
   return a;
 }
 
@@ -938,20 +960,20 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
-// The direct-to-LDS backward needs 256-multiples for d and d_ff (tile extents)
-// and token indices that fit the 16-bit LDS table.
+// The direct-to-LDS weight gradients need 256 | d and 128 | d_ff (tile
+// extents) and token indices that fit the 16-bit LDS table.
 bool use_dma_backward(const Sizes& z) {
-  return use_big_tiles(z) && z.dff % 256 == 0 && z.T <= 65535;
+  return use_big_tiles(z) && z.dff % 128 == 0 && z.T <= 65535;
 }
 
 template <class C>
 static void run_backward_dma(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* dx,
                              float* dw1, float* dw2, void* const* ev, hipStream_t st) {
   const size_t glds = gemm_lds_bytes<uint16_t, C>();
-  const size_t wlds = (size_t)kDmaStages * (32 * C::BM + 32 * C::BN) * 2 + (size_t)kTokTab * 2;
+  const size_t wlds = DwDual<DualCfg>::LDS_BYTES;
   static int ga = persistent_grid(k_bwd_da<uint16_t, C>, C::NT, glds);
   static int gx = persistent_grid(k_bwd_dx<uint16_t, C>, C::NT, glds);
-  static int gw = persistent_grid(k_bwd_dw_dma<C>, C::NT, wlds);
+  static int gw = persistent_grid(k_bwd_dw_dual<DualCfg>, DualCfg::NT, wlds);
   hipLaunchKernelGGL((k_bwd_da<uint16_t, C>), dim3(ga), dim3(C::NT), glds, st, a);
   rec(ev, 2, st);
   hipLaunchKernelGGL((k_bwd_dx<uint16_t, C>), dim3(gx), dim3(C::NT), glds, st, a);
@@ -961,7 +983,7 @@ static void run_backward_dma(const Sizes& z, ExecArgs& a, const int32_t* row_to_
     hipLaunchKernelGGL(k_combine<uint16_t>, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, st,
                        (const uint16_t*)a.bufO, row_to_slot, z.T, z.k, z.d, (uint16_t*)dx);
   rec(ev, 4, st);
-  hipLaunchKernelGGL(k_bwd_dw_dma<C>, dim3(gw), dim3(C::NT), wlds, st, a);
+  hipLaunchKernelGGL(k_bwd_dw_dual<DualCfg>, dim3(gw), dim3(DualCfg::NT), wlds, st, a);
   rec(ev, 5, st);
   hipLaunchKernelGGL(k_bwd_reduce, dim3(num_cus() * 4), dim3(256), 0, st, a.rep_slot,
                      a.owner_has, (const float*)a.rslots, z.E, z.P, z.d, z.dff, dw1, dw2);

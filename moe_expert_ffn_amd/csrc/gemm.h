@@ -386,36 +386,68 @@ MOE_DEV void gemm_tile_deep(LA la0, LB lb0, int nk, MOE_LDS T* smem, f32x16_t (&
 // (__syncthreads would wait for every load in flight).
 constexpr int kDmaStages = 4, kDmaBK = 32, kDmaRowBytes = 64;
 
+// Buffer resources: loads through a descriptor take a 32-bit byte offset per
+// lane (one register instead of a 64-bit address), and an offset at or past
+// the descriptor's size reads as zeros, which is how rows outside a segment
+// are padded.  Every buffer addressed this way is below 2 GiB.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+constexpr uint32_t kOob = 0x80000000u;            // any offset >= this reads zeros
+MOE_DEV BufRsrc make_rsrc(const void* base, uint32_t bytes) {
+  // word 3 = 0x00020000: raw 32-bit data format, the untyped-buffer setting on CDNA
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+MOE_DEV void buf_load_lds16(BufRsrc r, uint32_t off, MOE_LDS void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);
+}
+
 MOE_DEV int dma_swz(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row >> 3)) & 3); }
 
 template <int ROWS, int NWAVES> struct RowDma {
   static constexpr int NI = ROWS / 16 / NWAVES;     // load instructions per wave per step
   static constexpr int STAGE_ELEMS = ROWS * 32;
-  // MFMA operand fragment: rows row0 .. row0+31 (lane & 31), K chunk kc of the stage
-  static MOE_DEV bf16x8_t frag(const MOE_LDS uint16_t* st, int row0, int kc, int lane) {
-    const int row = row0 + (lane & 31);
-    return *(const MOE_LDS bf16x8_t*)(st + row * 32 + dma_swz(row, kc * 2 + (lane >> 5)) * 8);
+  // Fragment addresses.  Fragment i of a wave covers rows wave_base + 32 i ..
+  // +31 (lane & 31) and K chunk kc; wave_base is a multiple of 32, so the
+  // swizzle depends on the lane alone and the byte offset is
+  // (lane part ^ 32 kc) + 2048 i: one register per lane, the rest immediates.
+  struct Lane { uint32_t off; };
+  static MOE_DEV Lane lane_info(int wave_base, int lane) {
+    const int row = lane & 31;
+    return {(uint32_t)((wave_base + row) * kDmaRowBytes + dma_swz(row, lane >> 5) * 16)};
   }
-  const uint16_t* base;
-  int off[NI];                                      // element offset of this lane's chunk
-  template <class F> MOE_DEV void init(const uint16_t* b, F rowoff) {
-    base = b;
+  template <int KC>
+  static MOE_DEV bf16x8_t frag(const MOE_LDS uint16_t* st, const Lane& L, int i) {
+    const MOE_LDS char* p = (const MOE_LDS char*)st + ((L.off ^ (32u * KC)) + 32u * kDmaRowBytes * i);
+    return *(const MOE_LDS bf16x8_t*)p;
+  }
+  BufRsrc rs;
+  uint32_t off[NI];                                 // byte offset of this lane's chunk at K step 0
+  // rowoff(row) = element offset of the row's first element from b, or -1 for
+  // a row that reads as zeros; `bytes` = extent of the buffer at b.
+  template <class F> MOE_DEV void init(const uint16_t* b, uint32_t bytes, F rowoff) {
+    rs = make_rsrc(b, bytes);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int row = (w + NWAVES * i) * 16 + (lane >> 2);
       const int o = rowoff(row);
-      off[i] = (o < 0 ? 0 : o) + dma_swz(row, lane & 3) * 8;
+      off[i] = o < 0 ? kOob : (uint32_t)o * 2u + dma_swz(row, lane & 3) * 16u;
     }
   }
-  // issue this wave's loads of K step kt into the stage at `st` (LDS)
-  MOE_DEV void issue(int kt, MOE_LDS uint16_t* st) const {
+  // Offsets of this wave's loads of K step kt, then their issue into the
+  // stage at `st` (LDS).
+  struct Offs { uint32_t o[NI]; };
+  MOE_DEV Offs prep(int kt) const {
+    Offs q;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) q.o[i] = off[i] + (uint32_t)kt * kDmaRowBytes;
+    return q;
+  }
+  MOE_DEV void issue(const Offs& q, MOE_LDS uint16_t* st) const {
     const int w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      __builtin_amdgcn_global_load_lds(
-          (const MOE_GLB void*)(base + (size_t)(unsigned)off[i] + (size_t)kt * kDmaBK),
-          (MOE_LDS void*)(st + (w + NWAVES * i) * 16 * (kDmaRowBytes / 2)), 16, 0, 0);
+      buf_load_lds16(rs, q.o[i], (MOE_LDS void*)(st + (w + NWAVES * i) * 16 * (kDmaRowBytes / 2)));
   }
 };
 
@@ -426,9 +458,8 @@ template <int ROWS, int NWAVES> struct RowDma {
 // row k0 + j/4, columns m0 + 4 (j % 4) .. +3 and receives column m0 + j of rows
 // k0 .. k0+3, i.e. four consecutive K values of one M/N index; two such reads
 // give the eight K values an MFMA lane needs.
-// rowptr(k) returns the element pointer of (source row of stage row k, mn0) or
-// nullptr for a row that must read as zeros (it then reads `zero`, a zeroed
-// 16-byte-aligned block in global memory).
+// rowoff(k) returns the byte offset, inside the operand's buffer, of element
+// (source row of stage row k, mn0), or kOob for a row that reads as zeros.
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 MOE_DEV int mn_swz(int row) { return (row & 7) << 1; }
 
@@ -439,29 +470,59 @@ template <int MN, int NWAVES> struct MnDma {
   static constexpr int NI = 32 / RPI / NWAVES;      // load instructions per wave per step
   static constexpr int STAGE_ELEMS = 32 * MN;
   static_assert(NI * RPI * NWAVES == 32, "32 K rows per stage");
-  const uint16_t* zero;
-  template <class F> MOE_DEV void issue_rows(int kt, MOE_LDS uint16_t* st, F rowptr) const {
+  BufRsrc rs;
+  struct Offs { uint32_t o[NI]; };
+  template <class F> MOE_DEV Offs prep_rows(int kt, F rowoff) const {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    Offs p;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int q = w + NWAVES * i;
-      const int r = q * RPI + lane / CPR;
-      const int c = (lane % CPR) ^ mn_swz(r);
-      const uint16_t* src = rowptr(kt * 32 + r);
-      const uint16_t* g = src ? src + c * 8 : zero;
-      __builtin_amdgcn_global_load_lds((const MOE_GLB void*)g,
-                                       (MOE_LDS void*)(st + q * RPI * MN), 16, 0, 0);
+      const int r = (w + NWAVES * i) * RPI + lane / CPR;
+      const uint32_t c = (uint32_t)((lane % CPR) ^ mn_swz(r));
+      p.o[i] = rowoff(kt * 32 + r) + c * 16u;
     }
+    return p;
   }
-  static MOE_DEV bf16x8_t frag(const MOE_LDS uint16_t* st, int mn_base, int kc, int lane) {
+  MOE_DEV void issue(const Offs& p, MOE_LDS uint16_t* st) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      buf_load_lds16(rs, p.o[i], (MOE_LDS void*)(st + (w + NWAVES * i) * RPI * MN));
+  }
+  // Fragment addresses.  Lane j of 16-lane group G reads rows
+  // kc*16 + 8 (G >> 1) + j / 4 (+ 4 for the second read) at column
+  // wave_base + 32 i + 16 (G & 1) + 4 (j % 4).  The swizzle only moves 16-byte
+  // chunks inside bits 1..3 of the chunk index, which fragment i (4 i chunks,
+  // bits 2.. above the lane's own bits 0..1) never carries into, so
+  //   byte offset = (lane part ^ 64 i) + kc * 32 * MN,
+  // two registers per lane (one per read) and an XOR per fragment.
+  struct Lane { uint32_t off[2]; };
+  static MOE_DEV Lane lane_info(int wave_base, int lane) {
     const int G = lane >> 4, j = lane & 15;
-    const int row = kc * 16 + 8 * (G >> 1) + (j >> 2);
-    const int m = mn_base + 16 * (G & 1) + 4 * (j & 3);
+    const int m = wave_base + 16 * (G & 1) + 4 * (j & 3);
     const int c = m >> 3, within = m & 7;
-    const MOE_LDS uint16_t* p0 = st + row * MN + ((c ^ mn_swz(row)) << 3) + within;
-    const MOE_LDS uint16_t* p1 = st + (row + 4) * MN + ((c ^ mn_swz(row + 4)) << 3) + within;
-    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS s16x4_t*)p0);
-    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS s16x4_t*)p1);
+    Lane L;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 8 * (G >> 1) + (j >> 2) + 4 * h;
+      L.off[h] = (uint32_t)(row * MN + ((c ^ mn_swz(row)) << 3) + within) * 2u;
+    }
+    return L;
+  }
+  // The reads are issued from inline asm: the compiler treats the builtin as
+  // aliasing the direct-to-LDS loads in flight and would wait for all of them
+  // (vmcnt(0)) before every read, serialising the prefetch pipeline.  The
+  // pipeline orders the reads itself: each fragment is consumed only after an
+  // explicit lgkmcnt(0) wait, pinned by a scheduling barrier, and every
+  // fragment read is consumed.
+  template <int KC>
+  static MOE_DEV bf16x8_t frag(const MOE_LDS uint16_t* st, const Lane& L, int i) {
+    const MOE_LDS char* sb = (const MOE_LDS char*)st;
+    s16x4_t lo, hi;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                 : "=v"(lo) : "v"(sb + (L.off[0] ^ (64u * i))), "i"(KC * 32 * MN));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                 : "=v"(hi) : "v"(sb + (L.off[1] ^ (64u * i))), "i"(KC * 32 * MN));
     typedef short s16x8_t __attribute__((ext_vector_type(8)));
     const s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8_t, v);
@@ -471,11 +532,16 @@ template <int MN, int NWAVES> struct MnDma {
 // A loader bound to its row function, with the interface the pipeline uses.
 template <class OP, class F> struct MnOperand {
   const OP& op;
-  F rowptr;
+  F rowoff;
   static constexpr int NI = OP::NI, STAGE_ELEMS = OP::STAGE_ELEMS;
-  MOE_DEV void issue(int kt, MOE_LDS uint16_t* st) const { op.issue_rows(kt, st, rowptr); }
-  static MOE_DEV bf16x8_t frag(const MOE_LDS uint16_t* st, int b, int kc, int lane) {
-    return OP::frag(st, b, kc, lane);
+  using Lane = typename OP::Lane;
+  using Offs = typename OP::Offs;
+  MOE_DEV Offs prep(int kt) const { return op.prep_rows(kt, rowoff); }
+  MOE_DEV void issue(const Offs& p, MOE_LDS uint16_t* st) const { op.issue(p, st); }
+  static MOE_DEV Lane lane_info(int wave_base, int lane) { return OP::lane_info(wave_base, lane); }
+  template <int KC>
+  static MOE_DEV bf16x8_t frag(const MOE_LDS uint16_t* st, const Lane& L, int i) {
+    return OP::template frag<KC>(st, L, i);
   }
 };
 template <class OP, class F> MOE_DEV MnOperand<OP, F> mn_operand(const OP& op, F f) { return {op, f}; }
@@ -508,26 +574,33 @@ template <int N> MOE_DEV void wait_vm_lgkm0() {
 // sched_barrier pins each fragment read ahead of the 16 MFMAs that hide it.
 // OA / OB: operand objects with issue(step, stage) and a static
 // frag(stage, row0, kc, lane) (RowDma, or an MnOperand).
-template <class C, class OA, class OB> struct DmaPipe {
+template <class C, class OA, class OB, int STAGES = kDmaStages, bool SWAP = false>
+struct DmaPipe {
+  static_assert(STAGES >= 3, "at least three stages");
   static constexpr int STAGE_A = OA::STAGE_ELEMS, STAGE = OA::STAGE_ELEMS + OB::STAGE_ELEMS;
   static constexpr int LPS = OA::NI + OB::NI;
-  static constexpr size_t BYTES = (size_t)kDmaStages * STAGE * 2;
+  static constexpr size_t BYTES = (size_t)STAGES * STAGE * 2;
+  static_assert((STAGES - 1) * LPS < 64, "vmcnt range");
   bf16x8_t a0[C::MB], b0[C::NB], a1[C::MB], b1[C::NB];
-  MOE_DEV void read(bf16x8_t (&a)[C::MB], bf16x8_t (&b)[C::NB], const MOE_LDS uint16_t* st, int kc,
-                    int lane) {
-    const int wm = wave_id() / C::WAVES_N, wn = wave_id() % C::WAVES_N;
+  typename OA::Lane la;
+  typename OB::Lane lb;
+  template <int KC>
+  MOE_DEV void read(bf16x8_t (&a)[C::MB], bf16x8_t (&b)[C::NB], const MOE_LDS uint16_t* st) {
 #pragma unroll
-    for (int i = 0; i < C::MB; ++i) a[i] = OA::frag(st, wm * C::WM + i * 32, kc, lane);
+    for (int i = 0; i < C::MB; ++i) a[i] = OA::template frag<KC>(st, la, i);
 #pragma unroll
-    for (int j = 0; j < C::NB; ++j) b[j] = OB::frag(st + STAGE_A, wn * C::WN + j * 32, kc, lane);
+    for (int j = 0; j < C::NB; ++j) b[j] = OB::template frag<KC>(st + STAGE_A, lb, j);
   }
+  // SWAP: the N fragment is the MFMA's first operand, so accumulator block
+  // (i, j) holds the transposed 32 x 32 block: lane = row (M), registers = columns.
   static MOE_DEV void mma(f32x16_t (&acc)[C::MB][C::NB], const bf16x8_t (&a)[C::MB],
                           const bf16x8_t (&b)[C::NB]) {
 #pragma unroll
     for (int i = 0; i < C::MB; ++i)
 #pragma unroll
       for (int j = 0; j < C::NB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = SWAP ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0)
+                         : __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   }
   MOE_DEV void run(const OA& oa, const OB& ob, int nk, MOE_LDS uint16_t* smem,
                    f32x16_t (&acc)[C::MB][C::NB], bool accumulate = false) {
@@ -541,39 +614,53 @@ template <class C, class OA, class OB> struct DmaPipe {
           for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     }
     if (nk <= 0) return;
-    __syncthreads();                      // the previous tile's epilogue is done with the LDS
-    auto issue = [&](int step, MOE_LDS uint16_t* st) {
-      const int kk = step < nk ? step : nk - 1;
-      oa.issue(kk, st);
-      ob.issue(kk, st + STAGE_A);
-    };
+    la = OA::lane_info((wave_id() / C::WAVES_N) * C::WM, lane);
+    lb = OB::lane_info((wave_id() % C::WAVES_N) * C::WN, lane);
+    __syncthreads();                      // the previous tile's users of the LDS are done
+    // Load offsets of a step are computed (row tables read) well before the
+    // loads are issued, so issuing never waits on them.
 #pragma unroll
-    for (int s = 0; s < kDmaStages; ++s) issue(s, smem + s * STAGE);
-    wait_vm_lgkm0<3 * LPS>();
+    for (int s = 0; s < STAGES; ++s) {
+      const int kk = s < nk ? s : nk - 1;
+      const auto pa = oa.prep(kk);
+      const auto pb = ob.prep(kk);
+      oa.issue(pa, smem + s * STAGE);
+      ob.issue(pb, smem + s * STAGE + STAGE_A);
+    }
+    wait_vm_lgkm0<(STAGES - 1) * LPS>();
     __builtin_amdgcn_s_barrier();
-    read(a0, b0, smem, 0, lane);
+    read<0>(a0, b0, smem);
     for (int kt = 0; kt + 1 < nk; ++kt) {
-      const MOE_LDS uint16_t* sA = smem + (kt % kDmaStages) * STAGE;
-      const MOE_LDS uint16_t* nA = smem + ((kt + 1) % kDmaStages) * STAGE;
+      const MOE_LDS uint16_t* sA = smem + (kt % STAGES) * STAGE;
+      const MOE_LDS uint16_t* nA = smem + ((kt + 1) % STAGES) * STAGE;
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): chunk-0 fragments are in
       __builtin_amdgcn_sched_barrier(0);
-      read(a1, b1, sA, 1, lane);
+      read<1>(a1, b1, sA);
+      const int kn = kt + STAGES < nk ? kt + STAGES : nk - 1;
+      const auto pa = oa.prep(kn);
+      const auto pb = ob.prep(kn);
       __builtin_amdgcn_sched_barrier(0);
       mma(acc, a0, b0);
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm_lgkm0<2 * LPS>();
+      wait_vm_lgkm0<(STAGES - 2) * LPS>();
       __builtin_amdgcn_s_barrier();
-      issue(kt + kDmaStages, smem + (kt % kDmaStages) * STAGE);
-      read(a0, b0, nA, 0, lane);
+      oa.issue(pa, smem + (kt % STAGES) * STAGE);
+      ob.issue(pb, smem + (kt % STAGES) * STAGE + STAGE_A);
+      read<0>(a0, b0, nA);
       __builtin_amdgcn_sched_barrier(0);
       mma(acc, a1, b1);
       __builtin_amdgcn_sched_barrier(0);
     }
     {
-      const MOE_LDS uint16_t* sA = smem + ((nk - 1) % kDmaStages) * STAGE;
+      const MOE_LDS uint16_t* sA = smem + ((nk - 1) % STAGES) * STAGE;
       __builtin_amdgcn_s_waitcnt(0xC07F);
-      read(a1, b1, sA, 1, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      read<1>(a1, b1, sA);
+      __builtin_amdgcn_sched_barrier(0);
       mma(acc, a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_sched_barrier(0);
       mma(acc, a1, b1);
     }
     wait_vm_lgkm0<0>();
@@ -586,6 +673,25 @@ MOE_DEV void gemm_tile_dma(const OA& oa, const OB& ob, int nk, MOE_LDS uint16_t*
                            f32x16_t (&acc)[C::MB][C::NB], bool accumulate = false) {
   DmaPipe<C, OA, OB> p;
   p.run(oa, ob, nk, smem, acc, accumulate);
+}
+
+// ---- two workgroups per CU ----------------------------------------------------
+// 256 x 128 tiles, 4 waves of 128 x 64 (128 accumulator registers per lane), so
+// two workgroups share a CU (two waves per SIMD): one workgroup's epilogue
+// stores and pipeline bubbles overlap the other's MFMAs.  Three direct-to-LDS
+// stages (72 KB) per workgroup.  Accumulators are transposed (SWAP), so every
+// lane owns one output row and four consecutive columns per register quad and
+// stores straight from registers, with no LDS round trip.
+using DualCfg = GemmCfg<256, 128, 2, 2>;
+constexpr int kDualStages = 3;
+
+// Output position of accumulator quad g of block (i, j) in a SWAP tile:
+// row acc_row_t, columns acc_col_t .. +3.
+template <class C> MOE_DEV int acc_row_t(int i, int lane) {
+  return (wave_id() / C::WAVES_N) * C::WM + i * 32 + (lane & 31);
+}
+template <class C> MOE_DEV int acc_col_t(int j, int g, int lane) {
+  return (wave_id() % C::WAVES_N) * C::WN + j * 32 + 8 * g + 4 * (lane >> 5);
 }
 
 // Coordinates of accumulator register r of block (i, j) for this lane, within
