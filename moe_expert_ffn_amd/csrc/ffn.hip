@@ -541,6 +541,241 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dx(ExecArgs a) {
   }
 }
 
+// ---- two workgroups per CU: FC1, FC2, dA, dX -----------------------------------
+// 256-row M tiles of one (expert, worker) run, 128-wide N tiles, transposed
+// accumulators: lane (lane & 31) of wave (wm, wn) owns rows wm*128 + 32 i +
+// (lane & 31) and, per register quad g of block j, the four consecutive
+// columns wn*64 + 32 j + 8 g + 4 (lane >> 5) .. +3, stored straight from
+// registers.  Fast exp / reciprocal in the SiLU terms: their error is far
+// below the bf16 rounding of every value they feed.
+MOE_DEV float sigm(float g) { return __builtin_amdgcn_rcpf(1.f + __expf(-g)); }
+
+template <class C> MOE_DEV int dual_row(int i, int lane) { return acc_row_t<C>(i, lane); }
+template <class C> MOE_DEV int dual_col(int j, int g, int lane) { return acc_col_t<C>(j, g, lane); }
+
+// Dynamic LDS of the dual GEMM kernels: three stages of a 256-row and a
+// 128-row operand, 32 K values each.
+template <class C> constexpr size_t dual_lds_bytes() {
+  return (size_t)kDualStages * (C::BM + C::BN) * kDmaBK * 2;
+}
+
+// FC1 + SwiGLU.  N tile nj covers A columns [64 nj, 64 nj + 64): weight rows
+// alternate 32 G rows and the matching 32 U rows, so block j = 0 of a wave is
+// G and block j = 1 is U of the same 32 columns.
+template <class C>
+__global__ __launch_bounds__(C::NT, 2) void k_fc1_dual(ExecArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __shared__ int tslot;
+  MOE_LDS uint16_t* smem = (MOE_LDS uint16_t*)smem_raw;
+  constexpr int NW = C::NT / 64, HALF = C::BN / 2;
+  static_assert(C::NB == 2 && C::WN == 64, "one G block and one U block per wave");
+  const int r = worker_of_block(a.P);
+  const int nnt = a.dff / HALF;
+  const int total = a.mt_cnt[r] * nnt;
+  const int lane = threadIdx.x & 63;
+  const int wn = wave_id() % C::WAVES_N;
+  uint16_t* Ab = (uint16_t*)a.bufA;
+  uint16_t* Z = (uint16_t*)a.z_save;
+  const uint32_t bx = (uint32_t)((size_t)a.T * a.d * 2);
+  while (true) {
+    const int tile = next_tile(&a.ctr[PH_FC1 * kMaxP + r], &tslot);
+    if (tile >= total) break;
+    const int4 m = a.mt[(size_t)r * a.max_mt + tile / nnt];
+    const int nj = tile % nnt;
+    const int e = m.x, slot0 = m.y, nrows = m.z;
+    RowDma<C::BM, NW> da;
+    da.init((const uint16_t*)a.x, bx,
+            [&](int row) { return row < nrows ? (a.slot_to_row[slot0 + row] / a.k) * a.d : -1; });
+    RowDma<C::BN, NW> db;
+    db.init((const uint16_t*)a.w1 + (size_t)e * 2 * a.dff * a.d, (uint32_t)((size_t)4 * a.dff * a.d),
+            [&](int rho) {
+              const int q = rho >> 5;
+              return ((q & 1) * a.dff + nj * HALF + (q >> 1) * 32 + (rho & 31)) * a.d;
+            });
+    f32x16_t acc[C::MB][C::NB];
+    DmaPipe<C, RowDma<C::BM, NW>, RowDma<C::BN, NW>, kDualStages, true> p;
+    p.run(da, db, a.d / kDmaBK, smem, acc);
+    const int col0 = nj * HALF + wn * 32 + 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < C::MB; ++i) {
+      const int row = dual_row<C>(i, lane);
+      if (row >= nrows) continue;
+      const size_t sr = (size_t)slot0 + row;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float gv[4], uv[4], av[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          gv[q] = acc[i][0][4 * g + q];
+          uv[q] = acc[i][1][4 * g + q];
+          av[q] = gv[q] * sigm(gv[q]) * uv[q];
+        }
+        const int c = col0 + 8 * g;
+        store4(Ab + sr * a.dff + c, av);
+        if (Z) {
+          store4(Z + sr * 2 * a.dff + c, gv);
+          store4(Z + sr * 2 * a.dff + a.dff + c, uv);
+        }
+      }
+    }
+  }
+}
+
+// FC2 with the gate: O[slot] = p * A W2^T.
+template <class C>
+__global__ __launch_bounds__(C::NT, 2) void k_fc2_dual(ExecArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __shared__ int tslot;
+  MOE_LDS uint16_t* smem = (MOE_LDS uint16_t*)smem_raw;
+  constexpr int NW = C::NT / 64;
+  const int r = worker_of_block(a.P);
+  const int nnt = a.d / C::BN;
+  const int total = a.mt_cnt[r] * nnt;
+  const int lane = threadIdx.x & 63;
+  uint16_t* O = (uint16_t*)a.bufO;
+  while (true) {
+    const int tile = next_tile(&a.ctr[PH_FC2 * kMaxP + r], &tslot);
+    if (tile >= total) break;
+    const int4 m = a.mt[(size_t)r * a.max_mt + tile / nnt];
+    const int nj = tile % nnt;
+    const int e = m.x, slot0 = m.y, nrows = m.z;
+    RowDma<C::BM, NW> da;
+    da.init((const uint16_t*)a.bufA, (uint32_t)(a.slots * a.dff * 2),
+            [&](int row) { return row < nrows ? (slot0 + row) * a.dff : -1; });
+    RowDma<C::BN, NW> db;
+    db.init((const uint16_t*)a.w2 + (size_t)e * a.d * a.dff, (uint32_t)((size_t)2 * a.d * a.dff),
+            [&](int rho) { return (nj * C::BN + rho) * a.dff; });
+    f32x16_t acc[C::MB][C::NB];
+    DmaPipe<C, RowDma<C::BM, NW>, RowDma<C::BN, NW>, kDualStages, true> p;
+    p.run(da, db, a.dff / kDmaBK, smem, acc);
+#pragma unroll
+    for (int i = 0; i < C::MB; ++i) {
+      const int row = dual_row<C>(i, lane);
+      if (row >= nrows) continue;
+      const float pg = a.gates[a.slot_to_row[slot0 + row]];
+      uint16_t* orow = O + ((size_t)slot0 + row) * a.d + nj * C::BN;
+#pragma unroll
+      for (int j = 0; j < C::NB; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = pg * acc[i][j][4 * g + q];
+          store4(orow + dual_col<C>(j, g, lane), v);
+        }
+    }
+  }
+}
+
+// dA = p * dy W2 (W2 [d][d_ff] read K-major through transpose reads), then
+// dZ = [dA U s (1 + G (1 - s)), dA G s] with s = sigmoid(G), and the gated
+// activation P = p SiLU(G) U for the weight gradient of W2.
+template <class C>
+__global__ __launch_bounds__(C::NT, 2) void k_bwd_da_dual(ExecArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __shared__ int tslot;
+  MOE_LDS uint16_t* smem = (MOE_LDS uint16_t*)smem_raw;
+  constexpr int NW = C::NT / 64;
+  const int r = worker_of_block(a.P);
+  const int nnt = a.dff / C::BN;
+  const int total = a.mt_cnt[r] * nnt;
+  const int lane = threadIdx.x & 63;
+  const uint16_t* Z = (const uint16_t*)a.z_save;
+  uint16_t* dZ = (uint16_t*)a.bufA;
+  uint16_t* PA = (uint16_t*)a.bufP;
+  const uint32_t bx = (uint32_t)((size_t)a.T * a.d * 2);
+  while (true) {
+    const int tile = next_tile(&a.ctr[PH_DA * kMaxP + r], &tslot);
+    if (tile >= total) break;
+    const int4 m = a.mt[(size_t)r * a.max_mt + tile / nnt];
+    const int nj = tile % nnt;
+    const int e = m.x, slot0 = m.y, nrows = m.z;
+    RowDma<C::BM, NW> da;
+    da.init((const uint16_t*)a.dy, bx,
+            [&](int row) { return row < nrows ? (a.slot_to_row[slot0 + row] / a.k) * a.d : -1; });
+    const MnDma<C::BN, NW> mb{make_rsrc((const uint16_t*)a.w2 + (size_t)e * a.d * a.dff,
+                                        (uint32_t)((size_t)2 * a.d * a.dff))};
+    const uint32_t bcol = (uint32_t)nj * C::BN * 2u, bld = (uint32_t)a.dff * 2u;
+    auto ob = mn_operand(mb, [=](int kk) -> uint32_t { return (uint32_t)kk * bld + bcol; });
+    f32x16_t acc[C::MB][C::NB];
+    DmaPipe<C, RowDma<C::BM, NW>, decltype(ob), kDualStages, true> p;
+    p.run(da, ob, a.d / kDmaBK, smem, acc);
+#pragma unroll
+    for (int i = 0; i < C::MB; ++i) {
+      const int row = dual_row<C>(i, lane);
+      if (row >= nrows) continue;
+      const size_t sr = (size_t)slot0 + row;
+      const float pg = a.gates[a.slot_to_row[slot0 + row]];
+#pragma unroll
+      for (int j = 0; j < C::NB; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = nj * C::BN + dual_col<C>(j, g, lane);
+          float gv[4], uv[4], dg[4], du[4], pa[4];
+          load4(Z + sr * 2 * a.dff + n, gv);
+          load4(Z + sr * 2 * a.dff + a.dff + n, uv);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float v = pg * acc[i][j][4 * g + q];
+            const float sg = sigm(gv[q]);
+            dg[q] = v * uv[q] * sg * (1.f + gv[q] * (1.f - sg));
+            du[q] = v * gv[q] * sg;
+            pa[q] = pg * (gv[q] * sg * uv[q]);
+          }
+          store4(dZ + sr * 2 * a.dff + n, dg);
+          store4(dZ + sr * 2 * a.dff + a.dff + n, du);
+          store4(PA + sr * a.dff + n, pa);
+        }
+    }
+  }
+}
+
+// dX per routed row: dZ W1 (W1 [2 d_ff][d] read K-major through transpose reads).
+template <class C>
+__global__ __launch_bounds__(C::NT, 2) void k_bwd_dx_dual(ExecArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __shared__ int tslot;
+  MOE_LDS uint16_t* smem = (MOE_LDS uint16_t*)smem_raw;
+  constexpr int NW = C::NT / 64;
+  const int r = worker_of_block(a.P);
+  const int nnt = a.d / C::BN;
+  const int total = a.mt_cnt[r] * nnt;
+  const int lane = threadIdx.x & 63;
+  uint16_t* dXp = (uint16_t*)a.bufO;
+  while (true) {
+    const int tile = next_tile(&a.ctr[PH_DX * kMaxP + r], &tslot);
+    if (tile >= total) break;
+    const int4 m = a.mt[(size_t)r * a.max_mt + tile / nnt];
+    const int nj = tile % nnt;
+    const int e = m.x, slot0 = m.y, nrows = m.z;
+    RowDma<C::BM, NW> da;
+    da.init((const uint16_t*)a.bufA, (uint32_t)(a.slots * 4 * a.dff),
+            [&](int row) { return row < nrows ? (slot0 + row) * 2 * a.dff : -1; });
+    const MnDma<C::BN, NW> mb{make_rsrc((const uint16_t*)a.w1 + (size_t)e * 2 * a.dff * a.d,
+                                        (uint32_t)((size_t)4 * a.dff * a.d))};
+    const uint32_t bcol = (uint32_t)nj * C::BN * 2u, bld = (uint32_t)a.d * 2u;
+    auto ob = mn_operand(mb, [=](int kk) -> uint32_t { return (uint32_t)kk * bld + bcol; });
+    f32x16_t acc[C::MB][C::NB];
+    DmaPipe<C, RowDma<C::BM, NW>, decltype(ob), kDualStages, true> p;
+    p.run(da, ob, 2 * a.dff / kDmaBK, smem, acc);
+#pragma unroll
+    for (int i = 0; i < C::MB; ++i) {
+      const int row = dual_row<C>(i, lane);
+      if (row >= nrows) continue;
+      uint16_t* orow = dXp + ((size_t)slot0 + row) * a.d + nj * C::BN;
+#pragma unroll
+      for (int j = 0; j < C::NB; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q];
+          store4(orow + dual_col<C>(j, g, lane), v);
+        }
+    }
+  }
+}
+
 // ---- backward: weight gradients per (expert, worker) segment ------------------
 // K runs over the segment's routed rows.  dW2[c, n] = sum D[c] * A[n] with
 // D = dy_t (gathered) and the gate folded into A = p * SiLU(G) * U, rebuilt
@@ -937,6 +1172,32 @@ static void run_forward(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot,
   rec(ev, 4, st);
 }
 
+// The two-workgroup kernels: bf16, 256 | d and 128 | d_ff (every M/N tile
+// extent), and every operand addressed through a buffer descriptor below 2 GiB.
+bool use_dual(const Sizes& z) {
+  const size_t lim = (size_t)1 << 31;
+  return z.act_bytes == 2 && z.d % 256 == 0 && z.dff % 128 == 0 &&
+         (size_t)z.T * z.d * 2 < lim && z.max_slots * 4 * (size_t)z.dff < lim &&
+         z.max_slots * 2 * (size_t)z.d < lim && (size_t)4 * z.dff * z.d < lim;
+}
+
+static void run_forward_dual(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* y,
+                             void* const* ev, hipStream_t st) {
+  using C = DualCfg;
+  const size_t lds = dual_lds_bytes<C>();
+  static int g1 = persistent_grid(k_fc1_dual<C>, C::NT, lds);
+  static int g2 = persistent_grid(k_fc2_dual<C>, C::NT, lds);
+  hipLaunchKernelGGL(k_fc1_dual<C>, dim3(g1), dim3(C::NT), lds, st, a);
+  rec(ev, 2, st);
+  hipLaunchKernelGGL(k_fc2_dual<C>, dim3(g2), dim3(C::NT), lds, st, a);
+  rec(ev, 3, st);
+  const long long nth = (long long)z.T * (z.d / 8);
+  if (nth > 0)
+    hipLaunchKernelGGL(k_combine<uint16_t>, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, st,
+                       (const uint16_t*)a.bufO, row_to_slot, z.T, z.k, z.d, (uint16_t*)y);
+  rec(ev, 4, st);
+}
+
 int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const float* gates,
                    const int32_t* counts, const int32_t* boff, const int32_t* row_to_slot,
                    const int32_t* slot_to_row, const int32_t* block_worker, void* y,
@@ -949,7 +1210,8 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
   a.x = x; a.gates = gates; a.slot_to_row = slot_to_row; a.row_to_slot = row_to_slot;
   a.z_save = z_save;
   const bool big = use_big_tiles(z);
-  if (Lp.act_dtype == MOE_F32) run_forward<float, false, SmallCfg>(z, a, row_to_slot, y, ev, st);
+  if (Lp.act_dtype == MOE_BF16 && Lp.w_dtype == MOE_BF16 && use_dual(z)) run_forward_dual(z, a, row_to_slot, y, ev, st);
+  else if (Lp.act_dtype == MOE_F32) run_forward<float, false, SmallCfg>(z, a, row_to_slot, y, ev, st);
   else if (Lp.w_dtype == MOE_FP8_E4M3) {
     if (big) run_forward<uint16_t, true, BigCfg>(z, a, row_to_slot, y, ev, st);
     else run_forward<uint16_t, true, SmallCfg>(z, a, row_to_slot, y, ev, st);
@@ -960,30 +1222,28 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
-// The direct-to-LDS weight gradients need 256 | d and 128 | d_ff (tile
-// extents) and token indices that fit the 16-bit LDS table.
-bool use_dma_backward(const Sizes& z) {
-  return use_big_tiles(z) && z.dff % 128 == 0 && z.T <= 65535;
-}
+// The two-workgroup backward also needs token indices that fit the 16-bit
+// LDS table of the weight-gradient kernel.
+bool use_dma_backward(const Sizes& z) { return use_dual(z) && z.T <= 65535; }
 
-template <class C>
-static void run_backward_dma(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* dx,
-                             float* dw1, float* dw2, void* const* ev, hipStream_t st) {
-  const size_t glds = gemm_lds_bytes<uint16_t, C>();
-  const size_t wlds = DwDual<DualCfg>::LDS_BYTES;
-  static int ga = persistent_grid(k_bwd_da<uint16_t, C>, C::NT, glds);
-  static int gx = persistent_grid(k_bwd_dx<uint16_t, C>, C::NT, glds);
-  static int gw = persistent_grid(k_bwd_dw_dual<DualCfg>, DualCfg::NT, wlds);
-  hipLaunchKernelGGL((k_bwd_da<uint16_t, C>), dim3(ga), dim3(C::NT), glds, st, a);
+static void run_backward_dual(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* dx,
+                              float* dw1, float* dw2, void* const* ev, hipStream_t st) {
+  using C = DualCfg;
+  const size_t glds = dual_lds_bytes<C>();
+  const size_t wlds = DwDual<C>::LDS_BYTES;
+  static int ga = persistent_grid(k_bwd_da_dual<C>, C::NT, glds);
+  static int gx = persistent_grid(k_bwd_dx_dual<C>, C::NT, glds);
+  static int gw = persistent_grid(k_bwd_dw_dual<C>, C::NT, wlds);
+  hipLaunchKernelGGL(k_bwd_da_dual<C>, dim3(ga), dim3(C::NT), glds, st, a);
   rec(ev, 2, st);
-  hipLaunchKernelGGL((k_bwd_dx<uint16_t, C>), dim3(gx), dim3(C::NT), glds, st, a);
+  hipLaunchKernelGGL(k_bwd_dx_dual<C>, dim3(gx), dim3(C::NT), glds, st, a);
   rec(ev, 3, st);
   const long long nth = (long long)z.T * (z.d / 8);
   if (nth > 0)
     hipLaunchKernelGGL(k_combine<uint16_t>, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, st,
                        (const uint16_t*)a.bufO, row_to_slot, z.T, z.k, z.d, (uint16_t*)dx);
   rec(ev, 4, st);
-  hipLaunchKernelGGL(k_bwd_dw_dual<DualCfg>, dim3(gw), dim3(DualCfg::NT), wlds, st, a);
+  hipLaunchKernelGGL(k_bwd_dw_dual<C>, dim3(gw), dim3(C::NT), wlds, st, a);
   rec(ev, 5, st);
   hipLaunchKernelGGL(k_bwd_reduce, dim3(num_cus() * 4), dim3(256), 0, st, a.rep_slot,
                      a.owner_has, (const float*)a.rslots, z.E, z.P, z.d, z.dff, dw1, dw2);
@@ -1029,7 +1289,7 @@ int launch_backward(const Sizes& z, const LayerPtrs& Lp, const void* x, const fl
   a.z_save = const_cast<void*>(z_save);
   a.dy = dy; a.dw1 = dw1; a.dw2 = dw2;
   if (Lp.act_dtype == MOE_F32) run_backward<float, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
-  else if (use_dma_backward(z)) run_backward_dma<BigCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
+  else if (use_dma_backward(z)) run_backward_dual(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else if (use_big_tiles(z)) run_backward<uint16_t, BigCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else run_backward<uint16_t, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
