@@ -16,6 +16,9 @@
 //           fp32 reduction of replica partials into the owner slot.
 #include "common.h"
 #include "gemm.h"
+#include <cstdlib>
+#include <cstring>
+#include <utility>
 #include "moe_ffn.h"
 
 namespace moe {
@@ -553,17 +556,38 @@ MOE_DEV float sigm(float g) { return __builtin_amdgcn_rcpf(1.f + __expf(-g)); }
 template <class C> MOE_DEV int dual_row(int i, int lane) { return acc_row_t<C>(i, lane); }
 template <class C> MOE_DEV int dual_col(int j, int g, int lane) { return acc_col_t<C>(j, g, lane); }
 
-// Dynamic LDS of the dual GEMM kernels: three stages of a 256-row and a
-// 128-row operand, 32 K values each.
-template <class C> constexpr size_t dual_lds_bytes() {
-  return (size_t)kDualStages * (C::BM + C::BN) * kDmaBK * 2;
-}
+// Tile engines of the GEMM kernels below.  Both give every wave a 128 x 64
+// piece of the tile (128 accumulator registers, two waves per SIMD) with
+// transposed accumulators, so the epilogues are shared:
+//   EngDual: 256 x 128 tiles, 4 waves, two workgroups per CU, K = 32 per
+//            stage, three stages (72 KB);
+//   EngWide: 256 x 256 tiles, 8 waves, one workgroup per CU, K = 64 per
+//            stage (full 128-byte lines), two stages (128 KB).
+struct EngDual {
+  using C = DualCfg;
+  static constexpr int BK = kDmaBK, MINB = 2;
+  template <int R> using Row = RowDma<R, C::NT / 64>;
+  template <int M> using Mn = MnDma<M, C::NT / 64>;
+  template <class A, class B> using Pipe = DmaPipe<C, A, B, kDualStages, true>;
+  template <class OP, class F> static MOE_DEV MnOperand<OP, F> mn(const OP& op, F f) { return {op, f}; }
+  static constexpr size_t LDS = (size_t)kDualStages * (C::BM + C::BN) * kDmaBK * 2;
+};
+struct EngWide {
+  using C = WideCfg;
+  static constexpr int BK = kWideBK, MINB = 1;
+  template <int R> using Row = Row64<R, C::NT / 64>;
+  template <int M> using Mn = Mn64<M, C::NT / 64>;
+  template <class A, class B> using Pipe = WidePipe<C, A, B>;
+  template <class OP, class F> static MOE_DEV Mn64Operand<OP, F> mn(const OP& op, F f) { return {op, f}; }
+  static constexpr size_t LDS = (size_t)kWideStages * (C::BM + C::BN) * kWideRowBytes;
+};
 
 // FC1 + SwiGLU.  N tile nj covers A columns [64 nj, 64 nj + 64): weight rows
 // alternate 32 G rows and the matching 32 U rows, so block j = 0 of a wave is
 // G and block j = 1 is U of the same 32 columns.
-template <class C>
-__global__ __launch_bounds__(C::NT, 2) void k_fc1_dual(ExecArgs a) {
+template <class E>
+__global__ __launch_bounds__(E::C::NT, E::MINB) void k_fc1_t(ExecArgs a) {
+  using C = typename E::C;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int tslot;
   MOE_LDS uint16_t* smem = (MOE_LDS uint16_t*)smem_raw;
@@ -583,18 +607,18 @@ __global__ __launch_bounds__(C::NT, 2) void k_fc1_dual(ExecArgs a) {
     const int4 m = a.mt[(size_t)r * a.max_mt + tile / nnt];
     const int nj = tile % nnt;
     const int e = m.x, slot0 = m.y, nrows = m.z;
-    RowDma<C::BM, NW> da;
+    typename E::template Row<C::BM> da;
     da.init((const uint16_t*)a.x, bx,
             [&](int row) { return row < nrows ? (a.slot_to_row[slot0 + row] / a.k) * a.d : -1; });
-    RowDma<C::BN, NW> db;
+    typename E::template Row<C::BN> db;
     db.init((const uint16_t*)a.w1 + (size_t)e * 2 * a.dff * a.d, (uint32_t)((size_t)4 * a.dff * a.d),
             [&](int rho) {
               const int q = rho >> 5;
               return ((q & 1) * a.dff + nj * HALF + (q >> 1) * 32 + (rho & 31)) * a.d;
             });
     f32x16_t acc[C::MB][C::NB];
-    DmaPipe<C, RowDma<C::BM, NW>, RowDma<C::BN, NW>, kDualStages, true> p;
-    p.run(da, db, a.d / kDmaBK, smem, acc);
+    typename E::template Pipe<typename E::template Row<C::BM>, typename E::template Row<C::BN>> p;
+    p.run(da, db, a.d / E::BK, smem, acc);
     const int col0 = nj * HALF + wn * 32 + 4 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < C::MB; ++i) {
@@ -622,8 +646,9 @@ __global__ __launch_bounds__(C::NT, 2) void k_fc1_dual(ExecArgs a) {
 }
 
 // FC2 with the gate: O[slot] = p * A W2^T.
-template <class C>
-__global__ __launch_bounds__(C::NT, 2) void k_fc2_dual(ExecArgs a) {
+template <class E>
+__global__ __launch_bounds__(E::C::NT, E::MINB) void k_fc2_t(ExecArgs a) {
+  using C = typename E::C;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int tslot;
   MOE_LDS uint16_t* smem = (MOE_LDS uint16_t*)smem_raw;
@@ -639,15 +664,15 @@ __global__ __launch_bounds__(C::NT, 2) void k_fc2_dual(ExecArgs a) {
     const int4 m = a.mt[(size_t)r * a.max_mt + tile / nnt];
     const int nj = tile % nnt;
     const int e = m.x, slot0 = m.y, nrows = m.z;
-    RowDma<C::BM, NW> da;
+    typename E::template Row<C::BM> da;
     da.init((const uint16_t*)a.bufA, (uint32_t)(a.slots * a.dff * 2),
             [&](int row) { return row < nrows ? (slot0 + row) * a.dff : -1; });
-    RowDma<C::BN, NW> db;
+    typename E::template Row<C::BN> db;
     db.init((const uint16_t*)a.w2 + (size_t)e * a.d * a.dff, (uint32_t)((size_t)2 * a.d * a.dff),
             [&](int rho) { return (nj * C::BN + rho) * a.dff; });
     f32x16_t acc[C::MB][C::NB];
-    DmaPipe<C, RowDma<C::BM, NW>, RowDma<C::BN, NW>, kDualStages, true> p;
-    p.run(da, db, a.dff / kDmaBK, smem, acc);
+    typename E::template Pipe<typename E::template Row<C::BM>, typename E::template Row<C::BN>> p;
+    p.run(da, db, a.dff / E::BK, smem, acc);
 #pragma unroll
     for (int i = 0; i < C::MB; ++i) {
       const int row = dual_row<C>(i, lane);
@@ -670,8 +695,9 @@ __global__ __launch_bounds__(C::NT, 2) void k_fc2_dual(ExecArgs a) {
 // dA = p * dy W2 (W2 [d][d_ff] read K-major through transpose reads), then
 // dZ = [dA U s (1 + G (1 - s)), dA G s] with s = sigmoid(G), and the gated
 // activation P = p SiLU(G) U for the weight gradient of W2.
-template <class C>
-__global__ __launch_bounds__(C::NT, 2) void k_bwd_da_dual(ExecArgs a) {
+template <class E>
+__global__ __launch_bounds__(E::C::NT, E::MINB) void k_bwd_da_t(ExecArgs a) {
+  using C = typename E::C;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int tslot;
   MOE_LDS uint16_t* smem = (MOE_LDS uint16_t*)smem_raw;
@@ -690,16 +716,16 @@ __global__ __launch_bounds__(C::NT, 2) void k_bwd_da_dual(ExecArgs a) {
     const int4 m = a.mt[(size_t)r * a.max_mt + tile / nnt];
     const int nj = tile % nnt;
     const int e = m.x, slot0 = m.y, nrows = m.z;
-    RowDma<C::BM, NW> da;
+    typename E::template Row<C::BM> da;
     da.init((const uint16_t*)a.dy, bx,
             [&](int row) { return row < nrows ? (a.slot_to_row[slot0 + row] / a.k) * a.d : -1; });
-    const MnDma<C::BN, NW> mb{make_rsrc((const uint16_t*)a.w2 + (size_t)e * a.d * a.dff,
-                                        (uint32_t)((size_t)2 * a.d * a.dff))};
+    const typename E::template Mn<C::BN> mb{make_rsrc((const uint16_t*)a.w2 + (size_t)e * a.d * a.dff,
+                                                      (uint32_t)((size_t)2 * a.d * a.dff))};
     const uint32_t bcol = (uint32_t)nj * C::BN * 2u, bld = (uint32_t)a.dff * 2u;
-    auto ob = mn_operand(mb, [=](int kk) -> uint32_t { return (uint32_t)kk * bld + bcol; });
+    auto ob = E::mn(mb, [=](int kk) -> uint32_t { return (uint32_t)kk * bld + bcol; });
     f32x16_t acc[C::MB][C::NB];
-    DmaPipe<C, RowDma<C::BM, NW>, decltype(ob), kDualStages, true> p;
-    p.run(da, ob, a.d / kDmaBK, smem, acc);
+    typename E::template Pipe<typename E::template Row<C::BM>, decltype(ob)> p;
+    p.run(da, ob, a.d / E::BK, smem, acc);
 #pragma unroll
     for (int i = 0; i < C::MB; ++i) {
       const int row = dual_row<C>(i, lane);
@@ -731,8 +757,9 @@ __global__ __launch_bounds__(C::NT, 2) void k_bwd_da_dual(ExecArgs a) {
 }
 
 // dX per routed row: dZ W1 (W1 [2 d_ff][d] read K-major through transpose reads).
-template <class C>
-__global__ __launch_bounds__(C::NT, 2) void k_bwd_dx_dual(ExecArgs a) {
+template <class E>
+__global__ __launch_bounds__(E::C::NT, E::MINB) void k_bwd_dx_t(ExecArgs a) {
+  using C = typename E::C;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int tslot;
   MOE_LDS uint16_t* smem = (MOE_LDS uint16_t*)smem_raw;
@@ -748,16 +775,16 @@ __global__ __launch_bounds__(C::NT, 2) void k_bwd_dx_dual(ExecArgs a) {
     const int4 m = a.mt[(size_t)r * a.max_mt + tile / nnt];
     const int nj = tile % nnt;
     const int e = m.x, slot0 = m.y, nrows = m.z;
-    RowDma<C::BM, NW> da;
+    typename E::template Row<C::BM> da;
     da.init((const uint16_t*)a.bufA, (uint32_t)(a.slots * 4 * a.dff),
             [&](int row) { return row < nrows ? (slot0 + row) * 2 * a.dff : -1; });
-    const MnDma<C::BN, NW> mb{make_rsrc((const uint16_t*)a.w1 + (size_t)e * 2 * a.dff * a.d,
-                                        (uint32_t)((size_t)4 * a.dff * a.d))};
+    const typename E::template Mn<C::BN> mb{make_rsrc((const uint16_t*)a.w1 + (size_t)e * 2 * a.dff * a.d,
+                                                      (uint32_t)((size_t)4 * a.dff * a.d))};
     const uint32_t bcol = (uint32_t)nj * C::BN * 2u, bld = (uint32_t)a.d * 2u;
-    auto ob = mn_operand(mb, [=](int kk) -> uint32_t { return (uint32_t)kk * bld + bcol; });
+    auto ob = E::mn(mb, [=](int kk) -> uint32_t { return (uint32_t)kk * bld + bcol; });
     f32x16_t acc[C::MB][C::NB];
-    DmaPipe<C, RowDma<C::BM, NW>, decltype(ob), kDualStages, true> p;
-    p.run(da, ob, 2 * a.dff / kDmaBK, smem, acc);
+    typename E::template Pipe<typename E::template Row<C::BM>, decltype(ob)> p;
+    p.run(da, ob, 2 * a.dff / E::BK, smem, acc);
 #pragma unroll
     for (int i = 0; i < C::MB; ++i) {
       const int row = dual_row<C>(i, lane);
@@ -919,21 +946,22 @@ struct DwRows {
     return k < wrows ? o : kOob;
   }
 };
-template <class C> struct DwDual {
-  static constexpr int NW = C::NT / 64;
-  using OA = MnOperand<MnDma<C::BM, NW>, DwRows>;
-  using OB = MnOperand<MnDma<C::BN, NW>, DwRows>;
-  using Pipe = DmaPipe<C, OA, OB, kDualStages, true>;
+template <class E> struct DwEng {
+  using C = typename E::C;
+  using OA = decltype(E::mn(std::declval<const typename E::template Mn<C::BM>&>(), std::declval<DwRows>()));
+  using OB = decltype(E::mn(std::declval<const typename E::template Mn<C::BN>&>(), std::declval<DwRows>()));
+  using Pipe = typename E::template Pipe<OA, OB>;
   static constexpr size_t STAGE_BYTES = Pipe::BYTES;
   static constexpr size_t LDS_BYTES = STAGE_BYTES + (size_t)kTokWin * 2;
 };
 
-template <class C>
-__global__ __launch_bounds__(C::NT, 2) void k_bwd_dw_dual(ExecArgs a) {
+template <class E>
+__global__ __launch_bounds__(E::C::NT, E::MINB) void k_bwd_dw_t(ExecArgs a) {
+  using C = typename E::C;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int tslot;
   MOE_LDS uint16_t* smem = (MOE_LDS uint16_t*)smem_raw;
-  MOE_LDS uint16_t* tok = smem + DwDual<C>::STAGE_BYTES / 2;
+  MOE_LDS uint16_t* tok = smem + DwEng<E>::STAGE_BYTES / 2;
   constexpr int NW = C::NT / 64;
   const int r = worker_of_block(a.P);
   const int n2m = a.d / C::BM, n2n = a.dff / C::BN;          // dW2 [d][dff]
@@ -957,8 +985,8 @@ __global__ __launch_bounds__(C::NT, 2) void k_bwd_dw_dual(ExecArgs a) {
     const int mi = is2 ? loc / n2n : (loc - n2m * n2n) / n1n;
     const int nj = is2 ? loc % n2n : (loc - n2m * n2n) % n1n;
     // dW2 = dy^T P (A: gathered dy rows, B: P rows);  dW1 = dZ^T x (A: dZ rows, B: gathered x rows)
-    const MnDma<C::BM, NW> ma{is2 ? r_dy : r_dz};
-    const MnDma<C::BN, NW> mb{is2 ? r_p : r_x};
+    const typename E::template Mn<C::BM> ma{is2 ? r_dy : r_dz};
+    const typename E::template Mn<C::BN> mb{is2 ? r_p : r_x};
     f32x16_t acc[C::MB][C::NB];
     for (int w0 = 0; w0 < nrows; w0 += kTokWin) {
       const int wrows = min(kTokWin, nrows - w0);
@@ -970,8 +998,8 @@ __global__ __launch_bounds__(C::NT, 2) void k_bwd_dw_dual(ExecArgs a) {
       asm volatile("" : "+s"(ga));           // opaque: keeps the select arithmetic
       const DwRows ra{tok, wrows, s0, is2 ? a.d : 2 * a.dff, mi * C::BM, ga};
       const DwRows rb{tok, wrows, s0, is2 ? a.dff : a.d, nj * C::BN, 1u - ga};
-      typename DwDual<C>::Pipe p;
-      p.run(mn_operand(ma, ra), mn_operand(mb, rb), (wrows + kDmaBK - 1) / kDmaBK, smem, acc, w0 > 0);
+      typename DwEng<E>::Pipe p;
+      p.run(E::mn(ma, ra), E::mn(mb, rb), (wrows + E::BK - 1) / E::BK, smem, acc, w0 > 0);
     }
     float* out;
     int ldo;
@@ -1181,21 +1209,42 @@ bool use_dual(const Sizes& z) {
          z.max_slots * 2 * (size_t)z.d < lim && (size_t)4 * z.dff * z.d < lim;
 }
 
-static void run_forward_dual(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* y,
-                             void* const* ev, hipStream_t st) {
-  using C = DualCfg;
-  const size_t lds = dual_lds_bytes<C>();
-  static int g1 = persistent_grid(k_fc1_dual<C>, C::NT, lds);
-  static int g2 = persistent_grid(k_fc2_dual<C>, C::NT, lds);
-  hipLaunchKernelGGL(k_fc1_dual<C>, dim3(g1), dim3(C::NT), lds, st, a);
+template <class E>
+static void run_forward_eng(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* y,
+                            void* const* ev, hipStream_t st) {
+  using C = typename E::C;
+  const size_t lds = E::LDS;
+  static int g1 = persistent_grid(k_fc1_t<E>, C::NT, lds);
+  static int g2 = persistent_grid(k_fc2_t<E>, C::NT, lds);
+  hipLaunchKernelGGL(k_fc1_t<E>, dim3(g1), dim3(C::NT), lds, st, a);
   rec(ev, 2, st);
-  hipLaunchKernelGGL(k_fc2_dual<C>, dim3(g2), dim3(C::NT), lds, st, a);
+  hipLaunchKernelGGL(k_fc2_t<E>, dim3(g2), dim3(C::NT), lds, st, a);
   rec(ev, 3, st);
   const long long nth = (long long)z.T * (z.d / 8);
   if (nth > 0)
     hipLaunchKernelGGL(k_combine<uint16_t>, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, st,
                        (const uint16_t*)a.bufO, row_to_slot, z.T, z.k, z.d, (uint16_t*)y);
   rec(ev, 4, st);
+}
+
+// Engine choice: the wide tile wherever its extents divide the problem
+// (256 | d_ff for the backward's d_ff-wide N tiles), else the two-workgroup
+// tile.  MOE_FFN_ENGINE=dual|wide forces one (for measurement).
+static int engine_override() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("MOE_FFN_ENGINE");
+    v = (e && !strcmp(e, "dual")) ? 1 : (e && !strcmp(e, "wide")) ? 2 : 0;
+  }
+  return v;
+}
+static bool wide_fwd(const Sizes& z) { return engine_override() != 1; }
+static bool wide_bwd(const Sizes& z) { return engine_override() != 1 && z.dff % 256 == 0; }
+
+static void run_forward_sel(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* y,
+                            void* const* ev, hipStream_t st) {
+  if (wide_fwd(z)) run_forward_eng<EngWide>(z, a, row_to_slot, y, ev, st);
+  else run_forward_eng<EngDual>(z, a, row_to_slot, y, ev, st);
 }
 
 int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const float* gates,
@@ -1210,7 +1259,7 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
   a.x = x; a.gates = gates; a.slot_to_row = slot_to_row; a.row_to_slot = row_to_slot;
   a.z_save = z_save;
   const bool big = use_big_tiles(z);
-  if (Lp.act_dtype == MOE_BF16 && Lp.w_dtype == MOE_BF16 && use_dual(z)) run_forward_dual(z, a, row_to_slot, y, ev, st);
+  if (Lp.act_dtype == MOE_BF16 && Lp.w_dtype == MOE_BF16 && use_dual(z)) run_forward_sel(z, a, row_to_slot, y, ev, st);
   else if (Lp.act_dtype == MOE_F32) run_forward<float, false, SmallCfg>(z, a, row_to_slot, y, ev, st);
   else if (Lp.w_dtype == MOE_FP8_E4M3) {
     if (big) run_forward<uint16_t, true, BigCfg>(z, a, row_to_slot, y, ev, st);
@@ -1226,28 +1275,35 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
 // LDS table of the weight-gradient kernel.
 bool use_dma_backward(const Sizes& z) { return use_dual(z) && z.T <= 65535; }
 
-static void run_backward_dual(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* dx,
-                              float* dw1, float* dw2, void* const* ev, hipStream_t st) {
-  using C = DualCfg;
-  const size_t glds = dual_lds_bytes<C>();
-  const size_t wlds = DwDual<C>::LDS_BYTES;
-  static int ga = persistent_grid(k_bwd_da_dual<C>, C::NT, glds);
-  static int gx = persistent_grid(k_bwd_dx_dual<C>, C::NT, glds);
-  static int gw = persistent_grid(k_bwd_dw_dual<C>, C::NT, wlds);
-  hipLaunchKernelGGL(k_bwd_da_dual<C>, dim3(ga), dim3(C::NT), glds, st, a);
+template <class E, class EW>
+static void run_backward_eng(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* dx,
+                             float* dw1, float* dw2, void* const* ev, hipStream_t st) {
+  using C = typename E::C;
+  const size_t glds = E::LDS;
+  const size_t wlds = DwEng<EW>::LDS_BYTES;
+  static int ga = persistent_grid(k_bwd_da_t<E>, C::NT, glds);
+  static int gx = persistent_grid(k_bwd_dx_t<E>, C::NT, glds);
+  static int gw = persistent_grid(k_bwd_dw_t<EW>, EW::C::NT, wlds);
+  hipLaunchKernelGGL(k_bwd_da_t<E>, dim3(ga), dim3(C::NT), glds, st, a);
   rec(ev, 2, st);
-  hipLaunchKernelGGL(k_bwd_dx_dual<C>, dim3(gx), dim3(C::NT), glds, st, a);
+  hipLaunchKernelGGL(k_bwd_dx_t<E>, dim3(gx), dim3(C::NT), glds, st, a);
   rec(ev, 3, st);
   const long long nth = (long long)z.T * (z.d / 8);
   if (nth > 0)
     hipLaunchKernelGGL(k_combine<uint16_t>, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, st,
                        (const uint16_t*)a.bufO, row_to_slot, z.T, z.k, z.d, (uint16_t*)dx);
   rec(ev, 4, st);
-  hipLaunchKernelGGL(k_bwd_dw_dual<C>, dim3(gw), dim3(C::NT), wlds, st, a);
+  hipLaunchKernelGGL(k_bwd_dw_t<EW>, dim3(gw), dim3(EW::C::NT), wlds, st, a);
   rec(ev, 5, st);
   hipLaunchKernelGGL(k_bwd_reduce, dim3(num_cus() * 4), dim3(256), 0, st, a.rep_slot,
                      a.owner_has, (const float*)a.rslots, z.E, z.P, z.d, z.dff, dw1, dw2);
   rec(ev, 6, st);
+}
+
+static void run_backward_sel(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* dx,
+                             float* dw1, float* dw2, void* const* ev, hipStream_t st) {
+  if (wide_bwd(z)) run_backward_eng<EngWide, EngWide>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
+  else run_backward_eng<EngDual, EngDual>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
 }
 
 template <typename T, class C>
@@ -1289,7 +1345,7 @@ int launch_backward(const Sizes& z, const LayerPtrs& Lp, const void* x, const fl
   a.z_save = const_cast<void*>(z_save);
   a.dy = dy; a.dw1 = dw1; a.dw2 = dw2;
   if (Lp.act_dtype == MOE_F32) run_backward<float, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
-  else if (use_dma_backward(z)) run_backward_dual(z, a, row_to_slot, dx, dw1, dw2, ev, st);
+  else if (use_dma_backward(z)) run_backward_sel(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else if (use_big_tiles(z)) run_backward<uint16_t, BigCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else run_backward<uint16_t, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;

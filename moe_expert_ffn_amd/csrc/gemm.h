@@ -694,6 +694,241 @@ template <class C> MOE_DEV int acc_col_t(int j, int g, int lane) {
   return (wave_id() % C::WAVES_N) * C::WN + j * 32 + 8 * g + 4 * (lane >> 5);
 }
 
+// ---- wide tile: 256 x 256, 8 waves, K = 64 per stage --------------------------
+// Eight waves (2 x 4, each 128 x 64 with 128 accumulator registers, two waves
+// per SIMD) share one 256 x 256 tile; a stage holds K = 64, so every row
+// segment is a full 128-byte line, both for the global load and in LDS.  Two
+// direct-to-LDS stages (128 KB): the loads of step kt+1 land while step kt
+// computes.  Accumulators are transposed (the N fragment is the MFMA's first
+// operand), as for the two-workgroup tiles.
+//
+// LDS swizzles, chosen from measured bank behaviour of gfx950:
+//   ds_read_b128 on 128-byte rows serves 16 lanes per clock; XOR-ing the
+//   16-byte chunk index with (row ^ row >> 3) & 7 over 32 consecutive rows
+//   gives every group of 16 lanes distinct banks;
+//   ds_read_b64_tr_b16 serves 32 lanes per clock (4 rows x 64 bytes); XOR-ing
+//   the chunk index with 4 (row & 3) spreads those four rows over disjoint
+//   64-byte bank ranges.
+using WideCfg = GemmCfg<256, 256, 2, 4>;
+constexpr int kWideBK = 64, kWideStages = 2, kWideRowBytes = 128;
+
+MOE_DEV int swz_row128(int row) { return (row & 7) ^ ((row >> 3) & 3); }   // rows mod 32
+MOE_DEV int swz_tr(int row) { return (row & 3) << 2; }
+
+// K-contiguous operand: ROWS rows of K = 64 per stage, [row][128 bytes].
+// One wave instruction loads 8 rows (8 lanes x 16 bytes each).
+template <int ROWS, int NWAVES> struct Row64 {
+  static constexpr int NI = ROWS / 8 / NWAVES;
+  static constexpr int STAGE_BYTES = ROWS * kWideRowBytes;
+  static_assert(NI * 8 * NWAVES == ROWS, "rows per stage");
+  BufRsrc rs;
+  uint32_t off[NI];
+  // rowoff(row) = element offset of the row's first K element from b, or -1 for
+  // a row that reads as zeros; `bytes` = extent of the buffer at b.
+  template <class F> MOE_DEV void init(const uint16_t* b, uint32_t bytes, F rowoff) {
+    rs = make_rsrc(b, bytes);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = (w + NWAVES * i) * 8 + (lane >> 3);
+      const int o = rowoff(row);
+      off[i] = o < 0 ? kOob : (uint32_t)o * 2u + (uint32_t)(((lane & 7) ^ swz_row128(row)) * 16);
+    }
+  }
+  struct Offs { uint32_t o[NI]; };
+  MOE_DEV Offs prep(int kt) const {
+    Offs q;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) q.o[i] = off[i] + (uint32_t)kt * kWideRowBytes;
+    return q;
+  }
+  MOE_DEV void issue(const Offs& q, MOE_LDS char* st) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      buf_load_lds16(rs, q.o[i], (MOE_LDS void*)(st + (w + NWAVES * i) * 8 * kWideRowBytes));
+  }
+  // Fragment i of a wave: rows wave_base + 32 i + (lane & 31), K chunk
+  // 2 KC + (lane >> 5) of the stage; wave_base is a multiple of 32, so the
+  // offset is (lane part ^ 32 KC) + 4096 i.
+  struct Lane { uint32_t off; };
+  static MOE_DEV Lane lane_info(int wave_base, int lane) {
+    const int lr = lane & 31, h = lane >> 5;
+    return {(uint32_t)((wave_base + lr) * kWideRowBytes + ((h ^ swz_row128(lr)) * 16))};
+  }
+  template <int KC> static MOE_DEV bf16x8_t frag(const MOE_LDS char* st, const Lane& L, int i) {
+    return *(const MOE_LDS bf16x8_t*)(st + ((L.off ^ (32u * KC)) + 32u * kWideRowBytes * i));
+  }
+};
+
+// MN-contiguous operand: 64 K rows x MN elements per stage, [k][MN], fragments
+// through ds_read_b64_tr_b16 (see MnDma).  rowoff(k) = byte offset in the
+// buffer of (source row of K index k, mn0), or kOob for a zero row.
+template <int MN, int NWAVES> struct Mn64 {
+  static constexpr int ROWB = MN * 2;
+  static constexpr int RPI = 1024 / ROWB;           // K rows per wave instruction
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int NI = kWideBK / RPI / NWAVES;
+  static constexpr int STAGE_BYTES = kWideBK * ROWB;
+  static_assert(NI * RPI * NWAVES == kWideBK, "64 K rows per stage");
+  BufRsrc rs;
+  struct Offs { uint32_t o[NI]; };
+  template <class F> MOE_DEV Offs prep_rows(int kt, F rowoff) const {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    Offs p;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = (w + NWAVES * i) * RPI + lane / CPR;
+      const uint32_t c = (uint32_t)((lane % CPR) ^ swz_tr(r));
+      p.o[i] = rowoff(kt * kWideBK + r) + c * 16u;
+    }
+    return p;
+  }
+  MOE_DEV void issue(const Offs& p, MOE_LDS char* st) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      buf_load_lds16(rs, p.o[i], (MOE_LDS void*)(st + (w + NWAVES * i) * RPI * ROWB));
+  }
+  // Lane j of 16-lane group G reads rows 16 KC + 8 (G >> 1) + j / 4 (+ 4) at
+  // column wave_base + 32 i + 16 (G & 1) + 4 (j % 4); the swizzle touches
+  // chunk bits 2..3 and fragment i adds 4 i chunks above the lane's bits 0..1,
+  // so the offset is (lane part ^ 64 i) + KC * 16 * ROWB (see MnDma).
+  struct Lane { uint32_t off[2]; };
+  static MOE_DEV Lane lane_info(int wave_base, int lane) {
+    const int G = lane >> 4, j = lane & 15;
+    const int m = wave_base + 16 * (G & 1) + 4 * (j & 3);
+    const int c = m >> 3, within = m & 7;
+    Lane L;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 8 * (G >> 1) + (j >> 2) + 4 * h;
+      L.off[h] = (uint32_t)(row * ROWB + ((c ^ swz_tr(row)) << 4) + within * 2);
+    }
+    return L;
+  }
+  // Issued from inline asm for the reason given at MnDma::frag.
+  template <int KC> static MOE_DEV bf16x8_t frag(const MOE_LDS char* st, const Lane& L, int i) {
+    s16x4_t lo, hi;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                 : "=v"(lo) : "v"(st + (L.off[0] ^ (64u * i))), "i"(KC * 16 * ROWB));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                 : "=v"(hi) : "v"(st + (L.off[1] ^ (64u * i))), "i"(KC * 16 * ROWB));
+    typedef short s16x8_t __attribute__((ext_vector_type(8)));
+    const s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
+};
+
+template <class OP, class F> struct Mn64Operand {
+  const OP& op;
+  F rowoff;
+  static constexpr int NI = OP::NI, STAGE_BYTES = OP::STAGE_BYTES;
+  using Lane = typename OP::Lane;
+  using Offs = typename OP::Offs;
+  MOE_DEV Offs prep(int kt) const { return op.prep_rows(kt, rowoff); }
+  MOE_DEV void issue(const Offs& p, MOE_LDS char* st) const { op.issue(p, st); }
+  static MOE_DEV Lane lane_info(int wave_base, int lane) { return OP::lane_info(wave_base, lane); }
+  template <int KC> static MOE_DEV bf16x8_t frag(const MOE_LDS char* st, const Lane& L, int i) {
+    return OP::template frag<KC>(st, L, i);
+  }
+};
+template <class OP, class F> MOE_DEV Mn64Operand<OP, F> mn64_operand(const OP& op, F f) { return {op, f}; }
+
+// nk = K / 64 steps.  Step kt (stage kt % 2):
+//   four K chunks; the fragments of chunk c+1 are read while chunk c's 8 MFMAs
+//   run; the load offsets of step kt+2 are prepared early in the step;
+//   after chunk 2: wait for this wave's loads of step kt+1 and its LDS reads,
+//   barrier (every wave's part of step kt+1 is in LDS, nobody reads stage
+//   kt % 2 any more), issue step kt+2 into stage kt % 2, read chunk 0 of
+//   step kt+1, then chunk 3's MFMAs.
+// Loads past the last step re-read step nk-1 into a stage nobody reads again.
+// Fragments read from asm (Mn64) are consumed only after an explicit
+// lgkmcnt(0) wait pinned by a scheduling barrier.
+template <class C, class OA, class OB> struct WidePipe {
+  static constexpr int SA = OA::STAGE_BYTES, STAGE = OA::STAGE_BYTES + OB::STAGE_BYTES;
+  static constexpr int LPS = OA::NI + OB::NI;
+  static constexpr size_t BYTES = (size_t)kWideStages * STAGE;
+  bf16x8_t a[2][C::MB], b[2][C::NB];
+  typename OA::Lane la;
+  typename OB::Lane lb;
+  template <int KC, int S> MOE_DEV void read(const MOE_LDS char* st) {
+#pragma unroll
+    for (int i = 0; i < C::MB; ++i) a[S][i] = OA::template frag<KC>(st, la, i);
+#pragma unroll
+    for (int j = 0; j < C::NB; ++j) b[S][j] = OB::template frag<KC>(st + SA, lb, j);
+  }
+  template <int S> MOE_DEV void mma(f32x16_t (&acc)[C::MB][C::NB]) const {
+#pragma unroll
+    for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[S][j], a[S][i], acc[i][j], 0, 0, 0);
+  }
+  MOE_DEV void run(const OA& oa, const OB& ob, int nk, MOE_LDS uint16_t* smem16,
+                   f32x16_t (&acc)[C::MB][C::NB], bool accumulate = false) {
+    MOE_LDS char* smem = (MOE_LDS char*)smem16;
+    const int lane = threadIdx.x & 63;
+    if (!accumulate) {
+#pragma unroll
+      for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NB; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    }
+    if (nk <= 0) return;
+    la = OA::lane_info((wave_id() / C::WAVES_N) * C::WM, lane);
+    lb = OB::lane_info((wave_id() % C::WAVES_N) * C::WN, lane);
+    __syncthreads();                      // the previous users of the LDS are done
+#pragma unroll
+    for (int s = 0; s < kWideStages; ++s) {
+      const int kk = s < nk ? s : nk - 1;
+      const auto pa = oa.prep(kk);
+      const auto pb = ob.prep(kk);
+      oa.issue(pa, smem + s * STAGE);
+      ob.issue(pb, smem + s * STAGE + SA);
+    }
+    wait_vm_lgkm0<(kWideStages - 1) * LPS>();
+    __builtin_amdgcn_s_barrier();
+    read<0, 0>(smem);
+    for (int kt = 0; kt < nk; ++kt) {
+      const MOE_LDS char* st = smem + (kt & 1) * STAGE;
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_sched_barrier(0);
+      read<1, 1>(st);
+      const int kn = kt + 2 < nk ? kt + 2 : nk - 1;
+      const auto pa = oa.prep(kn);
+      const auto pb = ob.prep(kn);
+      __builtin_amdgcn_sched_barrier(0);
+      mma<0>(acc);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_sched_barrier(0);
+      read<2, 0>(st);
+      __builtin_amdgcn_sched_barrier(0);
+      mma<1>(acc);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_sched_barrier(0);
+      read<3, 1>(st);
+      __builtin_amdgcn_sched_barrier(0);
+      mma<0>(acc);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm_lgkm0<0>();
+      __builtin_amdgcn_s_barrier();
+      oa.issue(pa, smem + (kt & 1) * STAGE);
+      ob.issue(pb, smem + (kt & 1) * STAGE + SA);
+      if (kt + 1 < nk) read<0, 0>(smem + ((kt + 1) & 1) * STAGE);
+      __builtin_amdgcn_sched_barrier(0);
+      mma<1>(acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vm_lgkm0<0>();
+    __syncthreads();                      // all loads landed, all waves done with the stages
+  }
+};
+
 // Coordinates of accumulator register r of block (i, j) for this lane, within
 // the tile.
 template <class C> MOE_DEV int acc_row(int i, int r, int lane) {
