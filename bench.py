@@ -120,10 +120,76 @@ def time_steps(case, steps, warmup, with_events=True):
     return wall_ms, stages
 
 
-def kernel_flops(w, R):
-    dd = w.d * w.d_ff
-    return {"fwd.fc1": 4 * dd * R, "fwd.fc2": 2 * dd * R, "bwd.dA": 2 * dd * R,
-            "bwd.dX": 4 * dd * R, "bwd.dW": 6 * dd * R}
+def kernel_model(w, R, T, e_act, replicas):
+    """Algorithmic flops and HBM bytes of one launch of each kernel: every
+    operand read once from HBM and every output written once (weights of the
+    experts that have rows, gathered activations counted once per token, the
+    fp32 weight gradients of owners and replicas)."""
+    d, f, ab = w.d, w.d_ff, 2
+    wb = 1 if w.wdt == "fp8" else 2
+    w1 = 2 * f * d * wb * e_act
+    w2 = d * f * wb * e_act
+    x = T * d * ab
+    m = {
+        "fwd.fc1": (4 * d * f * R, w1 + x + R * f * ab + (R * 2 * f * ab if w.backward else 0)),
+        "fwd.fc2": (2 * d * f * R, w2 + R * f * ab + R * d * ab),
+        "fwd.combine": (0, R * d * ab + x),
+    }
+    if w.backward:
+        m.update({
+            "bwd.dA": (2 * d * f * R, w2 + x + 2 * R * 2 * f * ab + R * f * ab),
+            "bwd.dX": (4 * d * f * R, w1 + R * 2 * f * ab + R * d * ab),
+            "bwd.combine": (0, R * d * ab + x),
+            "bwd.dW": (6 * d * f * R, 2 * x + R * 2 * f * ab + R * f * ab + 3 * d * f * 4 * (e_act + replicas)),
+        })
+    return m
+
+
+# HBM traffic of the dominant kernel from rocprofv3 counters (FETCH_SIZE and
+# WRITE_SIZE per dispatch, scaled by the reading of a plain copy kernel of
+# known size), valid only for the kernel sources it was measured on.
+PROFILED_TRAFFIC = {"kernel": "bwd.dW", "source": "81570b68e5ace0e4", "bytes": 3660181307,
+                    "summary": "profiles/k_bwd_dw_qwen3_bf16_fwdbwd_hbm_traffic.md"}
+
+
+def source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "moe_expert_ffn_amd", "csrc")
+    for name in sorted(os.listdir(src)):
+        with open(os.path.join(src, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def roofline(w, stages, R, T, e_act, replicas):
+    model = kernel_model(w, R, T, e_act, replicas)
+    peak_f = PEAK_FP8_TFLOPS if w.wdt == "fp8" else PEAK_BF16_TFLOPS
+    rows = {}
+    for k, (fl, by) in model.items():
+        if k not in stages:
+            continue
+        t = stages[k] * 1e-3
+        tf, tb = fl / (peak_f * 1e12), by / (PEAK_HBM_GBS * 1e9)
+        if tf >= tb:
+            rows[k] = {"bound": "mfma", "achieved": fl / t / 1e12, "peak": peak_f, "unit": "TFLOP/s"}
+        else:
+            rows[k] = {"bound": "hbm", "achieved": by / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+        rows[k].update(frac=rows[k]["achieved"] / rows[k]["peak"], launch_us=stages[k] * 1e3,
+                       flops=fl, bytes=by)
+    dom = max(rows, key=lambda k: rows[k]["launch_us"])
+    r = rows[dom]
+    traffic = None
+    if PROFILED_TRAFFIC and PROFILED_TRAFFIC.get("kernel") == dom and \
+            PROFILED_TRAFFIC.get("source") == source_hash():
+        traffic = PROFILED_TRAFFIC["bytes"]
+    out = {"kernel": dom, "bound": r["bound"], "achieved": round(r["achieved"], 2), "peak": r["peak"],
+           "unit": r["unit"], "frac": round(r["frac"], 4), "traffic": traffic,
+           "launch_us": round(r["launch_us"], 2), "algorithmic_flops": r["flops"],
+           "algorithmic_bytes": r["bytes"]}
+    per = {k: {"bound": v["bound"], "frac": round(v["frac"], 4), "us": round(v["launch_us"], 1)}
+           for k, v in rows.items()}
+    return out, per
 
 
 def cpu_baseline(case, w, tokens):
@@ -181,15 +247,10 @@ def main():
     useful = (f_fwd + (f_bwd if w.backward else 0)) * R
     value = useful / (ms * 1e-3) / 1e12
 
-    kf = kernel_flops(w, R)
-    cand = {k: v for k, v in stages.items() if k in kf}
-    dom = max(cand, key=cand.get)
-    dur_s = cand[dom] * 1e-3
-    achieved = kf[dom] / dur_s / 1e12
-    peak = PEAK_BF16_TFLOPS
-    roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-            "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-            "launch_us": round(cand[dom] * 1e3, 2), "flops_per_launch": kf[dom]}
+    import numpy as np
+    e_act = int((np.bincount(case["ids_np"][case["ids_np"] >= 0].ravel(), minlength=w.E) > 0).sum())
+    replicas = int(case["runner"].plan_b["plan_info"][2].item()) if w.backward else 0
+    roof, per_kernel = roofline(w, stages, R, case["T"], e_act, replicas)
 
     plan_f = case["runner"].plan_f["plan_info"].cpu().tolist()
     out = {
@@ -206,6 +267,7 @@ def main():
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "stages_us": {k: round(v * 1e3, 2) for k, v in stages.items()},
         "roofline": roof,
+        "kernels": per_kernel,
     }
     if args.sweep:
         sweep = []
