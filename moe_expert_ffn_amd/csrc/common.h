@@ -26,6 +26,9 @@ MOE_DEV uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f);
 // every access becomes a flat load that waits on both memory counters.
 #define MOE_LDS __attribute__((address_space(3)))
 #define MOE_GLB __attribute__((address_space(1)))
+// Constant address space: loads of wave-uniform values that are not written
+// during the kernel become scalar loads (counted by lgkmcnt, not vmcnt).
+#define MOE_CONST __attribute__((address_space(4)))
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 MOE_DEV uint4 ldg16(const void* p) {

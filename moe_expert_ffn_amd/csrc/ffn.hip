@@ -213,6 +213,8 @@ struct ExecArgs {
   float* rslots;
   void* bufP;             // backward: P = p * SiLU(G) * U per routed row
   size_t slots;           // padded slot capacity (rows of bufA, bufO, bufP, z_save)
+  const float* sgate;     // per-slot gate (0 for padding slots)
+  uint32_t kmagic;        // ceil(2^32 / k): token = umulhi(row, kmagic)
 };
 
 enum { PH_FC1 = 0, PH_FC2 = 1, PH_DA = 2, PH_DX = 3, PH_DW = 4 };
@@ -544,263 +546,386 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dx(ExecArgs a) {
   }
 }
 
-// ---- two workgroups per CU: FC1, FC2, dA, dX -----------------------------------
-// 256-row M tiles of one (expert, worker) run, 128-wide N tiles, transposed
-// accumulators: lane (lane & 31) of wave (wm, wn) owns rows wm*128 + 32 i +
-// (lane & 31) and, per register quad g of block j, the four consecutive
-// columns wn*64 + 32 j + 8 g + 4 (lane >> 5) .. +3, stored straight from
-// registers.  Fast exp / reciprocal in the SiLU terms: their error is far
-// below the bf16 rounding of every value they feed.
+// ---- GEMM kernels on the persistent wide tile -----------------------------------
+// 256 x 256 tiles, 8 waves, transposed accumulators: lane (lane & 31) of wave
+// (wm, wn) owns rows wm*128 + 32 i + (lane & 31) and, per register quad g of
+// block j, the four consecutive columns wn*64 + 32 j + 8 g + 4 (lane >> 5)
+// .. +3, stored straight from registers.  Each workgroup walks its worker's
+// items (M tile x N tile) in a static sequence through WideStream.  Fast exp
+// and reciprocal in the SiLU terms: their error is far below the bf16
+// rounding of every value they feed.
 MOE_DEV float sigm(float g) { return __builtin_amdgcn_rcpf(1.f + __expf(-g)); }
 
-template <class C> MOE_DEV int dual_row(int i, int lane) { return acc_row_t<C>(i, lane); }
-template <class C> MOE_DEV int dual_col(int j, int g, int lane) { return acc_col_t<C>(j, g, lane); }
+using WC = WideCfg;
+constexpr int kWNW = WC::NT / 64;
+using RowW = Row64<256, kWNW>;
+using MnW = Mn64<256, kWNW>;
+constexpr int kItemSlots = 3;
+constexpr size_t kItemBytes = 2048;           // 256 slot -> row entries, 256 slot gates
+constexpr size_t kStageBytes = (size_t)kWideStages * (WC::BM + WC::BN) * kWideRowBytes;
+constexpr size_t kEpiOff = kStageBytes + kItemSlots * kItemBytes;   // per-wave epilogue scratch
+constexpr size_t kEpiWave = 2048;
+constexpr size_t kStreamLds = kEpiOff + (WC::NT / 64) * kEpiWave;
 
-// Tile engines of the GEMM kernels below.  Both give every wave a 128 x 64
-// piece of the tile (128 accumulator registers, two waves per SIMD) with
-// transposed accumulators, so the epilogues are shared:
-//   EngDual: 256 x 128 tiles, 4 waves, two workgroups per CU, K = 32 per
-//            stage, three stages (72 KB);
-//   EngWide: 256 x 256 tiles, 8 waves, one workgroup per CU, K = 64 per
-//            stage (full 128-byte lines), two stages (128 KB).
-struct EngDual {
-  using C = DualCfg;
-  static constexpr int BK = kDmaBK, MINB = 2;
-  template <int R> using Row = RowDma<R, C::NT / 64>;
-  template <int M> using Mn = MnDma<M, C::NT / 64>;
-  template <class A, class B> using Pipe = DmaPipe<C, A, B, kDualStages, true>;
-  template <class OP, class F> static MOE_DEV MnOperand<OP, F> mn(const OP& op, F f) { return {op, f}; }
-  static constexpr size_t LDS = (size_t)kDualStages * (C::BM + C::BN) * kDmaBK * 2;
-};
-struct EngWide {
-  using C = WideCfg;
-  static constexpr int BK = kWideBK, MINB = 1;
-  template <int R> using Row = Row64<R, C::NT / 64>;
-  template <int M> using Mn = Mn64<M, C::NT / 64>;
-  template <class A, class B> using Pipe = WidePipe<C, A, B>;
-  template <class OP, class F> static MOE_DEV Mn64Operand<OP, F> mn(const OP& op, F f) { return {op, f}; }
-  static constexpr size_t LDS = (size_t)kWideStages * (C::BM + C::BN) * kWideRowBytes;
-};
-
-// FC1 + SwiGLU.  N tile nj covers A columns [64 nj, 64 nj + 64): weight rows
-// alternate 32 G rows and the matching 32 U rows, so block j = 0 of a wave is
-// G and block j = 1 is U of the same 32 columns.
-template <class E>
-__global__ __launch_bounds__(E::C::NT, E::MINB) void k_fc1_t(ExecArgs a) {
-  using C = typename E::C;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  __shared__ int tslot;
-  MOE_LDS uint16_t* smem = (MOE_LDS uint16_t*)smem_raw;
-  constexpr int NW = C::NT / 64, HALF = C::BN / 2;
-  static_assert(C::NB == 2 && C::WN == 64, "one G block and one U block per wave");
-  const int r = worker_of_block(a.P);
-  const int nnt = a.dff / HALF;
-  const int total = a.mt_cnt[r] * nnt;
-  const int lane = threadIdx.x & 63;
-  const int wn = wave_id() % C::WAVES_N;
-  uint16_t* Ab = (uint16_t*)a.bufA;
-  uint16_t* Z = (uint16_t*)a.z_save;
-  const uint32_t bx = (uint32_t)((size_t)a.T * a.d * 2);
-  while (true) {
-    const int tile = next_tile(&a.ctr[PH_FC1 * kMaxP + r], &tslot);
-    if (tile >= total) break;
-    const int4 m = a.mt[(size_t)r * a.max_mt + tile / nnt];
-    const int nj = tile % nnt;
-    const int e = m.x, slot0 = m.y, nrows = m.z;
-    typename E::template Row<C::BM> da;
-    da.init((const uint16_t*)a.x, bx,
-            [&](int row) { return row < nrows ? (a.slot_to_row[slot0 + row] / a.k) * a.d : -1; });
-    typename E::template Row<C::BN> db;
-    db.init((const uint16_t*)a.w1 + (size_t)e * 2 * a.dff * a.d, (uint32_t)((size_t)4 * a.dff * a.d),
-            [&](int rho) {
-              const int q = rho >> 5;
-              return ((q & 1) * a.dff + nj * HALF + (q >> 1) * 32 + (rho & 31)) * a.d;
-            });
-    f32x16_t acc[C::MB][C::NB];
-    typename E::template Pipe<typename E::template Row<C::BM>, typename E::template Row<C::BN>> p;
-    p.run(da, db, a.d / E::BK, smem, acc);
-    const int col0 = nj * HALF + wn * 32 + 4 * (lane >> 5);
+// ---- row-contiguous epilogue stores ------------------------------------------
+// A wave's transposed accumulators hold, per lane, 4-value pieces of one row;
+// stored directly, every store instruction would touch 32 rows with 16 bytes
+// each, which sustains well under a third of the HBM write rate of row
+// segments.  So each 16-row half of a 32-row block goes through a 2 KB
+// per-wave LDS scratch: the lanes holding those rows write their pieces, then
+// all 64 lanes read back 16-byte chunks in row order and store them, each
+// instruction covering whole row segments of SEG 32-column blocks
+// (RB = 32 * SEG * sizeof(T) bytes, 64 or 128).  Chunk c of scratch row r
+// sits at chunk c ^ swz(r), which keeps the 16-lane groups of both the writes
+// and the reads on distinct banks.  A wave's LDS operations complete in
+// order, so no barrier or wait is needed between the passes.
+template <typename T, int SEG> struct RowStore {
+  static constexpr int RB = 32 * SEG * (int)sizeof(T);
+  static constexpr int CPR = RB / 16;
+  static constexpr int NRD = 16 * CPR / 64;                 // read/store instructions per half block
+  static_assert(RB == 64 || RB == 128, "segment row bytes");
+  static MOE_DEV int swz(int r) { return RB == 128 ? (r >> 1) & 7 : (r >> 2) & 3; }
+  // vals(jj, g, v): the 4 values of quad g of block j0 + jj of this lane's row;
+  // emit(row, chunk, data): store 16 bytes at `row` (0..31 inside the block)
+  // and 16-byte chunk `chunk` of the segment.
+  // The values are computed and packed by every lane first; the two halves of
+  // the block then take turns in the per-wave scratch.
+  using Packed = typename std::conditional<sizeof(T) == 4, u32x4_t, u32x2_t>::type;
+  template <class V>
+  static MOE_DEV void pack(V vals, Packed (&p)[SEG][4]) {
 #pragma unroll
-    for (int i = 0; i < C::MB; ++i) {
-      const int row = dual_row<C>(i, lane);
-      if (row >= nrows) continue;
-      const size_t sr = (size_t)slot0 + row;
+    for (int jj = 0; jj < SEG; ++jj)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        float gv[4], uv[4], av[4];
+        float v[4];
+        vals(jj, g, v);
+        if constexpr (sizeof(T) == 4)
+          p[jj][g] = u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                             __float_as_uint(v[3])};
+        else
+          p[jj][g] = u32x2_t{(uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16),
+                             (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16)};
+      }
+  }
+  template <class EM>
+  static MOE_DEV void store(MOE_LDS char* scr, const Packed (&p)[SEG][4], EM emit) {
+    const int lane = threadIdx.x & 63, lr = lane & 31, h = lane >> 5;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          gv[q] = acc[i][0][4 * g + q];
-          uv[q] = acc[i][1][4 * g + q];
-          av[q] = gv[q] * sigm(gv[q]) * uv[q];
-        }
-        const int c = col0 + 8 * g;
-        store4(Ab + sr * a.dff + c, av);
-        if (Z) {
-          store4(Z + sr * 2 * a.dff + c, gv);
-          store4(Z + sr * 2 * a.dff + a.dff + c, uv);
-        }
+    for (int half = 0; half < 2; ++half) {
+      wave_lds_sync();                     // the previous reads of the scratch are done
+      if ((lr >> 4) == half) {
+        const int r = lr & 15;
+#pragma unroll
+        for (int jj = 0; jj < SEG; ++jj)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            if constexpr (sizeof(T) == 4) {
+              const int c = jj * 8 + 2 * g + h;
+              *(MOE_LDS u32x4_t*)(scr + r * RB + ((c ^ swz(r)) << 4)) = p[jj][g];
+            } else {
+              const int c = jj * 4 + g;
+              *(MOE_LDS u32x2_t*)(scr + r * RB + ((c ^ swz(r)) << 4) + 8 * h) = p[jj][g];
+            }
+          }
+      }
+      wave_lds_sync();                     // other lanes' writes are visible
+      u32x4_t d[NRD];
+#pragma unroll
+      for (int sI = 0; sI < NRD; ++sI) {
+        const int q = sI * 64 + lane, rr = q / CPR, c = q % CPR;
+        d[sI] = *(const MOE_LDS u32x4_t*)(scr + rr * RB + ((c ^ swz(rr)) << 4));
+      }
+#pragma unroll
+      for (int sI = 0; sI < NRD; ++sI) {
+        const int q = sI * 64 + lane;
+        emit(16 * half + q / CPR, q % CPR, d[sI]);
       }
     }
   }
-}
+  template <class V, class EM>
+  static MOE_DEV void run(MOE_LDS char* scr, V vals, EM emit) {
+    Packed p[SEG][4];
+    pack(vals, p);
+    store(scr, p, emit);
+  }
+};
 
-// FC2 with the gate: O[slot] = p * A W2^T.
-template <class E>
-__global__ __launch_bounds__(E::C::NT, E::MINB) void k_fc2_t(ExecArgs a) {
-  using C = typename E::C;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  __shared__ int tslot;
-  MOE_LDS uint16_t* smem = (MOE_LDS uint16_t*)smem_raw;
-  constexpr int NW = C::NT / 64;
-  const int r = worker_of_block(a.P);
-  const int nnt = a.d / C::BN;
-  const int total = a.mt_cnt[r] * nnt;
-  const int lane = threadIdx.x & 63;
-  uint16_t* O = (uint16_t*)a.bufO;
-  while (true) {
-    const int tile = next_tile(&a.ctr[PH_FC2 * kMaxP + r], &tslot);
-    if (tile >= total) break;
-    const int4 m = a.mt[(size_t)r * a.max_mt + tile / nnt];
-    const int nj = tile % nnt;
-    const int e = m.x, slot0 = m.y, nrows = m.z;
-    typename E::template Row<C::BM> da;
-    da.init((const uint16_t*)a.bufA, (uint32_t)(a.slots * a.dff * 2),
-            [&](int row) { return row < nrows ? (slot0 + row) * a.dff : -1; });
-    typename E::template Row<C::BN> db;
-    db.init((const uint16_t*)a.w2 + (size_t)e * a.d * a.dff, (uint32_t)((size_t)2 * a.d * a.dff),
-            [&](int rho) { return (nj * C::BN + rho) * a.dff; });
-    f32x16_t acc[C::MB][C::NB];
-    typename E::template Pipe<typename E::template Row<C::BM>, typename E::template Row<C::BN>> p;
-    p.run(da, db, a.dff / E::BK, smem, acc);
+MOE_DEV MOE_LDS char* epi_scratch(MOE_LDS uint16_t* smem) {
+  return (MOE_LDS char*)smem + kEpiOff + (size_t)wave_id() * kEpiWave;
+}
+MOE_DEV void stg16v(void* p, const u32x4_t& d) { *(MOE_GLB u32x4_t*)p = d; }
+
+MOE_DEV const MOE_LDS int* item_rows(const MOE_LDS uint16_t* smem, int slot) {
+  return (const MOE_LDS int*)((const MOE_LDS char*)smem + kStageBytes + slot * kItemBytes);
+}
+MOE_DEV const MOE_LDS float* item_gates(const MOE_LDS uint16_t* smem, int slot) {
+  return (const MOE_LDS float*)((const MOE_LDS char*)smem + kStageBytes + slot * kItemBytes + 1024);
+}
+// 256 consecutive 4-byte values from byte offset `off` of `rs` into LDS (one
+// wave instruction; slots past the buffer read as zeros).
+MOE_DEV void load_1k(BufRsrc rs, uint32_t off, MOE_LDS uint16_t* smem, size_t lds_off) {
+  buf_load_lds16(rs, off + (uint32_t)(threadIdx.x & 63) * 16u,
+                 (MOE_LDS void*)((MOE_LDS char*)smem + lds_off));
+}
+// token of routed row `row` = row / k, exact for the sizes the host admits
+MOE_DEV uint32_t token_of(uint32_t row, uint32_t kmagic) { return __umulhi(row, kmagic); }
+
+// M-tile item: tile idx / nnt of the worker's list, N tile idx % nnt.
+struct MItem { int e, slot0, nrows, nj; };
+struct MSrcBase {
+  ExecArgs a;              // a copy: the fields stay in scalar registers
+  MOE_LDS uint16_t* smem;
+  int r, nnt, count, first, stride;
+  MOE_DEV void init(const ExecArgs& args, MOE_LDS uint16_t* sm, int ntiles_n) {
+    a = args;
+    smem = sm;
+    const WorkerSlot w = worker_slot(args.P);
+    r = w.r;
+    nnt = ntiles_n;
+    count = args.mt_cnt[r] * nnt;
+    first = w.j;
+    stride = w.n;
+  }
+  // scalar load: nothing waits on vector loads in flight
+  MOE_DEV MItem load(int idx) const {
+    const u32x4_t m = ((const MOE_CONST u32x4_t*)a.mt)[(size_t)r * a.max_mt + idx / nnt];
+    return {(int)m.x, (int)m.y, (int)m.z, idx % nnt};
+  }
+  MOE_DEV void fill_rows(const MItem& it, int slot) const {     // slot -> row of the tile's rows
+    if (wave_id() == 0)
+      load_1k(make_rsrc(a.slot_to_row, (uint32_t)(a.slots * 4)), (uint32_t)it.slot0 * 4u, smem,
+              kStageBytes + slot * kItemBytes);
+  }
+  MOE_DEV void fill_gates(const MItem& it, int slot) const {    // gate of the tile's rows
+    if (wave_id() == 1)
+      load_1k(make_rsrc(a.sgate, (uint32_t)(a.slots * 4)), (uint32_t)it.slot0 * 4u, smem,
+              kStageBytes + slot * kItemBytes + 1024);
+  }
+  // A operand: gathered token rows of `base` ([T][ld]) for the tile's slots
+  MOE_DEV RowW gathered(const MItem& it, int slot, const void* base, int ld) const {
+    const MOE_LDS int* rows = item_rows(smem, slot);
+    int o[RowW::NI];
 #pragma unroll
-    for (int i = 0; i < C::MB; ++i) {
-      const int row = dual_row<C>(i, lane);
-      if (row >= nrows) continue;
-      const float pg = a.gates[a.slot_to_row[slot0 + row]];
-      uint16_t* orow = O + ((size_t)slot0 + row) * a.d + nj * C::BN;
+    for (int i = 0; i < RowW::NI; ++i) {
+      const int row = RowW::lane_row(i);
+      o[i] = row < it.nrows ? (int)token_of((uint32_t)rows[row], a.kmagic) * ld : -1;
+    }
+    RowW x;
+    x.init_offsets((const uint16_t*)base, (uint32_t)((size_t)a.T * ld * 2), o);
+    return x;
+  }
+  // A operand: slot rows of `base` ([slots][ld])
+  MOE_DEV RowW slotrows(const MItem& it, const void* base, int ld) const {
+    RowW x;
+    x.init((const uint16_t*)base, (uint32_t)(a.slots * ld * 2),
+           [&](int row) { return row < it.nrows ? (it.slot0 + row) * ld : -1; });
+    return x;
+  }
+};
+
+// K-major weight operand: row k of a [K][ld] matrix from column col.
+struct MnFixed {
+  uint32_t ld2, col2;
+  MOE_DEV uint32_t pre(int k) const { return (uint32_t)k; }
+  MOE_DEV uint32_t post(uint32_t raw, int) const { return raw * ld2 + col2; }
+};
+using MnFixedOp = Mn64Operand<MnW, MnFixed>;
+
+// FC1 + SwiGLU.  N tile nj covers A columns [128 nj, 128 nj + 128): weight
+// rows alternate 32 G rows and the matching 32 U rows, so block j = 0 of a
+// wave is G and block j = 1 is U of the same 32 columns.
+struct SrcFc1 : MSrcBase {
+  using Item = MItem;
+  MOE_DEV void fill(const Item& it, int slot) const { fill_rows(it, slot); }
+  MOE_DEV RowW opA(const Item& it, int slot) const { return gathered(it, slot, a.x, a.d); }
+  MOE_DEV RowW opB(const Item& it, int) const {
+    RowW w;
+    const int dff = a.dff, nj = it.nj;
+    w.init((const uint16_t*)a.w1 + (size_t)it.e * 2 * dff * a.d, (uint32_t)((size_t)4 * dff * a.d),
+           [&](int rho) {
+             const int q = rho >> 5;
+             return ((q & 1) * dff + nj * (WC::BN / 2) + (q >> 1) * 32 + (rho & 31)) * a.d;
+           });
+    return w;
+  }
+  MOE_DEV int steps(const Item&) const { return a.d / kWideBK; }
+  MOE_DEV void epilogue(const Item& it, int, const f32x16_t (&acc)[WC::MB][WC::NB]) const {
+    const int wm = wave_id() / WC::WAVES_N, wn = wave_id() % WC::WAVES_N;
+    uint16_t* Ab = (uint16_t*)a.bufA;
+    uint16_t* Z = (uint16_t*)a.z_save;
+    const int dff = a.dff, colb = it.nj * (WC::BN / 2) + wn * 32;
+    MOE_LDS char* scr = epi_scratch(smem);
 #pragma unroll
-      for (int j = 0; j < C::NB; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float v[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = pg * acc[i][j][4 * g + q];
-          store4(orow + dual_col<C>(j, g, lane), v);
+    for (int i = 0; i < WC::MB; ++i) {
+      const int rb = wm * WC::WM + i * 32;
+      auto emit_to = [&](uint16_t* base, size_t ld) {
+        return [&, base, ld](int row, int c, const u32x4_t& d) {
+          if (rb + row < it.nrows) stg16v(base + ((size_t)it.slot0 + rb + row) * ld + colb + c * 8, d);
+        };
+      };
+      RowStore<uint16_t, 1>::run(scr, [&](int, int g, float* v) {
+        for (int q = 0; q < 4; ++q) {
+          const float gv = acc[i][0][4 * g + q];
+          v[q] = gv * sigm(gv) * acc[i][1][4 * g + q];
         }
+      }, emit_to(Ab, dff));
+      if (Z) {
+        RowStore<uint16_t, 1>::run(scr, [&](int, int g, float* v) {
+          for (int q = 0; q < 4; ++q) v[q] = acc[i][0][4 * g + q];
+        }, emit_to(Z, 2 * dff));
+        RowStore<uint16_t, 1>::run(scr, [&](int, int g, float* v) {
+          for (int q = 0; q < 4; ++q) v[q] = acc[i][1][4 * g + q];
+        }, emit_to(Z + dff, 2 * dff));
+      }
     }
   }
-}
+};
+
+// FC2 with the gate: O[slot] = p * A W2^T.
+struct SrcFc2 : MSrcBase {
+  using Item = MItem;
+  MOE_DEV void fill(const Item& it, int slot) const { fill_gates(it, slot); }
+  MOE_DEV RowW opA(const Item& it, int) const { return slotrows(it, a.bufA, a.dff); }
+  MOE_DEV RowW opB(const Item& it, int) const {
+    RowW w;
+    const int nj = it.nj, dff = a.dff;
+    w.init((const uint16_t*)a.w2 + (size_t)it.e * a.d * dff, (uint32_t)((size_t)2 * a.d * dff),
+           [&](int rho) { return (nj * WC::BN + rho) * dff; });
+    return w;
+  }
+  MOE_DEV int steps(const Item&) const { return a.dff / kWideBK; }
+  MOE_DEV void epilogue(const Item& it, int slot, const f32x16_t (&acc)[WC::MB][WC::NB]) const {
+    const int lane = threadIdx.x & 63, wm = wave_id() / WC::WAVES_N, wn = wave_id() % WC::WAVES_N;
+    const MOE_LDS float* gt = item_gates(smem, slot);
+    uint16_t* O = (uint16_t*)a.bufO;
+    const int colb = it.nj * WC::BN + wn * WC::WN;
+    MOE_LDS char* scr = epi_scratch(smem);
+#pragma unroll
+    for (int i = 0; i < WC::MB; ++i) {
+      const int rb = wm * WC::WM + i * 32;
+      const float pg = gt[rb + (lane & 31)];
+      RowStore<uint16_t, 2>::run(scr, [&](int jj, int g, float* v) {
+        for (int q = 0; q < 4; ++q) v[q] = pg * acc[i][jj][4 * g + q];
+      }, [&](int row, int c, const u32x4_t& d) {
+        if (rb + row < it.nrows) stg16v(O + ((size_t)it.slot0 + rb + row) * a.d + colb + c * 8, d);
+      });
+    }
+  }
+};
 
 // dA = p * dy W2 (W2 [d][d_ff] read K-major through transpose reads), then
 // dZ = [dA U s (1 + G (1 - s)), dA G s] with s = sigmoid(G), and the gated
 // activation P = p SiLU(G) U for the weight gradient of W2.
-template <class E>
-__global__ __launch_bounds__(E::C::NT, E::MINB) void k_bwd_da_t(ExecArgs a) {
-  using C = typename E::C;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  __shared__ int tslot;
-  MOE_LDS uint16_t* smem = (MOE_LDS uint16_t*)smem_raw;
-  constexpr int NW = C::NT / 64;
-  const int r = worker_of_block(a.P);
-  const int nnt = a.dff / C::BN;
-  const int total = a.mt_cnt[r] * nnt;
-  const int lane = threadIdx.x & 63;
-  const uint16_t* Z = (const uint16_t*)a.z_save;
-  uint16_t* dZ = (uint16_t*)a.bufA;
-  uint16_t* PA = (uint16_t*)a.bufP;
-  const uint32_t bx = (uint32_t)((size_t)a.T * a.d * 2);
-  while (true) {
-    const int tile = next_tile(&a.ctr[PH_DA * kMaxP + r], &tslot);
-    if (tile >= total) break;
-    const int4 m = a.mt[(size_t)r * a.max_mt + tile / nnt];
-    const int nj = tile % nnt;
-    const int e = m.x, slot0 = m.y, nrows = m.z;
-    typename E::template Row<C::BM> da;
-    da.init((const uint16_t*)a.dy, bx,
-            [&](int row) { return row < nrows ? (a.slot_to_row[slot0 + row] / a.k) * a.d : -1; });
-    const typename E::template Mn<C::BN> mb{make_rsrc((const uint16_t*)a.w2 + (size_t)e * a.d * a.dff,
-                                                      (uint32_t)((size_t)2 * a.d * a.dff))};
-    const uint32_t bcol = (uint32_t)nj * C::BN * 2u, bld = (uint32_t)a.dff * 2u;
-    auto ob = E::mn(mb, [=](int kk) -> uint32_t { return (uint32_t)kk * bld + bcol; });
-    f32x16_t acc[C::MB][C::NB];
-    typename E::template Pipe<typename E::template Row<C::BM>, decltype(ob)> p;
-    p.run(da, ob, a.d / E::BK, smem, acc);
+struct SrcDa : MSrcBase {
+  using Item = MItem;
+  MOE_DEV void fill(const Item& it, int slot) const { fill_rows(it, slot); fill_gates(it, slot); }
+  MOE_DEV RowW opA(const Item& it, int slot) const { return gathered(it, slot, a.dy, a.d); }
+  MOE_DEV MnFixedOp opB(const Item& it, int) const {
+    const MnW m{make_rsrc((const uint16_t*)a.w2 + (size_t)it.e * a.d * a.dff,
+                          (uint32_t)((size_t)2 * a.d * a.dff))};
+    return {m, MnFixed{(uint32_t)a.dff * 2u, (uint32_t)it.nj * WC::BN * 2u}};
+  }
+  MOE_DEV int steps(const Item&) const { return a.d / kWideBK; }
+  MOE_DEV void epilogue(const Item& it, int slot, const f32x16_t (&acc)[WC::MB][WC::NB]) const {
+    const int lane = threadIdx.x & 63, wm = wave_id() / WC::WAVES_N, wn = wave_id() % WC::WAVES_N;
+    const MOE_LDS float* gt = item_gates(smem, slot);
+    const uint16_t* Z = (const uint16_t*)a.z_save;
+    uint16_t* dZ = (uint16_t*)a.bufA;
+    uint16_t* PA = (uint16_t*)a.bufP;
+    const int dff = a.dff, colb = it.nj * WC::BN + wn * WC::WN;
+    MOE_LDS char* scr = epi_scratch(smem);
+    // per 32 x 32 block: the 8 [G, U] loads of the lane's row are issued
+    // together, then dG, dU and P are formed in one pass (one sigmoid per
+    // element) and leave through the per-wave scratch as 64-byte row pieces
 #pragma unroll
-    for (int i = 0; i < C::MB; ++i) {
-      const int row = dual_row<C>(i, lane);
-      if (row >= nrows) continue;
-      const size_t sr = (size_t)slot0 + row;
-      const float pg = a.gates[a.slot_to_row[slot0 + row]];
+    for (int i = 0; i < WC::MB; ++i) {
+      const int rb = wm * WC::WM + i * 32, myrow = rb + (lane & 31);
+      const float pg = gt[myrow];
+      const size_t sr = (size_t)it.slot0 + (myrow < it.nrows ? myrow : 0);
 #pragma unroll
-      for (int j = 0; j < C::NB; ++j)
+      for (int j = 0; j < WC::NB; ++j) {
+        const int cb = colb + j * 32;
+        u32x2_t zg[4], zu[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int n = nj * C::BN + dual_col<C>(j, g, lane);
-          float gv[4], uv[4], dg[4], du[4], pa[4];
-          load4(Z + sr * 2 * a.dff + n, gv);
-          load4(Z + sr * 2 * a.dff + a.dff + n, uv);
+          const int n = cb + 8 * g + 4 * (lane >> 5);
+          zg[g] = *(const MOE_GLB u32x2_t*)(Z + sr * 2 * dff + n);
+          zu[g] = *(const MOE_GLB u32x2_t*)(Z + sr * 2 * dff + dff + n);
+        }
+        using RS = RowStore<uint16_t, 1>;
+        RS::Packed pgp[1][4], pup[1][4], ppp[1][4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float vg[4], vu[4], vp[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float v = pg * acc[i][j][4 * g + q];
-            const float sg = sigm(gv[q]);
-            dg[q] = v * uv[q] * sg * (1.f + gv[q] * (1.f - sg));
-            du[q] = v * gv[q] * sg;
-            pa[q] = pg * (gv[q] * sg * uv[q]);
+            const uint32_t wg = q < 2 ? zg[g].x : zg[g].y, wu = q < 2 ? zu[g].x : zu[g].y;
+            const float gv = bf2f((uint16_t)((q & 1) ? wg >> 16 : wg & 0xffff));
+            const float uv = bf2f((uint16_t)((q & 1) ? wu >> 16 : wu & 0xffff));
+            const float sg = sigm(gv), da = pg * acc[i][j][4 * g + q];
+            vg[q] = da * uv * sg * (1.f + gv * (1.f - sg));
+            vu[q] = da * gv * sg;
+            vp[q] = pg * (gv * sg * uv);
           }
-          store4(dZ + sr * 2 * a.dff + n, dg);
-          store4(dZ + sr * 2 * a.dff + a.dff + n, du);
-          store4(PA + sr * a.dff + n, pa);
+          pgp[0][g] = u32x2_t{(uint32_t)f2bf(vg[0]) | ((uint32_t)f2bf(vg[1]) << 16),
+                              (uint32_t)f2bf(vg[2]) | ((uint32_t)f2bf(vg[3]) << 16)};
+          pup[0][g] = u32x2_t{(uint32_t)f2bf(vu[0]) | ((uint32_t)f2bf(vu[1]) << 16),
+                              (uint32_t)f2bf(vu[2]) | ((uint32_t)f2bf(vu[3]) << 16)};
+          ppp[0][g] = u32x2_t{(uint32_t)f2bf(vp[0]) | ((uint32_t)f2bf(vp[1]) << 16),
+                              (uint32_t)f2bf(vp[2]) | ((uint32_t)f2bf(vp[3]) << 16)};
         }
+        auto emit_to = [&](uint16_t* base, size_t ld) {
+          return [&, base, ld](int row, int c, const u32x4_t& d) {
+            if (rb + row < it.nrows) stg16v(base + ((size_t)it.slot0 + rb + row) * ld + cb + c * 8, d);
+          };
+        };
+        RS::store(scr, pgp, emit_to(dZ, 2 * dff));
+        RS::store(scr, pup, emit_to(dZ + dff, 2 * dff));
+        RS::store(scr, ppp, emit_to(PA, dff));
+      }
     }
   }
-}
+};
 
 // dX per routed row: dZ W1 (W1 [2 d_ff][d] read K-major through transpose reads).
-template <class E>
-__global__ __launch_bounds__(E::C::NT, E::MINB) void k_bwd_dx_t(ExecArgs a) {
-  using C = typename E::C;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  __shared__ int tslot;
-  MOE_LDS uint16_t* smem = (MOE_LDS uint16_t*)smem_raw;
-  constexpr int NW = C::NT / 64;
-  const int r = worker_of_block(a.P);
-  const int nnt = a.d / C::BN;
-  const int total = a.mt_cnt[r] * nnt;
-  const int lane = threadIdx.x & 63;
-  uint16_t* dXp = (uint16_t*)a.bufO;
-  while (true) {
-    const int tile = next_tile(&a.ctr[PH_DX * kMaxP + r], &tslot);
-    if (tile >= total) break;
-    const int4 m = a.mt[(size_t)r * a.max_mt + tile / nnt];
-    const int nj = tile % nnt;
-    const int e = m.x, slot0 = m.y, nrows = m.z;
-    typename E::template Row<C::BM> da;
-    da.init((const uint16_t*)a.bufA, (uint32_t)(a.slots * 4 * a.dff),
-            [&](int row) { return row < nrows ? (slot0 + row) * 2 * a.dff : -1; });
-    const typename E::template Mn<C::BN> mb{make_rsrc((const uint16_t*)a.w1 + (size_t)e * 2 * a.dff * a.d,
-                                                      (uint32_t)((size_t)4 * a.dff * a.d))};
-    const uint32_t bcol = (uint32_t)nj * C::BN * 2u, bld = (uint32_t)a.d * 2u;
-    auto ob = E::mn(mb, [=](int kk) -> uint32_t { return (uint32_t)kk * bld + bcol; });
-    f32x16_t acc[C::MB][C::NB];
-    typename E::template Pipe<typename E::template Row<C::BM>, decltype(ob)> p;
-    p.run(da, ob, 2 * a.dff / E::BK, smem, acc);
+struct SrcDx : MSrcBase {
+  using Item = MItem;
+  MOE_DEV void fill(const Item&, int) const {}
+  MOE_DEV RowW opA(const Item& it, int) const { return slotrows(it, a.bufA, 2 * a.dff); }
+  MOE_DEV MnFixedOp opB(const Item& it, int) const {
+    const MnW m{make_rsrc((const uint16_t*)a.w1 + (size_t)it.e * 2 * a.dff * a.d,
+                          (uint32_t)((size_t)4 * a.dff * a.d))};
+    return {m, MnFixed{(uint32_t)a.d * 2u, (uint32_t)it.nj * WC::BN * 2u}};
+  }
+  MOE_DEV int steps(const Item&) const { return 2 * a.dff / kWideBK; }
+  MOE_DEV void epilogue(const Item& it, int, const f32x16_t (&acc)[WC::MB][WC::NB]) const {
+    const int wm = wave_id() / WC::WAVES_N, wn = wave_id() % WC::WAVES_N;
+    uint16_t* dXp = (uint16_t*)a.bufO;
+    const int colb = it.nj * WC::BN + wn * WC::WN;
+    MOE_LDS char* scr = epi_scratch(smem);
 #pragma unroll
-    for (int i = 0; i < C::MB; ++i) {
-      const int row = dual_row<C>(i, lane);
-      if (row >= nrows) continue;
-      uint16_t* orow = dXp + ((size_t)slot0 + row) * a.d + nj * C::BN;
-#pragma unroll
-      for (int j = 0; j < C::NB; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float v[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q];
-          store4(orow + dual_col<C>(j, g, lane), v);
-        }
+    for (int i = 0; i < WC::MB; ++i) {
+      const int rb = wm * WC::WM + i * 32;
+      RowStore<uint16_t, 2>::run(scr, [&](int jj, int g, float* v) {
+        for (int q = 0; q < 4; ++q) v[q] = acc[i][jj][4 * g + q];
+      }, [&](int row, int c, const u32x4_t& d) {
+        if (rb + row < it.nrows) stg16v(dXp + ((size_t)it.slot0 + rb + row) * a.d + colb + c * 8, d);
+      });
     }
   }
+};
+
+// One persistent workgroup per CU for the 256 x 256 tile (8 waves), two per
+// CU for the 128 x 128 tile (4 waves): either way two waves per SIMD.
+template <class Src, class C, class OA, class OB>
+__global__ __launch_bounds__(C::NT, 512 / C::NT) void k_stream(ExecArgs a, int ntiles_n) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  MOE_LDS uint16_t* smem = (MOE_LDS uint16_t*)smem_raw;
+  Src src;
+  src.init(a, smem, ntiles_n);
+  f32x16_t acc[C::MB][C::NB];
+  WideStream<C, OA, OB> p;
+  p.run(src, smem, acc);
 }
 
 // ---- backward: weight gradients per (expert, worker) segment ------------------
@@ -919,110 +1044,118 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dw(ExecArgs a) {
   }
 }
 
-// ---- weight gradients on the direct-to-LDS pipeline, two workgroups per CU ------
-// Weight gradients per (expert, worker) segment; K = the segment's routed rows,
-// in windows of up to kTokWin rows whose token indices sit in an LDS table.
-// dW2[c, n] = sum dy_t[c] * P[n];  dW1[j, c] = sum dZ[j] * x_t[c].
-// Every operand is read in its natural [row][feature] layout through transpose
-// reads; rows past the segment read as zeros.  Tiles are 256 (M) x 128
-// (N) with transposed accumulators: each lane stores 16-byte runs of one fp32
-// output row directly, and the other workgroup on the CU computes meanwhile.
-constexpr int kTokWin = 2048;
-// Byte offset of (source row of K index k, col) in one operand: a gathered
-// token row (token index from the LDS table) or a slot row; kOob past the
-// window, which reads as zeros.
-// The table is read unconditionally and the row picked arithmetically
-// (g = 1: gathered, 0: slot row) so the reads of one step are all in flight
-// together instead of each behind a branch.
-struct DwRows {
-  const MOE_LDS uint16_t* tok;
-  int wrows, s0, ld, col;
-  uint32_t g;
-  MOE_DEV uint32_t operator()(int k) const {
-    const int kk = min(k, wrows - 1);
-    const uint32_t t = tok[kk];
-    const uint32_t row = t * g + (uint32_t)(s0 + kk) * (1u - g);
-    const uint32_t o = (row * (uint32_t)ld + (uint32_t)col) * 2u;
-    return k < wrows ? o : kOob;
+// ---- weight gradients on the persistent wide tile --------------------------------
+// Items are (segment, output tile): a segment is one (expert, worker) run of
+// routed rows, K = its rows.  dW2[c, n] = sum dy_t[c] * P[n] (A: gathered dy
+// rows, B: P rows); dW1[j, c] = sum dZ[j] * x_t[c] (A: dZ rows, B: gathered x
+// rows).  Every operand is read in its natural [row][feature] layout through
+// transpose reads; the token of a gathered row is read from the slot map
+// early in the step before its loads are issued; rows past the segment read
+// as zeros.  fp32 tiles go straight from registers to the owner slot or a
+// replica slot.
+struct MnSeg {
+  const int32_t* slot_to_row;
+  uint32_t kmagic, ld2, col2;
+  int s0, nrows, gather;
+  // the slot map is read for every row (no branch, so nothing waits on it
+  // before the step-end wait) and used only for gathered operands
+  MOE_DEV uint32_t pre(int k) const { return (uint32_t)slot_to_row[s0 + min(k, nrows - 1)]; }
+  MOE_DEV uint32_t post(uint32_t raw, int k) const {
+    const uint32_t row = gather ? token_of(raw, kmagic) : (uint32_t)(s0 + min(k, nrows - 1));
+    return k < nrows ? row * ld2 + col2 : kOob;
   }
 };
-template <class E> struct DwEng {
-  using C = typename E::C;
-  using OA = decltype(E::mn(std::declval<const typename E::template Mn<C::BM>&>(), std::declval<DwRows>()));
-  using OB = decltype(E::mn(std::declval<const typename E::template Mn<C::BN>&>(), std::declval<DwRows>()));
-  using Pipe = typename E::template Pipe<OA, OB>;
-  static constexpr size_t STAGE_BYTES = Pipe::BYTES;
-  static constexpr size_t LDS_BYTES = STAGE_BYTES + (size_t)kTokWin * 2;
-};
+// Weight-gradient tiles: the 256 x 256 wide tile.
+using DwCfg = WideCfg;
+template <class C> using MnSegOpT = Mn64Operand<Mn64<C::BN, C::NT / 64>, MnSeg>;
+using MnSegOp = MnSegOpT<DwCfg>;
+constexpr size_t kDwLds = kStreamLds;
 
-template <class E>
-__global__ __launch_bounds__(E::C::NT, E::MINB) void k_bwd_dw_t(ExecArgs a) {
-  using C = typename E::C;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  __shared__ int tslot;
-  MOE_LDS uint16_t* smem = (MOE_LDS uint16_t*)smem_raw;
-  MOE_LDS uint16_t* tok = smem + DwEng<E>::STAGE_BYTES / 2;
-  constexpr int NW = C::NT / 64;
-  const int r = worker_of_block(a.P);
-  const int n2m = a.d / C::BM, n2n = a.dff / C::BN;          // dW2 [d][dff]
-  const int n1m = 2 * a.dff / C::BM, n1n = a.d / C::BN;      // dW1 [2dff][d]
-  const int per_seg = n2m * n2n + n1m * n1n;
-  const int total = a.seg_cnt[r] * per_seg;
-  const size_t w_elems = (size_t)3 * a.d * a.dff;
-  const uint32_t bx = (uint32_t)((size_t)a.T * a.d * 2);
-  const BufRsrc r_dy = make_rsrc(a.dy, bx), r_x = make_rsrc(a.x, bx);
-  const BufRsrc r_dz = make_rsrc(a.bufA, (uint32_t)(a.slots * 4 * a.dff));
-  const BufRsrc r_p = make_rsrc(a.bufP, (uint32_t)(a.slots * 2 * a.dff));
-  const int lane = threadIdx.x & 63;
-  while (true) {
-    const int tile = next_tile(&a.ctr[PH_DW * kMaxP + r], &tslot);
-    if (tile >= total) break;
-    const int4 sg = a.seg[(size_t)r * a.E + tile / per_seg];
-    const int e = sg.x, slot0 = sg.y, nrows = sg.z, dst = sg.w;
-    if (e < 0) continue;
-    const int loc = tile % per_seg;
-    const bool is2 = loc < n2m * n2n;
-    const int mi = is2 ? loc / n2n : (loc - n2m * n2n) / n1n;
-    const int nj = is2 ? loc % n2n : (loc - n2m * n2n) % n1n;
-    // dW2 = dy^T P (A: gathered dy rows, B: P rows);  dW1 = dZ^T x (A: dZ rows, B: gathered x rows)
-    const typename E::template Mn<C::BM> ma{is2 ? r_dy : r_dz};
-    const typename E::template Mn<C::BN> mb{is2 ? r_p : r_x};
-    f32x16_t acc[C::MB][C::NB];
-    for (int w0 = 0; w0 < nrows; w0 += kTokWin) {
-      const int wrows = min(kTokWin, nrows - w0);
-      const int s0 = slot0 + w0;
-      __syncthreads();                       // previous users of the table are done
-      for (int i = threadIdx.x; i < wrows; i += C::NT) tok[i] = (uint16_t)(a.slot_to_row[s0 + i] / a.k);
-      __syncthreads();
-      uint32_t ga = __builtin_amdgcn_readfirstlane(is2 ? 1u : 0u);
-      asm volatile("" : "+s"(ga));           // opaque: keeps the select arithmetic
-      const DwRows ra{tok, wrows, s0, is2 ? a.d : 2 * a.dff, mi * C::BM, ga};
-      const DwRows rb{tok, wrows, s0, is2 ? a.dff : a.d, nj * C::BN, 1u - ga};
-      typename DwEng<E>::Pipe p;
-      p.run(E::mn(ma, ra), E::mn(mb, rb), (wrows + E::BK - 1) / E::BK, smem, acc, w0 > 0);
-    }
+struct DwItem { int e, slot0, nrows, dst, is2, mi, nj; };
+template <class C> struct SrcDwT {
+  using Item = DwItem;
+  using MnC = Mn64<C::BN, C::NT / 64>;
+  static_assert(C::BM == C::BN, "one MN operand type for both sides");
+  ExecArgs a;              // a copy: the fields stay in scalar registers
+  MOE_LDS uint16_t* smem;
+  int r, n2m, n2n, n1m, n1n, per_seg, count, first, stride;
+  BufRsrc r_dy, r_x, r_dz, r_p;
+  MOE_DEV void init(const ExecArgs& args, MOE_LDS uint16_t* sm, int) {
+    a = args;
+    smem = sm;
+    const WorkerSlot w = worker_slot(args.P);
+    r = w.r;
+    n2m = args.d / C::BM; n2n = args.dff / C::BN;           // dW2 [d][dff]
+    n1m = 2 * args.dff / C::BM; n1n = args.d / C::BN;       // dW1 [2dff][d]
+    per_seg = n2m * n2n + n1m * n1n;
+    count = args.seg_cnt[r] * per_seg;
+    first = w.j;
+    stride = w.n;
+    const uint32_t bx = (uint32_t)((size_t)args.T * args.d * 2);
+    r_dy = make_rsrc(args.dy, bx);
+    r_x = make_rsrc(args.x, bx);
+    r_dz = make_rsrc(args.bufA, (uint32_t)(args.slots * 4 * args.dff));
+    r_p = make_rsrc(args.bufP, (uint32_t)(args.slots * 2 * args.dff));
+  }
+  MOE_DEV Item load(int idx) const {
+    const u32x4_t sg = ((const MOE_CONST u32x4_t*)a.seg)[(size_t)r * a.E + idx / per_seg];
+    const int loc = idx % per_seg;
+    const int is2 = loc < n2m * n2n;
+    const int l1 = loc - n2m * n2n;
+    return {(int)sg.x, (int)sg.y, (int)sg.z, (int)sg.w, is2, is2 ? loc / n2n : l1 / n1n,
+            is2 ? loc % n2n : l1 % n1n};
+  }
+  MOE_DEV void fill(const Item&, int) const {}
+  MOE_DEV MnSegOpT<C> opA(const Item& it, int) const {
+    const MnC m{it.is2 ? r_dy : r_dz};
+    const int ld = it.is2 ? a.d : 2 * a.dff;
+    return {m, MnSeg{a.slot_to_row, a.kmagic, (uint32_t)ld * 2u, (uint32_t)it.mi * C::BM * 2u,
+                     it.slot0, it.nrows, it.is2}};
+  }
+  MOE_DEV MnSegOpT<C> opB(const Item& it, int) const {
+    const MnC m{it.is2 ? r_p : r_x};
+    const int ld = it.is2 ? a.dff : a.d;
+    return {m, MnSeg{a.slot_to_row, a.kmagic, (uint32_t)ld * 2u, (uint32_t)it.nj * C::BN * 2u,
+                     it.slot0, it.nrows, !it.is2}};
+  }
+  MOE_DEV int steps(const Item& it) const { return max(2, (it.nrows + kWideBK - 1) / kWideBK); }
+  MOE_DEV void epilogue(const Item& it, int, const f32x16_t (&acc)[C::MB][C::NB]) const {
+    const int lane = threadIdx.x & 63;
+    const size_t w_elems = (size_t)3 * a.d * a.dff;
     float* out;
     int ldo;
-    if (is2) {
-      out = (dst < 0 ? a.dw2 + (size_t)e * a.d * a.dff
-                     : a.rslots + (size_t)dst * w_elems + (size_t)2 * a.dff * a.d);
+    if (it.is2) {
+      out = (it.dst < 0 ? a.dw2 + (size_t)it.e * a.d * a.dff
+                        : a.rslots + (size_t)it.dst * w_elems + (size_t)2 * a.dff * a.d);
       ldo = a.dff;
     } else {
-      out = (dst < 0 ? a.dw1 + (size_t)e * 2 * a.dff * a.d : a.rslots + (size_t)dst * w_elems);
+      out = (it.dst < 0 ? a.dw1 + (size_t)it.e * 2 * a.dff * a.d : a.rslots + (size_t)it.dst * w_elems);
       ldo = a.d;
     }
-    out += (size_t)mi * C::BM * ldo + (size_t)nj * C::BN;
+    out += (size_t)it.mi * C::BM * ldo + (size_t)it.nj * C::BN;
+    const int wm = wave_id() / C::WAVES_N, wn = wave_id() % C::WAVES_N;
+    MOE_LDS char* scr = epi_scratch(smem);
 #pragma unroll
-    for (int i = 0; i < C::MB; ++i) {
-      float* orow = out + (size_t)acc_row_t<C>(i, lane) * ldo;
+    for (int i = 0; i < C::MB; ++i)
 #pragma unroll
-      for (int j = 0; j < C::NB; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          stg16(orow + acc_col_t<C>(j, g, lane),
-                make_uint4(__float_as_uint(acc[i][j][4 * g]), __float_as_uint(acc[i][j][4 * g + 1]),
-                           __float_as_uint(acc[i][j][4 * g + 2]), __float_as_uint(acc[i][j][4 * g + 3])));
-    }
+      for (int j = 0; j < C::NB; ++j) {
+        float* ob = out + (size_t)(wm * C::WM + i * 32) * ldo + wn * C::WN + j * 32;
+        RowStore<float, 1>::run(scr, [&](int, int g, float* v) {
+          for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q];
+        }, [&](int row, int c, const u32x4_t& d) { stg16v(ob + (size_t)row * ldo + c * 4, d); });
+      }
+  }
+};
+
+using SrcDw = SrcDwT<DwCfg>;
+
+// per-slot gate p (0 for padding slots), read by FC2 and dA through LDS
+__global__ __launch_bounds__(256) void k_slot_gate(const int32_t* __restrict__ slot_to_row,
+                                                   const float* __restrict__ gates, size_t n,
+                                                   float* __restrict__ sgate) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const int row = slot_to_row[i];
+    sgate[i] = row >= 0 ? gates[row] : 0.f;
   }
 }
 
@@ -1090,6 +1223,7 @@ WsLayout exec_layout(const Sizes& z, bool backward) {
   L.bufO = take((size_t)z.act_bytes * z.max_slots * z.d);
   L.rslots = backward ? take(sizeof(float) * (size_t)z.P * z.s * 3 * z.d * z.dff) : o;
   L.bufP = backward ? take((size_t)z.act_bytes * z.max_slots * z.dff) : o;
+  L.sgate = take(sizeof(float) * z.max_slots);
   L.total = o;
   return L;
 }
@@ -1180,6 +1314,8 @@ static ExecArgs make_exec(const Sizes& z, const LayerPtrs& Lp, char* ws, const W
   a.rslots = (float*)(ws + L.rslots);
   a.bufP = ws + L.bufP;
   a.slots = z.max_slots;
+  a.sgate = (const float*)(ws + L.sgate);
+  a.kmagic = (uint32_t)((((uint64_t)1 << 32) + (uint64_t)z.k - 1) / (uint64_t)z.k);
   return a;
 }
 
@@ -1200,51 +1336,47 @@ static void run_forward(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot,
   rec(ev, 4, st);
 }
 
-// The two-workgroup kernels: bf16, 256 | d and 128 | d_ff (every M/N tile
-// extent), and every operand addressed through a buffer descriptor below 2 GiB.
-bool use_dual(const Sizes& z) {
+// The persistent wide-tile kernels: bf16 activations and weights, 256 | d and
+// 256 | d_ff (every M/N tile extent), every operand addressed through a
+// buffer descriptor below 2 GiB, and token = umulhi(row, ceil(2^32/k)) exact
+// for every routed row (row * (ceil(2^32/k) k - 2^32) < 2^32).
+bool use_stream(const Sizes& z) {
   const size_t lim = (size_t)1 << 31;
-  return z.act_bytes == 2 && z.d % 256 == 0 && z.dff % 128 == 0 &&
-         (size_t)z.T * z.d * 2 < lim && z.max_slots * 4 * (size_t)z.dff < lim &&
-         z.max_slots * 2 * (size_t)z.d < lim && (size_t)4 * z.dff * z.d < lim;
+  if (z.act_bytes != 2 || z.d % 256 || z.dff % 256 || z.k <= 0) return false;
+  if ((size_t)z.T * z.d * 2 >= lim || z.max_slots * 4 * (size_t)z.dff >= lim ||
+      z.max_slots * 2 * (size_t)z.d >= lim || (size_t)4 * z.dff * z.d >= lim || z.max_slots * 4 >= lim)
+    return false;
+  const uint64_t magic = (((uint64_t)1 << 32) + (uint64_t)z.k - 1) / (uint64_t)z.k;
+  const uint64_t err = magic * (uint64_t)z.k - ((uint64_t)1 << 32);
+  return (uint64_t)z.T * (uint64_t)z.k * err < ((uint64_t)1 << 32);
 }
 
-template <class E>
-static void run_forward_eng(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* y,
-                            void* const* ev, hipStream_t st) {
-  using C = typename E::C;
-  const size_t lds = E::LDS;
-  static int g1 = persistent_grid(k_fc1_t<E>, C::NT, lds);
-  static int g2 = persistent_grid(k_fc2_t<E>, C::NT, lds);
-  hipLaunchKernelGGL(k_fc1_t<E>, dim3(g1), dim3(C::NT), lds, st, a);
+template <class Src, class C, class OA, class OB>
+static void launch_stream(ExecArgs& a, int ntiles_n, size_t lds, hipStream_t st) {
+  static int g = persistent_grid(k_stream<Src, C, OA, OB>, C::NT, lds);
+  hipLaunchKernelGGL((k_stream<Src, C, OA, OB>), dim3(g), dim3(C::NT), lds, st, a, ntiles_n);
+}
+
+static void launch_slot_gate(const Sizes& z, const ExecArgs& a, hipStream_t st) {
+  const size_t n = z.max_slots;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
+  if (n > 0)
+    hipLaunchKernelGGL(k_slot_gate, dim3(blocks), dim3(256), 0, st, a.slot_to_row, a.gates, n,
+                       (float*)a.sgate);
+}
+
+static void run_forward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* y,
+                               void* const* ev, hipStream_t st) {
+  launch_slot_gate(z, a, st);
+  launch_stream<SrcFc1, WC, RowW, RowW>(a, z.dff / (WC::BN / 2), kStreamLds, st);
   rec(ev, 2, st);
-  hipLaunchKernelGGL(k_fc2_t<E>, dim3(g2), dim3(C::NT), lds, st, a);
+  launch_stream<SrcFc2, WC, RowW, RowW>(a, z.d / WC::BN, kStreamLds, st);
   rec(ev, 3, st);
   const long long nth = (long long)z.T * (z.d / 8);
   if (nth > 0)
     hipLaunchKernelGGL(k_combine<uint16_t>, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, st,
                        (const uint16_t*)a.bufO, row_to_slot, z.T, z.k, z.d, (uint16_t*)y);
   rec(ev, 4, st);
-}
-
-// Engine choice: the wide tile wherever its extents divide the problem
-// (256 | d_ff for the backward's d_ff-wide N tiles), else the two-workgroup
-// tile.  MOE_FFN_ENGINE=dual|wide forces one (for measurement).
-static int engine_override() {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = getenv("MOE_FFN_ENGINE");
-    v = (e && !strcmp(e, "dual")) ? 1 : (e && !strcmp(e, "wide")) ? 2 : 0;
-  }
-  return v;
-}
-static bool wide_fwd(const Sizes& z) { return engine_override() != 1; }
-static bool wide_bwd(const Sizes& z) { return engine_override() != 1 && z.dff % 256 == 0; }
-
-static void run_forward_sel(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* y,
-                            void* const* ev, hipStream_t st) {
-  if (wide_fwd(z)) run_forward_eng<EngWide>(z, a, row_to_slot, y, ev, st);
-  else run_forward_eng<EngDual>(z, a, row_to_slot, y, ev, st);
 }
 
 int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const float* gates,
@@ -1259,7 +1391,7 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
   a.x = x; a.gates = gates; a.slot_to_row = slot_to_row; a.row_to_slot = row_to_slot;
   a.z_save = z_save;
   const bool big = use_big_tiles(z);
-  if (Lp.act_dtype == MOE_BF16 && Lp.w_dtype == MOE_BF16 && use_dual(z)) run_forward_sel(z, a, row_to_slot, y, ev, st);
+  if (Lp.act_dtype == MOE_BF16 && Lp.w_dtype == MOE_BF16 && use_stream(z)) run_forward_stream(z, a, row_to_slot, y, ev, st);
   else if (Lp.act_dtype == MOE_F32) run_forward<float, false, SmallCfg>(z, a, row_to_slot, y, ev, st);
   else if (Lp.w_dtype == MOE_FP8_E4M3) {
     if (big) run_forward<uint16_t, true, BigCfg>(z, a, row_to_slot, y, ev, st);
@@ -1271,39 +1403,23 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
-// The two-workgroup backward also needs token indices that fit the 16-bit
-// LDS table of the weight-gradient kernel.
-bool use_dma_backward(const Sizes& z) { return use_dual(z) && z.T <= 65535; }
-
-template <class E, class EW>
-static void run_backward_eng(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* dx,
-                             float* dw1, float* dw2, void* const* ev, hipStream_t st) {
-  using C = typename E::C;
-  const size_t glds = E::LDS;
-  const size_t wlds = DwEng<EW>::LDS_BYTES;
-  static int ga = persistent_grid(k_bwd_da_t<E>, C::NT, glds);
-  static int gx = persistent_grid(k_bwd_dx_t<E>, C::NT, glds);
-  static int gw = persistent_grid(k_bwd_dw_t<EW>, EW::C::NT, wlds);
-  hipLaunchKernelGGL(k_bwd_da_t<E>, dim3(ga), dim3(C::NT), glds, st, a);
+static void run_backward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* dx,
+                                float* dw1, float* dw2, void* const* ev, hipStream_t st) {
+  launch_slot_gate(z, a, st);
+  launch_stream<SrcDa, WC, RowW, MnFixedOp>(a, z.dff / WC::BN, kStreamLds, st);
   rec(ev, 2, st);
-  hipLaunchKernelGGL(k_bwd_dx_t<E>, dim3(gx), dim3(C::NT), glds, st, a);
+  launch_stream<SrcDx, WC, RowW, MnFixedOp>(a, z.d / WC::BN, kStreamLds, st);
   rec(ev, 3, st);
   const long long nth = (long long)z.T * (z.d / 8);
   if (nth > 0)
     hipLaunchKernelGGL(k_combine<uint16_t>, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, st,
                        (const uint16_t*)a.bufO, row_to_slot, z.T, z.k, z.d, (uint16_t*)dx);
   rec(ev, 4, st);
-  hipLaunchKernelGGL(k_bwd_dw_t<EW>, dim3(gw), dim3(EW::C::NT), wlds, st, a);
+  launch_stream<SrcDw, DwCfg, MnSegOp, MnSegOp>(a, 0, kDwLds, st);
   rec(ev, 5, st);
   hipLaunchKernelGGL(k_bwd_reduce, dim3(num_cus() * 4), dim3(256), 0, st, a.rep_slot,
                      a.owner_has, (const float*)a.rslots, z.E, z.P, z.d, z.dff, dw1, dw2);
   rec(ev, 6, st);
-}
-
-static void run_backward_sel(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* dx,
-                             float* dw1, float* dw2, void* const* ev, hipStream_t st) {
-  if (wide_bwd(z)) run_backward_eng<EngWide, EngWide>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
-  else run_backward_eng<EngDual, EngDual>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
 }
 
 template <typename T, class C>
@@ -1345,7 +1461,7 @@ int launch_backward(const Sizes& z, const LayerPtrs& Lp, const void* x, const fl
   a.z_save = const_cast<void*>(z_save);
   a.dy = dy; a.dw1 = dw1; a.dw2 = dw2;
   if (Lp.act_dtype == MOE_F32) run_backward<float, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
-  else if (use_dma_backward(z)) run_backward_sel(z, a, row_to_slot, dx, dw1, dw2, ev, st);
+  else if (use_stream(z)) run_backward_stream(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else if (use_big_tiles(z)) run_backward<uint16_t, BigCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else run_backward<uint16_t, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;

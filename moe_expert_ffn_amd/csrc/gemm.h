@@ -66,7 +66,18 @@ union V16 {
 
 MOE_DEV uint4 zero4() { return make_uint4(0, 0, 0, 0); }
 
-MOE_DEV int wave_id() { return threadIdx.x >> 6; }
+// wave index within the workgroup, known to the compiler to be wave-uniform
+MOE_DEV int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Lanes of one wave exchanging data through LDS.  The hardware keeps a wave's
+// LDS accesses in order, so no wait is needed; the wavefront-scope fences tell
+// the compiler that other lanes read and write the memory, so it neither
+// reuses a value loaded before the exchange nor moves an access across it.
+MOE_DEV void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // ---- MFMA on one K chunk of the staged tile -------------------------------
 template <class C>
@@ -472,6 +483,8 @@ template <int MN, int NWAVES> struct MnDma {
   static_assert(NI * RPI * NWAVES == 32, "32 K rows per stage");
   BufRsrc rs;
   struct Offs { uint32_t o[NI]; };
+  // stage row (K index within the step) loaded by this lane's instruction i
+  static MOE_DEV int row_of(int i) { return ((threadIdx.x >> 6) + NWAVES * i) * RPI + (threadIdx.x & 63) / CPR; }
   template <class F> MOE_DEV Offs prep_rows(int kt, F rowoff) const {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     Offs p;
@@ -735,6 +748,16 @@ template <int ROWS, int NWAVES> struct Row64 {
       off[i] = o < 0 ? kOob : (uint32_t)o * 2u + (uint32_t)(((lane & 7) ^ swz_row128(row)) * 16);
     }
   }
+  // Rows this lane loads: row(i) = (wave + NWAVES i) * 8 + lane / 8.
+  static MOE_DEV int lane_row(int i) { return ((threadIdx.x >> 6) + NWAVES * i) * 8 + ((threadIdx.x & 63) >> 3); }
+  // From the element offsets of this lane's rows (-1 = zero row).
+  MOE_DEV void init_offsets(const uint16_t* b, uint32_t bytes, const int (&o)[NI]) {
+    rs = make_rsrc(b, bytes);
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      off[i] = o[i] < 0 ? kOob : (uint32_t)o[i] * 2u + (uint32_t)(((lane & 7) ^ swz_row128(lane_row(i))) * 16);
+  }
   struct Offs { uint32_t o[NI]; };
   MOE_DEV Offs prep(int kt) const {
     Offs q;
@@ -773,6 +796,8 @@ template <int MN, int NWAVES> struct Mn64 {
   static_assert(NI * RPI * NWAVES == kWideBK, "64 K rows per stage");
   BufRsrc rs;
   struct Offs { uint32_t o[NI]; };
+  // stage row (K index within the step) loaded by this lane's instruction i
+  static MOE_DEV int row_of(int i) { return ((threadIdx.x >> 6) + NWAVES * i) * RPI + (threadIdx.x & 63) / CPR; }
   template <class F> MOE_DEV Offs prep_rows(int kt, F rowoff) const {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     Offs p;
@@ -820,14 +845,34 @@ template <int MN, int NWAVES> struct Mn64 {
   }
 };
 
+// MN-contiguous operand bound to its row function.  F::pre(k) gives a raw
+// value for K index k (an index, or a value loaded from memory, not yet
+// combined with anything, so no wait is needed until the loads are issued),
+// F::post(raw, k) turns it into the byte offset of (row, mn0) in the buffer,
+// or kOob for a zero row.  prep() runs early in a step, issue() after the
+// step-end wait.
 template <class OP, class F> struct Mn64Operand {
-  const OP& op;
-  F rowoff;
+  OP op;
+  F f;
   static constexpr int NI = OP::NI, STAGE_BYTES = OP::STAGE_BYTES;
   using Lane = typename OP::Lane;
-  using Offs = typename OP::Offs;
-  MOE_DEV Offs prep(int kt) const { return op.prep_rows(kt, rowoff); }
-  MOE_DEV void issue(const Offs& p, MOE_LDS char* st) const { op.issue(p, st); }
+  struct Offs { uint32_t raw[NI]; int kt; };
+  MOE_DEV Offs prep(int kt) const {
+    Offs p;
+    p.kt = kt;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) p.raw[i] = f.pre(kt * kWideBK + OP::row_of(i));
+    return p;
+  }
+  MOE_DEV void issue(const Offs& p, MOE_LDS char* st) const {
+    typename OP::Offs q;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = OP::row_of(i);
+      q.o[i] = f.post(p.raw[i], p.kt * kWideBK + r) + (uint32_t)(((threadIdx.x & 63) % OP::CPR) ^ swz_tr(r)) * 16u;
+    }
+    op.issue(q, st);
+  }
   static MOE_DEV Lane lane_info(int wave_base, int lane) { return OP::lane_info(wave_base, lane); }
   template <int KC> static MOE_DEV bf16x8_t frag(const MOE_LDS char* st, const Lane& L, int i) {
     return OP::template frag<KC>(st, L, i);
@@ -928,6 +973,174 @@ template <class C, class OA, class OB> struct WidePipe {
     __syncthreads();                      // all loads landed, all waves done with the stages
   }
 };
+
+// ---- wide tile, persistent across tiles -------------------------------------
+// The same per-step schedule as WidePipe, but the stream of K steps runs on
+// from one work item to the next: the first two steps of the next item are
+// issued during the last two steps of the current one, so a tile starts with
+// its operands already in LDS, and the previous tile's stores drain while the
+// next tile's first step computes.  Items come from a static per-workgroup
+// sequence (no queue atomics).  Because vector-memory completions are counted
+// in order, nothing issued while loads are in flight may be waited for early:
+// an item's descriptor is read three items ahead, its per-row data (moved
+// into LDS by direct loads) two items ahead, and its operands are set up one
+// item ahead; every one of those waits falls on a step-end wait that happens
+// anyway.
+//
+// Src provides:
+//   Item load(int idx)                 descriptor of item idx (plain loads)
+//   void fill(const Item&, int slot)   issue direct loads of per-row data into LDS
+//                                      item slot `slot` (after a barrier: the
+//                                      slot's previous item is finished)
+//   OA opA(const Item&, int slot), OB opB(const Item&, int slot)
+//   int steps(const Item&)             K steps, >= 2
+//   void epilogue(const Item&, int slot, acc)
+//   int count, first, stride           items first, first + stride, ... < count
+template <class C, class OA, class OB> struct WideStream {
+  static constexpr int SA = OA::STAGE_BYTES, STAGE = OA::STAGE_BYTES + OB::STAGE_BYTES;
+  static constexpr int LPS = OA::NI + OB::NI;
+  static constexpr size_t BYTES = (size_t)kWideStages * STAGE;
+  bf16x8_t a[2][C::MB], b[2][C::NB];
+  typename OA::Lane la;
+  typename OB::Lane lb;
+  template <int KC, int S> MOE_DEV void read(const MOE_LDS char* st) {
+#pragma unroll
+    for (int i = 0; i < C::MB; ++i) a[S][i] = OA::template frag<KC>(st, la, i);
+#pragma unroll
+    for (int j = 0; j < C::NB; ++j) b[S][j] = OB::template frag<KC>(st + SA, lb, j);
+  }
+  template <int S> MOE_DEV void mma(f32x16_t (&acc)[C::MB][C::NB]) const {
+#pragma unroll
+    for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[S][j], a[S][i], acc[i][j], 0, 0, 0);
+  }
+  template <class Src>
+  MOE_DEV void run(Src& src, MOE_LDS uint16_t* smem16, f32x16_t (&acc)[C::MB][C::NB]) {
+    MOE_LDS char* smem = (MOE_LDS char*)smem16;
+    const int lane = threadIdx.x & 63;
+    const int s = src.stride;
+    int idx = src.first;
+    if (idx >= src.count) return;
+    la = OA::lane_info((wave_id() / C::WAVES_N) * C::WM, lane);
+    lb = OB::lane_info((wave_id() % C::WAVES_N) * C::WN, lane);
+    using Item = typename Src::Item;
+    // prologue: items 0 and 1 filled, item 2's descriptor read
+    Item it0 = src.load(idx), it1 = it0, it2 = it0;
+    bool h1 = idx + s < src.count, h2 = idx + 2 * s < src.count;
+    if (h1) it1 = src.load(idx + s);
+    if (h2) it2 = src.load(idx + 2 * s);
+    src.fill(it0, 0);
+    if (h1) src.fill(it1, 1);
+    wait_vm_lgkm0<0>();
+    __syncthreads();
+    int slot = 0;                                // LDS item slot of it0 (items rotate over 3)
+    OA a0 = src.opA(it0, slot);
+    OB b0 = src.opB(it0, slot);
+    int n0 = src.steps(it0);
+#pragma unroll
+    for (int st = 0; st < kWideStages; ++st) {
+      const auto pa = a0.prep(st);
+      const auto pb = b0.prep(st);
+      a0.issue(pa, smem + st * STAGE);
+      b0.issue(pb, smem + st * STAGE + SA);
+    }
+    wait_vm_lgkm0<(kWideStages - 1) * LPS>();
+    __builtin_amdgcn_s_barrier();
+    read<0, 0>(smem);
+    int g = 0;                                   // global step index: stage g & 1
+    while (true) {
+      const int s1 = slot == 2 ? 0 : slot + 1, s2 = s1 == 2 ? 0 : s1 + 1;
+      const bool h3 = idx + 3 * s < src.count;
+      Item it3 = it2;
+      if (h3) it3 = src.load(idx + 3 * s);
+      OA a1 = a0;
+      OB b1 = b0;
+      int n1 = n0;
+      if (h1) { a1 = src.opA(it1, s1); b1 = src.opB(it1, s1); n1 = src.steps(it1); }
+#pragma unroll
+      for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NB; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      // the item's first step landed before the previous item's last barrier
+      if (g > 0) read<0, 0>(smem + (g & 1) * STAGE);
+      for (int kt = 0; kt < n0; ++kt, ++g) {
+        const MOE_LDS char* st = smem + (g & 1) * STAGE;
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_sched_barrier(0);
+        read<1, 1>(st);
+        // step g + 2 of the stream: this item, the next one, or a harmless
+        // re-read of this item's last step when the stream ends
+        const bool own = kt + 2 < n0;
+        const bool nxt = !own && h1;
+        const int ks = own ? kt + 2 : nxt ? kt + 2 - n0 : n0 - 1;
+        const auto pa = nxt ? a1.prep(ks) : a0.prep(ks);
+        const auto pb = nxt ? b1.prep(ks) : b0.prep(ks);
+        __builtin_amdgcn_sched_barrier(0);
+        mma<0>(acc);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_sched_barrier(0);
+        read<2, 0>(st);
+        __builtin_amdgcn_sched_barrier(0);
+        mma<1>(acc);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_sched_barrier(0);
+        read<3, 1>(st);
+        __builtin_amdgcn_sched_barrier(0);
+        mma<0>(acc);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm_lgkm0<0>();
+        __builtin_amdgcn_s_barrier();
+        // every wave is past the previous item's epilogue: item slot s2 is free
+        if (kt == 0 && h2) src.fill(it2, s2);
+        if (nxt) {
+          a1.issue(pa, smem + (g & 1) * STAGE);
+          b1.issue(pb, smem + (g & 1) * STAGE + SA);
+        } else {
+          a0.issue(pa, smem + (g & 1) * STAGE);
+          b0.issue(pb, smem + (g & 1) * STAGE + SA);
+        }
+        // chunk 0 of the next step; for the next item it is read after the
+        // epilogue, so its fragments are not live across it
+        if (kt + 1 < n0) read<0, 0>(smem + ((g + 1) & 1) * STAGE);
+        __builtin_amdgcn_sched_barrier(0);
+        mma<1>(acc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      src.epilogue(it0, slot, acc);
+      if (!h1) break;
+      idx += s;
+      slot = s1;
+      it0 = it1;
+      a0 = a1;
+      b0 = b1;
+      n0 = n1;
+      it1 = it2;
+      h1 = h2;
+      it2 = it3;
+      h2 = h3;
+    }
+    wait_vm_lgkm0<0>();
+    __syncthreads();                      // all loads landed, all waves done with the stages
+  }
+};
+
+// This workgroup's place among its worker's workgroups: worker r owns the
+// XCDs x with x * P / 8 == r; the workgroups of a launch are dealt to XCDs
+// round-robin (blockIdx % 8).
+struct WorkerSlot { int r, j, n; };
+MOE_DEV WorkerSlot worker_slot(int P) {
+  const int x = (int)(blockIdx.x % kXcds), per = kXcds / P;
+  const int r = x * P / kXcds;
+  const int j = (int)(blockIdx.x / kXcds) * per + (x - r * per);
+  const int n = (int)(gridDim.x / kXcds) * per;
+  return {r, j, n};
+}
 
 // Coordinates of accumulator register r of block (i, j) for this lane, within
 // the tile.

@@ -24,7 +24,7 @@ struct Sizes {
 };
 
 struct WsLayout {
-  size_t ctr, mt_cnt, mt, seg_cnt, seg, rep_slot, owner_has, bufA, bufO, rslots, bufP, total;
+  size_t ctr, mt_cnt, mt, seg_cnt, seg, rep_slot, owner_has, bufA, bufO, rslots, bufP, sgate, total;
 };
 
 WsLayout exec_layout(const Sizes& z, bool backward);

@@ -20,6 +20,10 @@ SMALL = {
                             beta=32, P=8, s=3, kappas=(0,), cfg_id=22),
     "small_f32": Workload("small_f32", "f32", "f32", T=150, k=3, E=6, d=256, d_ff=128,
                           beta=16, P=2, s=1, kappas=(0,), cfg_id=23),
+    # d and d_ff multiples of 256: the persistent 256 x 256 tile kernels (dA, dX,
+    # dW through the per-wave LDS store staging), replicas reduced into owners
+    "stream_bf16": Workload("stream_bf16", "bf16", "bf16", T=700, k=4, E=8, d=512, d_ff=256,
+                            beta=128, P=8, s=4, kappas=(0,), cfg_id=24),
 }
 
 
@@ -55,7 +59,7 @@ def test_backward_full_parity(name):
     assert max(e_dx, e_w1, e_w2) <= tol
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16", "beta32_bf16"])
+@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16", "beta32_bf16", "stream_bf16"])
 def test_backward_plan_invariance(name):
     w = WORKLOADS.get(name) or SMALL[name]
     say(f"[bwd-invariance] {name}")
