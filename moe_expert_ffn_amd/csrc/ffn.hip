@@ -583,8 +583,13 @@ template <typename T, int SEG> struct RowStore {
   static constexpr int RB = 32 * SEG * (int)sizeof(T);
   static constexpr int CPR = RB / 16;
   static constexpr int NRD = 16 * CPR / 64;                 // read/store instructions per half block
+  static constexpr int STORES = 2 * NRD;                    // emits per block
   static_assert(RB == 64 || RB == 128, "segment row bytes");
-  static MOE_DEV int swz(int r) { return RB == 128 ? (r >> 1) & 7 : (r >> 2) & 3; }
+  // measured on gfx950 (bank-conflict counter): with these chunk swizzles the
+  // row-block reads are conflict-free, the fp32 16-byte writes too, and the
+  // bf16 8-byte writes of half the lanes take the 2 extra cycles that every
+  // swizzle tried leaves them
+  static MOE_DEV int swz(int r) { return RB == 128 ? r & 7 : (r >> 2) & 3; }
   // vals(jj, g, v): the 4 values of quad g of block j0 + jj of this lane's row;
   // emit(row, chunk, data): store 16 bytes at `row` (0..31 inside the block)
   // and 16-byte chunk `chunk` of the segment.
@@ -654,6 +659,12 @@ MOE_DEV MOE_LDS char* epi_scratch(MOE_LDS uint16_t* smem) {
   return (MOE_LDS char*)smem + kEpiOff + (size_t)wave_id() * kEpiWave;
 }
 MOE_DEV void stg16v(void* p, const u32x4_t& d) { *(MOE_GLB u32x4_t*)p = d; }
+// 16 bytes at element column `col` of slot row `srow` of a [slots][ld] bf16
+// buffer; a row past the tile's end is sent out of range and dropped, so an
+// epilogue issues the same number of stores for every tile
+MOE_DEV void st_row16(const BufRsrc& r, int srow, int ld, int col, bool ok, const u32x4_t& d) {
+  buf_store16(r, ok ? ((uint32_t)srow * (uint32_t)ld + (uint32_t)col) * 2u : kOob, d);
+}
 
 MOE_DEV const MOE_LDS int* item_rows(const MOE_LDS uint16_t* smem, int slot) {
   return (const MOE_LDS int*)((const MOE_LDS char*)smem + kStageBytes + slot * kItemBytes);
@@ -726,8 +737,9 @@ struct MSrcBase {
 // K-major weight operand: row k of a [K][ld] matrix from column col.
 struct MnFixed {
   uint32_t ld2, col2;
-  MOE_DEV uint32_t pre(int k) const { return (uint32_t)k; }
-  MOE_DEV uint32_t post(uint32_t raw, int) const { return raw * ld2 + col2; }
+  using Raw = uint32_t;
+  MOE_DEV Raw pre(int, int k) const { return (uint32_t)k; }
+  MOE_DEV uint32_t post(Raw raw, int) const { return raw * ld2 + col2; }
 };
 using MnFixedOp = Mn64Operand<MnW, MnFixed>;
 
@@ -749,18 +761,23 @@ struct SrcFc1 : MSrcBase {
     return w;
   }
   MOE_DEV int steps(const Item&) const { return a.d / kWideBK; }
+  static constexpr int kEpiVmA = WC::MB * RowStore<uint16_t, 1>::STORES;   // A only
+  MOE_DEV void relaxed_wait() const {
+    if (a.z_save) wait_vm_lgkm0<3 * kEpiVmA>();
+    else wait_vm_lgkm0<kEpiVmA>();
+  }
   MOE_DEV void epilogue(const Item& it, int, const f32x16_t (&acc)[WC::MB][WC::NB]) const {
     const int wm = wave_id() / WC::WAVES_N, wn = wave_id() % WC::WAVES_N;
-    uint16_t* Ab = (uint16_t*)a.bufA;
-    uint16_t* Z = (uint16_t*)a.z_save;
     const int dff = a.dff, colb = it.nj * (WC::BN / 2) + wn * 32;
+    const BufRsrc ra = make_rsrc(a.bufA, (uint32_t)(a.slots * dff * 2));
+    const BufRsrc rz = make_rsrc(a.z_save, (uint32_t)(a.slots * dff * 4));
     MOE_LDS char* scr = epi_scratch(smem);
 #pragma unroll
     for (int i = 0; i < WC::MB; ++i) {
       const int rb = wm * WC::WM + i * 32;
-      auto emit_to = [&](uint16_t* base, size_t ld) {
-        return [&, base, ld](int row, int c, const u32x4_t& d) {
-          if (rb + row < it.nrows) stg16v(base + ((size_t)it.slot0 + rb + row) * ld + colb + c * 8, d);
+      auto emit_to = [&](const BufRsrc& r, int col0, int ld) {
+        return [&, col0, ld](int row, int c, const u32x4_t& d) {
+          st_row16(r, it.slot0 + rb + row, ld, col0 + colb + c * 8, rb + row < it.nrows, d);
         };
       };
       RowStore<uint16_t, 1>::run(scr, [&](int, int g, float* v) {
@@ -768,14 +785,14 @@ struct SrcFc1 : MSrcBase {
           const float gv = acc[i][0][4 * g + q];
           v[q] = gv * sigm(gv) * acc[i][1][4 * g + q];
         }
-      }, emit_to(Ab, dff));
-      if (Z) {
+      }, emit_to(ra, 0, dff));
+      if (a.z_save) {
         RowStore<uint16_t, 1>::run(scr, [&](int, int g, float* v) {
           for (int q = 0; q < 4; ++q) v[q] = acc[i][0][4 * g + q];
-        }, emit_to(Z, 2 * dff));
+        }, emit_to(rz, 0, 2 * dff));
         RowStore<uint16_t, 1>::run(scr, [&](int, int g, float* v) {
           for (int q = 0; q < 4; ++q) v[q] = acc[i][1][4 * g + q];
-        }, emit_to(Z + dff, 2 * dff));
+        }, emit_to(rz, dff, 2 * dff));
       }
     }
   }
@@ -794,10 +811,12 @@ struct SrcFc2 : MSrcBase {
     return w;
   }
   MOE_DEV int steps(const Item&) const { return a.dff / kWideBK; }
+  static constexpr int kEpiVm = WC::MB * RowStore<uint16_t, 2>::STORES;
+  MOE_DEV void relaxed_wait() const { wait_vm_lgkm0<kEpiVm>(); }
   MOE_DEV void epilogue(const Item& it, int slot, const f32x16_t (&acc)[WC::MB][WC::NB]) const {
     const int lane = threadIdx.x & 63, wm = wave_id() / WC::WAVES_N, wn = wave_id() % WC::WAVES_N;
     const MOE_LDS float* gt = item_gates(smem, slot);
-    uint16_t* O = (uint16_t*)a.bufO;
+    const BufRsrc ro = make_rsrc(a.bufO, (uint32_t)(a.slots * a.d * 2));
     const int colb = it.nj * WC::BN + wn * WC::WN;
     MOE_LDS char* scr = epi_scratch(smem);
 #pragma unroll
@@ -807,7 +826,7 @@ struct SrcFc2 : MSrcBase {
       RowStore<uint16_t, 2>::run(scr, [&](int jj, int g, float* v) {
         for (int q = 0; q < 4; ++q) v[q] = pg * acc[i][jj][4 * g + q];
       }, [&](int row, int c, const u32x4_t& d) {
-        if (rb + row < it.nrows) stg16v(O + ((size_t)it.slot0 + rb + row) * a.d + colb + c * 8, d);
+        st_row16(ro, it.slot0 + rb + row, a.d, colb + c * 8, rb + row < it.nrows, d);
       });
     }
   }
@@ -826,63 +845,76 @@ struct SrcDa : MSrcBase {
     return {m, MnFixed{(uint32_t)a.dff * 2u, (uint32_t)it.nj * WC::BN * 2u}};
   }
   MOE_DEV int steps(const Item&) const { return a.d / kWideBK; }
+  // per 32 x 32 block: 8 [G, U] loads and three row-store runs
+  static constexpr int kEpiVm = WC::MB * WC::NB * (8 + 3 * RowStore<uint16_t, 1>::STORES);
+  MOE_DEV void relaxed_wait() const { wait_vm_lgkm0<(kEpiVm < 63 ? kEpiVm : 63)>(); }
   MOE_DEV void epilogue(const Item& it, int slot, const f32x16_t (&acc)[WC::MB][WC::NB]) const {
+    constexpr int NBLK = WC::MB * WC::NB;
     const int lane = threadIdx.x & 63, wm = wave_id() / WC::WAVES_N, wn = wave_id() % WC::WAVES_N;
     const MOE_LDS float* gt = item_gates(smem, slot);
     const uint16_t* Z = (const uint16_t*)a.z_save;
-    uint16_t* dZ = (uint16_t*)a.bufA;
-    uint16_t* PA = (uint16_t*)a.bufP;
     const int dff = a.dff, colb = it.nj * WC::BN + wn * WC::WN;
+    const BufRsrc rdz = make_rsrc(a.bufA, (uint32_t)(a.slots * dff * 4));
+    const BufRsrc rp = make_rsrc(a.bufP, (uint32_t)(a.slots * dff * 2));
     MOE_LDS char* scr = epi_scratch(smem);
-    // per 32 x 32 block: the 8 [G, U] loads of the lane's row are issued
-    // together, then dG, dU and P are formed in one pass (one sigmoid per
-    // element) and leave through the per-wave scratch as 64-byte row pieces
-#pragma unroll
-    for (int i = 0; i < WC::MB; ++i) {
-      const int rb = wm * WC::WM + i * 32, myrow = rb + (lane & 31);
-      const float pg = gt[myrow];
+    // Block b = (i, j) of 32 x 32.  The lane's [G, U] of block b + 1 are loaded
+    // into the same registers once block b's last output is formed and before
+    // its stores are issued, so waiting for them never waits for those stores.
+    // dG, dU and P leave through the per-wave scratch as 64-byte row pieces.
+    u32x2_t zg[4], zu[4];
+    auto zload = [&](int b, u32x2_t (&g_)[4], u32x2_t (&u_)[4]) {
+      const int i = b / WC::NB, j = b % WC::NB;
+      const int myrow = wm * WC::WM + i * 32 + (lane & 31);
       const size_t sr = (size_t)it.slot0 + (myrow < it.nrows ? myrow : 0);
 #pragma unroll
-      for (int j = 0; j < WC::NB; ++j) {
-        const int cb = colb + j * 32;
-        u32x2_t zg[4], zu[4];
+      for (int g = 0; g < 4; ++g) {
+        const int n = colb + j * 32 + 8 * g + 4 * (lane >> 5);
+        g_[g] = *(const MOE_GLB u32x2_t*)(Z + sr * 2 * dff + n);
+        u_[g] = *(const MOE_GLB u32x2_t*)(Z + sr * 2 * dff + dff + n);
+      }
+    };
+    zload(0, zg, zu);
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b) {
+      const int i = b / WC::NB, j = b % WC::NB;
+      const int rb = wm * WC::WM + i * 32, cb = colb + j * 32;
+      const float pg = gt[rb + (lane & 31)];
+      using RS = RowStore<uint16_t, 1>;
+      auto emit_to = [&](const BufRsrc& r, int col0, int ld) {
+        return [&, col0, ld](int row, int c, const u32x4_t& d) {
+          st_row16(r, it.slot0 + rb + row, ld, col0 + cb + c * 8, rb + row < it.nrows, d);
+        };
+      };
+      // one output per pass, 8 packed registers at a time; the sigmoid is
+      // taken again in each pass (the empty asm keeps the passes apart, so
+      // the compiler does not hold 32 sigmoids across them)
+      auto pass = [&](int which, RS::Packed (&p)[1][4]) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int n = cb + 8 * g + 4 * (lane >> 5);
-          zg[g] = *(const MOE_GLB u32x2_t*)(Z + sr * 2 * dff + n);
-          zu[g] = *(const MOE_GLB u32x2_t*)(Z + sr * 2 * dff + dff + n);
-        }
-        using RS = RowStore<uint16_t, 1>;
-        RS::Packed pgp[1][4], pup[1][4], ppp[1][4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float vg[4], vu[4], vp[4];
+          float v[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const uint32_t wg = q < 2 ? zg[g].x : zg[g].y, wu = q < 2 ? zu[g].x : zu[g].y;
-            const float gv = bf2f((uint16_t)((q & 1) ? wg >> 16 : wg & 0xffff));
+            float gv = bf2f((uint16_t)((q & 1) ? wg >> 16 : wg & 0xffff));
+            asm volatile("" : "+v"(gv));
             const float uv = bf2f((uint16_t)((q & 1) ? wu >> 16 : wu & 0xffff));
-            const float sg = sigm(gv), da = pg * acc[i][j][4 * g + q];
-            vg[q] = da * uv * sg * (1.f + gv * (1.f - sg));
-            vu[q] = da * gv * sg;
-            vp[q] = pg * (gv * sg * uv);
+            const float sg = sigm(gv);
+            if (which == 0) v[q] = pg * acc[i][j][4 * g + q] * uv * sg * (1.f + gv * (1.f - sg));
+            else if (which == 1) v[q] = pg * acc[i][j][4 * g + q] * gv * sg;
+            else v[q] = pg * (gv * sg * uv);
           }
-          pgp[0][g] = u32x2_t{(uint32_t)f2bf(vg[0]) | ((uint32_t)f2bf(vg[1]) << 16),
-                              (uint32_t)f2bf(vg[2]) | ((uint32_t)f2bf(vg[3]) << 16)};
-          pup[0][g] = u32x2_t{(uint32_t)f2bf(vu[0]) | ((uint32_t)f2bf(vu[1]) << 16),
-                              (uint32_t)f2bf(vu[2]) | ((uint32_t)f2bf(vu[3]) << 16)};
-          ppp[0][g] = u32x2_t{(uint32_t)f2bf(vp[0]) | ((uint32_t)f2bf(vp[1]) << 16),
-                              (uint32_t)f2bf(vp[2]) | ((uint32_t)f2bf(vp[3]) << 16)};
+          p[0][g] = u32x2_t{(uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16),
+                            (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16)};
         }
-        auto emit_to = [&](uint16_t* base, size_t ld) {
-          return [&, base, ld](int row, int c, const u32x4_t& d) {
-            if (rb + row < it.nrows) stg16v(base + ((size_t)it.slot0 + rb + row) * ld + cb + c * 8, d);
-          };
-        };
-        RS::store(scr, pgp, emit_to(dZ, 2 * dff));
-        RS::store(scr, pup, emit_to(dZ + dff, 2 * dff));
-        RS::store(scr, ppp, emit_to(PA, dff));
-      }
+      };
+      RS::Packed pk[1][4];
+      pass(0, pk);
+      RS::store(scr, pk, emit_to(rdz, 0, 2 * dff));
+      pass(1, pk);
+      RS::store(scr, pk, emit_to(rdz, dff, 2 * dff));
+      pass(2, pk);
+      if (b + 1 < NBLK) zload(b + 1, zg, zu);
+      RS::store(scr, pk, emit_to(rp, 0, dff));
     }
   }
 };
@@ -898,9 +930,11 @@ struct SrcDx : MSrcBase {
     return {m, MnFixed{(uint32_t)a.d * 2u, (uint32_t)it.nj * WC::BN * 2u}};
   }
   MOE_DEV int steps(const Item&) const { return 2 * a.dff / kWideBK; }
+  static constexpr int kEpiVm = WC::MB * RowStore<uint16_t, 2>::STORES;
+  MOE_DEV void relaxed_wait() const { wait_vm_lgkm0<kEpiVm>(); }
   MOE_DEV void epilogue(const Item& it, int, const f32x16_t (&acc)[WC::MB][WC::NB]) const {
     const int wm = wave_id() / WC::WAVES_N, wn = wave_id() % WC::WAVES_N;
-    uint16_t* dXp = (uint16_t*)a.bufO;
+    const BufRsrc ro = make_rsrc(a.bufO, (uint32_t)(a.slots * a.d * 2));
     const int colb = it.nj * WC::BN + wn * WC::WN;
     MOE_LDS char* scr = epi_scratch(smem);
 #pragma unroll
@@ -909,7 +943,7 @@ struct SrcDx : MSrcBase {
       RowStore<uint16_t, 2>::run(scr, [&](int jj, int g, float* v) {
         for (int q = 0; q < 4; ++q) v[q] = acc[i][jj][4 * g + q];
       }, [&](int row, int c, const u32x4_t& d) {
-        if (rb + row < it.nrows) stg16v(dXp + ((size_t)it.slot0 + rb + row) * a.d + colb + c * 8, d);
+        st_row16(ro, it.slot0 + rb + row, a.d, colb + c * 8, rb + row < it.nrows, d);
       });
     }
   }
@@ -1057,10 +1091,11 @@ struct MnSeg {
   const int32_t* slot_to_row;
   uint32_t kmagic, ld2, col2;
   int s0, nrows, gather;
-  // the slot map is read for every row (no branch, so nothing waits on it
-  // before the step-end wait) and used only for gathered operands
-  MOE_DEV uint32_t pre(int k) const { return (uint32_t)slot_to_row[s0 + min(k, nrows - 1)]; }
-  MOE_DEV uint32_t post(uint32_t raw, int k) const {
+  // The slot map is read for every row (no branch, so nothing waits on it
+  // before the step-end wait) and used only for gathered operands.
+  using Raw = uint32_t;
+  MOE_DEV Raw pre(int, int k) const { return (uint32_t)slot_to_row[s0 + min(k, nrows - 1)]; }
+  MOE_DEV uint32_t post(Raw raw, int k) const {
     const uint32_t row = gather ? token_of(raw, kmagic) : (uint32_t)(s0 + min(k, nrows - 1));
     return k < nrows ? row * ld2 + col2 : kOob;
   }
@@ -1076,6 +1111,7 @@ template <class C> struct SrcDwT {
   using Item = DwItem;
   using MnC = Mn64<C::BN, C::NT / 64>;
   static_assert(C::BM == C::BN, "one MN operand type for both sides");
+  static_assert(MnC::RPI == 2, "a load instruction covers the K row pair kb, kb + 1");
   ExecArgs a;              // a copy: the fields stay in scalar registers
   MOE_LDS uint16_t* smem;
   int r, n2m, n2n, n1m, n1n, per_seg, count, first, stride;
@@ -1119,6 +1155,9 @@ template <class C> struct SrcDwT {
                      it.slot0, it.nrows, !it.is2}};
   }
   MOE_DEV int steps(const Item& it) const { return max(2, (it.nrows + kWideBK - 1) / kWideBK); }
+  // vector memory operations of one epilogue, per wave: all stores
+  static constexpr int kEpiVm = C::MB * C::NB * RowStore<float, 1>::STORES;
+  MOE_DEV void relaxed_wait() const { wait_vm_lgkm0<(kEpiVm < 63 ? kEpiVm : 63)>(); }
   MOE_DEV void epilogue(const Item& it, int, const f32x16_t (&acc)[C::MB][C::NB]) const {
     const int lane = threadIdx.x & 63;
     const size_t w_elems = (size_t)3 * a.d * a.dff;

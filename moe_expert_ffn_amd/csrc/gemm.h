@@ -411,6 +411,12 @@ MOE_DEV BufRsrc make_rsrc(const void* base, uint32_t bytes) {
 MOE_DEV void buf_load_lds16(BufRsrc r, uint32_t off, MOE_LDS void* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);
 }
+// 16-byte store through a buffer descriptor; an offset past the descriptor's
+// size (kOob) is dropped by the buffer unit, so a masked store still counts as
+// one vector memory operation
+MOE_DEV void buf_store16(BufRsrc r, uint32_t off, const u32x4_t& d) {
+  __builtin_amdgcn_raw_buffer_store_b128(d, r, off, 0, 0);
+}
 
 MOE_DEV int dma_swz(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row >> 3)) & 3); }
 
@@ -485,6 +491,8 @@ template <int MN, int NWAVES> struct MnDma {
   struct Offs { uint32_t o[NI]; };
   // stage row (K index within the step) loaded by this lane's instruction i
   static MOE_DEV int row_of(int i) { return ((threadIdx.x >> 6) + NWAVES * i) * RPI + (threadIdx.x & 63) / CPR; }
+  // first of the RPI rows of instruction i (wave-uniform)
+  static MOE_DEV int row_base(int i) { return (wave_id() + NWAVES * i) * RPI; }
   template <class F> MOE_DEV Offs prep_rows(int kt, F rowoff) const {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     Offs p;
@@ -798,6 +806,8 @@ template <int MN, int NWAVES> struct Mn64 {
   struct Offs { uint32_t o[NI]; };
   // stage row (K index within the step) loaded by this lane's instruction i
   static MOE_DEV int row_of(int i) { return ((threadIdx.x >> 6) + NWAVES * i) * RPI + (threadIdx.x & 63) / CPR; }
+  // first of the RPI rows of instruction i (wave-uniform)
+  static MOE_DEV int row_base(int i) { return (wave_id() + NWAVES * i) * RPI; }
   template <class F> MOE_DEV Offs prep_rows(int kt, F rowoff) const {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     Offs p;
@@ -856,12 +866,14 @@ template <class OP, class F> struct Mn64Operand {
   F f;
   static constexpr int NI = OP::NI, STAGE_BYTES = OP::STAGE_BYTES;
   using Lane = typename OP::Lane;
-  struct Offs { uint32_t raw[NI]; int kt; };
+  // f.pre(kb, k): what post needs for the lane's K row k, where kb is the
+  // wave-uniform first row of the same instruction
+  struct Offs { typename F::Raw raw[NI]; int kt; };
   MOE_DEV Offs prep(int kt) const {
     Offs p;
     p.kt = kt;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) p.raw[i] = f.pre(kt * kWideBK + OP::row_of(i));
+    for (int i = 0; i < NI; ++i) p.raw[i] = f.pre(kt * kWideBK + OP::row_base(i), kt * kWideBK + OP::row_of(i));
     return p;
   }
   MOE_DEV void issue(const Offs& p, MOE_LDS char* st) const {
@@ -1067,6 +1079,11 @@ template <class C, class OA, class OB> struct WideStream {
           for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
       // the item's first step landed before the previous item's last barrier
       if (g > 0) read<0, 0>(smem + (g & 1) * STAGE);
+      // At the end of this item's first step the loads it waits for were issued
+      // before the previous item's epilogue, so the epilogue's stores (and
+      // loads) may stay in flight: they drain under this step and the next.
+      // The next step's wait is a full one, so the item needs two steps.
+      const bool relax = g > 0 && n0 >= 2;
       for (int kt = 0; kt < n0; ++kt, ++g) {
         const MOE_LDS char* st = smem + (g & 1) * STAGE;
         __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -1094,7 +1111,8 @@ template <class C, class OA, class OB> struct WideStream {
         __builtin_amdgcn_sched_barrier(0);
         mma<0>(acc);
         __builtin_amdgcn_sched_barrier(0);
-        wait_vm_lgkm0<0>();
+        if (relax && kt == 0) src.relaxed_wait();
+        else wait_vm_lgkm0<0>();
         __builtin_amdgcn_s_barrier();
         // every wave is past the previous item's epilogue: item slot s2 is free
         if (kt == 0 && h2) src.fill(it2, s2);
