@@ -148,8 +148,8 @@ def kernel_model(w, R, T, e_act, replicas):
 # HBM traffic of the dominant kernel from rocprofv3 counters (FETCH_SIZE and
 # WRITE_SIZE per dispatch, scaled by the reading of a plain copy kernel of
 # known size), valid only for the kernel sources it was measured on.
-PROFILED_TRAFFIC = {"kernel": "bwd.dW", "source": "81570b68e5ace0e4", "bytes": 3660181307,
-                    "summary": "profiles/k_bwd_dw_qwen3_bf16_fwdbwd_hbm_traffic.md"}
+PROFILED_TRAFFIC = {"kernel": "bwd.dW", "source": "3fd5a67860c262f4", "bytes": 3823876747,
+                    "summary": "profiles/k_stream_SrcDwT_qwen3_bf16_fwdbwd_hbm_traffic.md"}
 
 
 def source_hash():

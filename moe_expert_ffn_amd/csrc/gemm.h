@@ -308,82 +308,6 @@ MOE_DEV void gemm_tile(LA la, LB lb, int nk, MOE_LDS T* smem, f32x16_t (&acc)[C:
   }
 }
 
-// Deeper pipeline: two register sets of global prefetch, so the loads of K step
-// kt+2 are in flight while step kt computes; the LDS stores of step kt+1 (whose
-// loads were issued a full step earlier) are made between the MFMA chunks of
-// step kt; and the operand fragments of chunk kc+1 are read while chunk kc's
-// MFMAs run.  One barrier per step.  LA/LB are copyable loader values.
-template <class C, typename T> struct Frags;
-template <class C> struct Frags<C, uint16_t> {
-  bf16x8_t a[C::MB], b[C::NB];
-  MOE_DEV void read(const MOE_LDS uint16_t* sA, const MOE_LDS uint16_t* sB, int kc, int lane) {
-    constexpr int LDK = TileLds<uint16_t, C>::LDK;
-    const int wm = wave_id() / C::WAVES_N, wn = wave_id() % C::WAVES_N;
-    const int ko = kc * 16 + (lane >> 5) * 8;
-#pragma unroll
-    for (int i = 0; i < C::MB; ++i)
-      a[i] = *(const MOE_LDS bf16x8_t*)(sA + (wm * C::WM + i * 32 + (lane & 31)) * LDK + ko);
-#pragma unroll
-    for (int j = 0; j < C::NB; ++j)
-      b[j] = *(const MOE_LDS bf16x8_t*)(sB + (wn * C::WN + j * 32 + (lane & 31)) * LDK + ko);
-  }
-  MOE_DEV void mma(f32x16_t (&acc)[C::MB][C::NB]) const {
-#pragma unroll
-    for (int i = 0; i < C::MB; ++i)
-#pragma unroll
-      for (int j = 0; j < C::NB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
-};
-
-template <typename T, class C, class LA, class LB>
-MOE_DEV void gemm_tile_deep(LA la0, LB lb0, int nk, MOE_LDS T* smem, f32x16_t (&acc)[C::MB][C::NB]) {
-  using L = TileLds<T, C>;
-  constexpr int STAGE = L::A_ELEMS + L::B_ELEMS;
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int i = 0; i < C::MB; ++i)
-#pragma unroll
-    for (int j = 0; j < C::NB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  if (nk <= 0) return;
-  LA la1 = la0;
-  LB lb1 = lb0;
-  // prologue: step 0 -> LDS stage 0; step 1 in flight in set 1
-  la0.load(0);
-  lb0.load(0);
-  if (nk > 1) { la1.load(1); lb1.load(1); }
-  la0.store(smem);
-  lb0.store(smem + L::A_ELEMS);
-  __syncthreads();
-  Frags<C, T> f0, f1;
-  auto step = [&](int kt, LA& lan, LB& lbn, LA& las, LB& lbs) {
-    // lan/lbn: set to load step kt+2 into; las/lbs: set holding step kt+1
-    const MOE_LDS T* sA = smem + (kt & 1) * STAGE;
-    const MOE_LDS T* sB = sA + L::A_ELEMS;
-    MOE_LDS T* nA = smem + ((kt + 1) & 1) * STAGE;
-    if (kt + 2 < nk) { lan.load(kt + 2); lbn.load(kt + 2); }
-    f0.read(sA, sB, 0, lane);
-#pragma unroll
-    for (int kc = 0; kc < L::NKC; kc += 2) {
-      f1.read(sA, sB, kc + 1, lane);
-      f0.mma(acc);
-      if (kc == 0 && kt + 1 < nk) las.store(nA);
-      if (kc + 2 < L::NKC) f0.read(sA, sB, kc + 2, lane);
-      f1.mma(acc);
-      if (kc == 0 && kt + 1 < nk) lbs.store(nA + L::A_ELEMS);
-    }
-    __syncthreads();
-  };
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    step(kt, la0, lb0, la1, lb1);
-    step(kt + 1, la1, lb1, la0, lb0);
-  }
-  if (kt < nk) step(kt, la0, lb0, la1, lb1);
-}
-
 // ---- direct-to-LDS pipeline (bf16, K-contiguous operands) ---------------------
 // global_load_lds_dwordx4 moves 16 bytes per lane from global memory straight
 // into LDS (lane i of a wave writes LDS bytes [16 i, 16 i + 16) after the
@@ -467,110 +391,6 @@ template <int ROWS, int NWAVES> struct RowDma {
       buf_load_lds16(rs, q.o[i], (MOE_LDS void*)(st + (w + NWAVES * i) * 16 * (kDmaRowBytes / 2)));
   }
 };
-
-// MN-contiguous operand (the K index walks source rows, M or N is contiguous):
-// a stage holds 32 K rows x MN elements in their natural layout, [k][mn], 16-byte
-// chunks XOR-swizzled by 2 * (k % 8).  MFMA fragments come from
-// ds_read_b64_tr_b16: inside each 16-lane group, lane j supplies the address of
-// row k0 + j/4, columns m0 + 4 (j % 4) .. +3 and receives column m0 + j of rows
-// k0 .. k0+3, i.e. four consecutive K values of one M/N index; two such reads
-// give the eight K values an MFMA lane needs.
-// rowoff(k) returns the byte offset, inside the operand's buffer, of element
-// (source row of stage row k, mn0), or kOob for a row that reads as zeros.
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-MOE_DEV int mn_swz(int row) { return (row & 7) << 1; }
-
-template <int MN, int NWAVES> struct MnDma {
-  static constexpr int ROWB = MN * 2;               // bytes per stage row
-  static constexpr int RPI = 1024 / ROWB;           // rows per wave load instruction
-  static constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
-  static constexpr int NI = 32 / RPI / NWAVES;      // load instructions per wave per step
-  static constexpr int STAGE_ELEMS = 32 * MN;
-  static_assert(NI * RPI * NWAVES == 32, "32 K rows per stage");
-  BufRsrc rs;
-  struct Offs { uint32_t o[NI]; };
-  // stage row (K index within the step) loaded by this lane's instruction i
-  static MOE_DEV int row_of(int i) { return ((threadIdx.x >> 6) + NWAVES * i) * RPI + (threadIdx.x & 63) / CPR; }
-  // first of the RPI rows of instruction i (wave-uniform)
-  static MOE_DEV int row_base(int i) { return (wave_id() + NWAVES * i) * RPI; }
-  template <class F> MOE_DEV Offs prep_rows(int kt, F rowoff) const {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    Offs p;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int r = (w + NWAVES * i) * RPI + lane / CPR;
-      const uint32_t c = (uint32_t)((lane % CPR) ^ mn_swz(r));
-      p.o[i] = rowoff(kt * 32 + r) + c * 16u;
-    }
-    return p;
-  }
-  MOE_DEV void issue(const Offs& p, MOE_LDS uint16_t* st) const {
-    const int w = threadIdx.x >> 6;
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      buf_load_lds16(rs, p.o[i], (MOE_LDS void*)(st + (w + NWAVES * i) * RPI * MN));
-  }
-  // Fragment addresses.  Lane j of 16-lane group G reads rows
-  // kc*16 + 8 (G >> 1) + j / 4 (+ 4 for the second read) at column
-  // wave_base + 32 i + 16 (G & 1) + 4 (j % 4).  The swizzle only moves 16-byte
-  // chunks inside bits 1..3 of the chunk index, which fragment i (4 i chunks,
-  // bits 2.. above the lane's own bits 0..1) never carries into, so
-  //   byte offset = (lane part ^ 64 i) + kc * 32 * MN,
-  // two registers per lane (one per read) and an XOR per fragment.
-  struct Lane { uint32_t off[2]; };
-  static MOE_DEV Lane lane_info(int wave_base, int lane) {
-    const int G = lane >> 4, j = lane & 15;
-    const int m = wave_base + 16 * (G & 1) + 4 * (j & 3);
-    const int c = m >> 3, within = m & 7;
-    Lane L;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int row = 8 * (G >> 1) + (j >> 2) + 4 * h;
-      L.off[h] = (uint32_t)(row * MN + ((c ^ mn_swz(row)) << 3) + within) * 2u;
-    }
-    return L;
-  }
-  // The reads are issued from inline asm: the compiler treats the builtin as
-  // aliasing the direct-to-LDS loads in flight and would wait for all of them
-  // (vmcnt(0)) before every read, serialising the prefetch pipeline.  The
-  // pipeline orders the reads itself: each fragment is consumed only after an
-  // explicit lgkmcnt(0) wait, pinned by a scheduling barrier, and every
-  // fragment read is consumed.
-  template <int KC>
-  static MOE_DEV bf16x8_t frag(const MOE_LDS uint16_t* st, const Lane& L, int i) {
-    const MOE_LDS char* sb = (const MOE_LDS char*)st;
-    s16x4_t lo, hi;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
-                 : "=v"(lo) : "v"(sb + (L.off[0] ^ (64u * i))), "i"(KC * 32 * MN));
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
-                 : "=v"(hi) : "v"(sb + (L.off[1] ^ (64u * i))), "i"(KC * 32 * MN));
-    typedef short s16x8_t __attribute__((ext_vector_type(8)));
-    const s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8_t, v);
-  }
-};
-
-// A loader bound to its row function, with the interface the pipeline uses.
-template <class OP, class F> struct MnOperand {
-  const OP& op;
-  F rowoff;
-  static constexpr int NI = OP::NI, STAGE_ELEMS = OP::STAGE_ELEMS;
-  using Lane = typename OP::Lane;
-  using Offs = typename OP::Offs;
-  MOE_DEV Offs prep(int kt) const { return op.prep_rows(kt, rowoff); }
-  MOE_DEV void issue(const Offs& p, MOE_LDS uint16_t* st) const { op.issue(p, st); }
-  static MOE_DEV Lane lane_info(int wave_base, int lane) { return OP::lane_info(wave_base, lane); }
-  template <int KC>
-  static MOE_DEV bf16x8_t frag(const MOE_LDS uint16_t* st, const Lane& L, int i) {
-    return OP::template frag<KC>(st, L, i);
-  }
-};
-template <class OP, class F> MOE_DEV MnOperand<OP, F> mn_operand(const OP& op, F f) { return {op, f}; }
-
-template <int N> MOE_DEV void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 template <class C> struct DmaCfg {
   static constexpr int STAGE_A = C::BM * 32, STAGE_B = C::BN * 32;   // elements
@@ -696,32 +516,14 @@ MOE_DEV void gemm_tile_dma(const OA& oa, const OB& ob, int nk, MOE_LDS uint16_t*
   p.run(oa, ob, nk, smem, acc, accumulate);
 }
 
-// ---- two workgroups per CU ----------------------------------------------------
-// 256 x 128 tiles, 4 waves of 128 x 64 (128 accumulator registers per lane), so
-// two workgroups share a CU (two waves per SIMD): one workgroup's epilogue
-// stores and pipeline bubbles overlap the other's MFMAs.  Three direct-to-LDS
-// stages (72 KB) per workgroup.  Accumulators are transposed (SWAP), so every
-// lane owns one output row and four consecutive columns per register quad and
-// stores straight from registers, with no LDS round trip.
-using DualCfg = GemmCfg<256, 128, 2, 2>;
-constexpr int kDualStages = 3;
-
-// Output position of accumulator quad g of block (i, j) in a SWAP tile:
-// row acc_row_t, columns acc_col_t .. +3.
-template <class C> MOE_DEV int acc_row_t(int i, int lane) {
-  return (wave_id() / C::WAVES_N) * C::WM + i * 32 + (lane & 31);
-}
-template <class C> MOE_DEV int acc_col_t(int j, int g, int lane) {
-  return (wave_id() % C::WAVES_N) * C::WN + j * 32 + 8 * g + 4 * (lane >> 5);
-}
-
 // ---- wide tile: 256 x 256, 8 waves, K = 64 per stage --------------------------
 // Eight waves (2 x 4, each 128 x 64 with 128 accumulator registers, two waves
 // per SIMD) share one 256 x 256 tile; a stage holds K = 64, so every row
 // segment is a full 128-byte line, both for the global load and in LDS.  Two
 // direct-to-LDS stages (128 KB): the loads of step kt+1 land while step kt
 // computes.  Accumulators are transposed (the N fragment is the MFMA's first
-// operand), as for the two-workgroup tiles.
+// operand): each lane owns one output row and four consecutive columns per
+// register quad.
 //
 // LDS swizzles, chosen from measured bank behaviour of gfx950:
 //   ds_read_b128 on 128-byte rows serves 16 lanes per clock; XOR-ing the
@@ -735,6 +537,7 @@ constexpr int kWideBK = 64, kWideStages = 2, kWideRowBytes = 128;
 
 MOE_DEV int swz_row128(int row) { return (row & 7) ^ ((row >> 3) & 3); }   // rows mod 32
 MOE_DEV int swz_tr(int row) { return (row & 3) << 2; }
+typedef short s16x4_t __attribute__((ext_vector_type(4)));   // one transpose read
 
 // K-contiguous operand: ROWS rows of K = 64 per stage, [row][128 bytes].
 // One wave instruction loads 8 rows (8 lanes x 16 bytes each).
@@ -793,7 +596,10 @@ template <int ROWS, int NWAVES> struct Row64 {
 };
 
 // MN-contiguous operand: 64 K rows x MN elements per stage, [k][MN], fragments
-// through ds_read_b64_tr_b16 (see MnDma).  rowoff(k) = byte offset in the
+// through ds_read_b64_tr_b16: inside each 16-lane group, lane j supplies the
+// address of row k0 + j/4, columns m0 + 4 (j % 4) .. +3 and receives column
+// m0 + j of rows k0 .. k0+3, i.e. four consecutive K values of one M/N index;
+// two such reads give the eight K values an MFMA lane needs.  rowoff(k) = byte offset in the
 // buffer of (source row of K index k, mn0), or kOob for a zero row.
 template <int MN, int NWAVES> struct Mn64 {
   static constexpr int ROWB = MN * 2;
@@ -828,7 +634,7 @@ template <int MN, int NWAVES> struct Mn64 {
   // Lane j of 16-lane group G reads rows 16 KC + 8 (G >> 1) + j / 4 (+ 4) at
   // column wave_base + 32 i + 16 (G & 1) + 4 (j % 4); the swizzle touches
   // chunk bits 2..3 and fragment i adds 4 i chunks above the lane's bits 0..1,
-  // so the offset is (lane part ^ 64 i) + KC * 16 * ROWB (see MnDma).
+  // so the offset is (lane part ^ 64 i) + KC * 16 * ROWB.
   struct Lane { uint32_t off[2]; };
   static MOE_DEV Lane lane_info(int wave_base, int lane) {
     const int G = lane >> 4, j = lane & 15;
@@ -842,7 +648,10 @@ template <int MN, int NWAVES> struct Mn64 {
     }
     return L;
   }
-  // Issued from inline asm for the reason given at MnDma::frag.
+  // Issued from inline asm: for a compiler-visible LDS read the compiler waits
+  // for every direct-to-LDS load in flight first, which would serialise the
+  // pipeline.  The caller consumes the result only after an explicit
+  // lgkmcnt(0) wait.
   template <int KC> static MOE_DEV bf16x8_t frag(const MOE_LDS char* st, const Lane& L, int i) {
     s16x4_t lo, hi;
     asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
@@ -890,8 +699,6 @@ template <class OP, class F> struct Mn64Operand {
     return OP::template frag<KC>(st, L, i);
   }
 };
-template <class OP, class F> MOE_DEV Mn64Operand<OP, F> mn64_operand(const OP& op, F f) { return {op, f}; }
-
 // nk = K / 64 steps.  Step kt (stage kt % 2):
 //   four K chunks; the fragments of chunk c+1 are read while chunk c's 8 MFMAs
 //   run; the load offsets of step kt+2 are prepared early in the step;
@@ -902,92 +709,8 @@ template <class OP, class F> MOE_DEV Mn64Operand<OP, F> mn64_operand(const OP& o
 // Loads past the last step re-read step nk-1 into a stage nobody reads again.
 // Fragments read from asm (Mn64) are consumed only after an explicit
 // lgkmcnt(0) wait pinned by a scheduling barrier.
-template <class C, class OA, class OB> struct WidePipe {
-  static constexpr int SA = OA::STAGE_BYTES, STAGE = OA::STAGE_BYTES + OB::STAGE_BYTES;
-  static constexpr int LPS = OA::NI + OB::NI;
-  static constexpr size_t BYTES = (size_t)kWideStages * STAGE;
-  bf16x8_t a[2][C::MB], b[2][C::NB];
-  typename OA::Lane la;
-  typename OB::Lane lb;
-  template <int KC, int S> MOE_DEV void read(const MOE_LDS char* st) {
-#pragma unroll
-    for (int i = 0; i < C::MB; ++i) a[S][i] = OA::template frag<KC>(st, la, i);
-#pragma unroll
-    for (int j = 0; j < C::NB; ++j) b[S][j] = OB::template frag<KC>(st + SA, lb, j);
-  }
-  template <int S> MOE_DEV void mma(f32x16_t (&acc)[C::MB][C::NB]) const {
-#pragma unroll
-    for (int i = 0; i < C::MB; ++i)
-#pragma unroll
-      for (int j = 0; j < C::NB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[S][j], a[S][i], acc[i][j], 0, 0, 0);
-  }
-  MOE_DEV void run(const OA& oa, const OB& ob, int nk, MOE_LDS uint16_t* smem16,
-                   f32x16_t (&acc)[C::MB][C::NB], bool accumulate = false) {
-    MOE_LDS char* smem = (MOE_LDS char*)smem16;
-    const int lane = threadIdx.x & 63;
-    if (!accumulate) {
-#pragma unroll
-      for (int i = 0; i < C::MB; ++i)
-#pragma unroll
-        for (int j = 0; j < C::NB; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    }
-    if (nk <= 0) return;
-    la = OA::lane_info((wave_id() / C::WAVES_N) * C::WM, lane);
-    lb = OB::lane_info((wave_id() % C::WAVES_N) * C::WN, lane);
-    __syncthreads();                      // the previous users of the LDS are done
-#pragma unroll
-    for (int s = 0; s < kWideStages; ++s) {
-      const int kk = s < nk ? s : nk - 1;
-      const auto pa = oa.prep(kk);
-      const auto pb = ob.prep(kk);
-      oa.issue(pa, smem + s * STAGE);
-      ob.issue(pb, smem + s * STAGE + SA);
-    }
-    wait_vm_lgkm0<(kWideStages - 1) * LPS>();
-    __builtin_amdgcn_s_barrier();
-    read<0, 0>(smem);
-    for (int kt = 0; kt < nk; ++kt) {
-      const MOE_LDS char* st = smem + (kt & 1) * STAGE;
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_sched_barrier(0);
-      read<1, 1>(st);
-      const int kn = kt + 2 < nk ? kt + 2 : nk - 1;
-      const auto pa = oa.prep(kn);
-      const auto pb = ob.prep(kn);
-      __builtin_amdgcn_sched_barrier(0);
-      mma<0>(acc);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_sched_barrier(0);
-      read<2, 0>(st);
-      __builtin_amdgcn_sched_barrier(0);
-      mma<1>(acc);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_sched_barrier(0);
-      read<3, 1>(st);
-      __builtin_amdgcn_sched_barrier(0);
-      mma<0>(acc);
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vm_lgkm0<0>();
-      __builtin_amdgcn_s_barrier();
-      oa.issue(pa, smem + (kt & 1) * STAGE);
-      ob.issue(pb, smem + (kt & 1) * STAGE + SA);
-      if (kt + 1 < nk) read<0, 0>(smem + ((kt + 1) & 1) * STAGE);
-      __builtin_amdgcn_sched_barrier(0);
-      mma<1>(acc);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    wait_vm_lgkm0<0>();
-    __syncthreads();                      // all loads landed, all waves done with the stages
-  }
-};
-
 // ---- wide tile, persistent across tiles -------------------------------------
-// The same per-step schedule as WidePipe, but the stream of K steps runs on
+// The per-step schedule above, with the stream of K steps running on
 // from one work item to the next: the first two steps of the next item are
 // issued during the last two steps of the current one, so a tile starts with
 // its operands already in LDS, and the previous tile's stores drain while the
@@ -1007,6 +730,11 @@ template <class C, class OA, class OB> struct WidePipe {
 //   OA opA(const Item&, int slot), OB opB(const Item&, int slot)
 //   int steps(const Item&)             K steps, >= 2
 //   void epilogue(const Item&, int slot, acc)
+//   void relaxed_wait()                the wait at the end of an item's first
+//                                      step: vmcnt(N) with N at most the vector
+//                                      memory operations one epilogue issues
+//                                      (all issued after the loads that step
+//                                      needs), then lgkmcnt(0)
 //   int count, first, stride           items first, first + stride, ... < count
 template <class C, class OA, class OB> struct WideStream {
   static constexpr int SA = OA::STAGE_BYTES, STAGE = OA::STAGE_BYTES + OB::STAGE_BYTES;

@@ -5,7 +5,9 @@
         <copy_fetch.csv> <copy_write.csv> <copy_bytes> <kernel>
 
 `stats` prints a markdown table of the library's kernels (calls, average and
-total duration).  `traffic` prints, for one kernel, the average FETCH_SIZE and
+total duration).  Kernel names are shortened to k_stream<SrcX> for the
+persistent GEMM kernels (SrcX names the stage) and to the bare name otherwise;
+`traffic` takes such a short name.  `traffic` prints, for one kernel, the average FETCH_SIZE and
 WRITE_SIZE per dispatch (KiB), the calibration of both counters against a
 plain elementwise copy of `copy_bytes` bytes read and written (the copy's own
 dispatch is the one with the largest reading), and the calibrated HBM bytes
@@ -18,19 +20,22 @@ import csv
 import re
 import sys
 
-STAGE_OF = {"k_fc1_t": "fwd.fc1", "k_fc2_t": "fwd.fc2", "k_bwd_da_t": "bwd.dA",
-            "k_bwd_dx_t": "bwd.dX", "k_bwd_dw_t": "bwd.dW", "k_bwd_reduce": "bwd.reduce",
+STAGE_OF = {"k_stream<SrcFc1>": "fwd.fc1", "k_stream<SrcFc2>": "fwd.fc2",
+            "k_stream<SrcDa>": "bwd.dA", "k_stream<SrcDx>": "bwd.dX", "k_stream<SrcDwT>": "bwd.dW",
+            "k_fc1": "fwd.fc1", "k_fc2": "fwd.fc2", "k_bwd_da": "bwd.dA", "k_bwd_dx": "bwd.dX",
+            "k_bwd_dw": "bwd.dW", "k_bwd_reduce": "bwd.reduce",
             "k_combine": "fwd.combine + bwd.combine", "k_sched": "fwd.sched + bwd.sched",
-            "k_plan": "plan (fwd + bwd)", "k_route_count": "route", "k_route_scan": "route",
-            "k_route_slot": "route"}
+            "k_slot_gate": "fwd.sched + bwd.sched", "k_plan": "plan (fwd + bwd)",
+            "k_route_count": "route", "k_route_scan": "route", "k_route_slot": "route"}
 
 
 def short(name: str) -> str:
+    """k_stream<SrcX> for the persistent GEMM kernels, the bare kernel name otherwise."""
+    m = re.search(r"k_stream<moe::(\w+)", name)
+    if m:
+        return f"k_stream<{m.group(1)}>"
     m = re.search(r"moe::(\w+)", name)
-    if not m:
-        return name[:60]
-    eng = re.search(r"Eng(Wide|Dual)", name)
-    return m.group(1) + (f"<{eng.group(1)}>" if eng else "")
+    return m.group(1) if m else name[:60]
 
 
 def stats(path: str) -> str:
@@ -40,8 +45,7 @@ def stats(path: str) -> str:
         if "moe::" not in r["Name"]:
             continue
         k = short(r["Name"])
-        base = k.split("<")[0]
-        out.append(f"| {k} | {STAGE_OF.get(base, '')} | {r['Calls']} | "
+        out.append(f"| {k} | {STAGE_OF.get(k, '')} | {r['Calls']} | "
                    f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['TotalDurationNs']) / 1e3:.1f} |")
     return "\n".join(out)
 
@@ -61,7 +65,7 @@ def copy_reading(path: str) -> float:
 def traffic(fetch: str, write: str, cfetch: str, cwrite: str, copy_bytes: int, kernel: str) -> str:
     f = per_kernel(fetch)
     w = per_kernel(write)
-    key = next(k for k in f if k.split("<")[0] == kernel)
+    key = next(k for k in f if k == kernel)
     fk = sum(f[key]) / len(f[key])
     wk = sum(w[key]) / len(w[key])
     sf = copy_bytes / (copy_reading(cfetch) * 1024.0)
