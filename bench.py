@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--kappa", type=float, default=1)
     ap.add_argument("--fixed", action="store_true", help="fixed placement (s = 0)")
     ap.add_argument("--sweep", action="store_true",
-                    help="also time every kappa of the workload, fixed and planned")
+                    help="also time every kappa of the workload: fixed placement, the bounded "
+                         "greedy planner and the quota planner, and compare the two planners")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=512)
     return ap.parse_args()
@@ -52,7 +53,7 @@ def flops_per_row(w):
     return 6 * w.d * w.d_ff, 12 * w.d * w.d_ff
 
 
-def build_case(w, kappa, fixed, dev):
+def build_case(w, kappa, fixed, dev, quota_umin=None):
     import torch
 
     from moe_expert_ffn_amd.inputs import contiguous_owners, make_dy, make_layer, make_routing, make_x
@@ -65,7 +66,8 @@ def build_case(w, kappa, fixed, dev):
     dy = make_dy(w, T, dev) if w.backward else None
     r = LayerRunner(lay["w1"], lay["w2"], lay.get("w1_scale"), lay.get("w2_scale"), act_dtype=act,
                     T=T, k=w.k, beta=w.beta, P=w.P, s=0 if fixed else w.s,
-                    owner=torch.from_numpy(contiguous_owners(w.E, w.P)), with_backward=w.backward)
+                    owner=torch.from_numpy(contiguous_owners(w.E, w.P)), with_backward=w.backward,
+                    quota_umin=quota_umin)
     return dict(runner=r, x=x, gates=torch.from_numpy(gates).to(dev), ids=torch.from_numpy(ids).to(dev),
                 dy=dy, ids_np=ids, gates_np=gates, lay=lay, T=T)
 
@@ -192,6 +194,33 @@ def roofline(w, stages, R, T, e_act, replicas):
     return out, per
 
 
+def compare_planners(case, w, n=50):
+    """Both planners on this case's route statistics: objective (max blocks per
+    worker), replicas and mean on-device time of one moe_plan call."""
+    import torch
+
+    from moe_expert_ffn_amd import binding as B
+    r = case["runner"]
+    r.route(case["ids"])
+    out = {}
+    for name, mode, lam in (("greedy_fwd", B.PLAN_FWD, r.lam), ("quota_umin1", B.PLAN_QUOTA, 1)):
+        plan = B.alloc_plan(r.E, r.P, B.max_blocks(r.T, r.k, r.E, r.beta), r.dev)
+        args = (r.rs["block_counts"], r.rs["block_offsets"], r.owner, r.P, w.s, mode, lam, plan,
+                r.ws, r.status)
+        for _ in range(5):
+            B.plan(*args)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            B.plan(*args)
+        e1.record()
+        torch.cuda.synchronize()
+        info = plan["plan_info"].cpu().tolist()
+        out[name] = {"objective": info[0], "replicas": info[2], "tau": info[3],
+                     "us": round(e0.elapsed_time(e1) * 1e3 / n, 2)}
+    return out
+
+
 def cpu_baseline(case, w, tokens):
     """The oracle, untuned, on the first `tokens` tokens of the same workload:
     forward of those tokens plus their dx, and dW of every expert over their
@@ -270,20 +299,24 @@ def main():
         "kernels": per_kernel,
     }
     if args.sweep:
-        sweep = []
+        sweep, planners = [], []
         for kap in w.kappas:
-            for fixed in (True, False):
-                c = build_case(w, kap, fixed, dev)
+            for arm, fixed, umin in (("fixed", True, None), ("planned", False, None),
+                                     ("planned-quota", False, 1)):
+                c = build_case(w, kap, fixed, dev, quota_umin=umin)
                 Rk = int((c["ids_np"] >= 0).sum())
                 msk, st = time_steps(c, max(5, args.steps // 2), 2)
                 uk = (f_fwd + (f_bwd if w.backward else 0)) * Rk
-                sweep.append({"kappa": kap, "placement": "fixed" if fixed else "planned",
+                sweep.append({"kappa": kap, "placement": arm,
                               "ms": round(msk, 4), "tflops": round(uk / (msk * 1e-3) / 1e12, 2),
                               "fwd_us": round(sum(v for k_, v in st.items() if k_.startswith("fwd.")) * 1e3, 1),
                               "bwd_us": round(sum(v for k_, v in st.items() if k_.startswith("bwd.")) * 1e3, 1)})
+                if arm == "planned":
+                    planners.append({"kappa": kap, **compare_planners(c, w)})
                 del c
                 torch.cuda.empty_cache()
         out["kappa_sweep"] = sweep
+        out["planners"] = planners
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case, w, args.cpu_tokens)
     print(json.dumps(out), flush=True)

@@ -62,7 +62,7 @@ typedef enum {
 #define MOE_DEV_BAD_OWNER  4   /* owner[e] outside [0,P) */
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
-typedef enum { MOE_PLAN_FWD = 0, MOE_PLAN_BWD = 1 } moe_plan_mode;
+typedef enum { MOE_PLAN_FWD = 0, MOE_PLAN_BWD = 1, MOE_PLAN_QUOTA = 2 } moe_plan_mode;
 
 /* One expert layer.  The weights are stored transposed with respect to the
  * pages' X W notation, so that both operands of every forward product are
@@ -123,11 +123,21 @@ int moe_route_stats(const int32_t* topk_ids, int T, int k, int E, int beta,
  *   owner [E]: h(e) in [0, P), the home worker of each expert.
  *   mode MOE_PLAN_FWD minimises max_r l_r; MOE_PLAN_BWD minimises
  *   max_r (l_r + lambda * n_r), n_r = remote copies of r's experts.
- *   s = 0 gives fixed placement.
+ *   mode MOE_PLAN_QUOTA is the quota-driven solver of the UltraEP reading
+ *   notes (section 4, Algorithm 1): a binary search for the smallest load
+ *   threshold tau that a greedy quota pass meets; for this mode `lambda` is
+ *   the quota floor u_min (>= 1 blocks): no replica is made for fewer blocks.
+ *   s = 0 gives fixed placement (every mode).
  * Outputs: q [E][P] blocks of e on r; load [P] = l_r; block_worker
  *   [moe_max_blocks]: worker of each block (expert e's blocks go to its owner
  *   first, then to ascending workers; entries past sum b are untouched);
- *   plan_info [4] = {objective, chosen search 0..3, replica count, tau}.
+ *   plan_info [4] = {objective, chosen search 0..3 (4 for MOE_PLAN_QUOTA),
+ *   replica count, tau (ceil(sum b / P), or the threshold found by
+ *   MOE_PLAN_QUOTA)}.
+ * Errors: MOE_ERR_ARG for a bad mode, s < 0, lambda < 0 (< 1 with
+ *   MOE_PLAN_QUOTA) or a null pointer; MOE_ERR_UNSUPPORTED for E > 512 or P
+ *   outside {1,2,4,8}; an owner outside [0, P) sets MOE_DEV_BAD_OWNER in
+ *   *status_dev.
  * Limits: 1 <= E <= 512, P in {1,2,4,8}, s >= 0, lambda >= 0. */
 int moe_plan(const int32_t* block_counts, const int32_t* block_offsets,
              const int32_t* owner, int E, int P, int s, int mode, int lambda,

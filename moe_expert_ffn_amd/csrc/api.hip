@@ -119,7 +119,9 @@ int moe_plan(const int32_t* block_counts, const int32_t* block_offsets, const in
              size_t ws_bytes, void* stream) {
   (void)ws;
   (void)ws_bytes;
-  if (E < 1 || s < 0 || lambda < 0 || (mode != MOE_PLAN_FWD && mode != MOE_PLAN_BWD))
+  if (E < 1 || s < 0 || lambda < 0 ||
+      (mode != MOE_PLAN_FWD && mode != MOE_PLAN_BWD && mode != MOE_PLAN_QUOTA) ||
+      (mode == MOE_PLAN_QUOTA && lambda < 1))
     return MOE_ERR_ARG;
   if (!valid_P(P) || E > kMaxPlanExperts) return MOE_ERR_UNSUPPORTED;
   if (!block_counts || !block_offsets || !owner || !q || !load || !block_worker ||

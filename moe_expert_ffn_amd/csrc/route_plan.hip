@@ -339,6 +339,207 @@ __global__ __launch_bounds__(256) void k_plan(const int32_t* __restrict__ bcnt,
 }
 
 // ---------------------------------------------------------------------------
+// Quota-driven planner (UltraEP reading notes, section 4 "The Quota-Driven
+// Planning Solver", Algorithm 1), in block units: the smallest load threshold
+// tau in [ceil(B/P), max fixed load] that one greedy pass meets, found by
+// binary search.  A pass at tau starts from the fixed placement with
+// exc_r = max(l_r - tau, 0), slk_r = max(tau - l_r, 0); overloaded workers by
+// decreasing excess (ties: smaller r) hand their own experts (by decreasing
+// b_e, ties: smaller e) to the worker with the most slack that does not host
+// the expert yet and has a free replica slot (ties: smaller t), in amounts
+// min(exc_r, slk_t, blocks left on r), but only when that is >= u_min.
+//
+// An expert's blocks and its set of hosts change only while that expert is
+// being handed out, so a pass needs no per-expert state beyond the expert in
+// hand: lane r of a wave holds worker r's load, excess, slack and replica
+// count, and the expert order is a table built once.  Seven waves evaluate the
+// next three levels of the binary search at once (the root's midpoint and
+// the midpoints of every interval either answer can leave), which gives the
+// same threshold as probing one midpoint at a time in a third of the rounds.
+// The eighth wave then replays the pass at the chosen tau and records the
+// moves for the outputs.
+// ---------------------------------------------------------------------------
+constexpr int kQuotaWaves = 8, kQuotaProbes = 7;
+
+// One feasibility pass at tau on one wave.  With `moves` non-null the blocks
+// each recipient takes are added to moves[e * 8 + t].  Lane r < P ends with
+// worker r's load and replica count.
+MOE_DEV bool quota_pass(int tau, int E, int P, int s, int umin, const int* b_s, const int* ord_s,
+                        const int* goff_s, const int* ell0_s, int lane, int& ell, int& rep,
+                        int* moves) {
+  ell = lane < P ? ell0_s[lane] : 0;
+  int exc = lane < P ? max(ell - tau, 0) : 0;
+  int slk = lane < P ? max(tau - ell, 0) : 0;
+  rep = 0;
+  const bool isdon = exc > 0;
+  int rank = 0;
+  for (int r2 = 0; r2 < P; ++r2) {
+    const int x2 = __shfl(exc, r2, 64);
+    if (x2 > 0 && (x2 > exc || (x2 == exc && r2 < lane))) ++rank;
+  }
+  const int ndon = __popcll(__ballot(isdon));
+  for (int j = 0; j < ndon; ++j) {
+    const int r = __ffsll((unsigned long long)__ballot(isdon && rank == j)) - 1;
+    for (int idx = goff_s[r]; idx < goff_s[r + 1]; ++idx) {
+      if (__shfl(exc, r, 64) == 0) break;
+      const int e = ord_s[idx];
+      int left = b_s[e];                 // blocks of e still on r
+      uint32_t hosts = 1u << r;          // workers holding a copy of e
+      // each transfer gives e to a new worker, so at most P - 1 of them
+      for (int guard = 0; guard < P && left > 0; ++guard) {
+        const int er = __shfl(exc, r, 64);
+        if (er == 0) break;
+        long long cand = -1;
+        if (lane < P && !((hosts >> lane) & 1u) && rep < s && slk > 0)
+          cand = ((long long)slk << 8) | (long long)(255 - lane);
+        const long long bc = wave_max64(cand);
+        if (bc < 0) break;
+        const int t = 255 - (int)(bc & 255);
+        const int delta = min(min(er, (int)(bc >> 8)), left);
+        if (delta < umin) break;
+        if (lane == r) { exc -= delta; ell -= delta; }
+        if (lane == t) { slk -= delta; ell += delta; rep += 1; }
+        if (moves && lane == 0) moves[e * 8 + t] += delta;
+        hosts |= 1u << t;
+        left -= delta;
+      }
+    }
+  }
+  return __ballot(lane < P && exc > 0) == 0;
+}
+
+__global__ __launch_bounds__(512) void k_plan_quota(const int32_t* __restrict__ bcnt,
+                                                    const int32_t* __restrict__ boff,
+                                                    const int32_t* __restrict__ owner, int E,
+                                                    int P, int s, int umin, int32_t* q_out,
+                                                    int32_t* load_out, int32_t* bw_out,
+                                                    int32_t* info_out, int32_t* status) {
+  extern __shared__ int sm[];
+  int* b_s = sm;                     // [E]
+  int* h_s = b_s + E;                // [E]
+  int* boff_s = h_s + E;             // [E+1]
+  int* ord_s = boff_s + E + 1;       // [E] experts grouped by owner, by b desc, e asc
+  int* mv_s = ord_s + E;             // [E][8] blocks moved from e's owner to t
+  __shared__ int goff_s[kMaxP + 1], gcnt_s[kMaxP], ell0_s[kMaxP], feas_s[kQuotaProbes];
+  __shared__ int lo_s, hi_s, fin_ell[kMaxP], fin_rep;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid < kMaxP) { gcnt_s[tid] = 0; ell0_s[tid] = 0; }
+  __syncthreads();
+  for (int e = tid; e < E; e += 512) {
+    b_s[e] = bcnt[e];
+    int h = owner[e];
+    if (h < 0 || h >= P) { atomicOr(status, MOE_DEV_BAD_OWNER); h = 0; }
+    h_s[e] = h;
+    atomicAdd(&gcnt_s[h], 1);
+    atomicAdd(&ell0_s[h], bcnt[e]);
+  }
+  for (int e = tid; e <= E; e += 512) boff_s[e] = boff[e];
+  for (int i = tid; i < E * 8; i += 512) mv_s[i] = 0;
+  __syncthreads();
+  if (tid == 0) {
+    goff_s[0] = 0;
+    for (int r = 0; r < P; ++r) goff_s[r + 1] = goff_s[r] + gcnt_s[r];
+    long long B = 0;
+    int mx = 0;
+    for (int r = 0; r < P; ++r) { B += ell0_s[r]; mx = max(mx, ell0_s[r]); }
+    lo_s = (int)((B + P - 1) / P);
+    hi_s = mx;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 512) {   // place e inside its owner's group
+    const int h = h_s[e], be = b_s[e];
+    int pos = goff_s[h];
+    for (int e2 = 0; e2 < E; ++e2)
+      if (h_s[e2] == h && (b_s[e2] > be || (b_s[e2] == be && e2 < e))) ++pos;
+    ord_s[pos] = e;
+  }
+  __syncthreads();
+
+  // binary search, three levels per round: probe wave i takes node i of the
+  // next three levels (heap order) and the walk below follows the answers
+  // exactly as a one-midpoint-at-a-time search would
+  for (int round = 0; round < 32; ++round) {
+    const int lo = lo_s, hi = hi_s;
+    if (lo >= hi) break;
+    if (w < kQuotaProbes) {
+      int a = lo, bnd = hi;
+      const int path = w + 1;                 // heap index + 1: bits below the top bit are the turns
+      const int depth = 31 - __clz(path);
+      for (int d = depth - 1; d >= 0; --d) {
+        const int mid = (a + bnd) >> 1;
+        if ((path >> d) & 1) a = mid + 1; else bnd = mid;   // right: infeasible at mid
+      }
+      int f = -1;
+      if (a < bnd) {
+        int ell, rep;
+        f = quota_pass((a + bnd) >> 1, E, P, s, umin, b_s, ord_s, goff_s, ell0_s, lane, ell, rep,
+                       nullptr) ? 1 : 0;
+      }
+      if (lane == 0) feas_s[w] = f;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int a = lo, bnd = hi, i = 0;
+      for (int d = 0; d < 3 && a < bnd; ++d) {
+        const int mid = (a + bnd) >> 1;
+        if (feas_s[i] == 1) { bnd = mid; i = 2 * i + 1; } else { a = mid + 1; i = 2 * i + 2; }
+      }
+      lo_s = a;
+      hi_s = bnd;
+    }
+    __syncthreads();
+  }
+  const int tau = lo_s;
+  if (w == kQuotaWaves - 1) {
+    int ell, rep;
+    quota_pass(tau, E, P, s, umin, b_s, ord_s, goff_s, ell0_s, lane, ell, rep, mv_s);
+    if (lane < P) fin_ell[lane] = ell;
+    const int reps = wave_sum(lane < P ? rep : 0);
+    if (lane == 0) fin_rep = reps;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int obj = 0;
+    for (int r = 0; r < P; ++r) obj = max(obj, fin_ell[r]);
+    info_out[0] = obj;
+    info_out[1] = 4;
+    info_out[2] = fin_rep;
+    info_out[3] = tau;
+  }
+  if (tid < P) load_out[tid] = fin_ell[tid];
+  for (int i = tid; i < E * P; i += 512) {
+    const int e = i / P, t = i % P;
+    int moved = 0;
+    for (int u = 0; u < P; ++u) moved += mv_s[e * 8 + u];
+    q_out[i] = (t == h_s[e]) ? b_s[e] - moved : mv_s[e * 8 + t];
+  }
+  const int nb = boff_s[E];
+  for (int g = tid; g < nb; g += 512) {
+    int lo = 0, hi = E;  // largest e with boff_s[e] <= g
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (boff_s[mid] <= g) lo = mid; else hi = mid;
+    }
+    const int e = lo, h = h_s[e];
+    int moved = 0;
+    for (int u = 0; u < P; ++u) moved += mv_s[e * 8 + u];
+    int i = g - boff_s[e];
+    int wk = h;
+    if (i >= b_s[e] - moved) {
+      i -= b_s[e] - moved;
+      for (int t = 0; t < P; ++t) {
+        if (t == h) continue;
+        const int qt = mv_s[e * 8 + t];
+        if (i < qt) { wk = t; break; }
+        i -= qt;
+      }
+    }
+    bw_out[g] = wk;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 size_t route_ws_bytes(int T, int k, int E) {
@@ -368,6 +569,12 @@ int launch_route_stats(const int32_t* ids, int T, int k, int E, int beta, int32_
 int launch_plan(const int32_t* bcnt, const int32_t* boff, const int32_t* owner, int E, int P,
                 int s, int mode, int lam, int32_t* q, int32_t* load, int32_t* bw,
                 int32_t* info, int32_t* status, hipStream_t st) {
+  if (mode == MOE_PLAN_QUOTA) {
+    const size_t lds = sizeof(int) * (size_t)(4 * E + 1 + 8 * E);
+    hipLaunchKernelGGL(k_plan_quota, dim3(1), dim3(512), lds, st, bcnt, boff, owner, E, P, s,
+                       lam, q, load, bw, info, status);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  }
   const size_t lds = sizeof(int) * (size_t)(3 * E + 1 + 4 * E + 4 * E * 8);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(256), lds, st, bcnt, boff, owner, E, P, s, mode,
                      lam, q, load, bw, info, status);

@@ -12,13 +12,16 @@ from . import binding as B
 
 class LayerRunner:
     def __init__(self, w1, w2, w1_scale=None, w2_scale=None, *, act_dtype, T, k, beta, P, s,
-                 owner, lam=12, with_backward=False, save_z=None):
+                 owner, lam=12, with_backward=False, save_z=None, quota_umin=None):
         dev = w1.device
         self.dev = dev
         self.layer = B.make_layer(w1, w2, w1_scale, w2_scale, act_dtype)
         self.keep = (w1, w2, w1_scale, w2_scale)
         self.E, self.d, self.dff = self.layer.E, self.layer.d, self.layer.d_ff
         self.T, self.k, self.beta, self.P, self.s, self.lam = T, k, beta, P, s, lam
+        # quota_umin set: every plan (forward and backward) comes from the
+        # quota-driven solver with that quota floor
+        self.quota_umin = quota_umin
         self.act_dtype = act_dtype
         self.owner = owner.to(device=dev, dtype=torch.int32).contiguous()
         self.with_backward = with_backward
@@ -42,8 +45,11 @@ class LayerRunner:
 
     def make_plan(self, mode=B.PLAN_FWD, s=None, out=None):
         out = self.plan_f if out is None else out
+        lam = self.lam
+        if self.quota_umin is not None:
+            mode, lam = B.PLAN_QUOTA, self.quota_umin
         return B.plan(self.rs["block_counts"], self.rs["block_offsets"], self.owner, self.P,
-                      self.s if s is None else s, mode, self.lam, out, self.ws, self.status)
+                      self.s if s is None else s, mode, lam, out, self.ws, self.status)
 
     def forward(self, x, gates, topk_ids, block_worker=None, events=None):
         bw = self.plan_f["block_worker"] if block_worker is None else block_worker

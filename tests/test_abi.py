@@ -67,7 +67,9 @@ def test_host_validation_errors():
     # planner
     assert lib.moe_plan(P, P, P, 8, 3, 1, 0, 12, *([P] * 5), P, 0, None) == B.MOE_ERR_UNSUPPORTED
     assert lib.moe_plan(P, P, P, 8, 4, -1, 0, 12, *([P] * 5), P, 0, None) == B.MOE_ERR_ARG
-    assert lib.moe_plan(P, P, P, 8, 4, 1, 2, 12, *([P] * 5), P, 0, None) == B.MOE_ERR_ARG
+    assert lib.moe_plan(P, P, P, 8, 4, 1, 3, 12, *([P] * 5), P, 0, None) == B.MOE_ERR_ARG
+    # quota mode: lambda is the quota floor and must be at least one block
+    assert lib.moe_plan(P, P, P, 8, 4, 1, B.PLAN_QUOTA, 0, *([P] * 5), P, 0, None) == B.MOE_ERR_ARG
     assert lib.moe_plan(P, P, P, 8, 4, 1, 0, -1, *([P] * 5), P, 0, None) == B.MOE_ERR_ARG
     assert lib.moe_plan(P, P, P, 600, 4, 1, 0, 12, *([P] * 5), P, 0, None) == B.MOE_ERR_UNSUPPORTED
     # forward / backward layer checks
