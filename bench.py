@@ -44,6 +44,11 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="also time every kappa of the workload: fixed placement, the bounded "
                          "greedy planner and the quota planner, and compare the two planners")
+    ap.add_argument("--gate-sweep", action="store_true",
+                    help="time near-balanced kappas: fixed placement, the planner, and the "
+                         "planner behind the replication gate")
+    ap.add_argument("--gate-rho", type=int, default=1000,
+                    help="replication gate price per replica, thousandths of a block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=512)
     return ap.parse_args()
@@ -53,7 +58,7 @@ def flops_per_row(w):
     return 6 * w.d * w.d_ff, 12 * w.d * w.d_ff
 
 
-def build_case(w, kappa, fixed, dev, quota_umin=None):
+def build_case(w, kappa, fixed, dev, quota_umin=None, gate_rho=None, lam=12):
     import torch
 
     from moe_expert_ffn_amd.inputs import contiguous_owners, make_dy, make_layer, make_routing, make_x
@@ -67,7 +72,7 @@ def build_case(w, kappa, fixed, dev, quota_umin=None):
     r = LayerRunner(lay["w1"], lay["w2"], lay.get("w1_scale"), lay.get("w2_scale"), act_dtype=act,
                     T=T, k=w.k, beta=w.beta, P=w.P, s=0 if fixed else w.s,
                     owner=torch.from_numpy(contiguous_owners(w.E, w.P)), with_backward=w.backward,
-                    quota_umin=quota_umin)
+                    quota_umin=quota_umin, gate_rho=gate_rho, lam=lam)
     return dict(runner=r, x=x, gates=torch.from_numpy(gates).to(dev), ids=torch.from_numpy(ids).to(dev),
                 dy=dy, ids_np=ids, gates_np=gates, lay=lay, T=T)
 
@@ -301,9 +306,10 @@ def main():
     if args.sweep:
         sweep, planners = [], []
         for kap in w.kappas:
-            for arm, fixed, umin in (("fixed", True, None), ("planned", False, None),
-                                     ("planned-quota", False, 1)):
-                c = build_case(w, kap, fixed, dev, quota_umin=umin)
+            for arm, fixed, umin, lam in (("fixed", True, None, 12), ("planned", False, None, 12),
+                                          ("planned-lambda1", False, None, 1),
+                                          ("planned-quota", False, 1, 12)):
+                c = build_case(w, kap, fixed, dev, quota_umin=umin, lam=lam)
                 Rk = int((c["ids_np"] >= 0).sum())
                 msk, st = time_steps(c, max(5, args.steps // 2), 2)
                 uk = (f_fwd + (f_bwd if w.backward else 0)) * Rk
@@ -317,6 +323,20 @@ def main():
                 torch.cuda.empty_cache()
         out["kappa_sweep"] = sweep
         out["planners"] = planners
+    if args.gate_sweep:
+        gs = []
+        for kap in (1.05, 1.1, 1.25, 1.5, 2.0):
+            for arm, fixed, rho in (("fixed", True, None), ("planned", False, None),
+                                    ("planned-gated", False, args.gate_rho)):
+                c = build_case(w, kap, fixed, dev, gate_rho=rho)
+                msk, _ = time_steps(c, max(5, args.steps // 2), 2)
+                pf = c["runner"].plan_f["plan_info"].cpu().tolist()
+                pb = c["runner"].plan_b["plan_info"].cpu().tolist() if w.backward else None
+                gs.append({"kappa": kap, "placement": arm, "ms": round(msk, 4),
+                           "plan_info_fwd": pf, "plan_info_bwd": pb})
+                del c
+                torch.cuda.empty_cache()
+        out["gate_sweep"] = {"rho_milli": args.gate_rho, "runs": gs}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case, w, args.cpu_tokens)
     print(json.dumps(out), flush=True)

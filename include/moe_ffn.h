@@ -144,6 +144,27 @@ int moe_plan(const int32_t* block_counts, const int32_t* block_offsets,
              int32_t* q, int32_t* load, int32_t* block_worker, int32_t* plan_info,
              int32_t* status_dev, void* ws, size_t ws_bytes, void* stream);
 
+/* Runtime replication gate (MegaFlux summary, "Limitations": enable
+ * replication only when the predicted saving exceeds its cost; "Empirical
+ * Validation": near-balanced routes gain nothing from replicas).  Applied on
+ * the device to a plan made by moe_plan, in place, with no host round trip.
+ * A plan's predicted cost is its objective max_r l_r (blocks on the busiest
+ * worker) plus rho per replica; rho_milli is rho in thousandths of a block.
+ * The plan is kept when
+ *     1000 * (fixed-placement objective - plan objective) > rho_milli * replicas
+ * or when it has no replica; otherwise q, load and block_worker are rewritten
+ * as the fixed placement (every block on its owner) and plan_info becomes
+ * {fixed objective, -1, 0, tau}.
+ *   block_counts [E], block_offsets [E+1], owner [E]: as given to moe_plan.
+ *   q [E][P], load [P], block_worker [sum b], plan_info [4]: moe_plan's
+ *   outputs, read and (when gated off) overwritten.
+ * Errors: MOE_ERR_ARG for E < 1, rho_milli < 0 or a null pointer;
+ *   MOE_ERR_UNSUPPORTED for E > 512 or P outside {1,2,4,8}; an owner outside
+ *   [0, P) sets MOE_DEV_BAD_OWNER in *status_dev. */
+int moe_plan_gate(const int32_t* block_counts, const int32_t* block_offsets,
+                  const int32_t* owner, int E, int P, int rho_milli, int32_t* q, int32_t* load,
+                  int32_t* block_worker, int32_t* plan_info, int32_t* status_dev, void* stream);
+
 /* Forward expert layer ("Backward" section, expert-computation equation):
  *   y_t = sum_{j: id_tj >= 0} p_tj * W2_e (SiLU(G) * U),  [G; U] = W1_e x_t,
  * executed over the planned blocks: worker r's CU partition runs the blocks

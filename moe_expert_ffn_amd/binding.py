@@ -21,7 +21,8 @@ PLAN_FWD, PLAN_BWD, PLAN_QUOTA = 0, 1, 2
 DEV_BAD_EXPERT, DEV_BAD_PLAN, DEV_BAD_OWNER = 1, 2, 4
 
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_max_slots", "moe_max_blocks",
-           "moe_workspace_size", "moe_route_stats", "moe_plan", "moe_forward", "moe_backward",
+           "moe_workspace_size", "moe_route_stats", "moe_plan", "moe_plan_gate", "moe_forward",
+           "moe_backward",
            "moe_event_create", "moe_event_destroy", "moe_event_record", "moe_event_elapsed_ms",
            "moe_device_info"]
 
@@ -64,6 +65,8 @@ def load():
     lib.moe_route_stats.argtypes = [_P, _I, _I, _I, _I] + [_P] * 8 + [_P, _SZ, _P]
     lib.moe_plan.restype = _I
     lib.moe_plan.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I] + [_P] * 5 + [_P, _SZ, _P]
+    lib.moe_plan_gate.restype = _I
+    lib.moe_plan_gate.argtypes = [_P, _P, _P, _I, _I, _I] + [_P] * 5 + [_P]
     lib.moe_forward.restype = _I
     lib.moe_forward.argtypes = ([ctypes.POINTER(Layer), _P, _P, _P, _I, _I, _I, _I]
                                 + [_P] * 8 + [_P, _SZ, _P, _P])
@@ -166,6 +169,16 @@ def alloc_plan(E, P, nblocks_cap, device):
     return {"q": torch.empty((E, P), **i32), "load": torch.empty(P, **i32),
             "block_worker": torch.full((max(nblocks_cap, 1),), -1, **i32),
             "plan_info": torch.empty(4, **i32)}
+
+
+def plan_gate(block_counts, block_offsets, owner, P, rho_milli, out, status):
+    _require_device(block_counts, block_offsets, owner, status, *out.values())
+    E = block_counts.numel()
+    _check(load().moe_plan_gate(_ptr(block_counts), _ptr(block_offsets), _ptr(owner), E, P,
+                                rho_milli, _ptr(out["q"]), _ptr(out["load"]),
+                                _ptr(out["block_worker"]), _ptr(out["plan_info"]), _ptr(status),
+                                _stream()))
+    return out
 
 
 def plan(block_counts, block_offsets, owner, P, s, mode, lam, out, ws, status):

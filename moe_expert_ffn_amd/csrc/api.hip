@@ -131,6 +131,18 @@ int moe_plan(const int32_t* block_counts, const int32_t* block_offsets, const in
                      block_worker, plan_info, status_dev, (hipStream_t)stream);
 }
 
+int moe_plan_gate(const int32_t* block_counts, const int32_t* block_offsets, const int32_t* owner,
+                  int E, int P, int rho_milli, int32_t* q, int32_t* load, int32_t* block_worker,
+                  int32_t* plan_info, int32_t* status_dev, void* stream) {
+  if (E < 1 || rho_milli < 0) return MOE_ERR_ARG;
+  if (!valid_P(P) || E > kMaxPlanExperts) return MOE_ERR_UNSUPPORTED;
+  if (!block_counts || !block_offsets || !owner || !q || !load || !block_worker || !plan_info ||
+      !status_dev)
+    return MOE_ERR_ARG;
+  return launch_plan_gate(block_counts, block_offsets, owner, E, P, rho_milli, q, load,
+                          block_worker, plan_info, status_dev, (hipStream_t)stream);
+}
+
 int moe_forward(const moe_layer* L, const void* x, const float* gates, const int32_t* topk_ids,
                 int T, int k, int beta, int P, const int32_t* counts,
                 const int32_t* block_offsets, const int32_t* row_to_slot,

@@ -540,6 +540,65 @@ __global__ __launch_bounds__(512) void k_plan_quota(const int32_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// Runtime replication gate (MegaFlux summary, "Limitations": replication only
+// when the predicted saving exceeds its cost; "Empirical Validation": balanced
+// routes gain nothing).  Predicted cost of a plan, in blocks on the busiest
+// worker: objective + rho per replica (rho in thousandths of a block).  The
+// plan stays when 1000 (fixed objective - plan objective) > rho * replicas;
+// otherwise it is rewritten in place as the fixed placement with plan_info =
+// {fixed objective, -1, 0, tau}.  A plan without replicas is left as it is.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_plan_gate(const int32_t* __restrict__ bcnt,
+                                                   const int32_t* __restrict__ boff,
+                                                   const int32_t* __restrict__ owner, int E, int P,
+                                                   int rho_milli, int32_t* q, int32_t* load,
+                                                   int32_t* bw, int32_t* info, int32_t* status) {
+  __shared__ int ellfix[kMaxP], keep_s;
+  const int tid = threadIdx.x;
+  if (tid < kMaxP) ellfix[tid] = 0;
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    int h = owner[e];
+    if (h < 0 || h >= P) { atomicOr(status, MOE_DEV_BAD_OWNER); h = 0; }
+    atomicAdd(&ellfix[h], bcnt[e]);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int objfix = 0, objplan = 0;
+    for (int r = 0; r < P; ++r) { objfix = max(objfix, ellfix[r]); objplan = max(objplan, load[r]); }
+    const int reps = info[2];
+    const bool keep = reps == 0 ||
+                      1000LL * (long long)(objfix - objplan) > (long long)rho_milli * (long long)reps;
+    keep_s = keep;
+    if (!keep) {
+      info[0] = objfix;
+      info[1] = -1;
+      info[2] = 0;
+    }
+  }
+  __syncthreads();
+  if (keep_s) return;
+  if (tid < P) load[tid] = ellfix[tid];
+  for (int i = tid; i < E * P; i += 256) {
+    const int e = i / P, t = i % P;
+    int h = owner[e];
+    if (h < 0 || h >= P) h = 0;
+    q[i] = (t == h) ? bcnt[e] : 0;
+  }
+  const int nb = boff[E];
+  for (int g = tid; g < nb; g += 256) {
+    int lo = 0, hi = E;  // largest e with boff[e] <= g
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (boff[mid] <= g) lo = mid; else hi = mid;
+    }
+    int h = owner[lo];
+    if (h < 0 || h >= P) h = 0;
+    bw[g] = h;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 size_t route_ws_bytes(int T, int k, int E) {
@@ -578,6 +637,14 @@ int launch_plan(const int32_t* bcnt, const int32_t* boff, const int32_t* owner, 
   const size_t lds = sizeof(int) * (size_t)(3 * E + 1 + 4 * E + 4 * E * 8);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(256), lds, st, bcnt, boff, owner, E, P, s, mode,
                      lam, q, load, bw, info, status);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int launch_plan_gate(const int32_t* bcnt, const int32_t* boff, const int32_t* owner, int E, int P,
+                     int rho_milli, int32_t* q, int32_t* load, int32_t* bw, int32_t* info,
+                     int32_t* status, hipStream_t st) {
+  hipLaunchKernelGGL(k_plan_gate, dim3(1), dim3(256), 0, st, bcnt, boff, owner, E, P, rho_milli,
+                     q, load, bw, info, status);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

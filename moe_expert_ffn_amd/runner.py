@@ -12,7 +12,8 @@ from . import binding as B
 
 class LayerRunner:
     def __init__(self, w1, w2, w1_scale=None, w2_scale=None, *, act_dtype, T, k, beta, P, s,
-                 owner, lam=12, with_backward=False, save_z=None, quota_umin=None):
+                 owner, lam=12, with_backward=False, save_z=None, quota_umin=None,
+                 gate_rho=None):
         dev = w1.device
         self.dev = dev
         self.layer = B.make_layer(w1, w2, w1_scale, w2_scale, act_dtype)
@@ -22,6 +23,9 @@ class LayerRunner:
         # quota_umin set: every plan (forward and backward) comes from the
         # quota-driven solver with that quota floor
         self.quota_umin = quota_umin
+        # gate_rho set: every plan passes the replication gate with that price
+        # per replica (thousandths of a block)
+        self.gate_rho = gate_rho
         self.act_dtype = act_dtype
         self.owner = owner.to(device=dev, dtype=torch.int32).contiguous()
         self.with_backward = with_backward
@@ -48,8 +52,12 @@ class LayerRunner:
         lam = self.lam
         if self.quota_umin is not None:
             mode, lam = B.PLAN_QUOTA, self.quota_umin
-        return B.plan(self.rs["block_counts"], self.rs["block_offsets"], self.owner, self.P,
-                      self.s if s is None else s, mode, lam, out, self.ws, self.status)
+        B.plan(self.rs["block_counts"], self.rs["block_offsets"], self.owner, self.P,
+               self.s if s is None else s, mode, lam, out, self.ws, self.status)
+        if self.gate_rho is not None:
+            B.plan_gate(self.rs["block_counts"], self.rs["block_offsets"], self.owner, self.P,
+                        self.gate_rho, out, self.status)
+        return out
 
     def forward(self, x, gates, topk_ids, block_worker=None, events=None):
         bw = self.plan_f["block_worker"] if block_worker is None else block_worker

@@ -72,6 +72,12 @@ def test_host_validation_errors():
     assert lib.moe_plan(P, P, P, 8, 4, 1, B.PLAN_QUOTA, 0, *([P] * 5), P, 0, None) == B.MOE_ERR_ARG
     assert lib.moe_plan(P, P, P, 8, 4, 1, 0, -1, *([P] * 5), P, 0, None) == B.MOE_ERR_ARG
     assert lib.moe_plan(P, P, P, 600, 4, 1, 0, 12, *([P] * 5), P, 0, None) == B.MOE_ERR_UNSUPPORTED
+    # replication gate: price >= 0, P in {1,2,4,8}, E <= 512, no null pointers
+    assert lib.moe_plan_gate(P, P, P, 8, 4, -1, *([P] * 5), None) == B.MOE_ERR_ARG
+    assert lib.moe_plan_gate(P, P, P, 0, 4, 1000, *([P] * 5), None) == B.MOE_ERR_ARG
+    assert lib.moe_plan_gate(P, P, P, 8, 3, 1000, *([P] * 5), None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_plan_gate(P, P, P, 600, 4, 1000, *([P] * 5), None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_plan_gate(P, None, P, 8, 4, 1000, *([P] * 5), None) == B.MOE_ERR_ARG
     # forward / backward layer checks
     bad_d = _layer(d=96)
     assert lib.moe_forward(ctypes.byref(bad_d), P, P, P, 4, 2, 16, 4, *([P] * 8), P, 1 << 30,
