@@ -1,0 +1,126 @@
+"""Oracle: wave-quantized cost model for choosing the CU partition count P
+-- TEST INFRASTRUCTURE ONLY.
+
+The page "Analytical Resource Management for Fine-grained MoE
+Computation-Communication Overlap" (weekinpapers.com, abstract) selects a
+launch's resource partition before the launch from routed-tile counts, kernel
+occupancy and residency, with a wave-quantized analytical model and no
+candidate execution.  Here the resource partition is P, the number of CU
+partitions (workers) the expert layer runs on, and the model predicts the
+time of one forward + backward pass of a plan made for that P.
+
+Reading (the HIP cost kernel computes exactly the same integers):
+* a worker owns G / P workgroups (G = one workgroup per CU); the persistent
+  GEMM launches deal a worker's items round-robin: workgroup j takes items
+  j, j + n, j + 2n, ... (n = G / P), so a phase lasts, on that worker, as long
+  as its busiest workgroup, and the phase as long as its busiest worker;
+* items: a (row tile, N tile) pair for FC1, FC2, dA and dX, and a (segment,
+  256 x 256 output tile) pair for the weight gradients; a row tile is up to
+  bm = 256 consecutive slots of one (expert, worker) run of blocks: a run of
+  n_b blocks gives ceil(n_b * beta / bm) tiles when beta divides bm, and
+  every block gives ceil(rows / bm) tiles otherwise; N tiles: 2 d_ff / 256
+  (FC1), d / 256 (FC2, dX), d_ff / 256 (dA); a segment is the rows of one
+  (expert, worker) pair of the backward plan, replica segments first, each
+  in expert order, with (d / 256)(d_ff / 256) + (2 d_ff / 256)(d / 256) tiles;
+* an item costs its K steps (K / 64; d / 64 for FC1 and dA, d_ff / 64 for
+  FC2, 2 d_ff / 64 for dX, max(2, ceil(rows / 64)) for a weight-gradient
+  tile) plus its epilogue, counted in thousandths of a step: the bytes it
+  writes (and for dA the bytes of [G, U] it reads) divided by what one CU
+  stores during one step (EPI_BYTES_PER_STEP, 214,000 bytes: 121 GB/s per CU
+  times 1.77 us per step, both measured once on MI355X for this engine);
+* the predicted cost of a plan is the sum over the five phases, in
+  thousandths of a step; the selector takes the P of smallest cost, ties to
+  the larger P.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+EPI_BYTES_PER_STEP = 214_000
+CANDIDATE_P = (1, 2, 4, 8)
+
+
+def epilogue_milli(bytes_moved: int) -> int:
+    return (bytes_moved * 1000) // EPI_BYTES_PER_STEP
+
+
+def _row_tiles(counts, block_worker, beta, P, bm=256):
+    """Row tiles per worker (how the executors cut each (expert, worker) run)."""
+    E = len(counts)
+    nb = [(int(c) + beta - 1) // beta for c in counts]
+    tiles = [0] * P
+    g = 0
+    for e in range(E):
+        per_w = {}
+        for i in range(nb[e]):
+            w = int(block_worker[g + i])
+            rows = min(beta, int(counts[e]) - beta * i)
+            per_w.setdefault(w, []).append(rows)
+        for w, rows in per_w.items():
+            if bm % beta == 0:
+                f = bm // beta
+                tiles[w] += (len(rows) + f - 1) // f
+            else:
+                tiles[w] += sum((r + bm - 1) // bm for r in rows)
+        g += nb[e]
+    return tiles
+
+
+def _segments(counts, block_worker, owner, beta, P):
+    """Weight-gradient segments per worker: list of row counts in execution order."""
+    E = len(counts)
+    rows = np.zeros((E, P), dtype=np.int64)
+    g = 0
+    for e in range(E):
+        nbe = (int(counts[e]) + beta - 1) // beta
+        for i in range(nbe):
+            rows[e, int(block_worker[g + i])] += min(beta, int(counts[e]) - beta * i)
+        g += nbe
+    segs = []
+    for r in range(P):
+        order = [e for e in range(E) if owner[e] != r] + [e for e in range(E) if owner[e] == r]
+        segs.append([int(rows[e, r]) for e in order if rows[e, r] > 0])
+    return segs
+
+
+def _phase(items_per_worker_costs, n):
+    """Busiest workgroup over all workers; items are dealt round-robin."""
+    worst = 0
+    for costs in items_per_worker_costs:
+        wg = [0] * n
+        for i, c in enumerate(costs):
+            wg[i % n] += c
+        worst = max(worst, max(wg) if wg else 0)
+    return worst
+
+
+def predicted_cost(counts, bw_fwd, bw_bwd, owner, beta, P, d, d_ff, G=256, bm=256) -> int:
+    """Predicted forward + backward time of the plans, thousandths of a step."""
+    n = G // P
+    tf = _row_tiles(counts, bw_fwd, beta, P, bm)
+    tb = _row_tiles(counts, bw_bwd, beta, P, bm)
+    fc1 = 1000 * (d // 64) + epilogue_milli(bm * (128 + 256) * 2)    # A and the saved [G, U]
+    fc2 = 1000 * (d_ff // 64) + epilogue_milli(bm * 256 * 2)
+    da = 1000 * (d // 64) + epilogue_milli(bm * 256 * 3 * 2 + bm * 512 * 2)
+    dx = 1000 * (2 * d_ff // 64) + epilogue_milli(bm * 256 * 2)
+    cost = 0
+    cost += _phase([[fc1] * (t * (2 * d_ff // 256)) for t in tf], n)
+    cost += _phase([[fc2] * (t * (d // 256)) for t in tf], n)
+    cost += _phase([[da] * (t * (d_ff // 256)) for t in tb], n)
+    cost += _phase([[dx] * (t * (d // 256)) for t in tb], n)
+    per_seg = (d // 256) * (d_ff // 256) + (2 * d_ff // 256) * (d // 256)
+    dw_epi = epilogue_milli(256 * 256 * 4)
+    dw = []
+    for segs in _segments(counts, bw_bwd, owner, beta, P):
+        costs = []
+        for rows in segs:
+            c = 1000 * max(2, (rows + 63) // 64) + dw_epi
+            costs += [c] * per_seg
+        dw.append(costs)
+    cost += _phase(dw, n)
+    return int(cost)
+
+
+def select_partition(costs: dict) -> int:
+    """P of smallest predicted cost; ties go to the larger P."""
+    return min(costs, key=lambda p: (costs[p], -p))
