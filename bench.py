@@ -49,6 +49,9 @@ def parse():
                          "planner behind the replication gate")
     ap.add_argument("--gate-rho", type=int, default=1000,
                     help="replication gate price per replica, thousandths of a block")
+    ap.add_argument("--size-sweep", action="store_true",
+                    help="time every CU partition count P at every kappa next to the "
+                         "wave-quantized cost model's prediction, and report the selector's regret")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=512)
     return ap.parse_args()
@@ -58,7 +61,7 @@ def flops_per_row(w):
     return 6 * w.d * w.d_ff, 12 * w.d * w.d_ff
 
 
-def build_case(w, kappa, fixed, dev, quota_umin=None, gate_rho=None, lam=12):
+def build_case(w, kappa, fixed, dev, quota_umin=None, gate_rho=None, lam=12, P=None):
     import torch
 
     from moe_expert_ffn_amd.inputs import contiguous_owners, make_dy, make_layer, make_routing, make_x
@@ -70,8 +73,8 @@ def build_case(w, kappa, fixed, dev, quota_umin=None, gate_rho=None, lam=12):
     act = torch.float32 if w.act == "f32" else torch.bfloat16
     dy = make_dy(w, T, dev) if w.backward else None
     r = LayerRunner(lay["w1"], lay["w2"], lay.get("w1_scale"), lay.get("w2_scale"), act_dtype=act,
-                    T=T, k=w.k, beta=w.beta, P=w.P, s=0 if fixed else w.s,
-                    owner=torch.from_numpy(contiguous_owners(w.E, w.P)), with_backward=w.backward,
+                    T=T, k=w.k, beta=w.beta, P=P or w.P, s=0 if fixed else w.s,
+                    owner=torch.from_numpy(contiguous_owners(w.E, P or w.P)), with_backward=w.backward,
                     quota_umin=quota_umin, gate_rho=gate_rho, lam=lam)
     return dict(runner=r, x=x, gates=torch.from_numpy(gates).to(dev), ids=torch.from_numpy(ids).to(dev),
                 dy=dy, ids_np=ids, gates_np=gates, lay=lay, T=T)
@@ -337,6 +340,29 @@ def main():
                 del c
                 torch.cuda.empty_cache()
         out["gate_sweep"] = {"rho_milli": args.gate_rho, "runs": gs}
+    if args.size_sweep:
+        rows, regrets = [], []
+        for kap in w.kappas:
+            per = {}
+            for P in (1, 2, 4, 8):
+                c = build_case(w, kap, False, dev, P=P)
+                msk, _ = time_steps(c, max(5, args.steps // 2), 2)
+                r = c["runner"]
+                cost = torch.zeros(1, dtype=torch.int64, device=dev)
+                B.predict_cost(r.rs["counts"], r.rs["block_offsets"], r.plan_f["block_worker"],
+                               r.plan_b["block_worker"], r.owner, w.beta, P, w.d, w.d_ff, cost,
+                               r.status)
+                per[P] = (msk, int(cost.item()))
+                del c
+                torch.cuda.empty_cache()
+            chosen = min(per, key=lambda p: (per[p][1], -p))
+            best = min(per, key=lambda p: per[p][0])
+            regret = per[chosen][0] / per[best][0] - 1
+            regrets.append(regret)
+            rows.append({"kappa": kap, "chosen_P": chosen, "best_P": best, "regret": round(regret, 4),
+                         "per_P": {p: {"ms": round(v[0], 4), "predicted_steps": round(v[1] / 1000, 1)}
+                                   for p, v in per.items()}})
+        out["size_sweep"] = {"runs": rows, "mean_regret": round(sum(regrets) / len(regrets), 4)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case, w, args.cpu_tokens)
     print(json.dumps(out), flush=True)

@@ -165,6 +165,35 @@ int moe_plan_gate(const int32_t* block_counts, const int32_t* block_offsets,
                   const int32_t* owner, int E, int P, int rho_milli, int32_t* q, int32_t* load,
                   int32_t* block_worker, int32_t* plan_info, int32_t* status_dev, void* stream);
 
+/* Predicted time of one forward + backward pass under a pair of plans
+ * ("Analytical Resource Management for Fine-grained MoE
+ * Computation-Communication Overlap", abstract: a wave-quantized analytical
+ * model picks the resource partition before each launch from routed-tile
+ * counts and occupancy, with no candidate run).  The partition chosen here is
+ * P, the number of CU partitions: call moe_plan for each candidate P (with
+ * that P's owners), then this for each, and run with the smallest cost.
+ *   counts [E], block_offsets [E+1]: from moe_route_stats.
+ *   block_worker_fwd / block_worker_bwd [sum b]: the forward and backward
+ *   plans' block workers; owner [E]: h(e) for this P.
+ *   num_workgroups: workgroups of the persistent launches (one per CU);
+ *   <= 0 takes the device's CU count.
+ * Model: worker r owns n = num_workgroups / P workgroups and deals its items
+ * round-robin, so each phase lasts as long as its busiest workgroup.  Items:
+ * (row tile, N tile) pairs for FC1, FC2, dA and dX, a row tile being up to 256
+ * slots of one (expert, worker) run; (segment, 256 x 256 tile) pairs for the
+ * weight gradients, replica segments first.  An item costs its K steps of 64
+ * plus its epilogue's bytes over 214,000 (what one CU stores in one step).
+ * *cost_dev (int64): the sum over the five phases, thousandths of a step.
+ * Errors: MOE_ERR_ARG for a non-positive size or a null pointer;
+ *   MOE_ERR_UNSUPPORTED for E > 512, P outside {1,2,4,8}, d or d_ff not a
+ *   multiple of 256, or num_workgroups not a multiple of P or above 256 P;
+ *   a worker outside [0, P) in a plan sets MOE_DEV_BAD_PLAN, an owner outside
+ *   [0, P) MOE_DEV_BAD_OWNER in *status_dev. */
+int moe_predict_cost(const int32_t* counts, const int32_t* block_offsets,
+                     const int32_t* block_worker_fwd, const int32_t* block_worker_bwd,
+                     const int32_t* owner, int E, int beta, int P, int d, int d_ff,
+                     int num_workgroups, int64_t* cost_dev, int32_t* status_dev, void* stream);
+
 /* Forward expert layer ("Backward" section, expert-computation equation):
  *   y_t = sum_{j: id_tj >= 0} p_tj * W2_e (SiLU(G) * U),  [G; U] = W1_e x_t,
  * executed over the planned blocks: worker r's CU partition runs the blocks

@@ -21,7 +21,8 @@ PLAN_FWD, PLAN_BWD, PLAN_QUOTA = 0, 1, 2
 DEV_BAD_EXPERT, DEV_BAD_PLAN, DEV_BAD_OWNER = 1, 2, 4
 
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_max_slots", "moe_max_blocks",
-           "moe_workspace_size", "moe_route_stats", "moe_plan", "moe_plan_gate", "moe_forward",
+           "moe_workspace_size", "moe_route_stats", "moe_plan", "moe_plan_gate",
+           "moe_predict_cost", "moe_forward",
            "moe_backward",
            "moe_event_create", "moe_event_destroy", "moe_event_record", "moe_event_elapsed_ms",
            "moe_device_info"]
@@ -65,6 +66,8 @@ def load():
     lib.moe_route_stats.argtypes = [_P, _I, _I, _I, _I] + [_P] * 8 + [_P, _SZ, _P]
     lib.moe_plan.restype = _I
     lib.moe_plan.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I] + [_P] * 5 + [_P, _SZ, _P]
+    lib.moe_predict_cost.restype = _I
+    lib.moe_predict_cost.argtypes = [_P] * 5 + [_I] * 6 + [_P, _P, _P]
     lib.moe_plan_gate.restype = _I
     lib.moe_plan_gate.argtypes = [_P, _P, _P, _I, _I, _I] + [_P] * 5 + [_P]
     lib.moe_forward.restype = _I
@@ -169,6 +172,16 @@ def alloc_plan(E, P, nblocks_cap, device):
     return {"q": torch.empty((E, P), **i32), "load": torch.empty(P, **i32),
             "block_worker": torch.full((max(nblocks_cap, 1),), -1, **i32),
             "plan_info": torch.empty(4, **i32)}
+
+
+def predict_cost(counts, block_offsets, bw_fwd, bw_bwd, owner, beta, P, d, d_ff, cost, status,
+                 num_workgroups=0):
+    """Wave-quantized predicted cost (int64, thousandths of a K step) into cost[0]."""
+    _require_device(counts, block_offsets, bw_fwd, bw_bwd, owner, cost, status)
+    _check(load().moe_predict_cost(_ptr(counts), _ptr(block_offsets), _ptr(bw_fwd), _ptr(bw_bwd),
+                                   _ptr(owner), counts.numel(), beta, P, d, d_ff, num_workgroups,
+                                   _ptr(cost), _ptr(status), _stream()))
+    return cost
 
 
 def plan_gate(block_counts, block_offsets, owner, P, rho_milli, out, status):

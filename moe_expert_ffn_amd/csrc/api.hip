@@ -143,6 +143,28 @@ int moe_plan_gate(const int32_t* block_counts, const int32_t* block_offsets, con
                           block_worker, plan_info, status_dev, (hipStream_t)stream);
 }
 
+int moe_predict_cost(const int32_t* counts, const int32_t* block_offsets,
+                     const int32_t* block_worker_fwd, const int32_t* block_worker_bwd,
+                     const int32_t* owner, int E, int beta, int P, int d, int d_ff,
+                     int num_workgroups, int64_t* cost_dev, int32_t* status_dev, void* stream) {
+  if (E < 1 || beta < 1 || d < 1 || d_ff < 1) return MOE_ERR_ARG;
+  if (!counts || !block_offsets || !block_worker_fwd || !block_worker_bwd || !owner || !cost_dev ||
+      !status_dev)
+    return MOE_ERR_ARG;
+  if (!valid_P(P) || E > kMaxPlanExperts || d % 256 || d_ff % 256) return MOE_ERR_UNSUPPORTED;
+  int G = num_workgroups;
+  if (G <= 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&G, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  if (G % P || G / P > 256) return MOE_ERR_UNSUPPORTED;
+  return launch_predict_cost(counts, block_offsets, block_worker_fwd, block_worker_bwd, owner, E,
+                             beta, P, d, d_ff, G, (long long*)cost_dev, status_dev,
+                             (hipStream_t)stream);
+}
+
 int moe_forward(const moe_layer* L, const void* x, const float* gates, const int32_t* topk_ids,
                 int T, int k, int beta, int P, const int32_t* counts,
                 const int32_t* block_offsets, const int32_t* row_to_slot,

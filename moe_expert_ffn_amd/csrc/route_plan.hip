@@ -599,6 +599,131 @@ __global__ __launch_bounds__(256) void k_plan_gate(const int32_t* __restrict__ b
 }
 
 // ---------------------------------------------------------------------------
+// Wave-quantized cost of a plan ("Analytical Resource Management for
+// Fine-grained MoE Computation-Communication Overlap", abstract: choose the
+// resource partition before the launch from routed-tile counts and occupancy,
+// without candidate runs).  The resource partition here is P: a worker owns
+// n = G / P workgroups and the persistent GEMM launches deal its items
+// round-robin (workgroup j takes items j, j + n, ...), so a phase lasts as long
+// as its busiest workgroup.  Items and their costs, in thousandths of a K step:
+//   FC1, FC2, dA, dX: (row tile, N tile) pairs; a row tile is up to 256 slots
+//   of one (expert, worker) run (beta | 256: ceil(blocks * beta / 256) per
+//   run, else ceil(rows / 256) per block); cost = K / 64 steps plus the
+//   epilogue's bytes over what one CU stores during a step (kEpiBytesPerStep);
+//   weight gradients: (segment, 256 x 256 tile) pairs, replica segments first,
+//   cost = max(2, ceil(rows / 64)) steps plus the fp32 tile's epilogue.
+// One workgroup; every quantity is an integer.
+// ---------------------------------------------------------------------------
+constexpr long long kEpiBytesPerStep = 214000;
+MOE_DEV long long epi_milli(long long bytes) { return bytes * 1000 / kEpiBytesPerStep; }
+MOE_DEV long long ceil_div_ll(long long a, long long b) { return (a + b - 1) / b; }
+
+__global__ __launch_bounds__(256) void k_predict_cost(const int32_t* __restrict__ counts,
+                                                      const int32_t* __restrict__ boff,
+                                                      const int32_t* __restrict__ bw_f,
+                                                      const int32_t* __restrict__ bw_b,
+                                                      const int32_t* __restrict__ owner, int E,
+                                                      int beta, int P, int d, int dff, int G,
+                                                      long long* cost_out, int32_t* status) {
+  extern __shared__ int sm[];
+  int* cnt_s = sm;                    // [E]
+  int* boff_s = cnt_s + E;            // [E+1]
+  int* own_s = boff_s + E + 1;        // [E]
+  int* nbf_s = own_s + E;             // [E][P] blocks of e on worker w, forward plan
+  int* nbb_s = nbf_s + E * P;         // [E][P] same, backward plan
+  int* rows_s = nbb_s + E * P;        // [E][P] valid rows of e on w, backward plan
+  __shared__ int tiles_s[2][kMaxP];   // per-block tiles when beta does not divide 256
+  __shared__ long long red_s[256];
+  const int tid = threadIdx.x;
+  constexpr int bm = 256;
+  for (int e = tid; e < E; e += 256) {
+    cnt_s[e] = counts[e];
+    int h = owner[e];
+    if (h < 0 || h >= P) { atomicOr(status, MOE_DEV_BAD_OWNER); h = 0; }
+    own_s[e] = h;
+  }
+  for (int e = tid; e <= E; e += 256) boff_s[e] = boff[e];
+  for (int i = tid; i < 3 * E * P; i += 256) nbf_s[i] = 0;
+  if (tid < 2 * kMaxP) tiles_s[tid / kMaxP][tid % kMaxP] = 0;
+  __syncthreads();
+  const int nb = boff_s[E];
+  for (int g = tid; g < nb; g += 256) {
+    int lo = 0, hi = E;  // largest e with boff_s[e] <= g
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (boff_s[mid] <= g) lo = mid; else hi = mid;
+    }
+    const int e = lo;
+    const int vrows = min(beta, cnt_s[e] - beta * (g - boff_s[e]));
+    int wf = bw_f[g], wb = bw_b[g];
+    if (wf < 0 || wf >= P || wb < 0 || wb >= P) { atomicOr(status, MOE_DEV_BAD_PLAN); wf = wb = 0; }
+    atomicAdd(&nbf_s[e * P + wf], 1);
+    atomicAdd(&nbb_s[e * P + wb], 1);
+    atomicAdd(&rows_s[e * P + wb], vrows);
+    if (bm % beta != 0) {
+      atomicAdd(&tiles_s[0][wf], (vrows + bm - 1) / bm);
+      atomicAdd(&tiles_s[1][wb], (vrows + bm - 1) / bm);
+    }
+  }
+  __syncthreads();
+  const int n = G / P;
+  // thread j < n is workgroup j of every worker in the weight-gradient phase
+  long long dw = 0;
+  if (tid < n) {
+    const long long per_seg = (long long)(d / 256) * (dff / 256) + (long long)(2 * dff / 256) * (d / 256);
+    const long long dwe = epi_milli(256LL * 256 * 4);
+    for (int r = 0; r < P; ++r) {
+      long long mine = 0, pos = 0;
+      for (int pass = 0; pass < 2; ++pass)
+        for (int e = 0; e < E; ++e) {
+          const int rows = rows_s[e * P + r];
+          if (rows <= 0 || (own_s[e] == r) != (pass == 1)) continue;
+          const long long c = 1000LL * max(2, (rows + 63) / 64) + dwe;
+          const long long base = pos * per_seg;
+          const long long t0 = ((tid - base) % n + n) % n;     // first tile of this segment on j
+          if (t0 < per_seg) mine += c * (1 + (per_seg - 1 - t0) / n);
+          ++pos;
+        }
+      dw = max(dw, mine);
+    }
+  }
+  red_s[tid] = dw;
+  __syncthreads();
+  if (tid == 0) {
+    long long dwmax = 0;
+    for (int j = 0; j < 256; ++j) dwmax = max(dwmax, red_s[j]);
+    long long tf[kMaxP], tb[kMaxP];
+    for (int r = 0; r < P; ++r) {
+      if (bm % beta == 0) {
+        const int f = bm / beta;
+        long long a = 0, b = 0;
+        for (int e = 0; e < E; ++e) {
+          a += (nbf_s[e * P + r] + f - 1) / f;
+          b += (nbb_s[e * P + r] + f - 1) / f;
+        }
+        tf[r] = a;
+        tb[r] = b;
+      } else {
+        tf[r] = tiles_s[0][r];
+        tb[r] = tiles_s[1][r];
+      }
+    }
+    const long long fc1 = 1000LL * (d / 64) + epi_milli((long long)bm * (128 + 256) * 2);
+    const long long fc2 = 1000LL * (dff / 64) + epi_milli((long long)bm * 256 * 2);
+    const long long da = 1000LL * (d / 64) + epi_milli((long long)bm * 256 * 3 * 2 + (long long)bm * 512 * 2);
+    const long long dx = 1000LL * (2 * dff / 64) + epi_milli((long long)bm * 256 * 2);
+    long long p1 = 0, p2 = 0, p3 = 0, p4 = 0;
+    for (int r = 0; r < P; ++r) {
+      p1 = max(p1, ceil_div_ll(tf[r] * (2 * dff / 256), n) * fc1);
+      p2 = max(p2, ceil_div_ll(tf[r] * (d / 256), n) * fc2);
+      p3 = max(p3, ceil_div_ll(tb[r] * (dff / 256), n) * da);
+      p4 = max(p4, ceil_div_ll(tb[r] * (d / 256), n) * dx);
+    }
+    *cost_out = p1 + p2 + p3 + p4 + dwmax;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 size_t route_ws_bytes(int T, int k, int E) {
@@ -645,6 +770,15 @@ int launch_plan_gate(const int32_t* bcnt, const int32_t* boff, const int32_t* ow
                      int32_t* status, hipStream_t st) {
   hipLaunchKernelGGL(k_plan_gate, dim3(1), dim3(256), 0, st, bcnt, boff, owner, E, P, rho_milli,
                      q, load, bw, info, status);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int launch_predict_cost(const int32_t* counts, const int32_t* boff, const int32_t* bw_f,
+                        const int32_t* bw_b, const int32_t* owner, int E, int beta, int P, int d,
+                        int dff, int G, long long* cost, int32_t* status, hipStream_t st) {
+  const size_t lds = sizeof(int) * (size_t)(3 * E + 1 + 3 * E * P);
+  hipLaunchKernelGGL(k_predict_cost, dim3(1), dim3(256), lds, st, counts, boff, bw_f, bw_b,
+                     owner, E, beta, P, d, dff, G, cost, status);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

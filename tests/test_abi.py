@@ -78,6 +78,13 @@ def test_host_validation_errors():
     assert lib.moe_plan_gate(P, P, P, 8, 3, 1000, *([P] * 5), None) == B.MOE_ERR_UNSUPPORTED
     assert lib.moe_plan_gate(P, P, P, 600, 4, 1000, *([P] * 5), None) == B.MOE_ERR_UNSUPPORTED
     assert lib.moe_plan_gate(P, None, P, 8, 4, 1000, *([P] * 5), None) == B.MOE_ERR_ARG
+    # cost model: sizes, P, shapes the model covers, workgroups divisible by P
+    assert lib.moe_predict_cost(*([P] * 5), 8, 128, 4, 256, 0, 256, P, P, None) == B.MOE_ERR_ARG
+    assert lib.moe_predict_cost(*([P] * 5), 8, 128, 3, 256, 256, 256, P, P, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_predict_cost(*([P] * 5), 8, 128, 4, 384, 256, 256, P, P, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_predict_cost(*([P] * 5), 8, 128, 4, 256, 256, 254, P, P, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_predict_cost(*([P] * 5), 8, 128, 1, 256, 256, 512, P, P, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_predict_cost(*([P] * 4), None, 8, 128, 4, 256, 256, 256, P, P, None) == B.MOE_ERR_ARG
     # forward / backward layer checks
     bad_d = _layer(d=96)
     assert lib.moe_forward(ctypes.byref(bad_d), P, P, P, 4, 2, 16, 4, *([P] * 8), P, 1 << 30,
