@@ -121,3 +121,52 @@ def backward(x, w1, w2, topk_ids, gates, dy, tokens=None, experts=None):
     for jj in range(k):
         dx += dx_contrib[:, jj]
     return {"dx": dx, "dw1": dw1, "dw2": dw2}
+
+
+def backward_fp8(x, w1, w2, topk_ids, gates, dy, beta, tokens=None, experts=None):
+    """The backward of an fp8-weight layer with token-axis requantization
+    (MegaFlux summary, "Backward": overlapped requantization of D_e and dZ_e).
+
+    Reading: dA, dZ and dx use the exact D = p * dy and the dequantized
+    weights (w1, w2 as given, already dequantized); the weight gradients take
+    D and dZ requantized to e4m3 in blocks of beta consecutive slots of the
+    expert (its rows in flat (token, slot) order, which is the slot order)
+    times one column (oracle.fp8.quantize_token_blocks), with x and
+    A = SiLU(G) U unquantized:  dW2 = Dq^T A,  dW1 = dZq^T X.  D is formed in
+    fp32 as p * dy (the value the device quantizes); dZ enters the
+    quantizer as fp32.
+    """
+    from oracle.fp8 import dequant_token_blocks, quantize_token_blocks
+    out = backward(x, w1, w2, topk_ids, gates, dy, tokens=tokens, experts=experts)
+    x = np.asarray(x, dtype=np.float64)
+    dy32 = np.asarray(dy, dtype=np.float32)
+    ids = np.asarray(topk_ids)
+    p32 = np.asarray(gates, dtype=np.float32)
+    T, k = ids.shape
+    E = w1.shape[0]
+    F = w1.shape[1] // 2
+    experts = range(E) if experts is None else experts
+    all_pairs = _pairs_by_expert(ids, np.arange(T))
+    for e in experts:
+        e = int(e)
+        ti, j = all_pairs.get(e, (np.zeros(0, int), np.zeros(0, int)))
+        w1e = np.asarray(w1[e], dtype=np.float64)
+        w2e = np.asarray(w2[e], dtype=np.float64)
+        if len(ti) == 0:
+            out["dw1"][e] = np.zeros((2 * F, x.shape[1]))
+            out["dw2"][e] = np.zeros((w2e.shape[0], F))
+            continue
+        xe = x[ti]
+        D32 = (p32[ti, j][:, None] * dy32[ti]).astype(np.float32)
+        D = D32.astype(np.float64)
+        z = xe @ w1e.T
+        g, u = z[:, :F], z[:, F:]
+        sg = sigmoid(g)
+        a = g * sg * u
+        dA = D @ w2e
+        dZ = np.concatenate([dA * u * sg * (1.0 + g * (1.0 - sg)), dA * g * sg], axis=1)
+        Dq = dequant_token_blocks(*quantize_token_blocks(D32, beta), beta)
+        dZq = dequant_token_blocks(*quantize_token_blocks(dZ.astype(np.float32), beta), beta)
+        out["dw2"][e] = Dq.T @ a
+        out["dw1"][e] = dZq.T @ xe
+    return out

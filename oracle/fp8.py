@@ -9,6 +9,15 @@ largest finite magnitude is 1.75 * 2^8 = 448.
 Block scaling of the weights (reading of the "per-128 block scales" of the
 fp8 workload): weight element (n, c) of an expert is code(n, c) *
 scale[n // 128][c // 128], one fp32 scale per 128 x 128 block.
+
+Token-axis requantization (MegaFlux summary, "Backward", overlapped
+requantization of D_e and dZ_e; reading: the weight-gradient operands, whose
+contraction runs over tokens, are quantized in blocks of beta consecutive
+slots -- one planner block -- times one column): scale = amax / 448 over the
+block's column and code = e4m3(value / scale), every step in fp32 (the
+quantized code is an integer decided by floating point, so the oracle and the
+device both decide it in fp32); an all-zero block column has scale 0 and
+codes 0.
 """
 from __future__ import annotations
 
@@ -37,4 +46,51 @@ def dequant_blocks(codes, scales) -> np.ndarray:
     v = _TABLE[np.asarray(codes, dtype=np.uint8)]
     s = np.asarray(scales, dtype=np.float64)
     s = np.repeat(np.repeat(s, 128, axis=-2), 128, axis=-1)
+    return v * s
+
+
+def encode_e4m3(values) -> np.ndarray:
+    """fp32 values -> e4m3fn codes: round to nearest on the e4m3 grid, ties to
+    even; magnitudes above 448 saturate to 448 (no value reaches NaN)."""
+    v = np.asarray(values, dtype=np.float32).astype(np.float64)
+    sign = np.where(np.signbit(v), 0x80, 0).astype(np.int64)
+    a = np.minimum(np.abs(v), 448.0)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))        # binade; the subnormals share 2^-6's step
+    step = np.power(2.0, e - 3)                              # 3 mantissa bits
+    q = np.rint(a / step).astype(np.int64)                  # half-way cases to even
+    up = q == 16                                             # rounded into the next binade
+    e = np.where(up, e + 1, e)
+    q = np.where(up, 8, q)
+    normal = q >= 8
+    code = np.where(normal, ((e.astype(np.int64) + 7) << 3) | (q - 8), q)
+    return (sign | code).astype(np.uint8)
+
+
+def quantize_token_blocks(values, block_rows: int):
+    """values fp32 [rows, cols] -> (codes uint8 [rows, cols], scales fp32
+    [ceil(rows / block_rows), cols]): one scale per block of block_rows
+    consecutive rows and one column."""
+    v = np.asarray(values, dtype=np.float32)
+    rows, cols = v.shape
+    nblk = (rows + block_rows - 1) // block_rows
+    codes = np.zeros((rows, cols), dtype=np.uint8)
+    scales = np.zeros((nblk, cols), dtype=np.float32)
+    for b in range(nblk):
+        blk = v[b * block_rows:(b + 1) * block_rows]
+        amax = np.max(np.abs(blk), axis=0).astype(np.float32)
+        sc = (amax / np.float32(448.0)).astype(np.float32)
+        scales[b] = sc
+        safe = np.where(sc > 0, sc, np.float32(1.0)).astype(np.float32)
+        q = np.where(sc > 0, (blk / safe).astype(np.float32), np.float32(0.0))
+        codes[b * block_rows:(b + 1) * block_rows] = encode_e4m3(q)
+    return codes, scales
+
+
+def dequant_token_blocks(codes, scales, block_rows: int) -> np.ndarray:
+    """Inverse of quantize_token_blocks up to the rounding: fp64 values."""
+    global _TABLE
+    if _TABLE is None:
+        _TABLE = decode_e4m3(np.arange(256, dtype=np.uint8))
+    v = _TABLE[np.asarray(codes, dtype=np.uint8)]
+    s = np.repeat(np.asarray(scales, dtype=np.float64), block_rows, axis=0)[: v.shape[0]]
     return v * s

@@ -18,6 +18,8 @@ import numpy as np
 import pytest
 
 from oracle import ffn
+from oracle import ffn as offn
+from oracle.fp8 import decode_e4m3
 
 
 def _rand_case(rng, T=6, k=2, E=3, d=5, F=3, neg=False):
@@ -159,3 +161,57 @@ def test_backward_subsets_and_linearity():
     np.testing.assert_allclose(twice["dx"], 2 * full["dx"], rtol=1e-13)
     zero = ffn.backward(x, w1, w2, ids, gates, 0 * dy)
     assert all(np.abs(v).max() == 0 for v in zero["dw2"].values())
+
+
+# ---- fp8 backward with token-axis requantization ----------------------------
+
+def _fp8_case(seed, T=96, k=2, E=3, d=16, F=8):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d))
+    w1 = rng.standard_normal((E, 2 * F, d)) / np.sqrt(d)
+    w2 = rng.standard_normal((E, d, F)) / np.sqrt(F)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    g = rng.random((T, k)).astype(np.float32)
+    dy = rng.standard_normal((T, d)).astype(np.float32).astype(np.float64)
+    return x, w1, w2, ids, g, dy
+
+
+def test_fp8_backward_dx_is_the_exact_one():
+    x, w1, w2, ids, g, dy = _fp8_case(1)
+    a = offn.backward(x, w1, w2, ids, g, dy)
+    b = offn.backward_fp8(x, w1, w2, ids, g, dy, beta=16)
+    np.testing.assert_array_equal(a["dx"], b["dx"])
+
+
+def test_fp8_backward_dw_within_the_e4m3_bound():
+    x, w1, w2, ids, g, dy = _fp8_case(2)
+    a = offn.backward(x, w1, w2, ids, g, dy)
+    b = offn.backward_fp8(x, w1, w2, ids, g, dy, beta=16)
+    for key in ("dw1", "dw2"):
+        A = np.stack([a[key][e] for e in range(3)])
+        Bq = np.stack([b[key][e] for e in range(3)])
+        err = np.linalg.norm(Bq - A) / np.linalg.norm(A)
+        assert 1e-4 < err < 2.0 ** -4, (key, err)        # quantized, within half an e4m3 step
+
+
+def test_fp8_backward_exact_when_D_is_representable():
+    # gates 1 and dy drawn from e4m3 codes times 2^-3 with each block column's
+    # largest magnitude 448 * 2^-3: every D value is code * scale exactly, so
+    # dW2 equals the unquantized one
+    rng = np.random.default_rng(5)
+    T, k, E, d, F, beta = 64, 1, 2, 8, 4, 16
+    x = rng.standard_normal((T, d))
+    w1 = rng.standard_normal((E, 2 * F, d)) / 3
+    w2 = rng.standard_normal((E, d, F)) / 3
+    ids = (np.arange(T) % E)[:, None]
+    g = np.ones((T, k), dtype=np.float32)
+    grid = decode_e4m3(np.arange(0, 0x7F, dtype=np.uint8))
+    dy = rng.choice(np.concatenate([grid, -grid]), size=(T, d)) * 2.0 ** -3
+    for e in range(E):                 # every beta-row block of each expert gets a 448
+        rows = np.nonzero(ids[:, 0] == e)[0]
+        for b0 in range(0, len(rows), beta):
+            dy[rows[b0], :] = 448 * 2.0 ** -3
+    a = offn.backward(x, w1, w2, ids, g, dy)
+    b = offn.backward_fp8(x, w1, w2, ids, g, dy, beta=beta)
+    for e in range(E):
+        np.testing.assert_allclose(b["dw2"][e], a["dw2"][e], rtol=1e-12, atol=1e-12)

@@ -27,3 +27,50 @@ def test_block_scales_layout():
         for n in (0, 127, 128, 255):
             for c in (0, 5, 128, 300, 383):
                 assert got[e, n, c] == vals[e, n, c] * np.float64(scales[e, n // 128, c // 128])
+
+
+# ---- token-axis requantization (encoder and block quantizer) ----------------
+
+def test_encode_matches_torch_cast():
+    from oracle.fp8 import encode_e4m3
+    rng = np.random.default_rng(3)
+    v = (rng.standard_normal(100000) * 10.0 ** rng.uniform(-4, 2.6, 100000)).astype(np.float32)
+    v = np.clip(v, -448, 448)
+    # half-way points between neighbouring codes go to the even mantissa
+    grid = decode_e4m3(np.arange(0, 0x7F, dtype=np.uint8))
+    mids = ((grid[1:] + grid[:-1]) / 2).astype(np.float32)
+    v = np.concatenate([v, mids, -mids])
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(encode_e4m3(v), ref)
+
+
+def test_encode_round_trip_and_saturation():
+    from oracle.fp8 import encode_e4m3
+    codes = np.arange(256, dtype=np.uint8)
+    vals = decode_e4m3(codes)
+    ok = ~np.isnan(vals)
+    np.testing.assert_array_equal(encode_e4m3(vals[ok].astype(np.float32)), codes[ok])
+    assert encode_e4m3(np.float32(1000.0)) == 0x7E and encode_e4m3(np.float32(-449.0)) == 0xFE
+
+
+def test_quantize_token_blocks():
+    from oracle.fp8 import dequant_token_blocks, quantize_token_blocks
+    rng = np.random.default_rng(4)
+    v = (rng.standard_normal((300, 40)) * 3).astype(np.float32)
+    v[128:256, 7] = 0.0                               # an all-zero block column
+    codes, scales = quantize_token_blocks(v, 128)
+    assert scales.shape == (3, 40)
+    for b in range(3):
+        blk = v[b * 128:(b + 1) * 128]
+        amax = np.abs(blk).max(axis=0)
+        np.testing.assert_array_equal(scales[b], (amax / np.float32(448)).astype(np.float32))
+        # the largest magnitude of a block column lands on the top code
+        for c in range(40):
+            if amax[c] > 0:
+                i = int(np.argmax(np.abs(blk[:, c])))
+                assert codes[b * 128 + i, c] & 0x7F == 0x7E
+    assert scales[1, 7] == 0 and not codes[128:256, 7].any()
+    back = dequant_token_blocks(codes, scales, 128)
+    # within half a step of e4m3: 2^-4 relative, or 2^-10 of the scale below 2^-6
+    bound = np.maximum(np.abs(v) * 2.0 ** -4, np.repeat(scales, 128, axis=0)[:300] * 2.0 ** -10)
+    assert np.all(np.abs(back - v) <= bound * (1 + 1e-6))
