@@ -71,7 +71,7 @@ typedef enum { MOE_PLAN_FWD = 0, MOE_PLAN_BWD = 1, MOE_PLAN_QUOTA = 2 } moe_plan
  *   w2 [E][d][d_ff].
  * act_dtype (MOE_F32 or MOE_BF16) is the dtype of x, y, dy, dx and z_save.
  * w_dtype is MOE_F32 (with act MOE_F32), MOE_BF16 (with act MOE_BF16) or
- * MOE_FP8_E4M3 (OCP e4m3fn codes, act MOE_BF16, forward only); fp8 weights
+ * MOE_FP8_E4M3 (OCP e4m3fn codes, act MOE_BF16; forward and backward); fp8 weights
  * carry one fp32 scale per 128x128 block:
  *   w1_scale [E][2*d_ff/128][d/128], w2_scale [E][d/128][d_ff/128].
  * Requires d % 128 == 0 and d_ff % 64 == 0 (fp8: d_ff % 128 == 0). */
@@ -230,7 +230,13 @@ int moe_forward(const moe_layer* L, const void* x, const float* gates,
  *   stage_events (host, nullable): 7 events: start / after scheduling /
  *     after dA / after dX / after dx combine / after weight gradients /
  *     after replica reduction.
- * MOE_ERR_UNSUPPORTED for fp8 weights. */
+ * fp8 weights (MegaFlux summary, "Backward": overlapped token-axis
+ * requantization of D_e and dZ_e): dA, dZ and dx use D and the weights as
+ * the forward does (e4m3 codes times their 128 x 128 block scales); the
+ * weight gradients take D and dZ requantized to e4m3 along the tokens, in
+ * blocks of beta consecutive slots times one column (moe_quantize_token_blocks),
+ * with x and A = SiLU(G) U unquantized: dw2 = Dq A^T, dw1 = dZq x^T.  The
+ * codes and scales live in `ws` (moe_workspace_size counts them). */
 int moe_backward(const moe_layer* L, const void* x, const float* gates, const void* dy,
                  const void* z_save, const int32_t* topk_ids, int T, int k, int beta,
                  int P, int s, const int32_t* counts, const int32_t* block_offsets,
@@ -238,6 +244,27 @@ int moe_backward(const moe_layer* L, const void* x, const float* gates, const vo
                  const int32_t* owner, const int32_t* block_worker, void* dx, float* dw1,
                  float* dw2, int32_t* status_dev, void* ws, size_t ws_bytes,
                  void* const* stage_events, void* stream);
+
+/* Token-axis e4m3 requantization (MegaFlux summary, "Backward": D_e and dZ_e
+ * are requantized along the tokens for the weight-gradient products).
+ * Blocks of block_rows consecutive rows times one column: scale = amax / 448
+ * over the block's column, code = e4m3(value / scale) rounded to nearest,
+ * ties to even, magnitudes saturated at 448 (OCP e4m3fn), every step in fp32;
+ * an all-zero block column gets scale 0 and codes 0.  Row r's values:
+ *   row_map == NULL:  src[r * ld + c]
+ *   row_map[r] < 0:   0
+ *   otherwise:        src[(gather ? row_map[r] / row_div : r) * ld + c]
+ *                     * (row_scale ? row_scale[row_map[r]] : 1)
+ * (the backward uses slot_to_row as row_map: with gather, row_div = k and
+ * row_scale = gates it forms D = p * dy per slot; without, it masks padding).
+ *   src bf16, device; codes [rows][cols] uint8; scales
+ *   [ceil(rows / block_rows)][cols] fp32; all device pointers, caller-owned.
+ * Errors: MOE_ERR_ARG for rows < 0, cols < 8 or not a multiple of 8,
+ *   ld < cols or not a multiple of 8, block_rows < 1, row_div < 1, or a null
+ *   src/codes/scales. */
+int moe_quantize_token_blocks(const void* src, int ld, const int32_t* row_map, int gather,
+                              int row_div, const float* row_scale, int rows, int cols,
+                              int block_rows, uint8_t* codes, float* scales, void* stream);
 
 /* Timing helpers so a caller without a HIP binding can time the stages:
  * create / destroy a hipEvent_t, and the milliseconds between two recorded

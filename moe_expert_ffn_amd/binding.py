@@ -22,7 +22,7 @@ DEV_BAD_EXPERT, DEV_BAD_PLAN, DEV_BAD_OWNER = 1, 2, 4
 
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_max_slots", "moe_max_blocks",
            "moe_workspace_size", "moe_route_stats", "moe_plan", "moe_plan_gate",
-           "moe_predict_cost", "moe_forward",
+           "moe_predict_cost", "moe_quantize_token_blocks", "moe_forward",
            "moe_backward",
            "moe_event_create", "moe_event_destroy", "moe_event_record", "moe_event_elapsed_ms",
            "moe_device_info"]
@@ -66,6 +66,8 @@ def load():
     lib.moe_route_stats.argtypes = [_P, _I, _I, _I, _I] + [_P] * 8 + [_P, _SZ, _P]
     lib.moe_plan.restype = _I
     lib.moe_plan.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I] + [_P] * 5 + [_P, _SZ, _P]
+    lib.moe_quantize_token_blocks.restype = _I
+    lib.moe_quantize_token_blocks.argtypes = [_P, _I, _P, _I, _I, _P, _I, _I, _I, _P, _P, _P]
     lib.moe_predict_cost.restype = _I
     lib.moe_predict_cost.argtypes = [_P] * 5 + [_I] * 6 + [_P, _P, _P]
     lib.moe_plan_gate.restype = _I
@@ -182,6 +184,17 @@ def predict_cost(counts, block_offsets, bw_fwd, bw_bwd, owner, beta, P, d, d_ff,
                                    _ptr(owner), counts.numel(), beta, P, d, d_ff, num_workgroups,
                                    _ptr(cost), _ptr(status), _stream()))
     return cost
+
+
+def quantize_token_blocks(src, rows, cols, block_rows, codes, scales, row_map=None, gather=False,
+                          row_div=1, row_scale=None, ld=None):
+    """Token-axis e4m3 codes [rows][cols] and scales [ceil(rows/block_rows)][cols]."""
+    _require_device(src, codes, scales, *[t for t in (row_map, row_scale) if t is not None])
+    _check(load().moe_quantize_token_blocks(
+        _ptr(src), cols if ld is None else ld, _ptr(row_map) if row_map is not None else None,
+        1 if gather else 0, row_div, _ptr(row_scale) if row_scale is not None else None, rows, cols,
+        block_rows, _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales
 
 
 def plan_gate(block_counts, block_offsets, owner, P, rho_milli, out, status):

@@ -31,7 +31,6 @@ int check_layer(const moe_layer* L, bool backward) {
   if (!f32 && !bf && !f8) return L->act_dtype > MOE_BF16 || L->w_dtype > MOE_FP8_E4M3
                                      ? MOE_ERR_ARG : MOE_ERR_UNSUPPORTED;
   if (f8) {
-    if (backward) return MOE_ERR_UNSUPPORTED;
     if (L->d_ff % 128 != 0) return MOE_ERR_UNSUPPORTED;
     if (!L->w1_scale || !L->w2_scale) return MOE_ERR_ARG;
   }
@@ -42,6 +41,7 @@ Sizes make_sizes(const moe_layer* L, int T, int k, int beta, int P, int s) {
   Sizes z{};
   z.T = T; z.k = k; z.E = L->E; z.d = L->d; z.dff = L->d_ff; z.beta = beta; z.P = P; z.s = s;
   z.act_bytes = L->act_dtype == MOE_F32 ? 4 : 2;
+  z.fp8 = L->w_dtype == MOE_FP8_E4M3 ? 1 : 0;
   z.max_slots = moe_max_slots(T, k, L->E, beta);
   z.max_blocks = moe_max_blocks(T, k, L->E, beta);
   z.max_mt = max_tiles(z);
@@ -141,6 +141,16 @@ int moe_plan_gate(const int32_t* block_counts, const int32_t* block_offsets, con
     return MOE_ERR_ARG;
   return launch_plan_gate(block_counts, block_offsets, owner, E, P, rho_milli, q, load,
                           block_worker, plan_info, status_dev, (hipStream_t)stream);
+}
+
+int moe_quantize_token_blocks(const void* src, int ld, const int32_t* row_map, int gather,
+                              int row_div, const float* row_scale, int rows, int cols,
+                              int block_rows, uint8_t* codes, float* scales, void* stream) {
+  if (rows < 0 || cols < 8 || cols % 8 || ld < cols || ld % 8 || block_rows < 1 || row_div < 1)
+    return MOE_ERR_ARG;
+  if (!src || !codes || !scales) return MOE_ERR_ARG;
+  return launch_quant_tok((const uint16_t*)src, ld, row_map, gather ? 1 : 0, row_div, row_scale,
+                          rows, cols, block_rows, codes, scales, (hipStream_t)stream);
 }
 
 int moe_predict_cost(const int32_t* counts, const int32_t* block_offsets,

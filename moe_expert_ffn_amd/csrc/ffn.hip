@@ -195,7 +195,7 @@ struct ExecArgs {
   const float* w2s;
   const int32_t* slot_to_row;
   const int32_t* row_to_slot;
-  int T, k, E, d, dff, P, s;
+  int T, k, E, d, dff, P, s, beta;
   const int4* mt;
   const int32_t* mt_cnt;
   int max_mt;
@@ -215,6 +215,10 @@ struct ExecArgs {
   size_t slots;           // padded slot capacity (rows of bufA, bufO, bufP, z_save)
   const float* sgate;     // per-slot gate (0 for padding slots)
   uint32_t kmagic;        // ceil(2^32 / k): token = umulhi(row, kmagic)
+  uint8_t* dq;            // fp8 backward: D = p * dy per slot, e4m3 [slots][d]
+  float* dqs;             //   its scales [slots / beta][d]
+  uint8_t* zq;            //   dZ, e4m3 [slots][2 d_ff]
+  float* zqs;             //   its scales [slots / beta][2 d_ff]
 };
 
 enum { PH_FC1 = 0, PH_FC2 = 1, PH_DA = 2, PH_DX = 3, PH_DW = 4 };
@@ -423,6 +427,143 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ src,
 // ---- backward: dA -> dZ -------------------------------------------------------
 // dA[slot, n] = p * sum_c dy[t, c] W2[c, n]; W2 is read as a K-major (c) by
 // N-contiguous operand and transposed into LDS.
+// ---- token-axis e4m3 requantization (fp8 backward) ----------------------------
+// MegaFlux summary, "Backward": token-axis requantization of D_e and dZ_e.
+// Blocks of `brows` consecutive rows (slots) times one column: scale =
+// amax / 448, code = e4m3(value / scale) with round to nearest, ties to even,
+// magnitudes saturated at 448; every step in fp32.  Row r's value is
+//   map == nullptr: src[r * ld + c]
+//   map[r] < 0:     0
+//   otherwise:      src[(gather ? map[r] / div : r) * ld + c] * (rscale ? rscale[map[r]] : 1).
+MOE_DEV uint32_t f32_to_e4m3(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fminf(fabsf(v), 448.f);
+  const uint32_t x = __float_as_uint(a);
+  const int ex = (int)(x >> 23) - 127;
+  const uint32_t mant = (x & 0x7FFFFFu) | 0x800000u;         // 1.m with the implicit bit
+  if (ex >= -6) {                                             // normal: keep 3 fraction bits
+    uint32_t q = mant >> 20;
+    const uint32_t rem = mant & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
+    int e = ex;
+    if (q == 16u) { q = 8u; ++e; }
+    return sign | ((uint32_t)(e + 7) << 3) | (q - 8u);
+  }
+  // subnormal: value = q * 2^-9 (q == 8 carries into the smallest normal)
+  const int sh = 20 + (-6 - ex);
+  if (sh > 24) return sign;                                   // below half of 2^-9: rounds to 0
+  uint32_t q = mant >> sh;
+  const uint32_t rem = mant & ((1u << sh) - 1u), half = 1u << (sh - 1);
+  if (rem > half || (rem == half && (q & 1u))) ++q;
+  return sign | q;
+}
+
+__global__ __launch_bounds__(256) void k_quant_tok(const uint16_t* __restrict__ src, int ld,
+                                                   const int32_t* __restrict__ map, int gather, int div,
+                                                   const float* __restrict__ rscale, int rows,
+                                                   int cols, int brows, uint8_t* __restrict__ codes,
+                                                   float* __restrict__ scales) {
+  const int nch = cols / 8, nblk = (rows + brows - 1) / brows;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)nblk * nch) return;
+  const int b = (int)(idx / nch), c0 = (int)(idx % nch) * 8;
+  const int r0 = b * brows, r1 = min(rows, r0 + brows);
+  auto value8 = [&](int r, float* v) {
+    const uint16_t* row;
+    float f = 1.f;
+    if (map) {
+      const int m = map[r];
+      if (m < 0) { for (int i = 0; i < 8; ++i) v[i] = 0.f; return; }
+      row = src + (size_t)(gather ? m / div : r) * ld;
+      if (rscale) f = rscale[m];
+    } else {
+      row = src + (size_t)r * ld;
+    }
+    const uint4 q = *(const uint4*)(row + c0);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16) * f;
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u) * f;
+    }
+  };
+  float amax[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int r = r0; r < r1; ++r) {
+    float v[8];
+    value8(r, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax[i] = fmaxf(amax[i], fabsf(v[i]));
+  }
+  float sc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    sc[i] = amax[i] / 448.f;
+    scales[(size_t)b * cols + c0 + i] = sc[i];
+  }
+  for (int r = r0; r < r1; ++r) {
+    float v[8];
+    value8(r, v);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t cd = sc[i] > 0.f ? f32_to_e4m3(v[i] / sc[i]) : 0u;
+      if (i < 4) lo |= cd << (8 * i); else hi |= cd << (8 * (i - 4));
+    }
+    *(uint2*)(codes + (size_t)r * cols + c0) = make_uint2(lo, hi);
+  }
+}
+
+int launch_quant_tok(const uint16_t* src, int ld, const int32_t* map, int gather, int div,
+                     const float* rscale, int rows, int cols, int brows, uint8_t* codes,
+                     float* scales, hipStream_t st) {
+  const long long n = (long long)((rows + brows - 1) / brows) * (cols / 8);
+  if (n > 0)
+    hipLaunchKernelGGL(k_quant_tok, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src, ld,
+                       map, gather, div, rscale, rows, cols, brows, codes, scales);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// fp8 weight rows read K-major: element (k, n) = code[k * ld + n] * scale[k / 128][n / 128],
+// eight consecutive n widened to bf16 (n0 and every mn are multiples of 8)
+struct SrcRowsMNFp8 {
+  const uint8_t* base;
+  const float* scale;
+  int ld, n0, nlim, sld;
+  MOE_DEV uint4 operator()(int kk, int mn) const {
+    const int n = n0 + mn;
+    if (n >= nlim) return zero4();
+    const uint2 c = *(const uint2*)(base + (size_t)kk * ld + n);
+    const float s = scale[(size_t)(kk >> 7) * sld + (n >> 7)];
+    const uint32_t w[2] = {c.x, c.y};
+    V16 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o.h[i] = f2bf(e4m3_to_f32((w[i >> 2] >> (8 * (i & 3))) & 0xFFu) * s);
+    return o.u;
+  }
+};
+
+// token-axis e4m3 slot rows: element (k, m) = code[(slot0 + k) * ld + m0 + m] *
+// scale[(slot0 + k) / beta][m0 + m], widened to bf16
+struct SrcSlotRowFp8 {
+  const uint8_t* codes;
+  const float* scales;
+  int slot0, nrows, ld, m0, mlim, beta;
+  MOE_DEV uint4 operator()(int kk, int mn) const {
+    const int m = m0 + mn;
+    if (kk >= nrows || m >= mlim) return zero4();
+    const size_t slot = (size_t)slot0 + kk;
+    const uint2 c = *(const uint2*)(codes + slot * ld + m);
+    const float4 s0 = *(const float4*)(scales + (slot / beta) * ld + m);
+    const float4 s1 = *(const float4*)(scales + (slot / beta) * ld + m + 4);
+    const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    const uint32_t w[2] = {c.x, c.y};
+    V16 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o.h[i] = f2bf(e4m3_to_f32((w[i >> 2] >> (8 * (i & 3))) & 0xFFu) * s[i]);
+    return o.u;
+  }
+};
+
 template <typename T> struct SrcRowsMN {       // element (k, n) = base[k * ld + n0 + n]
   const T* base;
   int ld, n0, nlim;
@@ -449,7 +590,7 @@ MOE_DEV void store4(uint16_t* p, const float* v) {
 }
 MOE_DEV void store4(float* p, const float* v) { *(float4*)p = make_float4(v[0], v[1], v[2], v[3]); }
 
-template <typename T, class C>
+template <typename T, class C, bool FP8 = false>
 __global__ __launch_bounds__(C::NT) void k_bwd_da(ExecArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int tslot;
@@ -475,10 +616,18 @@ __global__ __launch_bounds__(C::NT) void k_bwd_da(ExecArgs a) {
     la.init(DY, [&](int row) { return row < nrows ? (a.slot_to_row[slot0 + row] / a.k) * a.d : -1; });
     TransLoad<T, C::BN, C::NT> lb;
     lb.init();
-    SrcRowsMN<T> src{(const T*)a.w2 + (size_t)e * a.d * a.dff, a.dff, nj * C::BN, a.dff};
     f32x16_t acc[C::MB][C::NB];
-    gemm_tile<T, C>(PlainLd<decltype(la)>{la}, TransLd<decltype(lb), SrcRowsMN<T>>{lb, src},
-                    a.d / Elem<T>::BK, smem, acc);
+    if constexpr (FP8) {
+      SrcRowsMNFp8 src{(const uint8_t*)a.w2 + (size_t)e * a.d * a.dff,
+                       a.w2s + (size_t)e * (a.d / 128) * (a.dff / 128), a.dff, nj * C::BN, a.dff,
+                       a.dff / 128};
+      gemm_tile<T, C>(PlainLd<decltype(la)>{la}, TransLd<decltype(lb), SrcRowsMNFp8>{lb, src},
+                      a.d / Elem<T>::BK, smem, acc);
+    } else {
+      SrcRowsMN<T> src{(const T*)a.w2 + (size_t)e * a.d * a.dff, a.dff, nj * C::BN, a.dff};
+      gemm_tile<T, C>(PlainLd<decltype(la)>{la}, TransLd<decltype(lb), SrcRowsMN<T>>{lb, src},
+                      a.d / Elem<T>::BK, smem, acc);
+    }
     // p * dA in fp32 through LDS, 128 rows at a time; the SwiGLU gradient is
     // applied on the way out with 4-wide coalesced reads of the saved [G, U]
     constexpr int PASS = 128, LDD = C::BN + 4;
@@ -511,7 +660,7 @@ __global__ __launch_bounds__(C::NT) void k_bwd_da(ExecArgs a) {
 }
 
 // ---- backward: dX per routed row ----------------------------------------------
-template <typename T, class C>
+template <typename T, class C, bool FP8 = false>
 __global__ __launch_bounds__(C::NT) void k_bwd_dx(ExecArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int tslot;
@@ -532,10 +681,18 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dx(ExecArgs a) {
     la.init(dZ + (size_t)slot0 * 2 * a.dff, [&](int row) { return row < nrows ? row * 2 * a.dff : -1; });
     TransLoad<T, C::BN, C::NT> lb;
     lb.init();
-    SrcRowsMN<T> src{(const T*)a.w1 + (size_t)e * 2 * a.dff * a.d, a.d, nj * C::BN, a.d};
     f32x16_t acc[C::MB][C::NB];
-    gemm_tile<T, C>(PlainLd<decltype(la)>{la}, TransLd<decltype(lb), SrcRowsMN<T>>{lb, src},
-                    2 * a.dff / Elem<T>::BK, smem, acc);
+    if constexpr (FP8) {
+      SrcRowsMNFp8 src{(const uint8_t*)a.w1 + (size_t)e * 2 * a.dff * a.d,
+                       a.w1s + (size_t)e * (2 * a.dff / 128) * (a.d / 128), a.d, nj * C::BN, a.d,
+                       a.d / 128};
+      gemm_tile<T, C>(PlainLd<decltype(la)>{la}, TransLd<decltype(lb), SrcRowsMNFp8>{lb, src},
+                      2 * a.dff / Elem<T>::BK, smem, acc);
+    } else {
+      SrcRowsMN<T> src{(const T*)a.w1 + (size_t)e * 2 * a.dff * a.d, a.d, nj * C::BN, a.d};
+      gemm_tile<T, C>(PlainLd<decltype(la)>{la}, TransLd<decltype(lb), SrcRowsMN<T>>{lb, src},
+                      2 * a.dff / Elem<T>::BK, smem, acc);
+    }
     constexpr int LDO = C::BN + 16 / (int)sizeof(T);
     acc_to_lds<C>(acc, smem, LDO, 0, C::BM, [&](float v, int, int) { return to_act<T>(v); });
     __syncthreads();
@@ -996,7 +1153,7 @@ template <typename T> struct SrcGatedAct {     // element (k, n) = p * SiLU(G) *
     const int n = n0 + mn;
     if (kk >= nrows || n >= dff) return zero4();
     const size_t zb = ((size_t)slot0 + kk) * 2 * dff;
-    const float p = gates[slot_to_row[slot0 + kk]];
+    const float p = gates ? gates[slot_to_row[slot0 + kk]] : 1.f;   // no gates: A itself
     V16 g, u, o;
     g.u = ldg16(z + zb + n);
     u.u = ldg16(z + zb + dff + n);
@@ -1013,7 +1170,7 @@ template <typename T> struct SrcGatedAct {     // element (k, n) = p * SiLU(G) *
   }
 };
 
-template <typename T, class C>
+template <typename T, class C, bool FP8 = false>
 __global__ __launch_bounds__(C::NT) void k_bwd_dw(ExecArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int tslot;
@@ -1043,11 +1200,19 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dw(ExecArgs a) {
     if (loc < n2m * n2n) {
       mi = loc / n2n;
       nj = loc % n2n;
-      SrcGatherRow<T> sa{(const T*)a.dy, a.slot_to_row, slot0, nrows, a.k, a.d, mi * C::BM, a.d};
-      SrcGatedAct<T> sb{(const T*)a.z_save, a.gates, a.slot_to_row, slot0, nrows, a.dff,
-                        nj * C::BN};
-      gemm_tile<T, C>(TransLd<decltype(la), SrcGatherRow<T>>{la, sa},
-                      TransLd<decltype(lb), SrcGatedAct<T>>{lb, sb}, nk, smem, acc);
+      if constexpr (FP8) {   // dW2 = Dq^T A: token-axis e4m3 D, ungated A
+        SrcSlotRowFp8 sa{a.dq, a.dqs, slot0, nrows, a.d, mi * C::BM, a.d, a.beta};
+        SrcGatedAct<T> sb{(const T*)a.z_save, nullptr, a.slot_to_row, slot0, nrows, a.dff,
+                          nj * C::BN};
+        gemm_tile<T, C>(TransLd<decltype(la), SrcSlotRowFp8>{la, sa},
+                        TransLd<decltype(lb), SrcGatedAct<T>>{lb, sb}, nk, smem, acc);
+      } else {
+        SrcGatherRow<T> sa{(const T*)a.dy, a.slot_to_row, slot0, nrows, a.k, a.d, mi * C::BM, a.d};
+        SrcGatedAct<T> sb{(const T*)a.z_save, a.gates, a.slot_to_row, slot0, nrows, a.dff,
+                          nj * C::BN};
+        gemm_tile<T, C>(TransLd<decltype(la), SrcGatherRow<T>>{la, sa},
+                        TransLd<decltype(lb), SrcGatedAct<T>>{lb, sb}, nk, smem, acc);
+      }
       out = (dst < 0 ? a.dw2 + (size_t)e * a.d * a.dff
                      : a.rslots + (size_t)dst * w_elems + (size_t)2 * a.dff * a.d);
       ldo = a.dff;
@@ -1056,10 +1221,16 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dw(ExecArgs a) {
       loc -= n2m * n2n;
       mi = loc / n1n;
       nj = loc % n1n;
-      SrcSlotRow<T> sa{(const T*)a.bufA, slot0, nrows, 2 * a.dff, mi * C::BM, 2 * a.dff};
       SrcGatherRow<T> sb{(const T*)a.x, a.slot_to_row, slot0, nrows, a.k, a.d, nj * C::BN, a.d};
-      gemm_tile<T, C>(TransLd<decltype(la), SrcSlotRow<T>>{la, sa},
-                      TransLd<decltype(lb), SrcGatherRow<T>>{lb, sb}, nk, smem, acc);
+      if constexpr (FP8) {   // dW1 = dZq^T X: token-axis e4m3 dZ
+        SrcSlotRowFp8 sa{a.zq, a.zqs, slot0, nrows, 2 * a.dff, mi * C::BM, 2 * a.dff, a.beta};
+        gemm_tile<T, C>(TransLd<decltype(la), SrcSlotRowFp8>{la, sa},
+                        TransLd<decltype(lb), SrcGatherRow<T>>{lb, sb}, nk, smem, acc);
+      } else {
+        SrcSlotRow<T> sa{(const T*)a.bufA, slot0, nrows, 2 * a.dff, mi * C::BM, 2 * a.dff};
+        gemm_tile<T, C>(TransLd<decltype(la), SrcSlotRow<T>>{la, sa},
+                        TransLd<decltype(lb), SrcGatherRow<T>>{lb, sb}, nk, smem, acc);
+      }
       out = (dst < 0 ? a.dw1 + (size_t)e * 2 * a.dff * a.d : a.rslots + (size_t)dst * w_elems);
       ldo = a.d;
       nlim = a.d;
@@ -1263,6 +1434,14 @@ WsLayout exec_layout(const Sizes& z, bool backward) {
   L.rslots = backward ? take(sizeof(float) * (size_t)z.P * z.s * 3 * z.d * z.dff) : o;
   L.bufP = backward ? take((size_t)z.act_bytes * z.max_slots * z.dff) : o;
   L.sgate = take(sizeof(float) * z.max_slots);
+  L.dq = L.dqs = L.zq = L.zqs = o;
+  if (backward && z.fp8) {
+    const size_t nblk = (z.max_slots + z.beta - 1) / z.beta;
+    L.dq = take(z.max_slots * (size_t)z.d);
+    L.dqs = take(sizeof(float) * nblk * z.d);
+    L.zq = take(z.max_slots * (size_t)2 * z.dff);
+    L.zqs = take(sizeof(float) * nblk * 2 * z.dff);
+  }
   L.total = o;
   return L;
 }
@@ -1339,7 +1518,7 @@ static void launch_sched(const Sizes& z, const int32_t* counts, const int32_t* b
 static ExecArgs make_exec(const Sizes& z, const LayerPtrs& Lp, char* ws, const WsLayout& L) {
   ExecArgs a{};
   a.w1 = Lp.w1; a.w2 = Lp.w2; a.w1s = Lp.w1s; a.w2s = Lp.w2s;
-  a.T = z.T; a.k = z.k; a.E = z.E; a.d = z.d; a.dff = z.dff; a.P = z.P; a.s = z.s;
+  a.T = z.T; a.k = z.k; a.E = z.E; a.d = z.d; a.dff = z.dff; a.P = z.P; a.s = z.s; a.beta = z.beta;
   a.mt = (const int4*)(ws + L.mt);
   a.mt_cnt = (const int32_t*)(ws + L.mt_cnt);
   a.max_mt = (int)z.max_mt;
@@ -1355,6 +1534,12 @@ static ExecArgs make_exec(const Sizes& z, const LayerPtrs& Lp, char* ws, const W
   a.slots = z.max_slots;
   a.sgate = (const float*)(ws + L.sgate);
   a.kmagic = (uint32_t)((((uint64_t)1 << 32) + (uint64_t)z.k - 1) / (uint64_t)z.k);
+  if (z.fp8) {
+    a.dq = (uint8_t*)(ws + L.dq);
+    a.dqs = (float*)(ws + L.dqs);
+    a.zq = (uint8_t*)(ws + L.zq);
+    a.zqs = (float*)(ws + L.zqs);
+  }
   return a;
 }
 
@@ -1461,24 +1646,31 @@ static void run_backward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_
   rec(ev, 6, st);
 }
 
-template <typename T, class C>
+template <typename T, class C, bool FP8 = false>
 static void run_backward(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* dx,
                          float* dw1, float* dw2, void* const* ev, hipStream_t st) {
   a.bufP = nullptr;
   const size_t lds = gemm_lds_bytes<T, C>();
-  static int ga = persistent_grid(k_bwd_da<T, C>, C::NT, lds);
-  static int gx = persistent_grid(k_bwd_dx<T, C>, C::NT, lds);
-  static int gw = persistent_grid(k_bwd_dw<T, C>, C::NT, lds);
-  hipLaunchKernelGGL((k_bwd_da<T, C>), dim3(ga), dim3(C::NT), lds, st, a);
+  static int ga = persistent_grid(k_bwd_da<T, C, FP8>, C::NT, lds);
+  static int gx = persistent_grid(k_bwd_dx<T, C, FP8>, C::NT, lds);
+  static int gw = persistent_grid(k_bwd_dw<T, C, FP8>, C::NT, lds);
+  const int rows = (int)z.max_slots;
+  if constexpr (FP8)   // D = p * dy per slot, e4m3 along tokens, for dW2
+    launch_quant_tok((const uint16_t*)a.dy, z.d, a.slot_to_row, 1, z.k, a.gates, rows, z.d, z.beta,
+                     a.dq, a.dqs, st);
+  hipLaunchKernelGGL((k_bwd_da<T, C, FP8>), dim3(ga), dim3(C::NT), lds, st, a);
+  if constexpr (FP8)   // dZ per slot (padding slots read as zero), for dW1
+    launch_quant_tok((const uint16_t*)a.bufA, 2 * z.dff, a.slot_to_row, 0, 1, nullptr, rows,
+                     2 * z.dff, z.beta, a.zq, a.zqs, st);
   rec(ev, 2, st);
-  hipLaunchKernelGGL((k_bwd_dx<T, C>), dim3(gx), dim3(C::NT), lds, st, a);
+  hipLaunchKernelGGL((k_bwd_dx<T, C, FP8>), dim3(gx), dim3(C::NT), lds, st, a);
   rec(ev, 3, st);
   const long long nth = (long long)z.T * (z.d / Elem<T>::VE);
   if (nth > 0)
     hipLaunchKernelGGL(k_combine<T>, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, st,
                        (const T*)a.bufO, row_to_slot, z.T, z.k, z.d, (T*)dx);
   rec(ev, 4, st);
-  hipLaunchKernelGGL((k_bwd_dw<T, C>), dim3(gw), dim3(C::NT), lds, st, a);
+  hipLaunchKernelGGL((k_bwd_dw<T, C, FP8>), dim3(gw), dim3(C::NT), lds, st, a);
   rec(ev, 5, st);
   hipLaunchKernelGGL(k_bwd_reduce, dim3(num_cus() * 4), dim3(256), 0, st, a.rep_slot,
                      a.owner_has, (const float*)a.rslots, z.E, z.P, z.d, z.dff, dw1, dw2);
@@ -1500,7 +1692,10 @@ int launch_backward(const Sizes& z, const LayerPtrs& Lp, const void* x, const fl
   a.z_save = const_cast<void*>(z_save);
   a.dy = dy; a.dw1 = dw1; a.dw2 = dw2;
   if (Lp.act_dtype == MOE_F32) run_backward<float, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
-  else if (use_stream(z)) run_backward_stream(z, a, row_to_slot, dx, dw1, dw2, ev, st);
+  else if (Lp.w_dtype == MOE_FP8_E4M3) {
+    if (use_big_tiles(z)) run_backward<uint16_t, BigCfg, true>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
+    else run_backward<uint16_t, SmallCfg, true>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
+  } else if (use_stream(z)) run_backward_stream(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else if (use_big_tiles(z)) run_backward<uint16_t, BigCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else run_backward<uint16_t, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;

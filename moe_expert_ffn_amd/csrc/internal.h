@@ -20,11 +20,14 @@ inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 struct Sizes {
   int T, k, E, d, dff, beta, P, s;
   int act_bytes;
+  int fp8;            // e4m3 weights: the backward requantizes D and dZ
   size_t max_slots, max_blocks, max_mt;
 };
 
 struct WsLayout {
-  size_t ctr, mt_cnt, mt, seg_cnt, seg, rep_slot, owner_has, bufA, bufO, rslots, bufP, sgate, total;
+  size_t ctr, mt_cnt, mt, seg_cnt, seg, rep_slot, owner_has, bufA, bufO, rslots, bufP, sgate;
+  size_t dq, dqs, zq, zqs;   // fp8 backward: token-axis e4m3 codes and scales of D and dZ
+  size_t total;
 };
 
 WsLayout exec_layout(const Sizes& z, bool backward);
@@ -39,6 +42,9 @@ int launch_route_stats(const int32_t* ids, int T, int k, int E, int beta, int32_
 int launch_plan(const int32_t* bcnt, const int32_t* boff, const int32_t* owner, int E, int P,
                 int s, int mode, int lam, int32_t* q, int32_t* load, int32_t* bw,
                 int32_t* info, int32_t* status, hipStream_t st);
+int launch_quant_tok(const uint16_t* src, int ld, const int32_t* map, int gather, int div,
+                     const float* rscale, int rows, int cols, int brows, uint8_t* codes,
+                     float* scales, hipStream_t st);
 int launch_predict_cost(const int32_t* counts, const int32_t* boff, const int32_t* bw_f,
                         const int32_t* bw_b, const int32_t* owner, int E, int beta, int P, int d,
                         int dff, int G, long long* cost, int32_t* status, hipStream_t st);

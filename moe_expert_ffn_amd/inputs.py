@@ -64,6 +64,10 @@ WORKLOADS = {
     # DeepSeek-V3 one-GPU EP share: 32 of 256 experts, e4m3 weights
     "dsv3_fp8": Workload("dsv3_fp8", "bf16", "fp8", T=0, k=8, E=32, d=7168, d_ff=2048,
                          beta=128, P=8, s=4, kappas=(1, 4, 8), rows=16384, cfg_id=4),
+    # the same DeepSeek-V3 share, forward + backward (fp8 backward with token-axis requantization)
+    "dsv3_fp8_fwdbwd": Workload("dsv3_fp8_fwdbwd", "bf16", "fp8", T=0, k=8, E=32, d=7168,
+                                d_ff=2048, beta=128, P=8, s=4, kappas=(1, 4, 8), rows=16384,
+                                backward=True, cfg_id=4),
     # Qwen3-shaped forward + backward
     "qwen3_bf16_fwdbwd": Workload("qwen3_bf16_fwdbwd", "bf16", "bf16", T=8192, k=8, E=128,
                                   d=2048, d_ff=768, beta=128, P=8, s=4, kappas=(1, 4, 8),

@@ -93,8 +93,24 @@ def test_host_validation_errors():
     assert lib.moe_forward(ctypes.byref(mixed), P, P, P, 4, 2, 16, 4, *([P] * 8), P, 1 << 30,
                            None, None) == B.MOE_ERR_UNSUPPORTED
     fp8 = B.Layer(8, 128, 128, B.MOE_BF16, B.MOE_FP8_E4M3, 16, 32, 64, 64)
+    # fp8 weights have a backward (token-axis requantization): the call gets past
+    # the layer checks and stops at a workspace too small for the e4m3 buffers
     assert lib.moe_backward(ctypes.byref(fp8), P, P, P, P, P, 4, 2, 16, 4, 1, *([P] * 10), P,
+                            16, None, None) == B.MOE_ERR_WORKSPACE
+    nofp8 = B.Layer(8, 128, 192, B.MOE_BF16, B.MOE_FP8_E4M3, 16, 32, 64, 64)   # d_ff % 128
+    assert lib.moe_backward(ctypes.byref(nofp8), P, P, P, P, P, 4, 2, 16, 4, 1, *([P] * 10), P,
                             1 << 30, None, None) == B.MOE_ERR_UNSUPPORTED
+    # token-axis quantization: shapes and pointers are checked on the host
+    # (src, ld, row_map, gather, row_div, row_scale, rows, cols, block_rows, codes, scales, stream)
+    q = lib.moe_quantize_token_blocks
+    assert q(P, 16, None, 0, 1, None, 4, 12, 128, P, P, None) == B.MOE_ERR_ARG     # cols % 8
+    assert q(P, 8, None, 0, 1, None, 4, 16, 128, P, P, None) == B.MOE_ERR_ARG      # ld < cols
+    assert q(P, 20, None, 0, 1, None, 4, 16, 128, P, P, None) == B.MOE_ERR_ARG     # ld % 8
+    assert q(P, 16, None, 0, 1, None, -1, 16, 128, P, P, None) == B.MOE_ERR_ARG    # rows
+    assert q(P, 16, None, 0, 1, None, 4, 16, 0, P, P, None) == B.MOE_ERR_ARG       # block rows
+    assert q(P, 16, None, 0, 0, None, 4, 16, 128, P, P, None) == B.MOE_ERR_ARG     # row_div
+    assert q(None, 16, None, 0, 1, None, 4, 16, 128, P, P, None) == B.MOE_ERR_ARG  # src
+    assert q(P, 16, None, 0, 1, None, 4, 16, 128, None, P, None) == B.MOE_ERR_ARG  # codes
     ok = _layer()
     assert lib.moe_forward(ctypes.byref(ok), P, P, P, 4, 2, 16, 4, *([P] * 8), P, 16, None,
                            None) == B.MOE_ERR_WORKSPACE

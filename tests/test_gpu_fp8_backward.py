@@ -1,0 +1,190 @@
+"""GPU parity of the fp8 backward (MegaFlux summary, "Backward": token-axis
+requantization of D_e and dZ_e for the weight gradients).
+
+* moe_quantize_token_blocks is bit-exact with oracle.fp8.quantize_token_blocks
+  (codes and scales), for plain rows, masked rows and gathered rows scaled by
+  the gates, with ragged last blocks and all-zero block columns.
+* moe_backward on fp8 weights matches oracle.ffn.backward_fp8 within rel-L2
+  6e-2 (dx, dW1, dW2), and its weight gradients sit closer to the
+  requantized oracle than to the unquantized one (dW2, whose quantized D the
+  device forms exactly as the oracle does, at least twice as close), which
+  shows the requantization is the one the oracle defines.
+"""
+import numpy as np
+import pytest
+import torch
+
+from moe_expert_ffn_amd import binding as B
+from moe_expert_ffn_amd.inputs import WORKLOADS, Workload
+from oracle import ffn as offn
+from oracle.fp8 import quantize_token_blocks as oq
+from tests.conftest import rel_l2
+from tests.gpu_util import Case, say
+
+pytestmark = pytest.mark.gpu
+
+TOL_FP8 = 6e-2
+
+SMALL = {
+    # 256 x 256 persistent tiles, replicated experts, ragged blocks
+    "fp8_stream": Workload("fp8_stream", "bf16", "fp8", T=300, k=4, E=8, d=256, d_ff=256,
+                           beta=128, P=4, s=2, kappas=(0,), cfg_id=31),
+    # d_ff a multiple of 128 but not of 256 (the smaller tile configuration), beta 32
+    "fp8_b32": Workload("fp8_b32", "bf16", "fp8", T=200, k=3, E=12, d=384, d_ff=128,
+                        beta=32, P=8, s=3, kappas=(0,), cfg_id=32),
+}
+
+
+def _bf16(rng, shape, col_scale=None):
+    v = rng.standard_normal(shape).astype(np.float32)
+    if col_scale is not None:
+        v *= col_scale[None, :]
+    return torch.from_numpy(v).to(torch.bfloat16)
+
+
+def _quant_dev(src, rows, cols, brows, ld=None, row_map=None, gather=False, row_div=1,
+               row_scale=None):
+    dev = "cuda"
+    nblk = (rows + brows - 1) // brows
+    codes = torch.full((max(rows, 1), cols), 0xA5, dtype=torch.uint8, device=dev)
+    scales = torch.full((max(nblk, 1), cols), -1.0, dtype=torch.float32, device=dev)
+    B.quantize_token_blocks(src.to(dev), rows, cols, brows, codes, scales,
+                            row_map=None if row_map is None else torch.from_numpy(row_map).to(dev),
+                            gather=gather, row_div=row_div,
+                            row_scale=None if row_scale is None else torch.from_numpy(row_scale).to(dev),
+                            ld=ld)
+    torch.cuda.synchronize()
+    return codes[:rows].cpu().numpy(), scales[:nblk].cpu().numpy()
+
+
+def _check_exact(codes, scales, values, brows):
+    ec, es = oq(values, brows)
+    assert np.array_equal(scales.view(np.uint32), es.view(np.uint32)), "scales differ"
+    bad = np.argwhere(codes != ec)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:4].tolist()}"
+
+
+@pytest.mark.parametrize("rows,cols,brows,ld", [(300, 136, 128, 136), (300, 136, 128, 144),
+                                                (64, 8, 1, 8), (77, 256, 32, 264),
+                                                (129, 64, 256, 64)])
+def test_quantize_plain(rows, cols, brows, ld):
+    say(f"[quant-plain] rows={rows} cols={cols} brows={brows} ld={ld}")
+    rng = np.random.default_rng(rows * 7 + cols)
+    # columns spread over many binades; one all-zero column; a tiny-magnitude column
+    col_scale = np.exp2(rng.integers(-12, 12, size=ld)).astype(np.float32)
+    col_scale[3 % cols] = 0.0
+    col_scale[5 % cols] = 2.0 ** -30
+    src = _bf16(rng, (rows, ld), col_scale)
+    codes, scales = _quant_dev(src, rows, cols, brows, ld=ld)
+    _check_exact(codes, scales, src.float().numpy()[:, :cols], brows)
+
+
+@pytest.mark.parametrize("rows,brows", [(0, 128), (1, 128), (513, 128), (200, 32)])
+def test_quantize_gather_scaled(rows, brows):
+    say(f"[quant-gather] rows={rows} brows={brows}")
+    rng = np.random.default_rng(1000 + rows)
+    T, k, cols = 97, 4, 192
+    dy = _bf16(rng, (T, cols))
+    gates = rng.random(T * k).astype(np.float32)
+    row_map = rng.integers(0, T * k, size=rows).astype(np.int32)
+    row_map[rng.random(rows) < 0.2] = -1            # padding slots
+    codes, scales = _quant_dev(dy, rows, cols, brows, row_map=row_map, gather=True, row_div=k,
+                               row_scale=gates)
+    dy32 = dy.float().numpy()
+    vals = np.zeros((rows, cols), dtype=np.float32)
+    for r, m in enumerate(row_map):
+        if m >= 0:
+            vals[r] = gates[m] * dy32[m // k]           # fp32 product, as the device forms p * dy
+    _check_exact(codes, scales, vals, brows)
+
+
+def test_quantize_masked_rows():
+    say("[quant-mask]")
+    rng = np.random.default_rng(5)
+    rows, cols, brows = 390, 128, 128
+    src = _bf16(rng, (rows, cols))
+    row_map = np.arange(rows, dtype=np.int32)
+    row_map[rng.random(rows) < 0.3] = -1
+    row_map[128:256] = -1                              # one whole block masked: scales 0, codes 0
+    codes, scales = _quant_dev(src, rows, cols, brows, row_map=row_map)
+    vals = np.where((row_map >= 0)[:, None], src.float().numpy(), 0.0).astype(np.float32)
+    _check_exact(codes, scales, vals, brows)
+    assert not scales[1].any() and not codes[128:256].any()
+
+
+def _run(c, s=None):
+    r = c.runner
+    r.status.zero_()
+    r.step(c.x, c.gates, c.ids, dy=c.dy, s=s)
+    torch.cuda.synchronize()
+    return r.dx.clone(), r.dw1.clone(), r.dw2.clone()
+
+
+def _errs(dx, dw1, dw2, o, tokens=None, experts=None):
+    ex = range(dw1.shape[0]) if experts is None else experts
+    dxs = dx if tokens is None else dx[tokens]
+    return (rel_l2(dxs.double().cpu().numpy(), o["dx"]),
+            rel_l2(dw1[list(ex)].double().cpu().numpy(), np.stack([o["dw1"][e] for e in ex])),
+            rel_l2(dw2[list(ex)].double().cpu().numpy(), np.stack([o["dw2"][e] for e in ex])))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fp8_backward_full_parity(name):
+    w = SMALL[name]
+    say(f"[fp8-bwd] {name}")
+    c = Case(w, 0, backward=True)
+    dx, dw1, dw2 = _run(c)
+    assert c.status() == 0
+    say(f"  bwd plan_info={c.runner.plan_b['plan_info'].cpu().numpy().tolist()}")
+    x, w1, w2, ids, gates = c.oracle_inputs()
+    dy = c.dy.double().cpu().numpy()
+    o8 = offn.backward_fp8(x, w1, w2, ids, gates, dy, w.beta)
+    o = offn.backward(x, w1, w2, ids, gates, dy)
+    e8 = _errs(dx, dw1, dw2, o8)
+    e0 = _errs(dx, dw1, dw2, o)
+    say(f"  vs requantized oracle dx={e8[0]:.3e} dw1={e8[1]:.3e} dw2={e8[2]:.3e}")
+    say(f"  vs unquantized oracle dx={e0[0]:.3e} dw1={e0[1]:.3e} dw2={e0[2]:.3e}")
+    assert max(e8) <= TOL_FP8
+    # the weight gradients carry the requantization the oracle defines.  D is
+    # formed in fp32 exactly as the oracle forms it, so Dq's codes agree and dW2
+    # sits far closer to the requantized oracle; dZ comes from bf16-staged
+    # weights and is kept in bf16, so a block column's amax -- and with it the
+    # whole e4m3 grid of that column -- moves slightly and some codes land one
+    # step apart: dW1 is only required to be the closer of the two
+    assert e8[2] < 0.5 * e0[2]
+    assert e8[1] < e0[1]
+
+
+def test_fp8_backward_plan_invariance():
+    w = SMALL["fp8_stream"]
+    say("[fp8-bwd-invariance]")
+    c = Case(w, 0, backward=True)
+    dx_p, dw1_p, dw2_p = _run(c)
+    dx_f, dw1_f, dw2_f = _run(c, s=0)
+    assert torch.equal(dx_p, dx_f)
+    assert rel_l2(dw1_p.double().cpu().numpy(), dw1_f.double().cpu().numpy()) < 1e-6
+    assert rel_l2(dw2_p.double().cpu().numpy(), dw2_f.double().cpu().numpy()) < 1e-6
+
+
+@pytest.mark.parametrize("kappa", [1, 8])
+def test_fp8_backward_full_size_sampled(kappa):
+    w = WORKLOADS["dsv3_fp8_fwdbwd"]
+    say(f"[fp8-bwd-full] kappa={kappa}")
+    c = Case(w, kappa, backward=True)
+    dx, dw1, dw2 = _run(c)
+    assert c.status() == 0
+    q = c.runner.plan_b["q"].cpu().numpy()
+    say(f"  bwd plan_info={c.runner.plan_b['plan_info'].cpu().numpy().tolist()}")
+    counts = np.bincount(c.ids_np[c.ids_np >= 0], minlength=w.E)
+    hot = int(np.argmax(counts))
+    replicated = [e for e in range(w.E) if (q[e] > 0).sum() > 1 and e != hot]
+    experts = sorted({hot, *(replicated[:1])})
+    rng = np.random.default_rng(kappa)
+    tok = np.sort(rng.choice(c.T, size=16, replace=False))
+    x, w1, w2, ids, gates = c.oracle_inputs()
+    o = offn.backward_fp8(x, w1, w2, ids, gates, c.dy.double().cpu().numpy(), w.beta,
+                          tokens=tok, experts=experts)
+    e = _errs(dx, dw1, dw2, o, tokens=tok, experts=experts)
+    say(f"  experts={experts} rows={counts[experts].tolist()} dx={e[0]:.3e} dw1={e[1]:.3e} "
+        f"dw2={e[2]:.3e}")
+    assert max(e) <= TOL_FP8
