@@ -900,21 +900,36 @@ struct MnFixed {
 };
 using MnFixedOp = Mn64Operand<MnW, MnFixed>;
 
+// e4m3 weight rows for the wide tile (the stream widens them to bf16)
+using RowF8 = Row64Fp8<256, kWNW>;
+
 // FC1 + SwiGLU.  N tile nj covers A columns [128 nj, 128 nj + 128): weight
 // rows alternate 32 G rows and the matching 32 U rows, so block j = 0 of a
-// wave is G and block j = 1 is U of the same 32 columns.
-struct SrcFc1 : MSrcBase {
+// wave is G and block j = 1 is U of the same 32 columns.  With e4m3 weights
+// the G rows of tile nj lie in scale block nj and the U rows in d_ff/128 + nj.
+template <bool FP8> struct SrcFc1T : MSrcBase {
   using Item = MItem;
+  using OB = typename std::conditional<FP8, RowF8, RowW>::type;
   MOE_DEV void fill(const Item& it, int slot) const { fill_rows(it, slot); }
   MOE_DEV RowW opA(const Item& it, int slot) const { return gathered(it, slot, a.x, a.d); }
-  MOE_DEV RowW opB(const Item& it, int) const {
-    RowW w;
+  MOE_DEV OB opB(const Item& it, int) const {
+    OB w;
     const int dff = a.dff, nj = it.nj;
-    w.init((const uint16_t*)a.w1 + (size_t)it.e * 2 * dff * a.d, (uint32_t)((size_t)4 * dff * a.d),
-           [&](int rho) {
-             const int q = rho >> 5;
-             return ((q & 1) * dff + nj * (WC::BN / 2) + (q >> 1) * 32 + (rho & 31)) * a.d;
-           });
+    auto row = [&](int rho) {
+      const int q = rho >> 5;
+      return ((q & 1) * dff + nj * (WC::BN / 2) + (q >> 1) * 32 + (rho & 31)) * a.d;
+    };
+    if constexpr (FP8) {
+      w.init((const uint8_t*)a.w1 + (size_t)it.e * 2 * dff * a.d, (uint32_t)((size_t)2 * dff * a.d),
+             row);
+      const int kb = a.d / 128;
+      const MOE_CONST float* sc = (const MOE_CONST float*)a.w1s + (size_t)it.e * (2 * dff / 128) * kb;
+      w.sp[0] = sc + (size_t)nj * kb;
+      w.sp[1] = sc + (size_t)(dff / 128 + nj) * kb;
+    } else {
+      w.init((const uint16_t*)a.w1 + (size_t)it.e * 2 * dff * a.d, (uint32_t)((size_t)4 * dff * a.d),
+             row);
+    }
     return w;
   }
   MOE_DEV int steps(const Item&) const { return a.d / kWideBK; }
@@ -955,16 +970,26 @@ struct SrcFc1 : MSrcBase {
   }
 };
 
-// FC2 with the gate: O[slot] = p * A W2^T.
-struct SrcFc2 : MSrcBase {
+// FC2 with the gate: O[slot] = p * A W2^T.  With e4m3 weights a wave's 64
+// rows nj * 256 + 64 wn .. +63 lie in scale block 2 nj + wn / 2.
+template <bool FP8> struct SrcFc2T : MSrcBase {
   using Item = MItem;
+  using OB = typename std::conditional<FP8, RowF8, RowW>::type;
   MOE_DEV void fill(const Item& it, int slot) const { fill_gates(it, slot); }
   MOE_DEV RowW opA(const Item& it, int) const { return slotrows(it, a.bufA, a.dff); }
-  MOE_DEV RowW opB(const Item& it, int) const {
-    RowW w;
+  MOE_DEV OB opB(const Item& it, int) const {
+    OB w;
     const int nj = it.nj, dff = a.dff;
-    w.init((const uint16_t*)a.w2 + (size_t)it.e * a.d * dff, (uint32_t)((size_t)2 * a.d * dff),
-           [&](int rho) { return (nj * WC::BN + rho) * dff; });
+    auto row = [&](int rho) { return (nj * WC::BN + rho) * dff; };
+    if constexpr (FP8) {
+      w.init((const uint8_t*)a.w2 + (size_t)it.e * a.d * dff, (uint32_t)((size_t)a.d * dff), row);
+      const int kb = dff / 128;
+      const int wn = wave_id() % WC::WAVES_N;
+      w.sp[0] = w.sp[1] = (const MOE_CONST float*)a.w2s + (size_t)it.e * (a.d / 128) * kb +
+                          (size_t)(2 * nj + wn / 2) * kb;
+    } else {
+      w.init((const uint16_t*)a.w2 + (size_t)it.e * a.d * dff, (uint32_t)((size_t)2 * a.d * dff), row);
+    }
     return w;
   }
   MOE_DEV int steps(const Item&) const { return a.dff / kWideBK; }
@@ -1589,12 +1614,14 @@ static void launch_slot_gate(const Sizes& z, const ExecArgs& a, hipStream_t st) 
                        (float*)a.sgate);
 }
 
+template <bool FP8>
 static void run_forward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* y,
                                void* const* ev, hipStream_t st) {
   launch_slot_gate(z, a, st);
-  launch_stream<SrcFc1, WC, RowW, RowW>(a, z.dff / (WC::BN / 2), kStreamLds, st);
+  launch_stream<SrcFc1T<FP8>, WC, RowW, typename SrcFc1T<FP8>::OB>(a, z.dff / (WC::BN / 2),
+                                                                   kStreamLds, st);
   rec(ev, 2, st);
-  launch_stream<SrcFc2, WC, RowW, RowW>(a, z.d / WC::BN, kStreamLds, st);
+  launch_stream<SrcFc2T<FP8>, WC, RowW, typename SrcFc2T<FP8>::OB>(a, z.d / WC::BN, kStreamLds, st);
   rec(ev, 3, st);
   const long long nth = (long long)z.T * (z.d / 8);
   if (nth > 0)
@@ -1615,7 +1642,10 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
   a.x = x; a.gates = gates; a.slot_to_row = slot_to_row; a.row_to_slot = row_to_slot;
   a.z_save = z_save;
   const bool big = use_big_tiles(z);
-  if (Lp.act_dtype == MOE_BF16 && Lp.w_dtype == MOE_BF16 && use_stream(z)) run_forward_stream(z, a, row_to_slot, y, ev, st);
+  if (Lp.act_dtype == MOE_BF16 && Lp.w_dtype == MOE_BF16 && use_stream(z))
+    run_forward_stream<false>(z, a, row_to_slot, y, ev, st);
+  else if (Lp.act_dtype == MOE_BF16 && Lp.w_dtype == MOE_FP8_E4M3 && use_stream(z))
+    run_forward_stream<true>(z, a, row_to_slot, y, ev, st);
   else if (Lp.act_dtype == MOE_F32) run_forward<float, false, SmallCfg>(z, a, row_to_slot, y, ev, st);
   else if (Lp.w_dtype == MOE_FP8_E4M3) {
     if (big) run_forward<uint16_t, true, BigCfg>(z, a, row_to_slot, y, ev, st);

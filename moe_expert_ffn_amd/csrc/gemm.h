@@ -595,6 +595,83 @@ template <int ROWS, int NWAVES> struct Row64 {
   }
 };
 
+// K-contiguous e4m3 operand with 128 x 128 block scales: ROWS rows of 64 codes
+// per stage, [row][64 bytes], 16-byte chunk c of row r at chunk c ^ ((r >> 2) & 3).
+// One wave instruction loads 16 rows (4 lanes x 16 bytes each).  An MFMA lane
+// reads its 8 codes of a K chunk with one 8-byte LDS read; the stream widens
+// them to bf16 (code times the block's scale, rounded to nearest even) just
+// before the MFMAs that use them.  A wave's 32-row blocks j and a 64-wide K
+// step lie inside one 128 x 128 scale block each, so a step needs one scale
+// per block j: sp[j][kt / 2] (sp[j] = the scale row of block j's 128 rows).
+template <int ROWS, int NWAVES> struct Row64Fp8 {
+  static constexpr bool kFp8 = true;
+  static constexpr int ROWB = kWideBK;              // one code per K element
+  static constexpr int RPI = 1024 / ROWB;           // rows per wave instruction
+  static constexpr int NI = ROWS / RPI / NWAVES;
+  static constexpr int STAGE_BYTES = ROWS * ROWB;
+  static_assert(NI * RPI * NWAVES == ROWS, "rows per stage");
+  BufRsrc rs;
+  uint32_t off[NI];
+  const MOE_CONST float* sp[2];
+  static MOE_DEV int swz(int row) { return (row >> 2) & 3; }
+  // rowoff(row) = byte offset of the row's first code from b, or -1 for a row
+  // that reads as zeros; `bytes` = extent of the buffer at b.
+  template <class F> MOE_DEV void init(const uint8_t* b, uint32_t bytes, F rowoff) {
+    rs = make_rsrc(b, bytes);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = (w + NWAVES * i) * RPI + (lane >> 2);
+      const int o = rowoff(row);
+      off[i] = o < 0 ? kOob : (uint32_t)o + (uint32_t)(((lane & 3) ^ swz(row)) * 16);
+    }
+  }
+  struct Offs { uint32_t o[NI]; };
+  MOE_DEV Offs prep(int kt) const {
+    Offs q;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) q.o[i] = off[i] + (uint32_t)kt * ROWB;
+    return q;
+  }
+  MOE_DEV void issue(const Offs& q, MOE_LDS char* st) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      buf_load_lds16(rs, q.o[i], (MOE_LDS void*)(st + (w + NWAVES * i) * RPI * ROWB));
+  }
+  // scale of block j for K step kt (wave-uniform: scalar loads)
+  MOE_DEV float scale(int j, int kt) const { return sp[j & 1][kt >> 1]; }
+  // Block j of a wave: rows wave_base + 32 j + (lane & 31), codes 16 KC + 8 (lane >> 5)
+  // .. +7 of the stage; wave_base is a multiple of 32, so the swizzle depends on
+  // the lane only and the offset is (lane part ^ 16 KC) + 2048 j.
+  struct Lane { uint32_t off; };
+  static MOE_DEV Lane lane_info(int wave_base, int lane) {
+    const int lr = lane & 31, h = lane >> 5;
+    return {(uint32_t)((wave_base + lr) * ROWB + swz(lr) * 16 + 8 * h)};
+  }
+  template <int KC> static MOE_DEV u32x2_t codes(const MOE_LDS char* st, const Lane& L, int j) {
+    return *(const MOE_LDS u32x2_t*)(st + ((L.off ^ (16u * KC)) + 32u * ROWB * j));
+  }
+};
+
+// 8 e4m3 codes (bytes of q, low first) times s, as bf16 rounded to nearest even.
+MOE_DEV bf16x8_t dequant8(const u32x2_t& q, float s) {
+  bf16x8_t o;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[w], false);   // bytes 0, 1
+    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[w], true);    // bytes 2, 3
+    o[4 * w + 0] = (__bf16)(lo[0] * s);
+    o[4 * w + 1] = (__bf16)(lo[1] * s);
+    o[4 * w + 2] = (__bf16)(hi[0] * s);
+    o[4 * w + 3] = (__bf16)(hi[1] * s);
+  }
+  return o;
+}
+
+template <class T, class = void> struct op_fp8 { static constexpr bool value = false; };
+template <class T> struct op_fp8<T, decltype((void)T::kFp8)> { static constexpr bool value = T::kFp8; };
+
 // MN-contiguous operand: 64 K rows x MN elements per stage, [k][MN], fragments
 // through ds_read_b64_tr_b16: inside each 16-lane group, lane j supplies the
 // address of row k0 + j/4, columns m0 + 4 (j % 4) .. +3 and receives column
@@ -736,25 +813,46 @@ template <class OP, class F> struct Mn64Operand {
 //                                      (all issued after the loads that step
 //                                      needs), then lgkmcnt(0)
 //   int count, first, stride           items first, first + stride, ... < count
+// An e4m3 B operand (kFp8) hands out raw codes and a scale per 32-row block
+// and K step; the stream loads the next step's scales one step ahead and
+// widens the codes to bf16 in mma().
 template <class C, class OA, class OB> struct WideStream {
   static constexpr int SA = OA::STAGE_BYTES, STAGE = OA::STAGE_BYTES + OB::STAGE_BYTES;
   static constexpr int LPS = OA::NI + OB::NI;
   static constexpr size_t BYTES = (size_t)kWideStages * STAGE;
+  // an e4m3 B operand keeps its raw codes in bq and is widened in mma()
+  static constexpr bool BF8 = op_fp8<OB>::value;
+  static_assert(!BF8 || C::NB == 2, "e4m3 operand: two 32-row blocks per wave");
   bf16x8_t a[2][C::MB], b[2][C::NB];
+  u32x2_t bq[2][C::NB];
+  float bs[C::NB];                                // B scales of the current step
   typename OA::Lane la;
   typename OB::Lane lb;
   template <int KC, int S> MOE_DEV void read(const MOE_LDS char* st) {
 #pragma unroll
     for (int i = 0; i < C::MB; ++i) a[S][i] = OA::template frag<KC>(st, la, i);
 #pragma unroll
-    for (int j = 0; j < C::NB; ++j) b[S][j] = OB::template frag<KC>(st + SA, lb, j);
+    for (int j = 0; j < C::NB; ++j) {
+      if constexpr (BF8) bq[S][j] = OB::template codes<KC>(st + SA, lb, j);
+      else b[S][j] = OB::template frag<KC>(st + SA, lb, j);
+    }
   }
   template <int S> MOE_DEV void mma(f32x16_t (&acc)[C::MB][C::NB]) const {
+    if constexpr (BF8) {
 #pragma unroll
-    for (int i = 0; i < C::MB; ++i)
+      for (int j = 0; j < C::NB; ++j) {
+        const bf16x8_t bj = dequant8(bq[S][j], bs[j]);
 #pragma unroll
-      for (int j = 0; j < C::NB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[S][j], a[S][i], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < C::MB; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bj, a[S][i], acc[i][j], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[S][j], a[S][i], acc[i][j], 0, 0, 0);
+    }
   }
   template <class Src>
   MOE_DEV void run(Src& src, MOE_LDS uint16_t* smem16, f32x16_t (&acc)[C::MB][C::NB]) {
@@ -786,6 +884,11 @@ template <class C, class OA, class OB> struct WideStream {
       a0.issue(pa, smem + st * STAGE);
       b0.issue(pb, smem + st * STAGE + SA);
     }
+    float bsn[C::NB];                            // B scales of the next step
+    if constexpr (BF8) {
+#pragma unroll
+      for (int j = 0; j < C::NB; ++j) bsn[j] = b0.scale(j, 0);
+    }
     wait_vm_lgkm0<(kWideStages - 1) * LPS>();
     __builtin_amdgcn_s_barrier();
     read<0, 0>(smem);
@@ -814,6 +917,10 @@ template <class C, class OA, class OB> struct WideStream {
       const bool relax = g > 0 && n0 >= 2;
       for (int kt = 0; kt < n0; ++kt, ++g) {
         const MOE_LDS char* st = smem + (g & 1) * STAGE;
+        if constexpr (BF8) {
+#pragma unroll
+          for (int j = 0; j < C::NB; ++j) bs[j] = bsn[j];
+        }
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_sched_barrier(0);
         read<1, 1>(st);
@@ -824,6 +931,13 @@ template <class C, class OA, class OB> struct WideStream {
         const int ks = own ? kt + 2 : nxt ? kt + 2 - n0 : n0 - 1;
         const auto pa = nxt ? a1.prep(ks) : a0.prep(ks);
         const auto pb = nxt ? b1.prep(ks) : b0.prep(ks);
+        // B scales of the next step (or of the next item's first), scalar
+        // loads that land by the next chunk's wait
+        if constexpr (BF8) {
+#pragma unroll
+          for (int j = 0; j < C::NB; ++j)
+            bsn[j] = kt + 1 < n0 ? b0.scale(j, kt + 1) : h1 ? b1.scale(j, 0) : bs[j];
+        }
         __builtin_amdgcn_sched_barrier(0);
         mma<0>(acc);
         __builtin_amdgcn_sched_barrier(0);

@@ -21,6 +21,7 @@ import re
 import sys
 
 STAGE_OF = {"k_stream<SrcFc1>": "fwd.fc1", "k_stream<SrcFc2>": "fwd.fc2",
+            "k_stream<SrcFc1Fp8>": "fwd.fc1", "k_stream<SrcFc2Fp8>": "fwd.fc2",
             "k_stream<SrcDa>": "bwd.dA", "k_stream<SrcDx>": "bwd.dX", "k_stream<SrcDwT>": "bwd.dW",
             "k_fc1": "fwd.fc1", "k_fc2": "fwd.fc2", "k_bwd_da": "bwd.dA", "k_bwd_dx": "bwd.dX",
             "k_bwd_dw": "bwd.dW", "k_bwd_reduce": "bwd.reduce",
@@ -31,9 +32,9 @@ STAGE_OF = {"k_stream<SrcFc1>": "fwd.fc1", "k_stream<SrcFc2>": "fwd.fc2",
 
 def short(name: str) -> str:
     """k_stream<SrcX> for the persistent GEMM kernels, the bare kernel name otherwise."""
-    m = re.search(r"k_stream<moe::(\w+)", name)
+    m = re.search(r"k_stream<moe::(\w+?)(T<(true|false)>)?[,<>]", name)
     if m:
-        return f"k_stream<{m.group(1)}>"
+        return f"k_stream<{m.group(1)}{'Fp8' if m.group(3) == 'true' else ''}>"
     m = re.search(r"moe::(\w+)", name)
     return m.group(1) if m else name[:60]
 
