@@ -715,11 +715,15 @@ MOE_DEV float sigm(float g) { return __builtin_amdgcn_rcpf(1.f + __expf(-g)); }
 
 using WC = WideCfg;
 constexpr int kWNW = WC::NT / 64;
-using RowW = Row64<256, kWNW>;
-using MnW = Mn64<256, kWNW>;
+// the row-tile kernels (FC1, FC2, dA, dX): K = 64 per stage, two stages
+constexpr int kRowBK = 64;
+using RowW = RowK<256, kWNW, kRowBK>;
+using MnW = MnK<256, kWNW, kRowBK>;
 constexpr int kItemSlots = 3;
 constexpr size_t kItemBytes = 2048;           // 256 slot -> row entries, 256 slot gates
-constexpr size_t kStageBytes = (size_t)kWideStages * (WC::BM + WC::BN) * kWideRowBytes;
+constexpr size_t kStageBytes = kWideLdsStages;
+// vmcnt wait counts saturate at 63: a smaller count only waits for more
+constexpr int vm_clamp(int n) { return n < 63 ? n : 63; }
 constexpr size_t kEpiOff = kStageBytes + kItemSlots * kItemBytes;   // per-wave epilogue scratch
 constexpr size_t kEpiWave = 2048;
 constexpr size_t kStreamLds = kEpiOff + (WC::NT / 64) * kEpiWave;
@@ -898,10 +902,10 @@ struct MnFixed {
   MOE_DEV Raw pre(int, int k) const { return (uint32_t)k; }
   MOE_DEV uint32_t post(Raw raw, int) const { return raw * ld2 + col2; }
 };
-using MnFixedOp = Mn64Operand<MnW, MnFixed>;
+using MnFixedOp = MnKOperand<MnW, MnFixed>;
 
 // e4m3 weight rows for the wide tile (the stream widens them to bf16)
-using RowF8 = Row64Fp8<256, kWNW>;
+using RowF8 = RowKFp8<256, kWNW, kRowBK>;
 
 // FC1 + SwiGLU.  N tile nj covers A columns [128 nj, 128 nj + 128): weight
 // rows alternate 32 G rows and the matching 32 U rows, so block j = 0 of a
@@ -932,11 +936,11 @@ template <bool FP8> struct SrcFc1T : MSrcBase {
     }
     return w;
   }
-  MOE_DEV int steps(const Item&) const { return a.d / kWideBK; }
+  MOE_DEV int steps(const Item&) const { return a.d / kRowBK; }
   static constexpr int kEpiVmA = WC::MB * RowStore<uint16_t, 1>::STORES;   // A only
-  MOE_DEV void relaxed_wait() const {
-    if (a.z_save) wait_vm_lgkm0<3 * kEpiVmA>();
-    else wait_vm_lgkm0<kEpiVmA>();
+  template <int B> MOE_DEV void relaxed_wait() const {
+    if (a.z_save) wait_vm_lgkm0<vm_clamp(B + 3 * kEpiVmA)>();
+    else wait_vm_lgkm0<vm_clamp(B + kEpiVmA)>();
   }
   MOE_DEV void epilogue(const Item& it, int, const f32x16_t (&acc)[WC::MB][WC::NB]) const {
     const int wm = wave_id() / WC::WAVES_N, wn = wave_id() % WC::WAVES_N;
@@ -992,9 +996,9 @@ template <bool FP8> struct SrcFc2T : MSrcBase {
     }
     return w;
   }
-  MOE_DEV int steps(const Item&) const { return a.dff / kWideBK; }
+  MOE_DEV int steps(const Item&) const { return a.dff / kRowBK; }
   static constexpr int kEpiVm = WC::MB * RowStore<uint16_t, 2>::STORES;
-  MOE_DEV void relaxed_wait() const { wait_vm_lgkm0<kEpiVm>(); }
+  template <int B> MOE_DEV void relaxed_wait() const { wait_vm_lgkm0<vm_clamp(B + kEpiVm)>(); }
   MOE_DEV void epilogue(const Item& it, int slot, const f32x16_t (&acc)[WC::MB][WC::NB]) const {
     const int lane = threadIdx.x & 63, wm = wave_id() / WC::WAVES_N, wn = wave_id() % WC::WAVES_N;
     const MOE_LDS float* gt = item_gates(smem, slot);
@@ -1026,10 +1030,10 @@ struct SrcDa : MSrcBase {
                           (uint32_t)((size_t)2 * a.d * a.dff))};
     return {m, MnFixed{(uint32_t)a.dff * 2u, (uint32_t)it.nj * WC::BN * 2u}};
   }
-  MOE_DEV int steps(const Item&) const { return a.d / kWideBK; }
+  MOE_DEV int steps(const Item&) const { return a.d / kRowBK; }
   // per 32 x 32 block: 8 [G, U] loads and three row-store runs
   static constexpr int kEpiVm = WC::MB * WC::NB * (8 + 3 * RowStore<uint16_t, 1>::STORES);
-  MOE_DEV void relaxed_wait() const { wait_vm_lgkm0<(kEpiVm < 63 ? kEpiVm : 63)>(); }
+  template <int B> MOE_DEV void relaxed_wait() const { wait_vm_lgkm0<vm_clamp(B + kEpiVm)>(); }
   MOE_DEV void epilogue(const Item& it, int slot, const f32x16_t (&acc)[WC::MB][WC::NB]) const {
     constexpr int NBLK = WC::MB * WC::NB;
     const int lane = threadIdx.x & 63, wm = wave_id() / WC::WAVES_N, wn = wave_id() % WC::WAVES_N;
@@ -1111,9 +1115,9 @@ struct SrcDx : MSrcBase {
                           (uint32_t)((size_t)4 * a.dff * a.d))};
     return {m, MnFixed{(uint32_t)a.d * 2u, (uint32_t)it.nj * WC::BN * 2u}};
   }
-  MOE_DEV int steps(const Item&) const { return 2 * a.dff / kWideBK; }
+  MOE_DEV int steps(const Item&) const { return 2 * a.dff / kRowBK; }
   static constexpr int kEpiVm = WC::MB * RowStore<uint16_t, 2>::STORES;
-  MOE_DEV void relaxed_wait() const { wait_vm_lgkm0<kEpiVm>(); }
+  template <int B> MOE_DEV void relaxed_wait() const { wait_vm_lgkm0<vm_clamp(B + kEpiVm)>(); }
   MOE_DEV void epilogue(const Item& it, int, const f32x16_t (&acc)[WC::MB][WC::NB]) const {
     const int wm = wave_id() / WC::WAVES_N, wn = wave_id() % WC::WAVES_N;
     const BufRsrc ro = make_rsrc(a.bufO, (uint32_t)(a.slots * a.d * 2));
@@ -1298,14 +1302,18 @@ struct MnSeg {
 };
 // Weight-gradient tiles: the 256 x 256 wide tile.
 using DwCfg = WideCfg;
-template <class C> using MnSegOpT = Mn64Operand<Mn64<C::BN, C::NT / 64>, MnSeg>;
+// K = 64 per stage, two stages.  The slot map of each K row is read with
+// vector loads during the step, so a deeper pipeline would have to wait for
+// them, and everything issued before them, ahead of the next step's loads.
+constexpr int kDwBK = 64;
+template <class C> using MnSegOpT = MnKOperand<MnK<C::BN, C::NT / 64, kDwBK>, MnSeg>;
 using MnSegOp = MnSegOpT<DwCfg>;
 constexpr size_t kDwLds = kStreamLds;
 
 struct DwItem { int e, slot0, nrows, dst, is2, mi, nj; };
 template <class C> struct SrcDwT {
   using Item = DwItem;
-  using MnC = Mn64<C::BN, C::NT / 64>;
+  using MnC = MnK<C::BN, C::NT / 64, kDwBK>;
   static_assert(C::BM == C::BN, "one MN operand type for both sides");
   static_assert(MnC::RPI == 2, "a load instruction covers the K row pair kb, kb + 1");
   ExecArgs a;              // a copy: the fields stay in scalar registers
@@ -1350,10 +1358,12 @@ template <class C> struct SrcDwT {
     return {m, MnSeg{a.slot_to_row, a.kmagic, (uint32_t)ld * 2u, (uint32_t)it.nj * C::BN * 2u,
                      it.slot0, it.nrows, !it.is2}};
   }
-  MOE_DEV int steps(const Item& it) const { return max(2, (it.nrows + kWideBK - 1) / kWideBK); }
+  MOE_DEV int steps(const Item& it) const {
+    return max(wide_stages(kDwBK), (it.nrows + kDwBK - 1) / kDwBK);
+  }
   // vector memory operations of one epilogue, per wave: all stores
   static constexpr int kEpiVm = C::MB * C::NB * RowStore<float, 1>::STORES;
-  MOE_DEV void relaxed_wait() const { wait_vm_lgkm0<(kEpiVm < 63 ? kEpiVm : 63)>(); }
+  template <int B> MOE_DEV void relaxed_wait() const { wait_vm_lgkm0<vm_clamp(B + kEpiVm)>(); }
   MOE_DEV void epilogue(const Item& it, int, const f32x16_t (&acc)[C::MB][C::NB]) const {
     const int lane = threadIdx.x & 63;
     const size_t w_elems = (size_t)3 * a.d * a.dff;

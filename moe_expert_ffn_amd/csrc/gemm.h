@@ -516,104 +516,125 @@ MOE_DEV void gemm_tile_dma(const OA& oa, const OB& ob, int nk, MOE_LDS uint16_t*
   p.run(oa, ob, nk, smem, acc, accumulate);
 }
 
-// ---- wide tile: 256 x 256, 8 waves, K = 64 per stage --------------------------
+// ---- wide tile: 256 x 256, 8 waves, direct-to-LDS stages -----------------------
 // Eight waves (2 x 4, each 128 x 64 with 128 accumulator registers, two waves
-// per SIMD) share one 256 x 256 tile; a stage holds K = 64, so every row
-// segment is a full 128-byte line, both for the global load and in LDS.  Two
-// direct-to-LDS stages (128 KB): the loads of step kt+1 land while step kt
-// computes.  Accumulators are transposed (the N fragment is the MFMA's first
-// operand): each lane owns one output row and four consecutive columns per
-// register quad.
+// per SIMD) share one 256 x 256 tile.  The operands stream through 128 KB of
+// LDS in stages loaded with direct-to-LDS buffer loads; the K per stage comes
+// from the operand types and fixes the depth:
+//   K = 64 per stage, two stages: every row segment is a full 128-byte line,
+//     and a stage's loads have one step of MFMAs to land;
+//   K = 32 per stage, four stages: three steps to land, half-line segments.
+// Both are supported; every kernel here uses K = 64.  Measured on the FC1,
+// FC2, dA and dX kernels, the four-stage form was 4-8% slower: the steps are
+// bound by the throughput of the per-CU load path (about 18 bytes per clock
+// per CU), not by its latency, and the shorter steps add barriers.
+// Accumulators are transposed (the N fragment is the MFMA's first operand):
+// each lane owns one output row and four consecutive columns per register quad.
 //
 // LDS swizzles, chosen from measured bank behaviour of gfx950:
-//   ds_read_b128 on 128-byte rows serves 16 lanes per clock; XOR-ing the
-//   16-byte chunk index with (row ^ row >> 3) & 7 over 32 consecutive rows
-//   gives every group of 16 lanes distinct banks;
+//   ds_read_b128 serves 16 lanes per clock; on 128-byte rows XOR-ing the
+//   16-byte chunk index with (row ^ row >> 3) & 7, on 64-byte rows with
+//   (row >> 2) & 3, gives every group of 16 lanes distinct banks;
 //   ds_read_b64_tr_b16 serves 32 lanes per clock (4 rows x 64 bytes); XOR-ing
 //   the chunk index with 4 (row & 3) spreads those four rows over disjoint
 //   64-byte bank ranges.
 using WideCfg = GemmCfg<256, 256, 2, 4>;
-constexpr int kWideBK = 64, kWideStages = 2, kWideRowBytes = 128;
+constexpr size_t kWideLdsStages = 128 * 1024;     // LDS for the operand stages
+// stages of a K-per-stage: as many as fit 128 KB for a 256 + 256 row tile
+constexpr int wide_stages(int bk) { return (int)(kWideLdsStages / (512 * 2 * (size_t)bk)); }
 
 MOE_DEV int swz_row128(int row) { return (row & 7) ^ ((row >> 3) & 3); }   // rows mod 32
+MOE_DEV int swz_row64(int row) { return (row >> 2) & 3; }                   // rows mod 16
 MOE_DEV int swz_tr(int row) { return (row & 3) << 2; }
 typedef short s16x4_t __attribute__((ext_vector_type(4)));   // one transpose read
 
-// K-contiguous operand: ROWS rows of K = 64 per stage, [row][128 bytes].
-// One wave instruction loads 8 rows (8 lanes x 16 bytes each).
-template <int ROWS, int NWAVES> struct Row64 {
-  static constexpr int NI = ROWS / 8 / NWAVES;
-  static constexpr int STAGE_BYTES = ROWS * kWideRowBytes;
-  static_assert(NI * 8 * NWAVES == ROWS, "rows per stage");
+// K-contiguous bf16 operand: ROWS rows of K = BK per stage, [row][2 BK bytes].
+// One wave instruction loads 1024 bytes: 8 rows of 128 bytes or 16 of 64.
+template <int ROWS, int NWAVES, int BK_> struct RowK {
+  static constexpr int BK = BK_;
+  static constexpr int RB = 2 * BK;                 // row bytes per stage
+  static constexpr int CPR = RB / 16;               // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;              // rows per wave instruction
+  static constexpr int NI = ROWS / RPI / NWAVES;
+  static constexpr int STAGE_BYTES = ROWS * RB;
+  static_assert(NI * RPI * NWAVES == ROWS, "rows per stage");
+  static_assert(RB == 64 || RB == 128, "stage row bytes");
+  static MOE_DEV int swz(int row) { return RB == 128 ? swz_row128(row) : swz_row64(row); }
   BufRsrc rs;
   uint32_t off[NI];
+  // Rows this lane loads: row(i) = (wave + NWAVES i) * RPI + lane / CPR.
+  static MOE_DEV int lane_row(int i) {
+    return ((threadIdx.x >> 6) + NWAVES * i) * RPI + ((threadIdx.x & 63) / CPR);
+  }
   // rowoff(row) = element offset of the row's first K element from b, or -1 for
   // a row that reads as zeros; `bytes` = extent of the buffer at b.
   template <class F> MOE_DEV void init(const uint16_t* b, uint32_t bytes, F rowoff) {
     rs = make_rsrc(b, bytes);
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int row = (w + NWAVES * i) * 8 + (lane >> 3);
+      const int row = lane_row(i);
       const int o = rowoff(row);
-      off[i] = o < 0 ? kOob : (uint32_t)o * 2u + (uint32_t)(((lane & 7) ^ swz_row128(row)) * 16);
+      off[i] = o < 0 ? kOob : (uint32_t)o * 2u + (uint32_t)(((lane % CPR) ^ swz(row)) * 16);
     }
   }
-  // Rows this lane loads: row(i) = (wave + NWAVES i) * 8 + lane / 8.
-  static MOE_DEV int lane_row(int i) { return ((threadIdx.x >> 6) + NWAVES * i) * 8 + ((threadIdx.x & 63) >> 3); }
   // From the element offsets of this lane's rows (-1 = zero row).
   MOE_DEV void init_offsets(const uint16_t* b, uint32_t bytes, const int (&o)[NI]) {
     rs = make_rsrc(b, bytes);
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      off[i] = o[i] < 0 ? kOob : (uint32_t)o[i] * 2u + (uint32_t)(((lane & 7) ^ swz_row128(lane_row(i))) * 16);
+      off[i] = o[i] < 0 ? kOob : (uint32_t)o[i] * 2u + (uint32_t)(((lane % CPR) ^ swz(lane_row(i))) * 16);
   }
   struct Offs { uint32_t o[NI]; };
   MOE_DEV Offs prep(int kt) const {
     Offs q;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) q.o[i] = off[i] + (uint32_t)kt * kWideRowBytes;
+    for (int i = 0; i < NI; ++i) q.o[i] = off[i] + (uint32_t)kt * RB;
     return q;
   }
   MOE_DEV void issue(const Offs& q, MOE_LDS char* st) const {
     const int w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      buf_load_lds16(rs, q.o[i], (MOE_LDS void*)(st + (w + NWAVES * i) * 8 * kWideRowBytes));
+      buf_load_lds16(rs, q.o[i], (MOE_LDS void*)(st + (w + NWAVES * i) * RPI * RB));
   }
   // Fragment i of a wave: rows wave_base + 32 i + (lane & 31), K chunk
   // 2 KC + (lane >> 5) of the stage; wave_base is a multiple of 32, so the
-  // offset is (lane part ^ 32 KC) + 4096 i.
+  // swizzle depends on the lane only and the offset is (lane part ^ 32 KC) +
+  // 32 RB i.
   struct Lane { uint32_t off; };
   static MOE_DEV Lane lane_info(int wave_base, int lane) {
     const int lr = lane & 31, h = lane >> 5;
-    return {(uint32_t)((wave_base + lr) * kWideRowBytes + ((h ^ swz_row128(lr)) * 16))};
+    return {(uint32_t)((wave_base + lr) * RB + ((h ^ swz(lr)) * 16))};
   }
   template <int KC> static MOE_DEV bf16x8_t frag(const MOE_LDS char* st, const Lane& L, int i) {
-    return *(const MOE_LDS bf16x8_t*)(st + ((L.off ^ (32u * KC)) + 32u * kWideRowBytes * i));
+    return *(const MOE_LDS bf16x8_t*)(st + ((L.off ^ (32u * KC)) + 32u * RB * i));
   }
 };
 
-// K-contiguous e4m3 operand with 128 x 128 block scales: ROWS rows of 64 codes
-// per stage, [row][64 bytes], 16-byte chunk c of row r at chunk c ^ ((r >> 2) & 3).
-// One wave instruction loads 16 rows (4 lanes x 16 bytes each).  An MFMA lane
-// reads its 8 codes of a K chunk with one 8-byte LDS read; the stream widens
-// them to bf16 (code times the block's scale, rounded to nearest even) just
-// before the MFMAs that use them.  A wave's 32-row blocks j and a 64-wide K
-// step lie inside one 128 x 128 scale block each, so a step needs one scale
-// per block j: sp[j][kt / 2] (sp[j] = the scale row of block j's 128 rows).
-template <int ROWS, int NWAVES> struct Row64Fp8 {
+// K-contiguous e4m3 operand with 128 x 128 block scales: ROWS rows of BK codes
+// per stage, [row][BK bytes]; one wave instruction loads 1024 / BK rows, and
+// the 16-byte chunk c of row r sits at chunk c ^ swz(r).  An MFMA lane reads
+// its 8 codes of a K chunk with one 8-byte LDS read; the stream widens them to
+// bf16 (code times the block's scale, rounded to nearest even) just before
+// the MFMAs that use them.  A wave's 32-row blocks j and a K step lie inside
+// one 128 x 128 scale block each, so a step needs one scale per block j:
+// sp[j][kt * BK / 128] (sp[j] = the scale row of block j's 128 rows).
+template <int ROWS, int NWAVES, int BK_> struct RowKFp8 {
   static constexpr bool kFp8 = true;
-  static constexpr int ROWB = kWideBK;              // one code per K element
-  static constexpr int RPI = 1024 / ROWB;           // rows per wave instruction
+  static constexpr int BK = BK_;
+  static constexpr int RB = BK;                     // one code per K element
+  static constexpr int CPR = RB / 16;
+  static constexpr int RPI = 64 / CPR;
   static constexpr int NI = ROWS / RPI / NWAVES;
-  static constexpr int STAGE_BYTES = ROWS * ROWB;
+  static constexpr int STAGE_BYTES = ROWS * RB;
   static_assert(NI * RPI * NWAVES == ROWS, "rows per stage");
+  static_assert(RB == 32 || RB == 64, "stage row bytes");
   BufRsrc rs;
   uint32_t off[NI];
   const MOE_CONST float* sp[2];
-  static MOE_DEV int swz(int row) { return (row >> 2) & 3; }
+  static MOE_DEV int swz(int row) { return RB == 64 ? (row >> 2) & 3 : (row >> 3) & 1; }
   // rowoff(row) = byte offset of the row's first code from b, or -1 for a row
   // that reads as zeros; `bytes` = extent of the buffer at b.
   template <class F> MOE_DEV void init(const uint8_t* b, uint32_t bytes, F rowoff) {
@@ -621,36 +642,36 @@ template <int ROWS, int NWAVES> struct Row64Fp8 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int row = (w + NWAVES * i) * RPI + (lane >> 2);
+      const int row = (w + NWAVES * i) * RPI + lane / CPR;
       const int o = rowoff(row);
-      off[i] = o < 0 ? kOob : (uint32_t)o + (uint32_t)(((lane & 3) ^ swz(row)) * 16);
+      off[i] = o < 0 ? kOob : (uint32_t)o + (uint32_t)(((lane % CPR) ^ swz(row)) * 16);
     }
   }
   struct Offs { uint32_t o[NI]; };
   MOE_DEV Offs prep(int kt) const {
     Offs q;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) q.o[i] = off[i] + (uint32_t)kt * ROWB;
+    for (int i = 0; i < NI; ++i) q.o[i] = off[i] + (uint32_t)kt * RB;
     return q;
   }
   MOE_DEV void issue(const Offs& q, MOE_LDS char* st) const {
     const int w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      buf_load_lds16(rs, q.o[i], (MOE_LDS void*)(st + (w + NWAVES * i) * RPI * ROWB));
+      buf_load_lds16(rs, q.o[i], (MOE_LDS void*)(st + (w + NWAVES * i) * RPI * RB));
   }
   // scale of block j for K step kt (wave-uniform: scalar loads)
-  MOE_DEV float scale(int j, int kt) const { return sp[j & 1][kt >> 1]; }
+  MOE_DEV float scale(int j, int kt) const { return sp[j & 1][kt / (128 / BK)]; }
   // Block j of a wave: rows wave_base + 32 j + (lane & 31), codes 16 KC + 8 (lane >> 5)
   // .. +7 of the stage; wave_base is a multiple of 32, so the swizzle depends on
-  // the lane only and the offset is (lane part ^ 16 KC) + 2048 j.
+  // the lane only and the offset is (lane part ^ 16 KC) + 32 RB j.
   struct Lane { uint32_t off; };
   static MOE_DEV Lane lane_info(int wave_base, int lane) {
     const int lr = lane & 31, h = lane >> 5;
-    return {(uint32_t)((wave_base + lr) * ROWB + swz(lr) * 16 + 8 * h)};
+    return {(uint32_t)((wave_base + lr) * RB + swz(lr) * 16 + 8 * h)};
   }
   template <int KC> static MOE_DEV u32x2_t codes(const MOE_LDS char* st, const Lane& L, int j) {
-    return *(const MOE_LDS u32x2_t*)(st + ((L.off ^ (16u * KC)) + 32u * ROWB * j));
+    return *(const MOE_LDS u32x2_t*)(st + ((L.off ^ (16u * KC)) + 32u * RB * j));
   }
 };
 
@@ -672,36 +693,26 @@ MOE_DEV bf16x8_t dequant8(const u32x2_t& q, float s) {
 template <class T, class = void> struct op_fp8 { static constexpr bool value = false; };
 template <class T> struct op_fp8<T, decltype((void)T::kFp8)> { static constexpr bool value = T::kFp8; };
 
-// MN-contiguous operand: 64 K rows x MN elements per stage, [k][MN], fragments
+// MN-contiguous operand: BK K rows x MN elements per stage, [k][MN], fragments
 // through ds_read_b64_tr_b16: inside each 16-lane group, lane j supplies the
 // address of row k0 + j/4, columns m0 + 4 (j % 4) .. +3 and receives column
 // m0 + j of rows k0 .. k0+3, i.e. four consecutive K values of one M/N index;
 // two such reads give the eight K values an MFMA lane needs.  rowoff(k) = byte offset in the
 // buffer of (source row of K index k, mn0), or kOob for a zero row.
-template <int MN, int NWAVES> struct Mn64 {
+template <int MN, int NWAVES, int BK_> struct MnK {
+  static constexpr int BK = BK_;
   static constexpr int ROWB = MN * 2;
   static constexpr int RPI = 1024 / ROWB;           // K rows per wave instruction
   static constexpr int CPR = ROWB / 16;
-  static constexpr int NI = kWideBK / RPI / NWAVES;
-  static constexpr int STAGE_BYTES = kWideBK * ROWB;
-  static_assert(NI * RPI * NWAVES == kWideBK, "64 K rows per stage");
+  static constexpr int NI = BK / RPI / NWAVES;
+  static constexpr int STAGE_BYTES = BK * ROWB;
+  static_assert(NI * RPI * NWAVES == BK, "K rows per stage");
   BufRsrc rs;
   struct Offs { uint32_t o[NI]; };
   // stage row (K index within the step) loaded by this lane's instruction i
   static MOE_DEV int row_of(int i) { return ((threadIdx.x >> 6) + NWAVES * i) * RPI + (threadIdx.x & 63) / CPR; }
   // first of the RPI rows of instruction i (wave-uniform)
   static MOE_DEV int row_base(int i) { return (wave_id() + NWAVES * i) * RPI; }
-  template <class F> MOE_DEV Offs prep_rows(int kt, F rowoff) const {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    Offs p;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int r = (w + NWAVES * i) * RPI + lane / CPR;
-      const uint32_t c = (uint32_t)((lane % CPR) ^ swz_tr(r));
-      p.o[i] = rowoff(kt * kWideBK + r) + c * 16u;
-    }
-    return p;
-  }
   MOE_DEV void issue(const Offs& p, MOE_LDS char* st) const {
     const int w = threadIdx.x >> 6;
 #pragma unroll
@@ -747,10 +758,10 @@ template <int MN, int NWAVES> struct Mn64 {
 // F::post(raw, k) turns it into the byte offset of (row, mn0) in the buffer,
 // or kOob for a zero row.  prep() runs early in a step, issue() after the
 // step-end wait.
-template <class OP, class F> struct Mn64Operand {
+template <class OP, class F> struct MnKOperand {
   OP op;
   F f;
-  static constexpr int NI = OP::NI, STAGE_BYTES = OP::STAGE_BYTES;
+  static constexpr int BK = OP::BK, NI = OP::NI, STAGE_BYTES = OP::STAGE_BYTES;
   using Lane = typename OP::Lane;
   // f.pre(kb, k): what post needs for the lane's K row k, where kb is the
   // wave-uniform first row of the same instruction
@@ -759,7 +770,7 @@ template <class OP, class F> struct Mn64Operand {
     Offs p;
     p.kt = kt;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) p.raw[i] = f.pre(kt * kWideBK + OP::row_base(i), kt * kWideBK + OP::row_of(i));
+    for (int i = 0; i < NI; ++i) p.raw[i] = f.pre(kt * BK + OP::row_base(i), kt * BK + OP::row_of(i));
     return p;
   }
   MOE_DEV void issue(const Offs& p, MOE_LDS char* st) const {
@@ -767,7 +778,7 @@ template <class OP, class F> struct Mn64Operand {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int r = OP::row_of(i);
-      q.o[i] = f.post(p.raw[i], p.kt * kWideBK + r) + (uint32_t)(((threadIdx.x & 63) % OP::CPR) ^ swz_tr(r)) * 16u;
+      q.o[i] = f.post(p.raw[i], p.kt * BK + r) + (uint32_t)(((threadIdx.x & 63) % OP::CPR) ^ swz_tr(r)) * 16u;
     }
     op.issue(q, st);
   }
@@ -776,28 +787,32 @@ template <class OP, class F> struct Mn64Operand {
     return OP::template frag<KC>(st, L, i);
   }
 };
-// nk = K / 64 steps.  Step kt (stage kt % 2):
-//   four K chunks; the fragments of chunk c+1 are read while chunk c's 8 MFMAs
-//   run; the load offsets of step kt+2 are prepared early in the step;
-//   after chunk 2: wait for this wave's loads of step kt+1 and its LDS reads,
-//   barrier (every wave's part of step kt+1 is in LDS, nobody reads stage
-//   kt % 2 any more), issue step kt+2 into stage kt % 2, read chunk 0 of
-//   step kt+1, then chunk 3's MFMAs.
-// Loads past the last step re-read step nk-1 into a stage nobody reads again.
-// Fragments read from asm (Mn64) are consumed only after an explicit
-// lgkmcnt(0) wait pinned by a scheduling barrier.
 // ---- wide tile, persistent across tiles -------------------------------------
-// The per-step schedule above, with the stream of K steps running on
-// from one work item to the next: the first two steps of the next item are
-// issued during the last two steps of the current one, so a tile starts with
-// its operands already in LDS, and the previous tile's stores drain while the
-// next tile's first step computes.  Items come from a static per-workgroup
-// sequence (no queue atomics).  Because vector-memory completions are counted
-// in order, nothing issued while loads are in flight may be waited for early:
-// an item's descriptor is read three items ahead, its per-row data (moved
-// into LDS by direct loads) two items ahead, and its operands are set up one
-// item ahead; every one of those waits falls on a step-end wait that happens
-// anyway.
+// K runs in steps of BK (32 or 64) over S = wide_stages(BK) LDS stages; step
+// g of the stream uses stage g % S.  A step is NCH = BK / 16 K chunks; the
+// fragments of chunk c+1 are read while chunk c's 8 MFMAs per wave run, and
+// the load offsets of step g+S are prepared early in the step.  After the
+// second-to-last chunk's MFMAs: wait until this wave's loads of step g+1 have
+// landed (the loads of the S-2 steps issued after them may stay in flight)
+// and its LDS reads are done; barrier (every wave's part of step g+1 is in
+// LDS and nobody reads stage g % S any more); issue step g+S into stage g % S;
+// read chunk 0 of step g+1; then the last chunk's MFMAs.  Fragments read from
+// asm (MnK) are consumed only after an explicit lgkmcnt(0) wait pinned by a
+// scheduling barrier.
+//
+// The stream of K steps runs on from one work item to the next: the first S
+// steps of the next item are issued during the last S steps of the current
+// one, so a tile starts with its operands already in LDS, and the previous
+// tile's stores drain while the next tile's first S-1 steps compute.  Items
+// come from a static per-workgroup sequence (no queue atomics).  Because
+// vector-memory completions are counted in order, nothing issued while loads
+// are in flight may be waited for early: an item's descriptor is read three
+// items ahead, its per-row data (moved into LDS by direct loads) two items
+// ahead, and its operands are set up one item ahead; every one of those
+// waits falls on a step-end wait that happens anyway.  Every item has at
+// least S steps, and every step issues the same loads (past the stream's end
+// they re-read the last step into stages nobody reads again), so the wait
+// counts are fixed.
 //
 // Src provides:
 //   Item load(int idx)                 descriptor of item idx (plain loads)
@@ -805,21 +820,26 @@ template <class OP, class F> struct Mn64Operand {
 //                                      item slot `slot` (after a barrier: the
 //                                      slot's previous item is finished)
 //   OA opA(const Item&, int slot), OB opB(const Item&, int slot)
-//   int steps(const Item&)             K steps, >= 2
+//   int steps(const Item&)             K steps, >= S
 //   void epilogue(const Item&, int slot, acc)
-//   void relaxed_wait()                the wait at the end of an item's first
-//                                      step: vmcnt(N) with N at most the vector
-//                                      memory operations one epilogue issues
-//                                      (all issued after the loads that step
-//                                      needs), then lgkmcnt(0)
+//   template <int B> relaxed_wait()    the wait at the end of an item's first
+//                                      S-1 steps: vmcnt(B + N) with N at most
+//                                      the vector memory operations one
+//                                      epilogue issues, then lgkmcnt(0)
 //   int count, first, stride           items first, first + stride, ... < count
 // An e4m3 B operand (kFp8) hands out raw codes and a scale per 32-row block
 // and K step; the stream loads the next step's scales one step ahead and
 // widens the codes to bf16 in mma().
 template <class C, class OA, class OB> struct WideStream {
+  static constexpr int BK = OA::BK;
+  static_assert(OB::BK == BK, "one K step for both operands");
+  static constexpr int S = wide_stages(BK), NCH = BK / 16;
+  static_assert(S >= 2 && (S & (S - 1)) == 0 && (NCH == 2 || NCH == 4), "stage shape");
   static constexpr int SA = OA::STAGE_BYTES, STAGE = OA::STAGE_BYTES + OB::STAGE_BYTES;
+  static_assert((size_t)S * STAGE <= kWideLdsStages, "stages fit");
   static constexpr int LPS = OA::NI + OB::NI;
-  static constexpr size_t BYTES = (size_t)kWideStages * STAGE;
+  static constexpr int VM_AHEAD = (S - 2) * LPS;  // loads younger than the next step's
+  static_assert(VM_AHEAD < 64, "vmcnt range");
   // an e4m3 B operand keeps its raw codes in bq and is widened in mma()
   static constexpr bool BF8 = op_fp8<OB>::value;
   static_assert(!BF8 || C::NB == 2, "e4m3 operand: two 32-row blocks per wave");
@@ -828,31 +848,35 @@ template <class C, class OA, class OB> struct WideStream {
   float bs[C::NB];                                // B scales of the current step
   typename OA::Lane la;
   typename OB::Lane lb;
-  template <int KC, int S> MOE_DEV void read(const MOE_LDS char* st) {
+  template <int KC, int SB> MOE_DEV void read(const MOE_LDS char* st) {
 #pragma unroll
-    for (int i = 0; i < C::MB; ++i) a[S][i] = OA::template frag<KC>(st, la, i);
+    for (int i = 0; i < C::MB; ++i) a[SB][i] = OA::template frag<KC>(st, la, i);
 #pragma unroll
     for (int j = 0; j < C::NB; ++j) {
-      if constexpr (BF8) bq[S][j] = OB::template codes<KC>(st + SA, lb, j);
-      else b[S][j] = OB::template frag<KC>(st + SA, lb, j);
+      if constexpr (BF8) bq[SB][j] = OB::template codes<KC>(st + SA, lb, j);
+      else b[SB][j] = OB::template frag<KC>(st + SA, lb, j);
     }
   }
-  template <int S> MOE_DEV void mma(f32x16_t (&acc)[C::MB][C::NB]) const {
+  template <int SB> MOE_DEV void mma(f32x16_t (&acc)[C::MB][C::NB]) const {
     if constexpr (BF8) {
 #pragma unroll
       for (int j = 0; j < C::NB; ++j) {
-        const bf16x8_t bj = dequant8(bq[S][j], bs[j]);
+        const bf16x8_t bj = dequant8(bq[SB][j], bs[j]);
 #pragma unroll
         for (int i = 0; i < C::MB; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bj, a[S][i], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bj, a[SB][i], acc[i][j], 0, 0, 0);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < C::MB; ++i)
 #pragma unroll
         for (int j = 0; j < C::NB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[S][j], a[S][i], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[SB][j], a[SB][i], acc[i][j], 0, 0, 0);
     }
+  }
+  static MOE_DEV void lgkm0() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_sched_barrier(0);
   }
   template <class Src>
   MOE_DEV void run(Src& src, MOE_LDS uint16_t* smem16, f32x16_t (&acc)[C::MB][C::NB]) {
@@ -878,7 +902,7 @@ template <class C, class OA, class OB> struct WideStream {
     OB b0 = src.opB(it0, slot);
     int n0 = src.steps(it0);
 #pragma unroll
-    for (int st = 0; st < kWideStages; ++st) {
+    for (int st = 0; st < S; ++st) {
       const auto pa = a0.prep(st);
       const auto pb = b0.prep(st);
       a0.issue(pa, smem + st * STAGE);
@@ -889,10 +913,10 @@ template <class C, class OA, class OB> struct WideStream {
 #pragma unroll
       for (int j = 0; j < C::NB; ++j) bsn[j] = b0.scale(j, 0);
     }
-    wait_vm_lgkm0<(kWideStages - 1) * LPS>();
+    wait_vm_lgkm0<(S - 1) * LPS>();
     __builtin_amdgcn_s_barrier();
     read<0, 0>(smem);
-    int g = 0;                                   // global step index: stage g & 1
+    int g = 0;                                   // global step index: stage g % S
     while (true) {
       const int s1 = slot == 2 ? 0 : slot + 1, s2 = s1 == 2 ? 0 : s1 + 1;
       const bool h3 = idx + 3 * s < src.count;
@@ -909,26 +933,24 @@ template <class C, class OA, class OB> struct WideStream {
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
       // the item's first step landed before the previous item's last barrier
-      if (g > 0) read<0, 0>(smem + (g & 1) * STAGE);
-      // At the end of this item's first step the loads it waits for were issued
+      if (g > 0) read<0, 0>(smem + (g & (S - 1)) * STAGE);
+      // During its first S-1 steps, the loads an item waits for were issued
       // before the previous item's epilogue, so the epilogue's stores (and
-      // loads) may stay in flight: they drain under this step and the next.
-      // The next step's wait is a full one, so the item needs two steps.
-      const bool relax = g > 0 && n0 >= 2;
+      // loads) may stay in flight: they drain under those steps.
+      const bool relax = g > 0;
       for (int kt = 0; kt < n0; ++kt, ++g) {
-        const MOE_LDS char* st = smem + (g & 1) * STAGE;
+        const MOE_LDS char* st = smem + (g & (S - 1)) * STAGE;
         if constexpr (BF8) {
 #pragma unroll
           for (int j = 0; j < C::NB; ++j) bs[j] = bsn[j];
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_sched_barrier(0);
+        lgkm0();
         read<1, 1>(st);
-        // step g + 2 of the stream: this item, the next one, or a harmless
+        // step g + S of the stream: this item, the next one, or a harmless
         // re-read of this item's last step when the stream ends
-        const bool own = kt + 2 < n0;
+        const bool own = kt + S < n0;
         const bool nxt = !own && h1;
-        const int ks = own ? kt + 2 : nxt ? kt + 2 - n0 : n0 - 1;
+        const int ks = own ? kt + S : nxt ? kt + S - n0 : n0 - 1;
         const auto pa = nxt ? a1.prep(ks) : a0.prep(ks);
         const auto pb = nxt ? b1.prep(ks) : b0.prep(ks);
         // B scales of the next step (or of the next item's first), scalar
@@ -941,33 +963,33 @@ template <class C, class OA, class OB> struct WideStream {
         __builtin_amdgcn_sched_barrier(0);
         mma<0>(acc);
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_sched_barrier(0);
-        read<2, 0>(st);
-        __builtin_amdgcn_sched_barrier(0);
-        mma<1>(acc);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_sched_barrier(0);
-        read<3, 1>(st);
-        __builtin_amdgcn_sched_barrier(0);
-        mma<0>(acc);
-        __builtin_amdgcn_sched_barrier(0);
-        if (relax && kt == 0) src.relaxed_wait();
-        else wait_vm_lgkm0<0>();
+        if constexpr (NCH == 4) {
+          lgkm0();
+          read<2, 0>(st);
+          __builtin_amdgcn_sched_barrier(0);
+          mma<1>(acc);
+          __builtin_amdgcn_sched_barrier(0);
+          lgkm0();
+          read<3, 1>(st);
+          __builtin_amdgcn_sched_barrier(0);
+          mma<0>(acc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (relax && kt < S - 1) src.template relaxed_wait<VM_AHEAD>();
+        else wait_vm_lgkm0<VM_AHEAD>();
         __builtin_amdgcn_s_barrier();
         // every wave is past the previous item's epilogue: item slot s2 is free
         if (kt == 0 && h2) src.fill(it2, s2);
         if (nxt) {
-          a1.issue(pa, smem + (g & 1) * STAGE);
-          b1.issue(pb, smem + (g & 1) * STAGE + SA);
+          a1.issue(pa, smem + (g & (S - 1)) * STAGE);
+          b1.issue(pb, smem + (g & (S - 1)) * STAGE + SA);
         } else {
-          a0.issue(pa, smem + (g & 1) * STAGE);
-          b0.issue(pb, smem + (g & 1) * STAGE + SA);
+          a0.issue(pa, smem + (g & (S - 1)) * STAGE);
+          b0.issue(pb, smem + (g & (S - 1)) * STAGE + SA);
         }
         // chunk 0 of the next step; for the next item it is read after the
         // epilogue, so its fragments are not live across it
-        if (kt + 1 < n0) read<0, 0>(smem + ((g + 1) & 1) * STAGE);
+        if (kt + 1 < n0) read<0, 0>(smem + ((g + 1) & (S - 1)) * STAGE);
         __builtin_amdgcn_sched_barrier(0);
         mma<1>(acc);
         __builtin_amdgcn_sched_barrier(0);
