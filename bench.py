@@ -157,7 +157,7 @@ def kernel_model(w, R, T, e_act, replicas):
 # HBM traffic of the dominant kernel from rocprofv3 counters (FETCH_SIZE and
 # WRITE_SIZE per dispatch, scaled by the reading of a plain copy kernel of
 # known size), valid only for the kernel sources it was measured on.
-PROFILED_TRAFFIC = {"kernel": "bwd.dW", "source": "3fd5a67860c262f4", "bytes": 3823876747,
+PROFILED_TRAFFIC = {"kernel": "bwd.dW", "source": "7fe2a1a2d1426459", "bytes": 3820671184,
                     "summary": "profiles/k_stream_SrcDwT_qwen3_bf16_fwdbwd_hbm_traffic.md"}
 
 
