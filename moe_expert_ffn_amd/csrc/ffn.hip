@@ -219,6 +219,8 @@ struct ExecArgs {
   float* dqs;             //   its scales [slots / beta][d]
   uint8_t* zq;            //   dZ, e4m3 [slots][2 d_ff]
   float* zqs;             //   its scales [slots / beta][2 d_ff]
+  void* dhat;             // fp8 backward on the stream kernels: D requantized and
+                          //   widened back to bf16, [slots][d]
 };
 
 enum { PH_FC1 = 0, PH_FC2 = 1, PH_DA = 2, PH_DX = 3, PH_DW = 4 };
@@ -458,11 +460,15 @@ MOE_DEV uint32_t f32_to_e4m3(float v) {
   return sign | q;
 }
 
-__global__ __launch_bounds__(256) void k_quant_tok(const uint16_t* __restrict__ src, int ld,
+// DEQ: instead of codes and scales, write code * scale as bf16 to deq
+// [rows][cols] (which may be src itself: a thread reads each of its values
+// before it overwrites them).
+template <bool DEQ>
+__global__ __launch_bounds__(256) void k_quant_tok(const uint16_t* src, int ld,
                                                    const int32_t* __restrict__ map, int gather, int div,
                                                    const float* __restrict__ rscale, int rows,
-                                                   int cols, int brows, uint8_t* __restrict__ codes,
-                                                   float* __restrict__ scales) {
+                                                   int cols, int brows, uint8_t* codes,
+                                                   float* scales, uint16_t* deq) {
   const int nch = cols / 8, nblk = (rows + brows - 1) / brows;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long long)nblk * nch) return;
@@ -498,18 +504,22 @@ __global__ __launch_bounds__(256) void k_quant_tok(const uint16_t* __restrict__ 
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     sc[i] = amax[i] / 448.f;
-    scales[(size_t)b * cols + c0 + i] = sc[i];
+    if constexpr (!DEQ) scales[(size_t)b * cols + c0 + i] = sc[i];
   }
   for (int r = r0; r < r1; ++r) {
     float v[8];
     value8(r, v);
     uint32_t lo = 0, hi = 0;
+    V16 o;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t cd = sc[i] > 0.f ? f32_to_e4m3(v[i] / sc[i]) : 0u;
-      if (i < 4) lo |= cd << (8 * i); else hi |= cd << (8 * (i - 4));
+      if constexpr (DEQ) o.h[i] = f2bf(e4m3_to_f32(cd) * sc[i]);
+      else if (i < 4) lo |= cd << (8 * i);
+      else hi |= cd << (8 * (i - 4));
     }
-    *(uint2*)(codes + (size_t)r * cols + c0) = make_uint2(lo, hi);
+    if constexpr (DEQ) *(uint4*)(deq + (size_t)r * cols + c0) = o.u;
+    else *(uint2*)(codes + (size_t)r * cols + c0) = make_uint2(lo, hi);
   }
 }
 
@@ -518,9 +528,19 @@ int launch_quant_tok(const uint16_t* src, int ld, const int32_t* map, int gather
                      float* scales, hipStream_t st) {
   const long long n = (long long)((rows + brows - 1) / brows) * (cols / 8);
   if (n > 0)
-    hipLaunchKernelGGL(k_quant_tok, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src, ld,
-                       map, gather, div, rscale, rows, cols, brows, codes, scales);
+    hipLaunchKernelGGL(k_quant_tok<false>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src,
+                       ld, map, gather, div, rscale, rows, cols, brows, codes, scales, nullptr);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// The same blocks, written back as bf16 code * scale into deq [rows][cols].
+static void launch_quant_dequant(const uint16_t* src, int ld, const int32_t* map, int gather,
+                                 int div, const float* rscale, int rows, int cols, int brows,
+                                 uint16_t* deq, hipStream_t st) {
+  const long long n = (long long)((rows + brows - 1) / brows) * (cols / 8);
+  if (n > 0)
+    hipLaunchKernelGGL(k_quant_tok<true>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src,
+                       ld, map, gather, div, rscale, rows, cols, brows, nullptr, nullptr, deq);
 }
 
 // fp8 weight rows read K-major: element (k, n) = code[k * ld + n] * scale[k / 128][n / 128],
@@ -903,6 +923,9 @@ struct MnFixed {
   MOE_DEV uint32_t post(Raw raw, int) const { return raw * ld2 + col2; }
 };
 using MnFixedOp = MnKOperand<MnW, MnFixed>;
+// e4m3 K-major weights (dA, dX)
+using MnF8 = MnKFp8<256, kWNW, kRowBK>;
+using MnF8Op = MnKOperand<MnF8, MnFixed>;
 
 // e4m3 weight rows for the wide tile (the stream widens them to bf16)
 using RowF8 = RowKFp8<256, kWNW, kRowBK>;
@@ -1020,15 +1043,28 @@ template <bool FP8> struct SrcFc2T : MSrcBase {
 
 // dA = p * dy W2 (W2 [d][d_ff] read K-major through transpose reads), then
 // dZ = [dA U s (1 + G (1 - s)), dA G s] with s = sigmoid(G), and the gated
-// activation P = p SiLU(G) U for the weight gradient of W2.
-struct SrcDa : MSrcBase {
+// activation P = p SiLU(G) U for the weight gradient of W2.  With e4m3
+// weights the weight gradient of W2 takes the requantized D = p dy instead,
+// so P is written without the gate.
+template <bool FP8> struct SrcDaT : MSrcBase {
   using Item = MItem;
+  using OB = typename std::conditional<FP8, MnF8Op, MnFixedOp>::type;
   MOE_DEV void fill(const Item& it, int slot) const { fill_rows(it, slot); fill_gates(it, slot); }
   MOE_DEV RowW opA(const Item& it, int slot) const { return gathered(it, slot, a.dy, a.d); }
-  MOE_DEV MnFixedOp opB(const Item& it, int) const {
-    const MnW m{make_rsrc((const uint16_t*)a.w2 + (size_t)it.e * a.d * a.dff,
-                          (uint32_t)((size_t)2 * a.d * a.dff))};
-    return {m, MnFixed{(uint32_t)a.dff * 2u, (uint32_t)it.nj * WC::BN * 2u}};
+  MOE_DEV OB opB(const Item& it, int) const {
+    if constexpr (FP8) {   // W2 [d][d_ff] codes; scale block (kt / 2, 2 nj + wn / 2)
+      MnF8 m;
+      m.rs = make_rsrc((const uint8_t*)a.w2 + (size_t)it.e * a.d * a.dff, (uint32_t)((size_t)a.d * a.dff));
+      const int wn = wave_id() % WC::WAVES_N;
+      m.sp = (const MOE_CONST float*)a.w2s + (size_t)it.e * (a.d / 128) * (a.dff / 128) +
+             (2 * it.nj + wn / 2);
+      m.sld = a.dff / 128;
+      return {m, MnFixed{(uint32_t)a.dff, (uint32_t)it.nj * WC::BN}};
+    } else {
+      const MnW m{make_rsrc((const uint16_t*)a.w2 + (size_t)it.e * a.d * a.dff,
+                            (uint32_t)((size_t)2 * a.d * a.dff))};
+      return {m, MnFixed{(uint32_t)a.dff * 2u, (uint32_t)it.nj * WC::BN * 2u}};
+    }
   }
   MOE_DEV int steps(const Item&) const { return a.d / kRowBK; }
   // per 32 x 32 block: 8 [G, U] loads and three row-store runs
@@ -1087,7 +1123,7 @@ struct SrcDa : MSrcBase {
             const float sg = sigm(gv);
             if (which == 0) v[q] = pg * acc[i][j][4 * g + q] * uv * sg * (1.f + gv * (1.f - sg));
             else if (which == 1) v[q] = pg * acc[i][j][4 * g + q] * gv * sg;
-            else v[q] = pg * (gv * sg * uv);
+            else v[q] = (FP8 ? 1.f : pg) * (gv * sg * uv);
           }
           p[0][g] = u32x2_t{(uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16),
                             (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16)};
@@ -1106,14 +1142,26 @@ struct SrcDa : MSrcBase {
 };
 
 // dX per routed row: dZ W1 (W1 [2 d_ff][d] read K-major through transpose reads).
-struct SrcDx : MSrcBase {
+template <bool FP8> struct SrcDxT : MSrcBase {
   using Item = MItem;
+  using OB = typename std::conditional<FP8, MnF8Op, MnFixedOp>::type;
   MOE_DEV void fill(const Item&, int) const {}
   MOE_DEV RowW opA(const Item& it, int) const { return slotrows(it, a.bufA, 2 * a.dff); }
-  MOE_DEV MnFixedOp opB(const Item& it, int) const {
-    const MnW m{make_rsrc((const uint16_t*)a.w1 + (size_t)it.e * 2 * a.dff * a.d,
-                          (uint32_t)((size_t)4 * a.dff * a.d))};
-    return {m, MnFixed{(uint32_t)a.d * 2u, (uint32_t)it.nj * WC::BN * 2u}};
+  MOE_DEV OB opB(const Item& it, int) const {
+    if constexpr (FP8) {   // W1 [2 d_ff][d] codes; scale block (kt / 2, 2 nj + wn / 2)
+      MnF8 m;
+      m.rs = make_rsrc((const uint8_t*)a.w1 + (size_t)it.e * 2 * a.dff * a.d,
+                       (uint32_t)((size_t)2 * a.dff * a.d));
+      const int wn = wave_id() % WC::WAVES_N;
+      m.sp = (const MOE_CONST float*)a.w1s + (size_t)it.e * (2 * a.dff / 128) * (a.d / 128) +
+             (2 * it.nj + wn / 2);
+      m.sld = a.d / 128;
+      return {m, MnFixed{(uint32_t)a.d, (uint32_t)it.nj * WC::BN}};
+    } else {
+      const MnW m{make_rsrc((const uint16_t*)a.w1 + (size_t)it.e * 2 * a.dff * a.d,
+                            (uint32_t)((size_t)4 * a.dff * a.d))};
+      return {m, MnFixed{(uint32_t)a.d * 2u, (uint32_t)it.nj * WC::BN * 2u}};
+    }
   }
   MOE_DEV int steps(const Item&) const { return 2 * a.dff / kRowBK; }
   static constexpr int kEpiVm = WC::MB * RowStore<uint16_t, 2>::STORES;
@@ -1311,7 +1359,10 @@ using MnSegOp = MnSegOpT<DwCfg>;
 constexpr size_t kDwLds = kStreamLds;
 
 struct DwItem { int e, slot0, nrows, dst, is2, mi, nj; };
-template <class C> struct SrcDwT {
+// With e4m3 weights (FP8) dW2's left operand is the requantized D, widened
+// back to bf16 per slot (dhat), and P holds SiLU(G) U without the gate; dZ
+// in bufA has been requantized in place.
+template <class C, bool FP8 = false> struct SrcDwT {
   using Item = DwItem;
   using MnC = MnK<C::BN, C::NT / 64, kDwBK>;
   static_assert(C::BM == C::BN, "one MN operand type for both sides");
@@ -1319,7 +1370,7 @@ template <class C> struct SrcDwT {
   ExecArgs a;              // a copy: the fields stay in scalar registers
   MOE_LDS uint16_t* smem;
   int r, n2m, n2n, n1m, n1n, per_seg, count, first, stride;
-  BufRsrc r_dy, r_x, r_dz, r_p;
+  BufRsrc r_dy, r_x, r_dz, r_p, r_dh;
   MOE_DEV void init(const ExecArgs& args, MOE_LDS uint16_t* sm, int) {
     a = args;
     smem = sm;
@@ -1336,6 +1387,7 @@ template <class C> struct SrcDwT {
     r_x = make_rsrc(args.x, bx);
     r_dz = make_rsrc(args.bufA, (uint32_t)(args.slots * 4 * args.dff));
     r_p = make_rsrc(args.bufP, (uint32_t)(args.slots * 2 * args.dff));
+    if constexpr (FP8) r_dh = make_rsrc(args.dhat, (uint32_t)(args.slots * 2 * args.d));
   }
   MOE_DEV Item load(int idx) const {
     const u32x4_t sg = ((const MOE_CONST u32x4_t*)a.seg)[(size_t)r * a.E + idx / per_seg];
@@ -1347,10 +1399,10 @@ template <class C> struct SrcDwT {
   }
   MOE_DEV void fill(const Item&, int) const {}
   MOE_DEV MnSegOpT<C> opA(const Item& it, int) const {
-    const MnC m{it.is2 ? r_dy : r_dz};
+    const MnC m{it.is2 ? (FP8 ? r_dh : r_dy) : r_dz};
     const int ld = it.is2 ? a.d : 2 * a.dff;
     return {m, MnSeg{a.slot_to_row, a.kmagic, (uint32_t)ld * 2u, (uint32_t)it.mi * C::BM * 2u,
-                     it.slot0, it.nrows, it.is2}};
+                     it.slot0, it.nrows, FP8 ? 0 : it.is2}};
   }
   MOE_DEV MnSegOpT<C> opB(const Item& it, int) const {
     const MnC m{it.is2 ? r_p : r_x};
@@ -1392,7 +1444,6 @@ template <class C> struct SrcDwT {
   }
 };
 
-using SrcDw = SrcDwT<DwCfg>;
 
 // per-slot gate p (0 for padding slots), read by FC2 and dA through LDS
 __global__ __launch_bounds__(256) void k_slot_gate(const int32_t* __restrict__ slot_to_row,
@@ -1469,8 +1520,10 @@ WsLayout exec_layout(const Sizes& z, bool backward) {
   L.rslots = backward ? take(sizeof(float) * (size_t)z.P * z.s * 3 * z.d * z.dff) : o;
   L.bufP = backward ? take((size_t)z.act_bytes * z.max_slots * z.dff) : o;
   L.sgate = take(sizeof(float) * z.max_slots);
-  L.dq = L.dqs = L.zq = L.zqs = o;
-  if (backward && z.fp8) {
+  L.dq = L.dqs = L.zq = L.zqs = L.dhat = o;
+  if (backward && z.fp8 && use_stream(z)) {
+    L.dhat = take((size_t)2 * z.max_slots * z.d);           // requantized D as bf16
+  } else if (backward && z.fp8) {
     const size_t nblk = (z.max_slots + z.beta - 1) / z.beta;
     L.dq = take(z.max_slots * (size_t)z.d);
     L.dqs = take(sizeof(float) * nblk * z.d);
@@ -1574,6 +1627,7 @@ static ExecArgs make_exec(const Sizes& z, const LayerPtrs& Lp, char* ws, const W
     a.dqs = (float*)(ws + L.dqs);
     a.zq = (uint8_t*)(ws + L.zq);
     a.zqs = (float*)(ws + L.zqs);
+    a.dhat = ws + L.dhat;
   }
   return a;
 }
@@ -1667,19 +1721,30 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+// With e4m3 weights (FP8): D = p dy per slot is requantized along the tokens
+// and widened back to bf16 (dhat) before dA; dZ is requantized in place in
+// bufA once dX has used it; the weight gradients then read both as bf16.
+template <bool FP8>
 static void run_backward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* dx,
                                 float* dw1, float* dw2, void* const* ev, hipStream_t st) {
+  const int rows = (int)z.max_slots;
   launch_slot_gate(z, a, st);
-  launch_stream<SrcDa, WC, RowW, MnFixedOp>(a, z.dff / WC::BN, kStreamLds, st);
+  if constexpr (FP8)
+    launch_quant_dequant((const uint16_t*)a.dy, z.d, a.slot_to_row, 1, z.k, a.gates, rows, z.d,
+                         z.beta, (uint16_t*)a.dhat, st);
+  launch_stream<SrcDaT<FP8>, WC, RowW, typename SrcDaT<FP8>::OB>(a, z.dff / WC::BN, kStreamLds, st);
   rec(ev, 2, st);
-  launch_stream<SrcDx, WC, RowW, MnFixedOp>(a, z.d / WC::BN, kStreamLds, st);
+  launch_stream<SrcDxT<FP8>, WC, RowW, typename SrcDxT<FP8>::OB>(a, z.d / WC::BN, kStreamLds, st);
   rec(ev, 3, st);
   const long long nth = (long long)z.T * (z.d / 8);
   if (nth > 0)
     hipLaunchKernelGGL(k_combine<uint16_t>, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, st,
                        (const uint16_t*)a.bufO, row_to_slot, z.T, z.k, z.d, (uint16_t*)dx);
   rec(ev, 4, st);
-  launch_stream<SrcDw, DwCfg, MnSegOp, MnSegOp>(a, 0, kDwLds, st);
+  if constexpr (FP8)
+    launch_quant_dequant((const uint16_t*)a.bufA, 2 * z.dff, a.slot_to_row, 0, 1, nullptr, rows,
+                         2 * z.dff, z.beta, (uint16_t*)a.bufA, st);
+  launch_stream<SrcDwT<DwCfg, FP8>, DwCfg, MnSegOp, MnSegOp>(a, 0, kDwLds, st);
   rec(ev, 5, st);
   hipLaunchKernelGGL(k_bwd_reduce, dim3(num_cus() * 4), dim3(256), 0, st, a.rep_slot,
                      a.owner_has, (const float*)a.rslots, z.E, z.P, z.d, z.dff, dw1, dw2);
@@ -1733,9 +1798,10 @@ int launch_backward(const Sizes& z, const LayerPtrs& Lp, const void* x, const fl
   a.dy = dy; a.dw1 = dw1; a.dw2 = dw2;
   if (Lp.act_dtype == MOE_F32) run_backward<float, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else if (Lp.w_dtype == MOE_FP8_E4M3) {
-    if (use_big_tiles(z)) run_backward<uint16_t, BigCfg, true>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
+    if (use_stream(z)) run_backward_stream<true>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
+    else if (use_big_tiles(z)) run_backward<uint16_t, BigCfg, true>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
     else run_backward<uint16_t, SmallCfg, true>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
-  } else if (use_stream(z)) run_backward_stream(z, a, row_to_slot, dx, dw1, dw2, ev, st);
+  } else if (use_stream(z)) run_backward_stream<false>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else if (use_big_tiles(z)) run_backward<uint16_t, BigCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else run_backward<uint16_t, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;

@@ -709,6 +709,7 @@ template <int MN, int NWAVES, int BK_> struct MnK {
   static_assert(NI * RPI * NWAVES == BK, "K rows per stage");
   BufRsrc rs;
   struct Offs { uint32_t o[NI]; };
+  static MOE_DEV int chunk_swz(int row) { return swz_tr(row); }
   // stage row (K index within the step) loaded by this lane's instruction i
   static MOE_DEV int row_of(int i) { return ((threadIdx.x >> 6) + NWAVES * i) * RPI + (threadIdx.x & 63) / CPR; }
   // first of the RPI rows of instruction i (wave-uniform)
@@ -752,6 +753,64 @@ template <int MN, int NWAVES, int BK_> struct MnK {
   }
 };
 
+// MN-contiguous e4m3 operand with 128 x 128 block scales: BK K rows x MN
+// codes per stage, [k][MN bytes]; 16-byte chunk c of stage row r sits at chunk
+// c ^ 2 (r & 7).  Fragments through ds_read_b64_tr_b8: inside each 16-lane
+// group, lane j supplies the address of row k0 + j/2, codes m0 + 8 (j % 2) ..
+// +7, and receives code m0 + j of rows k0 .. k0+7 (byte i from row k0 + i),
+// i.e. the eight consecutive K values an MFMA lane needs, in one read.  The 8
+// rows one 32-lane half of a read touches then cover all 16 chunk positions
+// of a 256-byte bank window.  A wave's 64 columns and a K step lie inside one
+// scale block: scale(j, kt) = sp[(kt * BK / 128) * sld] for both blocks j.
+template <int MN, int NWAVES, int BK_> struct MnKFp8 {
+  static constexpr bool kFp8 = true;
+  static constexpr int BK = BK_;
+  static constexpr int ROWB = MN;                   // one code per element
+  static constexpr int RPI = 1024 / ROWB;
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int NI = BK / RPI / NWAVES;
+  static constexpr int STAGE_BYTES = BK * ROWB;
+  static_assert(NI * RPI * NWAVES == BK, "K rows per stage");
+  static_assert(CPR == 16, "chunk swizzle spans 16 chunks");
+  BufRsrc rs;
+  const MOE_CONST float* sp;
+  int sld;
+  struct Offs { uint32_t o[NI]; };
+  static MOE_DEV int chunk_swz(int row) { return 2 * (row & 7); }
+  static MOE_DEV int row_of(int i) { return ((threadIdx.x >> 6) + NWAVES * i) * RPI + (threadIdx.x & 63) / CPR; }
+  static MOE_DEV int row_base(int i) { return (wave_id() + NWAVES * i) * RPI; }
+  MOE_DEV void issue(const Offs& p, MOE_LDS char* st) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      buf_load_lds16(rs, p.o[i], (MOE_LDS void*)(st + (w + NWAVES * i) * RPI * ROWB));
+  }
+  MOE_DEV float scale(int, int kt) const { return sp[(kt / (128 / BK)) * sld]; }
+  // Block j: lane j' of 16-lane group G covers column wave_base + 32 j +
+  // 16 (G & 1) + j' and K rows 16 KC + 8 (G >> 1) .. +7; it addresses row
+  // 16 KC + 8 (G >> 1) + j'/2, whose swizzle 2 (j'/2) depends on the lane only.
+  struct Lane { uint32_t off[2]; };
+  static MOE_DEV Lane lane_info(int wave_base, int lane) {
+    const int G = lane >> 4, jl = lane & 15;
+    const int row = 8 * (G >> 1) + (jl >> 1);
+    Lane L;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = (wave_base + 32 * j) / 16 + (G & 1);
+      L.off[j] = (uint32_t)(row * ROWB + ((c ^ chunk_swz(row)) << 4) + 8 * (jl & 1));
+    }
+    return L;
+  }
+  // Issued from inline asm, like MnK::frag: consumed after an explicit
+  // lgkmcnt(0) wait.
+  template <int KC> static MOE_DEV u32x2_t codes(const MOE_LDS char* st, const Lane& L, int j) {
+    u32x2_t v;
+    asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2"
+                 : "=v"(v) : "v"(st + L.off[j & 1]), "i"(KC * 16 * ROWB));
+    return v;
+  }
+};
+
 // MN-contiguous operand bound to its row function.  F::pre(k) gives a raw
 // value for K index k (an index, or a value loaded from memory, not yet
 // combined with anything, so no wait is needed until the loads are issued),
@@ -762,6 +821,7 @@ template <class OP, class F> struct MnKOperand {
   OP op;
   F f;
   static constexpr int BK = OP::BK, NI = OP::NI, STAGE_BYTES = OP::STAGE_BYTES;
+  static constexpr bool kFp8 = op_fp8<OP>::value;
   using Lane = typename OP::Lane;
   // f.pre(kb, k): what post needs for the lane's K row k, where kb is the
   // wave-uniform first row of the same instruction
@@ -778,7 +838,7 @@ template <class OP, class F> struct MnKOperand {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int r = OP::row_of(i);
-      q.o[i] = f.post(p.raw[i], p.kt * BK + r) + (uint32_t)(((threadIdx.x & 63) % OP::CPR) ^ swz_tr(r)) * 16u;
+      q.o[i] = f.post(p.raw[i], p.kt * BK + r) + (uint32_t)(((threadIdx.x & 63) % OP::CPR) ^ OP::chunk_swz(r)) * 16u;
     }
     op.issue(q, st);
   }
@@ -786,6 +846,10 @@ template <class OP, class F> struct MnKOperand {
   template <int KC> static MOE_DEV bf16x8_t frag(const MOE_LDS char* st, const Lane& L, int i) {
     return OP::template frag<KC>(st, L, i);
   }
+  template <int KC> static MOE_DEV u32x2_t codes(const MOE_LDS char* st, const Lane& L, int j) {
+    return OP::template codes<KC>(st, L, j);
+  }
+  MOE_DEV float scale(int j, int kt) const { return op.scale(j, kt); }
 };
 // ---- wide tile, persistent across tiles -------------------------------------
 // K runs in steps of BK (32 or 64) over S = wide_stages(BK) LDS stages; step

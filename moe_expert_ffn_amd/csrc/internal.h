@@ -27,11 +27,13 @@ struct Sizes {
 struct WsLayout {
   size_t ctr, mt_cnt, mt, seg_cnt, seg, rep_slot, owner_has, bufA, bufO, rslots, bufP, sgate;
   size_t dq, dqs, zq, zqs;   // fp8 backward: token-axis e4m3 codes and scales of D and dZ
+  size_t dhat;               // fp8 backward on the stream kernels: requantized D as bf16
   size_t total;
 };
 
 WsLayout exec_layout(const Sizes& z, bool backward);
 bool use_big_tiles(const Sizes& z);
+bool use_stream(const Sizes& z);
 size_t max_tiles(const Sizes& z);
 size_t route_ws_bytes(int T, int k, int E);
 
