@@ -259,7 +259,8 @@ int moe_backward(const moe_layer* L, const void* x, const float* gates, const vo
  * row_scale = gates it forms D = p * dy per slot; without, it masks padding).
  *   src bf16, device; codes [rows][cols] uint8; scales
  *   [ceil(rows / block_rows)][cols] fp32; all device pointers, caller-owned.
- * Errors: MOE_ERR_ARG for rows < 0, cols < 8 or not a multiple of 8,
+ * Errors: MOE_ERR_ARG for rows < 0, cols < 8, not a multiple of 8 or above
+ *   8,388,480 (65535 tiles of 128 columns),
  *   ld < cols or not a multiple of 8, block_rows < 1, row_div < 1, or a null
  *   src/codes/scales. */
 int moe_quantize_token_blocks(const void* src, int ld, const int32_t* row_map, int gather,

@@ -146,7 +146,8 @@ int moe_plan_gate(const int32_t* block_counts, const int32_t* block_offsets, con
 int moe_quantize_token_blocks(const void* src, int ld, const int32_t* row_map, int gather,
                               int row_div, const float* row_scale, int rows, int cols,
                               int block_rows, uint8_t* codes, float* scales, void* stream) {
-  if (rows < 0 || cols < 8 || cols % 8 || ld < cols || ld % 8 || block_rows < 1 || row_div < 1)
+  if (rows < 0 || cols < 8 || cols % 8 || cols > kQtMaxCols || ld < cols || ld % 8 ||
+      block_rows < 1 || row_div < 1)
     return MOE_ERR_ARG;
   if (!src || !codes || !scales) return MOE_ERR_ARG;
   return launch_quant_tok((const uint16_t*)src, ld, row_map, gather ? 1 : 0, row_div, row_scale,

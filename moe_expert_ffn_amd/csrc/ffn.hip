@@ -221,6 +221,7 @@ struct ExecArgs {
   float* zqs;             //   its scales [slots / beta][2 d_ff]
   void* dhat;             // fp8 backward on the stream kernels: D requantized and
                           //   widened back to bf16, [slots][d]
+  const int32_t* boff;    // block offsets [E + 1]: boff[E] blocks of beta slots are in use
 };
 
 enum { PH_FC1 = 0, PH_FC2 = 1, PH_DA = 2, PH_DX = 3, PH_DW = 4 };
@@ -437,110 +438,154 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ src,
 //   map == nullptr: src[r * ld + c]
 //   map[r] < 0:     0
 //   otherwise:      src[(gather ? map[r] / div : r) * ld + c] * (rscale ? rscale[map[r]] : 1).
-MOE_DEV uint32_t f32_to_e4m3(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fminf(fabsf(v), 448.f);
-  const uint32_t x = __float_as_uint(a);
-  const int ex = (int)(x >> 23) - 127;
-  const uint32_t mant = (x & 0x7FFFFFu) | 0x800000u;         // 1.m with the implicit bit
-  if (ex >= -6) {                                             // normal: keep 3 fraction bits
-    uint32_t q = mant >> 20;
-    const uint32_t rem = mant & 0xFFFFFu;
-    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
-    int e = ex;
-    if (q == 16u) { q = 8u; ++e; }
-    return sign | ((uint32_t)(e + 7) << 3) | (q - 8u);
-  }
-  // subnormal: value = q * 2^-9 (q == 8 carries into the smallest normal)
-  const int sh = 20 + (-6 - ex);
-  if (sh > 24) return sign;                                   // below half of 2^-9: rounds to 0
-  uint32_t q = mant >> sh;
-  const uint32_t rem = mant & ((1u << sh) - 1u), half = 1u << (sh - 1);
-  if (rem > half || (rem == half && (q & 1u))) ++q;
-  return sign | q;
-}
-
+// One workgroup per (block b, 128 columns): 16 threads cover a row's 128
+// columns (8 each) and 16 rows are read at once.  Pass 1 takes each column's
+// amax over the block's rows (exact in any order), reduced through LDS; pass
+// 2 encodes.  A thread keeps its first kQtKeep rows (a 128-row block) in
+// registers between the passes; rows beyond them are read again.  Row reads
+// are branchless (a masked row loads row 0 and selects +0), so a thread's
+// rows are all in flight at once.
 // DEQ: instead of codes and scales, write code * scale as bf16 to deq
-// [rows][cols] (which may be src itself: a thread reads each of its values
-// before it overwrites them).
+// [rows][cols] (which may be src itself: pass 2 reads each value before the
+// same thread overwrites it, and workgroups cover disjoint tiles).
+// blk_end (nullable, device): only blocks b < *blk_end are processed; the
+// layer passes the number of blocks in use, so the slot capacity beyond them
+// costs one early exit per workgroup.
+constexpr int kQtCols = 128, kQtRowLanes = 16, kQtKeep = 8;
 template <bool DEQ>
 __global__ __launch_bounds__(256) void k_quant_tok(const uint16_t* src, int ld,
                                                    const int32_t* __restrict__ map, int gather, int div,
                                                    const float* __restrict__ rscale, int rows,
                                                    int cols, int brows, uint8_t* codes,
-                                                   float* scales, uint16_t* deq) {
-  const int nch = cols / 8, nblk = (rows + brows - 1) / brows;
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long long)nblk * nch) return;
-  const int b = (int)(idx / nch), c0 = (int)(idx % nch) * 8;
+                                                   float* scales, uint16_t* deq,
+                                                   const int32_t* __restrict__ blk_end) {
+  __shared__ float part[kQtRowLanes][kQtCols];
+  __shared__ float bsc[kQtCols];
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  const int b = blockIdx.x, c0 = blockIdx.y * kQtCols + tx * 8;
+  if (blk_end && b >= *blk_end) return;                   // whole workgroup, before any barrier
+  const bool colok = c0 < cols;
   const int r0 = b * brows, r1 = min(rows, r0 + brows);
   auto value8 = [&](int r, float* v) {
-    const uint16_t* row;
+    int srow = r;
+    bool ok = true;
     float f = 1.f;
     if (map) {
       const int m = map[r];
-      if (m < 0) { for (int i = 0; i < 8; ++i) v[i] = 0.f; return; }
-      row = src + (size_t)(gather ? m / div : r) * ld;
-      if (rscale) f = rscale[m];
-    } else {
-      row = src + (size_t)r * ld;
+      ok = m >= 0;
+      if (gather) srow = ok ? m / div : 0;
+      if (rscale) f = rscale[ok ? m : 0];
     }
-    const uint4 q = *(const uint4*)(row + c0);
+    const uint4 q = *(const uint4*)(src + (size_t)srow * ld + c0);
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16) * f;
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u) * f;
+      v[2 * i] = ok ? __uint_as_float(w[i] << 16) * f : 0.f;
+      v[2 * i + 1] = ok ? __uint_as_float(w[i] & 0xFFFF0000u) * f : 0.f;
     }
   };
+  // v_cvt_pk_fp8_f32 rounds to nearest even on the OCP e4m3 grid: checked on
+  // MI355X against a bit-level round-to-nearest-even encoder on every fp32
+  // value of magnitude below 464, which covers every finite quotient here
+  // (|v| <= amax, so |v / scale| <= 448 up to rounding)
+  auto encode = [&](int r, const float* v, const float* sc) {
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = sc[i] > 0.f ? v[i] / sc[i] : 0.f;
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int p = __builtin_amdgcn_cvt_pk_fp8_f32(q[4 * h], q[4 * h + 1], 0, false);
+      p = __builtin_amdgcn_cvt_pk_fp8_f32(q[4 * h + 2], q[4 * h + 3], p, true);
+      w[h] = (uint32_t)p;
+    }
+    if constexpr (DEQ) {
+      V16 o;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], false);
+        const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], true);
+        o.h[4 * h + 0] = f2bf(lo[0] * sc[4 * h + 0]);
+        o.h[4 * h + 1] = f2bf(lo[1] * sc[4 * h + 1]);
+        o.h[4 * h + 2] = f2bf(hi[0] * sc[4 * h + 2]);
+        o.h[4 * h + 3] = f2bf(hi[1] * sc[4 * h + 3]);
+      }
+      *(uint4*)(deq + (size_t)r * cols + c0) = o.u;
+    } else {
+      *(uint2*)(codes + (size_t)r * cols + c0) = make_uint2(w[0], w[1]);
+    }
+  };
+  float keep[kQtKeep][8];
   float amax[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int r = r0; r < r1; ++r) {
-    float v[8];
-    value8(r, v);
+  if (colok) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax[i] = fmaxf(amax[i], fabsf(v[i]));
-  }
-  float sc[8];
+    for (int u = 0; u < kQtKeep; ++u) {
+      const int r = r0 + ty + kQtRowLanes * u;
+      if (r < r1) {
+        value8(r, keep[u]);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    sc[i] = amax[i] / 448.f;
-    if constexpr (!DEQ) scales[(size_t)b * cols + c0 + i] = sc[i];
+        for (int i = 0; i < 8; ++i) amax[i] = fmaxf(amax[i], fabsf(keep[u][i]));
+      }
+    }
+    for (int r = r0 + ty + kQtRowLanes * kQtKeep; r < r1; r += kQtRowLanes) {
+      float v[8];
+      value8(r, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax[i] = fmaxf(amax[i], fabsf(v[i]));
+    }
   }
-  for (int r = r0; r < r1; ++r) {
-    float v[8];
-    value8(r, v);
-    uint32_t lo = 0, hi = 0;
-    V16 o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) part[ty][tx * 8 + i] = amax[i];
+  __syncthreads();
+  if (ty == 0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t cd = sc[i] > 0.f ? f32_to_e4m3(v[i] / sc[i]) : 0u;
-      if constexpr (DEQ) o.h[i] = f2bf(e4m3_to_f32(cd) * sc[i]);
-      else if (i < 4) lo |= cd << (8 * i);
-      else hi |= cd << (8 * (i - 4));
+      float m = part[0][tx * 8 + i];
+      for (int y = 1; y < kQtRowLanes; ++y) m = fmaxf(m, part[y][tx * 8 + i]);
+      const float sc = m / 448.f;
+      bsc[tx * 8 + i] = sc;
+      if constexpr (!DEQ)
+        if (colok) scales[(size_t)b * cols + c0 + i] = sc;
     }
-    if constexpr (DEQ) *(uint4*)(deq + (size_t)r * cols + c0) = o.u;
-    else *(uint2*)(codes + (size_t)r * cols + c0) = make_uint2(lo, hi);
   }
+  __syncthreads();
+  if (!colok) return;
+  float sc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sc[i] = bsc[tx * 8 + i];
+#pragma unroll
+  for (int u = 0; u < kQtKeep; ++u) {
+    const int r = r0 + ty + kQtRowLanes * u;
+    if (r < r1) encode(r, keep[u], sc);
+  }
+  for (int r = r0 + ty + kQtRowLanes * kQtKeep; r < r1; r += kQtRowLanes) {
+    float v[8];
+    value8(r, v);
+    encode(r, v, sc);
+  }
+}
+
+// blocks on x (up to 2^31 - 1), 128-column tiles on y (cols <= kQtMaxCols)
+static dim3 quant_grid(int rows, int cols, int brows) {
+  return dim3((unsigned)((rows + brows - 1) / brows), (unsigned)((cols + kQtCols - 1) / kQtCols));
 }
 
 int launch_quant_tok(const uint16_t* src, int ld, const int32_t* map, int gather, int div,
                      const float* rscale, int rows, int cols, int brows, uint8_t* codes,
-                     float* scales, hipStream_t st) {
-  const long long n = (long long)((rows + brows - 1) / brows) * (cols / 8);
-  if (n > 0)
-    hipLaunchKernelGGL(k_quant_tok<false>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src,
-                       ld, map, gather, div, rscale, rows, cols, brows, codes, scales, nullptr);
+                     float* scales, hipStream_t st, const int32_t* blk_end) {
+  if (rows > 0)
+    hipLaunchKernelGGL(k_quant_tok<false>, quant_grid(rows, cols, brows), dim3(256), 0, st, src, ld,
+                       map, gather, div, rscale, rows, cols, brows, codes, scales, nullptr, blk_end);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 // The same blocks, written back as bf16 code * scale into deq [rows][cols].
 static void launch_quant_dequant(const uint16_t* src, int ld, const int32_t* map, int gather,
                                  int div, const float* rscale, int rows, int cols, int brows,
-                                 uint16_t* deq, hipStream_t st) {
-  const long long n = (long long)((rows + brows - 1) / brows) * (cols / 8);
-  if (n > 0)
-    hipLaunchKernelGGL(k_quant_tok<true>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src,
-                       ld, map, gather, div, rscale, rows, cols, brows, nullptr, nullptr, deq);
+                                 uint16_t* deq, const int32_t* blk_end, hipStream_t st) {
+  if (rows > 0)
+    hipLaunchKernelGGL(k_quant_tok<true>, quant_grid(rows, cols, brows), dim3(256), 0, st, src, ld,
+                       map, gather, div, rscale, rows, cols, brows, nullptr, nullptr, deq, blk_end);
 }
 
 // fp8 weight rows read K-major: element (k, n) = code[k * ld + n] * scale[k / 128][n / 128],
@@ -1731,7 +1776,7 @@ static void run_backward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_
   launch_slot_gate(z, a, st);
   if constexpr (FP8)
     launch_quant_dequant((const uint16_t*)a.dy, z.d, a.slot_to_row, 1, z.k, a.gates, rows, z.d,
-                         z.beta, (uint16_t*)a.dhat, st);
+                         z.beta, (uint16_t*)a.dhat, a.boff + z.E, st);
   launch_stream<SrcDaT<FP8>, WC, RowW, typename SrcDaT<FP8>::OB>(a, z.dff / WC::BN, kStreamLds, st);
   rec(ev, 2, st);
   launch_stream<SrcDxT<FP8>, WC, RowW, typename SrcDxT<FP8>::OB>(a, z.d / WC::BN, kStreamLds, st);
@@ -1743,7 +1788,7 @@ static void run_backward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_
   rec(ev, 4, st);
   if constexpr (FP8)
     launch_quant_dequant((const uint16_t*)a.bufA, 2 * z.dff, a.slot_to_row, 0, 1, nullptr, rows,
-                         2 * z.dff, z.beta, (uint16_t*)a.bufA, st);
+                         2 * z.dff, z.beta, (uint16_t*)a.bufA, a.boff + z.E, st);
   launch_stream<SrcDwT<DwCfg, FP8>, DwCfg, MnSegOp, MnSegOp>(a, 0, kDwLds, st);
   rec(ev, 5, st);
   hipLaunchKernelGGL(k_bwd_reduce, dim3(num_cus() * 4), dim3(256), 0, st, a.rep_slot,
@@ -1762,11 +1807,11 @@ static void run_backward(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot
   const int rows = (int)z.max_slots;
   if constexpr (FP8)   // D = p * dy per slot, e4m3 along tokens, for dW2
     launch_quant_tok((const uint16_t*)a.dy, z.d, a.slot_to_row, 1, z.k, a.gates, rows, z.d, z.beta,
-                     a.dq, a.dqs, st);
+                     a.dq, a.dqs, st, a.boff + z.E);
   hipLaunchKernelGGL((k_bwd_da<T, C, FP8>), dim3(ga), dim3(C::NT), lds, st, a);
   if constexpr (FP8)   // dZ per slot (padding slots read as zero), for dW1
     launch_quant_tok((const uint16_t*)a.bufA, 2 * z.dff, a.slot_to_row, 0, 1, nullptr, rows,
-                     2 * z.dff, z.beta, a.zq, a.zqs, st);
+                     2 * z.dff, z.beta, a.zq, a.zqs, st, a.boff + z.E);
   rec(ev, 2, st);
   hipLaunchKernelGGL((k_bwd_dx<T, C, FP8>), dim3(gx), dim3(C::NT), lds, st, a);
   rec(ev, 3, st);
@@ -1795,7 +1840,7 @@ int launch_backward(const Sizes& z, const LayerPtrs& Lp, const void* x, const fl
   ExecArgs a = make_exec(z, Lp, ws, L);
   a.x = x; a.gates = gates; a.slot_to_row = slot_to_row; a.row_to_slot = row_to_slot;
   a.z_save = const_cast<void*>(z_save);
-  a.dy = dy; a.dw1 = dw1; a.dw2 = dw2;
+  a.dy = dy; a.dw1 = dw1; a.dw2 = dw2; a.boff = boff;
   if (Lp.act_dtype == MOE_F32) run_backward<float, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else if (Lp.w_dtype == MOE_FP8_E4M3) {
     if (use_stream(z)) run_backward_stream<true>(z, a, row_to_slot, dx, dw1, dw2, ev, st);

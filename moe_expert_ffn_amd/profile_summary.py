@@ -22,6 +22,8 @@ import sys
 
 STAGE_OF = {"k_stream<SrcFc1>": "fwd.fc1", "k_stream<SrcFc2>": "fwd.fc2",
             "k_stream<SrcFc1Fp8>": "fwd.fc1", "k_stream<SrcFc2Fp8>": "fwd.fc2",
+            "k_stream<SrcDaFp8>": "bwd.dA", "k_stream<SrcDxFp8>": "bwd.dX",
+            "k_quant_tok": "bwd.dA (D) + bwd.dW (dZ)",
             "k_stream<SrcDa>": "bwd.dA", "k_stream<SrcDx>": "bwd.dX", "k_stream<SrcDwT>": "bwd.dW",
             "k_fc1": "fwd.fc1", "k_fc2": "fwd.fc2", "k_bwd_da": "bwd.dA", "k_bwd_dx": "bwd.dX",
             "k_bwd_dw": "bwd.dW", "k_bwd_reduce": "bwd.reduce",

@@ -111,6 +111,8 @@ def test_host_validation_errors():
     assert q(P, 16, None, 0, 0, None, 4, 16, 128, P, P, None) == B.MOE_ERR_ARG     # row_div
     assert q(None, 16, None, 0, 1, None, 4, 16, 128, P, P, None) == B.MOE_ERR_ARG  # src
     assert q(P, 16, None, 0, 1, None, 4, 16, 128, None, P, None) == B.MOE_ERR_ARG  # codes
+    big = 65535 * 128 + 8                                                            # > 65535 column tiles
+    assert q(P, big, None, 0, 1, None, 4, big, 128, P, P, None) == B.MOE_ERR_ARG
     ok = _layer()
     assert lib.moe_forward(ctypes.byref(ok), P, P, P, 4, 2, 16, 4, *([P] * 8), P, 16, None,
                            None) == B.MOE_ERR_WORKSPACE

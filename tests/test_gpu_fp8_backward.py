@@ -17,6 +17,7 @@ import torch
 from moe_expert_ffn_amd import binding as B
 from moe_expert_ffn_amd.inputs import WORKLOADS, Workload
 from oracle import ffn as offn
+from oracle.fp8 import decode_e4m3
 from oracle.fp8 import quantize_token_blocks as oq
 from tests.conftest import rel_l2
 from tests.gpu_util import Case, say
@@ -188,3 +189,27 @@ def test_fp8_backward_full_size_sampled(kappa):
     say(f"  experts={experts} rows={counts[experts].tolist()} dx={e[0]:.3e} dw1={e[1]:.3e} "
         f"dw2={e[2]:.3e}")
     assert max(e) <= TOL_FP8
+
+
+def test_quantize_rounding_ties():
+    """Scale exactly 1 (one 448 per column), so value / scale is exact: every
+    e4m3 grid midpoint (ties to even), its bf16 neighbours, subnormals and
+    both signs reach the encoder unchanged."""
+    say("[quant-ties]")
+    grid = np.array(sorted({float(v) for v in decode_e4m3(np.arange(127))}))
+    mids = (grid[:-1] + grid[1:]) / 2                     # exact in bf16: one more mantissa bit
+    m16 = torch.from_numpy(mids.astype(np.float32)).to(torch.bfloat16)
+    bits = m16.view(torch.int16)
+    below, above = (bits - 1).view(torch.bfloat16), (bits + 1).view(torch.bfloat16)   # bf16 neighbours
+    odd = torch.from_numpy((grid[:8] / 3).astype(np.float32)).to(torch.bfloat16)   # subnormal range
+    v16 = torch.cat([m16, below[1:], above, odd])          # below[0] would be the zero's neighbour
+    v16 = torch.cat([v16, -v16])
+    cols = 16
+    rows = 1 + v16.numel()
+    src = torch.zeros((rows, cols), dtype=torch.bfloat16)
+    src[0, :] = 448.0
+    for c in range(cols):
+        src[1:, c] = v16.roll(c)
+    codes, scales = _quant_dev(src, rows, cols, rows)
+    assert np.all(scales == 1.0)
+    _check_exact(codes, scales, src.float().numpy(), rows)
