@@ -52,7 +52,10 @@ def parse():
                     help="time every CU partition count P at every kappa next to the "
                          "wave-quantized cost model's prediction, and report the selector's regret")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens of the workload in the CPU oracle sample (0: all)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the CPU oracle sample until this much time has passed")
     return ap.parse_args()
 
 
@@ -230,38 +233,51 @@ def compare_planners(case, w, n=50):
     return out
 
 
-def cpu_baseline(case, w, tokens):
-    """The oracle, untuned, on the first `tokens` tokens of the same workload:
-    forward of those tokens plus their dx, and dW of every expert over their
-    rows.  Useful TFLOP/s of that sample."""
+def cpu_baseline(case, w, tokens, min_seconds):
+    """The oracle, untuned, on the first `tokens` tokens (0: all) of the same
+    workload: forward of those tokens plus their dx, and dW of every expert
+    over their rows, in passes until at least `min_seconds` have elapsed.
+    Useful TFLOP/s of those passes."""
     import numpy as np
 
     from oracle import ffn as offn
+    from oracle.fp8 import dequant_blocks
     try:
         from threadpoolctl import threadpool_info
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count() or 1
-    n = min(tokens, case["T"])
+    n = case["T"] if tokens <= 0 else min(tokens, case["T"])
     ids = case["ids_np"][:n]
     gates = case["gates_np"][:n].astype(np.float64)
     lay = case["lay"]
     x = case["x"][:n].double().cpu().numpy()
-    w1 = lay["w1"].double().cpu().numpy()
-    w2 = lay["w2"].double().cpu().numpy()
+    if w.wdt == "fp8":        # the oracle takes the dequantized weights
+        w1 = dequant_blocks(lay["w1"].cpu().numpy(), lay["w1_scale"].cpu().numpy())
+        w2 = dequant_blocks(lay["w2"].cpu().numpy(), lay["w2_scale"].cpu().numpy())
+    else:
+        w1 = lay["w1"].double().cpu().numpy()
+        w2 = lay["w2"].double().cpu().numpy()
+    dy = case["dy"][:n].double().cpu().numpy() if case["dy"] is not None else None
     rows = int((ids >= 0).sum())
     f_fwd, f_bwd = flops_per_row(w)
+    passes, flops = 0, 0.0
     t0 = time.perf_counter()
-    offn.forward(x, w1, w2, ids, gates)
-    flops = f_fwd * rows
-    if case["dy"] is not None:
-        dy = case["dy"][:n].double().cpu().numpy()
-        offn.backward(x, w1, w2, ids, gates, dy)
-        flops += f_bwd * rows
-    dt = time.perf_counter() - t0
+    while True:
+        offn.forward(x, w1, w2, ids, gates)
+        flops += f_fwd * rows
+        if dy is not None:
+            offn.backward(x, w1, w2, ids, gates, dy)
+            flops += f_bwd * rows
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or passes >= 10:
+            break
+    what = "all" if n == case["T"] else f"first {n} of"
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {n} of {case['T']} tokens ({rows} routed rows): dense fp64 forward"
-                      f"{' + backward (dx, dW)' if case['dy'] is not None else ''}, numpy",
+            "sample": f"{what} {case['T']} tokens ({rows} routed rows), {passes} pass"
+                      f"{'es' if passes > 1 else ''}: dense fp64 forward"
+                      f"{' + backward (dx, dW)' if dy is not None else ''}, numpy",
             "seconds": dt}
 
 
@@ -365,7 +381,7 @@ def main():
                                    for p, v in per.items()}})
         out["size_sweep"] = {"runs": rows, "mean_regret": round(sum(regrets) / len(regrets), 4)}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(case, w, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(case, w, args.cpu_tokens, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
