@@ -82,6 +82,19 @@ def build_case(w, kappa, fixed, dev, quota_umin=None, gate_rho=None, lam=12, P=N
                 dy=dy, ids_np=ids, gates_np=gates, lay=lay, T=T)
 
 
+def predicted_cost(case, w, P):
+    """moe_predict_cost of the case's current plans, thousandths of a step."""
+    import torch
+
+    from moe_expert_ffn_amd import binding as B
+    r = case["runner"]
+    cost = torch.zeros(1, dtype=torch.int64, device=r.owner.device)
+    bw_b = r.plan_b["block_worker"] if w.backward else r.plan_f["block_worker"]
+    B.predict_cost(r.rs["counts"], r.rs["block_offsets"], r.plan_f["block_worker"], bw_b, r.owner,
+                   w.beta, P, w.d, w.d_ff, cost, r.status)
+    return int(cost.item())
+
+
 def time_steps(case, steps, warmup, with_events=True):
     """Times `steps` full steps; returns wall ms/step and per-stage mean ms."""
     import torch
@@ -341,6 +354,27 @@ def main():
                     planners.append({"kappa": kap, **compare_planners(c, w)})
                 del c
                 torch.cuda.empty_cache()
+            # quota planner with the partition count P picked by the cost model
+            chosen = None
+            for P in (1, 2, 4, 8):
+                c = build_case(w, kap, False, dev, quota_umin=1, P=P)
+                time_steps(c, 1, 0, with_events=False)          # route and plan once
+                cost = predicted_cost(c, w, P)
+                if chosen is None or (cost, -P) < (chosen[1], -chosen[2]):
+                    chosen = (c, cost, P)
+                else:
+                    del c
+                torch.cuda.empty_cache()
+            c, _, P = chosen
+            Rk = int((c["ids_np"] >= 0).sum())
+            msk, st = time_steps(c, max(5, args.steps // 2), 2)
+            uk = (f_fwd + (f_bwd if w.backward else 0)) * Rk
+            sweep.append({"kappa": kap, "placement": f"planned-quota-sized (P={P})",
+                          "ms": round(msk, 4), "tflops": round(uk / (msk * 1e-3) / 1e12, 2),
+                          "fwd_us": round(sum(v for k_, v in st.items() if k_.startswith("fwd.")) * 1e3, 1),
+                          "bwd_us": round(sum(v for k_, v in st.items() if k_.startswith("bwd.")) * 1e3, 1)})
+            del c, chosen
+            torch.cuda.empty_cache()
         out["kappa_sweep"] = sweep
         out["planners"] = planners
     if args.gate_sweep:
@@ -364,12 +398,7 @@ def main():
             for P in (1, 2, 4, 8):
                 c = build_case(w, kap, False, dev, P=P)
                 msk, _ = time_steps(c, max(5, args.steps // 2), 2)
-                r = c["runner"]
-                cost = torch.zeros(1, dtype=torch.int64, device=dev)
-                B.predict_cost(r.rs["counts"], r.rs["block_offsets"], r.plan_f["block_worker"],
-                               r.plan_b["block_worker"], r.owner, w.beta, P, w.d, w.d_ff, cost,
-                               r.status)
-                per[P] = (msk, int(cost.item()))
+                per[P] = (msk, predicted_cost(c, w, P))
                 del c
                 torch.cuda.empty_cache()
             chosen = min(per, key=lambda p: (per[p][1], -p))
