@@ -236,7 +236,9 @@ int moe_forward(const moe_layer* L, const void* x, const float* gates,
  * weight gradients take D and dZ requantized to e4m3 along the tokens, in
  * blocks of beta consecutive slots times one column (moe_quantize_token_blocks),
  * with x and A = SiLU(G) U unquantized: dw2 = Dq A^T, dw1 = dZq x^T.  The
- * codes and scales live in `ws` (moe_workspace_size counts them). */
+ * requantized D and dZ live in `ws` (moe_workspace_size counts them): as
+ * codes and scales, or, when d and d_ff are multiples of 256, widened back
+ * to bf16 (code times scale), which is the value the products use. */
 int moe_backward(const moe_layer* L, const void* x, const float* gates, const void* dy,
                  const void* z_save, const int32_t* topk_ids, int T, int k, int beta,
                  int P, int s, const int32_t* counts, const int32_t* block_offsets,

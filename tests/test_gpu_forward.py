@@ -29,6 +29,12 @@ SMALL = {
                           beta=16, P=2, s=1, kappas=(0,), cfg_id=14),
     "small_fp8": Workload("small_fp8", "bf16", "fp8", T=160, k=2, E=8, d=256, d_ff=256,
                           beta=128, P=4, s=2, kappas=(0,), cfg_id=15),
+    # e4m3 weights off the 256 grid: the register-staged tile kernels
+    "odd_fp8": Workload("odd_fp8", "bf16", "fp8", T=240, k=3, E=6, d=384, d_ff=128,
+                        beta=64, P=2, s=1, kappas=(0,), cfg_id=17),
+    # e4m3 weights on the stream kernels with several tiles each way and replicas
+    "stream_fp8": Workload("stream_fp8", "bf16", "fp8", T=700, k=4, E=8, d=512, d_ff=512,
+                           beta=128, P=8, s=4, kappas=(0,), cfg_id=18),
     # d and d_ff multiples of 256: the persistent 256 x 256 tile kernels, with
     # several tiles in both directions, ragged blocks and replicated experts
     "stream_bf16": Workload("stream_bf16", "bf16", "bf16", T=700, k=4, E=8, d=512, d_ff=256,
@@ -62,7 +68,8 @@ def test_forward_full_parity(name):
     assert err <= _tol(w)
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16", "beta32_bf16", "stream_bf16"])
+@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16", "beta32_bf16", "stream_bf16", "odd_fp8",
+                                  "stream_fp8"])
 def test_forward_plan_invariance(name):
     w = WORKLOADS.get(name) or SMALL[name]
     say(f"[fwd-invariance] {name}")
