@@ -28,7 +28,7 @@ struct SchedArgs {
   const int32_t* boff;
   const int32_t* bw;
   const int32_t* owner;
-  int E, P, s, beta, backward, bm;
+  int E, P, s, beta, backward, bm, max_blocks;
   int32_t* ctr;
   int32_t* mt_cnt;
   int4* mt;
@@ -62,41 +62,55 @@ MOE_DEV int block_rows(int g, int e, int beta, const int* boff_s, const int* cnt
   return min(beta, beta * boff_s[e] + cnt_s[e] - beta * g);
 }
 
-__global__ __launch_bounds__(256) void k_sched(SchedArgs a) {
+// One workgroup, one wave per worker (P <= 8).  BWL: block_worker is first
+// copied to LDS (when max_blocks entries fit), so each worker's pass over the
+// blocks reads LDS instead of issuing a global load per 64 blocks.
+constexpr int kSchedThreads = 512;
+template <bool BWL>
+__global__ __launch_bounds__(kSchedThreads) void k_sched(SchedArgs a) {
   extern __shared__ int sm[];
   const int E = a.E, P = a.P;
   int* boff_s = sm;
   int* cnt_s = boff_s + E + 1;
-  int* s0_s = cnt_s + E;
+  int* bw_s = cnt_s + E;                          // max_blocks entries when BWL
+  int* s0_s = bw_s + (BWL ? a.max_blocks : 0);
   int* rows_s = s0_s + E * P;
   int* starts_s = rows_s + E * P;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  for (int i = tid; i <= E; i += 256) boff_s[i] = a.boff[i];
-  for (int i = tid; i < E; i += 256) cnt_s[i] = a.counts[i];
+  constexpr int NT = kSchedThreads, NW = kSchedThreads / 64;
+  for (int i = tid; i <= E; i += NT) boff_s[i] = a.boff[i];
+  for (int i = tid; i < E; i += NT) cnt_s[i] = a.counts[i];
   if (tid < kNumCounters) a.ctr[tid] = 0;
   if (a.backward)
-    for (int i = tid; i < E * P; i += 256) { s0_s[i] = INT_MAX; rows_s[i] = 0; starts_s[i] = 0; }
+    for (int i = tid; i < E * P; i += NT) { s0_s[i] = INT_MAX; rows_s[i] = 0; starts_s[i] = 0; }
   __syncthreads();
   const int nb = boff_s[E];
-  for (int g = tid; g < nb; g += 256) {
+  if (BWL && nb > a.max_blocks) {                 // more blocks than the plan can hold
+    if (tid == 0) atomicOr(a.status, MOE_DEV_BAD_PLAN);
+    return;
+  }
+  for (int g = tid; g < nb; g += NT) {
     const int w = a.bw[g];
     if (w < 0 || w >= P) atomicOr(a.status, MOE_DEV_BAD_PLAN);
+    if constexpr (BWL) bw_s[g] = w;
   }
+  if constexpr (BWL) __syncthreads();
+  auto bw = [&](int g) { if constexpr (BWL) return bw_s[g]; else return a.bw[g]; };
   const bool grouped = (a.bm % a.beta) == 0;
   const int f = grouped ? a.bm / a.beta : 1;
   const uint64_t le_mask = (lane == 63) ? ~0ull : ((1ull << (lane + 1)) - 1);
-  for (int r = wv; r < P; r += 4) {
+  for (int r = wv; r < P; r += NW) {
     int run = 0, carry = 0;
     for (int base = 0; base < nb; base += 64) {
       const int g = base + lane;
-      const bool mine = g < nb && a.bw[g] == r;
+      const bool mine = g < nb && bw(g) == r;
       int e = 0, bstart = 0, vrows = 0;
       bool start = false;
       if (mine) {
         e = expert_of(g, boff_s, E);
         bstart = a.beta * g;
         vrows = block_rows(g, e, a.beta, boff_s, cnt_s);
-        start = (g == boff_s[e]) || a.bw[g - 1] != r;
+        start = (g == boff_s[e]) || bw(g - 1) != r;
       }
       const uint64_t sm_ = __ballot(start) & le_mask;
       const int rs = sm_ ? base + 63 - __clzll(sm_) : carry;
@@ -108,7 +122,7 @@ __global__ __launch_bounds__(256) void k_sched(SchedArgs a) {
             nt = 1;
             for (int i = 0; i < f; ++i) {
               const int gi = g + i;
-              if (gi >= boff_s[e + 1] || (i > 0 && a.bw[gi] != r)) break;
+              if (gi >= boff_s[e + 1] || (i > 0 && bw(gi) != r)) break;
               trows += block_rows(gi, e, a.beta, boff_s, cnt_s);
             }
           }
@@ -128,23 +142,23 @@ __global__ __launch_bounds__(256) void k_sched(SchedArgs a) {
   }
   if (!a.backward) return;
 
-  for (int g = tid; g < nb; g += 256) {
-    const int w = a.bw[g];
+  for (int g = tid; g < nb; g += NT) {
+    const int w = bw(g);
     if (w < 0 || w >= P) continue;
     const int e = expert_of(g, boff_s, E);
     const int vrows = min(a.beta, a.beta * boff_s[e] + cnt_s[e] - a.beta * g);
     atomicMin(&s0_s[e * P + w], a.beta * g);
     atomicAdd(&rows_s[e * P + w], vrows);
-    if (g == boff_s[e] || a.bw[g - 1] != w) atomicAdd(&starts_s[e * P + w], 1);
+    if (g == boff_s[e] || bw(g - 1) != w) atomicAdd(&starts_s[e * P + w], 1);
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 256) {
+  for (int e = tid; e < E; e += NT) {
     const int h = a.owner[e];
     const bool ok = h >= 0 && h < P;
     if (!ok) atomicOr(a.status, MOE_DEV_BAD_OWNER);
     a.owner_has[e] = (ok && rows_s[e * P + h] > 0 && starts_s[e * P + h] == 1) ? 1 : 0;
   }
-  for (int r = wv; r < P; r += 4) {
+  for (int r = wv; r < P; r += NW) {
     // pass 0: replica segments (non-home experts) first; pass 1: home segments
     int run = 0, rrun = 0;
     for (int pass = 0; pass < 2; ++pass) {
@@ -1622,8 +1636,9 @@ static void rec(void* const* ev, int i, hipStream_t st) {
   if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], st);
 }
 
-static size_t sched_lds(const Sizes& z, bool bwd) {
-  return sizeof(int) * ((size_t)2 * z.E + 1 + (bwd ? (size_t)3 * z.E * z.P : 0));
+static size_t sched_lds(const Sizes& z, bool bwd, bool bwl) {
+  return sizeof(int) * ((size_t)2 * z.E + 1 + (bwl ? z.max_blocks : 0) +
+                        (bwd ? (size_t)3 * z.E * z.P : 0));
 }
 
 static void launch_sched(const Sizes& z, const int32_t* counts, const int32_t* boff,
@@ -1642,10 +1657,19 @@ static void launch_sched(const Sizes& z, const int32_t* counts, const int32_t* b
   s.rep_slot = (int32_t*)(ws + L.rep_slot);
   s.owner_has = (int32_t*)(ws + L.owner_has);
   s.status = status;
-  const size_t lds = sched_lds(z, bwd);
-  (void)hipFuncSetAttribute((const void*)k_sched, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)sched_lds(z, true));
-  hipLaunchKernelGGL(k_sched, dim3(1), dim3(256), lds, st, s);
+  s.max_blocks = (int)z.max_blocks;
+  // block_worker goes through LDS when it fits next to the rest (64 KB)
+  const bool bwl = sched_lds(z, true, true) <= 64 * 1024;
+  const size_t lds = sched_lds(z, bwd, bwl);
+  if (bwl) {
+    (void)hipFuncSetAttribute((const void*)k_sched<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)sched_lds(z, true, true));
+    hipLaunchKernelGGL(k_sched<true>, dim3(1), dim3(kSchedThreads), lds, st, s);
+  } else {
+    (void)hipFuncSetAttribute((const void*)k_sched<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)sched_lds(z, true, false));
+    hipLaunchKernelGGL(k_sched<false>, dim3(1), dim3(kSchedThreads), lds, st, s);
+  }
 }
 
 static ExecArgs make_exec(const Sizes& z, const LayerPtrs& Lp, char* ws, const WsLayout& L) {
