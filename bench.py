@@ -173,7 +173,7 @@ def kernel_model(w, R, T, e_act, replicas):
 # HBM traffic of the dominant kernel from rocprofv3 counters (FETCH_SIZE and
 # WRITE_SIZE per dispatch, scaled by the reading of a plain copy kernel of
 # known size), valid only for the kernel sources it was measured on.
-PROFILED_TRAFFIC = {"kernel": "bwd.dW", "source": "7fe2a1a2d1426459", "bytes": 3820671184,
+PROFILED_TRAFFIC = {"kernel": "bwd.dW", "source": "8fd02422f9540889", "bytes": 3800572926,
                     "summary": "profiles/k_stream_SrcDwT_qwen3_bf16_fwdbwd_hbm_traffic.md"}
 
 
