@@ -409,37 +409,72 @@ __global__ __launch_bounds__(C::NT) void k_fc2(ExecArgs a) {
 }
 
 // ---- combine: out_t = sum_{j: slot(t,j) >= 0} src[slot(t,j)], fp32, j order ---
+// One wave per token: the token's slot indices are read once (64 per load,
+// lane j holding slot j) and taken out of their lanes as wave-uniform values;
+// each lane covers 16-byte chunks c, c + 64, ... of the row, two at a time.
+// For every chunk the values of up to 8 slots are loaded together and then
+// added in slot order, starting from 0, in fp32, and rounded once.
 template <typename T>
 __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ src,
                                                  const int32_t* __restrict__ row_to_slot,
                                                  int T_, int k, int d, T* __restrict__ out) {
-  constexpr int VE = Elem<T>::VE;
-  const int per_row = d / VE;
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long long)T_ * per_row) return;
-  const int t = (int)(idx / per_row), c = (int)(idx % per_row) * VE;
-  float acc[VE];
+  constexpr int VE = Elem<T>::VE, U = 2, G = 8;
+  const int t = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (t >= T_) return;                                  // the whole wave
+  const int nch = d / VE;
+  const int32_t* slots = row_to_slot + (size_t)t * k;
+  for (int c = lane; c < nch; c += 64 * U) {
+    float acc[U][VE];
 #pragma unroll
-  for (int v = 0; v < VE; ++v) acc[v] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int s = row_to_slot[(size_t)t * k + j];
-    if (s < 0) continue;
-    V16 in;
-    in.u = ldg16(src + (size_t)s * d + c);
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int v = 0; v < VE; ++v) {
-      if constexpr (sizeof(T) == 2) acc[v] += bf2f(in.h[v]);
-      else acc[v] += in.f[v];
+      for (int v = 0; v < VE; ++v) acc[u][v] = 0.f;
+    for (int j64 = 0; j64 < k; j64 += 64) {
+      const int sl = j64 + lane < k ? slots[j64 + lane] : -1;
+      const int nj = min(64, k - j64);
+      for (int j0 = 0; j0 < nj; j0 += G) {
+        V16 in[G][U];
+        int sj[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          sj[g] = j0 + g < nj ? __builtin_amdgcn_readlane(sl, j0 + g) : -1;
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int cc = c + 64 * u;
+            in[g][u].u = (sj[g] >= 0 && cc < nch) ? ldg16(src + (size_t)sj[g] * d + (size_t)cc * VE)
+                                                 : zero4();
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          if (sj[g] < 0) continue;                      // wave-uniform
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int v = 0; v < VE; ++v) {
+              if constexpr (sizeof(T) == 2) acc[u][v] += bf2f(in[g][u].h[v]);
+              else acc[u][v] += in[g][u].f[v];
+            }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int cc = c + 64 * u;
+      if (cc >= nch) continue;
+      V16 o;
+#pragma unroll
+      for (int v = 0; v < VE; ++v) {
+        if constexpr (sizeof(T) == 2) o.h[v] = f2bf(acc[u][v]);
+        else o.f[v] = acc[u][v];
+      }
+      stg16(out + (size_t)t * d + (size_t)cc * VE, o.u);
     }
   }
-  V16 o;
-#pragma unroll
-  for (int v = 0; v < VE; ++v) {
-    if constexpr (sizeof(T) == 2) o.h[v] = f2bf(acc[v]);
-    else o.f[v] = acc[v];
-  }
-  stg16(out + (size_t)t * d + c, o.u);
 }
+
+// grid of the combine: one wave per token, four tokens per workgroup
+static dim3 combine_grid(int T) { return dim3((unsigned)((T + 3) / 4)); }
 
 // ---- backward: dA -> dZ -------------------------------------------------------
 // dA[slot, n] = p * sum_c dy[t, c] W2[c, n]; W2 is read as a K-major (c) by
@@ -1711,9 +1746,8 @@ static void run_forward(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot,
   rec(ev, 2, st);
   hipLaunchKernelGGL((k_fc2<T, FP8, C>), dim3(g2), dim3(C::NT), lds, st, a);
   rec(ev, 3, st);
-  const long long nth = (long long)z.T * (z.d / Elem<T>::VE);
-  if (nth > 0)
-    hipLaunchKernelGGL(k_combine<T>, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, st,
+  if (z.T > 0)
+    hipLaunchKernelGGL(k_combine<T>, combine_grid(z.T), dim3(256), 0, st,
                        (const T*)a.bufO, row_to_slot, z.T, z.k, z.d, (T*)y);
   rec(ev, 4, st);
 }
@@ -1756,9 +1790,8 @@ static void run_forward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_t
   rec(ev, 2, st);
   launch_stream<SrcFc2T<FP8>, WC, RowW, typename SrcFc2T<FP8>::OB>(a, z.d / WC::BN, kStreamLds, st);
   rec(ev, 3, st);
-  const long long nth = (long long)z.T * (z.d / 8);
-  if (nth > 0)
-    hipLaunchKernelGGL(k_combine<uint16_t>, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, st,
+  if (z.T > 0)
+    hipLaunchKernelGGL(k_combine<uint16_t>, combine_grid(z.T), dim3(256), 0, st,
                        (const uint16_t*)a.bufO, row_to_slot, z.T, z.k, z.d, (uint16_t*)y);
   rec(ev, 4, st);
 }
@@ -1805,9 +1838,8 @@ static void run_backward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_
   rec(ev, 2, st);
   launch_stream<SrcDxT<FP8>, WC, RowW, typename SrcDxT<FP8>::OB>(a, z.d / WC::BN, kStreamLds, st);
   rec(ev, 3, st);
-  const long long nth = (long long)z.T * (z.d / 8);
-  if (nth > 0)
-    hipLaunchKernelGGL(k_combine<uint16_t>, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, st,
+  if (z.T > 0)
+    hipLaunchKernelGGL(k_combine<uint16_t>, combine_grid(z.T), dim3(256), 0, st,
                        (const uint16_t*)a.bufO, row_to_slot, z.T, z.k, z.d, (uint16_t*)dx);
   rec(ev, 4, st);
   if constexpr (FP8)
@@ -1839,9 +1871,8 @@ static void run_backward(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot
   rec(ev, 2, st);
   hipLaunchKernelGGL((k_bwd_dx<T, C, FP8>), dim3(gx), dim3(C::NT), lds, st, a);
   rec(ev, 3, st);
-  const long long nth = (long long)z.T * (z.d / Elem<T>::VE);
-  if (nth > 0)
-    hipLaunchKernelGGL(k_combine<T>, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, st,
+  if (z.T > 0)
+    hipLaunchKernelGGL(k_combine<T>, combine_grid(z.T), dim3(256), 0, st,
                        (const T*)a.bufO, row_to_slot, z.T, z.k, z.d, (T*)dx);
   rec(ev, 4, st);
   hipLaunchKernelGGL((k_bwd_dw<T, C, FP8>), dim3(gw), dim3(C::NT), lds, st, a);
