@@ -141,6 +141,11 @@ def time_steps(case, steps, warmup, with_events=True):
                     acc.setdefault("bwd." + nm, []).append(eb.elapsed_ms(j, j + 1))
             acc.setdefault("step", []).append(es.elapsed_ms(0, 1))
         stages = {k: sum(v) / len(v) for k, v in acc.items()}
+        steps_sorted = sorted(acc["step"])
+
+        def pct(q):
+            return steps_sorted[min(len(steps_sorted) - 1, int(q * len(steps_sorted)))]
+        stages["step_p10"], stages["step_median"], stages["step_p90"] = pct(0.1), pct(0.5), pct(0.9)
     assert int(r.status.item()) == 0, "device status word set"
     return wall_ms, stages
 
