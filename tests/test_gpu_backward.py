@@ -24,6 +24,10 @@ SMALL = {
     # dW through the per-wave LDS store staging), replicas reduced into owners
     "stream_bf16": Workload("stream_bf16", "bf16", "bf16", T=700, k=4, E=8, d=512, d_ff=256,
                             beta=128, P=8, s=4, kappas=(0,), cfg_id=24),
+    # the most experts the planner takes and tiny blocks: 4,608 block slots, so
+    # the scheduler keeps block_worker in global memory instead of LDS
+    "many_experts_bf16": Workload("many_experts_bf16", "bf16", "bf16", T=2048, k=8, E=512, d=128,
+                                  d_ff=128, beta=4, P=8, s=2, kappas=(0,), cfg_id=25),
 }
 
 
@@ -59,7 +63,8 @@ def test_backward_full_parity(name):
     assert max(e_dx, e_w1, e_w2) <= tol
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16", "beta32_bf16", "stream_bf16"])
+@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16", "beta32_bf16", "stream_bf16",
+                                  "many_experts_bf16"])
 def test_backward_plan_invariance(name):
     w = WORKLOADS.get(name) or SMALL[name]
     say(f"[bwd-invariance] {name}")
