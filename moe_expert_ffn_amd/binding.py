@@ -106,6 +106,14 @@ def _require_device(*ts):
             raise MoeError("all buffers must be contiguous device tensors")
 
 
+def _expect(t, dtype, min_numel, name):
+    """Element type and minimum size of a buffer the library writes or reads."""
+    if t.dtype != dtype:
+        raise MoeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.numel() < min_numel:
+        raise MoeError(f"{name}: needs at least {min_numel} elements, has {t.numel()}")
+
+
 def act_code(dtype) -> int:
     return MOE_F32 if dtype == torch.float32 else MOE_BF16
 
@@ -190,6 +198,16 @@ def quantize_token_blocks(src, rows, cols, block_rows, codes, scales, row_map=No
                           row_div=1, row_scale=None, ld=None):
     """Token-axis e4m3 codes [rows][cols] and scales [ceil(rows/block_rows)][cols]."""
     _require_device(src, codes, scales, *[t for t in (row_map, row_scale) if t is not None])
+    if rows > 0 and block_rows > 0:
+        nblk = (rows + block_rows - 1) // block_rows
+        _expect(codes, torch.uint8, rows * cols, "codes")
+        _expect(scales, torch.float32, nblk * cols, "scales")
+        _expect(src, torch.bfloat16, 0 if gather else (rows - 1) * (cols if ld is None else ld) + cols,
+                "src")
+        if row_map is not None:
+            _expect(row_map, torch.int32, rows, "row_map")
+        if row_scale is not None:
+            _expect(row_scale, torch.float32, 1, "row_scale")
     _check(load().moe_quantize_token_blocks(
         _ptr(src), cols if ld is None else ld, _ptr(row_map) if row_map is not None else None,
         1 if gather else 0, row_div, _ptr(row_scale) if row_scale is not None else None, rows, cols,

@@ -118,3 +118,33 @@ def test_host_validation_errors():
                            None) == B.MOE_ERR_WORKSPACE
     assert lib.moe_forward(ctypes.byref(ok), P, P, P, 4, 2, 16, 5, *([P] * 8), P, 1 << 30, None,
                            None) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_quantizer_binding_checks_buffers():
+    """The Python binding refuses buffers of the wrong element type or size
+    before anything reaches the device (no GPU needed: the checks come first)."""
+    import torch
+
+    class FakeDev:
+        """A tensor stand-in that claims to be a contiguous device tensor."""
+        def __init__(self, dtype, n):
+            self.dtype, self._n = dtype, n
+            self.is_cuda = True
+
+        def is_contiguous(self):
+            return True
+
+        def numel(self):
+            return self._n
+
+    src = FakeDev(torch.bfloat16, 64 * 16)
+    ok_codes, ok_scales = FakeDev(torch.uint8, 64 * 16), FakeDev(torch.float32, 16)
+    with pytest.raises(B.MoeError, match="codes"):
+        B.quantize_token_blocks(src, 64, 16, 128, FakeDev(torch.uint8, 10), ok_scales)
+    with pytest.raises(B.MoeError, match="scales"):
+        B.quantize_token_blocks(src, 64, 16, 128, ok_codes, FakeDev(torch.float16, 16))
+    with pytest.raises(B.MoeError, match="src"):
+        B.quantize_token_blocks(FakeDev(torch.float32, 64 * 16), 64, 16, 128, ok_codes, ok_scales)
+    with pytest.raises(B.MoeError, match="row_map"):
+        B.quantize_token_blocks(src, 64, 16, 128, ok_codes, ok_scales,
+                                row_map=FakeDev(torch.int64, 64))
