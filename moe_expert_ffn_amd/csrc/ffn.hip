@@ -933,7 +933,13 @@ template <typename T, int SEG> struct RowStore {
 MOE_DEV MOE_LDS char* epi_scratch(MOE_LDS uint16_t* smem) {
   return (MOE_LDS char*)smem + kEpiOff + (size_t)wave_id() * kEpiWave;
 }
-MOE_DEV void stg16v(void* p, const u32x4_t& d) { *(MOE_GLB u32x4_t*)p = d; }
+// Weight-gradient tiles are written once and not read again by this layer:
+// non-temporal stores keep the 2.4 GB of fp32 tiles of a launch from evicting
+// the operand panels the next tiles of the same segment read from L2 (6% off
+// the kernel on the Qwen3-shaped workload, measured against plain stores).
+MOE_DEV void stg16v(void* p, const u32x4_t& d) {
+  __builtin_nontemporal_store(d, (MOE_GLB u32x4_t*)p);
+}
 // 16 bytes at element column `col` of slot row `srow` of a [slots][ld] bf16
 // buffer; a row past the tile's end is sent out of range and dropped, so an
 // epilogue issues the same number of stores for every tile
@@ -1173,11 +1179,14 @@ template <bool FP8> struct SrcDaT : MSrcBase {
     const BufRsrc rdz = make_rsrc(a.bufA, (uint32_t)(a.slots * dff * 4));
     const BufRsrc rp = make_rsrc(a.bufP, (uint32_t)(a.slots * dff * 2));
     MOE_LDS char* scr = epi_scratch(smem);
-    // Block b = (i, j) of 32 x 32.  The lane's [G, U] of block b + 1 are loaded
-    // into the same registers once block b's last output is formed and before
-    // its stores are issued, so waiting for them never waits for those stores.
-    // dG, dU and P leave through the per-wave scratch as 64-byte row pieces.
-    u32x2_t zg[4], zu[4];
+    // Block b = (i, j) of 32 x 32.  The lane's [G, U] of block b + 1 go into
+    // the other register set while block b is formed, so their round trip runs
+    // under block b's passes and stores: from block 1 on they are issued when
+    // block b starts; block 1's wait until block 0's accumulators are spent
+    // (after its second pass), which keeps the peak register count where a
+    // single set puts it.  dG, dU and P leave through the per-wave scratch as
+    // 64-byte row pieces.
+    u32x2_t zg2[2][4], zu2[2][4];
     auto zload = [&](int b, u32x2_t (&g_)[4], u32x2_t (&u_)[4]) {
       const int i = b / WC::NB, j = b % WC::NB;
       const int myrow = wm * WC::WM + i * 32 + (lane & 31);
@@ -1189,10 +1198,13 @@ template <bool FP8> struct SrcDaT : MSrcBase {
         u_[g] = *(const MOE_GLB u32x2_t*)(Z + sr * 2 * dff + dff + n);
       }
     };
-    zload(0, zg, zu);
+    zload(0, zg2[0], zu2[0]);
 #pragma unroll
     for (int b = 0; b < NBLK; ++b) {
       const int i = b / WC::NB, j = b % WC::NB;
+      if (b >= 1 && b + 1 < NBLK) zload(b + 1, zg2[(b + 1) & 1], zu2[(b + 1) & 1]);
+      const u32x2_t(&zg)[4] = zg2[b & 1];
+      const u32x2_t(&zu)[4] = zu2[b & 1];
       const int rb = wm * WC::WM + i * 32, cb = colb + j * 32;
       const float pg = gt[rb + (lane & 31)];
       using RS = RowStore<uint16_t, 1>;
@@ -1227,9 +1239,9 @@ template <bool FP8> struct SrcDaT : MSrcBase {
       pass(0, pk);
       RS::store(scr, pk, emit_to(rdz, 0, 2 * dff));
       pass(1, pk);
+      if (b == 0 && NBLK > 1) zload(1, zg2[1], zu2[1]);
       RS::store(scr, pk, emit_to(rdz, dff, 2 * dff));
       pass(2, pk);
-      if (b + 1 < NBLK) zload(b + 1, zg, zu);
       RS::store(scr, pk, emit_to(rp, 0, dff));
     }
   }
