@@ -178,7 +178,7 @@ def kernel_model(w, R, T, e_act, replicas):
 # HBM traffic of the dominant kernel from rocprofv3 counters (FETCH_SIZE and
 # WRITE_SIZE per dispatch, scaled by the reading of a plain copy kernel of
 # known size), valid only for the kernel sources it was measured on.
-PROFILED_TRAFFIC = {"kernel": "bwd.dW", "source": "8f4fd2b11cc8e1b0", "bytes": 3823006086,
+PROFILED_TRAFFIC = {"kernel": "bwd.dW", "source": "10ef1959d8128126", "bytes": 3358777054,
                     "summary": "profiles/k_stream_SrcDwT_qwen3_bf16_fwdbwd_hbm_traffic.md"}
 
 

@@ -61,9 +61,24 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
   const bool worker = g < G;
   const int c0 = worker ? (int)((long long)g * nchunks / G) : 0;
   const int c1 = worker ? (int)((long long)(g + 1) * nchunks / G) : 0;
+  // The chunk counts were just written by every XCD, so each batch of loads is
+  // a full memory round trip.  When a thread owns at most kKeep chunks (every
+  // workload here: 32 at most), they are loaded once, all in flight together,
+  // and kept in registers for the rewrite below.
+  constexpr int kKeep = 32;
+  const bool keep = c1 - c0 <= kKeep;
+  int held[kKeep];
   int ps = 0;
+  if (keep) {
+#pragma unroll
+    for (int u = 0; u < kKeep; ++u)
+      held[u] = c0 + u < c1 ? chunk_cnt[(size_t)(c0 + u) * E + e_own] : 0;
+#pragma unroll
+    for (int u = 0; u < kKeep; ++u) ps += held[u];
+  } else {
 #pragma unroll 8
-  for (int ch = c0; ch < c1; ++ch) ps += chunk_cnt[(size_t)ch * E + e_own];
+    for (int ch = c0; ch < c1; ++ch) ps += chunk_cnt[(size_t)ch * E + e_own];
+  }
   if (worker) part[g * E + e_own] = ps;
   __syncthreads();
   const int e = tid;
@@ -94,14 +109,33 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
     *kappa = (S == 0) ? 1.0 : (double)((long long)E * S2) / (double)(S * S);
   }
   __syncthreads();
-  if (worker) {
+  // Otherwise eight chunks' counts are loaded before any of them is
+  // rewritten: loads and stores of one array do not pass each other, so a
+  // load per store would wait out one memory round trip per chunk.
+  if (worker && keep) {
     int run = bbase[e_own];
     for (int q = 0; q < g; ++q) run += part[q * E + e_own];
-    for (int ch = c0; ch < c1; ++ch) {
-      const size_t at = (size_t)ch * E + e_own;
-      const int t = chunk_cnt[at];
-      chunk_cnt[at] = run;
-      run += t;
+#pragma unroll
+    for (int u = 0; u < kKeep; ++u)
+      if (c0 + u < c1) {
+        chunk_cnt[(size_t)(c0 + u) * E + e_own] = run;
+        run += held[u];
+      }
+  } else if (worker) {
+    int run = bbase[e_own];
+    for (int q = 0; q < g; ++q) run += part[q * E + e_own];
+    constexpr int U = 8;
+    for (int ch0 = c0; ch0 < c1; ch0 += U) {
+      int t[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        t[u] = ch0 + u < c1 ? chunk_cnt[(size_t)(ch0 + u) * E + e_own] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (ch0 + u < c1) {
+          chunk_cnt[(size_t)(ch0 + u) * E + e_own] = run;
+          run += t[u];
+        }
     }
   }
 }

@@ -57,7 +57,10 @@ def test_route_stats_workloads(name, kappa):
 
 @pytest.mark.parametrize("T,k,E,beta,neg", [(1, 1, 1, 1, 0.0), (5, 2, 4, 2, 1.0), (257, 3, 37, 7, 0.3),
                                             (1000, 8, 512, 128, 0.0), (300, 6, 1024, 1, 0.1),
-                                            (4097, 2, 2, 3, 0.0), (0, 4, 8, 16, 0.0)])
+                                            (4097, 2, 2, 3, 0.0), (0, 4, 8, 16, 0.0),
+                                            # more than 32 chunks of 256 rows per scan thread
+                                            # (1024 threads = E x groups): the scan's general path
+                                            (3000, 4, 1024, 16, 0.1), (9000, 8, 128, 128, 0.05)])
 def test_route_stats_edges(T, k, E, beta, neg):
     say(f"[route-edge] T={T} k={k} E={E} beta={beta} neg={neg}")
     rng = np.random.default_rng(T + E)
