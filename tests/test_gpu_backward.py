@@ -77,7 +77,7 @@ def test_backward_plan_invariance(name):
     assert rel_l2(dw2_p.double().cpu().numpy(), dw2_f.double().cpu().numpy()) < 1e-6
 
 
-@pytest.mark.parametrize("kappa", [1, 8])
+@pytest.mark.parametrize("kappa", WORKLOADS["qwen3_bf16_fwdbwd"].kappas)
 def test_backward_full_size_sampled(kappa):
     w = WORKLOADS["qwen3_bf16_fwdbwd"]
     say(f"[bwd-full] kappa={kappa}")

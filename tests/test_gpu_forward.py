@@ -101,8 +101,9 @@ def test_forward_saves_z():
     assert err <= TOL["bf16"]
 
 
-FULL = [("olmoe_bf16", 1), ("olmoe_bf16", 8), ("qwen3_bf16", 1), ("qwen3_bf16", 8),
-        ("dsv3_fp8", 1), ("dsv3_fp8", 8)]
+# every skew level each workload is run at
+FULL = [(name, kappa) for name in ("olmoe_bf16", "qwen3_bf16", "dsv3_fp8")
+        for kappa in WORKLOADS[name].kappas]
 
 
 @pytest.mark.parametrize("name,kappa", FULL)

@@ -167,7 +167,7 @@ def test_fp8_backward_plan_invariance():
     assert rel_l2(dw2_p.double().cpu().numpy(), dw2_f.double().cpu().numpy()) < 1e-6
 
 
-@pytest.mark.parametrize("kappa", [1, 8])
+@pytest.mark.parametrize("kappa", WORKLOADS["dsv3_fp8_fwdbwd"].kappas)
 def test_fp8_backward_full_size_sampled(kappa):
     w = WORKLOADS["dsv3_fp8_fwdbwd"]
     say(f"[fp8-bwd-full] kappa={kappa}")
