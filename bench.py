@@ -79,7 +79,8 @@ def build_case(w, kappa, fixed, dev, quota_umin=None, gate_rho=None, lam=12, P=N
                     owner=torch.from_numpy(contiguous_owners(w.E, P or w.P)), with_backward=w.backward,
                     quota_umin=quota_umin, gate_rho=gate_rho, lam=lam)
     return dict(runner=r, x=x, gates=torch.from_numpy(gates).to(dev), ids=torch.from_numpy(ids).to(dev),
-                dy=dy, ids_np=ids, gates_np=gates, lay=lay, T=T)
+                dy=dy, ids_np=ids, gates_np=gates, lay=lay, T=T,
+                owner_np=contiguous_owners(w.E, P or w.P))
 
 
 def predicted_cost(case, w, P):
@@ -150,11 +151,12 @@ def time_steps(case, steps, warmup, with_events=True):
     return wall_ms, stages
 
 
-def kernel_model(w, R, T, e_act, replicas):
+def kernel_model(w, R, T, e_act, replicas, red_bytes=0):
     """Algorithmic flops and HBM bytes of one launch of each kernel: every
     operand read once from HBM and every output written once (weights of the
     experts that have rows, gathered activations counted once per token, the
-    fp32 weight gradients of owners and replicas)."""
+    fp32 weight gradients of owners and replicas; the replica reduction's
+    bytes come from the backward plan, see reduce_bytes)."""
     d, f, ab = w.d, w.d_ff, 2
     wb = 1 if w.wdt == "fp8" else 2
     w1 = 2 * f * d * wb * e_act
@@ -172,13 +174,32 @@ def kernel_model(w, R, T, e_act, replicas):
             "bwd.combine": (0, R * d * ab + x),
             "bwd.dW": (6 * d * f * R, 2 * x + R * 2 * f * ab + R * f * ab + 3 * d * f * 4 * (e_act + replicas)),
         })
+        if red_bytes > 0:
+            m["bwd.reduce"] = (0, red_bytes)
     return m
+
+
+def reduce_bytes(case, w):
+    """Bytes the replica reduction moves under the backward plan: for every
+    expert with a replica partial, or with no owner partial, the owner
+    partial (if any) and each replica partial are read and the owner slot is
+    written, 3 * d * d_ff fp32 values each."""
+    q = case["runner"].plan_b["q"].cpu().numpy()
+    own = case["owner_np"]
+    per = 3 * w.d * w.d_ff * 4
+    total = 0
+    for e in range(w.E):
+        has_own = q[e, own[e]] > 0
+        nrep = int((q[e] > 0).sum()) - int(has_own)
+        if nrep > 0 or not has_own:
+            total += (int(has_own) + nrep + 1) * per
+    return total
 
 
 # HBM traffic of the dominant kernel from rocprofv3 counters (FETCH_SIZE and
 # WRITE_SIZE per dispatch, scaled by the reading of a plain copy kernel of
 # known size), valid only for the kernel sources it was measured on.
-PROFILED_TRAFFIC = {"kernel": "bwd.dW", "source": "10ef1959d8128126", "bytes": 3358777054,
+PROFILED_TRAFFIC = {"kernel": "bwd.dW", "source": "0f1cbeaf995561a2", "bytes": 3362913378,
                     "summary": "profiles/k_stream_SrcDwT_qwen3_bf16_fwdbwd_hbm_traffic.md"}
 
 
@@ -192,8 +213,8 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def roofline(w, stages, R, T, e_act, replicas):
-    model = kernel_model(w, R, T, e_act, replicas)
+def roofline(w, stages, R, T, e_act, replicas, red_bytes=0):
+    model = kernel_model(w, R, T, e_act, replicas, red_bytes)
     # every contraction runs on bf16 MFMA (e4m3 weights are widened to bf16
     # between LDS and the matrix cores), so the bf16 peak bounds it
     peak_f = PEAK_BF16_TFLOPS
@@ -280,23 +301,70 @@ def cpu_baseline(case, w, tokens, min_seconds):
     rows = int((ids >= 0).sum())
     f_fwd, f_bwd = flops_per_row(w)
     passes, flops = 0, 0.0
+    t_fwd, t_bwd = [], []
     t0 = time.perf_counter()
     while True:
+        ta = time.perf_counter()
         offn.forward(x, w1, w2, ids, gates)
+        t_fwd.append(time.perf_counter() - ta)
         flops += f_fwd * rows
         if dy is not None:
+            ta = time.perf_counter()
             offn.backward(x, w1, w2, ids, gates, dy)
+            t_bwd.append(time.perf_counter() - ta)
             flops += f_bwd * rows
         passes += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds or passes >= 10:
             break
     what = "all" if n == case["T"] else f"first {n} of"
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{what} {case['T']} tokens ({rows} routed rows), {passes} pass"
-                      f"{'es' if passes > 1 else ''}: dense fp64 forward"
-                      f"{' + backward (dx, dW)' if dy is not None else ''}, numpy",
-            "seconds": dt}
+    out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"{what} {case['T']} tokens ({rows} routed rows), {passes} pass"
+                     f"{'es' if passes > 1 else ''}: dense fp64 forward"
+                     f"{' + backward (dx, dW)' if dy is not None else ''}, numpy",
+           "seconds": dt}
+    out["stages_ms"] = cpu_stages(case, w, ids, t_fwd, t_bwd)
+    out["cpu_model"] = cpu_model()
+    return out
+
+
+def cpu_stages(case, w, ids, t_fwd, t_bwd):
+    """Median milliseconds of each oracle stage on the same sample: routing
+    statistics and the two plans (pure Python, one thread; three runs each),
+    and the forward and backward passes timed above (numpy on the BLAS
+    threads)."""
+    import numpy as np
+
+    from oracle import plan as oplan
+    from oracle import route as oroute
+
+    def med3(f):
+        ts = []
+        for _ in range(3):
+            ta = time.perf_counter()
+            res = f()
+            ts.append(time.perf_counter() - ta)
+        return float(np.median(ts)) * 1e3, res
+
+    t_route, rs = med3(lambda: oroute.route_stats(ids, w.E, w.beta))
+    own = case["owner_np"]
+    t_pf, _ = med3(lambda: oplan.plan(rs["block_counts"], own, w.P, w.s, oplan.FWD))
+    t_pb, _ = med3(lambda: oplan.plan(rs["block_counts"], own, w.P, w.s, oplan.BWD, 12))
+    st = {"route_1thread": round(t_route, 2), "plan_fwd_1thread": round(t_pf, 3),
+          "plan_bwd_1thread": round(t_pb, 3), "forward": round(float(np.median(t_fwd)) * 1e3, 1)}
+    if t_bwd:
+        st["backward"] = round(float(np.median(t_bwd)) * 1e3, 1)
+    return st
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -322,9 +390,11 @@ def main():
     import numpy as np
     e_act = int((np.bincount(case["ids_np"][case["ids_np"] >= 0].ravel(), minlength=w.E) > 0).sum())
     replicas = int(case["runner"].plan_b["plan_info"][2].item()) if w.backward else 0
-    roof, per_kernel = roofline(w, stages, R, case["T"], e_act, replicas)
+    red_bytes = reduce_bytes(case, w) if w.backward else 0
+    roof, per_kernel = roofline(w, stages, R, case["T"], e_act, replicas, red_bytes)
 
     plan_f = case["runner"].plan_f["plan_info"].cpu().tolist()
+    plan_b = case["runner"].plan_b["plan_info"].cpu().tolist() if w.backward else None
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -335,7 +405,8 @@ def main():
                                f"kappa={args.kappa:g} ({'fwd+bwd' if w.backward else 'fwd'})",
                    "kappa_realised": round(realised_kappa(case["ids_np"], w.E), 4),
                    "routed_rows": R, "placement": "fixed" if args.fixed else "planned",
-                   "plan_info_fwd": plan_f},
+                   "plan_info_fwd": plan_f,
+                   **({"plan_info_bwd": plan_b, "reduce_bytes": red_bytes} if w.backward else {})},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "stages_us": {k: round(v * 1e3, 2) for k, v in stages.items()},
         "roofline": roof,

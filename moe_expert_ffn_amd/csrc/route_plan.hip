@@ -178,6 +178,16 @@ MOE_DEV long long wave_max64(long long v) {
   }
   return v;
 }
+// max over lanes 0..7 (the xor partners 4, 2, 1 stay inside each group of
+// eight lanes), returned to every lane from lane 0
+MOE_DEV long long lanes8_max64(long long v) {
+#pragma unroll
+  for (int off = 4; off > 0; off >>= 1) {
+    long long o = __shfl_xor(v, off, 64);
+    v = o > v ? o : v;
+  }
+  return __shfl(v, 0, 64);
+}
 MOE_DEV int wave_max32(int v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -264,9 +274,22 @@ __global__ __launch_bounds__(256) void k_plan(const int32_t* __restrict__ bcnt,
       for (int guard_e = 0; guard_e <= E; ++guard_e) {
         const int Lr0 = __shfl(ell, r, 64) + (bwd ? lam * __shfl(nrem, r, 64) : 0);
         if (Lr0 <= tau) break;
+        // Backward mode: a home expert with at most lambda blocks and no copy
+        // elsewhere has no candidate (a new copy must move more than lambda
+        // blocks), and a failed search changes nothing, so it is skipped
+        // here rather than searched.  No move of another expert can give it
+        // a copy, so the experts that remain keep their snapshot order.
         long long bk = 0;
         for (int i = 0, e = lane; e < E; ++i, e += 64)
           if (h_s[e] == r && !((done >> i) & 1u) && qh[e] > 0) {
+            bool can = !bwd || qh[e] > lam;
+            if (!can) {
+              int any = 0;
+#pragma unroll
+              for (int t = 0; t < 8; ++t) any |= qn[e * 8 + t];
+              can = any != 0;                   // copy counts are never negative
+            }
+            if (!can) continue;
             const long long kk = ((long long)qh[e] << 32) | (long long)(0xFFFFFFFFu - (uint32_t)e);
             if (kk > bk) bk = kk;
           }
@@ -307,7 +330,7 @@ __global__ __launch_bounds__(256) void k_plan(const int32_t* __restrict__ bcnt,
               }
             }
           }
-          const long long bc = wave_max64(cand);
+          const long long bc = lanes8_max64(cand);     // candidates live on lanes t < P <= 8
           if (bc < 0) break;
           const int t = 255 - (int)(bc & 255);
           const int delta = __shfl(dl, t, 64);
