@@ -95,7 +95,8 @@ size_t moe_max_blocks(int T, int k, int E, int beta);
 
 /* Workspace needed by moe_route_stats, moe_plan, moe_forward and (when
  * with_backward != 0) moe_backward for these sizes; one workspace serves all
- * of them.  `L` (host) must be valid; returns 0 for invalid arguments. */
+ * of them.  `L` (host) must be valid; returns 0 for invalid arguments and for
+ * sizes moe_forward rejects as too large (see there). */
 size_t moe_workspace_size(const moe_layer* L, int T, int k, int beta, int P, int s,
                           int with_backward);
 
@@ -207,7 +208,16 @@ int moe_predict_cost(const int32_t* counts, const int32_t* block_offsets,
  *   z_save (nullable) [moe_max_slots][2*d_ff] act dtype: receives [G, U] of
  *     every routed row, as needed by moe_backward.
  *   stage_events (host, nullable): 5 hipEvent_t recorded on `stream` at
- *     start / after scheduling / after FC1 / after FC2 / after combine. */
+ *     start / after scheduling / after FC1 / after FC2 / after combine.
+ * Errors: MOE_ERR_ARG for an invalid layer, size or null pointer;
+ *   MOE_ERR_UNSUPPORTED for E > 512, P outside {1,2,4,8}, d not a multiple
+ *   of 128, d_ff not a multiple of 64 (128 with e4m3 weights), a dtype pair
+ *   other than fp32/fp32, bf16/bf16 or bf16 activations with e4m3 weights,
+ *   or an operand of 4 GB or more at 4 bytes per element (T*d,
+ *   moe_max_slots*2*d_ff, moe_max_slots*d or 2*d_ff*d elements times 4):
+ *   the kernels address operands with 32-bit byte offsets;
+ *   MOE_ERR_WORKSPACE for a missing, misaligned or short workspace.  A
+ *   block_worker entry outside [0, P) sets MOE_DEV_BAD_PLAN in *status_dev. */
 int moe_forward(const moe_layer* L, const void* x, const float* gates,
                 const int32_t* topk_ids, int T, int k, int beta, int P,
                 const int32_t* counts, const int32_t* block_offsets,
@@ -238,7 +248,11 @@ int moe_forward(const moe_layer* L, const void* x, const float* gates,
  * with x and A = SiLU(G) U unquantized: dw2 = Dq A^T, dw1 = dZq x^T.  The
  * requantized D and dZ live in `ws` (moe_workspace_size counts them): as
  * codes and scales, or, when d and d_ff are multiples of 256, widened back
- * to bf16 (code times scale), which is the value the products use. */
+ * to bf16 (code times scale), which is the value the products use.
+ * Errors: as moe_forward, plus MOE_ERR_ARG for s < 0.  On the device, a
+ *   plan whose blocks of one expert on one worker are not one contiguous run,
+ *   or that gives a worker more than s replica experts, sets
+ *   MOE_DEV_BAD_PLAN; an owner outside [0, P) sets MOE_DEV_BAD_OWNER. */
 int moe_backward(const moe_layer* L, const void* x, const float* gates, const void* dy,
                  const void* z_save, const int32_t* topk_ids, int T, int k, int beta,
                  int P, int s, const int32_t* counts, const int32_t* block_offsets,

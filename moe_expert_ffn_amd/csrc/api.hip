@@ -54,6 +54,19 @@ bool sizes_ok(int T, int k, int E, int beta) {
   return slots < (1ll << 31);
 }
 
+// The GEMM kernels address every operand through buffer descriptors, whose
+// sizes and offsets are 32-bit byte counts, and form row offsets as 32-bit
+// element counts.  Each such operand must therefore span less than 4 GB:
+// token rows (x, dy, y, dx), the slot-indexed buffers (A or dZ, O, P, z_save,
+// the requantized D) and one expert's weights.  Checked with 4 bytes per
+// element, which covers every dtype.
+bool extents_ok(const Sizes& z) {
+  const unsigned long long lim = 1ull << 32, S = (unsigned long long)z.max_slots;
+  const unsigned long long d = (unsigned long long)z.d, f = (unsigned long long)z.dff;
+  return (unsigned long long)z.T * d * 4 < lim && S * 2 * f * 4 < lim && S * d * 4 < lim &&
+         2 * f * d * 4 < lim;
+}
+
 }  // namespace
 
 extern "C" {
@@ -88,6 +101,7 @@ size_t moe_workspace_size(const moe_layer* L, int T, int k, int beta, int P, int
   size_t need = route_ws_bytes(T, k, L->E);
   if (L->E <= kMaxPlanExperts && L->d > 0 && L->d_ff > 0) {
     const Sizes z = make_sizes(L, T, k, beta, P, s);
+    if (!extents_ok(z)) return 0;
     const size_t f = exec_layout(z, false).total;
     if (f > need) need = f;
     if (with_backward) {
@@ -191,6 +205,7 @@ int moe_forward(const moe_layer* L, const void* x, const float* gates, const int
       !slot_to_row || !block_worker || !status_dev)
     return MOE_ERR_ARG;
   const Sizes z = make_sizes(L, T, k, beta, P, 0);
+  if (!extents_ok(z)) return MOE_ERR_UNSUPPORTED;
   if (!ws_ok(ws, ws_bytes, exec_layout(z, false).total)) return MOE_ERR_WORKSPACE;
   LayerPtrs Lp{L->w1, L->w2, L->w1_scale, L->w2_scale, L->act_dtype, L->w_dtype};
   return launch_forward(z, Lp, x, gates, counts, block_offsets, row_to_slot, slot_to_row,
@@ -214,6 +229,7 @@ int moe_backward(const moe_layer* L, const void* x, const float* gates, const vo
       !block_offsets || !slot_to_row || !owner || !block_worker || !dw1 || !dw2 || !status_dev)
     return MOE_ERR_ARG;
   const Sizes z = make_sizes(L, T, k, beta, P, s);
+  if (!extents_ok(z)) return MOE_ERR_UNSUPPORTED;
   if (!ws_ok(ws, ws_bytes, exec_layout(z, true).total)) return MOE_ERR_WORKSPACE;
   LayerPtrs Lp{L->w1, L->w2, L->w1_scale, L->w2_scale, L->act_dtype, L->w_dtype};
   return launch_backward(z, Lp, x, gates, dy, z_save, counts, block_offsets, row_to_slot,
