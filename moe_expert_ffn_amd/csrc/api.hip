@@ -54,14 +54,15 @@ bool sizes_ok(int T, int k, int E, int beta) {
   return slots < (1ll << 31);
 }
 
-// The GEMM kernels address every operand through buffer descriptors, whose
-// sizes and offsets are 32-bit byte counts, and form row offsets as 32-bit
-// element counts.  Each such operand must therefore span less than 4 GB:
-// token rows (x, dy, y, dx), the slot-indexed buffers (A or dZ, O, P, z_save,
-// the requantized D) and one expert's weights.  Checked with 4 bytes per
-// element, which covers every dtype.
+// The GEMM kernels address every operand through buffer descriptors with
+// 32-bit byte offsets, and send masked rows to offset 2^31, which reads as
+// zeros only while the descriptor's size is below it.  Each such operand must
+// therefore span less than 2 GiB: token rows (x, dy, y, dx), the
+// slot-indexed buffers (A or dZ, O, P, z_save, the requantized D) and one
+// expert's weights.  Checked with 4 bytes per element, which covers every
+// dtype.
 bool extents_ok(const Sizes& z) {
-  const unsigned long long lim = 1ull << 32, S = (unsigned long long)z.max_slots;
+  const unsigned long long lim = 1ull << 31, S = (unsigned long long)z.max_slots;
   const unsigned long long d = (unsigned long long)z.d, f = (unsigned long long)z.dff;
   return (unsigned long long)z.T * d * 4 < lim && S * 2 * f * 4 < lim && S * d * 4 < lim &&
          2 * f * d * 4 < lim;

@@ -54,23 +54,24 @@ def test_workspace_size_and_rejections():
     assert lib.moe_workspace_size(ctypes.byref(L), 256, 2, 0, 4, 1, 0) == 0     # beta < 1
 
 
-def test_operands_of_4gb_or_more_rejected():
-    """The GEMM kernels address operands with 32-bit byte offsets: sizes whose
-    token rows, slot buffers or expert weights reach 4 GB (at 4 bytes per
-    element) are refused before anything is launched."""
+def test_operands_of_2gib_or_more_rejected():
+    """The GEMM kernels address operands with 32-bit byte offsets and read
+    masked rows at offset 2^31: sizes whose token rows, slot buffers or expert
+    weights reach 2 GiB (at 4 bytes per element) are refused before anything
+    is launched."""
     lib = B.load()
     P = ctypes.c_void_p(16)
     L = _layer()                                            # d = 128, d_ff = 64
-    T = 1 << 23                                             # T * d * 4 = 4 GB exactly
+    T = 1 << 22                                             # T * d * 4 = 2 GiB exactly
     assert lib.moe_workspace_size(ctypes.byref(L), T, 2, 16, 4, 1, 1) == 0
-    # 2^20 tokens, top-2: token rows 0.5 GB, slot buffers about 1 GB each
-    assert lib.moe_workspace_size(ctypes.byref(L), 1 << 20, 2, 16, 4, 1, 1) > 0
+    # 2^19 tokens, top-2: token rows 256 MiB, slot buffers about 512 MiB each
+    assert lib.moe_workspace_size(ctypes.byref(L), 1 << 19, 2, 16, 4, 1, 1) > 0
     assert lib.moe_forward(ctypes.byref(L), P, P, P, T, 2, 16, 4, *([P] * 8), P, 1 << 30,
                            None, None) == B.MOE_ERR_UNSUPPORTED
     assert lib.moe_backward(ctypes.byref(L), P, P, P, P, P, T, 2, 16, 4, 1, *([P] * 10), P,
                             1 << 30, None, None) == B.MOE_ERR_UNSUPPORTED
-    # one expert's weights: 2 d_ff d elements at 4 bytes must stay below 4 GB
-    wide = _layer(d=32768, dff=16384)
+    # one expert's weights: 2 d_ff d elements at 4 bytes must stay below 2 GiB
+    wide = _layer(d=16384, dff=16384)
     assert lib.moe_workspace_size(ctypes.byref(wide), 16, 2, 16, 4, 1, 0) == 0
 
 
