@@ -213,10 +213,10 @@ int moe_predict_cost(const int32_t* counts, const int32_t* block_offsets,
  *   MOE_ERR_UNSUPPORTED for E > 512, P outside {1,2,4,8}, d not a multiple
  *   of 128, d_ff not a multiple of 64 (128 with e4m3 weights), a dtype pair
  *   other than fp32/fp32, bf16/bf16 or bf16 activations with e4m3 weights,
- *   or an operand of 2 GiB or more at 4 bytes per element (T*d,
- *   moe_max_slots*2*d_ff, moe_max_slots*d or 2*d_ff*d elements times 4):
- *   the kernels address operands with 32-bit byte offsets and read masked
- *   rows at offset 2^31;
+ *   or an operand of 2 GiB or more (T*d, moe_max_slots*2*d_ff or
+ *   moe_max_slots*d elements of the activation dtype, or 2*d_ff*d of the
+ *   weight dtype): the kernels address operands with 32-bit byte offsets and
+ *   read masked rows at offset 2^31;
  *   MOE_ERR_WORKSPACE for a missing, misaligned or short workspace.  A
  *   block_worker entry outside [0, P) sets MOE_DEV_BAD_PLAN in *status_dev. */
 int moe_forward(const moe_layer* L, const void* x, const float* gates,

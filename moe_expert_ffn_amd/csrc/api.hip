@@ -58,14 +58,14 @@ bool sizes_ok(int T, int k, int E, int beta) {
 // 32-bit byte offsets, and send masked rows to offset 2^31, which reads as
 // zeros only while the descriptor's size is below it.  Each such operand must
 // therefore span less than 2 GiB: token rows (x, dy, y, dx), the
-// slot-indexed buffers (A or dZ, O, P, z_save, the requantized D) and one
-// expert's weights.  Checked with 4 bytes per element, which covers every
-// dtype.
+// slot-indexed buffers (A or dZ, O, P, z_save, the requantized D), all in the
+// activation dtype, and one expert's weights.
 bool extents_ok(const Sizes& z) {
   const unsigned long long lim = 1ull << 31, S = (unsigned long long)z.max_slots;
   const unsigned long long d = (unsigned long long)z.d, f = (unsigned long long)z.dff;
-  return (unsigned long long)z.T * d * 4 < lim && S * 2 * f * 4 < lim && S * d * 4 < lim &&
-         2 * f * d * 4 < lim;
+  const unsigned long long ab = (unsigned long long)z.act_bytes, wb = z.fp8 ? 1ull : ab;
+  return (unsigned long long)z.T * d * ab < lim && S * 2 * f * ab < lim && S * d * ab < lim &&
+         2 * f * d * wb < lim;
 }
 
 }  // namespace

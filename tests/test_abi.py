@@ -57,8 +57,8 @@ def test_workspace_size_and_rejections():
 def test_operands_of_2gib_or_more_rejected():
     """The GEMM kernels address operands with 32-bit byte offsets and read
     masked rows at offset 2^31: sizes whose token rows, slot buffers or expert
-    weights reach 2 GiB (at 4 bytes per element) are refused before anything
-    is launched."""
+    weights reach 2 GiB (in their own dtypes) are refused before anything is
+    launched."""
     lib = B.load()
     P = ctypes.c_void_p(16)
     L = _layer()                                            # d = 128, d_ff = 64
@@ -70,9 +70,16 @@ def test_operands_of_2gib_or_more_rejected():
                            None, None) == B.MOE_ERR_UNSUPPORTED
     assert lib.moe_backward(ctypes.byref(L), P, P, P, P, P, T, 2, 16, 4, 1, *([P] * 10), P,
                             1 << 30, None, None) == B.MOE_ERR_UNSUPPORTED
-    # one expert's weights: 2 d_ff d elements at 4 bytes must stay below 2 GiB
+    # one expert's weights: 2 d_ff d fp32 elements must stay below 2 GiB
     wide = _layer(d=16384, dff=16384)
     assert lib.moe_workspace_size(ctypes.byref(wide), 16, 2, 16, 4, 1, 0) == 0
+    # the DeepSeek-V3 share (bf16 activations, e4m3 weights): 10.8k tokens at top-8 reserve
+    # about 90k slots, 1.3 GB of bf16 O rows, which the bf16 extent admits
+    ds = B.Layer(32, 7168, 2048, B.MOE_BF16, B.MOE_FP8_E4M3, 16, 32, 64, 64)
+    assert lib.moe_workspace_size(ctypes.byref(ds), 10800, 8, 128, 8, 4, 1) > 0
+    # the same shapes in fp32 would need 2.6 GB of O rows
+    ds32 = _layer(E=32, d=7168, dff=2048)
+    assert lib.moe_workspace_size(ctypes.byref(ds32), 10800, 8, 128, 8, 4, 1) == 0
 
 
 def test_host_validation_errors():
