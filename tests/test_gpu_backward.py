@@ -99,3 +99,56 @@ def test_backward_full_size_sampled(kappa):
     e_w2 = rel_l2(dw2[experts].double().cpu().numpy(), np.stack([o["dw2"][e] for e in experts]))
     say(f"  experts={experts} replicated={len(replicated)} dx={e_dx:.3e} dw1={e_w1:.3e} dw2={e_w2:.3e}")
     assert max(e_dx, e_w1, e_w2) <= 2e-2
+
+
+def _masked_routes(w, T, frac_tokens_masked, seed):
+    """Routes with whole tokens masked (every slot -1) and, in the rest, some
+    single slots masked; gates renormalised over the kept slots."""
+    rng = np.random.default_rng(seed)
+    ids = np.stack([rng.choice(w.E, size=w.k, replace=False) for _ in range(T)]).astype(np.int32)
+    ids[rng.random((T, w.k)) < 0.2] = -1
+    ids[rng.random(T) < frac_tokens_masked] = -1
+    g = rng.random((T, w.k)).astype(np.float32) * (ids >= 0)
+    s = g.sum(axis=1, keepdims=True)
+    gates = np.where(s > 0, g / np.where(s > 0, s, 1), 0).astype(np.float32)
+    return ids, gates
+
+
+@pytest.mark.parametrize("name", ["stream_bf16", "small_f32"])
+def test_nothing_routed_writes_zeros(name):
+    """No routed row at all: y, dx and every expert's weight gradients are
+    written as zeros (buffers filled with NaN beforehand), status stays 0."""
+    w = SMALL[name]
+    say(f"[nothing-routed] {name}")
+    T = 64
+    ids = np.full((T, w.k), -1, dtype=np.int32)
+    gates = np.zeros((T, w.k), dtype=np.float32)
+    c = Case(w, 0, backward=True, ids=ids, gates=gates)
+    r = c.runner
+    for t in (r.y, r.dx, r.dw1, r.dw2):
+        t.fill_(float("nan"))
+    dx, dw1, dw2 = _run(c)
+    assert c.status() == 0
+    for name_, t in (("y", r.y), ("dx", dx), ("dw1", dw1), ("dw2", dw2)):
+        assert not torch.isnan(t).any(), f"{name_} left unwritten"
+        assert torch.count_nonzero(t) == 0, f"{name_} not zero"
+
+
+def test_masked_tokens_match_oracle():
+    """Whole tokens without an expert (all slots -1) and single masked slots,
+    on the persistent kernels with replicas: dx of a masked token is zero and
+    everything matches the oracle."""
+    w = SMALL["stream_bf16"]
+    say("[masked-tokens] stream_bf16")
+    ids, gates = _masked_routes(w, 500, 0.3, 7)
+    c = Case(w, 0, backward=True, ids=ids, gates=gates)
+    c.runner.dx.fill_(float("nan"))
+    dx, dw1, dw2 = _run(c)
+    assert c.status() == 0
+    gone = np.where((ids < 0).all(axis=1))[0]
+    assert gone.size > 0 and torch.count_nonzero(dx[torch.from_numpy(gone).to(dx.device)]) == 0
+    o = _oracle(c)
+    refs = (o["dx"], np.stack([o["dw1"][e] for e in range(w.E)]),
+            np.stack([o["dw2"][e] for e in range(w.E)]))
+    for got, ref in zip((dx, dw1, dw2), refs):
+        assert rel_l2(got.double().cpu().numpy(), ref) <= 2e-2
