@@ -152,3 +152,22 @@ def test_masked_tokens_match_oracle():
             np.stack([o["dw2"][e] for e in range(w.E)]))
     for got, ref in zip((dx, dw1, dw2), refs):
         assert rel_l2(got.double().cpu().numpy(), ref) <= 2e-2
+
+
+@pytest.mark.parametrize("name", ["stream_bf16", "small_bf16"])
+def test_single_worker_matches_oracle(name):
+    """P = 1: one worker owns every CU and every expert (no replica is possible);
+    the layer still matches the oracle and dx equals the P = 8 result bit for bit."""
+    w = SMALL[name]
+    say(f"[single-worker] {name}")
+    c1 = Case(w, 0, backward=True, P=1)
+    dx1, dw1, dw2 = _run(c1)
+    assert c1.status() == 0
+    o = _oracle(c1)
+    refs = (o["dx"], np.stack([o["dw1"][e] for e in range(w.E)]),
+            np.stack([o["dw2"][e] for e in range(w.E)]))
+    for got, ref in zip((dx1, dw1, dw2), refs):
+        assert rel_l2(got.double().cpu().numpy(), ref) <= 2e-2
+    c8 = Case(w, 0, backward=True)
+    dx8, _, _ = _run(c8)
+    assert torch.equal(dx1, dx8)

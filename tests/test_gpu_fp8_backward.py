@@ -213,3 +213,22 @@ def test_quantize_rounding_ties():
     codes, scales = _quant_dev(src, rows, cols, rows)
     assert np.all(scales == 1.0)
     _check_exact(codes, scales, src.float().numpy(), rows)
+
+
+def test_fp8_nothing_routed_writes_zeros():
+    """e4m3 weights, every id -1: the requantization passes see no used block
+    and the outputs and weight gradients are still written, as zeros."""
+    w = SMALL["fp8_stream"]
+    say("[fp8-nothing-routed]")
+    T = 64
+    ids = np.full((T, w.k), -1, dtype=np.int32)
+    gates = np.zeros((T, w.k), dtype=np.float32)
+    c = Case(w, 0, backward=True, ids=ids, gates=gates)
+    r = c.runner
+    for t in (r.y, r.dx, r.dw1, r.dw2):
+        t.fill_(float("nan"))
+    dx, dw1, dw2 = _run(c)
+    assert c.status() == 0
+    for name, t in (("y", r.y), ("dx", dx), ("dw1", dw1), ("dw2", dw2)):
+        assert not torch.isnan(t).any(), f"{name} left unwritten"
+        assert torch.count_nonzero(t) == 0, f"{name} not zero"
