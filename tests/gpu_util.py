@@ -35,7 +35,7 @@ class LazyWeights:
 
 class Case:
     def __init__(self, w: Workload, kappa, device="cuda", P=None, s=None, backward=False, salt=0,
-                 ids=None, gates=None):
+                 ids=None, gates=None, lam=12):
         self.w = w
         self.P = w.P if P is None else P
         self.s = w.s if s is None else s
@@ -55,7 +55,8 @@ class Case:
         self.dy = make_dy(w, T, device, salt) if backward else None
         self.runner = LayerRunner(self.w1, self.w2, self.w1s, self.w2s, act_dtype=self.act, T=T,
                                   k=w.k, beta=w.beta, P=self.P, s=self.s,
-                                  owner=torch.from_numpy(self.owner_np), with_backward=backward)
+                                  owner=torch.from_numpy(self.owner_np), with_backward=backward,
+                                  lam=lam)
 
     def oracle_inputs(self):
         return (self.x.double().cpu().numpy(), LazyWeights(self.w1, self.w1s),

@@ -171,3 +171,24 @@ def test_single_worker_matches_oracle(name):
     c8 = Case(w, 0, backward=True)
     dx8, _, _ = _run(c8)
     assert torch.equal(dx1, dx8)
+
+
+@pytest.mark.parametrize("name", ["stream_bf16", "many_experts_bf16"])
+def test_runs_are_bitwise_deterministic(name):
+    """Two steps on the same inputs give identical y, dx, dW1 and dW2, bit for
+    bit: fixed tile accumulation order, slot-order combines and the fixed-order
+    replica reduction (lambda 1, so the backward plan places replicas)."""
+    w = SMALL[name]
+    say(f"[determinism] {name}")
+    c = Case(w, 0, backward=True, lam=1)
+    dx_a, dw1_a, dw2_a = _run(c)
+    y_a = c.runner.y.clone()
+    reps = int(c.runner.plan_b["plan_info"][2].item())
+    say(f"  backward replicas {reps}")
+    assert reps > 0
+    for t in (c.runner.y, c.runner.dx, c.runner.dw1, c.runner.dw2):
+        t.fill_(float("nan"))
+    dx_b, dw1_b, dw2_b = _run(c)
+    assert torch.equal(y_a, c.runner.y)
+    assert torch.equal(dx_a, dx_b)
+    assert torch.equal(dw1_a, dw1_b) and torch.equal(dw2_a, dw2_b)
