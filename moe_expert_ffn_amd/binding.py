@@ -118,6 +118,32 @@ def act_code(dtype) -> int:
     return MOE_F32 if dtype == torch.float32 else MOE_BF16
 
 
+def _act_dtype(layer) -> torch.dtype:
+    return torch.float32 if layer.act_dtype == MOE_F32 else torch.bfloat16
+
+
+def _ids_shape(topk_ids):
+    if topk_ids.dim() != 2:
+        raise MoeError(f"topk_ids: expected [T][k], got {tuple(topk_ids.shape)}")
+    _expect(topk_ids, torch.int32, 0, "topk_ids")
+    return topk_ids.shape
+
+
+def _expect_route(rs, T, k, E, beta):
+    """The routing statistics the executors read (from route_stats)."""
+    _expect(rs["counts"], torch.int32, E, "counts")
+    _expect(rs["block_offsets"], torch.int32, E + 1, "block_offsets")
+    _expect(rs["row_to_slot"], torch.int32, T * k, "row_to_slot")
+    _expect(rs["slot_to_row"], torch.int32, max_slots(T, k, E, beta), "slot_to_row")
+
+
+def _expect_plan_out(out, E, P):
+    _expect(out["q"], torch.int32, E * P, "q")
+    _expect(out["load"], torch.int32, P, "load")
+    _expect(out["block_worker"], torch.int32, 1, "block_worker")   # [max blocks]: not known here
+    _expect(out["plan_info"], torch.int32, 4, "plan_info")
+
+
 def make_layer(w1, w2, w1_scale=None, w2_scale=None, act_dtype=torch.bfloat16) -> Layer:
     _require_device(w1, w2, w1_scale, w2_scale)
     E, two_dff, d = w1.shape
@@ -167,7 +193,15 @@ def alloc_route(T, k, E, beta, device):
 def route_stats(topk_ids: torch.Tensor, E: int, beta: int, out: dict, ws: torch.Tensor,
                 status: torch.Tensor):
     _require_device(topk_ids, ws, status, *out.values())
-    T, k = topk_ids.shape
+    T, k = _ids_shape(topk_ids)
+    _expect(out["counts"], torch.int32, E, "counts")
+    _expect(out["offsets"], torch.int32, E + 1, "offsets")
+    _expect(out["block_counts"], torch.int32, E, "block_counts")
+    _expect(out["block_offsets"], torch.int32, E + 1, "block_offsets")
+    _expect(out["row_to_slot"], torch.int32, T * k, "row_to_slot")
+    _expect(out["slot_to_row"], torch.int32, max_slots(T, k, E, beta), "slot_to_row")
+    _expect(out["kappa"], torch.float64, 1, "kappa")
+    _expect(status, torch.int32, 1, "status")
     wsp, wsn = _aligned(ws)
     _check(load().moe_route_stats(_ptr(topk_ids), T, k, E, beta, _ptr(out["counts"]),
                                   _ptr(out["offsets"]), _ptr(out["block_counts"]),
@@ -218,6 +252,11 @@ def quantize_token_blocks(src, rows, cols, block_rows, codes, scales, row_map=No
 def plan_gate(block_counts, block_offsets, owner, P, rho_milli, out, status):
     _require_device(block_counts, block_offsets, owner, status, *out.values())
     E = block_counts.numel()
+    _expect(block_counts, torch.int32, E, "block_counts")
+    _expect(block_offsets, torch.int32, E + 1, "block_offsets")
+    _expect(owner, torch.int32, E, "owner")
+    _expect_plan_out(out, E, P)
+    _expect(status, torch.int32, 1, "status")
     _check(load().moe_plan_gate(_ptr(block_counts), _ptr(block_offsets), _ptr(owner), E, P,
                                 rho_milli, _ptr(out["q"]), _ptr(out["load"]),
                                 _ptr(out["block_worker"]), _ptr(out["plan_info"]), _ptr(status),
@@ -228,6 +267,11 @@ def plan_gate(block_counts, block_offsets, owner, P, rho_milli, out, status):
 def plan(block_counts, block_offsets, owner, P, s, mode, lam, out, ws, status):
     _require_device(block_counts, block_offsets, owner, ws, status, *out.values())
     E = block_counts.numel()
+    _expect(block_counts, torch.int32, E, "block_counts")
+    _expect(block_offsets, torch.int32, E + 1, "block_offsets")
+    _expect(owner, torch.int32, E, "owner")
+    _expect_plan_out(out, E, P)
+    _expect(status, torch.int32, 1, "status")
     wsp, wsn = _aligned(ws)
     _check(load().moe_plan(_ptr(block_counts), _ptr(block_offsets), _ptr(owner), E, P, s, mode,
                            lam, _ptr(out["q"]), _ptr(out["load"]), _ptr(out["block_worker"]),
@@ -238,7 +282,16 @@ def plan(block_counts, block_offsets, owner, P, s, mode, lam, out, ws, status):
 def forward(layer: Layer, x, gates, topk_ids, beta, P, rs, block_worker, y, z_save, ws, status,
             events=None):
     _require_device(x, gates, topk_ids, y, z_save, ws, status, block_worker)
-    T, k = topk_ids.shape
+    T, k = _ids_shape(topk_ids)
+    act, E, d, dff = _act_dtype(layer), layer.E, layer.d, layer.d_ff
+    _expect(x, act, T * d, "x")
+    _expect(gates, torch.float32, T * k, "gates")
+    _expect(y, act, T * d, "y")
+    if z_save is not None:
+        _expect(z_save, act, max_slots(T, k, E, beta) * 2 * dff, "z_save")
+    _expect_route(rs, T, k, E, beta)
+    _expect(block_worker, torch.int32, 1, "block_worker")
+    _expect(status, torch.int32, 1, "status")
     wsp, wsn = _aligned(ws)
     ev = None if events is None else (ctypes.c_void_p * len(events))(*events)
     _check(load().moe_forward(ctypes.byref(layer), _ptr(x), _ptr(gates), _ptr(topk_ids), T, k,
@@ -251,7 +304,19 @@ def forward(layer: Layer, x, gates, topk_ids, beta, P, rs, block_worker, y, z_sa
 def backward(layer: Layer, x, gates, dy, z_save, topk_ids, beta, P, s, rs, owner, block_worker,
              dx, dw1, dw2, ws, status, events=None):
     _require_device(x, gates, dy, z_save, topk_ids, owner, block_worker, dx, dw1, dw2, ws, status)
-    T, k = topk_ids.shape
+    T, k = _ids_shape(topk_ids)
+    act, E, d, dff = _act_dtype(layer), layer.E, layer.d, layer.d_ff
+    _expect(x, act, T * d, "x")
+    _expect(gates, torch.float32, T * k, "gates")
+    _expect(dy, act, T * d, "dy")
+    _expect(z_save, act, max_slots(T, k, E, beta) * 2 * dff, "z_save")
+    _expect_route(rs, T, k, E, beta)
+    _expect(owner, torch.int32, E, "owner")
+    _expect(block_worker, torch.int32, 1, "block_worker")
+    _expect(dx, act, T * d, "dx")
+    _expect(dw1, torch.float32, E * 2 * dff * d, "dw1")
+    _expect(dw2, torch.float32, E * d * dff, "dw2")
+    _expect(status, torch.int32, 1, "status")
     wsp, wsn = _aligned(ws)
     ev = None if events is None else (ctypes.c_void_p * len(events))(*events)
     _check(load().moe_backward(ctypes.byref(layer), _ptr(x), _ptr(gates), _ptr(dy), _ptr(z_save),

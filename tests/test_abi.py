@@ -176,3 +176,68 @@ def test_quantizer_binding_checks_buffers():
     with pytest.raises(B.MoeError, match="row_map"):
         B.quantize_token_blocks(src, 64, 16, 128, ok_codes, ok_scales,
                                 row_map=FakeDev(torch.int64, 64))
+
+
+def test_executor_bindings_check_buffers():
+    """route_stats, plan, forward and backward refuse tensors of the wrong
+    element type or too few elements before anything reaches the device (an
+    undersized output would be written past its end)."""
+    import torch
+
+    class FakeDev:
+        def __init__(self, dtype, n, shape=None):
+            self.dtype, self._n, self.shape = dtype, n, shape if shape is not None else (n,)
+            self.is_cuda = True
+
+        def is_contiguous(self):
+            return True
+
+        def numel(self):
+            return self._n
+
+        def dim(self):
+            return len(self.shape)
+
+        def data_ptr(self):
+            return 16
+
+    T, k, E, beta, P, d, dff = 32, 2, 8, 16, 4, 128, 64
+    i32, f32 = torch.int32, torch.float32
+    ids = FakeDev(i32, T * k, (T, k))
+    S = B.max_slots(T, k, E, beta)
+    rs = {"counts": FakeDev(i32, E), "offsets": FakeDev(i32, E + 1),
+          "block_counts": FakeDev(i32, E), "block_offsets": FakeDev(i32, E + 1),
+          "row_to_slot": FakeDev(i32, T * k), "slot_to_row": FakeDev(i32, S),
+          "kappa": FakeDev(torch.float64, 1)}
+    ws, st = FakeDev(torch.uint8, 1 << 20), FakeDev(i32, 1)
+    with pytest.raises(B.MoeError, match="slot_to_row"):
+        B.route_stats(ids, E, beta, {**rs, "slot_to_row": FakeDev(i32, S - 1)}, ws, st)
+    with pytest.raises(B.MoeError, match="kappa"):
+        B.route_stats(ids, E, beta, {**rs, "kappa": FakeDev(f32, 1)}, ws, st)
+    with pytest.raises(B.MoeError, match="topk_ids"):
+        B.route_stats(FakeDev(i32, T * k, (T * k,)), E, beta, rs, ws, st)
+    plan = {"q": FakeDev(i32, E * P), "load": FakeDev(i32, P), "block_worker": FakeDev(i32, 64),
+            "plan_info": FakeDev(i32, 4)}
+    with pytest.raises(B.MoeError, match="q"):
+        B.plan(rs["block_counts"], rs["block_offsets"], FakeDev(i32, E), P, 1, 0, 12,
+               {**plan, "q": FakeDev(i32, E * P - 1)}, ws, st)
+    with pytest.raises(B.MoeError, match="owner"):
+        B.plan(rs["block_counts"], rs["block_offsets"], FakeDev(torch.int64, E), P, 1, 0, 12, plan,
+               ws, st)
+    L = B.Layer(E, d, dff, B.MOE_BF16, B.MOE_BF16, 16, 32, None, None)
+    bf = torch.bfloat16
+    x, g = FakeDev(bf, T * d), FakeDev(f32, T * k)
+    z = FakeDev(bf, S * 2 * dff)
+    bw = FakeDev(i32, 64)
+    with pytest.raises(B.MoeError, match="y"):
+        B.forward(L, x, g, ids, beta, P, rs, bw, FakeDev(f32, T * d), z, ws, st)
+    with pytest.raises(B.MoeError, match="z_save"):
+        B.forward(L, x, g, ids, beta, P, rs, bw, FakeDev(bf, T * d), FakeDev(bf, S * dff), ws, st)
+    own = FakeDev(i32, E)
+    dw1, dw2 = FakeDev(f32, E * 2 * dff * d), FakeDev(f32, E * d * dff)
+    with pytest.raises(B.MoeError, match="dw1"):
+        B.backward(L, x, g, x, z, ids, beta, P, 1, rs, own, bw, FakeDev(bf, T * d),
+                   FakeDev(f32, E * 2 * dff * d - 1), dw2, ws, st)
+    with pytest.raises(B.MoeError, match="gates"):
+        B.backward(L, x, FakeDev(bf, T * k), x, z, ids, beta, P, 1, rs, own, bw,
+                   FakeDev(bf, T * d), dw1, dw2, ws, st)
