@@ -290,7 +290,7 @@ def forward(layer: Layer, x, gates, topk_ids, beta, P, rs, block_worker, y, z_sa
     if z_save is not None:
         _expect(z_save, act, max_slots(T, k, E, beta) * 2 * dff, "z_save")
     _expect_route(rs, T, k, E, beta)
-    _expect(block_worker, torch.int32, 1, "block_worker")
+    _expect(block_worker, torch.int32, max_blocks(T, k, E, beta), "block_worker")
     _expect(status, torch.int32, 1, "status")
     wsp, wsn = _aligned(ws)
     ev = None if events is None else (ctypes.c_void_p * len(events))(*events)
@@ -312,7 +312,7 @@ def backward(layer: Layer, x, gates, dy, z_save, topk_ids, beta, P, s, rs, owner
     _expect(z_save, act, max_slots(T, k, E, beta) * 2 * dff, "z_save")
     _expect_route(rs, T, k, E, beta)
     _expect(owner, torch.int32, E, "owner")
-    _expect(block_worker, torch.int32, 1, "block_worker")
+    _expect(block_worker, torch.int32, max_blocks(T, k, E, beta), "block_worker")
     _expect(dx, act, T * d, "dx")
     _expect(dw1, torch.float32, E * 2 * dff * d, "dw1")
     _expect(dw2, torch.float32, E * d * dff, "dw2")

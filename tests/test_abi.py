@@ -228,7 +228,10 @@ def test_executor_bindings_check_buffers():
     bf = torch.bfloat16
     x, g = FakeDev(bf, T * d), FakeDev(f32, T * k)
     z = FakeDev(bf, S * 2 * dff)
-    bw = FakeDev(i32, 64)
+    bw = FakeDev(i32, B.max_blocks(T, k, E, beta))
+    with pytest.raises(B.MoeError, match="block_worker"):
+        B.forward(L, x, g, ids, beta, P, rs, FakeDev(i32, B.max_blocks(T, k, E, beta) - 1),
+                  FakeDev(bf, T * d), z, ws, st)
     with pytest.raises(B.MoeError, match="y"):
         B.forward(L, x, g, ids, beta, P, rs, bw, FakeDev(f32, T * d), z, ws, st)
     with pytest.raises(B.MoeError, match="z_save"):
