@@ -146,13 +146,25 @@ def _expect_plan_out(out, E, P):
 
 def make_layer(w1, w2, w1_scale=None, w2_scale=None, act_dtype=torch.bfloat16) -> Layer:
     _require_device(w1, w2, w1_scale, w2_scale)
+    if w1.dim() != 3 or w2.dim() != 3:
+        raise MoeError("w1 and w2 are [E][2 d_ff][d] and [E][d][d_ff]")
     E, two_dff, d = w1.shape
+    if tuple(w2.shape) != (E, d, two_dff // 2) or two_dff % 2:
+        raise MoeError(f"w2: expected {(E, d, two_dff // 2)}, got {tuple(w2.shape)}")
+    if w2.dtype != w1.dtype:
+        raise MoeError(f"w2: expected {w1.dtype}, got {w2.dtype}")
     if w1.dtype == torch.uint8:
         wcode = MOE_FP8_E4M3
+        if w1_scale is None or w2_scale is None:
+            raise MoeError("e4m3 weights need w1_scale and w2_scale")
+        _expect(w1_scale, torch.float32, E * -(-two_dff // 128) * -(-d // 128), "w1_scale")
+        _expect(w2_scale, torch.float32, E * -(-d // 128) * -(-(two_dff // 2) // 128), "w2_scale")
     elif w1.dtype == torch.float32:
         wcode = MOE_F32
-    else:
+    elif w1.dtype == torch.bfloat16:
         wcode = MOE_BF16
+    else:
+        raise MoeError(f"w1: unsupported element type {w1.dtype}")
     return Layer(E, d, two_dff // 2, act_code(act_dtype), wcode, w1.data_ptr(), w2.data_ptr(),
                  w1_scale.data_ptr() if w1_scale is not None else None,
                  w2_scale.data_ptr() if w2_scale is not None else None)

@@ -244,3 +244,46 @@ def test_executor_bindings_check_buffers():
     with pytest.raises(B.MoeError, match="gates"):
         B.backward(L, x, FakeDev(bf, T * k), x, z, ids, beta, P, 1, rs, own, bw,
                    FakeDev(bf, T * d), dw1, dw2, ws, st)
+
+
+def test_make_layer_checks_weights():
+    """make_layer refuses mismatched weight shapes or types and e4m3 weights
+    without correctly sized block scales."""
+    import torch
+
+    class FakeW:
+        def __init__(self, dtype, shape):
+            self.dtype, self.shape = dtype, shape
+            self.is_cuda = True
+
+        def is_contiguous(self):
+            return True
+
+        def dim(self):
+            return len(self.shape)
+
+        def numel(self):
+            n = 1
+            for v in self.shape:
+                n *= v
+            return n
+
+        def data_ptr(self):
+            return 16
+
+    E, d, dff = 4, 256, 128
+    bf = torch.bfloat16
+    L = B.make_layer(FakeW(bf, (E, 2 * dff, d)), FakeW(bf, (E, d, dff)))
+    assert (L.E, L.d, L.d_ff, L.w_dtype) == (E, d, dff, B.MOE_BF16)
+    with pytest.raises(B.MoeError, match="w2"):
+        B.make_layer(FakeW(bf, (E, 2 * dff, d)), FakeW(bf, (E, dff, d)))
+    with pytest.raises(B.MoeError, match="w2"):
+        B.make_layer(FakeW(bf, (E, 2 * dff, d)), FakeW(torch.float32, (E, d, dff)))
+    u8 = torch.uint8
+    w1, w2 = FakeW(u8, (E, 2 * dff, d)), FakeW(u8, (E, d, dff))
+    with pytest.raises(B.MoeError, match="scale"):
+        B.make_layer(w1, w2)
+    s1, s2 = FakeW(torch.float32, (E, 2, 2)), FakeW(torch.float32, (E, 2, 1))
+    assert B.make_layer(w1, w2, s1, s2).w_dtype == B.MOE_FP8_E4M3
+    with pytest.raises(B.MoeError, match="w2_scale"):
+        B.make_layer(w1, w2, s1, FakeW(torch.float32, (E, 1, 1)))
