@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -57,8 +57,10 @@ typedef enum {
 
 /* bits OR-ed into *status_dev by device code */
 #define MOE_DEV_BAD_EXPERT 1   /* a top-k id >= E (that row is skipped) */
-#define MOE_DEV_BAD_PLAN   2   /* block_worker outside [0,P), or a worker with more
-                                  than s non-home experts (those blocks are skipped) */
+#define MOE_DEV_BAD_PLAN   2   /* block_worker outside [0,P), a worker with more than s
+                                  non-home experts, an (expert, worker) pair whose
+                                  blocks are not one run (those blocks are skipped),
+                                  or a plan that does not fit block_worker */
 #define MOE_DEV_BAD_OWNER  4   /* owner[e] outside [0,P) */
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
@@ -130,20 +132,23 @@ int moe_route_stats(const int32_t* topk_ids, int T, int k, int E, int beta,
  *   the quota floor u_min (>= 1 blocks): no replica is made for fewer blocks.
  *   s = 0 gives fixed placement (every mode).
  * Outputs: q [E][P] blocks of e on r; load [P] = l_r; block_worker
- *   [moe_max_blocks]: worker of each block (expert e's blocks go to its owner
- *   first, then to ascending workers; entries past sum b are untouched);
- *   plan_info [4] = {objective, chosen search 0..3 (4 for MOE_PLAN_QUOTA),
- *   replica count, tau (ceil(sum b / P), or the threshold found by
- *   MOE_PLAN_QUOTA)}.
+ *   [block_worker_cap entries, e.g. moe_max_blocks]: worker of each block
+ *   (expert e's blocks go to its owner first, then to ascending workers;
+ *   entries past sum b are untouched); plan_info [4] = {objective, chosen
+ *   search 0..3 (4 for MOE_PLAN_QUOTA), replica count, tau (ceil(sum b / P),
+ *   or the threshold found by MOE_PLAN_QUOTA)}.
  * Errors: MOE_ERR_ARG for a bad mode, s < 0, lambda < 0 (< 1 with
- *   MOE_PLAN_QUOTA) or a null pointer; MOE_ERR_UNSUPPORTED for E > 512 or P
- *   outside {1,2,4,8}; an owner outside [0, P) sets MOE_DEV_BAD_OWNER in
- *   *status_dev.
+ *   MOE_PLAN_QUOTA), block_worker_cap < 0 or a null pointer;
+ *   MOE_ERR_UNSUPPORTED for E > 512 or P outside {1,2,4,8}; an owner outside
+ *   [0, P) sets MOE_DEV_BAD_OWNER in *status_dev; sum b = block_offsets[E]
+ *   above block_worker_cap sets MOE_DEV_BAD_PLAN and leaves block_worker
+ *   untouched (q, load and plan_info are still written).
  * Limits: 1 <= E <= 512, P in {1,2,4,8}, s >= 0, lambda >= 0. */
 int moe_plan(const int32_t* block_counts, const int32_t* block_offsets,
              const int32_t* owner, int E, int P, int s, int mode, int lambda,
-             int32_t* q, int32_t* load, int32_t* block_worker, int32_t* plan_info,
-             int32_t* status_dev, void* ws, size_t ws_bytes, void* stream);
+             int32_t* q, int32_t* load, int32_t* block_worker, int block_worker_cap,
+             int32_t* plan_info, int32_t* status_dev, void* ws, size_t ws_bytes,
+             void* stream);
 
 /* Runtime replication gate (MegaFlux summary, "Limitations": enable
  * replication only when the predicted saving exceeds its cost; "Empirical
@@ -157,14 +162,17 @@ int moe_plan(const int32_t* block_counts, const int32_t* block_offsets,
  * as the fixed placement (every block on its owner) and plan_info becomes
  * {fixed objective, -1, 0, tau}.
  *   block_counts [E], block_offsets [E+1], owner [E]: as given to moe_plan.
- *   q [E][P], load [P], block_worker [sum b], plan_info [4]: moe_plan's
- *   outputs, read and (when gated off) overwritten.
- * Errors: MOE_ERR_ARG for E < 1, rho_milli < 0 or a null pointer;
- *   MOE_ERR_UNSUPPORTED for E > 512 or P outside {1,2,4,8}; an owner outside
- *   [0, P) sets MOE_DEV_BAD_OWNER in *status_dev. */
+ *   q [E][P], load [P], block_worker [block_worker_cap], plan_info [4]:
+ *   moe_plan's outputs, read and (when gated off) overwritten.
+ * Errors: MOE_ERR_ARG for E < 1, rho_milli < 0, block_worker_cap < 0 or a
+ *   null pointer; MOE_ERR_UNSUPPORTED for E > 512 or P outside {1,2,4,8}; an
+ *   owner outside [0, P) sets MOE_DEV_BAD_OWNER in *status_dev; a gated-off
+ *   plan whose sum b exceeds block_worker_cap sets MOE_DEV_BAD_PLAN and
+ *   leaves block_worker untouched. */
 int moe_plan_gate(const int32_t* block_counts, const int32_t* block_offsets,
                   const int32_t* owner, int E, int P, int rho_milli, int32_t* q, int32_t* load,
-                  int32_t* block_worker, int32_t* plan_info, int32_t* status_dev, void* stream);
+                  int32_t* block_worker, int block_worker_cap, int32_t* plan_info,
+                  int32_t* status_dev, void* stream);
 
 /* Predicted time of one forward + backward pass under a pair of plans
  * ("Analytical Resource Management for Fine-grained MoE
@@ -269,20 +277,26 @@ int moe_backward(const moe_layer* L, const void* x, const float* gates, const vo
  * ties to even, magnitudes saturated at 448 (OCP e4m3fn), every step in fp32;
  * an all-zero block column gets scale 0 and codes 0.  Row r's values:
  *   row_map == NULL:  src[r * ld + c]
- *   row_map[r] < 0:   0
+ *   row_map[r] < 0 or row_map[r] >= src_rows * row_div:   0
  *   otherwise:        src[(gather ? row_map[r] / row_div : r) * ld + c]
  *                     * (row_scale ? row_scale[row_map[r]] : 1)
  * (the backward uses slot_to_row as row_map: with gather, row_div = k and
  * row_scale = gates it forms D = p * dy per slot; without, it masks padding).
- *   src bf16, device; codes [rows][cols] uint8; scales
+ *   src bf16 [src_rows][ld], device; row_map [rows] (nullable); row_scale
+ *   (nullable) [src_rows * row_div] fp32; codes [rows][cols] uint8; scales
  *   [ceil(rows / block_rows)][cols] fp32; all device pointers, caller-owned.
+ *   Every row read is below src_rows: in place (no map, or a map without
+ *   gather) rows < src_rows is required; gathered map values past
+ *   src_rows * row_div read as zero rows.
  * Errors: MOE_ERR_ARG for rows < 0, cols < 8, not a multiple of 8 or above
  *   8,388,480 (65535 tiles of 128 columns),
- *   ld < cols or not a multiple of 8, block_rows < 1, row_div < 1, or a null
+ *   ld < cols or not a multiple of 8, block_rows < 1, row_div < 1,
+ *   src_rows < 0, src_rows < rows when rows are read in place, or a null
  *   src/codes/scales. */
-int moe_quantize_token_blocks(const void* src, int ld, const int32_t* row_map, int gather,
-                              int row_div, const float* row_scale, int rows, int cols,
-                              int block_rows, uint8_t* codes, float* scales, void* stream);
+int moe_quantize_token_blocks(const void* src, int ld, int src_rows, const int32_t* row_map,
+                              int gather, int row_div, const float* row_scale, int rows,
+                              int cols, int block_rows, uint8_t* codes, float* scales,
+                              void* stream);
 
 /* Timing helpers so a caller without a HIP binding can time the stages:
  * create / destroy a hipEvent_t, and the milliseconds between two recorded

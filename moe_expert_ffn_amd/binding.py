@@ -15,6 +15,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_ffn.so")
 
+ABI_VERSION = 2                 # MOE_ABI_VERSION of the header these signatures follow
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 PLAN_FWD, PLAN_BWD, PLAN_QUOTA = 0, 1, 2
@@ -65,13 +66,13 @@ def load():
     lib.moe_route_stats.restype = _I
     lib.moe_route_stats.argtypes = [_P, _I, _I, _I, _I] + [_P] * 8 + [_P, _SZ, _P]
     lib.moe_plan.restype = _I
-    lib.moe_plan.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I] + [_P] * 5 + [_P, _SZ, _P]
+    lib.moe_plan.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I] + [_P] * 3 + [_I] + [_P] * 2 + [_P, _SZ, _P]
     lib.moe_quantize_token_blocks.restype = _I
-    lib.moe_quantize_token_blocks.argtypes = [_P, _I, _P, _I, _I, _P, _I, _I, _I, _P, _P, _P]
+    lib.moe_quantize_token_blocks.argtypes = [_P, _I, _I, _P, _I, _I, _P, _I, _I, _I, _P, _P, _P]
     lib.moe_predict_cost.restype = _I
     lib.moe_predict_cost.argtypes = [_P] * 5 + [_I] * 6 + [_P, _P, _P]
     lib.moe_plan_gate.restype = _I
-    lib.moe_plan_gate.argtypes = [_P, _P, _P, _I, _I, _I] + [_P] * 5 + [_P]
+    lib.moe_plan_gate.argtypes = [_P, _P, _P, _I, _I, _I] + [_P] * 3 + [_I] + [_P] * 2 + [_P]
     lib.moe_forward.restype = _I
     lib.moe_forward.argtypes = ([ctypes.POINTER(Layer), _P, _P, _P, _I, _I, _I, _I]
                                 + [_P] * 8 + [_P, _SZ, _P, _P])
@@ -83,6 +84,9 @@ def load():
     lib.moe_event_record.argtypes = [_P, _P]
     lib.moe_event_elapsed_ms.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_float)]
     lib.moe_device_info.argtypes = [ctypes.POINTER(_I)] * 3
+    if lib.moe_abi_version() != ABI_VERSION:
+        raise MoeError(f"{LIB_PATH} has ABI {lib.moe_abi_version()}, the binding expects "
+                       f"{ABI_VERSION}: rebuild it")
     _lib = lib
     return lib
 
@@ -140,7 +144,9 @@ def _expect_route(rs, T, k, E, beta):
 def _expect_plan_out(out, E, P):
     _expect(out["q"], torch.int32, E * P, "q")
     _expect(out["load"], torch.int32, P, "load")
-    _expect(out["block_worker"], torch.int32, 1, "block_worker")   # [max blocks]: not known here
+    # block_worker [>= sum b]: its size goes to the library, which writes nothing
+    # (and flags the plan) when the blocks do not fit
+    _expect(out["block_worker"], torch.int32, 1, "block_worker")
     _expect(out["plan_info"], torch.int32, 4, "plan_info")
 
 
@@ -241,21 +247,29 @@ def predict_cost(counts, block_offsets, bw_fwd, bw_bwd, owner, beta, P, d, d_ff,
 
 
 def quantize_token_blocks(src, rows, cols, block_rows, codes, scales, row_map=None, gather=False,
-                          row_div=1, row_scale=None, ld=None):
-    """Token-axis e4m3 codes [rows][cols] and scales [ceil(rows/block_rows)][cols]."""
+                          row_div=1, row_scale=None, ld=None, src_rows=None):
+    """Token-axis e4m3 codes [rows][cols] and scales [ceil(rows/block_rows)][cols].
+
+    src holds src_rows rows of ld elements (default: rows, the rows read in
+    place); gathered map values past src_rows * row_div read as zero rows, and
+    row_scale must hold src_rows * row_div entries."""
     _require_device(src, codes, scales, *[t for t in (row_map, row_scale) if t is not None])
+    ld = cols if ld is None else ld
+    if src_rows is None:
+        if gather:
+            raise MoeError("gathered rows need src_rows (the rows of src)")
+        src_rows = rows
     if rows > 0 and block_rows > 0:
         nblk = (rows + block_rows - 1) // block_rows
         _expect(codes, torch.uint8, rows * cols, "codes")
         _expect(scales, torch.float32, nblk * cols, "scales")
-        _expect(src, torch.bfloat16, 0 if gather else (rows - 1) * (cols if ld is None else ld) + cols,
-                "src")
+        _expect(src, torch.bfloat16, (src_rows - 1) * ld + cols if src_rows > 0 else 0, "src")
         if row_map is not None:
             _expect(row_map, torch.int32, rows, "row_map")
         if row_scale is not None:
-            _expect(row_scale, torch.float32, 1, "row_scale")
+            _expect(row_scale, torch.float32, src_rows * row_div, "row_scale")
     _check(load().moe_quantize_token_blocks(
-        _ptr(src), cols if ld is None else ld, _ptr(row_map) if row_map is not None else None,
+        _ptr(src), ld, src_rows, _ptr(row_map) if row_map is not None else None,
         1 if gather else 0, row_div, _ptr(row_scale) if row_scale is not None else None, rows, cols,
         block_rows, _ptr(codes), _ptr(scales), _stream()))
     return codes, scales
@@ -271,8 +285,8 @@ def plan_gate(block_counts, block_offsets, owner, P, rho_milli, out, status):
     _expect(status, torch.int32, 1, "status")
     _check(load().moe_plan_gate(_ptr(block_counts), _ptr(block_offsets), _ptr(owner), E, P,
                                 rho_milli, _ptr(out["q"]), _ptr(out["load"]),
-                                _ptr(out["block_worker"]), _ptr(out["plan_info"]), _ptr(status),
-                                _stream()))
+                                _ptr(out["block_worker"]), out["block_worker"].numel(),
+                                _ptr(out["plan_info"]), _ptr(status), _stream()))
     return out
 
 
@@ -287,7 +301,8 @@ def plan(block_counts, block_offsets, owner, P, s, mode, lam, out, ws, status):
     wsp, wsn = _aligned(ws)
     _check(load().moe_plan(_ptr(block_counts), _ptr(block_offsets), _ptr(owner), E, P, s, mode,
                            lam, _ptr(out["q"]), _ptr(out["load"]), _ptr(out["block_worker"]),
-                           _ptr(out["plan_info"]), _ptr(status), wsp, wsn, _stream()))
+                           out["block_worker"].numel(), _ptr(out["plan_info"]), _ptr(status),
+                           wsp, wsn, _stream()))
     return out
 
 

@@ -130,11 +130,11 @@ int moe_route_stats(const int32_t* topk_ids, int T, int k, int E, int beta, int3
 
 int moe_plan(const int32_t* block_counts, const int32_t* block_offsets, const int32_t* owner,
              int E, int P, int s, int mode, int lambda, int32_t* q, int32_t* load,
-             int32_t* block_worker, int32_t* plan_info, int32_t* status_dev, void* ws,
-             size_t ws_bytes, void* stream) {
+             int32_t* block_worker, int block_worker_cap, int32_t* plan_info,
+             int32_t* status_dev, void* ws, size_t ws_bytes, void* stream) {
   (void)ws;
   (void)ws_bytes;
-  if (E < 1 || s < 0 || lambda < 0 ||
+  if (E < 1 || s < 0 || lambda < 0 || block_worker_cap < 0 ||
       (mode != MOE_PLAN_FWD && mode != MOE_PLAN_BWD && mode != MOE_PLAN_QUOTA) ||
       (mode == MOE_PLAN_QUOTA && lambda < 1))
     return MOE_ERR_ARG;
@@ -143,30 +143,35 @@ int moe_plan(const int32_t* block_counts, const int32_t* block_offsets, const in
       !plan_info || !status_dev)
     return MOE_ERR_ARG;
   return launch_plan(block_counts, block_offsets, owner, E, P, s, mode, lambda, q, load,
-                     block_worker, plan_info, status_dev, (hipStream_t)stream);
+                     block_worker, block_worker_cap, plan_info, status_dev, (hipStream_t)stream);
 }
 
 int moe_plan_gate(const int32_t* block_counts, const int32_t* block_offsets, const int32_t* owner,
                   int E, int P, int rho_milli, int32_t* q, int32_t* load, int32_t* block_worker,
-                  int32_t* plan_info, int32_t* status_dev, void* stream) {
-  if (E < 1 || rho_milli < 0) return MOE_ERR_ARG;
+                  int block_worker_cap, int32_t* plan_info, int32_t* status_dev, void* stream) {
+  if (E < 1 || rho_milli < 0 || block_worker_cap < 0) return MOE_ERR_ARG;
   if (!valid_P(P) || E > kMaxPlanExperts) return MOE_ERR_UNSUPPORTED;
   if (!block_counts || !block_offsets || !owner || !q || !load || !block_worker || !plan_info ||
       !status_dev)
     return MOE_ERR_ARG;
   return launch_plan_gate(block_counts, block_offsets, owner, E, P, rho_milli, q, load,
-                          block_worker, plan_info, status_dev, (hipStream_t)stream);
+                          block_worker, block_worker_cap, plan_info, status_dev,
+                          (hipStream_t)stream);
 }
 
-int moe_quantize_token_blocks(const void* src, int ld, const int32_t* row_map, int gather,
-                              int row_div, const float* row_scale, int rows, int cols,
+int moe_quantize_token_blocks(const void* src, int ld, int src_rows, const int32_t* row_map,
+                              int gather, int row_div, const float* row_scale, int rows, int cols,
                               int block_rows, uint8_t* codes, float* scales, void* stream) {
   if (rows < 0 || cols < 8 || cols % 8 || cols > kQtMaxCols || ld < cols || ld % 8 ||
-      block_rows < 1 || row_div < 1)
+      block_rows < 1 || row_div < 1 || src_rows < 0)
     return MOE_ERR_ARG;
+  // rows read in place (no map, or a map without gather) need src_rows >= rows
+  if ((!row_map || !gather) && src_rows < rows) return MOE_ERR_ARG;
   if (!src || !codes || !scales) return MOE_ERR_ARG;
+  const long long lim = (long long)src_rows * row_div;
   return launch_quant_tok((const uint16_t*)src, ld, row_map, gather ? 1 : 0, row_div, row_scale,
-                          rows, cols, block_rows, codes, scales, (hipStream_t)stream);
+                          lim < INT32_MAX ? (int)lim : INT32_MAX, rows, cols, block_rows, codes,
+                          scales, (hipStream_t)stream);
 }
 
 int moe_predict_cost(const int32_t* counts, const int32_t* block_offsets,

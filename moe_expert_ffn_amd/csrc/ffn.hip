@@ -57,7 +57,12 @@ MOE_DEV int expert_of(int g, const int* boff_s, int E) {
 // blocks of one (expert, worker) pair must form one contiguous run; its slot
 // range and valid-row count become one weight-gradient segment, with a replica
 // slot when the worker is not the owner (rank among that worker's non-home
-// experts, in expert order).
+// experts, in expert order).  A pair that breaks the plan's constraints (its
+// blocks are not one run, or its worker already holds s replica experts) sets
+// MOE_DEV_BAD_PLAN and gets no segment: its weight-gradient rows are dropped,
+// and an owner without a segment receives only the replica partials (zeros
+// when there are none).  A plan with more blocks than the slot space holds
+// (block_offsets[E] > max_blocks) sets the bit and schedules nothing.
 MOE_DEV int block_rows(int g, int e, int beta, const int* boff_s, const int* cnt_s) {
   return min(beta, beta * boff_s[e] + cnt_s[e] - beta * g);
 }
@@ -85,8 +90,16 @@ __global__ __launch_bounds__(kSchedThreads) void k_sched(SchedArgs a) {
     for (int i = tid; i < E * P; i += NT) { s0_s[i] = INT_MAX; rows_s[i] = 0; starts_s[i] = 0; }
   __syncthreads();
   const int nb = boff_s[E];
-  if (BWL && nb > a.max_blocks) {                 // more blocks than the plan can hold
+  if (nb > a.max_blocks) {                        // more blocks than the slot space holds
     if (tid == 0) atomicOr(a.status, MOE_DEV_BAD_PLAN);
+    if (tid < P) {
+      a.mt_cnt[tid] = 0;
+      if (a.backward) a.seg_cnt[tid] = 0;
+    }
+    if (a.backward) {                             // the replica reduction zeroes every owner slot
+      for (int i = tid; i < E * P; i += NT) a.rep_slot[i] = -1;
+      for (int e = tid; e < E; e += NT) a.owner_has[e] = 0;
+    }
     return;
   }
   for (int g = tid; g < nb; g += NT) {
@@ -164,33 +177,31 @@ __global__ __launch_bounds__(kSchedThreads) void k_sched(SchedArgs a) {
     for (int pass = 0; pass < 2; ++pass) {
       for (int base = 0; base < E; base += 64) {
         const int e = base + lane;
-        int take = 0, dst = -1;
+        int cand = 0, dst = -1;
         bool bad = false;
         if (e < E) {
           const int h = a.owner[e];
           const int rows = rows_s[e * P + r];
           const bool home = (h == r);
-          if (rows > 0 && starts_s[e * P + r] != 1) bad = true;
-          take = (rows > 0 && home == (pass == 1) && h >= 0 && h < P) ? 1 : 0;
+          const bool mine = rows > 0 && home == (pass == 1) && h >= 0 && h < P;
+          if (mine && starts_s[e * P + r] != 1) bad = true;   // not one run of blocks
+          cand = (mine && !bad) ? 1 : 0;
           if (pass == 0) a.rep_slot[e * P + r] = -1;
         }
-        const int nonhome = (pass == 0) ? take : 0;
+        // replica slots are ranked among the valid non-home segments
+        const int nonhome = (pass == 0) ? cand : 0;
         const int rinc = wave_incl_scan(nonhome);
         const int rpos = rrun + rinc - nonhome;
         if (nonhome) {
-          if (rpos >= a.s) bad = true;
+          if (rpos >= a.s) { bad = true; cand = 0; }         // over the replica budget
           else dst = r * a.s + rpos;
         }
-        const int inc = wave_incl_scan(take);
-        const int pos = run + inc - take;
-        if (take) {
-          if (bad) {
-            atomicOr(a.status, MOE_DEV_BAD_PLAN);
-            a.seg[(size_t)r * E + pos] = make_int4(-1, 0, 0, -1);
-          } else {
-            a.seg[(size_t)r * E + pos] = make_int4(e, s0_s[e * P + r], rows_s[e * P + r], dst);
-            if (nonhome) a.rep_slot[e * P + r] = dst;
-          }
+        if (bad) atomicOr(a.status, MOE_DEV_BAD_PLAN);
+        const int inc = wave_incl_scan(cand);
+        const int pos = run + inc - cand;
+        if (cand) {
+          a.seg[(size_t)r * E + pos] = make_int4(e, s0_s[e * P + r], rows_s[e * P + r], dst);
+          if (nonhome) a.rep_slot[e * P + r] = dst;
         }
         run += __shfl(inc, 63, 64);
         rrun += __shfl(rinc, 63, 64);
@@ -485,8 +496,9 @@ static dim3 combine_grid(int T) { return dim3((unsigned)((T + 3) / 4)); }
 // amax / 448, code = e4m3(value / scale) with round to nearest, ties to even,
 // magnitudes saturated at 448; every step in fp32.  Row r's value is
 //   map == nullptr: src[r * ld + c]
-//   map[r] < 0:     0
-//   otherwise:      src[(gather ? map[r] / div : r) * ld + c] * (rscale ? rscale[map[r]] : 1).
+//   map[r] < 0 or map[r] >= map_lim:  0
+//   otherwise:      src[(gather ? map[r] / div : r) * ld + c] * (rscale ? rscale[map[r]] : 1)
+// (map_lim = rows of src times div, so a gathered row and its scale are in range).
 // One workgroup per (block b, 128 columns): 16 threads cover a row's 128
 // columns (8 each) and 16 rows are read at once.  Pass 1 takes each column's
 // amax over the block's rows (exact in any order), reduced through LDS; pass
@@ -504,7 +516,8 @@ constexpr int kQtCols = 128, kQtRowLanes = 16, kQtKeep = 8;
 template <bool DEQ>
 __global__ __launch_bounds__(256) void k_quant_tok(const uint16_t* src, int ld,
                                                    const int32_t* __restrict__ map, int gather, int div,
-                                                   const float* __restrict__ rscale, int rows,
+                                                   const float* __restrict__ rscale, int map_lim,
+                                                   int rows,
                                                    int cols, int brows, uint8_t* codes,
                                                    float* scales, uint16_t* deq,
                                                    const int32_t* __restrict__ blk_end) {
@@ -521,7 +534,7 @@ __global__ __launch_bounds__(256) void k_quant_tok(const uint16_t* src, int ld,
     float f = 1.f;
     if (map) {
       const int m = map[r];
-      ok = m >= 0;
+      ok = m >= 0 && m < map_lim;
       if (gather) srow = ok ? m / div : 0;
       if (rscale) f = rscale[ok ? m : 0];
     }
@@ -620,21 +633,23 @@ static dim3 quant_grid(int rows, int cols, int brows) {
 }
 
 int launch_quant_tok(const uint16_t* src, int ld, const int32_t* map, int gather, int div,
-                     const float* rscale, int rows, int cols, int brows, uint8_t* codes,
-                     float* scales, hipStream_t st, const int32_t* blk_end) {
+                     const float* rscale, int map_lim, int rows, int cols, int brows,
+                     uint8_t* codes, float* scales, hipStream_t st, const int32_t* blk_end) {
   if (rows > 0)
     hipLaunchKernelGGL(k_quant_tok<false>, quant_grid(rows, cols, brows), dim3(256), 0, st, src, ld,
-                       map, gather, div, rscale, rows, cols, brows, codes, scales, nullptr, blk_end);
+                       map, gather, div, rscale, map_lim, rows, cols, brows, codes, scales, nullptr,
+                       blk_end);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 // The same blocks, written back as bf16 code * scale into deq [rows][cols].
 static void launch_quant_dequant(const uint16_t* src, int ld, const int32_t* map, int gather,
-                                 int div, const float* rscale, int rows, int cols, int brows,
-                                 uint16_t* deq, const int32_t* blk_end, hipStream_t st) {
+                                 int div, const float* rscale, int map_lim, int rows, int cols,
+                                 int brows, uint16_t* deq, const int32_t* blk_end, hipStream_t st) {
   if (rows > 0)
     hipLaunchKernelGGL(k_quant_tok<true>, quant_grid(rows, cols, brows), dim3(256), 0, st, src, ld,
-                       map, gather, div, rscale, rows, cols, brows, nullptr, nullptr, deq, blk_end);
+                       map, gather, div, rscale, map_lim, rows, cols, brows, nullptr, nullptr, deq,
+                       blk_end);
 }
 
 // fp8 weight rows read K-major: element (k, n) = code[k * ld + n] * scale[k / 128][n / 128],
@@ -1844,8 +1859,8 @@ static void run_backward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_
   const int rows = (int)z.max_slots;
   launch_slot_gate(z, a, st);
   if constexpr (FP8)
-    launch_quant_dequant((const uint16_t*)a.dy, z.d, a.slot_to_row, 1, z.k, a.gates, rows, z.d,
-                         z.beta, (uint16_t*)a.dhat, a.boff + z.E, st);
+    launch_quant_dequant((const uint16_t*)a.dy, z.d, a.slot_to_row, 1, z.k, a.gates, z.T * z.k,
+                         rows, z.d, z.beta, (uint16_t*)a.dhat, a.boff + z.E, st);
   launch_stream<SrcDaT<FP8>, WC, RowW, typename SrcDaT<FP8>::OB>(a, z.dff / WC::BN, kStreamLds, st);
   rec(ev, 2, st);
   launch_stream<SrcDxT<FP8>, WC, RowW, typename SrcDxT<FP8>::OB>(a, z.d / WC::BN, kStreamLds, st);
@@ -1855,8 +1870,8 @@ static void run_backward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_
                        (const uint16_t*)a.bufO, row_to_slot, z.T, z.k, z.d, (uint16_t*)dx);
   rec(ev, 4, st);
   if constexpr (FP8)
-    launch_quant_dequant((const uint16_t*)a.bufA, 2 * z.dff, a.slot_to_row, 0, 1, nullptr, rows,
-                         2 * z.dff, z.beta, (uint16_t*)a.bufA, a.boff + z.E, st);
+    launch_quant_dequant((const uint16_t*)a.bufA, 2 * z.dff, a.slot_to_row, 0, 1, nullptr,
+                         z.T * z.k, rows, 2 * z.dff, z.beta, (uint16_t*)a.bufA, a.boff + z.E, st);
   launch_stream<SrcDwT<DwCfg, FP8>, DwCfg, MnSegOp, MnSegOp>(a, 0, kDwLds, st);
   rec(ev, 5, st);
   hipLaunchKernelGGL(k_bwd_reduce, dim3(num_cus() * 4), dim3(256), 0, st, a.rep_slot,
@@ -1874,12 +1889,12 @@ static void run_backward(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot
   static int gw = persistent_grid(k_bwd_dw<T, C, FP8>, C::NT, lds);
   const int rows = (int)z.max_slots;
   if constexpr (FP8)   // D = p * dy per slot, e4m3 along tokens, for dW2
-    launch_quant_tok((const uint16_t*)a.dy, z.d, a.slot_to_row, 1, z.k, a.gates, rows, z.d, z.beta,
-                     a.dq, a.dqs, st, a.boff + z.E);
+    launch_quant_tok((const uint16_t*)a.dy, z.d, a.slot_to_row, 1, z.k, a.gates, z.T * z.k, rows,
+                     z.d, z.beta, a.dq, a.dqs, st, a.boff + z.E);
   hipLaunchKernelGGL((k_bwd_da<T, C, FP8>), dim3(ga), dim3(C::NT), lds, st, a);
   if constexpr (FP8)   // dZ per slot (padding slots read as zero), for dW1
-    launch_quant_tok((const uint16_t*)a.bufA, 2 * z.dff, a.slot_to_row, 0, 1, nullptr, rows,
-                     2 * z.dff, z.beta, a.zq, a.zqs, st, a.boff + z.E);
+    launch_quant_tok((const uint16_t*)a.bufA, 2 * z.dff, a.slot_to_row, 0, 1, nullptr, z.T * z.k,
+                     rows, 2 * z.dff, z.beta, a.zq, a.zqs, st, a.boff + z.E);
   rec(ev, 2, st);
   hipLaunchKernelGGL((k_bwd_dx<T, C, FP8>), dim3(gx), dim3(C::NT), lds, st, a);
   rec(ev, 3, st);

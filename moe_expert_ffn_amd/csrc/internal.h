@@ -42,18 +42,20 @@ int launch_route_stats(const int32_t* ids, int T, int k, int E, int beta, int32_
                        int32_t* row_to_slot, int32_t* slot_to_row, double* kappa,
                        int32_t* status, void* ws, hipStream_t st);
 int launch_plan(const int32_t* bcnt, const int32_t* boff, const int32_t* owner, int E, int P,
-                int s, int mode, int lam, int32_t* q, int32_t* load, int32_t* bw,
+                int s, int mode, int lam, int32_t* q, int32_t* load, int32_t* bw, int bw_cap,
                 int32_t* info, int32_t* status, hipStream_t st);
 constexpr int kQtMaxCols = 65535 * 128;   // column tiles of the quantizer grid
+// map_lim: map values m >= map_lim read as zero rows (src rows * div)
 int launch_quant_tok(const uint16_t* src, int ld, const int32_t* map, int gather, int div,
-                     const float* rscale, int rows, int cols, int brows, uint8_t* codes,
-                     float* scales, hipStream_t st, const int32_t* blk_end = nullptr);
+                     const float* rscale, int map_lim, int rows, int cols, int brows,
+                     uint8_t* codes, float* scales, hipStream_t st,
+                     const int32_t* blk_end = nullptr);
 int launch_predict_cost(const int32_t* counts, const int32_t* boff, const int32_t* bw_f,
                         const int32_t* bw_b, const int32_t* owner, int E, int beta, int P, int d,
                         int dff, int G, long long* cost, int32_t* status, hipStream_t st);
 int launch_plan_gate(const int32_t* bcnt, const int32_t* boff, const int32_t* owner, int E, int P,
-                     int rho_milli, int32_t* q, int32_t* load, int32_t* bw, int32_t* info,
-                     int32_t* status, hipStream_t st);
+                     int rho_milli, int32_t* q, int32_t* load, int32_t* bw, int bw_cap,
+                     int32_t* info, int32_t* status, hipStream_t st);
 
 struct LayerPtrs {
   const void* w1;

@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void k_plan(const int32_t* __restrict__ bcnt,
                                               const int32_t* __restrict__ owner, int E, int P,
                                               int s, int mode, int lam, int32_t* q_out,
                                               int32_t* load_out, int32_t* bw_out,
-                                              int32_t* info_out, int32_t* status) {
+                                              int bw_cap, int32_t* info_out, int32_t* status) {
   extern __shared__ int sm[];
   int* b_s = sm;                     // [E]
   int* h_s = b_s + E;                // [E]
@@ -373,6 +373,10 @@ __global__ __launch_bounds__(256) void k_plan(const int32_t* __restrict__ bcnt,
     q_out[i] = (t == h_s[e]) ? qhb[e] : qnb[e * 8 + t];
   }
   const int nb = boff_s[E];
+  if (nb > bw_cap) {                 // block_worker cannot hold the plan: nothing written
+    if (tid == 0) atomicOr(status, MOE_DEV_BAD_PLAN);
+    return;
+  }
   for (int g = tid; g < nb; g += 256) {
     int lo = 0, hi = E;  // largest e with boff_s[e] <= g
     while (hi - lo > 1) {
@@ -470,7 +474,8 @@ __global__ __launch_bounds__(512) void k_plan_quota(const int32_t* __restrict__ 
                                                     const int32_t* __restrict__ owner, int E,
                                                     int P, int s, int umin, int32_t* q_out,
                                                     int32_t* load_out, int32_t* bw_out,
-                                                    int32_t* info_out, int32_t* status) {
+                                                    int bw_cap, int32_t* info_out,
+                                                    int32_t* status) {
   extern __shared__ int sm[];
   int* b_s = sm;                     // [E]
   int* h_s = b_s + E;                // [E]
@@ -572,6 +577,10 @@ __global__ __launch_bounds__(512) void k_plan_quota(const int32_t* __restrict__ 
     q_out[i] = (t == h_s[e]) ? b_s[e] - moved : mv_s[e * 8 + t];
   }
   const int nb = boff_s[E];
+  if (nb > bw_cap) {                 // block_worker cannot hold the plan: nothing written
+    if (tid == 0) atomicOr(status, MOE_DEV_BAD_PLAN);
+    return;
+  }
   for (int g = tid; g < nb; g += 512) {
     int lo = 0, hi = E;  // largest e with boff_s[e] <= g
     while (hi - lo > 1) {
@@ -609,7 +618,8 @@ __global__ __launch_bounds__(256) void k_plan_gate(const int32_t* __restrict__ b
                                                    const int32_t* __restrict__ boff,
                                                    const int32_t* __restrict__ owner, int E, int P,
                                                    int rho_milli, int32_t* q, int32_t* load,
-                                                   int32_t* bw, int32_t* info, int32_t* status) {
+                                                   int32_t* bw, int bw_cap, int32_t* info,
+                                                   int32_t* status) {
   __shared__ int ellfix[kMaxP], keep_s;
   const int tid = threadIdx.x;
   if (tid < kMaxP) ellfix[tid] = 0;
@@ -643,6 +653,10 @@ __global__ __launch_bounds__(256) void k_plan_gate(const int32_t* __restrict__ b
     q[i] = (t == h) ? bcnt[e] : 0;
   }
   const int nb = boff[E];
+  if (nb > bw_cap) {                 // block_worker cannot hold the plan: nothing written
+    if (tid == 0) atomicOr(status, MOE_DEV_BAD_PLAN);
+    return;
+  }
   for (int g = tid; g < nb; g += 256) {
     int lo = 0, hi = E;  // largest e with boff[e] <= g
     while (hi - lo > 1) {
@@ -808,25 +822,25 @@ int launch_route_stats(const int32_t* ids, int T, int k, int E, int beta, int32_
 }
 
 int launch_plan(const int32_t* bcnt, const int32_t* boff, const int32_t* owner, int E, int P,
-                int s, int mode, int lam, int32_t* q, int32_t* load, int32_t* bw,
+                int s, int mode, int lam, int32_t* q, int32_t* load, int32_t* bw, int bw_cap,
                 int32_t* info, int32_t* status, hipStream_t st) {
   if (mode == MOE_PLAN_QUOTA) {
     const size_t lds = sizeof(int) * (size_t)(4 * E + 1 + 8 * E);
     hipLaunchKernelGGL(k_plan_quota, dim3(1), dim3(512), lds, st, bcnt, boff, owner, E, P, s,
-                       lam, q, load, bw, info, status);
+                       lam, q, load, bw, bw_cap, info, status);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   }
   const size_t lds = sizeof(int) * (size_t)(3 * E + 1 + 4 * E + 4 * E * 8);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(256), lds, st, bcnt, boff, owner, E, P, s, mode,
-                     lam, q, load, bw, info, status);
+                     lam, q, load, bw, bw_cap, info, status);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 int launch_plan_gate(const int32_t* bcnt, const int32_t* boff, const int32_t* owner, int E, int P,
-                     int rho_milli, int32_t* q, int32_t* load, int32_t* bw, int32_t* info,
-                     int32_t* status, hipStream_t st) {
+                     int rho_milli, int32_t* q, int32_t* load, int32_t* bw, int bw_cap,
+                     int32_t* info, int32_t* status, hipStream_t st) {
   hipLaunchKernelGGL(k_plan_gate, dim3(1), dim3(256), 0, st, bcnt, boff, owner, E, P, rho_milli,
-                     q, load, bw, info, status);
+                     q, load, bw, bw_cap, info, status);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

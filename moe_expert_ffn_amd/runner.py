@@ -48,6 +48,8 @@ class LayerRunner:
         return B.route_stats(topk_ids, self.E, self.beta, self.rs, self.ws, self.status)
 
     def make_plan(self, mode=B.PLAN_FWD, s=None, out=None):
+        if s is not None and s > self.s:
+            raise B.MoeError(f"replica budget s={s} above the runner's s={self.s}")
         out = self.plan_f if out is None else out
         lam = self.lam
         if self.quota_umin is not None:
@@ -72,7 +74,12 @@ class LayerRunner:
         return self.dx, self.dw1, self.dw2
 
     def step(self, x, gates, topk_ids, dy=None, s=None):
-        """One pass of the whole path: route -> plan -> forward [-> plan(bwd) -> backward]."""
+        """One pass of the whole path: route -> plan -> forward [-> plan(bwd) -> backward].
+
+        s (default: the runner's s) is the replica budget of both plans; it may
+        not exceed the runner's, whose replica slots the backward provides."""
+        if s is not None and s > self.s:
+            raise B.MoeError(f"replica budget s={s} above the runner's s={self.s}")
         self.route(topk_ids)
         self.make_plan(B.PLAN_FWD, s)
         self.forward(x, gates, topk_ids)

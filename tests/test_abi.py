@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = B.load()
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == B.ABI_VERSION == 2
     assert lib.moe_status_str(0) == b"ok"
     assert b"workspace" in lib.moe_status_str(-3)
 
@@ -93,19 +93,22 @@ def test_host_validation_errors():
     assert lib.moe_route_stats(P, 4, 2, 8, 16, *([P] * 8), ctypes.c_void_p(17), 1 << 20,
                                None) == B.MOE_ERR_WORKSPACE
     # planner
-    assert lib.moe_plan(P, P, P, 8, 3, 1, 0, 12, *([P] * 5), P, 0, None) == B.MOE_ERR_UNSUPPORTED
-    assert lib.moe_plan(P, P, P, 8, 4, -1, 0, 12, *([P] * 5), P, 0, None) == B.MOE_ERR_ARG
-    assert lib.moe_plan(P, P, P, 8, 4, 1, 3, 12, *([P] * 5), P, 0, None) == B.MOE_ERR_ARG
+    assert lib.moe_plan(P, P, P, 8, 3, 1, 0, 12, P, P, P, 64, P, P, P, 0, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_plan(P, P, P, 8, 4, -1, 0, 12, P, P, P, 64, P, P, P, 0, None) == B.MOE_ERR_ARG
+    assert lib.moe_plan(P, P, P, 8, 4, 1, 3, 12, P, P, P, 64, P, P, P, 0, None) == B.MOE_ERR_ARG
     # quota mode: lambda is the quota floor and must be at least one block
-    assert lib.moe_plan(P, P, P, 8, 4, 1, B.PLAN_QUOTA, 0, *([P] * 5), P, 0, None) == B.MOE_ERR_ARG
-    assert lib.moe_plan(P, P, P, 8, 4, 1, 0, -1, *([P] * 5), P, 0, None) == B.MOE_ERR_ARG
-    assert lib.moe_plan(P, P, P, 600, 4, 1, 0, 12, *([P] * 5), P, 0, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_plan(P, P, P, 8, 4, 1, B.PLAN_QUOTA, 0, P, P, P, 64, P, P, P, 0, None) == B.MOE_ERR_ARG
+    assert lib.moe_plan(P, P, P, 8, 4, 1, 0, -1, P, P, P, 64, P, P, P, 0, None) == B.MOE_ERR_ARG
+    assert lib.moe_plan(P, P, P, 600, 4, 1, 0, 12, P, P, P, 64, P, P, P, 0, None) == B.MOE_ERR_UNSUPPORTED
+    # block_worker capacity is a size
+    assert lib.moe_plan(P, P, P, 8, 4, 1, 0, 12, P, P, P, -1, P, P, P, 0, None) == B.MOE_ERR_ARG
     # replication gate: price >= 0, P in {1,2,4,8}, E <= 512, no null pointers
-    assert lib.moe_plan_gate(P, P, P, 8, 4, -1, *([P] * 5), None) == B.MOE_ERR_ARG
-    assert lib.moe_plan_gate(P, P, P, 0, 4, 1000, *([P] * 5), None) == B.MOE_ERR_ARG
-    assert lib.moe_plan_gate(P, P, P, 8, 3, 1000, *([P] * 5), None) == B.MOE_ERR_UNSUPPORTED
-    assert lib.moe_plan_gate(P, P, P, 600, 4, 1000, *([P] * 5), None) == B.MOE_ERR_UNSUPPORTED
-    assert lib.moe_plan_gate(P, None, P, 8, 4, 1000, *([P] * 5), None) == B.MOE_ERR_ARG
+    assert lib.moe_plan_gate(P, P, P, 8, 4, -1, P, P, P, 64, P, P, None) == B.MOE_ERR_ARG
+    assert lib.moe_plan_gate(P, P, P, 0, 4, 1000, P, P, P, 64, P, P, None) == B.MOE_ERR_ARG
+    assert lib.moe_plan_gate(P, P, P, 8, 3, 1000, P, P, P, 64, P, P, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_plan_gate(P, P, P, 600, 4, 1000, P, P, P, 64, P, P, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_plan_gate(P, None, P, 8, 4, 1000, P, P, P, 64, P, P, None) == B.MOE_ERR_ARG
+    assert lib.moe_plan_gate(P, P, P, 8, 4, 1000, P, P, P, -1, P, P, None) == B.MOE_ERR_ARG
     # cost model: sizes, P, shapes the model covers, workgroups divisible by P
     assert lib.moe_predict_cost(*([P] * 5), 8, 128, 4, 256, 0, 256, P, P, None) == B.MOE_ERR_ARG
     assert lib.moe_predict_cost(*([P] * 5), 8, 128, 3, 256, 256, 256, P, P, None) == B.MOE_ERR_UNSUPPORTED
@@ -129,18 +132,22 @@ def test_host_validation_errors():
     assert lib.moe_backward(ctypes.byref(nofp8), P, P, P, P, P, 4, 2, 16, 4, 1, *([P] * 10), P,
                             1 << 30, None, None) == B.MOE_ERR_UNSUPPORTED
     # token-axis quantization: shapes and pointers are checked on the host
-    # (src, ld, row_map, gather, row_div, row_scale, rows, cols, block_rows, codes, scales, stream)
+    # (src, ld, src_rows, row_map, gather, row_div, row_scale, rows, cols, block_rows, codes,
+    #  scales, stream)
     q = lib.moe_quantize_token_blocks
-    assert q(P, 16, None, 0, 1, None, 4, 12, 128, P, P, None) == B.MOE_ERR_ARG     # cols % 8
-    assert q(P, 8, None, 0, 1, None, 4, 16, 128, P, P, None) == B.MOE_ERR_ARG      # ld < cols
-    assert q(P, 20, None, 0, 1, None, 4, 16, 128, P, P, None) == B.MOE_ERR_ARG     # ld % 8
-    assert q(P, 16, None, 0, 1, None, -1, 16, 128, P, P, None) == B.MOE_ERR_ARG    # rows
-    assert q(P, 16, None, 0, 1, None, 4, 16, 0, P, P, None) == B.MOE_ERR_ARG       # block rows
-    assert q(P, 16, None, 0, 0, None, 4, 16, 128, P, P, None) == B.MOE_ERR_ARG     # row_div
-    assert q(None, 16, None, 0, 1, None, 4, 16, 128, P, P, None) == B.MOE_ERR_ARG  # src
-    assert q(P, 16, None, 0, 1, None, 4, 16, 128, None, P, None) == B.MOE_ERR_ARG  # codes
+    assert q(P, 16, 4, None, 0, 1, None, 4, 12, 128, P, P, None) == B.MOE_ERR_ARG     # cols % 8
+    assert q(P, 8, 4, None, 0, 1, None, 4, 16, 128, P, P, None) == B.MOE_ERR_ARG      # ld < cols
+    assert q(P, 20, 4, None, 0, 1, None, 4, 16, 128, P, P, None) == B.MOE_ERR_ARG     # ld % 8
+    assert q(P, 16, 4, None, 0, 1, None, -1, 16, 128, P, P, None) == B.MOE_ERR_ARG    # rows
+    assert q(P, 16, 4, None, 0, 1, None, 4, 16, 0, P, P, None) == B.MOE_ERR_ARG       # block rows
+    assert q(P, 16, 4, None, 0, 0, None, 4, 16, 128, P, P, None) == B.MOE_ERR_ARG     # row_div
+    assert q(None, 16, 4, None, 0, 1, None, 4, 16, 128, P, P, None) == B.MOE_ERR_ARG  # src
+    assert q(P, 16, 4, None, 0, 1, None, 4, 16, 128, None, P, None) == B.MOE_ERR_ARG  # codes
+    assert q(P, 16, -1, P, 1, 1, None, 4, 16, 128, P, P, None) == B.MOE_ERR_ARG       # src_rows
+    assert q(P, 16, 3, None, 0, 1, None, 4, 16, 128, P, P, None) == B.MOE_ERR_ARG     # rows in place
+    assert q(P, 16, 3, P, 0, 1, None, 4, 16, 128, P, P, None) == B.MOE_ERR_ARG        # > src_rows
     big = 65535 * 128 + 8                                                            # > 65535 column tiles
-    assert q(P, big, None, 0, 1, None, 4, big, 128, P, P, None) == B.MOE_ERR_ARG
+    assert q(P, big, 4, None, 0, 1, None, 4, big, 128, P, P, None) == B.MOE_ERR_ARG
     ok = _layer()
     assert lib.moe_forward(ctypes.byref(ok), P, P, P, 4, 2, 16, 4, *([P] * 8), P, 16, None,
                            None) == B.MOE_ERR_WORKSPACE
@@ -176,6 +183,18 @@ def test_quantizer_binding_checks_buffers():
     with pytest.raises(B.MoeError, match="row_map"):
         B.quantize_token_blocks(src, 64, 16, 128, ok_codes, ok_scales,
                                 row_map=FakeDev(torch.int64, 64))
+    # gathered rows: src_rows is required, src must hold that many rows and the
+    # row scales one entry per (src row, map divisor)
+    rmap = FakeDev(torch.int32, 64)
+    with pytest.raises(B.MoeError, match="src_rows"):
+        B.quantize_token_blocks(src, 64, 16, 128, ok_codes, ok_scales, row_map=rmap, gather=True,
+                                row_div=8)
+    with pytest.raises(B.MoeError, match="src"):
+        B.quantize_token_blocks(src, 64, 16, 128, ok_codes, ok_scales, row_map=rmap, gather=True,
+                                row_div=8, src_rows=65)
+    with pytest.raises(B.MoeError, match="row_scale"):
+        B.quantize_token_blocks(src, 64, 16, 128, ok_codes, ok_scales, row_map=rmap, gather=True,
+                                row_div=8, src_rows=64, row_scale=FakeDev(torch.float32, 64 * 8 - 1))
 
 
 def test_executor_bindings_check_buffers():

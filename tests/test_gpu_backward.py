@@ -192,3 +192,86 @@ def test_runs_are_bitwise_deterministic(name):
     assert torch.equal(y_a, c.runner.y)
     assert torch.equal(dx_a, dx_b)
     assert torch.equal(dw1_a, dw1_b) and torch.equal(dw2_a, dw2_b)
+
+
+def _guarded(n, dev, guard=4096, fill=12345.0):
+    """A float32 view of n elements inside a buffer with `guard` sentinel
+    elements on each side."""
+    buf = torch.full((n + 2 * guard,), fill, dtype=torch.float32, device=dev)
+    return buf, buf[guard:guard + n]
+
+
+def test_bad_backward_plan_is_flagged_and_stays_in_bounds():
+    """A backward plan that breaks its constraints -- non-home experts beyond
+    the replica budget, an expert whose blocks on one worker are not one run,
+    or more blocks than the slot space -- sets MOE_DEV_BAD_PLAN, drops those
+    segments, and writes nothing outside dw1 and dw2 (regression: such
+    segments used to reach the weight-gradient kernel with expert -1)."""
+    from moe_expert_ffn_amd import binding as B
+    w = SMALL["stream_bf16"]
+    say("[bwd-bad-plan] stream_bf16")
+    c = Case(w, 0, backward=True)
+    r = c.runner
+    dev = c.x.device
+    r.status.zero_()
+    r.route(c.ids)
+    r.make_plan(B.PLAN_FWD, s=0)
+    r.forward(c.x, c.gates, c.ids)
+    r.backward(c.x, c.gates, c.dy, c.ids, block_worker=r.plan_f["block_worker"])   # fixed placement
+    torch.cuda.synchronize()
+    assert c.status() == 0
+    dx_ref, dw1_ref, dw2_ref = r.dx.clone(), r.dw1.clone(), r.dw2.clone()
+
+    bc = r.rs["block_counts"].cpu().numpy()
+    boff = r.rs["block_offsets"].cpu().numpy()
+    owner = c.owner_np
+    bw = np.repeat(owner, bc).astype(np.int32)               # every block at home
+    moved = [e for e in range(w.E) if bc[e] >= 1][:2]        # all blocks on another worker
+    for e in moved:
+        bw[boff[e]:boff[e + 1]] = (owner[e] + 1) % w.P
+    split = [e for e in range(w.E) if bc[e] >= 3 and e not in moved][:1]
+    for e in split:                                          # home, other, home: two runs at home
+        bw[boff[e] + 1] = (owner[e] + 2) % w.P
+    assert moved and split
+    bw_dev = torch.from_numpy(bw).to(dev)
+    n1, n2 = w.E * 2 * w.d_ff * w.d, w.E * w.d * w.d_ff
+    G = 4096
+    for case in ("over_budget", "too_many_blocks"):
+        buf1, dw1 = _guarded(n1, dev, G)
+        buf2, dw2 = _guarded(n2, dev, G)
+        dx = torch.empty_like(r.dx)
+        rs = dict(r.rs)
+        if case == "too_many_blocks":
+            bo = rs["block_offsets"].clone()
+            bo[w.E] = B.max_blocks(c.T, w.k, w.E, w.beta) + 1
+            rs["block_offsets"] = bo
+        r.status.zero_()
+        B.backward(r.layer, c.x, c.gates, c.dy, r.z, c.ids, w.beta, w.P, 0, rs, r.owner, bw_dev,
+                   dx, dw1, dw2, r.ws, r.status)
+        torch.cuda.synchronize()
+        st = c.status()
+        say(f"  {case}: status={st}")
+        assert st & B.DEV_BAD_PLAN
+        assert torch.all(buf1[:G] == 12345.0) and torch.all(buf1[G + n1:] == 12345.0)
+        assert torch.all(buf2[:G] == 12345.0) and torch.all(buf2[G + n2:] == 12345.0)
+        dw1 = dw1.view(w.E, 2 * w.d_ff, w.d)
+        dw2 = dw2.view(w.E, w.d, w.d_ff)
+        if case == "too_many_blocks":                        # nothing scheduled: owner slots zeroed
+            assert torch.all(dw1 == 0) and torch.all(dw2 == 0)
+            continue
+        # rows are still computed by the plan's tiles, so dx is the fixed placement's
+        assert torch.equal(dx, dx_ref)
+        bad = set(moved) | set(split)
+        for e in range(w.E):
+            if e in bad:                                      # no segment holds them: zeros
+                assert torch.all(dw1[e] == 0) and torch.all(dw2[e] == 0), e
+            else:                                             # untouched experts: bit for bit
+                assert torch.equal(dw1[e], dw1_ref[e]) and torch.equal(dw2[e], dw2_ref[e]), e
+
+
+def test_runner_rejects_a_budget_above_its_own():
+    from moe_expert_ffn_amd import binding as B
+    w = SMALL["small_bf16"]
+    c = Case(w, 0, backward=True)
+    with pytest.raises(B.MoeError, match="replica budget"):
+        c.runner.step(c.x, c.gates, c.ids, dy=c.dy, s=w.s + 1)

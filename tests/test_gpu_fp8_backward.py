@@ -53,7 +53,7 @@ def _quant_dev(src, rows, cols, brows, ld=None, row_map=None, gather=False, row_
                             row_map=None if row_map is None else torch.from_numpy(row_map).to(dev),
                             gather=gather, row_div=row_div,
                             row_scale=None if row_scale is None else torch.from_numpy(row_scale).to(dev),
-                            ld=ld)
+                            ld=ld, src_rows=src.shape[0])
     torch.cuda.synchronize()
     return codes[:rows].cpu().numpy(), scales[:nblk].cpu().numpy()
 
@@ -89,12 +89,13 @@ def test_quantize_gather_scaled(rows, brows):
     gates = rng.random(T * k).astype(np.float32)
     row_map = rng.integers(0, T * k, size=rows).astype(np.int32)
     row_map[rng.random(rows) < 0.2] = -1            # padding slots
+    row_map[rng.random(rows) < 0.05] = T * k + 3    # past the source rows: read as zero rows
     codes, scales = _quant_dev(dy, rows, cols, brows, row_map=row_map, gather=True, row_div=k,
                                row_scale=gates)
     dy32 = dy.float().numpy()
     vals = np.zeros((rows, cols), dtype=np.float32)
     for r, m in enumerate(row_map):
-        if m >= 0:
+        if 0 <= m < T * k:
             vals[r] = gates[m] * dy32[m // k]           # fp32 product, as the device forms p * dy
     _check_exact(codes, scales, vals, brows)
 

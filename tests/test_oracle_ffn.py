@@ -215,3 +215,92 @@ def test_fp8_backward_exact_when_D_is_representable():
     b = offn.backward_fp8(x, w1, w2, ids, g, dy, beta=beta)
     for e in range(E):
         np.testing.assert_allclose(b["dw2"][e], a["dw2"][e], rtol=1e-12, atol=1e-12)
+
+
+# ---- the requantized operands, row by row -------------------------------------
+# With x_t the unit vector e_t (d >= T), column t of dW1_e = dZq^T X is the
+# requantized dZ row of token t in expert e; with A_t = a e_t (one-hot), column
+# t of dW2_e = Dq^T A is a times the requantized D row.  The exact rows come
+# from the unquantized backward (pinned above by finite differences and the
+# closed forms).  What the pages fix (MegaFlux summary, "Backward": D_e and
+# dZ_e requantized along the tokens; readings F1-F4: blocks of beta
+# consecutive slots of one expert, counted from its first slot, times one
+# column; scale = amax / 448) then gives three properties per block column,
+# checked without re-running the quantizer:
+#   * its largest magnitude survives (code 448 times the scale);
+#   * every value is an e4m3 value times that scale (scale = largest / 448);
+#   * every value is within half an e4m3 step of the exact one.
+
+def _grid_units(r):
+    """Distance of |r| (<= 448) from the nearest e4m3 value, in steps of the
+    grid there: 3 mantissa bits above 2^-6, steps of 2^-9 below."""
+    a = np.abs(np.asarray(r, dtype=np.float64))
+    m, _ = np.frexp(a)                                  # a = m 2^e, 1/2 <= m < 1
+    normal = np.abs(m * 16 - np.rint(m * 16))
+    sub = np.abs(a / 2.0 ** -9 - np.rint(a / 2.0 ** -9))
+    return np.where(a >= 2.0 ** -6, normal, sub)
+
+
+def _tokens_of(ids, e):
+    """Tokens of expert e's rows in slot order (flat (token, slot) order)."""
+    flat = np.asarray(ids).ravel()
+    return np.nonzero(flat == e)[0] // ids.shape[1]
+
+
+def _check_token_blocks(q_rows, true_rows, beta):
+    n = q_rows.shape[0]
+    assert n > beta                                     # several blocks, the last one ragged
+    for b0 in range(0, n, beta):
+        q, v = q_rows[b0:b0 + beta], true_rows[b0:b0 + beta]
+        vmax = np.abs(v).max(axis=0)
+        zero = vmax == 0
+        assert np.all(q[:, zero] == 0)
+        q, v, vmax = q[:, ~zero], v[:, ~zero], vmax[~zero]
+        m = np.abs(q).max(axis=0)
+        assert np.all(np.abs(m - vmax) <= 2.0 ** -21 * vmax), "block column maximum not kept"
+        s = m / 448.0
+        assert np.all(_grid_units(q / s) <= 1e-6), "values off the block column's e4m3 grid"
+        err = np.abs(q - v)
+        assert np.all(err <= 2.0 ** -4 * np.abs(v) + 2.0 ** -10 * s + 2.0 ** -21 * np.abs(v)), \
+            "a value moved by more than half an e4m3 step"
+
+
+def _onehot_case(seed, T=48, k=2, E=3, d=64, F=8):
+    rng = np.random.default_rng(seed)
+    x = np.eye(T, d)                                    # x_t = e_t
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    g = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)   # gates != 1
+    dy = rng.standard_normal((T, d)).astype(np.float32).astype(np.float64)
+    return rng, x, ids, g, dy
+
+
+def test_fp8_backward_dz_rows_are_token_axis_blocks():
+    beta = 8
+    rng, x, ids, g, dy = _onehot_case(11)
+    E, d, F = 3, x.shape[1], 8
+    w1 = rng.standard_normal((E, 2 * F, d))
+    w2 = rng.standard_normal((E, d, F)) / np.sqrt(F)
+    a = offn.backward(x, w1, w2, ids, g, dy)
+    b = offn.backward_fp8(x, w1, w2, ids, g, dy, beta=beta)
+    for e in range(E):
+        t = _tokens_of(ids, e)
+        _check_token_blocks(b["dw1"][e][:, t].T, a["dw1"][e][:, t].T, beta)
+
+
+def test_fp8_backward_d_rows_are_token_axis_blocks_with_gates():
+    # G = 1 everywhere and U_t = e_t, so A_t = SiLU(1) e_t
+    beta = 8
+    rng, x, ids, g, dy = _onehot_case(12)
+    E, d, T = 3, x.shape[1], x.shape[0]
+    F = T
+    w1 = np.zeros((E, 2 * F, d))
+    w1[:, :F, :] = 1.0
+    w1[:, F + np.arange(T), np.arange(T)] = 1.0
+    w2 = rng.standard_normal((E, d, F)) / np.sqrt(F)
+    b = offn.backward_fp8(x, w1, w2, ids, g, dy, beta=beta)
+    silu1 = 1.0 / (1.0 + np.exp(-1.0))
+    for e in range(E):
+        t = _tokens_of(ids, e)
+        j = np.nonzero(ids[t] == e)[1]                  # slot of expert e in each token
+        d_exact = g[t, j].astype(np.float64)[:, None] * dy[t]     # D = p dy
+        _check_token_blocks(b["dw2"][e][:, t].T / silu1, d_exact, beta)
