@@ -10,7 +10,11 @@ kappa=1 by default.
 
 Prints one JSON line.  `value` is useful TFLOP/s: (6 + 12) * d * d_ff * R per
 step (R = routed rows; padding rows, SwiGLU, combine not counted), divided by
-the measured step time.
+the measured step time.  The same line carries `kappa_sweep`: every skew level
+of the workload (kappa 1, 4, 8 for the fwd+bwd layer) under fixed placement
+(s = 0), the pages' planner (lambda = 12) and the planner with lambda = 1 (the
+measured price of a replica on one GPU), in ms and useful TFLOP/s, and the
+latency ratio kappa=8 / kappa=1 of each arm (`skew`).
 """
 from __future__ import annotations
 
@@ -40,9 +44,15 @@ def parse():
     ap.add_argument("--workload", default="qwen3_bf16_fwdbwd")
     ap.add_argument("--kappa", type=float, default=1)
     ap.add_argument("--fixed", action="store_true", help="fixed placement (s = 0)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the default kappa sweep (fixed vs planned at every kappa)")
+    ap.add_argument("--sweep-steps", type=int, default=10,
+                    help="timed steps per arm of the default kappa sweep")
     ap.add_argument("--sweep", action="store_true",
-                    help="also time every kappa of the workload: fixed placement, the bounded "
-                         "greedy planner and the quota planner, and compare the two planners")
+                    help="the long sweep instead: every kappa of the workload under fixed "
+                         "placement, the bounded greedy planner (lambda 12 and 1), the quota "
+                         "planner and the quota planner with P chosen by the cost model, and "
+                         "the two planners compared")
     ap.add_argument("--gate-sweep", action="store_true",
                     help="time near-balanced kappas: fixed placement, the planner, and the "
                          "planner behind the replication gate")
@@ -63,14 +73,18 @@ def flops_per_row(w):
     return 6 * w.d * w.d_ff, 12 * w.d * w.d_ff
 
 
-def build_case(w, kappa, fixed, dev, quota_umin=None, gate_rho=None, lam=12, P=None):
+def build_case(w, kappa, fixed, dev, quota_umin=None, gate_rho=None, lam=12, P=None, lay=None,
+               routing=None):
+    """One timed configuration.  `lay` (the layer's weights, which do not depend
+    on kappa) and `routing` (make_routing's ids and gates) may be shared
+    between arms."""
     import torch
 
     from moe_expert_ffn_amd.inputs import contiguous_owners, make_dy, make_layer, make_routing, make_x
     from moe_expert_ffn_amd.runner import LayerRunner
-    ids, gates = make_routing(w, kappa)
+    ids, gates = make_routing(w, kappa) if routing is None else routing
     T = ids.shape[0]
-    lay = make_layer(w, dev)
+    lay = make_layer(w, dev) if lay is None else lay
     x = lay["x"] if "x" in lay and lay["x"].shape[0] == T else make_x(w, T, dev)
     act = torch.float32 if w.act == "f32" else torch.bfloat16
     dy = make_dy(w, T, dev) if w.backward else None
@@ -272,6 +286,47 @@ def compare_planners(case, w, n=50):
     return out
 
 
+SWEEP_ARMS = (("fixed", True, 12), ("planned", False, 12), ("planned-lambda1", False, 1))
+
+
+def kappa_sweep(w, dev, lay, steps, warmup=3):
+    """Every kappa of the workload under each arm of SWEEP_ARMS: ms per step
+    (HIP-event median over `steps` steps), useful TFLOP/s and its share of the
+    bf16 peak, the forward and backward stage sums, and the plans' objectives.
+    Returns (rows, skew) with skew[arm] = ms(max kappa) / ms(kappa 1)."""
+    import torch
+
+    from moe_expert_ffn_amd.inputs import make_routing, realised_kappa
+    f_fwd, f_bwd = flops_per_row(w)
+    rows = []
+    for kap in w.kappas:
+        routing = make_routing(w, kap)
+        R = int((routing[0] >= 0).sum())
+        useful = (f_fwd + (f_bwd if w.backward else 0)) * R
+        for arm, fixed, lam in SWEEP_ARMS:
+            c = build_case(w, kap, fixed, dev, lam=lam, lay=lay, routing=routing)
+            _, st = time_steps(c, steps, warmup)
+            ms = st["step_median"]
+            pf = c["runner"].plan_f["plan_info"].cpu().tolist()
+            pb = c["runner"].plan_b["plan_info"].cpu().tolist() if w.backward else None
+            rows.append({"kappa": kap, "kappa_realised": round(realised_kappa(routing[0], w.E), 3),
+                         "placement": arm, "lambda": lam, "ms": round(ms, 4),
+                         "tflops": round(useful / (ms * 1e-3) / 1e12, 2),
+                         "pct_bf16_peak": round(100 * useful / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                         "fwd_us": round(sum(v for k_, v in st.items() if k_.startswith("fwd.")) * 1e3, 1),
+                         "bwd_us": round(sum(v for k_, v in st.items() if k_.startswith("bwd.")) * 1e3, 1),
+                         "objective_fwd": pf[0], "replicas_fwd": pf[2],
+                         **({"objective_bwd": pb[0], "replicas_bwd": pb[2]} if pb else {})})
+            del c
+            torch.cuda.empty_cache()
+    skew = {}
+    k_lo, k_hi = min(w.kappas), max(w.kappas)
+    for arm, _, _ in SWEEP_ARMS:
+        t = {r["kappa"]: r["ms"] for r in rows if r["placement"] == arm}
+        skew[arm] = round(t[k_hi] / t[k_lo], 4)
+    return rows, {"kappa_hi": k_hi, "kappa_lo": k_lo, "ratio": skew}
+
+
 def cpu_baseline(case, w, tokens, min_seconds):
     """The oracle, untuned, on the first `tokens` tokens (0: all) of the same
     workload: forward of those tokens plus their dx, and dW of every expert
@@ -380,7 +435,9 @@ def main():
     B.load()
     dev = torch.device("cuda:0")
     w = WORKLOADS[args.workload]
-    case = build_case(w, args.kappa, args.fixed, dev)
+    from moe_expert_ffn_amd.inputs import make_layer
+    lay = make_layer(w, dev)                        # weights do not depend on kappa: shared
+    case = build_case(w, args.kappa, args.fixed, dev, lay=lay)
     R = int((case["ids_np"] >= 0).sum())
     ms, stages = time_steps(case, args.steps, args.warmup)
     f_fwd, f_bwd = flops_per_row(w)
@@ -412,13 +469,15 @@ def main():
         "roofline": roof,
         "kernels": per_kernel,
     }
+    if not args.sweep and not args.no_sweep and len(w.kappas) > 1:
+        out["kappa_sweep"], out["skew"] = kappa_sweep(w, dev, lay, args.sweep_steps)
     if args.sweep:
         sweep, planners = [], []
         for kap in w.kappas:
             for arm, fixed, umin, lam in (("fixed", True, None, 12), ("planned", False, None, 12),
                                           ("planned-lambda1", False, None, 1),
                                           ("planned-quota", False, 1, 12)):
-                c = build_case(w, kap, fixed, dev, quota_umin=umin, lam=lam)
+                c = build_case(w, kap, fixed, dev, quota_umin=umin, lam=lam, lay=lay)
                 Rk = int((c["ids_np"] >= 0).sum())
                 msk, st = time_steps(c, max(5, args.steps // 2), 2)
                 uk = (f_fwd + (f_bwd if w.backward else 0)) * Rk
@@ -433,7 +492,7 @@ def main():
             # quota planner with the partition count P picked by the cost model
             chosen = None
             for P in (1, 2, 4, 8):
-                c = build_case(w, kap, False, dev, quota_umin=1, P=P)
+                c = build_case(w, kap, False, dev, quota_umin=1, P=P, lay=lay)
                 time_steps(c, 1, 0, with_events=False)          # route and plan once
                 cost = predicted_cost(c, w, P)
                 if chosen is None or (cost, -P) < (chosen[1], -chosen[2]):
@@ -458,7 +517,7 @@ def main():
         for kap in (1.05, 1.1, 1.25, 1.5, 2.0):
             for arm, fixed, rho in (("fixed", True, None), ("planned", False, None),
                                     ("planned-gated", False, args.gate_rho)):
-                c = build_case(w, kap, fixed, dev, gate_rho=rho)
+                c = build_case(w, kap, fixed, dev, gate_rho=rho, lay=lay)
                 msk, _ = time_steps(c, max(5, args.steps // 2), 2)
                 pf = c["runner"].plan_f["plan_info"].cpu().tolist()
                 pb = c["runner"].plan_b["plan_info"].cpu().tolist() if w.backward else None
@@ -472,7 +531,7 @@ def main():
         for kap in w.kappas:
             per = {}
             for P in (1, 2, 4, 8):
-                c = build_case(w, kap, False, dev, P=P)
+                c = build_case(w, kap, False, dev, P=P, lay=lay)
                 msk, _ = time_steps(c, max(5, args.steps // 2), 2)
                 per[P] = (msk, predicted_cost(c, w, P))
                 del c

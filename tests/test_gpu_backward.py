@@ -233,6 +233,8 @@ def test_bad_backward_plan_is_flagged_and_stays_in_bounds():
     for e in split:                                          # home, other, home: two runs at home
         bw[boff[e] + 1] = (owner[e] + 2) % w.P
     assert moved and split
+    cap = B.max_blocks(c.T, w.k, w.E, w.beta)
+    bw = np.concatenate([bw, np.zeros(cap - len(bw), np.int32)])   # entries past sum b unused
     bw_dev = torch.from_numpy(bw).to(dev)
     n1, n2 = w.E * 2 * w.d_ff * w.d, w.E * w.d * w.d_ff
     G = 4096
