@@ -119,6 +119,24 @@ int moe_route_stats(const int32_t* topk_ids, int T, int k, int E, int beta,
                     double* kappa, int32_t* status_dev, void* ws, size_t ws_bytes,
                     void* stream);
 
+/* moe_route_stats for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments and results without `ws`.  Its per-chunk counts live in
+ * a scratch array inside the library, MOE_ROUTE_SCRATCH_BYTES on every GPU it
+ * runs on, held until the process ends; the call allocates nothing.  Calls on
+ * one GPU share that array: calls that overlap in time on one GPU (two
+ * streams, two host threads) race, so serialise them.
+ * Errors: as moe_route_stats, plus MOE_ERR_UNSUPPORTED when the counts need
+ *   more than the array: ceil(T*k / 256) * E * 4 > MOE_ROUTE_SCRATCH_BYTES
+ *   (e.g. T*k above 2,097,152 rows at E = 128); MOE_ERR_HIP when the array's
+ *   device address cannot be obtained. */
+#define MOE_ROUTE_SCRATCH_BYTES ((size_t)4 << 20)
+int moe_route_stats_noalloc(const int32_t* topk_ids, int T, int k, int E, int beta,
+                            int32_t* counts, int32_t* offsets, int32_t* block_counts,
+                            int32_t* block_offsets, int32_t* row_to_slot,
+                            int32_t* slot_to_row, double* kappa, int32_t* status_dev,
+                            void* stream);
+
 /* Replica placement and block assignment ("Problem Formulation", "Bounded
  * Greedy Search").  Runs entirely on the device (no host round trip), one
  * workgroup; integer-only, so the result is deterministic.

@@ -22,7 +22,8 @@ PLAN_FWD, PLAN_BWD, PLAN_QUOTA = 0, 1, 2
 DEV_BAD_EXPERT, DEV_BAD_PLAN, DEV_BAD_OWNER = 1, 2, 4
 
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_max_slots", "moe_max_blocks",
-           "moe_workspace_size", "moe_route_stats", "moe_plan", "moe_plan_gate",
+           "moe_workspace_size", "moe_route_stats", "moe_route_stats_noalloc", "moe_plan",
+           "moe_plan_gate",
            "moe_predict_cost", "moe_quantize_token_blocks", "moe_forward",
            "moe_backward",
            "moe_event_create", "moe_event_destroy", "moe_event_record", "moe_event_elapsed_ms",
@@ -65,6 +66,8 @@ def load():
     lib.moe_workspace_size.argtypes = [ctypes.POINTER(Layer), _I, _I, _I, _I, _I, _I]
     lib.moe_route_stats.restype = _I
     lib.moe_route_stats.argtypes = [_P, _I, _I, _I, _I] + [_P] * 8 + [_P, _SZ, _P]
+    lib.moe_route_stats_noalloc.restype = _I
+    lib.moe_route_stats_noalloc.argtypes = [_P, _I, _I, _I, _I] + [_P] * 8 + [_P]
     lib.moe_plan.restype = _I
     lib.moe_plan.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I] + [_P] * 3 + [_I] + [_P] * 2 + [_P, _SZ, _P]
     lib.moe_quantize_token_blocks.restype = _I
@@ -226,6 +229,28 @@ def route_stats(topk_ids: torch.Tensor, E: int, beta: int, out: dict, ws: torch.
                                   _ptr(out["block_offsets"]), _ptr(out["row_to_slot"]),
                                   _ptr(out["slot_to_row"]), _ptr(out["kappa"]), _ptr(status),
                                   wsp, wsn, _stream()))
+    return out
+
+
+def route_stats_noalloc(topk_ids: torch.Tensor, E: int, beta: int, out: dict,
+                        status: torch.Tensor):
+    """route_stats without a workspace (moe_route_stats_noalloc): the library's
+    own scratch array holds the per-chunk counts."""
+    _require_device(topk_ids, status, *out.values())
+    T, k = _ids_shape(topk_ids)
+    _expect(out["counts"], torch.int32, E, "counts")
+    _expect(out["offsets"], torch.int32, E + 1, "offsets")
+    _expect(out["block_counts"], torch.int32, E, "block_counts")
+    _expect(out["block_offsets"], torch.int32, E + 1, "block_offsets")
+    _expect(out["row_to_slot"], torch.int32, T * k, "row_to_slot")
+    _expect(out["slot_to_row"], torch.int32, max_slots(T, k, E, beta), "slot_to_row")
+    _expect(out["kappa"], torch.float64, 1, "kappa")
+    _expect(status, torch.int32, 1, "status")
+    _check(load().moe_route_stats_noalloc(_ptr(topk_ids), T, k, E, beta, _ptr(out["counts"]),
+                                          _ptr(out["offsets"]), _ptr(out["block_counts"]),
+                                          _ptr(out["block_offsets"]), _ptr(out["row_to_slot"]),
+                                          _ptr(out["slot_to_row"]), _ptr(out["kappa"]),
+                                          _ptr(status), _stream()))
     return out
 
 

@@ -128,6 +128,24 @@ int moe_route_stats(const int32_t* topk_ids, int T, int k, int E, int beta, int3
                             (hipStream_t)stream);
 }
 
+int moe_route_stats_noalloc(const int32_t* topk_ids, int T, int k, int E, int beta,
+                            int32_t* counts, int32_t* offsets, int32_t* block_counts,
+                            int32_t* block_offsets, int32_t* row_to_slot, int32_t* slot_to_row,
+                            double* kappa, int32_t* status_dev, void* stream) {
+  if (!sizes_ok(T, k, E, beta)) return MOE_ERR_ARG;
+  if (E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if ((T > 0 && (!topk_ids || !row_to_slot)) || !counts || !offsets || !block_counts ||
+      !block_offsets || !slot_to_row || !kappa || !status_dev)
+    return MOE_ERR_ARG;
+  if (route_ws_bytes(T, k, E) > kRouteScratchBytes) return MOE_ERR_UNSUPPORTED;
+  void* scr = nullptr;
+  const int rc = route_scratch(&scr);
+  if (rc != MOE_OK) return rc;
+  return launch_route_stats(topk_ids, T, k, E, beta, counts, offsets, block_counts,
+                            block_offsets, row_to_slot, slot_to_row, kappa, status_dev, scr,
+                            (hipStream_t)stream);
+}
+
 int moe_plan(const int32_t* block_counts, const int32_t* block_offsets, const int32_t* owner,
              int E, int P, int s, int mode, int lambda, int32_t* q, int32_t* load,
              int32_t* block_worker, int block_worker_cap, int32_t* plan_info,

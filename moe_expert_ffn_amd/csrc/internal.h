@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "moe_ffn.h"
+
 namespace moe {
 
 constexpr int kMaxExperts = 1024;      // routing statistics
@@ -36,6 +38,9 @@ bool use_big_tiles(const Sizes& z);
 bool use_stream(const Sizes& z);
 size_t max_tiles(const Sizes& z);
 size_t route_ws_bytes(int T, int k, int E);
+// the routing statistics' scratch array of moe_route_stats_noalloc
+constexpr size_t kRouteScratchBytes = MOE_ROUTE_SCRATCH_BYTES;
+int route_scratch(void** device_ptr);
 
 int launch_route_stats(const int32_t* ids, int T, int k, int E, int beta, int32_t* counts,
                        int32_t* offsets, int32_t* block_counts, int32_t* block_offsets,

@@ -16,6 +16,8 @@
 // search state q lives in LDS.  Every quantity is an integer, so the plan is
 // bit-identical on every run and to any other implementation of the same
 // reading (owner-first contiguous expansion, smallest index on every tie).
+#include <mutex>
+
 #include "common.h"
 #include "moe_ffn.h"
 #include "internal.h"
@@ -819,6 +821,35 @@ int launch_route_stats(const int32_t* ids, int T, int k, int E, int beta, int32_
     hipLaunchKernelGGL(k_route_slot, dim3(nch), dim3(kChunk), 0, st, ids, N, E, chunk,
                        row_to_slot, slot_to_row);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// ---- routing statistics without a caller workspace -----------------------------
+// For callers that cannot allocate: the per-chunk counts live in a file-scope
+// device array, one copy per GPU, held until the process ends.  Host code
+// never hands the array's name to a kernel (on the host it is only a stand-in
+// for the symbol): its device address is looked up once per device, with that
+// device current, and kept.  Every call writes the counts it reads before
+// reading them, so nothing needs clearing between calls; calls that overlap in
+// time on one GPU share the array and race.
+static __device__ __align__(256) int32_t scratch[kRouteScratchBytes / sizeof(int32_t)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+int route_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 int launch_plan(const int32_t* bcnt, const int32_t* boff, const int32_t* owner, int E, int P,
