@@ -287,6 +287,44 @@ def compare_planners(case, w, n=50):
 
 
 SWEEP_ARMS = (("fixed", True, 12), ("planned", False, 12), ("planned-lambda1", False, 1))
+TL_NAMES = ("fc1", "fc2", "dA", "dX", "dW")
+
+
+def worker_spread(tl, P):
+    """Per phase of one step's timeline: each worker's finish (its last
+    workgroup's end, from the phase's first start) over the mean finish of the
+    P workers; 1.0 is perfectly balanced.  Workgroup g belongs to worker
+    (g % 8) * P / 8."""
+    import numpy as np
+    out = {}
+    for ph, name in enumerate(TL_NAMES):
+        st, en = tl[ph, :, 0], tl[ph, :, 1]
+        n = int((st > 0).sum())
+        if n == 0:
+            continue
+        g = np.arange(n)
+        w = (g % 8) * P // 8
+        t0 = st[:n].min()
+        fin = np.array([en[:n][w == r].max() - t0 for r in range(P)], dtype=np.float64)
+        out[name] = round(float(fin.max() / fin.mean()), 3)
+    return out
+
+
+def timeline_step(case):
+    """One more step of the case with the library's per-workgroup timeline."""
+    import torch
+
+    from moe_expert_ffn_amd import binding as B
+    r = case["runner"]
+    tl = B.alloc_timeline(r.owner.device)
+    r.route(case["ids"])
+    r.make_plan(B.PLAN_FWD)
+    r.forward(case["x"], case["gates"], case["ids"], timeline=tl)
+    if case["dy"] is not None:
+        r.make_plan(B.PLAN_BWD, out=r.plan_b)
+        r.backward(case["x"], case["gates"], case["dy"], case["ids"], timeline=tl)
+    torch.cuda.synchronize()
+    return tl.cpu().numpy()
 
 
 def kappa_sweep(w, dev, lay, steps, warmup=3):
@@ -307,6 +345,7 @@ def kappa_sweep(w, dev, lay, steps, warmup=3):
             c = build_case(w, kap, fixed, dev, lam=lam, lay=lay, routing=routing)
             _, st = time_steps(c, steps, warmup)
             ms = st["step_median"]
+            spread = worker_spread(timeline_step(c), c["runner"].P)
             pf = c["runner"].plan_f["plan_info"].cpu().tolist()
             pb = c["runner"].plan_b["plan_info"].cpu().tolist() if w.backward else None
             rows.append({"kappa": kap, "kappa_realised": round(realised_kappa(routing[0], w.E), 3),
@@ -316,7 +355,8 @@ def kappa_sweep(w, dev, lay, steps, warmup=3):
                          "fwd_us": round(sum(v for k_, v in st.items() if k_.startswith("fwd.")) * 1e3, 1),
                          "bwd_us": round(sum(v for k_, v in st.items() if k_.startswith("bwd.")) * 1e3, 1),
                          "objective_fwd": pf[0], "replicas_fwd": pf[2],
-                         **({"objective_bwd": pb[0], "replicas_bwd": pb[2]} if pb else {})})
+                         **({"objective_bwd": pb[0], "replicas_bwd": pb[2]} if pb else {}),
+                         "worker_spread": spread})
             del c
             torch.cuda.empty_cache()
     skew = {}

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -64,6 +64,19 @@ typedef enum {
 #define MOE_DEV_BAD_OWNER  4   /* owner[e] outside [0,P) */
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/* Optional per-workgroup timeline of the persistent GEMM phases (moe_forward
+ * and moe_backward's `timeline` argument): uint64 [MOE_TL_PHASES]
+ * [MOE_TIMELINE_MAX_WG][2], entry [phase][g] = {start, end} of workgroup g of
+ * that phase's launch on the GPU's constant 100 MHz real-time counter (end:
+ * after the workgroup's last item and all its memory operations).  Workgroup g
+ * belongs to worker (g % 8) * P / 8.  Written by the persistent 256 x 256
+ * stream kernels (bf16 activations, d and d_ff multiples of 256, operands
+ * below 2 GiB); other shapes and workgroups beyond the launch leave their
+ * entries untouched.  Writing it changes no result. */
+#define MOE_TIMELINE_MAX_WG 1024
+enum { MOE_TL_FC1 = 0, MOE_TL_FC2 = 1, MOE_TL_DA = 2, MOE_TL_DX = 3, MOE_TL_DW = 4,
+       MOE_TL_PHASES = 5 };
 typedef enum { MOE_PLAN_FWD = 0, MOE_PLAN_BWD = 1, MOE_PLAN_QUOTA = 2 } moe_plan_mode;
 
 /* One expert layer.  The weights are stored transposed with respect to the
@@ -235,6 +248,7 @@ int moe_predict_cost(const int32_t* counts, const int32_t* block_offsets,
  *     every routed row, as needed by moe_backward.
  *   stage_events (host, nullable): 5 hipEvent_t recorded on `stream` at
  *     start / after scheduling / after FC1 / after FC2 / after combine.
+ *   timeline (nullable): phases MOE_TL_FC1 and MOE_TL_FC2 (see above).
  * Errors: MOE_ERR_ARG for an invalid layer, size or null pointer;
  *   MOE_ERR_UNSUPPORTED for E > 512, P outside {1,2,4,8}, d not a multiple
  *   of 128, d_ff not a multiple of 64 (128 with e4m3 weights), a dtype pair
@@ -251,7 +265,7 @@ int moe_forward(const moe_layer* L, const void* x, const float* gates,
                 const int32_t* row_to_slot, const int32_t* slot_to_row,
                 const int32_t* block_worker, void* y, void* z_save,
                 int32_t* status_dev, void* ws, size_t ws_bytes,
-                void* const* stage_events, void* stream);
+                void* const* stage_events, uint64_t* timeline, void* stream);
 
 /* Backward expert layer (gradient equations of the "Backward" section), with
  * D_t = p_tj * dy_t:
@@ -267,6 +281,7 @@ int moe_forward(const moe_layer* L, const void* x, const float* gates,
  *   stage_events (host, nullable): 7 events: start / after scheduling /
  *     after dA / after dX / after dx combine / after weight gradients /
  *     after replica reduction.
+ *   timeline (nullable): phases MOE_TL_DA, MOE_TL_DX and MOE_TL_DW.
  * fp8 weights (MegaFlux summary, "Backward": overlapped token-axis
  * requantization of D_e and dZ_e): dA, dZ and dx use D and the weights as
  * the forward does (e4m3 codes times their 128 x 128 block scales); the
@@ -286,7 +301,7 @@ int moe_backward(const moe_layer* L, const void* x, const float* gates, const vo
                  const int32_t* row_to_slot, const int32_t* slot_to_row,
                  const int32_t* owner, const int32_t* block_worker, void* dx, float* dw1,
                  float* dw2, int32_t* status_dev, void* ws, size_t ws_bytes,
-                 void* const* stage_events, void* stream);
+                 void* const* stage_events, uint64_t* timeline, void* stream);
 
 /* Token-axis e4m3 requantization (MegaFlux summary, "Backward": D_e and dZ_e
  * are requantized along the tokens for the weight-gradient products).

@@ -247,6 +247,8 @@ struct ExecArgs {
   void* dhat;             // fp8 backward on the stream kernels: D requantized and
                           //   widened back to bf16, [slots][d]
   const int32_t* boff;    // block offsets [E + 1]: boff[E] blocks of beta slots are in use
+  uint64_t* timeline;     // nullable: per-workgroup start / end stamps of each stream phase
+  int tl_phase;           //   this launch's phase row
 };
 
 enum { PH_FC1 = 0, PH_FC2 = 1, PH_DA = 2, PH_DX = 3, PH_DW = 4 };
@@ -1310,11 +1312,25 @@ template <class Src, class C, class OA, class OB>
 __global__ __launch_bounds__(C::NT, 512 / C::NT) void k_stream(ExecArgs a, int ntiles_n) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   MOE_LDS uint16_t* smem = (MOE_LDS uint16_t*)smem_raw;
+  // optional timeline: the constant 100 MHz real-time counter when the
+  // workgroup starts and once its last item is done (run() ends with a wait
+  // for every memory operation and a barrier), written with vector stores
+  const uint64_t t0 = a.timeline ? __builtin_amdgcn_s_memrealtime() : 0;
   Src src;
   src.init(a, smem, ntiles_n);
   f32x16_t acc[C::MB][C::NB];
   WideStream<C, OA, OB> p;
   p.run(src, smem, acc);
+  if (a.timeline) {
+    __syncthreads();
+    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0 && blockIdx.x < MOE_TIMELINE_MAX_WG) {
+      MOE_GLB uint64_t* out =
+          (MOE_GLB uint64_t*)a.timeline + ((size_t)a.tl_phase * MOE_TIMELINE_MAX_WG + blockIdx.x) * 2;
+      out[0] = t0;
+      out[1] = t1;
+    }
+  }
 }
 
 // ---- backward: weight gradients per (expert, worker) segment ------------------
@@ -1812,9 +1828,11 @@ template <bool FP8>
 static void run_forward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* y,
                                void* const* ev, hipStream_t st) {
   launch_slot_gate(z, a, st);
+  a.tl_phase = MOE_TL_FC1;
   launch_stream<SrcFc1T<FP8>, WC, RowW, typename SrcFc1T<FP8>::OB>(a, z.dff / (WC::BN / 2),
                                                                    kStreamLds, st);
   rec(ev, 2, st);
+  a.tl_phase = MOE_TL_FC2;
   launch_stream<SrcFc2T<FP8>, WC, RowW, typename SrcFc2T<FP8>::OB>(a, z.d / WC::BN, kStreamLds, st);
   rec(ev, 3, st);
   if (z.T > 0)
@@ -1826,7 +1844,8 @@ static void run_forward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_t
 int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const float* gates,
                    const int32_t* counts, const int32_t* boff, const int32_t* row_to_slot,
                    const int32_t* slot_to_row, const int32_t* block_worker, void* y,
-                   void* z_save, int32_t* status, char* ws, void* const* ev, hipStream_t st) {
+                   void* z_save, int32_t* status, char* ws, void* const* ev,
+                   uint64_t* timeline, hipStream_t st) {
   const WsLayout L = exec_layout(z, false);
   rec(ev, 0, st);
   launch_sched(z, counts, boff, block_worker, nullptr, false, ws, L, status, st);
@@ -1834,6 +1853,7 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
   ExecArgs a = make_exec(z, Lp, ws, L);
   a.x = x; a.gates = gates; a.slot_to_row = slot_to_row; a.row_to_slot = row_to_slot;
   a.z_save = z_save;
+  a.timeline = timeline;
   const bool big = use_big_tiles(z);
   if (Lp.act_dtype == MOE_BF16 && Lp.w_dtype == MOE_BF16 && use_stream(z))
     run_forward_stream<false>(z, a, row_to_slot, y, ev, st);
@@ -1861,8 +1881,10 @@ static void run_backward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_
   if constexpr (FP8)
     launch_quant_dequant((const uint16_t*)a.dy, z.d, a.slot_to_row, 1, z.k, a.gates, z.T * z.k,
                          rows, z.d, z.beta, (uint16_t*)a.dhat, a.boff + z.E, st);
+  a.tl_phase = MOE_TL_DA;
   launch_stream<SrcDaT<FP8>, WC, RowW, typename SrcDaT<FP8>::OB>(a, z.dff / WC::BN, kStreamLds, st);
   rec(ev, 2, st);
+  a.tl_phase = MOE_TL_DX;
   launch_stream<SrcDxT<FP8>, WC, RowW, typename SrcDxT<FP8>::OB>(a, z.d / WC::BN, kStreamLds, st);
   rec(ev, 3, st);
   if (z.T > 0)
@@ -1872,6 +1894,7 @@ static void run_backward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_
   if constexpr (FP8)
     launch_quant_dequant((const uint16_t*)a.bufA, 2 * z.dff, a.slot_to_row, 0, 1, nullptr,
                          z.T * z.k, rows, 2 * z.dff, z.beta, (uint16_t*)a.bufA, a.boff + z.E, st);
+  a.tl_phase = MOE_TL_DW;
   launch_stream<SrcDwT<DwCfg, FP8>, DwCfg, MnSegOp, MnSegOp>(a, 0, kDwLds, st);
   rec(ev, 5, st);
   hipLaunchKernelGGL(k_bwd_reduce, dim3(num_cus() * 4), dim3(256), 0, st, a.rep_slot,
@@ -1914,7 +1937,8 @@ int launch_backward(const Sizes& z, const LayerPtrs& Lp, const void* x, const fl
                     const int32_t* boff, const int32_t* row_to_slot,
                     const int32_t* slot_to_row, const int32_t* owner,
                     const int32_t* block_worker, void* dx, float* dw1, float* dw2,
-                    int32_t* status, char* ws, void* const* ev, hipStream_t st) {
+                    int32_t* status, char* ws, void* const* ev, uint64_t* timeline,
+                    hipStream_t st) {
   const WsLayout L = exec_layout(z, true);
   rec(ev, 0, st);
   launch_sched(z, counts, boff, block_worker, owner, true, ws, L, status, st);
@@ -1923,6 +1947,7 @@ int launch_backward(const Sizes& z, const LayerPtrs& Lp, const void* x, const fl
   a.x = x; a.gates = gates; a.slot_to_row = slot_to_row; a.row_to_slot = row_to_slot;
   a.z_save = const_cast<void*>(z_save);
   a.dy = dy; a.dw1 = dw1; a.dw2 = dw2; a.boff = boff;
+  a.timeline = timeline;
   if (Lp.act_dtype == MOE_F32) run_backward<float, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else if (Lp.w_dtype == MOE_FP8_E4M3) {
     if (use_stream(z)) run_backward_stream<true>(z, a, row_to_slot, dx, dw1, dw2, ev, st);

@@ -73,14 +73,16 @@ struct LayerPtrs {
 int launch_forward(const Sizes& z, const LayerPtrs& L, const void* x, const float* gates,
                    const int32_t* counts, const int32_t* boff, const int32_t* row_to_slot,
                    const int32_t* slot_to_row, const int32_t* block_worker, void* y,
-                   void* z_save, int32_t* status, char* ws, void* const* ev, hipStream_t st);
+                   void* z_save, int32_t* status, char* ws, void* const* ev,
+                   uint64_t* timeline, hipStream_t st);
 
 int launch_backward(const Sizes& z, const LayerPtrs& L, const void* x, const float* gates,
                     const void* dy, const void* z_save, const int32_t* counts,
                     const int32_t* boff, const int32_t* row_to_slot,
                     const int32_t* slot_to_row, const int32_t* owner,
                     const int32_t* block_worker, void* dx, float* dw1, float* dw2,
-                    int32_t* status, char* ws, void* const* ev, hipStream_t st);
+                    int32_t* status, char* ws, void* const* ev, uint64_t* timeline,
+                    hipStream_t st);
 
 int gemm_wg_per_cu();
 

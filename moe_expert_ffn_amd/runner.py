@@ -61,19 +61,20 @@ class LayerRunner:
                         self.gate_rho, out, self.status)
         return out
 
-    def forward(self, x, gates, topk_ids, block_worker=None, events=None):
+    def forward(self, x, gates, topk_ids, block_worker=None, events=None, timeline=None):
         bw = self.plan_f["block_worker"] if block_worker is None else block_worker
         B.forward(self.layer, x, gates, topk_ids, self.beta, self.P, self.rs, bw, self.y, self.z,
-                  self.ws, self.status, events)
+                  self.ws, self.status, events, timeline)
         return self.y
 
-    def backward(self, x, gates, dy, topk_ids, block_worker=None, events=None):
+    def backward(self, x, gates, dy, topk_ids, block_worker=None, events=None, timeline=None):
         bw = self.plan_b["block_worker"] if block_worker is None else block_worker
         B.backward(self.layer, x, gates, dy, self.z, topk_ids, self.beta, self.P, self.s, self.rs,
-                   self.owner, bw, self.dx, self.dw1, self.dw2, self.ws, self.status, events)
+                   self.owner, bw, self.dx, self.dw1, self.dw2, self.ws, self.status, events,
+                   timeline)
         return self.dx, self.dw1, self.dw2
 
-    def step(self, x, gates, topk_ids, dy=None, s=None):
+    def step(self, x, gates, topk_ids, dy=None, s=None, timeline=None):
         """One pass of the whole path: route -> plan -> forward [-> plan(bwd) -> backward].
 
         s (default: the runner's s) is the replica budget of both plans; it may
@@ -82,8 +83,8 @@ class LayerRunner:
             raise B.MoeError(f"replica budget s={s} above the runner's s={self.s}")
         self.route(topk_ids)
         self.make_plan(B.PLAN_FWD, s)
-        self.forward(x, gates, topk_ids)
+        self.forward(x, gates, topk_ids, timeline=timeline)
         if dy is not None:
             self.make_plan(B.PLAN_BWD, s, self.plan_b)
-            self.backward(x, gates, dy, topk_ids)
+            self.backward(x, gates, dy, topk_ids, timeline=timeline)
         return self.y

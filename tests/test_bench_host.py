@@ -46,3 +46,13 @@ def test_kernel_model_reduce_entry_only_with_bytes():
     # the useful flops of the five contractions add up to 18 d d_ff per routed row
     fl = sum(v[0] for v in m1.values())
     assert fl == 18 * w.d * w.d_ff * R
+
+
+def test_worker_spread_from_a_hand_timeline():
+    # 16 workgroups, P = 2: workers own workgroups with g % 8 < 4 (worker 0) and >= 4 (worker 1)
+    tl = np.zeros((5, 1024, 2), dtype=np.int64)
+    g = np.arange(16)
+    tl[0, :16, 0] = 100
+    tl[0, :16, 1] = np.where(g % 8 < 4, 200, 400)       # worker 0 ends at +100, worker 1 at +300
+    sp = bench.worker_spread(tl, 2)
+    assert sp == {"fc1": round(300 / 200, 3)}
