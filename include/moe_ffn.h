@@ -239,7 +239,9 @@ int moe_predict_cost(const int32_t* counts, const int32_t* block_offsets,
  * executed over the planned blocks: worker r's CU partition runs the blocks
  * with block_worker == r.  The result does not depend on the plan: every
  * routed row is computed by the same code whatever worker runs it, and the k
- * contributions of a token are added in slot order in fp32, rounded once.
+ * contributions of a token are added in slot order in fp32.  Each
+ * contribution p_tj * O is first stored in the activation dtype (for bf16 it
+ * is rounded there, and the fp32 sum is rounded again to give y_t).
  *   x [T][d] act dtype; gates [T][k] fp32 (p_tj);
  *   counts/block_offsets/row_to_slot/slot_to_row from moe_route_stats;
  *   block_worker from moe_plan (or any assignment of blocks to [0,P)).

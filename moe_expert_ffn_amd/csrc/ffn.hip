@@ -426,7 +426,9 @@ __global__ __launch_bounds__(C::NT) void k_fc2(ExecArgs a) {
 // lane j holding slot j) and taken out of their lanes as wave-uniform values;
 // each lane covers 16-byte chunks c, c + 64, ... of the row, two at a time.
 // For every chunk the values of up to 8 slots are loaded together and then
-// added in slot order, starting from 0, in fp32, and rounded once.
+// added in slot order, starting from 0, in fp32, and the sum is rounded to the
+// output dtype.  The slot rows themselves arrive in that dtype (FC2 and dX
+// store them rounded), so a bf16 output is rounded twice in all.
 template <typename T>
 __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ src,
                                                  const int32_t* __restrict__ row_to_slot,
