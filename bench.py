@@ -111,7 +111,12 @@ def predicted_cost(case, w, P):
 
 
 def time_steps(case, steps, warmup, with_events=True):
-    """Times `steps` full steps; returns wall ms/step and per-stage mean ms."""
+    """Times `steps` full steps with nothing but the layer's own launches
+    between the two synchronisations (wall ms/step).  With `with_events`, the
+    same number of steps is run again with HIP events recorded around every
+    stage for the per-stage mean ms: each recorded event holds the stream for
+    a few microseconds (about 6 us measured between kernels), so those steps
+    are longer and are not the step time."""
     import torch
 
     from moe_expert_ffn_amd import binding as B
@@ -129,22 +134,22 @@ def time_steps(case, steps, warmup, with_events=True):
     for _ in range(warmup):
         one()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     evs = []
     if with_events:
         for _ in range(steps):
             evs.append((B.Events(5), B.Events(7) if bwd else None, B.Events(2)))
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        if with_events:
+        torch.cuda.synchronize()
+        for i in range(steps):
             ef, eb, es = evs[i]
             es.record(0)
             one(ef.ev, eb.ev if eb else None)
             es.record(1)
-        else:
-            one()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+        torch.cuda.synchronize()
     stages = {}
     if with_events:
         acc = {}
@@ -329,7 +334,7 @@ def timeline_step(case):
 
 def kappa_sweep(w, dev, lay, steps, warmup=3):
     """Every kappa of the workload under each arm of SWEEP_ARMS: ms per step
-    (HIP-event median over `steps` steps), useful TFLOP/s and its share of the
+    (wall clock over `steps` steps, no stage events), useful TFLOP/s and its share of the
     bf16 peak, the forward and backward stage sums, and the plans' objectives.
     Returns (rows, skew) with skew[arm] = ms(max kappa) / ms(kappa 1)."""
     import torch
@@ -343,8 +348,7 @@ def kappa_sweep(w, dev, lay, steps, warmup=3):
         useful = (f_fwd + (f_bwd if w.backward else 0)) * R
         for arm, fixed, lam in SWEEP_ARMS:
             c = build_case(w, kap, fixed, dev, lam=lam, lay=lay, routing=routing)
-            _, st = time_steps(c, steps, warmup)
-            ms = st["step_median"]
+            ms, st = time_steps(c, steps, warmup)
             spread = worker_spread(timeline_step(c), c["runner"].P)
             pf = c["runner"].plan_f["plan_info"].cpu().tolist()
             pb = c["runner"].plan_b["plan_info"].cpu().tolist() if w.backward else None
@@ -505,6 +509,9 @@ def main():
                    "plan_info_fwd": plan_f,
                    **({"plan_info_bwd": plan_b, "reduce_bytes": red_bytes} if w.backward else {})},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        # per-stage means from a second pass of the same steps with HIP events
+        # around every stage (each event holds the stream a few microseconds,
+        # so "step" there is above ms_per_step)
         "stages_us": {k: round(v * 1e3, 2) for k, v in stages.items()},
         "roofline": roof,
         "kernels": per_kernel,
