@@ -32,8 +32,12 @@ METRIC = "MoE-layer useful TFLOP/s (fwd,bwd) at κ=1/2/4/8; % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 4096 flop/clk x 2.4 GHz, dense
 PEAK_HBM_GBS = 8000.0
 
-FWD_STAGES = ["sched", "fc1", "fc2", "combine"]
-BWD_STAGES = ["sched", "dA", "dX", "combine", "dW", "reduce"]
+# stage names between consecutive stage events, keyed by the two-phase launch
+# (FC1 and FC2, dA and dX in one kernel), which records its two events back to
+# back (None: that interval holds no work)
+FWD_STAGES = {False: ["sched", "fc1", "fc2", "combine"], True: ["sched", "fc1+fc2", None, "combine"]}
+BWD_STAGES = {False: ["sched", "dA", "dX", "combine", "dW", "reduce"],
+              True: ["sched", "dA+dX", None, "combine", "dW", "reduce"]}
 
 
 def parse():
@@ -153,12 +157,15 @@ def time_steps(case, steps, warmup, with_events=True):
     stages = {}
     if with_events:
         acc = {}
+        two = r.two_phase
         for ef, eb, es in evs:
-            for j, nm in enumerate(FWD_STAGES):
-                acc.setdefault("fwd." + nm, []).append(ef.elapsed_ms(j, j + 1))
+            for j, nm in enumerate(FWD_STAGES[two]):
+                if nm:
+                    acc.setdefault("fwd." + nm, []).append(ef.elapsed_ms(j, j + 1))
             if eb:
-                for j, nm in enumerate(BWD_STAGES):
-                    acc.setdefault("bwd." + nm, []).append(eb.elapsed_ms(j, j + 1))
+                for j, nm in enumerate(BWD_STAGES[two]):
+                    if nm:
+                        acc.setdefault("bwd." + nm, []).append(eb.elapsed_ms(j, j + 1))
             acc.setdefault("step", []).append(es.elapsed_ms(0, 1))
         stages = {k: sum(v) / len(v) for k, v in acc.items()}
         steps_sorted = sorted(acc["step"])
@@ -195,6 +202,10 @@ def kernel_model(w, R, T, e_act, replicas, red_bytes=0):
         })
         if red_bytes > 0:
             m["bwd.reduce"] = (0, red_bytes)
+    # the two-phase launches: both products, their rows written and read back
+    for a, b, k in (("fwd.fc1", "fwd.fc2", "fwd.fc1+fc2"), ("bwd.dA", "bwd.dX", "bwd.dA+dX")):
+        if a in m:
+            m[k] = (m[a][0] + m[b][0], m[a][1] + m[b][1])
     return m
 
 
@@ -484,6 +495,10 @@ def main():
     case = build_case(w, args.kappa, args.fixed, dev, lay=lay)
     R = int((case["ids_np"] >= 0).sum())
     ms, stages = time_steps(case, args.steps, args.warmup)
+    # the same steps with FC1 / FC2 and dA / dX in one two-phase launch each
+    case["runner"].two_phase = True
+    ms_two, stages_two = time_steps(case, args.steps, args.warmup)
+    case["runner"].two_phase = False
     f_fwd, f_bwd = flops_per_row(w)
     useful = (f_fwd + (f_bwd if w.backward else 0)) * R
     value = useful / (ms * 1e-3) / 1e12
@@ -493,6 +508,10 @@ def main():
     replicas = int(case["runner"].plan_b["plan_info"][2].item()) if w.backward else 0
     red_bytes = reduce_bytes(case, w) if w.backward else 0
     roof, per_kernel = roofline(w, stages, R, case["T"], e_act, replicas, red_bytes)
+    _, per_two = roofline(w, stages_two, R, case["T"], e_act, replicas, red_bytes)
+    for k in ("fwd.fc1+fc2", "bwd.dA+dX"):
+        if k in per_two:
+            per_kernel[k + " (two-phase launch)"] = per_two[k]
 
     plan_f = case["runner"].plan_f["plan_info"].cpu().tolist()
     plan_b = case["runner"].plan_b["plan_info"].cpu().tolist() if w.backward else None
@@ -513,6 +532,9 @@ def main():
         # around every stage (each event holds the stream a few microseconds,
         # so "step" there is above ms_per_step)
         "stages_us": {k: round(v * 1e3, 2) for k, v in stages.items()},
+        # FC1 / FC2 and dA / dX in one two-phase launch each (MOE_EXEC_TWO_PHASE)
+        "two_phase": {"ms_per_step": round(ms_two, 4),
+                      "stages_us": {k: round(v * 1e3, 2) for k, v in stages_two.items()}},
         "roofline": roof,
         "kernels": per_kernel,
     }

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -62,6 +62,15 @@ typedef enum {
                                   blocks are not one run (those blocks are skipped),
                                   or a plan that does not fit block_worker */
 #define MOE_DEV_BAD_OWNER  4   /* owner[e] outside [0,P) */
+#define MOE_DEV_WAIT_TIMEOUT 8 /* a two-phase launch waited over 2 s for rows of its
+                                  first phase (its workgroups were not all resident);
+                                  the results are not valid */
+
+/* exec_flags of moe_forward and moe_backward */
+#define MOE_EXEC_TWO_PHASE 1    /* run FC1 and FC2 (dA and dX) as one two-phase
+                                   persistent launch with per-row-tile readiness
+                                   counters instead of two launches; the results
+                                   are the same bits */
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 
@@ -266,7 +275,7 @@ int moe_forward(const moe_layer* L, const void* x, const float* gates,
                 const int32_t* counts, const int32_t* block_offsets,
                 const int32_t* row_to_slot, const int32_t* slot_to_row,
                 const int32_t* block_worker, void* y, void* z_save,
-                int32_t* status_dev, void* ws, size_t ws_bytes,
+                int32_t* status_dev, void* ws, size_t ws_bytes, int exec_flags,
                 void* const* stage_events, uint64_t* timeline, void* stream);
 
 /* Backward expert layer (gradient equations of the "Backward" section), with
@@ -302,7 +311,7 @@ int moe_backward(const moe_layer* L, const void* x, const float* gates, const vo
                  int P, int s, const int32_t* counts, const int32_t* block_offsets,
                  const int32_t* row_to_slot, const int32_t* slot_to_row,
                  const int32_t* owner, const int32_t* block_worker, void* dx, float* dw1,
-                 float* dw2, int32_t* status_dev, void* ws, size_t ws_bytes,
+                 float* dw2, int32_t* status_dev, void* ws, size_t ws_bytes, int exec_flags,
                  void* const* stage_events, uint64_t* timeline, void* stream);
 
 /* Token-axis e4m3 requantization (MegaFlux summary, "Backward": D_e and dZ_e

@@ -15,11 +15,12 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_ffn.so")
 
-ABI_VERSION = 3                 # MOE_ABI_VERSION of the header these signatures follow
+ABI_VERSION = 4                 # MOE_ABI_VERSION of the header these signatures follow
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 PLAN_FWD, PLAN_BWD, PLAN_QUOTA = 0, 1, 2
-DEV_BAD_EXPERT, DEV_BAD_PLAN, DEV_BAD_OWNER = 1, 2, 4
+DEV_BAD_EXPERT, DEV_BAD_PLAN, DEV_BAD_OWNER, DEV_WAIT_TIMEOUT = 1, 2, 4, 8
+EXEC_TWO_PHASE = 1              # MOE_EXEC_TWO_PHASE
 TIMELINE_MAX_WG, TL_PHASES = 1024, 5          # MOE_TIMELINE_MAX_WG, MOE_TL_PHASES
 TL_FC1, TL_FC2, TL_DA, TL_DX, TL_DW = range(5)
 
@@ -80,10 +81,10 @@ def load():
     lib.moe_plan_gate.argtypes = [_P, _P, _P, _I, _I, _I] + [_P] * 3 + [_I] + [_P] * 2 + [_P]
     lib.moe_forward.restype = _I
     lib.moe_forward.argtypes = ([ctypes.POINTER(Layer), _P, _P, _P, _I, _I, _I, _I]
-                                + [_P] * 8 + [_P, _SZ, _P, _P, _P])
+                                + [_P] * 8 + [_P, _SZ, _I, _P, _P, _P])
     lib.moe_backward.restype = _I
     lib.moe_backward.argtypes = ([ctypes.POINTER(Layer), _P, _P, _P, _P, _P, _I, _I, _I, _I, _I]
-                                 + [_P] * 10 + [_P, _SZ, _P, _P, _P])
+                                 + [_P] * 10 + [_P, _SZ, _I, _P, _P, _P])
     lib.moe_event_create.argtypes = [ctypes.POINTER(_P)]
     lib.moe_event_destroy.argtypes = [_P]
     lib.moe_event_record.argtypes = [_P, _P]
@@ -344,7 +345,7 @@ def _expect_timeline(timeline):
 
 
 def forward(layer: Layer, x, gates, topk_ids, beta, P, rs, block_worker, y, z_save, ws, status,
-            events=None, timeline=None):
+            events=None, timeline=None, two_phase=False):
     _require_device(x, gates, topk_ids, y, z_save, ws, status, block_worker, timeline)
     _expect_timeline(timeline)
     T, k = _ids_shape(topk_ids)
@@ -363,11 +364,12 @@ def forward(layer: Layer, x, gates, topk_ids, beta, P, rs, block_worker, y, z_sa
                               beta, P, _ptr(rs["counts"]), _ptr(rs["block_offsets"]),
                               _ptr(rs["row_to_slot"]), _ptr(rs["slot_to_row"]),
                               _ptr(block_worker), _ptr(y), _ptr(z_save), _ptr(status), wsp, wsn,
-                              ev, _ptr(timeline), _stream()))
+                              EXEC_TWO_PHASE if two_phase else 0, ev, _ptr(timeline),
+                              _stream()))
 
 
 def backward(layer: Layer, x, gates, dy, z_save, topk_ids, beta, P, s, rs, owner, block_worker,
-             dx, dw1, dw2, ws, status, events=None, timeline=None):
+             dx, dw1, dw2, ws, status, events=None, timeline=None, two_phase=False):
     _require_device(x, gates, dy, z_save, topk_ids, owner, block_worker, dx, dw1, dw2, ws, status,
                     timeline)
     _expect_timeline(timeline)
@@ -390,7 +392,8 @@ def backward(layer: Layer, x, gates, dy, z_save, topk_ids, beta, P, s, rs, owner
                                _ptr(topk_ids), T, k, beta, P, s, _ptr(rs["counts"]),
                                _ptr(rs["block_offsets"]), _ptr(rs["row_to_slot"]),
                                _ptr(rs["slot_to_row"]), _ptr(owner), _ptr(block_worker), _ptr(dx),
-                               _ptr(dw1), _ptr(dw2), _ptr(status), wsp, wsn, ev, _ptr(timeline),
+                               _ptr(dw1), _ptr(dw2), _ptr(status), wsp, wsn,
+                               EXEC_TWO_PHASE if two_phase else 0, ev, _ptr(timeline),
                                _stream()))
 
 

@@ -218,10 +218,11 @@ int moe_forward(const moe_layer* L, const void* x, const float* gates, const int
                 int T, int k, int beta, int P, const int32_t* counts,
                 const int32_t* block_offsets, const int32_t* row_to_slot,
                 const int32_t* slot_to_row, const int32_t* block_worker, void* y, void* z_save,
-                int32_t* status_dev, void* ws, size_t ws_bytes, void* const* stage_events,
-                uint64_t* timeline, void* stream) {
+                int32_t* status_dev, void* ws, size_t ws_bytes, int exec_flags,
+                void* const* stage_events, uint64_t* timeline, void* stream) {
   (void)topk_ids;
   const int lc = check_layer(L, false);
+  if (exec_flags & ~MOE_EXEC_TWO_PHASE) return MOE_ERR_ARG;
   if (lc != MOE_OK) return lc;
   if (!sizes_ok(T, k, L->E, beta)) return MOE_ERR_ARG;
   if (!valid_P(P)) return MOE_ERR_UNSUPPORTED;
@@ -233,8 +234,8 @@ int moe_forward(const moe_layer* L, const void* x, const float* gates, const int
   if (!ws_ok(ws, ws_bytes, exec_layout(z, false).total)) return MOE_ERR_WORKSPACE;
   LayerPtrs Lp{L->w1, L->w2, L->w1_scale, L->w2_scale, L->act_dtype, L->w_dtype};
   return launch_forward(z, Lp, x, gates, counts, block_offsets, row_to_slot, slot_to_row,
-                        block_worker, y, z_save, status_dev, (char*)ws, stage_events, timeline,
-                        (hipStream_t)stream);
+                        block_worker, y, z_save, status_dev, (char*)ws, exec_flags, stage_events,
+                        timeline, (hipStream_t)stream);
 }
 
 int moe_backward(const moe_layer* L, const void* x, const float* gates, const void* dy,
@@ -242,10 +243,11 @@ int moe_backward(const moe_layer* L, const void* x, const float* gates, const vo
                  int s, const int32_t* counts, const int32_t* block_offsets,
                  const int32_t* row_to_slot, const int32_t* slot_to_row, const int32_t* owner,
                  const int32_t* block_worker, void* dx, float* dw1, float* dw2,
-                 int32_t* status_dev, void* ws, size_t ws_bytes, void* const* stage_events,
-                 uint64_t* timeline, void* stream) {
+                 int32_t* status_dev, void* ws, size_t ws_bytes, int exec_flags,
+                 void* const* stage_events, uint64_t* timeline, void* stream) {
   (void)topk_ids;
   const int lc = check_layer(L, true);
+  if (exec_flags & ~MOE_EXEC_TWO_PHASE) return MOE_ERR_ARG;
   if (lc != MOE_OK) return lc;
   if (!sizes_ok(T, k, L->E, beta) || s < 0) return MOE_ERR_ARG;
   if (!valid_P(P)) return MOE_ERR_UNSUPPORTED;
@@ -258,7 +260,7 @@ int moe_backward(const moe_layer* L, const void* x, const float* gates, const vo
   LayerPtrs Lp{L->w1, L->w2, L->w1_scale, L->w2_scale, L->act_dtype, L->w_dtype};
   return launch_backward(z, Lp, x, gates, dy, z_save, counts, block_offsets, row_to_slot,
                          slot_to_row, owner, block_worker, dx, dw1, dw2, status_dev, (char*)ws,
-                         stage_events, timeline, (hipStream_t)stream);
+                         exec_flags, stage_events, timeline, (hipStream_t)stream);
 }
 
 int moe_event_create(void** ev) {

@@ -37,6 +37,7 @@ struct SchedArgs {
   int4* seg;
   int32_t* rep_slot;
   int32_t* owner_has;
+  int32_t* flags;      // per (worker, row tile) readiness counters of the two-phase launches
   int32_t* status;
 };
 
@@ -86,6 +87,7 @@ __global__ __launch_bounds__(kSchedThreads) void k_sched(SchedArgs a) {
   for (int i = tid; i <= E; i += NT) boff_s[i] = a.boff[i];
   for (int i = tid; i < E; i += NT) cnt_s[i] = a.counts[i];
   if (tid < kNumCounters) a.ctr[tid] = 0;
+  for (int i = tid; i < P * a.max_mt; i += NT) a.flags[i] = 0;
   if (a.backward)
     for (int i = tid; i < E * P; i += NT) { s0_s[i] = INT_MAX; rows_s[i] = 0; starts_s[i] = 0; }
   __syncthreads();
@@ -248,7 +250,9 @@ struct ExecArgs {
                           //   widened back to bf16, [slots][d]
   const int32_t* boff;    // block offsets [E + 1]: boff[E] blocks of beta slots are in use
   uint64_t* timeline;     // nullable: per-workgroup start / end stamps of each stream phase
-  int tl_phase;           //   this launch's phase row
+  int tl_phase;           //   this launch's phase row (a two-phase launch: its first phase)
+  int32_t* flags;         // two-phase launches: finished first-phase items per (worker, row tile)
+  int32_t* status;
 };
 
 enum { PH_FC1 = 0, PH_FC2 = 1, PH_DA = 2, PH_DX = 3, PH_DW = 4 };
@@ -962,8 +966,9 @@ MOE_DEV void stg16v(void* p, const u32x4_t& d) {
 // 16 bytes at element column `col` of slot row `srow` of a [slots][ld] bf16
 // buffer; a row past the tile's end is sent out of range and dropped, so an
 // epilogue issues the same number of stores for every tile
+template <int CP = kStoreLocal>
 MOE_DEV void st_row16(const BufRsrc& r, int srow, int ld, int col, bool ok, const u32x4_t& d) {
-  buf_store16(r, ok ? ((uint32_t)srow * (uint32_t)ld + (uint32_t)col) * 2u : kOob, d);
+  buf_store16c<CP>(r, ok ? ((uint32_t)srow * (uint32_t)ld + (uint32_t)col) * 2u : kOob, d);
 }
 
 MOE_DEV const MOE_LDS int* item_rows(const MOE_LDS uint16_t* smem, int slot) {
@@ -1053,7 +1058,9 @@ using RowF8 = RowKFp8<256, kWNW, kRowBK>;
 // rows alternate 32 G rows and the matching 32 U rows, so block j = 0 of a
 // wave is G and block j = 1 is U of the same 32 columns.  With e4m3 weights
 // the G rows of tile nj lie in scale block nj and the U rows in d_ff/128 + nj.
-template <bool FP8> struct SrcFc1T : MSrcBase {
+// COH: A is stored with device-scope completion, read by FC2 items of the
+// same launch (the saved [G, U] is only read by later launches).
+template <bool FP8, bool COH = false> struct SrcFc1T : MSrcBase {
   using Item = MItem;
   using OB = typename std::conditional<FP8, RowF8, RowW>::type;
   MOE_DEV void fill(const Item& it, int slot) const { fill_rows(it, slot); }
@@ -1093,24 +1100,27 @@ template <bool FP8> struct SrcFc1T : MSrcBase {
 #pragma unroll
     for (int i = 0; i < WC::MB; ++i) {
       const int rb = wm * WC::WM + i * 32;
-      auto emit_to = [&](const BufRsrc& r, int col0, int ld) {
+      auto emit_to = [&](const BufRsrc& r, int col0, int ld, auto cp) {
         return [&, col0, ld](int row, int c, const u32x4_t& d) {
-          st_row16(r, it.slot0 + rb + row, ld, col0 + colb + c * 8, rb + row < it.nrows, d);
+          st_row16<decltype(cp)::value>(r, it.slot0 + rb + row, ld, col0 + colb + c * 8,
+                                        rb + row < it.nrows, d);
         };
       };
+      using CpA = std::integral_constant<int, COH ? kStoreDevice : kStoreLocal>;
+      using CpZ = std::integral_constant<int, kStoreLocal>;
       RowStore<uint16_t, 1>::run(scr, [&](int, int g, float* v) {
         for (int q = 0; q < 4; ++q) {
           const float gv = acc[i][0][4 * g + q];
           v[q] = gv * sigm(gv) * acc[i][1][4 * g + q];
         }
-      }, emit_to(ra, 0, dff));
+      }, emit_to(ra, 0, dff, CpA{}));
       if (a.z_save) {
         RowStore<uint16_t, 1>::run(scr, [&](int, int g, float* v) {
           for (int q = 0; q < 4; ++q) v[q] = acc[i][0][4 * g + q];
-        }, emit_to(rz, 0, 2 * dff));
+        }, emit_to(rz, 0, 2 * dff, CpZ{}));
         RowStore<uint16_t, 1>::run(scr, [&](int, int g, float* v) {
           for (int q = 0; q < 4; ++q) v[q] = acc[i][1][4 * g + q];
-        }, emit_to(rz, dff, 2 * dff));
+        }, emit_to(rz, dff, 2 * dff, CpZ{}));
       }
     }
   }
@@ -1165,7 +1175,9 @@ template <bool FP8> struct SrcFc2T : MSrcBase {
 // activation P = p SiLU(G) U for the weight gradient of W2.  With e4m3
 // weights the weight gradient of W2 takes the requantized D = p dy instead,
 // so P is written without the gate.
-template <bool FP8> struct SrcDaT : MSrcBase {
+// COH: dZ is stored with device-scope completion, read by dX items of the
+// same launch.
+template <bool FP8, bool COH = false> struct SrcDaT : MSrcBase {
   using Item = MItem;
   using OB = typename std::conditional<FP8, MnF8Op, MnFixedOp>::type;
   MOE_DEV void fill(const Item& it, int slot) const { fill_rows(it, slot); fill_gates(it, slot); }
@@ -1227,11 +1239,14 @@ template <bool FP8> struct SrcDaT : MSrcBase {
       const int rb = wm * WC::WM + i * 32, cb = colb + j * 32;
       const float pg = gt[rb + (lane & 31)];
       using RS = RowStore<uint16_t, 1>;
-      auto emit_to = [&](const BufRsrc& r, int col0, int ld) {
+      auto emit_to = [&](const BufRsrc& r, int col0, int ld, auto cp) {
         return [&, col0, ld](int row, int c, const u32x4_t& d) {
-          st_row16(r, it.slot0 + rb + row, ld, col0 + cb + c * 8, rb + row < it.nrows, d);
+          st_row16<decltype(cp)::value>(r, it.slot0 + rb + row, ld, col0 + cb + c * 8,
+                                        rb + row < it.nrows, d);
         };
       };
+      using CpZ = std::integral_constant<int, COH ? kStoreDevice : kStoreLocal>;
+      using CpP = std::integral_constant<int, kStoreLocal>;
       // one output per pass, 8 packed registers at a time; the sigmoid is
       // taken again in each pass (the empty asm keeps the passes apart, so
       // the compiler does not hold 32 sigmoids across them)
@@ -1256,12 +1271,12 @@ template <bool FP8> struct SrcDaT : MSrcBase {
       };
       RS::Packed pk[1][4];
       pass(0, pk);
-      RS::store(scr, pk, emit_to(rdz, 0, 2 * dff));
+      RS::store(scr, pk, emit_to(rdz, 0, 2 * dff, CpZ{}));
       pass(1, pk);
       if (b == 0 && NBLK > 1) zload(1, zg2[1], zu2[1]);
-      RS::store(scr, pk, emit_to(rdz, dff, 2 * dff));
+      RS::store(scr, pk, emit_to(rdz, dff, 2 * dff, CpZ{}));
       pass(2, pk);
-      RS::store(scr, pk, emit_to(rp, 0, dff));
+      RS::store(scr, pk, emit_to(rp, 0, dff, CpP{}));
     }
   }
 };
@@ -1308,6 +1323,81 @@ template <bool FP8> struct SrcDxT : MSrcBase {
   }
 };
 
+// Two GEMM phases in one persistent launch (MegaFlux summary, Methodology
+// section 2, "Executor: Pipelined Expert Replication — Forward": the second
+// product of a block needs only the completed activation block of the first).
+// P1 produces rows that P2 consumes: FC1 -> A -> FC2, or dA -> dZ -> dX.  Each
+// workgroup first streams its share of the worker's P1 items (row tile m, N
+// tile j), then its share of the P2 items, as two passes of the stream engine
+// in one kernel.  Each finished P1 item adds one to flags[worker][m] once its
+// stores are complete (at the next step's full wait, or at the end of the
+// pass); a P2 item of row tile m issues its first loads only once that
+// counter holds P1's N-tile count.  The rows P1 writes for P2 are stored with
+// device-scope completion, and no workgroup reads them before their counter
+// is complete, so no cache level holds an older copy when they are read (each
+// launch starts with clean caches).  The workgroups of one launch are all
+// resident (one per CU, grid = CU count) and a P2 wait depends only on P1
+// items, which never wait.  A wait that outlasts kFlowWaitTicks (2 s) sets
+// MOE_DEV_WAIT_TIMEOUT and goes on.
+struct PItem : MItem { int m; };
+constexpr uint64_t kFlowWaitTicks = 200000000ull;   // the 100 MHz real-time counter
+template <class Src> struct FlowBase : Src {
+  static constexpr bool kFlow = true;
+  using Item = PItem;
+  MOE_DEV Item load(int idx) const {
+    const int m = idx / this->nnt;
+    const u32x4_t d = ((const MOE_CONST u32x4_t*)this->a.mt)[(size_t)this->r * this->a.max_mt + m];
+    Item it;
+    it.e = (int)d.x;
+    it.slot0 = (int)d.y;
+    it.nrows = (int)d.z;
+    it.nj = idx - m * this->nnt;
+    it.m = m;
+    return it;
+  }
+  MOE_DEV int32_t* flag(int m) const {
+    return this->a.flags + (size_t)this->r * this->a.max_mt + m;
+  }
+};
+// first phase: publishes each finished row-tile item
+template <class P1> struct FlowProducer : FlowBase<P1> {
+  MOE_DEV int peek(const PItem&) const { return -1; }
+  MOE_DEV void ready(const PItem&, int) const {}
+  MOE_DEV int publish_key(const PItem& it) const { return it.m; }
+  MOE_DEV void signal(int m) const {
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(this->flag(m), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+};
+// second phase: waits for the n1 first-phase items of its row tile
+template <class P2> struct FlowConsumer : FlowBase<P2> {
+  int n1;
+  MOE_DEV int publish_key(const PItem&) const { return -1; }
+  MOE_DEV void signal(int) const {}
+  MOE_DEV int peek(const PItem& it) const {
+    return __hip_atomic_load(this->flag(it.m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // the counter only grows: a complete value seen earlier stays complete
+  MOE_DEV void ready(const PItem& it, int seen) const {
+    if (__builtin_amdgcn_readfirstlane(seen) >= n1) return;
+    int32_t* f = this->flag(it.m);
+    auto done = [&]() {
+      return __builtin_amdgcn_readfirstlane(
+                 __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >= n1;
+    };
+    if (done()) return;
+    const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + kFlowWaitTicks;
+    while (true) {
+      __builtin_amdgcn_s_sleep(8);
+      if (done()) return;
+      if (__builtin_amdgcn_s_memrealtime() > t_end) {
+        if ((threadIdx.x & 63) == 0) atomicOr(this->a.status, MOE_DEV_WAIT_TIMEOUT);
+        return;
+      }
+    }
+  }
+};
+
 // One persistent workgroup per CU for the 256 x 256 tile (8 waves), two per
 // CU for the 128 x 128 tile (4 waves): either way two waves per SIMD.
 template <class Src, class C, class OA, class OB>
@@ -1334,6 +1424,48 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void k_stream(ExecArgs a, int n
     }
   }
 }
+
+// The two-phase launch: the P1 pass, then the P2 pass (FlowProducer /
+// FlowConsumer above).  ntiles: P1's N tiles in the low 16 bits, P2's above.
+// The timeline gets both phases: P1 from the start to the end of the first
+// pass, P2 from there to the end.
+template <class S1, class S2, class C, class OA, class OB>
+__global__ __launch_bounds__(C::NT, 512 / C::NT) void k_stream2(ExecArgs a, int ntiles) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  MOE_LDS uint16_t* smem = (MOE_LDS uint16_t*)smem_raw;
+  const uint64_t t0 = a.timeline ? __builtin_amdgcn_s_memrealtime() : 0;
+  const int n1 = ntiles & 0xffff, n2 = ntiles >> 16;
+  f32x16_t acc[C::MB][C::NB];
+  WideStream<C, OA, OB> p;
+  {
+    S1 src;
+    src.init(a, smem, n1);
+    p.run(src, smem, acc);
+  }
+  const uint64_t tm = a.timeline ? __builtin_amdgcn_s_memrealtime() : 0;
+  {
+    S2 src;
+    src.init(a, smem, n2);
+    src.n1 = n1;
+    p.run(src, smem, acc);
+  }
+  if (a.timeline) {
+    __syncthreads();
+    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0 && blockIdx.x < MOE_TIMELINE_MAX_WG) {
+      MOE_GLB uint64_t* out =
+          (MOE_GLB uint64_t*)a.timeline + ((size_t)a.tl_phase * MOE_TIMELINE_MAX_WG + blockIdx.x) * 2;
+      out[0] = t0;
+      out[1] = tm;
+      out[2 * MOE_TIMELINE_MAX_WG] = tm;
+      out[2 * MOE_TIMELINE_MAX_WG + 1] = t1;
+    }
+  }
+}
+template <bool FP8> using FwdP1 = FlowProducer<SrcFc1T<FP8, true>>;
+template <bool FP8> using FwdP2 = FlowConsumer<SrcFc2T<FP8>>;
+template <bool FP8> using BwdP1 = FlowProducer<SrcDaT<FP8, true>>;
+template <bool FP8> using BwdP2 = FlowConsumer<SrcDxT<FP8>>;
 
 // ---- backward: weight gradients per (expert, worker) segment ------------------
 // K runs over the segment's routed rows.  dW2[c, n] = sum D[c] * A[n] with
@@ -1654,6 +1786,7 @@ WsLayout exec_layout(const Sizes& z, bool backward) {
   L.seg = take(sizeof(int4) * (size_t)z.P * z.E);
   L.rep_slot = take(sizeof(int32_t) * (size_t)z.E * z.P);
   L.owner_has = take(sizeof(int32_t) * (size_t)z.E);
+  L.flags = take(sizeof(int32_t) * (size_t)z.P * z.max_mt);
   L.bufA = take((size_t)z.act_bytes * z.max_slots * (backward ? 2 : 1) * z.dff);
   L.bufO = take((size_t)z.act_bytes * z.max_slots * z.d);
   L.rslots = backward ? take(sizeof(float) * (size_t)z.P * z.s * 3 * z.d * z.dff) : o;
@@ -1736,6 +1869,7 @@ static void launch_sched(const Sizes& z, const int32_t* counts, const int32_t* b
   s.seg = (int4*)(ws + L.seg);
   s.rep_slot = (int32_t*)(ws + L.rep_slot);
   s.owner_has = (int32_t*)(ws + L.owner_has);
+  s.flags = (int32_t*)(ws + L.flags);
   s.status = status;
   s.max_blocks = (int)z.max_blocks;
   // block_worker goes through LDS when it fits next to the rest (64 KB)
@@ -1763,6 +1897,7 @@ static ExecArgs make_exec(const Sizes& z, const LayerPtrs& Lp, char* ws, const W
   a.seg_cnt = (const int32_t*)(ws + L.seg_cnt);
   a.rep_slot = (const int32_t*)(ws + L.rep_slot);
   a.owner_has = (const int32_t*)(ws + L.owner_has);
+  a.flags = (int32_t*)(ws + L.flags);
   a.ctr = (int32_t*)(ws + L.ctr);
   a.bufA = ws + L.bufA;
   a.bufO = ws + L.bufO;
@@ -1817,6 +1952,15 @@ static void launch_stream(ExecArgs& a, int ntiles_n, size_t lds, hipStream_t st)
   static int g = persistent_grid(k_stream<Src, C, OA, OB>, C::NT, lds);
   hipLaunchKernelGGL((k_stream<Src, C, OA, OB>), dim3(g), dim3(C::NT), lds, st, a, ntiles_n);
 }
+// the two-phase launch relies on every workgroup being resident: the grid is
+// the persistent one (workgroups per CU that fit x CUs)
+template <class S1, class S2, class C, class OA, class OB>
+static void launch_stream2(ExecArgs& a, int ntiles, size_t lds, hipStream_t st) {
+  static_assert(std::is_same<typename S1::OB, OB>::value && std::is_same<typename S2::OB, OB>::value,
+                "one B operand type");
+  static int g = persistent_grid(k_stream2<S1, S2, C, OA, OB>, C::NT, lds);
+  hipLaunchKernelGGL((k_stream2<S1, S2, C, OA, OB>), dim3(g), dim3(C::NT), lds, st, a, ntiles);
+}
 
 static void launch_slot_gate(const Sizes& z, const ExecArgs& a, hipStream_t st) {
   const size_t n = z.max_slots;
@@ -1828,14 +1972,20 @@ static void launch_slot_gate(const Sizes& z, const ExecArgs& a, hipStream_t st) 
 
 template <bool FP8>
 static void run_forward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* y,
-                               void* const* ev, hipStream_t st) {
+                               bool split, void* const* ev, hipStream_t st) {
   launch_slot_gate(z, a, st);
+  const int n1 = z.dff / (WC::BN / 2), n2 = z.d / WC::BN;
   a.tl_phase = MOE_TL_FC1;
-  launch_stream<SrcFc1T<FP8>, WC, RowW, typename SrcFc1T<FP8>::OB>(a, z.dff / (WC::BN / 2),
-                                                                   kStreamLds, st);
-  rec(ev, 2, st);
-  a.tl_phase = MOE_TL_FC2;
-  launch_stream<SrcFc2T<FP8>, WC, RowW, typename SrcFc2T<FP8>::OB>(a, z.d / WC::BN, kStreamLds, st);
+  if (split) {
+    launch_stream<SrcFc1T<FP8>, WC, RowW, typename SrcFc1T<FP8>::OB>(a, n1, kStreamLds, st);
+    rec(ev, 2, st);
+    a.tl_phase = MOE_TL_FC2;
+    launch_stream<SrcFc2T<FP8>, WC, RowW, typename SrcFc2T<FP8>::OB>(a, n2, kStreamLds, st);
+  } else {
+    launch_stream2<FwdP1<FP8>, FwdP2<FP8>, WC, RowW, typename SrcFc1T<FP8>::OB>(
+        a, n1 | (n2 << 16), kStreamLds, st);
+    rec(ev, 2, st);
+  }
   rec(ev, 3, st);
   if (z.T > 0)
     hipLaunchKernelGGL(k_combine<uint16_t>, combine_grid(z.T), dim3(256), 0, st,
@@ -1846,7 +1996,7 @@ static void run_forward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_t
 int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const float* gates,
                    const int32_t* counts, const int32_t* boff, const int32_t* row_to_slot,
                    const int32_t* slot_to_row, const int32_t* block_worker, void* y,
-                   void* z_save, int32_t* status, char* ws, void* const* ev,
+                   void* z_save, int32_t* status, char* ws, int exec_flags, void* const* ev,
                    uint64_t* timeline, hipStream_t st) {
   const WsLayout L = exec_layout(z, false);
   rec(ev, 0, st);
@@ -1856,11 +2006,13 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
   a.x = x; a.gates = gates; a.slot_to_row = slot_to_row; a.row_to_slot = row_to_slot;
   a.z_save = z_save;
   a.timeline = timeline;
+  a.status = status;
   const bool big = use_big_tiles(z);
+  const bool split = (exec_flags & MOE_EXEC_TWO_PHASE) == 0;
   if (Lp.act_dtype == MOE_BF16 && Lp.w_dtype == MOE_BF16 && use_stream(z))
-    run_forward_stream<false>(z, a, row_to_slot, y, ev, st);
+    run_forward_stream<false>(z, a, row_to_slot, y, split, ev, st);
   else if (Lp.act_dtype == MOE_BF16 && Lp.w_dtype == MOE_FP8_E4M3 && use_stream(z))
-    run_forward_stream<true>(z, a, row_to_slot, y, ev, st);
+    run_forward_stream<true>(z, a, row_to_slot, y, split, ev, st);
   else if (Lp.act_dtype == MOE_F32) run_forward<float, false, SmallCfg>(z, a, row_to_slot, y, ev, st);
   else if (Lp.w_dtype == MOE_FP8_E4M3) {
     if (big) run_forward<uint16_t, true, BigCfg>(z, a, row_to_slot, y, ev, st);
@@ -1877,17 +2029,25 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
 // bufA once dX has used it; the weight gradients then read both as bf16.
 template <bool FP8>
 static void run_backward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* dx,
-                                float* dw1, float* dw2, void* const* ev, hipStream_t st) {
+                                float* dw1, float* dw2, bool split, void* const* ev,
+                                hipStream_t st) {
   const int rows = (int)z.max_slots;
   launch_slot_gate(z, a, st);
   if constexpr (FP8)
     launch_quant_dequant((const uint16_t*)a.dy, z.d, a.slot_to_row, 1, z.k, a.gates, z.T * z.k,
                          rows, z.d, z.beta, (uint16_t*)a.dhat, a.boff + z.E, st);
+  const int n1 = z.dff / WC::BN, n2 = z.d / WC::BN;
   a.tl_phase = MOE_TL_DA;
-  launch_stream<SrcDaT<FP8>, WC, RowW, typename SrcDaT<FP8>::OB>(a, z.dff / WC::BN, kStreamLds, st);
-  rec(ev, 2, st);
-  a.tl_phase = MOE_TL_DX;
-  launch_stream<SrcDxT<FP8>, WC, RowW, typename SrcDxT<FP8>::OB>(a, z.d / WC::BN, kStreamLds, st);
+  if (split) {
+    launch_stream<SrcDaT<FP8>, WC, RowW, typename SrcDaT<FP8>::OB>(a, n1, kStreamLds, st);
+    rec(ev, 2, st);
+    a.tl_phase = MOE_TL_DX;
+    launch_stream<SrcDxT<FP8>, WC, RowW, typename SrcDxT<FP8>::OB>(a, n2, kStreamLds, st);
+  } else {
+    launch_stream2<BwdP1<FP8>, BwdP2<FP8>, WC, RowW, typename SrcDaT<FP8>::OB>(
+        a, n1 | (n2 << 16), kStreamLds, st);
+    rec(ev, 2, st);
+  }
   rec(ev, 3, st);
   if (z.T > 0)
     hipLaunchKernelGGL(k_combine<uint16_t>, combine_grid(z.T), dim3(256), 0, st,
@@ -1939,8 +2099,8 @@ int launch_backward(const Sizes& z, const LayerPtrs& Lp, const void* x, const fl
                     const int32_t* boff, const int32_t* row_to_slot,
                     const int32_t* slot_to_row, const int32_t* owner,
                     const int32_t* block_worker, void* dx, float* dw1, float* dw2,
-                    int32_t* status, char* ws, void* const* ev, uint64_t* timeline,
-                    hipStream_t st) {
+                    int32_t* status, char* ws, int exec_flags, void* const* ev,
+                    uint64_t* timeline, hipStream_t st) {
   const WsLayout L = exec_layout(z, true);
   rec(ev, 0, st);
   launch_sched(z, counts, boff, block_worker, owner, true, ws, L, status, st);
@@ -1950,12 +2110,14 @@ int launch_backward(const Sizes& z, const LayerPtrs& Lp, const void* x, const fl
   a.z_save = const_cast<void*>(z_save);
   a.dy = dy; a.dw1 = dw1; a.dw2 = dw2; a.boff = boff;
   a.timeline = timeline;
+  a.status = status;
+  const bool split = (exec_flags & MOE_EXEC_TWO_PHASE) == 0;
   if (Lp.act_dtype == MOE_F32) run_backward<float, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else if (Lp.w_dtype == MOE_FP8_E4M3) {
-    if (use_stream(z)) run_backward_stream<true>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
+    if (use_stream(z)) run_backward_stream<true>(z, a, row_to_slot, dx, dw1, dw2, split, ev, st);
     else if (use_big_tiles(z)) run_backward<uint16_t, BigCfg, true>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
     else run_backward<uint16_t, SmallCfg, true>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
-  } else if (use_stream(z)) run_backward_stream<false>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
+  } else if (use_stream(z)) run_backward_stream<false>(z, a, row_to_slot, dx, dw1, dw2, split, ev, st);
   else if (use_big_tiles(z)) run_backward<uint16_t, BigCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else run_backward<uint16_t, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;

@@ -341,6 +341,12 @@ MOE_DEV void buf_load_lds16(BufRsrc r, uint32_t off, MOE_LDS void* dst) {
 MOE_DEV void buf_store16(BufRsrc r, uint32_t off, const u32x4_t& d) {
   __builtin_amdgcn_raw_buffer_store_b128(d, r, off, 0, 0);
 }
+// the same with cache-policy bits CP (16 = sc1: the store completes once it is
+// visible at device scope, so a workgroup on another XCD can read it)
+template <int CP> MOE_DEV void buf_store16c(BufRsrc r, uint32_t off, const u32x4_t& d) {
+  __builtin_amdgcn_raw_buffer_store_b128(d, r, off, 0, CP);
+}
+constexpr int kStoreLocal = 0, kStoreDevice = 16;
 
 MOE_DEV int dma_swz(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row >> 3)) & 3); }
 
@@ -692,6 +698,13 @@ MOE_DEV bf16x8_t dequant8(const u32x2_t& q, float s) {
 
 template <class T, class = void> struct op_fp8 { static constexpr bool value = false; };
 template <class T> struct op_fp8<T, decltype((void)T::kFp8)> { static constexpr bool value = T::kFp8; };
+// A source that takes part in a two-phase launch (kFlow): peek(it) loads the
+// readiness of the rows item `it` reads, ready(it, seen) returns once they are
+// complete (seen: an earlier peek's value, or a negative number for none),
+// publish_key(it) is what a finished item publishes (-1 for nothing), and
+// signal(key) publishes it once the item's stores are complete.
+template <class T, class = void> struct src_flow { static constexpr bool value = false; };
+template <class T> struct src_flow<T, decltype((void)T::kFlow)> { static constexpr bool value = T::kFlow; };
 
 // MN-contiguous operand: BK K rows x MN elements per stage, [k][MN], fragments
 // through ds_read_b64_tr_b16: inside each 16-lane group, lane j supplies the
@@ -965,6 +978,8 @@ template <class C, class OA, class OB> struct WideStream {
     OA a0 = src.opA(it0, slot);
     OB b0 = src.opB(it0, slot);
     int n0 = src.steps(it0);
+    constexpr bool FLOW = src_flow<Src>::value;
+    if constexpr (FLOW) src.ready(it0, -1);
 #pragma unroll
     for (int st = 0; st < S; ++st) {
       const auto pa = a0.prep(st);
@@ -972,6 +987,12 @@ template <class C, class OA, class OB> struct WideStream {
       a0.issue(pa, smem + st * STAGE);
       b0.issue(pb, smem + st * STAGE + SA);
     }
+    // two-phase sources: the last finished item not yet published (its
+    // epilogue stores are published at the next strict wait; -1: none)
+    int pend = -1;
+    // the next item's readiness, loaded one step before its first loads are
+    // issued; the full wait ending that step covers the load
+    int peeked = -1;
     float bsn[C::NB];                            // B scales of the next step
     if constexpr (BF8) {
 #pragma unroll
@@ -1039,9 +1060,18 @@ template <class C, class OA, class OB> struct WideStream {
           mma<0>(acc);
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (relax && kt < S - 1) src.template relaxed_wait<VM_AHEAD>();
+        const bool strict = !(relax && kt < S - 1);
+        if (!strict) src.template relaxed_wait<VM_AHEAD>();
         else wait_vm_lgkm0<VM_AHEAD>();
         __builtin_amdgcn_s_barrier();
+        if constexpr (FLOW) {
+          // every wave has waited for its stores of the previous item
+          if (pend >= 0 && strict) { src.signal(pend); pend = -1; }
+          if (nxt && ks == 0) {
+            src.ready(it1, (S < n0 && strict) ? peeked : -1);
+            peeked = -1;
+          }
+        }
         // every wave is past the previous item's epilogue: item slot s2 is free
         if (kt == 0 && h2) src.fill(it2, s2);
         if (nxt) {
@@ -1051,6 +1081,9 @@ template <class C, class OA, class OB> struct WideStream {
           a0.issue(pa, smem + (g & (S - 1)) * STAGE);
           b0.issue(pb, smem + (g & (S - 1)) * STAGE + SA);
         }
+        if constexpr (FLOW) {
+          if (h1 && kt + S + 1 == n0) peeked = src.peek(it1);
+        }
         // chunk 0 of the next step; for the next item it is read after the
         // epilogue, so its fragments are not live across it
         if (kt + 1 < n0) read<0, 0>(smem + ((g + 1) & (S - 1)) * STAGE);
@@ -1059,6 +1092,7 @@ template <class C, class OA, class OB> struct WideStream {
         __builtin_amdgcn_sched_barrier(0);
       }
       src.epilogue(it0, slot, acc);
+      if constexpr (FLOW) pend = src.publish_key(it0);
       if (!h1) break;
       idx += s;
       slot = s1;
@@ -1073,6 +1107,9 @@ template <class C, class OA, class OB> struct WideStream {
     }
     wait_vm_lgkm0<0>();
     __syncthreads();                      // all loads landed, all waves done with the stages
+    if constexpr (FLOW) {
+      if (pend >= 0) src.signal(pend);
+    }
   }
 };
 

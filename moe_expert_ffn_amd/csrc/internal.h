@@ -27,7 +27,7 @@ struct Sizes {
 };
 
 struct WsLayout {
-  size_t ctr, mt_cnt, mt, seg_cnt, seg, rep_slot, owner_has, bufA, bufO, rslots, bufP, sgate;
+  size_t ctr, mt_cnt, mt, seg_cnt, seg, rep_slot, owner_has, flags, bufA, bufO, rslots, bufP, sgate;
   size_t dq, dqs, zq, zqs;   // fp8 backward: token-axis e4m3 codes and scales of D and dZ
   size_t dhat;               // fp8 backward on the stream kernels: requantized D as bf16
   size_t total;
@@ -73,7 +73,7 @@ struct LayerPtrs {
 int launch_forward(const Sizes& z, const LayerPtrs& L, const void* x, const float* gates,
                    const int32_t* counts, const int32_t* boff, const int32_t* row_to_slot,
                    const int32_t* slot_to_row, const int32_t* block_worker, void* y,
-                   void* z_save, int32_t* status, char* ws, void* const* ev,
+                   void* z_save, int32_t* status, char* ws, int exec_flags, void* const* ev,
                    uint64_t* timeline, hipStream_t st);
 
 int launch_backward(const Sizes& z, const LayerPtrs& L, const void* x, const float* gates,
@@ -81,8 +81,8 @@ int launch_backward(const Sizes& z, const LayerPtrs& L, const void* x, const flo
                     const int32_t* boff, const int32_t* row_to_slot,
                     const int32_t* slot_to_row, const int32_t* owner,
                     const int32_t* block_worker, void* dx, float* dw1, float* dw2,
-                    int32_t* status, char* ws, void* const* ev, uint64_t* timeline,
-                    hipStream_t st);
+                    int32_t* status, char* ws, int exec_flags, void* const* ev,
+                    uint64_t* timeline, hipStream_t st);
 
 int gemm_wg_per_cu();
 

@@ -13,7 +13,7 @@ from . import binding as B
 class LayerRunner:
     def __init__(self, w1, w2, w1_scale=None, w2_scale=None, *, act_dtype, T, k, beta, P, s,
                  owner, lam=12, with_backward=False, save_z=None, quota_umin=None,
-                 gate_rho=None):
+                 gate_rho=None, two_phase=False):
         dev = w1.device
         self.dev = dev
         self.layer = B.make_layer(w1, w2, w1_scale, w2_scale, act_dtype)
@@ -27,6 +27,8 @@ class LayerRunner:
         # per replica (thousandths of a block)
         self.gate_rho = gate_rho
         self.act_dtype = act_dtype
+        # two_phase: FC1 / FC2 (dA / dX) in one two-phase launch instead of two
+        self.two_phase = two_phase
         self.owner = owner.to(device=dev, dtype=torch.int32).contiguous()
         self.with_backward = with_backward
         self.ws = B.workspace(self.layer, T, k, beta, P, s, with_backward, dev)
@@ -64,14 +66,14 @@ class LayerRunner:
     def forward(self, x, gates, topk_ids, block_worker=None, events=None, timeline=None):
         bw = self.plan_f["block_worker"] if block_worker is None else block_worker
         B.forward(self.layer, x, gates, topk_ids, self.beta, self.P, self.rs, bw, self.y, self.z,
-                  self.ws, self.status, events, timeline)
+                  self.ws, self.status, events, timeline, self.two_phase)
         return self.y
 
     def backward(self, x, gates, dy, topk_ids, block_worker=None, events=None, timeline=None):
         bw = self.plan_b["block_worker"] if block_worker is None else block_worker
         B.backward(self.layer, x, gates, dy, self.z, topk_ids, self.beta, self.P, self.s, self.rs,
                    self.owner, bw, self.dx, self.dw1, self.dw2, self.ws, self.status, events,
-                   timeline)
+                   timeline, self.two_phase)
         return self.dx, self.dw1, self.dw2
 
     def step(self, x, gates, topk_ids, dy=None, s=None, timeline=None):

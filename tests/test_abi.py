@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = B.load()
-    assert lib.moe_abi_version() == B.ABI_VERSION == 3
+    assert lib.moe_abi_version() == B.ABI_VERSION == 4
     assert lib.moe_status_str(0) == b"ok"
     assert b"workspace" in lib.moe_status_str(-3)
 
@@ -66,10 +66,10 @@ def test_operands_of_2gib_or_more_rejected():
     assert lib.moe_workspace_size(ctypes.byref(L), T, 2, 16, 4, 1, 1) == 0
     # 2^19 tokens, top-2: token rows 256 MiB, slot buffers about 512 MiB each
     assert lib.moe_workspace_size(ctypes.byref(L), 1 << 19, 2, 16, 4, 1, 1) > 0
-    assert lib.moe_forward(ctypes.byref(L), P, P, P, T, 2, 16, 4, *([P] * 8), P, 1 << 30,
+    assert lib.moe_forward(ctypes.byref(L), P, P, P, T, 2, 16, 4, *([P] * 8), P, 1 << 30, 0,
                            None, None, None) == B.MOE_ERR_UNSUPPORTED
     assert lib.moe_backward(ctypes.byref(L), P, P, P, P, P, T, 2, 16, 4, 1, *([P] * 10), P,
-                            1 << 30, None, None, None) == B.MOE_ERR_UNSUPPORTED
+                            1 << 30, 0, None, None, None) == B.MOE_ERR_UNSUPPORTED
     # one expert's weights: 2 d_ff d fp32 elements must stay below 2 GiB
     wide = _layer(d=16384, dff=16384)
     assert lib.moe_workspace_size(ctypes.byref(wide), 16, 2, 16, 4, 1, 0) == 0
@@ -118,19 +118,19 @@ def test_host_validation_errors():
     assert lib.moe_predict_cost(*([P] * 4), None, 8, 128, 4, 256, 256, 256, P, P, None) == B.MOE_ERR_ARG
     # forward / backward layer checks
     bad_d = _layer(d=96)
-    assert lib.moe_forward(ctypes.byref(bad_d), P, P, P, 4, 2, 16, 4, *([P] * 8), P, 1 << 30,
+    assert lib.moe_forward(ctypes.byref(bad_d), P, P, P, 4, 2, 16, 4, *([P] * 8), P, 1 << 30, 0,
                            None, None, None) == B.MOE_ERR_UNSUPPORTED
     mixed = _layer(act=B.MOE_F32, w=B.MOE_BF16)
-    assert lib.moe_forward(ctypes.byref(mixed), P, P, P, 4, 2, 16, 4, *([P] * 8), P, 1 << 30,
+    assert lib.moe_forward(ctypes.byref(mixed), P, P, P, 4, 2, 16, 4, *([P] * 8), P, 1 << 30, 0,
                            None, None, None) == B.MOE_ERR_UNSUPPORTED
     fp8 = B.Layer(8, 128, 128, B.MOE_BF16, B.MOE_FP8_E4M3, 16, 32, 64, 64)
     # fp8 weights have a backward (token-axis requantization): the call gets past
     # the layer checks and stops at a workspace too small for the e4m3 buffers
     assert lib.moe_backward(ctypes.byref(fp8), P, P, P, P, P, 4, 2, 16, 4, 1, *([P] * 10), P,
-                            16, None, None, None) == B.MOE_ERR_WORKSPACE
+                            16, 0, None, None, None) == B.MOE_ERR_WORKSPACE
     nofp8 = B.Layer(8, 128, 192, B.MOE_BF16, B.MOE_FP8_E4M3, 16, 32, 64, 64)   # d_ff % 128
     assert lib.moe_backward(ctypes.byref(nofp8), P, P, P, P, P, 4, 2, 16, 4, 1, *([P] * 10), P,
-                            1 << 30, None, None, None) == B.MOE_ERR_UNSUPPORTED
+                            1 << 30, 0, None, None, None) == B.MOE_ERR_UNSUPPORTED
     # token-axis quantization: shapes and pointers are checked on the host
     # (src, ld, src_rows, row_map, gather, row_div, row_scale, rows, cols, block_rows, codes,
     #  scales, stream)
@@ -149,10 +149,15 @@ def test_host_validation_errors():
     big = 65535 * 128 + 8                                                            # > 65535 column tiles
     assert q(P, big, 4, None, 0, 1, None, 4, big, 128, P, P, None) == B.MOE_ERR_ARG
     ok = _layer()
-    assert lib.moe_forward(ctypes.byref(ok), P, P, P, 4, 2, 16, 4, *([P] * 8), P, 16, None,
+    assert lib.moe_forward(ctypes.byref(ok), P, P, P, 4, 2, 16, 4, *([P] * 8), P, 16, 0, None,
                            None, None) == B.MOE_ERR_WORKSPACE
-    assert lib.moe_forward(ctypes.byref(ok), P, P, P, 4, 2, 16, 5, *([P] * 8), P, 1 << 30, None,
+    assert lib.moe_forward(ctypes.byref(ok), P, P, P, 4, 2, 16, 5, *([P] * 8), P, 1 << 30, 0, None,
                            None, None) == B.MOE_ERR_UNSUPPORTED
+    # exec_flags other than MOE_EXEC_TWO_PHASE
+    assert lib.moe_forward(ctypes.byref(ok), P, P, P, 4, 2, 16, 4, *([P] * 8), P, 1 << 30, 2, None,
+                           None, None) == B.MOE_ERR_ARG
+    assert lib.moe_backward(ctypes.byref(ok), P, P, P, P, P, 4, 2, 16, 4, 1, *([P] * 10), P,
+                            1 << 30, 4, None, None, None) == B.MOE_ERR_ARG
 
 
 def test_quantizer_binding_checks_buffers():

@@ -44,8 +44,12 @@ def test_kernel_model_reduce_entry_only_with_bytes():
     # every replica adds one fp32 partial (3 d d_ff values) to the weight-gradient writes
     assert m1["bwd.dW"][1] - m0["bwd.dW"][1] == 3 * (3 * w.d * w.d_ff * 4)
     # the useful flops of the five contractions add up to 18 d d_ff per routed row
-    fl = sum(v[0] for v in m1.values())
+    # (the two-phase launches' entries are sums of two of them)
+    fl = sum(v[0] for k, v in m1.items() if "+" not in k)
     assert fl == 18 * w.d * w.d_ff * R
+    for a, b in (("fwd.fc1", "fwd.fc2"), ("bwd.dA", "bwd.dX")):
+        both = m1[a + "+" + b.split(".")[1]]
+        assert both == (m1[a][0] + m1[b][0], m1[a][1] + m1[b][1])
 
 
 def test_worker_spread_from_a_hand_timeline():
