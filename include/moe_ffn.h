@@ -257,9 +257,12 @@ int moe_predict_cost(const int32_t* counts, const int32_t* block_offsets,
  *   y [T][d] act dtype.
  *   z_save (nullable) [moe_max_slots][2*d_ff] act dtype: receives [G, U] of
  *     every routed row, as needed by moe_backward.
+ *   exec_flags: 0, or MOE_EXEC_TWO_PHASE (FC1 and FC2 in one launch).
  *   stage_events (host, nullable): 5 hipEvent_t recorded on `stream` at
- *     start / after scheduling / after FC1 / after FC2 / after combine.
- *   timeline (nullable): phases MOE_TL_FC1 and MOE_TL_FC2 (see above).
+ *     start / after scheduling / after FC1 / after FC2 / after combine (with
+ *     MOE_EXEC_TWO_PHASE the FC1 and FC2 events follow the one launch).
+ *   timeline (nullable): phases MOE_TL_FC1 and MOE_TL_FC2 (see above; in
+ *     the two-phase launch a workgroup's FC1 ends where its FC2 starts).
  * Errors: MOE_ERR_ARG for an invalid layer, size or null pointer;
  *   MOE_ERR_UNSUPPORTED for E > 512, P outside {1,2,4,8}, d not a multiple
  *   of 128, d_ff not a multiple of 64 (128 with e4m3 weights), a dtype pair
@@ -289,9 +292,11 @@ int moe_forward(const moe_layer* L, const void* x, const float* gates,
  * ascending worker order, in fp32 (early fixed-order owner reduction).
  *   dy [T][d], z_save from moe_forward on the same routing, owner [E] = h(e);
  *   dx [T][d] act dtype; dw1 [E][2*d_ff][d] fp32; dw2 [E][d][d_ff] fp32.
+ *   exec_flags: 0, or MOE_EXEC_TWO_PHASE (dA and dX in one launch).
  *   stage_events (host, nullable): 7 events: start / after scheduling /
  *     after dA / after dX / after dx combine / after weight gradients /
- *     after replica reduction.
+ *     after replica reduction (with MOE_EXEC_TWO_PHASE the dA and dX events
+ *     follow the one launch).
  *   timeline (nullable): phases MOE_TL_DA, MOE_TL_DX and MOE_TL_DW.
  * fp8 weights (MegaFlux summary, "Backward": overlapped token-axis
  * requantization of D_e and dZ_e): dA, dZ and dx use D and the weights as
