@@ -1002,6 +1002,10 @@ struct MSrcBase {
     first = w.j;
     stride = w.n;
   }
+  // this wave's rows of the tile include routed rows
+  MOE_DEV bool wave_active(const MItem& it) const {
+    return (wave_id() / WC::WAVES_N) * WC::WM < it.nrows;
+  }
   // scalar load: nothing waits on vector loads in flight
   MOE_DEV MItem load(int idx) const {
     const u32x4_t m = ((const MOE_CONST u32x4_t*)a.mt)[(size_t)r * a.max_mt + idx / nnt];
@@ -1061,6 +1065,7 @@ using RowF8 = RowKFp8<256, kWNW, kRowBK>;
 // COH: A is stored with device-scope completion, read by FC2 items of the
 // same launch (the saved [G, U] is only read by later launches).
 template <bool FP8, bool COH = false> struct SrcFc1T : MSrcBase {
+  static constexpr bool kSkipIdle = true;
   using Item = MItem;
   using OB = typename std::conditional<FP8, RowF8, RowW>::type;
   MOE_DEV void fill(const Item& it, int slot) const { fill_rows(it, slot); }
@@ -1129,6 +1134,7 @@ template <bool FP8, bool COH = false> struct SrcFc1T : MSrcBase {
 // FC2 with the gate: O[slot] = p * A W2^T.  With e4m3 weights a wave's 64
 // rows nj * 256 + 64 wn .. +63 lie in scale block 2 nj + wn / 2.
 template <bool FP8> struct SrcFc2T : MSrcBase {
+  static constexpr bool kSkipIdle = true;
   using Item = MItem;
   using OB = typename std::conditional<FP8, RowF8, RowW>::type;
   MOE_DEV void fill(const Item& it, int slot) const { fill_gates(it, slot); }
@@ -1283,6 +1289,7 @@ template <bool FP8, bool COH = false> struct SrcDaT : MSrcBase {
 
 // dX per routed row: dZ W1 (W1 [2 d_ff][d] read K-major through transpose reads).
 template <bool FP8> struct SrcDxT : MSrcBase {
+  static constexpr bool kSkipIdle = true;
   using Item = MItem;
   using OB = typename std::conditional<FP8, MnF8Op, MnFixedOp>::type;
   MOE_DEV void fill(const Item&, int) const {}
@@ -1343,6 +1350,8 @@ struct PItem : MItem { int m; };
 constexpr uint64_t kFlowWaitTicks = 200000000ull;   // the 100 MHz real-time counter
 template <class Src> struct FlowBase : Src {
   static constexpr bool kFlow = true;
+  // the idle-wave branches push the merged kernels over the register file
+  static constexpr bool kSkipIdle = false;
   using Item = PItem;
   MOE_DEV Item load(int idx) const {
     const int m = idx / this->nnt;

@@ -705,6 +705,13 @@ template <class T> struct op_fp8<T, decltype((void)T::kFp8)> { static constexpr 
 // signal(key) publishes it once the item's stores are complete.
 template <class T, class = void> struct src_flow { static constexpr bool value = false; };
 template <class T> struct src_flow<T, decltype((void)T::kFlow)> { static constexpr bool value = T::kFlow; };
+// A source whose items may leave whole waves without rows (kSkipIdle):
+// wave_active(it) is false for a wave whose M range lies past the item's
+// rows; that wave then skips its fragment reads and MFMAs (its accumulators
+// stay zero, which is what those rows would hold) but still loads its share
+// of each stage.
+template <class T, class = void> struct src_skip_idle { static constexpr bool value = false; };
+template <class T> struct src_skip_idle<T, decltype((void)T::kSkipIdle)> { static constexpr bool value = T::kSkipIdle; };
 
 // MN-contiguous operand: BK K rows x MN elements per stage, [k][MN], fragments
 // through ds_read_b64_tr_b16: inside each 16-lane group, lane j supplies the
@@ -1000,7 +1007,10 @@ template <class C, class OA, class OB> struct WideStream {
     }
     wait_vm_lgkm0<(S - 1) * LPS>();
     __builtin_amdgcn_s_barrier();
-    read<0, 0>(smem);
+    constexpr bool SKIP = src_skip_idle<Src>::value;
+    bool act = true;                             // this wave has rows in item it0
+    if constexpr (SKIP) act = src.wave_active(it0);
+    if (act) read<0, 0>(smem);
     int g = 0;                                   // global step index: stage g % S
     while (true) {
       const int s1 = slot == 2 ? 0 : slot + 1, s2 = s1 == 2 ? 0 : s1 + 1;
@@ -1018,7 +1028,8 @@ template <class C, class OA, class OB> struct WideStream {
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
       // the item's first step landed before the previous item's last barrier
-      if (g > 0) read<0, 0>(smem + (g & (S - 1)) * STAGE);
+      if constexpr (SKIP) act = src.wave_active(it0);
+      if (g > 0 && act) read<0, 0>(smem + (g & (S - 1)) * STAGE);
       // During its first S-1 steps, the loads an item waits for were issued
       // before the previous item's epilogue, so the epilogue's stores (and
       // loads) may stay in flight: they drain under those steps.
@@ -1030,7 +1041,7 @@ template <class C, class OA, class OB> struct WideStream {
           for (int j = 0; j < C::NB; ++j) bs[j] = bsn[j];
         }
         lgkm0();
-        read<1, 1>(st);
+        if (act) read<1, 1>(st);
         // step g + S of the stream: this item, the next one, or a harmless
         // re-read of this item's last step when the stream ends
         const bool own = kt + S < n0;
@@ -1046,18 +1057,18 @@ template <class C, class OA, class OB> struct WideStream {
             bsn[j] = kt + 1 < n0 ? b0.scale(j, kt + 1) : h1 ? b1.scale(j, 0) : bs[j];
         }
         __builtin_amdgcn_sched_barrier(0);
-        mma<0>(acc);
+        if (act) mma<0>(acc);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (NCH == 4) {
           lgkm0();
-          read<2, 0>(st);
+          if (act) read<2, 0>(st);
           __builtin_amdgcn_sched_barrier(0);
-          mma<1>(acc);
+          if (act) mma<1>(acc);
           __builtin_amdgcn_sched_barrier(0);
           lgkm0();
-          read<3, 1>(st);
+          if (act) read<3, 1>(st);
           __builtin_amdgcn_sched_barrier(0);
-          mma<0>(acc);
+          if (act) mma<0>(acc);
           __builtin_amdgcn_sched_barrier(0);
         }
         const bool strict = !(relax && kt < S - 1);
@@ -1086,9 +1097,9 @@ template <class C, class OA, class OB> struct WideStream {
         }
         // chunk 0 of the next step; for the next item it is read after the
         // epilogue, so its fragments are not live across it
-        if (kt + 1 < n0) read<0, 0>(smem + ((g + 1) & (S - 1)) * STAGE);
+        if (kt + 1 < n0 && act) read<0, 0>(smem + ((g + 1) & (S - 1)) * STAGE);
         __builtin_amdgcn_sched_barrier(0);
-        mma<1>(acc);
+        if (act) mma<1>(acc);
         __builtin_amdgcn_sched_barrier(0);
       }
       src.epilogue(it0, slot, acc);
