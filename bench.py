@@ -229,7 +229,7 @@ def reduce_bytes(case, w):
 # HBM traffic of the dominant kernel from rocprofv3 counters (FETCH_SIZE and
 # WRITE_SIZE per dispatch, scaled by the reading of a plain copy kernel of
 # known size), valid only for the kernel sources it was measured on.
-PROFILED_TRAFFIC = {"kernel": "bwd.dW", "source": "39dea7cba4a693e6", "bytes": 3367087412,
+PROFILED_TRAFFIC = {"kernel": "bwd.dW", "source": "dc33a1b94f62e62c", "bytes": 3362717899,
                     "summary": "profiles/k_stream_SrcDwT_qwen3_bf16_fwdbwd_hbm_traffic.md"}
 
 

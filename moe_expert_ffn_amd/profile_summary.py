@@ -3,6 +3,7 @@
   python -m moe_expert_ffn_amd.profile_summary stats  <kernel_stats.csv>
   python -m moe_expert_ffn_amd.profile_summary traffic <fetch.csv> <write.csv> \
         <copy_fetch.csv> <copy_write.csv> <copy_bytes> <kernel>
+  python -m moe_expert_ffn_amd.profile_summary mfma <counter_collection.csv>
 
 `stats` prints a markdown table of the library's kernels (calls, average and
 total duration).  Kernel names are shortened to k_stream<SrcX> for the
@@ -11,7 +12,9 @@ persistent GEMM kernels (SrcX names the stage) and to the bare name otherwise;
 WRITE_SIZE per dispatch (KiB), the calibration of both counters against a
 plain elementwise copy of `copy_bytes` bytes read and written (the copy's own
 dispatch is the one with the largest reading), and the calibrated HBM bytes
-per dispatch.
+per dispatch.  `mfma` takes a `--pmc MfmaUtil MfmaFlopsBF16` run and prints,
+per GEMM kernel, the mean MfmaUtil, the executed bf16 MFMA work and the
+dispatch duration (its own timestamps; counter runs serialise dispatches).
 """
 from __future__ import annotations
 
@@ -25,6 +28,9 @@ STAGE_OF = {"k_stream<SrcFc1>": "fwd.fc1", "k_stream<SrcFc2>": "fwd.fc2",
             "k_stream<SrcDaFp8>": "bwd.dA", "k_stream<SrcDxFp8>": "bwd.dX",
             "k_quant_tok": "bwd.dA (D) + bwd.dW (dZ)",
             "k_stream<SrcDa>": "bwd.dA", "k_stream<SrcDx>": "bwd.dX", "k_stream<SrcDwT>": "bwd.dW",
+            "k_stream<SrcDwTFp8>": "bwd.dW",
+            "k_stream2<Fc1+Fc2>": "fwd.fc1+fc2", "k_stream2<Fc1+Fc2Fp8>": "fwd.fc1+fc2",
+            "k_stream2<Da+Dx>": "bwd.dA+dX", "k_stream2<Da+DxFp8>": "bwd.dA+dX",
             "k_fc1": "fwd.fc1", "k_fc2": "fwd.fc2", "k_bwd_da": "bwd.dA", "k_bwd_dx": "bwd.dX",
             "k_bwd_dw": "bwd.dW", "k_bwd_reduce": "bwd.reduce",
             "k_combine": "fwd.combine + bwd.combine", "k_sched": "fwd.sched + bwd.sched",
@@ -33,10 +39,20 @@ STAGE_OF = {"k_stream<SrcFc1>": "fwd.fc1", "k_stream<SrcFc2>": "fwd.fc2",
 
 
 def short(name: str) -> str:
-    """k_stream<SrcX> for the persistent GEMM kernels, the bare kernel name otherwise."""
-    m = re.search(r"k_stream<moe::(\w+?)(T<(true|false)>)?[,<>]", name)
+    """k_stream<SrcX> for the persistent GEMM kernels (SrcXFp8 with e4m3
+    weights), k_stream2<X+Y> for a two-phase launch, the bare kernel name
+    otherwise."""
+    fp8 = lambda b: "Fp8" if b == "true" else ""
+    m = re.search(r"k_stream2<moe::FlowProducer<moe::Src(\w+?)T<(true|false)\b.*?"
+                  r"FlowConsumer<moe::Src(\w+?)T<", name)
     if m:
-        return f"k_stream<{m.group(1)}{'Fp8' if m.group(3) == 'true' else ''}>"
+        return f"k_stream2<{m.group(1)}+{m.group(3)}{fp8(m.group(2))}>"
+    m = re.search(r"k_stream<moe::SrcDwT<moe::GemmCfg<[^>]*>, (true|false)>", name)
+    if m:
+        return f"k_stream<SrcDwT{fp8(m.group(1))}>"
+    m = re.search(r"k_stream<moe::Src(\w+?)T<(true|false)\b", name)
+    if m:
+        return f"k_stream<Src{m.group(1)}{fp8(m.group(2))}>"
     m = re.search(r"moe::(\w+)", name)
     return m.group(1) if m else name[:60]
 
@@ -58,6 +74,32 @@ def per_kernel(path: str):
     for r in csv.DictReader(open(path)):
         agg[short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
     return agg
+
+
+PEAK_BF16_TFLOPS = 2516.6
+
+
+def mfma(path: str) -> str:
+    util, flops, dur = (collections.defaultdict(list) for _ in range(3))
+    for r in csv.DictReader(open(path)):
+        if "moe::" not in r["Kernel_Name"]:
+            continue
+        k = short(r["Kernel_Name"])
+        if r["Counter_Name"] == "MfmaUtil":
+            util[k].append(float(r["Counter_Value"]))
+            dur[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        elif r["Counter_Name"] == "MfmaFlopsBF16":
+            flops[k].append(float(r["Counter_Value"]))
+    out = ["| kernel | dispatches | MfmaUtil % | executed bf16 MFMA GFLOP / launch | us / launch "
+           "| TFLOP/s | % of 2,516.6 TFLOP/s |", "|---|---|---|---|---|---|---|"]
+    for k in sorted(util, key=lambda k: -sum(dur[k]) / len(dur[k])):
+        if not flops.get(k) or sum(flops[k]) == 0:
+            continue
+        u, f, t = (sum(v) / len(v) for v in (util[k], flops[k], dur[k]))
+        tf = f / (t * 1e-6) / 1e12
+        out.append(f"| {k} | {len(util[k])} | {u:.1f} | {f / 1e9:.1f} | {t:.1f} | {tf:.1f} | "
+                   f"{100 * tf / PEAK_BF16_TFLOPS:.1f} |")
+    return "\n".join(out)
 
 
 def copy_reading(path: str) -> float:
@@ -85,6 +127,8 @@ def main(argv):
         print(stats(argv[2]))
     elif argv[1] == "traffic":
         print(traffic(argv[2], argv[3], argv[4], argv[5], int(argv[6]), argv[7]))
+    elif argv[1] == "mfma":
+        print(mfma(argv[2]))
     else:
         raise SystemExit(__doc__)
 
