@@ -90,14 +90,20 @@ def test_backward_full_size_sampled(kappa):
     counts = np.bincount(c.ids_np[c.ids_np >= 0], minlength=w.E)
     hot = int(np.argmax(counts))
     replicated = [e for e in range(w.E) if (q[e] > 0).sum() > 1]
-    experts = sorted({hot, *(replicated[:1]), 5})
+    # also the expert with the fewest rows: the shortest weight-gradient
+    # segment, whose last K step is mostly padding; each expert is checked on
+    # its own so that a small one is not hidden in a large one's norm
+    held = [e for e in range(w.E) if counts[e] > 0]
+    cold = min(held, key=lambda e: (counts[e], e))
+    experts = sorted({hot, *(replicated[:1]), 5, cold})
     rng = np.random.default_rng(kappa)
     tok = np.sort(rng.choice(c.T, size=32, replace=False))
     o = _oracle(c, tokens=tok, experts=experts)
     e_dx = rel_l2(dx[tok].double().cpu().numpy(), o["dx"])
-    e_w1 = rel_l2(dw1[experts].double().cpu().numpy(), np.stack([o["dw1"][e] for e in experts]))
-    e_w2 = rel_l2(dw2[experts].double().cpu().numpy(), np.stack([o["dw2"][e] for e in experts]))
-    say(f"  experts={experts} replicated={len(replicated)} dx={e_dx:.3e} dw1={e_w1:.3e} dw2={e_w2:.3e}")
+    e_w1 = max(rel_l2(dw1[e].double().cpu().numpy(), o["dw1"][e]) for e in experts)
+    e_w2 = max(rel_l2(dw2[e].double().cpu().numpy(), o["dw2"][e]) for e in experts)
+    say(f"  experts={experts} rows={counts[experts].tolist()} replicated={len(replicated)} "
+        f"dx={e_dx:.3e} dw1={e_w1:.3e} dw2={e_w2:.3e}")
     assert max(e_dx, e_w1, e_w2) <= 2e-2
 
 

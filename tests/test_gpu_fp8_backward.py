@@ -123,11 +123,15 @@ def _run(c, s=None):
 
 
 def _errs(dx, dw1, dw2, o, tokens=None, experts=None):
+    """rel-L2 of dx (the tokens given) and the worst expert's dW1 and dW2, each
+    expert on its own so that a small one is not hidden in a large one's norm
+    (for an expert without rows, rel_l2 is the absolute norm of the output)."""
     ex = range(dw1.shape[0]) if experts is None else experts
     dxs = dx if tokens is None else dx[tokens]
-    return (rel_l2(dxs.double().cpu().numpy(), o["dx"]),
-            rel_l2(dw1[list(ex)].double().cpu().numpy(), np.stack([o["dw1"][e] for e in ex])),
-            rel_l2(dw2[list(ex)].double().cpu().numpy(), np.stack([o["dw2"][e] for e in ex])))
+
+    def worst(dw, ref):
+        return max(rel_l2(dw[e].double().cpu().numpy(), ref[e]) for e in ex)
+    return (rel_l2(dxs.double().cpu().numpy(), o["dx"]), worst(dw1, o["dw1"]), worst(dw2, o["dw2"]))
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -180,9 +184,13 @@ def test_fp8_backward_full_size_sampled(kappa):
     counts = np.bincount(c.ids_np[c.ids_np >= 0], minlength=w.E)
     hot = int(np.argmax(counts))
     replicated = [e for e in range(w.E) if (q[e] > 0).sum() > 1 and e != hot]
-    experts = sorted({hot, *(replicated[:1])})
+    # the hottest expert, one replicated expert when the plan has one, and the
+    # expert with the fewest rows (the shortest weight-gradient segment)
+    held = [e for e in range(w.E) if counts[e] > 0]
+    cold = min(held, key=lambda e: (counts[e], e))
+    experts = sorted({hot, *(replicated[:1]), cold})
     rng = np.random.default_rng(kappa)
-    tok = np.sort(rng.choice(c.T, size=16, replace=False))
+    tok = np.sort(rng.choice(c.T, size=32, replace=False))
     x, w1, w2, ids, gates = c.oracle_inputs()
     o = offn.backward_fp8(x, w1, w2, ids, gates, c.dy.double().cpu().numpy(), w.beta,
                           tokens=tok, experts=experts)
