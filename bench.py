@@ -12,9 +12,10 @@ Prints one JSON line.  `value` is useful TFLOP/s: (6 + 12) * d * d_ff * R per
 step (R = routed rows; padding rows, SwiGLU, combine not counted), divided by
 the measured step time.  The same line carries `kappa_sweep`: every skew level
 of the workload (kappa 1, 4, 8 for the fwd+bwd layer) under fixed placement
-(s = 0), the pages' planner (lambda = 12) and the planner with lambda = 1 (the
-measured price of a replica on one GPU), in ms and useful TFLOP/s, and the
-latency ratio kappa=8 / kappa=1 of each arm (`skew`).
+(s = 0), the pages' planner (lambda = 12), the planner with lambda = 1 (the
+measured price of a replica on one GPU) and the quota planner, in ms and
+useful TFLOP/s, and the latency ratio kappa=8 / kappa=1 of each arm (`skew`);
+and `two_phase`: the same steps with FC1+FC2 and dA+dX in one launch each.
 """
 from __future__ import annotations
 
@@ -302,7 +303,11 @@ def compare_planners(case, w, n=50):
     return out
 
 
-SWEEP_ARMS = (("fixed", True, 12), ("planned", False, 12), ("planned-lambda1", False, 1))
+# (name, fixed placement, lambda, quota floor u_min or None): the pages'
+# bounded greedy at its lambda = 12 and at lambda = 1 (a replica's price on one
+# GPU), and the quota planner (every plan, forward and backward)
+SWEEP_ARMS = (("fixed", True, 12, None), ("planned", False, 12, None),
+              ("planned-lambda1", False, 1, None), ("planned-quota", False, 12, 1))
 TL_NAMES = ("fc1", "fc2", "dA", "dX", "dW")
 
 
@@ -357,14 +362,15 @@ def kappa_sweep(w, dev, lay, steps, warmup=3):
         routing = make_routing(w, kap)
         R = int((routing[0] >= 0).sum())
         useful = (f_fwd + (f_bwd if w.backward else 0)) * R
-        for arm, fixed, lam in SWEEP_ARMS:
-            c = build_case(w, kap, fixed, dev, lam=lam, lay=lay, routing=routing)
+        for arm, fixed, lam, umin in SWEEP_ARMS:
+            c = build_case(w, kap, fixed, dev, lam=lam, lay=lay, routing=routing, quota_umin=umin)
             ms, st = time_steps(c, steps, warmup)
             spread = worker_spread(timeline_step(c), c["runner"].P)
             pf = c["runner"].plan_f["plan_info"].cpu().tolist()
             pb = c["runner"].plan_b["plan_info"].cpu().tolist() if w.backward else None
             rows.append({"kappa": kap, "kappa_realised": round(realised_kappa(routing[0], w.E), 3),
-                         "placement": arm, "lambda": lam, "ms": round(ms, 4),
+                         "placement": arm, "lambda": lam if umin is None else None,
+                         "quota_umin": umin, "ms": round(ms, 4),
                          "tflops": round(useful / (ms * 1e-3) / 1e12, 2),
                          "pct_bf16_peak": round(100 * useful / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
                          "fwd_us": round(sum(v for k_, v in st.items() if k_.startswith("fwd.")) * 1e3, 1),
@@ -376,7 +382,7 @@ def kappa_sweep(w, dev, lay, steps, warmup=3):
             torch.cuda.empty_cache()
     skew = {}
     k_lo, k_hi = min(w.kappas), max(w.kappas)
-    for arm, _, _ in SWEEP_ARMS:
+    for arm, *_ in SWEEP_ARMS:
         t = {r["kappa"]: r["ms"] for r in rows if r["placement"] == arm}
         skew[arm] = round(t[k_hi] / t[k_lo], 4)
     return rows, {"kappa_hi": k_hi, "kappa_lo": k_lo, "ratio": skew}
