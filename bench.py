@@ -230,7 +230,8 @@ def reduce_bytes(case, w):
 # HBM traffic of the dominant kernel from rocprofv3 counters (FETCH_SIZE and
 # WRITE_SIZE per dispatch, scaled by the reading of a plain copy kernel of
 # known size), valid only for the kernel sources it was measured on.
-PROFILED_TRAFFIC = {"kernel": "bwd.dW", "source": "dc33a1b94f62e62c", "bytes": 3362717899,
+PROFILED_TRAFFIC = {"kernel": "bwd.dW", "workload": "qwen3_bf16_fwdbwd", "kappa": 1.0, "fixed": False,
+                    "source": "dc33a1b94f62e62c", "bytes": 3362717899,
                     "summary": "profiles/k_stream_SrcDwT_qwen3_bf16_fwdbwd_hbm_traffic.md"}
 
 
@@ -244,7 +245,7 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def roofline(w, stages, R, T, e_act, replicas, red_bytes=0):
+def roofline(w, stages, R, T, e_act, replicas, red_bytes=0, run=None):
     model = kernel_model(w, R, T, e_act, replicas, red_bytes)
     # every contraction runs on bf16 MFMA (e4m3 weights are widened to bf16
     # between LDS and the matrix cores), so the bf16 peak bounds it
@@ -264,7 +265,9 @@ def roofline(w, stages, R, T, e_act, replicas, red_bytes=0):
     dom = max(rows, key=lambda k: rows[k]["launch_us"])
     r = rows[dom]
     traffic = None
-    if PROFILED_TRAFFIC and PROFILED_TRAFFIC.get("kernel") == dom and \
+    # the counters belong to one kernel on one workload, kappa and placement
+    if PROFILED_TRAFFIC and PROFILED_TRAFFIC.get("kernel") == dom and run is not None and \
+            run == (PROFILED_TRAFFIC["workload"], PROFILED_TRAFFIC["kappa"], PROFILED_TRAFFIC["fixed"]) and \
             PROFILED_TRAFFIC.get("source") == source_hash():
         traffic = PROFILED_TRAFFIC["bytes"]
     out = {"kernel": dom, "bound": r["bound"], "achieved": round(r["achieved"], 2), "peak": r["peak"],
@@ -513,7 +516,8 @@ def main():
     e_act = int((np.bincount(case["ids_np"][case["ids_np"] >= 0].ravel(), minlength=w.E) > 0).sum())
     replicas = int(case["runner"].plan_b["plan_info"][2].item()) if w.backward else 0
     red_bytes = reduce_bytes(case, w) if w.backward else 0
-    roof, per_kernel = roofline(w, stages, R, case["T"], e_act, replicas, red_bytes)
+    roof, per_kernel = roofline(w, stages, R, case["T"], e_act, replicas, red_bytes,
+                                run=(w.name, float(args.kappa), bool(args.fixed)))
     _, per_two = roofline(w, stages_two, R, case["T"], e_act, replicas, red_bytes)
     for k in ("fwd.fc1+fc2", "bwd.dA+dX"):
         if k in per_two:

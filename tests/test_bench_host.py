@@ -60,3 +60,21 @@ def test_worker_spread_from_a_hand_timeline():
     tl[0, :16, 1] = np.where(g % 8 < 4, 200, 400)       # worker 0 ends at +100, worker 1 at +300
     sp = bench.worker_spread(tl, 2)
     assert sp == {"fc1": round(300 / 200, 3)}
+
+
+def test_profiled_traffic_only_for_its_own_workload():
+    """The counter-based traffic figure is reported only for the kernel,
+    workload, kappa and placement it was measured on, and only while the
+    kernel sources are the ones it was measured on."""
+    w = WORKLOADS["qwen3_bf16_fwdbwd"]
+    R, T = 65536, 8192
+    stages = {"bwd.dW": 1.0, "fwd.fc1": 0.4}
+    pt = bench.PROFILED_TRAFFIC
+    own = (pt["workload"], pt["kappa"], pt["fixed"])
+    roof, _ = bench.roofline(w, stages, R, T, w.E, 0, 0, run=own)
+    assert roof["kernel"] == "bwd.dW"
+    assert roof["traffic"] == (pt["bytes"] if pt["source"] == bench.source_hash() else None)
+    for other in (("dsv3_fp8_fwdbwd", 1.0, False), (pt["workload"], 8.0, False),
+                  (pt["workload"], 1.0, True)):
+        assert bench.roofline(w, stages, R, T, w.E, 0, 0, run=other)[0]["traffic"] is None
+    assert bench.roofline(w, stages, R, T, w.E, 0, 0)[0]["traffic"] is None
