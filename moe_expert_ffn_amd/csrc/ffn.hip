@@ -960,9 +960,7 @@ MOE_DEV MOE_LDS char* epi_scratch(MOE_LDS uint16_t* smem) {
 // non-temporal stores keep the 2.4 GB of fp32 tiles of a launch from evicting
 // the operand panels the next tiles of the same segment read from L2 (6% off
 // the kernel on the Qwen3-shaped workload, measured against plain stores).
-MOE_DEV void stg16v(void* p, const u32x4_t& d) {
-  __builtin_nontemporal_store(d, (MOE_GLB u32x4_t*)p);
-}
+MOE_DEV void stg4v(float* p, float v) { __builtin_nontemporal_store(v, (MOE_GLB float*)p); }
 // 16 bytes at element column `col` of slot row `srow` of a [slots][ld] bf16
 // buffer; a row past the tile's end is sent out of range and dropped, so an
 // epilogue issues the same number of stores for every tile
@@ -1420,7 +1418,7 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void k_stream(ExecArgs a, int n
   Src src;
   src.init(a, smem, ntiles_n);
   f32x16_t acc[C::MB][C::NB];
-  WideStream<C, OA, OB> p;
+  WideStream<C, OA, OB, src_rows_in_regs<Src>::value> p;
   p.run(src, smem, acc);
   if (a.timeline) {
     __syncthreads();
@@ -1644,6 +1642,7 @@ struct DwItem { int e, slot0, nrows, dst, is2, mi, nj; };
 // in bufA has been requantized in place.
 template <class C, bool FP8 = false> struct SrcDwT {
   using Item = DwItem;
+  static constexpr bool kRowsInRegs = true;      // the epilogue stores from the accumulators
   using MnC = MnK<C::BN, C::NT / 64, kDwBK>;
   static_assert(C::BM == C::BN, "one MN operand type for both sides");
   static_assert(MnC::RPI == 2, "a load instruction covers the K row pair kb, kb + 1");
@@ -1693,8 +1692,12 @@ template <class C, bool FP8 = false> struct SrcDwT {
   MOE_DEV int steps(const Item& it) const {
     return max(wide_stages(kDwBK), (it.nrows + kDwBK - 1) / kDwBK);
   }
-  // vector memory operations of one epilogue, per wave: all stores
-  static constexpr int kEpiVm = C::MB * C::NB * RowStore<float, 1>::STORES;
+  // vector memory operations of one epilogue, per wave: one store per
+  // accumulator register.  Above 63 the clamp makes the relaxed wait a no-op,
+  // which is still exact: a wave cannot hold more than 63 operations in
+  // flight (issue stalls), so by the time its last store issues, every load
+  // issued before the epilogue has landed.
+  static constexpr int kEpiVm = C::MB * C::NB * 16;
   template <int B> MOE_DEV void relaxed_wait() const { wait_vm_lgkm0<vm_clamp(B + kEpiVm)>(); }
   MOE_DEV void epilogue(const Item& it, int, const f32x16_t (&acc)[C::MB][C::NB]) const {
     const int lane = threadIdx.x & 63;
@@ -1711,15 +1714,19 @@ template <class C, bool FP8 = false> struct SrcDwT {
     }
     out += (size_t)it.mi * C::BM * ldo + (size_t)it.nj * C::BN;
     const int wm = wave_id() / C::WAVES_N, wn = wave_id() % C::WAVES_N;
-    MOE_LDS char* scr = epi_scratch(smem);
+    // Straight from the accumulators (kRowsInRegs): register r of a 32 x 32
+    // block holds row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32, so
+    // one store instruction writes two full 128-byte row pieces, with no LDS
+    // staging.
 #pragma unroll
     for (int i = 0; i < C::MB; ++i)
 #pragma unroll
       for (int j = 0; j < C::NB; ++j) {
-        float* ob = out + (size_t)(wm * C::WM + i * 32) * ldo + wn * C::WN + j * 32;
-        RowStore<float, 1>::run(scr, [&](int, int g, float* v) {
-          for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q];
-        }, [&](int row, int c, const u32x4_t& d) { stg16v(ob + (size_t)row * ldo + c * 4, d); });
+        float* ob = out + (size_t)(wm * C::WM + i * 32 + (lane >> 5) * 4) * ldo + wn * C::WN +
+                    j * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          stg4v(ob + (size_t)((r >> 2) * 8 + (r & 3)) * ldo, acc[i][j][r]);
       }
   }
 };

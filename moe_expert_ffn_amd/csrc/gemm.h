@@ -703,6 +703,10 @@ template <class T> struct op_fp8<T, decltype((void)T::kFp8)> { static constexpr 
 // complete (seen: an earlier peek's value, or a negative number for none),
 // publish_key(it) is what a finished item publishes (-1 for nothing), and
 // signal(key) publishes it once the item's stores are complete.
+template <class T, class = void> struct src_rows_in_regs { static constexpr bool value = false; };
+template <class T> struct src_rows_in_regs<T, decltype((void)T::kRowsInRegs)> {
+  static constexpr bool value = T::kRowsInRegs;
+};
 template <class T, class = void> struct src_flow { static constexpr bool value = false; };
 template <class T> struct src_flow<T, decltype((void)T::kFlow)> { static constexpr bool value = T::kFlow; };
 // A source whose items may leave whole waves without rows (kSkipIdle):
@@ -914,7 +918,13 @@ template <class OP, class F> struct MnKOperand {
 // An e4m3 B operand (kFp8) hands out raw codes and a scale per 32-row block
 // and K step; the stream loads the next step's scales one step ahead and
 // widens the codes to bf16 in mma().
-template <class C, class OA, class OB> struct WideStream {
+// Accumulator layout of the 32 x 32 blocks.  By default the B fragment is the
+// MFMA's first operand, so lane % 32 indexes the tile row (M) and register r
+// with lane / 32 the column: 8 (r / 4) + 4 (lane / 32) + r % 4.  With
+// ROWS_IN_REGS the A fragment goes first and the roles swap: register r with
+// lane / 32 gives the row and lane % 32 the column, so one store instruction
+// per register writes 32 consecutive elements of a row (two rows per wave).
+template <class C, class OA, class OB, bool ROWS_IN_REGS = false> struct WideStream {
   static constexpr int BK = OA::BK;
   static_assert(OB::BK == BK, "one K step for both operands");
   static constexpr int S = wide_stages(BK), NCH = BK / 16;
@@ -950,6 +960,12 @@ template <class C, class OA, class OB> struct WideStream {
         for (int i = 0; i < C::MB; ++i)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bj, a[SB][i], acc[i][j], 0, 0, 0);
       }
+    } else if constexpr (ROWS_IN_REGS) {
+#pragma unroll
+      for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[SB][i], b[SB][j], acc[i][j], 0, 0, 0);
     } else {
 #pragma unroll
       for (int i = 0; i < C::MB; ++i)
