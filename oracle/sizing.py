@@ -124,3 +124,84 @@ def predicted_cost(counts, bw_fwd, bw_bwd, owner, beta, P, d, d_ff, G=256, bm=25
 def select_partition(costs: dict) -> int:
     """P of smallest predicted cost; ties go to the larger P."""
     return min(costs, key=lambda p: (costs[p], -p))
+
+
+# ---------------------------------------------------------------------------
+# Producer/consumer split of a two-phase launch.
+#
+# The same page selects, besides the partition, how many CTAs of a
+# dependency-coupled pipeline produce and how many consume, from routed-tile
+# counts and split-level readiness, with no candidate run.  Here the pipeline
+# is one direction's pair of GEMM phases in one persistent launch: FC1 -> FC2
+# (forward) or dA -> dX (backward); the second phase's item of row tile t
+# needs every first-phase item of row tile t.  On each worker (n = G / P
+# workgroups, per-worker row tiles T_r as above, items tile-major: item i of a
+# phase belongs to row tile i // nnt) the modes are:
+# * mode -1, two launches: the second phase starts once the first has ended
+#   everywhere: max_r ceil(T_r nnt1 / n) c1 + max_r ceil(T_r nnt2 / n) c2;
+# * mode 0, temporal: workgroup j runs first-phase items j, j + n, ... and then
+#   second-phase items j, j + n, ...; a second-phase item starts when the
+#   workgroup is free and its row tile is ready;
+# * mode n1 (1 <= n1 < n), spatial: workgroups j < n1 deal the first-phase
+#   items among themselves, the other n - n1 deal the second-phase items;
+#   a consumer's item starts when it is free and its row tile is ready.
+# A first-phase item i dealt over m workgroups ends at (i // m + 1) c1 (all
+# items of a phase cost the same), so row tile t is ready at
+# ((t nnt1 + nnt1 - 1) // m + 1) c1.  The mode's time is the latest
+# workgroup over all workers; the selector takes the smallest, ties to the
+# lower mode (two launches first).
+# ---------------------------------------------------------------------------
+def _ready(t: int, nnt1: int, m: int, c1: int) -> int:
+    return ((t * nnt1 + nnt1 - 1) // m + 1) * c1
+
+
+def _consume(items: range, nnt2: int, c2: int, start: int, ready) -> int:
+    clock = start
+    for i2 in items:
+        clock = max(clock, ready(i2 // nnt2)) + c2
+    return clock
+
+
+def pair_cost(T, n, mode, nnt1, nnt2, c1, c2) -> int:
+    """Predicted time of one direction's phase pair under `mode`."""
+    if mode == -1:
+        m1 = max((t * nnt1 + n - 1) // n for t in T)
+        m2 = max((t * nnt2 + n - 1) // n for t in T)
+        return m1 * c1 + m2 * c2
+    worst = 0
+    for t_r in T:
+        N1, N2 = t_r * nnt1, t_r * nnt2
+        if mode == 0:
+            rd = lambda t: _ready(t, nnt1, n, c1)
+            for j in range(n):
+                own = len(range(j, N1, n)) * c1
+                worst = max(worst, _consume(range(j, N2, n), nnt2, c2, own, rd))
+        else:
+            n1, n2 = mode, n - mode
+            rd = lambda t: _ready(t, nnt1, n1, c1)
+            worst = max(worst, ((N1 + n1 - 1) // n1) * c1)
+            for j in range(n2):
+                worst = max(worst, _consume(range(j, N2, n2), nnt2, c2, 0, rd))
+    return worst
+
+
+def split_costs(counts, block_worker, beta, P, d, d_ff, backward, G=256, bm=256) -> list:
+    """Predicted times of every mode -1, 0, 1, ..., n - 1 (list index mode + 1)
+    of the forward (backward=False: FC1 -> FC2) or backward (dA -> dX) pair."""
+    n = G // P
+    T = _row_tiles(counts, block_worker, beta, P, bm)
+    if backward:
+        nnt1, nnt2 = d_ff // 256, d // 256
+        c1 = 1000 * (d // 64) + epilogue_milli(bm * 256 * 3 * 2 + bm * 512 * 2)
+        c2 = 1000 * (2 * d_ff // 64) + epilogue_milli(bm * 256 * 2)
+    else:
+        nnt1, nnt2 = 2 * d_ff // 256, d // 256
+        c1 = 1000 * (d // 64) + epilogue_milli(bm * (128 + 256) * 2)
+        c2 = 1000 * (d_ff // 64) + epilogue_milli(bm * 256 * 2)
+    return [pair_cost(T, n, m, nnt1, nnt2, c1, c2) for m in range(-1, n)]
+
+
+def select_split(costs: list) -> int:
+    """Mode of smallest predicted time; ties to the lower mode."""
+    best = min(range(len(costs)), key=lambda i: (costs[i], i))
+    return best - 1
