@@ -66,6 +66,10 @@ def parse():
     ap.add_argument("--size-sweep", action="store_true",
                     help="time every CU partition count P at every kappa next to the "
                          "wave-quantized cost model's prediction, and report the selector's regret")
+    ap.add_argument("--split-sweep", action="store_true",
+                    help="time the two-launch, one-launch and producer/consumer-split modes of "
+                         "the FC1 -> FC2 and dA -> dX pairs at every kappa next to "
+                         "moe_predict_split's prediction, and report its choice's regret")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens of the workload in the CPU oracle sample (0: all)")
@@ -113,6 +117,72 @@ def predicted_cost(case, w, P):
     B.predict_cost(r.rs["counts"], r.rs["block_offsets"], r.plan_f["block_worker"], bw_b, r.owner,
                    w.beta, P, w.d, w.d_ff, cost, r.status)
     return int(cost.item())
+
+
+def predicted_split(case, w, backward):
+    """moe_predict_split of the case's current plan for one direction: the
+    predicted time of every mode (dict mode -> thousandths of a step) and the
+    chosen mode."""
+    import torch
+
+    from moe_expert_ffn_amd import binding as B
+    r = case["runner"]
+    G = B.device_info()["num_cus"]
+    costs = torch.zeros(G // w.P + 1, dtype=torch.int64, device=r.owner.device)
+    choice = torch.zeros(1, dtype=torch.int32, device=r.owner.device)
+    bw = r.plan_b["block_worker"] if backward else r.plan_f["block_worker"]
+    B.predict_split(r.rs["counts"], r.rs["block_offsets"], bw, w.beta, w.P, w.d, w.d_ff, backward,
+                    costs, choice, r.status)
+    c = costs.cpu().tolist()
+    return {m - 1: v for m, v in enumerate(c)}, int(choice.item())
+
+
+def split_sweep(w, dev, lay, steps):
+    """Every kappa: the pair times (FC1 -> FC2, dA -> dX, from the stage
+    events) under two launches (-1), one launch (0) and producer counts n1,
+    each next to its prediction; the model's choice, the measured best and
+    the choice's regret per direction."""
+    import torch
+
+    from moe_expert_ffn_amd import binding as B
+    n = B.device_info()["num_cus"] // w.P
+    rows, regrets = [], []
+    for kap in w.kappas:
+        c = build_case(w, kap, False, dev, lay=lay)
+        r = c["runner"]
+        time_steps(c, 1, 0, with_events=False)                  # route and plan once
+        pred_f, ch_f = predicted_split(c, w, False)
+        pred_b, ch_b = predicted_split(c, w, True) if w.backward else ({}, None)
+        modes = sorted({-1, 0, n // 4, n // 2, (2 * n) // 3, (3 * n) // 4, n - 1, ch_f,
+                        ch_b if ch_b is not None else -1})
+        meas = {}
+        for m in modes:
+            r.two_phase = m >= 0
+            r.split_fwd = r.split_bwd = max(m, 0)
+            ms, st = time_steps(c, steps, 2)
+            fwd = sum(v for k, v in st.items() if k in ("fwd.fc1", "fwd.fc2", "fwd.fc1+fc2"))
+            bwd = sum(v for k, v in st.items() if k in ("bwd.dA", "bwd.dX", "bwd.dA+dX"))
+            meas[m] = (ms, fwd * 1e3, bwd * 1e3)
+        r.two_phase, r.split_fwd, r.split_bwd = False, 0, 0
+        row = {"kappa": kap, "n": n, "chosen_fwd": ch_f, "chosen_bwd": ch_b, "modes": {}}
+        for m, (ms, fu, bu) in meas.items():
+            row["modes"][m] = {"ms": round(ms, 4), "fwd_pair_us": round(fu, 1),
+                               "bwd_pair_us": round(bu, 1),
+                               "pred_fwd_steps": round(pred_f[m] / 1000, 1),
+                               **({"pred_bwd_steps": round(pred_b[m] / 1000, 1)} if pred_b else {})}
+        best_f = min(meas, key=lambda m: meas[m][1])
+        row["best_fwd"] = best_f
+        row["regret_fwd"] = round(meas[ch_f][1] / meas[best_f][1] - 1, 4)
+        regrets.append(row["regret_fwd"])
+        if w.backward:
+            best_b = min(meas, key=lambda m: meas[m][2])
+            row["best_bwd"] = best_b
+            row["regret_bwd"] = round(meas[ch_b][2] / meas[best_b][2] - 1, 4)
+            regrets.append(row["regret_bwd"])
+        rows.append(row)
+        del c
+        torch.cuda.empty_cache()
+    return {"runs": rows, "mean_regret": round(sum(regrets) / len(regrets), 4)}
 
 
 def time_steps(case, steps, warmup, with_events=True):
@@ -623,6 +693,8 @@ def main():
                          "per_P": {p: {"ms": round(v[0], 4), "predicted_steps": round(v[1] / 1000, 1)}
                                    for p, v in per.items()}})
         out["size_sweep"] = {"runs": rows, "mean_regret": round(sum(regrets) / len(regrets), 4)}
+    if args.split_sweep:
+        out["split_sweep"] = split_sweep(w, dev, lay, max(5, args.steps // 2))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case, w, args.cpu_tokens, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum {
   MOE_OK = 0,
@@ -71,6 +71,16 @@ typedef enum {
                                    persistent launch with per-row-tile readiness
                                    counters instead of two launches; the results
                                    are the same bits */
+/* With MOE_EXEC_TWO_PHASE, bits 8..15 of exec_flags split each worker's n
+ * workgroups (n = G / P, G = the launch's workgroups, one per CU) into
+ * producers and consumers: MOE_EXEC_SPLIT(n1), 1 <= n1 < n, lets the first n1
+ * run only the first phase (FC1 or dA), publishing each finished row tile,
+ * and the other n - n1 run only the second phase (FC2 or dX), each item
+ * waiting for its row tile.  0 lets every workgroup run its first-phase items
+ * and then its second-phase items.  moe_predict_split picks the mode from the
+ * plan.  The results are the same bits in every mode. */
+#define MOE_EXEC_SPLIT_SHIFT 8
+#define MOE_EXEC_SPLIT(n1) (((n1) & 0xff) << MOE_EXEC_SPLIT_SHIFT)
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 
@@ -243,6 +253,38 @@ int moe_predict_cost(const int32_t* counts, const int32_t* block_offsets,
                      const int32_t* owner, int E, int beta, int P, int d, int d_ff,
                      int num_workgroups, int64_t* cost_dev, int32_t* status_dev, void* stream);
 
+/* Producer/consumer split of the two-phase launches (same page, abstract:
+ * the count of communication CTAs of a dependency-coupled overlap pipeline,
+ * chosen before the launch from routed-tile counts, residency and split-level
+ * readiness, with no candidate run).  On one GPU the pipeline is a
+ * direction's pair of GEMM phases, FC1 -> FC2 (backward = 0) or dA -> dX
+ * (backward = 1): the second phase's items of a row tile need all of that
+ * row tile's first-phase items.  Predicts, for the plan block_worker, the
+ * time of every mode and picks one:
+ *   mode -1: two launches (exec_flags 0);
+ *   mode 0: one two-phase launch, every workgroup runs its first-phase items
+ *     and then its second-phase items (MOE_EXEC_TWO_PHASE);
+ *   mode n1, 1 <= n1 < n = num_workgroups / P: one launch, n1 producer
+ *     workgroups per worker run the first phase and n - n1 consumers the
+ *     second (MOE_EXEC_TWO_PHASE | MOE_EXEC_SPLIT(n1)).
+ * Model: worker r has T_r row tiles (as moe_predict_cost cuts them); items
+ * are tile-major and dealt round-robin; an item costs its K steps of 64 plus
+ * its epilogue bytes over 214,000; a first-phase item i dealt over m
+ * workgroups ends at (i / m + 1) c1, a row tile is ready when its last
+ * first-phase item ends, and a second-phase item starts when its workgroup is
+ * free and its row tile is ready.  Integers throughout.
+ *   counts [E], block_offsets [E+1]: from moe_route_stats; block_worker
+ *   [sum b]: the direction's plan.  num_workgroups <= 0: the device's CUs.
+ *   costs_dev (int64) [n + 1]: mode m's time at index m + 1, thousandths of a
+ *   step.  choice_dev (int32): the mode of smallest time, ties to the lower
+ *   mode.
+ * Errors: as moe_predict_cost; a worker outside [0, P) sets MOE_DEV_BAD_PLAN
+ *   in *status_dev. */
+int moe_predict_split(const int32_t* counts, const int32_t* block_offsets,
+                      const int32_t* block_worker, int E, int beta, int P, int d, int d_ff,
+                      int num_workgroups, int backward, int64_t* costs_dev, int32_t* choice_dev,
+                      int32_t* status_dev, void* stream);
+
 /* Forward expert layer ("Backward" section, expert-computation equation):
  *   y_t = sum_{j: id_tj >= 0} p_tj * W2_e (SiLU(G) * U),  [G; U] = W1_e x_t,
  * executed over the planned blocks: worker r's CU partition runs the blocks
@@ -257,7 +299,8 @@ int moe_predict_cost(const int32_t* counts, const int32_t* block_offsets,
  *   y [T][d] act dtype.
  *   z_save (nullable) [moe_max_slots][2*d_ff] act dtype: receives [G, U] of
  *     every routed row, as needed by moe_backward.
- *   exec_flags: 0, or MOE_EXEC_TWO_PHASE (FC1 and FC2 in one launch).
+ *   exec_flags: 0, or MOE_EXEC_TWO_PHASE (FC1 and FC2 in one launch), with
+ *     an optional MOE_EXEC_SPLIT(n1) (FC1 producers and FC2 consumers).
  *   stage_events (host, nullable): 5 hipEvent_t recorded on `stream` at
  *     start / after scheduling / after FC1 / after FC2 / after combine (with
  *     MOE_EXEC_TWO_PHASE the FC1 and FC2 events follow the one launch).
@@ -292,7 +335,8 @@ int moe_forward(const moe_layer* L, const void* x, const float* gates,
  * ascending worker order, in fp32 (early fixed-order owner reduction).
  *   dy [T][d], z_save from moe_forward on the same routing, owner [E] = h(e);
  *   dx [T][d] act dtype; dw1 [E][2*d_ff][d] fp32; dw2 [E][d][d_ff] fp32.
- *   exec_flags: 0, or MOE_EXEC_TWO_PHASE (dA and dX in one launch).
+ *   exec_flags: 0, or MOE_EXEC_TWO_PHASE (dA and dX in one launch), with
+ *     an optional MOE_EXEC_SPLIT(n1) (dA producers and dX consumers).
  *   stage_events (host, nullable): 7 events: start / after scheduling /
  *     after dA / after dX / after dx combine / after weight gradients /
  *     after replica reduction (with MOE_EXEC_TWO_PHASE the dA and dX events

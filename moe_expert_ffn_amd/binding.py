@@ -15,19 +15,31 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_ffn.so")
 
-ABI_VERSION = 4                 # MOE_ABI_VERSION of the header these signatures follow
+ABI_VERSION = 5                 # MOE_ABI_VERSION of the header these signatures follow
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 PLAN_FWD, PLAN_BWD, PLAN_QUOTA = 0, 1, 2
 DEV_BAD_EXPERT, DEV_BAD_PLAN, DEV_BAD_OWNER, DEV_WAIT_TIMEOUT = 1, 2, 4, 8
 EXEC_TWO_PHASE = 1              # MOE_EXEC_TWO_PHASE
+EXEC_SPLIT_SHIFT = 8            # MOE_EXEC_SPLIT(n1) = n1 << 8
+
+
+def exec_flags(two_phase=False, split=0):
+    """exec_flags of moe_forward / moe_backward: the two-phase launch and its
+    producer workgroups per worker (0: every workgroup runs both phases)."""
+    split = int(split)
+    if split and not two_phase:
+        raise MoeError("a producer/consumer split needs the two-phase launch")
+    if not 0 <= split <= 0xFF:
+        raise MoeError(f"split={split} outside 0..255")
+    return (EXEC_TWO_PHASE if two_phase else 0) | (split << EXEC_SPLIT_SHIFT)
 TIMELINE_MAX_WG, TL_PHASES = 1024, 5          # MOE_TIMELINE_MAX_WG, MOE_TL_PHASES
 TL_FC1, TL_FC2, TL_DA, TL_DX, TL_DW = range(5)
 
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_max_slots", "moe_max_blocks",
            "moe_workspace_size", "moe_route_stats", "moe_route_stats_noalloc", "moe_plan",
            "moe_plan_gate",
-           "moe_predict_cost", "moe_quantize_token_blocks", "moe_forward",
+           "moe_predict_cost", "moe_predict_split", "moe_quantize_token_blocks", "moe_forward",
            "moe_backward",
            "moe_event_create", "moe_event_destroy", "moe_event_record", "moe_event_elapsed_ms",
            "moe_device_info"]
@@ -77,6 +89,8 @@ def load():
     lib.moe_quantize_token_blocks.argtypes = [_P, _I, _I, _P, _I, _I, _P, _I, _I, _I, _P, _P, _P]
     lib.moe_predict_cost.restype = _I
     lib.moe_predict_cost.argtypes = [_P] * 5 + [_I] * 6 + [_P, _P, _P]
+    lib.moe_predict_split.restype = _I
+    lib.moe_predict_split.argtypes = [_P] * 3 + [_I] * 7 + [_P, _P, _P, _P]
     lib.moe_plan_gate.restype = _I
     lib.moe_plan_gate.argtypes = [_P, _P, _P, _I, _I, _I] + [_P] * 3 + [_I] + [_P] * 2 + [_P]
     lib.moe_forward.restype = _I
@@ -274,6 +288,24 @@ def predict_cost(counts, block_offsets, bw_fwd, bw_bwd, owner, beta, P, d, d_ff,
     return cost
 
 
+def predict_split(counts, block_offsets, block_worker, beta, P, d, d_ff, backward, costs, choice,
+                  status, num_workgroups=0):
+    """Predicted time (int64, thousandths of a K step) of every two-phase mode
+    into costs[m + 1] (m = -1 two launches, 0 one launch, n1 > 0 producer /
+    consumer split) and the chosen mode into choice[0]."""
+    _require_device(counts, block_offsets, block_worker, costs, choice, status)
+    _expect(costs, torch.int64, costs.numel(), "costs")
+    _expect(choice, torch.int32, 1, "choice")
+    G = num_workgroups if num_workgroups > 0 else device_info()["num_cus"]
+    if P > 0 and G % P == 0 and costs.numel() < G // P + 1:
+        raise MoeError(f"costs holds {costs.numel()} entries, the model writes {G // P + 1}")
+    _check(load().moe_predict_split(_ptr(counts), _ptr(block_offsets), _ptr(block_worker),
+                                    counts.numel(), beta, P, d, d_ff, num_workgroups,
+                                    1 if backward else 0, _ptr(costs), _ptr(choice), _ptr(status),
+                                    _stream()))
+    return costs, choice
+
+
 def quantize_token_blocks(src, rows, cols, block_rows, codes, scales, row_map=None, gather=False,
                           row_div=1, row_scale=None, ld=None, src_rows=None):
     """Token-axis e4m3 codes [rows][cols] and scales [ceil(rows/block_rows)][cols].
@@ -345,7 +377,7 @@ def _expect_timeline(timeline):
 
 
 def forward(layer: Layer, x, gates, topk_ids, beta, P, rs, block_worker, y, z_save, ws, status,
-            events=None, timeline=None, two_phase=False):
+            events=None, timeline=None, two_phase=False, split=0):
     _require_device(x, gates, topk_ids, y, z_save, ws, status, block_worker, timeline)
     _expect_timeline(timeline)
     T, k = _ids_shape(topk_ids)
@@ -364,12 +396,12 @@ def forward(layer: Layer, x, gates, topk_ids, beta, P, rs, block_worker, y, z_sa
                               beta, P, _ptr(rs["counts"]), _ptr(rs["block_offsets"]),
                               _ptr(rs["row_to_slot"]), _ptr(rs["slot_to_row"]),
                               _ptr(block_worker), _ptr(y), _ptr(z_save), _ptr(status), wsp, wsn,
-                              EXEC_TWO_PHASE if two_phase else 0, ev, _ptr(timeline),
+                              exec_flags(two_phase, split), ev, _ptr(timeline),
                               _stream()))
 
 
 def backward(layer: Layer, x, gates, dy, z_save, topk_ids, beta, P, s, rs, owner, block_worker,
-             dx, dw1, dw2, ws, status, events=None, timeline=None, two_phase=False):
+             dx, dw1, dw2, ws, status, events=None, timeline=None, two_phase=False, split=0):
     _require_device(x, gates, dy, z_save, topk_ids, owner, block_worker, dx, dw1, dw2, ws, status,
                     timeline)
     _expect_timeline(timeline)
@@ -393,7 +425,7 @@ def backward(layer: Layer, x, gates, dy, z_save, topk_ids, beta, P, s, rs, owner
                                _ptr(rs["block_offsets"]), _ptr(rs["row_to_slot"]),
                                _ptr(rs["slot_to_row"]), _ptr(owner), _ptr(block_worker), _ptr(dx),
                                _ptr(dw1), _ptr(dw2), _ptr(status), wsp, wsn,
-                               EXEC_TWO_PHASE if two_phase else 0, ev, _ptr(timeline),
+                               exec_flags(two_phase, split), ev, _ptr(timeline),
                                _stream()))
 
 

@@ -214,6 +214,35 @@ int moe_predict_cost(const int32_t* counts, const int32_t* block_offsets,
                              (hipStream_t)stream);
 }
 
+int moe_predict_split(const int32_t* counts, const int32_t* block_offsets,
+                      const int32_t* block_worker, int E, int beta, int P, int d, int d_ff,
+                      int num_workgroups, int backward, int64_t* costs_dev, int32_t* choice_dev,
+                      int32_t* status_dev, void* stream) {
+  if (E < 1 || beta < 1 || d < 1 || d_ff < 1) return MOE_ERR_ARG;
+  if (!counts || !block_offsets || !block_worker || !costs_dev || !choice_dev || !status_dev)
+    return MOE_ERR_ARG;
+  if (!valid_P(P) || E > kMaxPlanExperts || d % 256 || d_ff % 256) return MOE_ERR_UNSUPPORTED;
+  int G = num_workgroups;
+  if (G <= 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&G, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  if (G % P || G / P > 256) return MOE_ERR_UNSUPPORTED;
+  return launch_predict_split(counts, block_offsets, block_worker, E, beta, P, d, d_ff, G,
+                              backward ? 1 : 0, (long long*)costs_dev, choice_dev, status_dev,
+                              (hipStream_t)stream);
+}
+
+// known bits only; a producer/consumer split only with the two-phase launch
+// (its upper bound, the workgroups of one worker, is checked at launch)
+static bool exec_flags_ok(int f) {
+  const int split = (f >> MOE_EXEC_SPLIT_SHIFT) & 0xff;
+  if (f & ~(MOE_EXEC_TWO_PHASE | MOE_EXEC_SPLIT(0xff))) return false;
+  return split == 0 || (f & MOE_EXEC_TWO_PHASE);
+}
+
 int moe_forward(const moe_layer* L, const void* x, const float* gates, const int32_t* topk_ids,
                 int T, int k, int beta, int P, const int32_t* counts,
                 const int32_t* block_offsets, const int32_t* row_to_slot,
@@ -222,7 +251,7 @@ int moe_forward(const moe_layer* L, const void* x, const float* gates, const int
                 void* const* stage_events, uint64_t* timeline, void* stream) {
   (void)topk_ids;
   const int lc = check_layer(L, false);
-  if (exec_flags & ~MOE_EXEC_TWO_PHASE) return MOE_ERR_ARG;
+  if (!exec_flags_ok(exec_flags)) return MOE_ERR_ARG;
   if (lc != MOE_OK) return lc;
   if (!sizes_ok(T, k, L->E, beta)) return MOE_ERR_ARG;
   if (!valid_P(P)) return MOE_ERR_UNSUPPORTED;
@@ -247,7 +276,7 @@ int moe_backward(const moe_layer* L, const void* x, const float* gates, const vo
                  void* const* stage_events, uint64_t* timeline, void* stream) {
   (void)topk_ids;
   const int lc = check_layer(L, true);
-  if (exec_flags & ~MOE_EXEC_TWO_PHASE) return MOE_ERR_ARG;
+  if (!exec_flags_ok(exec_flags)) return MOE_ERR_ARG;
   if (lc != MOE_OK) return lc;
   if (!sizes_ok(T, k, L->E, beta) || s < 0) return MOE_ERR_ARG;
   if (!valid_P(P)) return MOE_ERR_UNSUPPORTED;

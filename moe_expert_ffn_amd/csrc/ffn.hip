@@ -1434,27 +1434,43 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void k_stream(ExecArgs a, int n
 
 // The two-phase launch: the P1 pass, then the P2 pass (FlowProducer /
 // FlowConsumer above).  ntiles: P1's N tiles in the low 16 bits, P2's above.
+// split = 0: every workgroup runs both passes, its P1 items first.  split =
+// n1 > 0 (a CTA split, "Analytical Resource Management for Fine-grained MoE
+// Computation-Communication Overlap", abstract: the producer-CTA count of a
+// dependency-coupled pipeline): workgroups j < n1 of each worker are
+// producers and deal the worker's P1 items among themselves; the other n - n1
+// are consumers and deal its P2 items.  Producers never wait, and every
+// workgroup of the persistent grid is resident, so the consumers' waits end.
 // The timeline gets both phases: P1 from the start to the end of the first
 // pass, P2 from there to the end.
 template <class S1, class S2, class C, class OA, class OB>
-__global__ __launch_bounds__(C::NT, 512 / C::NT) void k_stream2(ExecArgs a, int ntiles) {
+__global__ __launch_bounds__(C::NT, 512 / C::NT) void k_stream2(ExecArgs a, int ntiles, int split) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   MOE_LDS uint16_t* smem = (MOE_LDS uint16_t*)smem_raw;
   const uint64_t t0 = a.timeline ? __builtin_amdgcn_s_memrealtime() : 0;
   const int n1 = ntiles & 0xffff, n2 = ntiles >> 16;
+  const WorkerSlot w = worker_slot(a.P);
+  if (split >= w.n) split = 0;                   // the host admits 0 <= split < n only
+  const bool producer = split == 0 || w.j < split;
+  const bool consumer = split == 0 || w.j >= split;
   f32x16_t acc[C::MB][C::NB];
   WideStream<C, OA, OB> p;
   {
     S1 src;
     src.init(a, smem, n1);
-    p.run(src, smem, acc);
+    if (split > 0) src.stride = split;             // first = w.j < split
+    if (producer) p.run(src, smem, acc);
   }
   const uint64_t tm = a.timeline ? __builtin_amdgcn_s_memrealtime() : 0;
   {
     S2 src;
     src.init(a, smem, n2);
     src.n1 = n1;
-    p.run(src, smem, acc);
+    if (split > 0) {
+      src.first = w.j - split;
+      src.stride = w.n - split;
+    }
+    if (consumer) p.run(src, smem, acc);
   }
   if (a.timeline) {
     __syncthreads();
@@ -1971,11 +1987,12 @@ static void launch_stream(ExecArgs& a, int ntiles_n, size_t lds, hipStream_t st)
 // the two-phase launch relies on every workgroup being resident: the grid is
 // the persistent one (workgroups per CU that fit x CUs)
 template <class S1, class S2, class C, class OA, class OB>
-static void launch_stream2(ExecArgs& a, int ntiles, size_t lds, hipStream_t st) {
+static void launch_stream2(ExecArgs& a, int ntiles, int split, size_t lds, hipStream_t st) {
   static_assert(std::is_same<typename S1::OB, OB>::value && std::is_same<typename S2::OB, OB>::value,
                 "one B operand type");
   static int g = persistent_grid(k_stream2<S1, S2, C, OA, OB>, C::NT, lds);
-  hipLaunchKernelGGL((k_stream2<S1, S2, C, OA, OB>), dim3(g), dim3(C::NT), lds, st, a, ntiles);
+  hipLaunchKernelGGL((k_stream2<S1, S2, C, OA, OB>), dim3(g), dim3(C::NT), lds, st, a, ntiles,
+                     split);
 }
 
 static void launch_slot_gate(const Sizes& z, const ExecArgs& a, hipStream_t st) {
@@ -1986,9 +2003,25 @@ static void launch_slot_gate(const Sizes& z, const ExecArgs& a, hipStream_t st) 
                        (float*)a.sgate);
 }
 
+// workgroups of one worker in the two-phase launches (one per CU)
+static int wide_workers_wg(int P) {
+  static int g = persistent_grid(k_stream2<FlowProducer<SrcFc1T<false, true>>,
+                                           FlowConsumer<SrcFc2T<false>>, WC, RowW, RowW>,
+                                 WC::NT, kStreamLds);
+  return g / P;
+}
+
+// exec_flags: MOE_EXEC_TWO_PHASE and its producer count, checked against the
+// workgroups of one worker (MOE_ERR_ARG when out of range)
+static int exec_split(int exec_flags, int P, bool* two_launches) {
+  const int n1 = (exec_flags >> MOE_EXEC_SPLIT_SHIFT) & 0xff;
+  *two_launches = (exec_flags & MOE_EXEC_TWO_PHASE) == 0;
+  return n1 < wide_workers_wg(P) ? n1 : -1;
+}
+
 template <bool FP8>
 static void run_forward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* y,
-                               bool split, void* const* ev, hipStream_t st) {
+                               bool split, int n1split, void* const* ev, hipStream_t st) {
   launch_slot_gate(z, a, st);
   const int n1 = z.dff / (WC::BN / 2), n2 = z.d / WC::BN;
   a.tl_phase = MOE_TL_FC1;
@@ -1999,7 +2032,7 @@ static void run_forward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_t
     launch_stream<SrcFc2T<FP8>, WC, RowW, typename SrcFc2T<FP8>::OB>(a, n2, kStreamLds, st);
   } else {
     launch_stream2<FwdP1<FP8>, FwdP2<FP8>, WC, RowW, typename SrcFc1T<FP8>::OB>(
-        a, n1 | (n2 << 16), kStreamLds, st);
+        a, n1 | (n2 << 16), n1split, kStreamLds, st);
     rec(ev, 2, st);
   }
   rec(ev, 3, st);
@@ -2014,6 +2047,9 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
                    const int32_t* slot_to_row, const int32_t* block_worker, void* y,
                    void* z_save, int32_t* status, char* ws, int exec_flags, void* const* ev,
                    uint64_t* timeline, hipStream_t st) {
+  bool split = true;
+  const int n1split = exec_split(exec_flags, z.P, &split);
+  if (n1split < 0) return MOE_ERR_ARG;
   const WsLayout L = exec_layout(z, false);
   rec(ev, 0, st);
   launch_sched(z, counts, boff, block_worker, nullptr, false, ws, L, status, st);
@@ -2024,11 +2060,10 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
   a.timeline = timeline;
   a.status = status;
   const bool big = use_big_tiles(z);
-  const bool split = (exec_flags & MOE_EXEC_TWO_PHASE) == 0;
   if (Lp.act_dtype == MOE_BF16 && Lp.w_dtype == MOE_BF16 && use_stream(z))
-    run_forward_stream<false>(z, a, row_to_slot, y, split, ev, st);
+    run_forward_stream<false>(z, a, row_to_slot, y, split, n1split, ev, st);
   else if (Lp.act_dtype == MOE_BF16 && Lp.w_dtype == MOE_FP8_E4M3 && use_stream(z))
-    run_forward_stream<true>(z, a, row_to_slot, y, split, ev, st);
+    run_forward_stream<true>(z, a, row_to_slot, y, split, n1split, ev, st);
   else if (Lp.act_dtype == MOE_F32) run_forward<float, false, SmallCfg>(z, a, row_to_slot, y, ev, st);
   else if (Lp.w_dtype == MOE_FP8_E4M3) {
     if (big) run_forward<uint16_t, true, BigCfg>(z, a, row_to_slot, y, ev, st);
@@ -2045,7 +2080,7 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
 // bufA once dX has used it; the weight gradients then read both as bf16.
 template <bool FP8>
 static void run_backward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* dx,
-                                float* dw1, float* dw2, bool split, void* const* ev,
+                                float* dw1, float* dw2, bool split, int n1split, void* const* ev,
                                 hipStream_t st) {
   const int rows = (int)z.max_slots;
   launch_slot_gate(z, a, st);
@@ -2061,7 +2096,7 @@ static void run_backward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_
     launch_stream<SrcDxT<FP8>, WC, RowW, typename SrcDxT<FP8>::OB>(a, n2, kStreamLds, st);
   } else {
     launch_stream2<BwdP1<FP8>, BwdP2<FP8>, WC, RowW, typename SrcDaT<FP8>::OB>(
-        a, n1 | (n2 << 16), kStreamLds, st);
+        a, n1 | (n2 << 16), n1split, kStreamLds, st);
     rec(ev, 2, st);
   }
   rec(ev, 3, st);
@@ -2117,6 +2152,9 @@ int launch_backward(const Sizes& z, const LayerPtrs& Lp, const void* x, const fl
                     const int32_t* block_worker, void* dx, float* dw1, float* dw2,
                     int32_t* status, char* ws, int exec_flags, void* const* ev,
                     uint64_t* timeline, hipStream_t st) {
+  bool split = true;
+  const int n1split = exec_split(exec_flags, z.P, &split);
+  if (n1split < 0) return MOE_ERR_ARG;
   const WsLayout L = exec_layout(z, true);
   rec(ev, 0, st);
   launch_sched(z, counts, boff, block_worker, owner, true, ws, L, status, st);
@@ -2127,13 +2165,14 @@ int launch_backward(const Sizes& z, const LayerPtrs& Lp, const void* x, const fl
   a.dy = dy; a.dw1 = dw1; a.dw2 = dw2; a.boff = boff;
   a.timeline = timeline;
   a.status = status;
-  const bool split = (exec_flags & MOE_EXEC_TWO_PHASE) == 0;
   if (Lp.act_dtype == MOE_F32) run_backward<float, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else if (Lp.w_dtype == MOE_FP8_E4M3) {
-    if (use_stream(z)) run_backward_stream<true>(z, a, row_to_slot, dx, dw1, dw2, split, ev, st);
+    if (use_stream(z))
+      run_backward_stream<true>(z, a, row_to_slot, dx, dw1, dw2, split, n1split, ev, st);
     else if (use_big_tiles(z)) run_backward<uint16_t, BigCfg, true>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
     else run_backward<uint16_t, SmallCfg, true>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
-  } else if (use_stream(z)) run_backward_stream<false>(z, a, row_to_slot, dx, dw1, dw2, split, ev, st);
+  } else if (use_stream(z))
+    run_backward_stream<false>(z, a, row_to_slot, dx, dw1, dw2, split, n1split, ev, st);
   else if (use_big_tiles(z)) run_backward<uint16_t, BigCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else run_backward<uint16_t, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;

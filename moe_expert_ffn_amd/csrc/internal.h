@@ -58,6 +58,9 @@ int launch_quant_tok(const uint16_t* src, int ld, const int32_t* map, int gather
 int launch_predict_cost(const int32_t* counts, const int32_t* boff, const int32_t* bw_f,
                         const int32_t* bw_b, const int32_t* owner, int E, int beta, int P, int d,
                         int dff, int G, long long* cost, int32_t* status, hipStream_t st);
+int launch_predict_split(const int32_t* counts, const int32_t* boff, const int32_t* bw, int E,
+                         int beta, int P, int d, int dff, int G, int backward, long long* costs,
+                         int32_t* choice, int32_t* status, hipStream_t st);
 int launch_plan_gate(const int32_t* bcnt, const int32_t* boff, const int32_t* owner, int E, int P,
                      int rho_milli, int32_t* q, int32_t* load, int32_t* bw, int bw_cap,
                      int32_t* info, int32_t* status, hipStream_t st);

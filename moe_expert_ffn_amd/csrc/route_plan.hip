@@ -797,6 +797,132 @@ __global__ __launch_bounds__(256) void k_predict_cost(const int32_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Producer/consumer split of a two-phase launch (same page: the count of
+// producer CTAs of a dependency-coupled pipeline, chosen before the launch
+// from routed-tile counts and split-level readiness).  The pair is FC1 -> FC2
+// (forward) or dA -> dX (backward); a second-phase item of row tile t needs
+// every first-phase item of row tile t.  Worker r has T_r row tiles and
+// n = G / P workgroups; items are tile-major (item i: row tile i / nnt) and
+// all items of a phase cost the same (c1, c2: K steps plus the epilogue, as
+// in the cost model above).  Modes:
+//   -1  two launches: max_r ceil(T_r nnt1 / n) c1 + max_r ceil(T_r nnt2 / n) c2;
+//    0  one launch, every workgroup j runs first-phase items j, j + n, ...,
+//       then second-phase items j, j + n, ...;
+//   n1  one launch, workgroups j < n1 deal the first-phase items, the other
+//       n - n1 the second-phase items.
+// A first-phase item i dealt over m workgroups ends at (i / m + 1) c1, so row
+// tile t is ready at ((t nnt1 + nnt1 - 1) / m + 1) c1; a second-phase item
+// starts when its workgroup is free and its row tile is ready.  A mode costs
+// its latest workgroup over every worker.  One thread per mode.
+// ---------------------------------------------------------------------------
+MOE_DEV long long split_ready(long long t, int nnt1, int m, long long c1) {
+  return ((t * nnt1 + nnt1 - 1) / m + 1) * c1;
+}
+
+__global__ __launch_bounds__(256) void k_predict_split(const int32_t* __restrict__ counts,
+                                                       const int32_t* __restrict__ boff,
+                                                       const int32_t* __restrict__ bw, int E,
+                                                       int beta, int P, int d, int dff, int G,
+                                                       int backward, long long* cost_out,
+                                                       int32_t* choice_out, int32_t* status) {
+  extern __shared__ int sm[];
+  int* cnt_s = sm;                    // [E]
+  int* boff_s = cnt_s + E;            // [E+1]
+  int* nb_s = boff_s + E + 1;         // [E][P] blocks of e on worker w
+  __shared__ int tiles_s[kMaxP];      // per-block tiles when beta does not divide 256
+  __shared__ long long tr_s[kMaxP];   // row tiles of each worker
+  __shared__ long long cost_s[257];
+  const int tid = threadIdx.x;
+  constexpr int bm = 256;
+  for (int e = tid; e < E; e += 256) cnt_s[e] = counts[e];
+  for (int e = tid; e <= E; e += 256) boff_s[e] = boff[e];
+  for (int i = tid; i < E * P; i += 256) nb_s[i] = 0;
+  if (tid < kMaxP) tiles_s[tid] = 0;
+  __syncthreads();
+  const int nb = boff_s[E];
+  for (int g = tid; g < nb; g += 256) {
+    int lo = 0, hi = E;  // largest e with boff_s[e] <= g
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (boff_s[mid] <= g) lo = mid; else hi = mid;
+    }
+    const int e = lo;
+    const int vrows = min(beta, cnt_s[e] - beta * (g - boff_s[e]));
+    int w = bw[g];
+    if (w < 0 || w >= P) { atomicOr(status, MOE_DEV_BAD_PLAN); w = 0; }
+    atomicAdd(&nb_s[e * P + w], 1);
+    if (bm % beta != 0) atomicAdd(&tiles_s[w], (vrows + bm - 1) / bm);
+  }
+  __syncthreads();
+  if (tid < P) {
+    long long t = 0;
+    if (bm % beta == 0) {
+      const int f = bm / beta;
+      for (int e = 0; e < E; ++e) t += (nb_s[e * P + tid] + f - 1) / f;
+    } else {
+      t = tiles_s[tid];
+    }
+    tr_s[tid] = t;
+  }
+  __syncthreads();
+  const int n = G / P;
+  int nnt1, nnt2;
+  long long c1, c2;
+  if (backward) {
+    nnt1 = dff / 256;
+    nnt2 = d / 256;
+    c1 = 1000LL * (d / 64) + epi_milli((long long)bm * 256 * 3 * 2 + (long long)bm * 512 * 2);
+    c2 = 1000LL * (2 * dff / 64) + epi_milli((long long)bm * 256 * 2);
+  } else {
+    nnt1 = 2 * dff / 256;
+    nnt2 = d / 256;
+    c1 = 1000LL * (d / 64) + epi_milli((long long)bm * (128 + 256) * 2);
+    c2 = 1000LL * (dff / 64) + epi_milli((long long)bm * 256 * 2);
+  }
+  for (int m = tid - 1; m < n; m += 256) {
+    long long worst = 0;
+    if (m == -1) {
+      long long m1 = 0, m2 = 0;
+      for (int r = 0; r < P; ++r) {
+        m1 = max(m1, ceil_div_ll(tr_s[r] * nnt1, n));
+        m2 = max(m2, ceil_div_ll(tr_s[r] * nnt2, n));
+      }
+      worst = m1 * c1 + m2 * c2;
+    } else {
+      for (int r = 0; r < P; ++r) {
+        const long long N1 = tr_s[r] * nnt1, N2 = tr_s[r] * nnt2;
+        if (m == 0) {
+          for (int j = 0; j < n; ++j) {
+            long long clock = (j < N1 ? (N1 - 1 - j) / n + 1 : 0) * c1;
+            for (long long i2 = j; i2 < N2; i2 += n)
+              clock = max(clock, split_ready(i2 / nnt2, nnt1, n, c1)) + c2;
+            worst = max(worst, clock);
+          }
+        } else {
+          const int n1 = m, n2 = n - m;
+          worst = max(worst, ceil_div_ll(N1, n1) * c1);
+          for (int j = 0; j < n2; ++j) {
+            long long clock = 0;
+            for (long long i2 = j; i2 < N2; i2 += n2)
+              clock = max(clock, split_ready(i2 / nnt2, nnt1, n1, c1)) + c2;
+            worst = max(worst, clock);
+          }
+        }
+      }
+    }
+    cost_s[m + 1] = worst;
+    cost_out[m + 1] = worst;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int best = 0;
+    for (int i = 1; i <= n; ++i)
+      if (cost_s[i] < cost_s[best]) best = i;
+    *choice_out = best - 1;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 size_t route_ws_bytes(int T, int k, int E) {
@@ -881,6 +1007,15 @@ int launch_predict_cost(const int32_t* counts, const int32_t* boff, const int32_
   const size_t lds = sizeof(int) * (size_t)(3 * E + 1 + 3 * E * P);
   hipLaunchKernelGGL(k_predict_cost, dim3(1), dim3(256), lds, st, counts, boff, bw_f, bw_b,
                      owner, E, beta, P, d, dff, G, cost, status);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int launch_predict_split(const int32_t* counts, const int32_t* boff, const int32_t* bw, int E,
+                         int beta, int P, int d, int dff, int G, int backward, long long* costs,
+                         int32_t* choice, int32_t* status, hipStream_t st) {
+  const size_t lds = sizeof(int) * (size_t)(2 * E + 1 + E * P);
+  hipLaunchKernelGGL(k_predict_split, dim3(1), dim3(256), lds, st, counts, boff, bw, E, beta, P, d,
+                     dff, G, backward, costs, choice, status);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -29,6 +29,10 @@ class LayerRunner:
         self.act_dtype = act_dtype
         # two_phase: FC1 / FC2 (dA / dX) in one two-phase launch instead of two
         self.two_phase = two_phase
+        # producer workgroups per worker of the forward / backward two-phase
+        # launch (0: every workgroup runs both phases)
+        self.split_fwd = 0
+        self.split_bwd = 0
         self.owner = owner.to(device=dev, dtype=torch.int32).contiguous()
         self.with_backward = with_backward
         self.ws = B.workspace(self.layer, T, k, beta, P, s, with_backward, dev)
@@ -66,14 +70,14 @@ class LayerRunner:
     def forward(self, x, gates, topk_ids, block_worker=None, events=None, timeline=None):
         bw = self.plan_f["block_worker"] if block_worker is None else block_worker
         B.forward(self.layer, x, gates, topk_ids, self.beta, self.P, self.rs, bw, self.y, self.z,
-                  self.ws, self.status, events, timeline, self.two_phase)
+                  self.ws, self.status, events, timeline, self.two_phase, self.split_fwd)
         return self.y
 
     def backward(self, x, gates, dy, topk_ids, block_worker=None, events=None, timeline=None):
         bw = self.plan_b["block_worker"] if block_worker is None else block_worker
         B.backward(self.layer, x, gates, dy, self.z, topk_ids, self.beta, self.P, self.s, self.rs,
                    self.owner, bw, self.dx, self.dw1, self.dw2, self.ws, self.status, events,
-                   timeline, self.two_phase)
+                   timeline, self.two_phase, self.split_bwd)
         return self.dx, self.dw1, self.dw2
 
     def step(self, x, gates, topk_ids, dy=None, s=None, timeline=None):

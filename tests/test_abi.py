@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = B.load()
-    assert lib.moe_abi_version() == B.ABI_VERSION == 4
+    assert lib.moe_abi_version() == B.ABI_VERSION == 5
     assert lib.moe_status_str(0) == b"ok"
     assert b"workspace" in lib.moe_status_str(-3)
 
@@ -158,6 +158,29 @@ def test_host_validation_errors():
                            None, None) == B.MOE_ERR_ARG
     assert lib.moe_backward(ctypes.byref(ok), P, P, P, P, P, 4, 2, 16, 4, 1, *([P] * 10), P,
                             1 << 30, 4, None, None, None) == B.MOE_ERR_ARG
+    # a producer/consumer split without the two-phase launch, or bits past 15
+    for bad in (1 << 8, 1 | (1 << 16)):
+        assert lib.moe_forward(ctypes.byref(ok), P, P, P, 4, 2, 16, 4, *([P] * 8), P, 1 << 30, bad,
+                               None, None, None) == B.MOE_ERR_ARG
+        assert lib.moe_backward(ctypes.byref(ok), P, P, P, P, P, 4, 2, 16, 4, 1, *([P] * 10), P,
+                                1 << 30, bad, None, None, None) == B.MOE_ERR_ARG
+    # split model: (counts, offsets, block_worker, E, beta, P, d, d_ff, G, backward,
+    #  costs, choice, status, stream)
+    ps = lib.moe_predict_split
+    assert ps(P, P, P, 0, 16, 4, 256, 256, 256, 0, P, P, P, None) == B.MOE_ERR_ARG      # E
+    assert ps(P, P, P, 8, 0, 4, 256, 256, 256, 0, P, P, P, None) == B.MOE_ERR_ARG      # beta
+    assert ps(P, P, None, 8, 16, 4, 256, 256, 256, 0, P, P, P, None) == B.MOE_ERR_ARG  # plan
+    assert ps(P, P, P, 8, 16, 4, 256, 256, 256, 0, P, None, P, None) == B.MOE_ERR_ARG  # choice
+    assert ps(P, P, P, 8, 16, 3, 256, 256, 256, 0, P, P, P, None) == B.MOE_ERR_UNSUPPORTED  # P
+    assert ps(P, P, P, 8, 16, 4, 384, 256, 256, 0, P, P, P, None) == B.MOE_ERR_UNSUPPORTED  # d
+    assert ps(P, P, P, 8, 16, 4, 256, 256, 254, 0, P, P, P, None) == B.MOE_ERR_UNSUPPORTED  # G % P
+    assert ps(P, P, P, 8, 16, 1, 256, 256, 512, 0, P, P, P, None) == B.MOE_ERR_UNSUPPORTED  # G/P
+    # the binding builds the flags and refuses a split without the two-phase launch
+    assert B.exec_flags(True, 12) == 1 | (12 << 8)
+    with pytest.raises(B.MoeError):
+        B.exec_flags(False, 3)
+    with pytest.raises(B.MoeError):
+        B.exec_flags(True, 256)
 
 
 def test_quantizer_binding_checks_buffers():

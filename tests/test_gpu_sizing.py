@@ -52,3 +52,36 @@ def test_predict_cost_matches_oracle(name, kappa):
         say(f"[cost] {name} kappa={kappa} P={P} cost={want}")
         assert int(cost[0].item()) == want
         assert int(cost[1].item()) == want          # 256 CUs on this device
+
+
+@pytest.mark.parametrize("name,kappa", CASES)
+def test_predict_split_matches_oracle(name, kappa):
+    """moe_predict_split (every two-phase mode's predicted time and the choice)
+    is bit-exact with the oracle for both directions' plans at every P."""
+    from oracle.sizing import select_split, split_costs
+    w = WORKLOADS[name]
+    ids, _ = make_routing(w, kappa)
+    rs = oracle_route(ids, w.E, w.beta)
+    dev = lambda a: torch.from_numpy(np.asarray(a, dtype=np.int32)).to(DEV)
+    counts, boff, bc = dev(rs["counts"]), dev(rs["block_offsets"]), dev(rs["block_counts"])
+    nb = int(rs["block_offsets"][-1])
+    for P in (1, 2, 4, 8):
+        owner = dev(contiguous_owners(w.E, P))
+        st = torch.zeros(1, dtype=torch.int32, device=DEV)
+        for mode, backward in ((B.PLAN_FWD, False), (B.PLAN_BWD, True)):
+            pl = B.alloc_plan(w.E, P, max(nb, 1), DEV)
+            B.plan(bc, boff, owner, P, w.s, mode, 12, pl, _ws(w.E), st)
+            n = 256 // P
+            costs = torch.full((n + 1,), -7, dtype=torch.int64, device=DEV)
+            choice = torch.full((1,), -9, dtype=torch.int32, device=DEV)
+            B.predict_split(counts, boff, pl["block_worker"], w.beta, P, w.d, w.d_ff, backward,
+                            costs, choice, st, num_workgroups=256)
+            torch.cuda.synchronize()
+            assert int(st.item()) == 0
+            want = split_costs(rs["counts"], pl["block_worker"].cpu().numpy()[:nb], w.beta, P, w.d,
+                               w.d_ff, backward, G=256)
+            got = costs.cpu().tolist()
+            say(f"[split] {name} kappa={kappa} P={P} bwd={backward} choice={select_split(want)} "
+                f"two={want[0]} temporal={want[1]}")
+            assert got == want
+            assert int(choice.item()) == select_split(want)

@@ -3,7 +3,8 @@
 bit equals that of the two-launch form, at every placement, worker count and
 skew, including problems where a workgroup's next item reads the rows its
 current item writes (it restarts its pipeline after publishing them), and
-the wait never times out."""
+the wait never times out.  The same holds with the producer/consumer split
+(MOE_EXEC_SPLIT): few producers, about two thirds, and a single consumer."""
 import pytest
 import torch
 
@@ -27,9 +28,10 @@ CASES = {
 }
 
 
-def _outputs(c, split, s=None):
+def _outputs(c, split, s=None, n1=0):
     r = c.runner
     r.two_phase = not split
+    r.split_fwd = r.split_bwd = 0 if split else n1
     r.status.zero_()
     r.step(c.x, c.gates, c.ids, dy=c.dy, s=s)
     torch.cuda.synchronize()
@@ -66,8 +68,15 @@ def _check_equal(c, a, b):
             assert torch.equal(u, v), _describe(name, u, v)
 
 
-def _same(c, s=None):
-    _check_equal(c, _outputs(c, split=True, s=s), _outputs(c, split=False, s=s))
+def _same(c, s=None, n1s=(0,)):
+    ref = _outputs(c, split=True, s=s)
+    for n1 in n1s:
+        _check_equal(c, ref, _outputs(c, split=False, s=s, n1=n1))
+
+
+def _producer_counts(P):
+    n = B.device_info()["num_cus"] // P
+    return (1, (2 * n) // 3, n - 1)
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -76,7 +85,7 @@ def test_two_phase_launch_matches_split_launches(name, P):
     w = CASES[name]
     say(f"[two-phase] {name} P={P}")
     c = Case(w, 0, P=P, s=min(w.s, P - 1) if P > 1 else 0, backward=True)
-    _same(c)
+    _same(c, n1s=(0,) + _producer_counts(P))
     if P > 1 and w.s > 0:
         _same(c, s=0)                  # fixed placement
 
@@ -87,7 +96,22 @@ def test_two_phase_launch_full_size(kappa, P):
     w = WORKLOADS["qwen3_bf16_fwdbwd"]
     say(f"[two-phase] qwen3_bf16_fwdbwd kappa={kappa} P={P}")
     c = Case(w, kappa, P=P, s=min(w.s, P - 1) if P > 1 else 0, backward=True)
-    _same(c)
+    _same(c, n1s=(0, _producer_counts(P)[1]))
+
+
+def test_split_out_of_range_is_refused():
+    """A producer count of a whole worker's workgroups or more is refused on
+    the host before anything is launched."""
+    w = CASES["stream_bf16"]
+    say("[two-phase] split out of range")
+    c = Case(w, 0, P=8, s=4, backward=True)
+    n = B.device_info()["num_cus"] // 8
+    r = c.runner
+    r.route(c.ids)
+    r.make_plan()
+    with pytest.raises(B.MoeError):
+        B.forward(r.layer, c.x, c.gates, c.ids, r.beta, r.P, r.rs, r.plan_f["block_worker"], r.y,
+                  r.z, r.ws, r.status, two_phase=True, split=n)
 
 
 def test_two_phase_repeated_steps_are_identical():
