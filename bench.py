@@ -301,7 +301,7 @@ def reduce_bytes(case, w):
 # WRITE_SIZE per dispatch, scaled by the reading of a plain copy kernel of
 # known size), valid only for the kernel sources it was measured on.
 PROFILED_TRAFFIC = {"kernel": "bwd.dW", "workload": "qwen3_bf16_fwdbwd", "kappa": 1.0, "fixed": False,
-                    "source": "a1d30fbd3907db21", "bytes": 3341774598,
+                    "source": "023c0a71c6a329c3", "bytes": 3338825914,
                     "summary": "profiles/k_stream_SrcDwT_qwen3_bf16_fwdbwd_hbm_traffic.md"}
 
 
