@@ -18,6 +18,13 @@ block's column and code = e4m3(value / scale), every step in fp32 (the
 quantized code is an integer decided by floating point, so the oracle and the
 device both decide it in fp32); an all-zero block column has scale 0 and
 codes 0.
+
+Activation rows for an fp8 x fp8 product (the fp8 MFMA path of FC1; reading:
+the "per-1x128 e4m3 activations" of a block-scaled fp8 GEMM): each row is cut
+into blocks of 128 consecutive features, and each block gets a power-of-two
+scale 2^e, e the smallest integer with amax <= 448 * 2^e (so the largest
+value maps into the top binade of e4m3), clamped to [-127, 127]; an all-zero
+block has e = -127.  code = e4m3(value * 2^-e), the product exact in fp32.
 """
 from __future__ import annotations
 
@@ -84,6 +91,36 @@ def quantize_token_blocks(values, block_rows: int):
         q = np.where(sc > 0, (blk / safe).astype(np.float32), np.float32(0.0))
         codes[b * block_rows:(b + 1) * block_rows] = encode_e4m3(q)
     return codes, scales
+
+
+def quantize_row_blocks_pow2(values, block_cols: int = 128):
+    """values fp32 [rows, cols] (cols a multiple of block_cols) -> (codes
+    uint8 [rows, cols], exps int32 [rows, cols / block_cols]): per row and
+    block of block_cols columns, e = ceil(log2(amax / 448)) clamped to
+    [-127, 127] (-127 for a zero block), code = e4m3(value * 2^-e)."""
+    v = np.asarray(values, dtype=np.float32)
+    rows, cols = v.shape
+    assert cols % block_cols == 0
+    nb = cols // block_cols
+    blk = v.reshape(rows, nb, block_cols)
+    amax = np.max(np.abs(blk), axis=2).astype(np.float64)
+    # ceil(log2(x)) from x = m * 2^E, m in [0.5, 1): E - 1 when m is exactly 0.5
+    m, E = np.frexp(amax / 448.0)
+    e = np.where(m == 0.5, E - 1, E).astype(np.int64)
+    e = np.where(amax > 0, e, -127)
+    e = np.clip(e, -127, 127)
+    scaled = (blk.astype(np.float64) * np.power(2.0, -e)[:, :, None]).astype(np.float32)
+    codes = encode_e4m3(scaled).reshape(rows, cols)
+    return codes, e.astype(np.int32)
+
+
+def dequant_row_blocks_pow2(codes, exps, block_cols: int = 128) -> np.ndarray:
+    """Inverse of quantize_row_blocks_pow2 up to the rounding: fp64 values."""
+    global _TABLE
+    if _TABLE is None:
+        _TABLE = decode_e4m3(np.arange(256, dtype=np.uint8))
+    v = _TABLE[np.asarray(codes, dtype=np.uint8)]
+    return v * np.repeat(np.power(2.0, np.asarray(exps, dtype=np.float64)), block_cols, axis=1)
 
 
 def dequant_token_blocks(codes, scales, block_rows: int) -> np.ndarray:

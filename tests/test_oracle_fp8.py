@@ -74,3 +74,52 @@ def test_quantize_token_blocks():
     # within half a step of e4m3: 2^-4 relative, or 2^-10 of the scale below 2^-6
     bound = np.maximum(np.abs(v) * 2.0 ** -4, np.repeat(scales, 128, axis=0)[:300] * 2.0 ** -10)
     assert np.all(np.abs(back - v) <= bound * (1 + 1e-6))
+
+
+# ---- activation rows: per-row blocks of 128 with power-of-two scales ----------
+
+def test_row_blocks_pow2_exponent_boundaries():
+    """e is the smallest integer with amax <= 448 * 2^e: amax = 448 * 2^k
+    and one ulp below give k, one ulp above gives k + 1; 256 * 2^k still
+    needs k, and 128 * 2^k fits k - 1."""
+    from oracle.fp8 import quantize_row_blocks_pow2
+    rows = []
+    want = []
+    for k in (-20, -3, 0, 1, 7):
+        top = np.float32(448.0 * 2.0 ** k)
+        for amax, e in ((top, k), (np.nextafter(top, np.float32(np.inf)), k + 1),
+                        (np.nextafter(top, np.float32(0)), k), (np.float32(2.0 ** (k + 8)), k),
+                        (np.float32(2.0 ** (k + 7)), k - 1)):
+            r = np.zeros(128, dtype=np.float32)
+            r[5] = -amax
+            rows.append(r)
+            want.append(e)
+    codes, exps = quantize_row_blocks_pow2(np.stack(rows))
+    np.testing.assert_array_equal(exps[:, 0], want)
+    # the block maximum lands in the top binade [256, 448] of e4m3
+    top = decode_e4m3(codes[np.arange(len(rows)), 5])
+    assert (np.abs(top) >= 224).all() and (np.abs(top) <= 448).all()
+
+
+def test_row_blocks_pow2_codes_match_torch_cast():
+    """Codes are torch's e4m3fn cast of value * 2^-e (an independent encoder),
+    zero blocks have e = -127 and codes 0, and every value comes back within
+    half an e4m3 step of its scaled grid."""
+    from oracle.fp8 import dequant_row_blocks_pow2, quantize_row_blocks_pow2
+    rng = np.random.default_rng(9)
+    v = (rng.standard_normal((64, 512)) * 10.0 ** rng.uniform(-3, 3, (64, 1))).astype(np.float32)
+    v[3, 128:256] = 0.0
+    codes, exps = quantize_row_blocks_pow2(v)
+    assert exps.shape == (64, 4) and exps[3, 1] == -127 and (codes[3, 128:256] == 0).all()
+    scaled = (v.reshape(64, 4, 128) * np.power(2.0, -exps.astype(np.float64))[:, :, None]).astype(np.float32)
+    ref = torch.from_numpy(scaled.reshape(64, 512)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(codes, ref)
+    back = dequant_row_blocks_pow2(codes, exps)
+    step = np.repeat(np.power(2.0, exps.astype(np.float64)), 128, axis=1) * 2.0 ** -9
+    grid_step = np.maximum(np.abs(back), np.abs(v)) * 2.0 ** -3
+    assert (np.abs(back - v) <= np.maximum(grid_step / 2 * 1.0001, step)).all()
+    # power-of-two scales change the exponent only: a block scaled by 2^j
+    # gets the same codes and e + j
+    c2, e2 = quantize_row_blocks_pow2((v * np.float32(2.0 ** 5)).astype(np.float32))
+    np.testing.assert_array_equal(c2, codes)
+    np.testing.assert_array_equal(e2[exps > -127], exps[exps > -127] + 5)
