@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 
 METRIC = "MoE-layer useful TFLOP/s (fwd,bwd) at κ=1/2/4/8; % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PEAK_FP8_TFLOPS = 5033.2       # twice the bf16 rate on the fp8 MFMA, dense
 PEAK_HBM_GBS = 8000.0
 
 # stage names between consecutive stage events, keyed by the two-phase launch
@@ -618,6 +619,22 @@ def main():
         "roofline": roof,
         "kernels": per_kernel,
     }
+    if w.wdt == "fp8":
+        # the same steps with FC1 on the fp8 MFMA (MOE_EXEC_FP8_ACT: x quantized
+        # per row block of 128 features); FC1 priced against the fp8 peak
+        case["runner"].fp8_act = True
+        ms_f8, st_f8 = time_steps(case, args.steps, args.warmup)
+        case["runner"].fp8_act = False
+        fc1_flops = 4 * w.d * w.d_ff * R
+        fc1_us = st_f8.get("fwd.fc1", 0.0) * 1e3
+        out["fp8_act"] = {
+            "ms_per_step": round(ms_f8, 4),
+            "tflops": round(useful / (ms_f8 * 1e-3) / 1e12, 3),
+            "stages_us": {k: round(v * 1e3, 2) for k, v in st_f8.items()},
+            "fc1_tflops": round(fc1_flops / (fc1_us * 1e-6) / 1e12, 1) if fc1_us else None,
+            "fc1_pct_fp8_peak": round(100 * fc1_flops / (fc1_us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 2)
+            if fc1_us else None,
+        }
     if not args.sweep and not args.no_sweep and len(w.kappas) > 1:
         out["kappa_sweep"], out["skew"] = kappa_sweep(w, dev, lay, args.sweep_steps)
     if args.sweep:

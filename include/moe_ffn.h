@@ -81,6 +81,14 @@ typedef enum {
  * plan.  The results are the same bits in every mode. */
 #define MOE_EXEC_SPLIT_SHIFT 8
 #define MOE_EXEC_SPLIT(n1) (((n1) & 0xff) << MOE_EXEC_SPLIT_SHIFT)
+/* moe_forward only, e4m3 weights on the persistent stream kernels (d and
+ * d_ff multiples of 256), two launches: FC1 runs on the fp8 MFMA.  x is
+ * quantized per token row and 128 features with power-of-two scales
+ * (moe_quantize_act_rows) into the workspace, the weights' codes are used
+ * as stored, and per 128-deep K block the weights' fp32 block scale is
+ * applied to the accumulators.  The results differ from the default path by
+ * x's quantization (relative error about 2^-5 per value). */
+#define MOE_EXEC_FP8_ACT 2
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 
@@ -390,6 +398,19 @@ int moe_quantize_token_blocks(const void* src, int ld, int src_rows, const int32
                               int gather, int row_div, const float* row_scale, int rows,
                               int cols, int block_rows, uint8_t* codes, float* scales,
                               void* stream);
+
+/* Activation rows for an fp8 x fp8 product: each row of src [rows][cols]
+ * (bf16, cols a multiple of 128) is cut into blocks of 128 features; block b
+ * of row r gets the power-of-two scale 2^e, e the smallest integer with
+ * amax <= 448 * 2^e, clamped to [-127, 127] (-127 for a zero block), and
+ * codes[r][c] = e4m3(src[r][c] * 2^-e), round to nearest even (the product
+ * is exact).  This is how MOE_EXEC_FP8_ACT quantizes x for FC1.
+ *   codes uint8 [rows][cols]; exps int32 [cols / 128][rows] (block-major:
+ *   exps[b * rows + r] = e), all device memory owned by the caller.
+ * Errors: MOE_ERR_ARG for rows < 0, cols not a positive multiple of 128, or
+ *   a null pointer with rows > 0. */
+int moe_quantize_act_rows(const void* src, int rows, int cols, uint8_t* codes, int32_t* exps,
+                          void* stream);
 
 /* Timing helpers so a caller without a HIP binding can time the stages:
  * create / destroy a hipEvent_t, and the milliseconds between two recorded

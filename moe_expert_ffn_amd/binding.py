@@ -22,9 +22,10 @@ PLAN_FWD, PLAN_BWD, PLAN_QUOTA = 0, 1, 2
 DEV_BAD_EXPERT, DEV_BAD_PLAN, DEV_BAD_OWNER, DEV_WAIT_TIMEOUT = 1, 2, 4, 8
 EXEC_TWO_PHASE = 1              # MOE_EXEC_TWO_PHASE
 EXEC_SPLIT_SHIFT = 8            # MOE_EXEC_SPLIT(n1) = n1 << 8
+EXEC_FP8_ACT = 2                # MOE_EXEC_FP8_ACT
 
 
-def exec_flags(two_phase=False, split=0):
+def exec_flags(two_phase=False, split=0, fp8_act=False):
     """exec_flags of moe_forward / moe_backward: the two-phase launch and its
     producer workgroups per worker (0: every workgroup runs both phases)."""
     split = int(split)
@@ -32,14 +33,16 @@ def exec_flags(two_phase=False, split=0):
         raise MoeError("a producer/consumer split needs the two-phase launch")
     if not 0 <= split <= 0xFF:
         raise MoeError(f"split={split} outside 0..255")
-    return (EXEC_TWO_PHASE if two_phase else 0) | (split << EXEC_SPLIT_SHIFT)
+    return ((EXEC_TWO_PHASE if two_phase else 0) | (split << EXEC_SPLIT_SHIFT) |
+            (EXEC_FP8_ACT if fp8_act else 0))
 TIMELINE_MAX_WG, TL_PHASES = 1024, 5          # MOE_TIMELINE_MAX_WG, MOE_TL_PHASES
 TL_FC1, TL_FC2, TL_DA, TL_DX, TL_DW = range(5)
 
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_max_slots", "moe_max_blocks",
            "moe_workspace_size", "moe_route_stats", "moe_route_stats_noalloc", "moe_plan",
            "moe_plan_gate",
-           "moe_predict_cost", "moe_predict_split", "moe_quantize_token_blocks", "moe_forward",
+           "moe_predict_cost", "moe_predict_split", "moe_quantize_token_blocks",
+           "moe_quantize_act_rows", "moe_forward",
            "moe_backward",
            "moe_event_create", "moe_event_destroy", "moe_event_record", "moe_event_elapsed_ms",
            "moe_device_info"]
@@ -89,6 +92,8 @@ def load():
     lib.moe_quantize_token_blocks.argtypes = [_P, _I, _I, _P, _I, _I, _P, _I, _I, _I, _P, _P, _P]
     lib.moe_predict_cost.restype = _I
     lib.moe_predict_cost.argtypes = [_P] * 5 + [_I] * 6 + [_P, _P, _P]
+    lib.moe_quantize_act_rows.restype = _I
+    lib.moe_quantize_act_rows.argtypes = [_P, _I, _I, _P, _P, _P]
     lib.moe_predict_split.restype = _I
     lib.moe_predict_split.argtypes = [_P] * 3 + [_I] * 7 + [_P, _P, _P, _P]
     lib.moe_plan_gate.restype = _I
@@ -306,6 +311,20 @@ def predict_split(counts, block_offsets, block_worker, beta, P, d, d_ff, backwar
     return costs, choice
 
 
+def quantize_act_rows(src, codes, exps):
+    """e4m3 codes [rows][cols] and power-of-two exponents [cols/128][rows]
+    (int32) of the bf16 rows src [rows][cols], blocks of 128 features."""
+    _require_device(src, codes, exps)
+    if src.dim() != 2:
+        raise MoeError("src must be [rows][cols]")
+    rows, cols = src.shape
+    _expect(src, torch.bfloat16, rows * cols, "src")
+    _expect(codes, torch.uint8, rows * cols, "codes")
+    _expect(exps, torch.int32, rows * (cols // 128), "exps")
+    _check(load().moe_quantize_act_rows(_ptr(src), rows, cols, _ptr(codes), _ptr(exps), _stream()))
+    return codes, exps
+
+
 def quantize_token_blocks(src, rows, cols, block_rows, codes, scales, row_map=None, gather=False,
                           row_div=1, row_scale=None, ld=None, src_rows=None):
     """Token-axis e4m3 codes [rows][cols] and scales [ceil(rows/block_rows)][cols].
@@ -377,7 +396,7 @@ def _expect_timeline(timeline):
 
 
 def forward(layer: Layer, x, gates, topk_ids, beta, P, rs, block_worker, y, z_save, ws, status,
-            events=None, timeline=None, two_phase=False, split=0):
+            events=None, timeline=None, two_phase=False, split=0, fp8_act=False):
     _require_device(x, gates, topk_ids, y, z_save, ws, status, block_worker, timeline)
     _expect_timeline(timeline)
     T, k = _ids_shape(topk_ids)
@@ -396,7 +415,7 @@ def forward(layer: Layer, x, gates, topk_ids, beta, P, rs, block_worker, y, z_sa
                               beta, P, _ptr(rs["counts"]), _ptr(rs["block_offsets"]),
                               _ptr(rs["row_to_slot"]), _ptr(rs["slot_to_row"]),
                               _ptr(block_worker), _ptr(y), _ptr(z_save), _ptr(status), wsp, wsn,
-                              exec_flags(two_phase, split), ev, _ptr(timeline),
+                              exec_flags(two_phase, split, fp8_act), ev, _ptr(timeline),
                               _stream()))
 
 

@@ -192,6 +192,13 @@ int moe_quantize_token_blocks(const void* src, int ld, int src_rows, const int32
                           scales, (hipStream_t)stream);
 }
 
+int moe_quantize_act_rows(const void* src, int rows, int cols, uint8_t* codes, int32_t* exps,
+                          void* stream) {
+  if (rows < 0 || cols < 128 || cols % 128) return MOE_ERR_ARG;
+  if (rows > 0 && (!src || !codes || !exps)) return MOE_ERR_ARG;
+  return launch_quant_act((const uint16_t*)src, rows, cols, codes, exps, (hipStream_t)stream);
+}
+
 int moe_predict_cost(const int32_t* counts, const int32_t* block_offsets,
                      const int32_t* block_worker_fwd, const int32_t* block_worker_bwd,
                      const int32_t* owner, int E, int beta, int P, int d, int d_ff,
@@ -237,9 +244,10 @@ int moe_predict_split(const int32_t* counts, const int32_t* block_offsets,
 
 // known bits only; a producer/consumer split only with the two-phase launch
 // (its upper bound, the workgroups of one worker, is checked at launch)
-static bool exec_flags_ok(int f) {
+static bool exec_flags_ok(int f, bool backward) {
   const int split = (f >> MOE_EXEC_SPLIT_SHIFT) & 0xff;
-  if (f & ~(MOE_EXEC_TWO_PHASE | MOE_EXEC_SPLIT(0xff))) return false;
+  const int known = MOE_EXEC_TWO_PHASE | MOE_EXEC_SPLIT(0xff) | (backward ? 0 : MOE_EXEC_FP8_ACT);
+  if (f & ~known) return false;
   return split == 0 || (f & MOE_EXEC_TWO_PHASE);
 }
 
@@ -251,7 +259,7 @@ int moe_forward(const moe_layer* L, const void* x, const float* gates, const int
                 void* const* stage_events, uint64_t* timeline, void* stream) {
   (void)topk_ids;
   const int lc = check_layer(L, false);
-  if (!exec_flags_ok(exec_flags)) return MOE_ERR_ARG;
+  if (!exec_flags_ok(exec_flags, false)) return MOE_ERR_ARG;
   if (lc != MOE_OK) return lc;
   if (!sizes_ok(T, k, L->E, beta)) return MOE_ERR_ARG;
   if (!valid_P(P)) return MOE_ERR_UNSUPPORTED;
@@ -260,6 +268,11 @@ int moe_forward(const moe_layer* L, const void* x, const float* gates, const int
     return MOE_ERR_ARG;
   const Sizes z = make_sizes(L, T, k, beta, P, 0);
   if (!extents_ok(z)) return MOE_ERR_UNSUPPORTED;
+  // the fp8 MFMA forward: bf16 x, e4m3 weights on the stream kernels, two launches
+  if ((exec_flags & MOE_EXEC_FP8_ACT) &&
+      (L->act_dtype != MOE_BF16 || L->w_dtype != MOE_FP8_E4M3 || !use_stream(z) ||
+       (exec_flags & MOE_EXEC_TWO_PHASE)))
+    return MOE_ERR_ARG;
   if (!ws_ok(ws, ws_bytes, exec_layout(z, false).total)) return MOE_ERR_WORKSPACE;
   LayerPtrs Lp{L->w1, L->w2, L->w1_scale, L->w2_scale, L->act_dtype, L->w_dtype};
   return launch_forward(z, Lp, x, gates, counts, block_offsets, row_to_slot, slot_to_row,
@@ -276,7 +289,7 @@ int moe_backward(const moe_layer* L, const void* x, const float* gates, const vo
                  void* const* stage_events, uint64_t* timeline, void* stream) {
   (void)topk_ids;
   const int lc = check_layer(L, true);
-  if (!exec_flags_ok(exec_flags)) return MOE_ERR_ARG;
+  if (!exec_flags_ok(exec_flags, true)) return MOE_ERR_ARG;
   if (lc != MOE_OK) return lc;
   if (!sizes_ok(T, k, L->E, beta) || s < 0) return MOE_ERR_ARG;
   if (!valid_P(P)) return MOE_ERR_UNSUPPORTED;

@@ -246,6 +246,8 @@ struct ExecArgs {
   float* dqs;             //   its scales [slots / beta][d]
   uint8_t* zq;            //   dZ, e4m3 [slots][2 d_ff]
   float* zqs;             //   its scales [slots / beta][2 d_ff]
+  const void* xq;         // fp8 MFMA forward: x codes [T][d] and exponents [d/128][T]
+  const int32_t* xe;
   void* dhat;             // fp8 backward on the stream kernels: D requantized and
                           //   widened back to bf16, [slots][d]
   const int32_t* boff;    // block offsets [E + 1]: boff[E] blocks of beta slots are in use
@@ -647,6 +649,46 @@ int launch_quant_tok(const uint16_t* src, int ld, const int32_t* map, int gather
     hipLaunchKernelGGL(k_quant_tok<false>, quant_grid(rows, cols, brows), dim3(256), 0, st, src, ld,
                        map, gather, div, rscale, map_lim, rows, cols, brows, codes, scales, nullptr,
                        blk_end);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// ---- activation rows for the fp8 MFMA (power-of-two block scales) ------------
+// Each row of x [rows][cols] (bf16) is cut into blocks of 128 features; block
+// b of row r gets e = the smallest integer with amax <= 448 * 2^e (clamped to
+// [-127, 127]; -127 for a zero block) and codes e4m3(x * 2^-e).  With amax =
+// M * 2^E (M in [1, 2)) and 448 = 1.75 * 2^8 that is e = E - 8, or E - 7 when
+// M > 1.75 (mantissa field above 0x600000).  One wave per (row, block), two
+// values per lane; exps is block-major, exps[b * rows + r], so a GEMM step
+// (one block) reads the exponents of its rows from one array row.
+__global__ __launch_bounds__(256) void k_quant_act(const uint16_t* __restrict__ x, int rows,
+                                                   int cols, uint8_t* __restrict__ codes,
+                                                   int32_t* __restrict__ exps) {
+  const int nb = cols / 128;
+  const long long task = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (task >= (long long)rows * nb) return;                  // whole waves
+  const int r = (int)(task / nb), b = (int)(task % nb), lane = threadIdx.x & 63;
+  const size_t off = (size_t)r * cols + (size_t)b * 128 + 2 * lane;
+  const uint32_t w = *(const uint32_t*)(x + off);
+  const float v0 = __uint_as_float(w << 16), v1 = __uint_as_float(w & 0xFFFF0000u);
+  float m = fmaxf(fabsf(v0), fabsf(v1));
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) m = fmaxf(m, __shfl_xor(m, sh, 64));
+  const uint32_t bits = __float_as_uint(m);
+  const int E = (int)((bits >> 23) & 0xFF) - 127;
+  int e = (bits & 0x7FFFFFFFu) == 0 ? -127 : E - 8 + ((bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  const float s0 = ldexpf(v0, -e), s1 = ldexpf(v1, -e);     // exact: powers of two
+  const int p = __builtin_amdgcn_cvt_pk_fp8_f32(s0, s1, 0, false);
+  *(uint16_t*)(codes + off) = (uint16_t)(p & 0xFFFF);
+  if (lane == 0) exps[(size_t)b * rows + r] = e;
+}
+
+int launch_quant_act(const uint16_t* x, int rows, int cols, uint8_t* codes, int32_t* exps,
+                     hipStream_t st) {
+  const long long tasks = (long long)rows * (cols / 128);
+  if (tasks > 0)
+    hipLaunchKernelGGL(k_quant_act, dim3((unsigned)((tasks + 3) / 4)), dim3(256), 0, st, x, rows,
+                       cols, codes, exps);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -1127,6 +1169,54 @@ template <bool FP8, bool COH = false> struct SrcFc1T : MSrcBase {
       }
     }
   }
+};
+
+// FC1 on the fp8 MFMA (MOE_EXEC_FP8_ACT, e4m3 weights): the A rows are x
+// quantized per token row and 128 features with power-of-two scales
+// (k_quant_act: codes in xq, exponents in xe), the B rows the weights' codes
+// as stored; a K step is 128 codes (one weight scale block), the row
+// exponents ride in the MFMA's scale operand and the weights' fp32 block
+// scales are applied to the accumulators per step (WideStream's fp8 mode).
+// The epilogue is FC1's.
+constexpr size_t kScOff8 = kStreamLds;           // two 1 KB exponent regions after the scratch
+constexpr size_t kStreamLds8 = kStreamLds + 2 * 1024;
+using RowA8 = RowK8A<256, kWNW, kScOff8>;
+using RowW8 = RowK8W<256, kWNW>;
+struct SrcFc1F8 : SrcFc1T<true> {
+  using OB = RowW8;
+  MOE_DEV RowA8 opA(const Item& it, int slot) const {
+    const MOE_LDS int* rows = item_rows(smem, slot);
+    using RB = typename RowA8::Base;
+    int o[RB::NI];
+#pragma unroll
+    for (int i = 0; i < RB::NI; ++i) {
+      const int row = RB::lane_row(i);   // element offsets of bf16 pairs: token * d / 2
+      o[i] = row < it.nrows ? (int)token_of((uint32_t)rows[row], a.kmagic) * (a.d / 2) : -1;
+    }
+    RowA8 x;
+    x.init_offsets((const uint16_t*)a.xq, (uint32_t)((size_t)a.T * a.d), o);
+    const int w = wave_id(), row = w * 64 + (threadIdx.x & 63);
+    x.rsc = make_rsrc(a.xe, (uint32_t)((size_t)(a.d / 128) * a.T * 4));
+    x.scs = (uint32_t)a.T * 4u;
+    x.sco = (w < 4 && row < it.nrows) ? token_of((uint32_t)rows[row], a.kmagic) * 4u : kOob;
+    return x;
+  }
+  MOE_DEV RowW8 opB(const Item& it, int) const {
+    RowW8 w;
+    const int dff = a.dff, nj = it.nj;
+    auto row = [&](int rho) {           // element offsets of code pairs: row * d / 2
+      const int q = rho >> 5;
+      return ((q & 1) * dff + nj * (WC::BN / 2) + (q >> 1) * 32 + (rho & 31)) * (a.d / 2);
+    };
+    w.init((const uint16_t*)((const uint8_t*)a.w1 + (size_t)it.e * 2 * dff * a.d),
+           (uint32_t)((size_t)2 * dff * a.d), row);
+    const int kb = a.d / 128;
+    const MOE_CONST float* sc = (const MOE_CONST float*)a.w1s + (size_t)it.e * (2 * dff / 128) * kb;
+    w.sp[0] = sc + (size_t)nj * kb;
+    w.sp[1] = sc + (size_t)(dff / 128 + nj) * kb;
+    return w;
+  }
+  MOE_DEV int steps(const Item&) const { return a.d / 128; }
 };
 
 // FC2 with the gate: O[slot] = p * A W2^T.  With e4m3 weights a wave's 64
@@ -1824,7 +1914,11 @@ WsLayout exec_layout(const Sizes& z, bool backward) {
   L.rslots = backward ? take(sizeof(float) * (size_t)z.P * z.s * 3 * z.d * z.dff) : o;
   L.bufP = backward ? take((size_t)z.act_bytes * z.max_slots * z.dff) : o;
   L.sgate = take(sizeof(float) * z.max_slots);
-  L.dq = L.dqs = L.zq = L.zqs = L.dhat = o;
+  L.dq = L.dqs = L.zq = L.zqs = L.dhat = L.xq = L.xe = o;
+  if (!backward && z.fp8 && use_stream(z)) {      // MOE_EXEC_FP8_ACT
+    L.xq = take((size_t)z.T * z.d);
+    L.xe = take(sizeof(int32_t) * (size_t)(z.d / 128) * z.T);
+  }
   if (backward && z.fp8 && use_stream(z)) {
     L.dhat = take((size_t)2 * z.max_slots * z.d);           // requantized D as bf16
   } else if (backward && z.fp8) {
@@ -1939,6 +2033,8 @@ static ExecArgs make_exec(const Sizes& z, const LayerPtrs& Lp, char* ws, const W
   a.sgate = (const float*)(ws + L.sgate);
   a.kmagic = (uint32_t)((((uint64_t)1 << 32) + (uint64_t)z.k - 1) / (uint64_t)z.k);
   if (z.fp8) {
+    a.xq = ws + L.xq;
+    a.xe = (const int32_t*)(ws + L.xe);
     a.dq = (uint8_t*)(ws + L.dq);
     a.dqs = (float*)(ws + L.dqs);
     a.zq = (uint8_t*)(ws + L.zq);
@@ -2021,11 +2117,18 @@ static int exec_split(int exec_flags, int P, bool* two_launches) {
 
 template <bool FP8>
 static void run_forward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* y,
-                               bool split, int n1split, void* const* ev, hipStream_t st) {
+                               bool split, int n1split, bool f8act, void* const* ev,
+                               hipStream_t st) {
   launch_slot_gate(z, a, st);
   const int n1 = z.dff / (WC::BN / 2), n2 = z.d / WC::BN;
   a.tl_phase = MOE_TL_FC1;
-  if (split) {
+  if (FP8 && f8act) {                  // x quantized per row block, FC1 on the fp8 MFMA
+    launch_quant_act((const uint16_t*)a.x, z.T, z.d, (uint8_t*)a.xq, (int32_t*)a.xe, st);
+    launch_stream<SrcFc1F8, WC, RowA8, RowW8>(a, n1, kStreamLds8, st);
+    rec(ev, 2, st);
+    a.tl_phase = MOE_TL_FC2;
+    launch_stream<SrcFc2T<FP8>, WC, RowW, typename SrcFc2T<FP8>::OB>(a, n2, kStreamLds, st);
+  } else if (split) {
     launch_stream<SrcFc1T<FP8>, WC, RowW, typename SrcFc1T<FP8>::OB>(a, n1, kStreamLds, st);
     rec(ev, 2, st);
     a.tl_phase = MOE_TL_FC2;
@@ -2050,6 +2153,10 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
   bool split = true;
   const int n1split = exec_split(exec_flags, z.P, &split);
   if (n1split < 0) return MOE_ERR_ARG;
+  // the fp8 MFMA forward: e4m3 weights on the stream kernels, two launches
+  if ((exec_flags & MOE_EXEC_FP8_ACT) &&
+      (Lp.act_dtype != MOE_BF16 || Lp.w_dtype != MOE_FP8_E4M3 || !use_stream(z) || !split))
+    return MOE_ERR_ARG;
   const WsLayout L = exec_layout(z, false);
   rec(ev, 0, st);
   launch_sched(z, counts, boff, block_worker, nullptr, false, ws, L, status, st);
@@ -2060,10 +2167,11 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
   a.timeline = timeline;
   a.status = status;
   const bool big = use_big_tiles(z);
+  const bool f8act = (exec_flags & MOE_EXEC_FP8_ACT) != 0;
   if (Lp.act_dtype == MOE_BF16 && Lp.w_dtype == MOE_BF16 && use_stream(z))
-    run_forward_stream<false>(z, a, row_to_slot, y, split, n1split, ev, st);
+    run_forward_stream<false>(z, a, row_to_slot, y, split, n1split, false, ev, st);
   else if (Lp.act_dtype == MOE_BF16 && Lp.w_dtype == MOE_FP8_E4M3 && use_stream(z))
-    run_forward_stream<true>(z, a, row_to_slot, y, split, n1split, ev, st);
+    run_forward_stream<true>(z, a, row_to_slot, y, split, n1split, f8act, ev, st);
   else if (Lp.act_dtype == MOE_F32) run_forward<float, false, SmallCfg>(z, a, row_to_slot, y, ev, st);
   else if (Lp.w_dtype == MOE_FP8_E4M3) {
     if (big) run_forward<uint16_t, true, BigCfg>(z, a, row_to_slot, y, ev, st);

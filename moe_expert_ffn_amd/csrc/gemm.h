@@ -681,6 +681,81 @@ template <int ROWS, int NWAVES, int BK_> struct RowKFp8 {
   }
 };
 
+// ---- e4m3 x e4m3 on the fp8 MFMA ------------------------------------------------
+// v_mfma_scale_f32_32x32x64_f8f6f4 (probed on MI355X): lane l holds row l % 32
+// of its operand; its bytes 0..15 are K 16 (l / 32) + 0..15 of the 64 and
+// bytes 16..31 are K 32 + 16 (l / 32) + 0..15; the power-of-two scale of K
+// block b (32 wide) of row i comes from lane i + 32 b, byte op_sel.
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// K-contiguous e4m3 rows for the fp8 MFMA: 128 codes (one K step of 128) per
+// row and stage, loaded, laid out and swizzled exactly like a bf16 RowK row of
+// 64 elements.  Fragment c (K 64 c .. 64 c + 63) of block i is the lane's
+// 16-byte chunks 4c + h and 4c + 2 + h (h = lane / 32): RowK's fragments 2c
+// and 2c + 1, which gives the MFMA's K order for A and B alike.
+template <int ROWS, int NWAVES> struct RowK8 : RowK<ROWS, NWAVES, 64> {
+  static constexpr bool kF8Mma = true;
+  using Base = RowK<ROWS, NWAVES, 64>;
+  template <int C> static MOE_DEV i32x8_t frag8(const MOE_LDS char* st, const typename Base::Lane& L, int i) {
+    typedef int i32x4_t __attribute__((ext_vector_type(4)));
+    const i32x4_t lo = __builtin_bit_cast(i32x4_t, Base::template frag<2 * C>(st, L, i));
+    const i32x4_t hi = __builtin_bit_cast(i32x4_t, Base::template frag<2 * C + 1>(st, L, i));
+    return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+};
+
+// Weight rows (the MFMA's first operand) with 128 x 128 fp32 block scales: a
+// wave's 32-row block j and a K step lie in one scale block, sp[j & 1][kt].
+template <int ROWS, int NWAVES> struct RowK8W : RowK8<ROWS, NWAVES> {
+  const MOE_CONST float* sp[2];
+  MOE_DEV float scale(int j, int kt) const { return sp[j & 1][kt]; }
+};
+
+// Activation rows (the MFMA's second operand) with one power-of-two exponent
+// per row and K step: exps [K steps][T] int32 (block-major), row r of the tile
+// reading token t_r.  Waves 0 .. ROWS / 64 - 1 each move the exponents of 64
+// rows into the stage's 1 KB exponent region (SC_OFF + stage * 1024 in LDS)
+// with one dword direct load; a row past the item reads zero (scale 2^0,
+// with zero codes).
+template <int ROWS, int NWAVES, size_t SC_OFF> struct RowK8A : RowK8<ROWS, NWAVES> {
+  static constexpr size_t kScOff = SC_OFF;
+  static constexpr int kScRegion = 1024;
+  static_assert(ROWS * 4 <= kScRegion, "exponent region");
+  using Base = RowK<ROWS, NWAVES, 64>;
+  BufRsrc rsc;
+  uint32_t sco;          // this lane's exponent row: t_r * 4, or kOob
+  uint32_t scs;          // bytes per K step: T * 4
+  struct Offs { uint32_t o[Base::NI]; uint32_t s; };
+  MOE_DEV Offs prep(int kt) const {
+    Offs q;
+#pragma unroll
+    for (int i = 0; i < Base::NI; ++i) q.o[i] = this->off[i] + (uint32_t)kt * Base::RB;
+    q.s = sco == kOob ? kOob : sco + (uint32_t)kt * scs;
+    return q;
+  }
+  MOE_DEV void issue(const Offs& q, MOE_LDS char* st) const {
+    typename Base::Offs b;
+#pragma unroll
+    for (int i = 0; i < Base::NI; ++i) b.o[i] = q.o[i];
+    Base::issue(b, st);
+  }
+  MOE_DEV void issue_sc(const Offs& q, MOE_LDS char* region) const {
+    const int w = wave_id();
+    if (w < ROWS / 64)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (MOE_LDS void*)(region + w * 256), 4, q.s, 0, 0, 0);
+  }
+  // the lane's four rows wave_base + 32 i + lane % 32 as E8M0 bytes (e + 127), byte i
+  static MOE_DEV uint32_t scale_word(const MOE_LDS char* region, int wave_base, int lane) {
+    const MOE_LDS int32_t* e = (const MOE_LDS int32_t*)region + wave_base + (lane & 31);
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w |= ((uint32_t)(e[32 * i] + 127) & 0xFFu) << (8 * i);
+    return w;
+  }
+};
+template <class T, class = void> struct op_f8mma { static constexpr bool value = false; };
+template <class T> struct op_f8mma<T, decltype((void)T::kF8Mma)> { static constexpr bool value = T::kF8Mma; };
+
 // 8 e4m3 codes (bytes of q, low first) times s, as bf16 rounded to nearest even.
 MOE_DEV bf16x8_t dequant8(const u32x2_t& q, float s) {
   bf16x8_t o;
@@ -927,7 +1002,10 @@ template <class OP, class F> struct MnKOperand {
 template <class C, class OA, class OB, bool ROWS_IN_REGS = false> struct WideStream {
   static constexpr int BK = OA::BK;
   static_assert(OB::BK == BK, "one K step for both operands");
-  static constexpr int S = wide_stages(BK), NCH = BK / 16;
+  // e4m3 rows on both sides (kF8Mma): the fp8 MFMA, a K step of 128 codes in
+  // two 64-wide chunks
+  static constexpr bool F8M = op_f8mma<OB>::value;
+  static constexpr int S = wide_stages(BK), NCH = F8M ? 2 : BK / 16;
   static_assert(S >= 2 && (S & (S - 1)) == 0 && (NCH == 2 || NCH == 4), "stage shape");
   static constexpr int SA = OA::STAGE_BYTES, STAGE = OA::STAGE_BYTES + OB::STAGE_BYTES;
   static_assert((size_t)S * STAGE <= kWideLdsStages, "stages fit");
@@ -937,9 +1015,60 @@ template <class C, class OA, class OB, bool ROWS_IN_REGS = false> struct WideStr
   // an e4m3 B operand keeps its raw codes in bq and is widened in mma()
   static constexpr bool BF8 = op_fp8<OB>::value;
   static_assert(!BF8 || C::NB == 2, "e4m3 operand: two 32-row blocks per wave");
+  static_assert(!F8M || (op_f8mma<OA>::value && C::MB == 4 && C::NB == 2 && !ROWS_IN_REGS),
+                "fp8 MFMA: e4m3 rows on both sides, the 8-wave tile");
   bf16x8_t a[2][C::MB], b[2][C::NB];
   u32x2_t bq[2][C::NB];
   float bs[C::NB];                                // B scales of the current step
+  // fp8 MFMA: one fragment set (32 bytes a lane each), the E8M0 exponents of
+  // the lane's four rows for the current step, and per block j the scale the
+  // accumulators are counted in (seff: acc * seff is the running sum) with
+  // this step's factor seff_old / scale and whether the block is nonzero
+  i32x8_t a8[C::MB], b8[C::NB];
+  uint32_t sa8;
+  float seff[C::NB], rat[C::NB];
+  bool live[C::NB];
+  template <int CC> MOE_DEV void read8(const MOE_LDS char* st) {
+#pragma unroll
+    for (int i = 0; i < C::MB; ++i) a8[i] = OA::template frag8<CC>(st, la, i);
+#pragma unroll
+    for (int j = 0; j < C::NB; ++j) b8[j] = OB::template frag8<CC>(st + SA, lb, j);
+  }
+  template <int I>
+  static MOE_DEV f32x16_t mfma8(const i32x8_t& w, const i32x8_t& x, const f32x16_t& c, uint32_t sx) {
+    // first operand: weight rows, scale 2^0; second: activation rows, the
+    // E8M0 byte I of sx (row block I of the lane)
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, x, c, 0, 0, 0, 127, I, (int)sx);
+  }
+  // chunk CC of the step; chunk 0 first rescales the accumulators to the
+  // step's weight scale (a block of zero scale adds nothing and keeps its scale)
+  template <int CC> MOE_DEV void mma8(f32x16_t (&acc)[C::MB][C::NB]) const {
+#pragma unroll
+    for (int j = 0; j < C::NB; ++j) {
+      if (!live[j]) continue;
+#pragma unroll
+      for (int i = 0; i < C::MB; ++i) {
+        if constexpr (CC == 0) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) acc[i][j][q] *= rat[j];
+        }
+        if (i == 0) acc[i][j] = mfma8<0>(b8[j], a8[i], acc[i][j], sa8);
+        else if (i == 1) acc[i][j] = mfma8<1>(b8[j], a8[i], acc[i][j], sa8);
+        else if (i == 2) acc[i][j] = mfma8<2>(b8[j], a8[i], acc[i][j], sa8);
+        else acc[i][j] = mfma8<3>(b8[j], a8[i], acc[i][j], sa8);
+      }
+    }
+  }
+  // this step's weight scales bs: rescaling factors and live blocks
+  MOE_DEV void step_scales() {
+#pragma unroll
+    for (int j = 0; j < C::NB; ++j) {
+      const float sc = bs[j];
+      live[j] = sc != 0.f;
+      rat[j] = live[j] ? seff[j] / sc : 1.f;
+      if (live[j]) seff[j] = sc;
+    }
+  }
   typename OA::Lane la;
   typename OB::Lane lb;
   template <int KC, int SB> MOE_DEV void read(const MOE_LDS char* st) {
@@ -978,6 +1107,11 @@ template <class C, class OA, class OB, bool ROWS_IN_REGS = false> struct WideStr
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_sched_barrier(0);
   }
+  // LDS offset of a stage's row-exponent region (fp8 MFMA)
+  static MOE_DEV size_t sc_region(int stage) {
+    if constexpr (F8M) return OA::kScOff + (size_t)stage * OA::kScRegion;
+    else return 0;
+  }
   template <class Src>
   MOE_DEV void run(Src& src, MOE_LDS uint16_t* smem16, f32x16_t (&acc)[C::MB][C::NB]) {
     MOE_LDS char* smem = (MOE_LDS char*)smem16;
@@ -1009,6 +1143,7 @@ template <class C, class OA, class OB, bool ROWS_IN_REGS = false> struct WideStr
       const auto pb = b0.prep(st);
       a0.issue(pa, smem + st * STAGE);
       b0.issue(pb, smem + st * STAGE + SA);
+      if constexpr (F8M) a0.issue_sc(pa, smem + sc_region(st));
     }
     // two-phase sources: the last finished item not yet published (its
     // epilogue stores are published at the next strict wait; -1: none)
@@ -1017,16 +1152,28 @@ template <class C, class OA, class OB, bool ROWS_IN_REGS = false> struct WideStr
     // issued; the full wait ending that step covers the load
     int peeked = -1;
     float bsn[C::NB];                            // B scales of the next step
-    if constexpr (BF8) {
+    if constexpr (BF8 || F8M) {
 #pragma unroll
       for (int j = 0; j < C::NB; ++j) bsn[j] = b0.scale(j, 0);
     }
+    if constexpr (F8M) {
+#pragma unroll
+      for (int j = 0; j < C::NB; ++j) seff[j] = 0.f;
+    }
+    const int wrow = (wave_id() / C::WAVES_N) * C::WM;
     wait_vm_lgkm0<(S - 1) * LPS>();
     __builtin_amdgcn_s_barrier();
     constexpr bool SKIP = src_skip_idle<Src>::value;
     bool act = true;                             // this wave has rows in item it0
     if constexpr (SKIP) act = src.wave_active(it0);
-    if (act) read<0, 0>(smem);
+    if (act) {
+      if constexpr (F8M) {
+        read8<0>(smem);
+        sa8 = OA::scale_word(smem + sc_region(0), wrow, lane);
+      } else {
+        read<0, 0>(smem);
+      }
+    }
     int g = 0;                                   // global step index: stage g % S
     while (true) {
       const int s1 = slot == 2 ? 0 : slot + 1, s2 = s1 == 2 ? 0 : s1 + 1;
@@ -1045,19 +1192,37 @@ template <class C, class OA, class OB, bool ROWS_IN_REGS = false> struct WideStr
           for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
       // the item's first step landed before the previous item's last barrier
       if constexpr (SKIP) act = src.wave_active(it0);
-      if (g > 0 && act) read<0, 0>(smem + (g & (S - 1)) * STAGE);
+      if (g > 0 && act) {
+        if constexpr (F8M) {
+          read8<0>(smem + (g & (S - 1)) * STAGE);
+          sa8 = OA::scale_word(smem + sc_region(g & (S - 1)), wrow, lane);
+        } else {
+          read<0, 0>(smem + (g & (S - 1)) * STAGE);
+        }
+      }
       // During its first S-1 steps, the loads an item waits for were issued
       // before the previous item's epilogue, so the epilogue's stores (and
       // loads) may stay in flight: they drain under those steps.
       const bool relax = g > 0;
       for (int kt = 0; kt < n0; ++kt, ++g) {
         const MOE_LDS char* st = smem + (g & (S - 1)) * STAGE;
-        if constexpr (BF8) {
+        if constexpr (BF8 || F8M) {
 #pragma unroll
           for (int j = 0; j < C::NB; ++j) bs[j] = bsn[j];
         }
-        lgkm0();
-        if (act) read<1, 1>(st);
+        if constexpr (F8M) {
+          // single fragment set: chunk 0's MFMAs, then chunk 1's reads into
+          // the same registers (landed by the step-end wait)
+          step_scales();
+          lgkm0();
+          __builtin_amdgcn_sched_barrier(0);
+          if (act) mma8<0>(acc);
+          __builtin_amdgcn_sched_barrier(0);
+          if (act) read8<1>(st);
+        } else {
+          lgkm0();
+          if (act) read<1, 1>(st);
+        }
         // step g + S of the stream: this item, the next one, or a harmless
         // re-read of this item's last step when the stream ends
         const bool own = kt + S < n0;
@@ -1067,14 +1232,16 @@ template <class C, class OA, class OB, bool ROWS_IN_REGS = false> struct WideStr
         const auto pb = nxt ? b1.prep(ks) : b0.prep(ks);
         // B scales of the next step (or of the next item's first), scalar
         // loads that land by the next chunk's wait
-        if constexpr (BF8) {
+        if constexpr (BF8 || F8M) {
 #pragma unroll
           for (int j = 0; j < C::NB; ++j)
             bsn[j] = kt + 1 < n0 ? b0.scale(j, kt + 1) : h1 ? b1.scale(j, 0) : bs[j];
         }
-        __builtin_amdgcn_sched_barrier(0);
-        if (act) mma<0>(acc);
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!F8M) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (act) mma<0>(acc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if constexpr (NCH == 4) {
           lgkm0();
           if (act) read<2, 0>(st);
@@ -1104,19 +1271,44 @@ template <class C, class OA, class OB, bool ROWS_IN_REGS = false> struct WideStr
         if (nxt) {
           a1.issue(pa, smem + (g & (S - 1)) * STAGE);
           b1.issue(pb, smem + (g & (S - 1)) * STAGE + SA);
+          if constexpr (F8M) a1.issue_sc(pa, smem + sc_region(g & (S - 1)));
         } else {
           a0.issue(pa, smem + (g & (S - 1)) * STAGE);
           b0.issue(pb, smem + (g & (S - 1)) * STAGE + SA);
+          if constexpr (F8M) a0.issue_sc(pa, smem + sc_region(g & (S - 1)));
         }
         if constexpr (FLOW) {
           if (h1 && kt + S + 1 == n0) peeked = src.peek(it1);
         }
-        // chunk 0 of the next step; for the next item it is read after the
-        // epilogue, so its fragments are not live across it
-        if (kt + 1 < n0 && act) read<0, 0>(smem + ((g + 1) & (S - 1)) * STAGE);
-        __builtin_amdgcn_sched_barrier(0);
-        if (act) mma<1>(acc);
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (F8M) {
+          // chunk 1's MFMAs, then chunk 0 of the next step (and its row
+          // exponents) into the registers they have read
+          __builtin_amdgcn_sched_barrier(0);
+          if (act) mma8<1>(acc);
+          __builtin_amdgcn_sched_barrier(0);
+          if (kt + 1 < n0 && act) {
+            read8<0>(smem + ((g + 1) & (S - 1)) * STAGE);
+            sa8 = OA::scale_word(smem + sc_region((g + 1) & (S - 1)), wrow, lane);
+          }
+        } else {
+          // chunk 0 of the next step; for the next item it is read after the
+          // epilogue, so its fragments are not live across it
+          if (kt + 1 < n0 && act) read<0, 0>(smem + ((g + 1) & (S - 1)) * STAGE);
+          __builtin_amdgcn_sched_barrier(0);
+          if (act) mma<1>(acc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if constexpr (F8M) {
+        // back from units of the last scale to values; the next item starts over
+#pragma unroll
+        for (int j = 0; j < C::NB; ++j) {
+#pragma unroll
+          for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] *= seff[j];
+          seff[j] = 0.f;
+        }
       }
       src.epilogue(it0, slot, acc);
       if constexpr (FLOW) pend = src.publish_key(it0);

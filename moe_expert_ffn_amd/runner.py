@@ -33,6 +33,8 @@ class LayerRunner:
         # launch (0: every workgroup runs both phases)
         self.split_fwd = 0
         self.split_bwd = 0
+        # e4m3 weights: FC1 on the fp8 MFMA with x quantized per row block
+        self.fp8_act = False
         self.owner = owner.to(device=dev, dtype=torch.int32).contiguous()
         self.with_backward = with_backward
         self.ws = B.workspace(self.layer, T, k, beta, P, s, with_backward, dev)
@@ -70,7 +72,8 @@ class LayerRunner:
     def forward(self, x, gates, topk_ids, block_worker=None, events=None, timeline=None):
         bw = self.plan_f["block_worker"] if block_worker is None else block_worker
         B.forward(self.layer, x, gates, topk_ids, self.beta, self.P, self.rs, bw, self.y, self.z,
-                  self.ws, self.status, events, timeline, self.two_phase, self.split_fwd)
+                  self.ws, self.status, events, timeline, self.two_phase, self.split_fwd,
+                  self.fp8_act)
         return self.y
 
     def backward(self, x, gates, dy, topk_ids, block_worker=None, events=None, timeline=None):

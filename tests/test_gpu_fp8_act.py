@@ -1,0 +1,169 @@
+"""GPU parity of the fp8 MFMA forward (MOE_EXEC_FP8_ACT) and its activation
+quantizer.
+
+- The quantizer (moe_quantize_act_rows) is bit-exact against the oracle's
+  power-of-two row blocks: codes and exponents.
+- The forward is checked two ways:
+  - against the oracle run on the quantized x (its dequantized values), where
+    only accumulation order and the bf16 roundings differ: saved [G, U] within
+    1e-2, y within 2e-2;
+  - against the exact oracle (bf16 x, dequantized weights) within the e4m3
+    bar of 6e-2.
+- Placement does not change a bit. A zero weight-scale block adds nothing.
+"""
+import numpy as np
+import pytest
+import torch
+
+from moe_expert_ffn_amd import binding as B
+from moe_expert_ffn_amd.inputs import WORKLOADS, Workload
+from oracle import ffn as offn
+from oracle.fp8 import dequant_row_blocks_pow2, quantize_row_blocks_pow2
+from oracle.route import route_stats as oracle_route
+from tests.conftest import rel_l2
+from tests.gpu_util import Case, say
+
+pytestmark = pytest.mark.gpu
+
+TOL_MODEL_Z = 1e-2      # [G, U] against the oracle on the quantized x (bf16 storage)
+TOL_MODEL_Y = 2e-2      # y against the same
+TOL_EXACT = 6e-2        # y against the exact oracle (the e4m3 bar)
+
+SMALL = {
+    # one tile each way, ragged blocks
+    "small_fp8": Workload("small_fp8", "bf16", "fp8", T=160, k=2, E=8, d=256, d_ff=256,
+                          beta=128, P=4, s=2, kappas=(0,), cfg_id=15),
+    # several tiles each way, replicas, a K loop of 4 steps
+    "stream_fp8": Workload("stream_fp8", "bf16", "fp8", T=700, k=4, E=8, d=512, d_ff=512,
+                           beta=128, P=8, s=4, kappas=(0,), cfg_id=18),
+}
+
+
+def _xhat(x):
+    """The oracle's quantize-dequantize of x's rows (fp64)."""
+    xf = x.float().cpu().numpy()
+    codes, exps = quantize_row_blocks_pow2(xf)
+    return dequant_row_blocks_pow2(codes, exps)
+
+
+def _run(c, fp8_act=True, s=None):
+    r = c.runner
+    r.fp8_act = fp8_act
+    r.status.zero_()
+    r.step(c.x, c.gates, c.ids, s=s)
+    torch.cuda.synchronize()
+    assert c.status() == 0
+    return r.y.clone()
+
+
+def test_quantize_act_rows_matches_oracle():
+    g = torch.Generator(device="cuda").manual_seed(5)
+    rows, cols = 300, 1024
+    x = torch.randn(rows, cols, device="cuda", generator=g)
+    x *= torch.pow(10.0, torch.empty(rows, 1, device="cuda").uniform_(-6, 6, generator=g))
+    x[7, 256:384] = 0.0                                  # a zero block
+    x[9] = 0.0                                           # a zero row
+    x[11, :128] *= 1e-3
+    x[11, 5] = 448.0 * 2.0 ** 3                          # amax exactly on a binade edge
+    x[12, 130] = -3.0e38                                 # near the top of the range
+    xb = x.to(torch.bfloat16).contiguous()
+    codes = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
+    exps = torch.empty(cols // 128, rows, dtype=torch.int32, device="cuda")
+    B.quantize_act_rows(xb, codes, exps)
+    torch.cuda.synchronize()
+    rc, re = quantize_row_blocks_pow2(xb.float().cpu().numpy())
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+    np.testing.assert_array_equal(exps.cpu().numpy(), re.T)
+    assert int(exps[2, 7]) == -127 and int(exps[0, 11]) == 3
+
+
+def _z_check(c, zg):
+    """Saved [G, U] of every routed row against the oracle on the quantized x."""
+    x, w1, w2, ids, gates = c.oracle_inputs()
+    xh = _xhat(c.x)
+    _, zs = offn.forward(xh, w1, w2, ids, gates, return_z=True)
+    rs = oracle_route(ids, c.w.E, c.w.beta)
+    got, ref = [], []
+    for e, (toks, j, z) in zs.items():
+        got.append(zg[rs["row_to_slot"][toks * c.w.k + j]])
+        ref.append(z)
+    return rel_l2(np.concatenate(got), np.concatenate(ref))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fp8_act_forward_parity(name):
+    w = SMALL[name]
+    say(f"[fp8-act] {name}")
+    c = Case(w, 0, backward=True)          # a backward-capable runner keeps [G, U]
+    y0 = _run(c, fp8_act=False)
+    y = _run(c)
+    x, w1, w2, ids, gates = c.oracle_inputs()
+    ez = _z_check(c, c.runner.z.double().cpu().numpy())
+    ym = rel_l2(y.double().cpu().numpy(), offn.forward(_xhat(c.x), w1, w2, ids, gates))
+    ye = rel_l2(y.double().cpu().numpy(), offn.forward(x, w1, w2, ids, gates))
+    moved = rel_l2(y.double().cpu().numpy(), y0.double().cpu().numpy())
+    say(f"  z vs quantized-x oracle {ez:.3e}, y {ym:.3e}; y vs exact {ye:.3e}; "
+        f"vs the bf16-x path {moved:.3e}")
+    assert ez <= TOL_MODEL_Z and ym <= TOL_MODEL_Y and ye <= TOL_EXACT
+    assert moved > 1e-4                    # the flag took the fp8 path
+    assert torch.isfinite(y.float()).all()
+
+
+def test_fp8_act_plan_invariance():
+    w = SMALL["stream_fp8"]
+    say("[fp8-act] plan invariance")
+    c = Case(w, 0)
+    y_plan = _run(c)
+    assert torch.equal(_run(c, s=0), y_plan)
+    assert torch.equal(_run(Case(w, 0, P=1, s=0)), y_plan)
+
+
+def test_fp8_act_zero_scale_block():
+    """A weight block whose scale is 0 contributes nothing; the blocks after
+    it keep their own scales."""
+    w = SMALL["stream_fp8"]
+    say("[fp8-act] zero weight-scale blocks")
+    c = Case(w, 0, backward=True)
+    c.w1s[1, 2, 0] = 0.0                   # expert 1, G rows 256..383, K 0..127
+    c.w1s[3, 5, 3] = 0.0                   # expert 3, U rows, the last K block
+    c.w1s[3, 5, 1] = 0.0
+    _run(c)
+    ez = _z_check(c, c.runner.z.double().cpu().numpy())
+    say(f"  z vs quantized-x oracle {ez:.3e}")
+    assert ez <= TOL_MODEL_Z
+
+
+@pytest.mark.parametrize("kappa", [1, 8])
+def test_fp8_act_full_size_sampled(kappa):
+    w = WORKLOADS["dsv3_fp8"]
+    say(f"[fp8-act] dsv3_fp8 kappa={kappa}")
+    c = Case(w, kappa)
+    y = _run(c)
+    rng = np.random.default_rng(kappa + 100)
+    tok = np.sort(rng.choice(c.T, size=48, replace=False))
+    x, w1, w2, ids, gates = c.oracle_inputs()
+    yt = y[tok].double().cpu().numpy()
+    ym = rel_l2(yt, offn.forward(_xhat(c.x), w1, w2, ids, gates, tokens=tok))
+    ye = rel_l2(yt, offn.forward(x, w1, w2, ids, gates, tokens=tok))
+    say(f"  y vs quantized-x oracle {ym:.3e}; vs exact {ye:.3e}")
+    assert ym <= TOL_MODEL_Y and ye <= TOL_EXACT
+    assert torch.isfinite(y.float()).all()
+
+
+def test_fp8_act_rejected_where_unsupported():
+    """bf16 weights, the two-phase launch and the backward refuse the flag."""
+    say("[fp8-act] refusals")
+    c = Case(SMALL["small_fp8"], 0)
+    r = c.runner
+    r.route(c.ids)
+    r.make_plan()
+    with pytest.raises(B.MoeError):
+        B.forward(r.layer, c.x, c.gates, c.ids, r.beta, r.P, r.rs, r.plan_f["block_worker"], r.y,
+                  r.z, r.ws, r.status, two_phase=True, fp8_act=True)
+    cb = Case(WORKLOADS["tiny_f32"], 0)
+    rb = cb.runner
+    rb.route(cb.ids)
+    rb.make_plan()
+    with pytest.raises(B.MoeError):
+        B.forward(rb.layer, cb.x, cb.gates, cb.ids, rb.beta, rb.P, rb.rs, rb.plan_f["block_worker"],
+                  rb.y, rb.z, rb.ws, rb.status, fp8_act=True)
