@@ -67,6 +67,38 @@ def forward(x, w1, w2, topk_ids, gates, tokens=None, return_z=False):
     return (y, zs) if return_z else y
 
 
+def forward_fp8act(x, w1, w2, topk_ids, gates, tokens=None, return_z=False):
+    """The forward of an e4m3-weight layer whose two products run on fp8
+    operands (reading of "per-1x128 e4m3 activations"): each row of x and each
+    row of A = SiLU(G) U is quantized in blocks of 128 features with
+    power-of-two scales (oracle.fp8.quantize_row_blocks_pow2) before the
+    product that reads it; the weights are as given (dequantized).  A is
+    formed from Z in fp64 and rounded to fp32 before its quantization (the
+    device quantizes its fp32 value).  The gated combine is forward's."""
+    from oracle.fp8 import dequant_row_blocks_pow2, quantize_row_blocks_pow2
+    x = np.asarray(x, dtype=np.float64)
+    xh = dequant_row_blocks_pow2(*quantize_row_blocks_pow2(x.astype(np.float32)))
+    ids = np.asarray(topk_ids)
+    p = np.asarray(gates, dtype=np.float64)
+    T, k = ids.shape
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    F = w1.shape[1] // 2
+    contrib = np.zeros((len(tokens), k, x.shape[1]))
+    zs = {}
+    for e, (ti, j) in _pairs_by_expert(ids, tokens).items():
+        z = xh[tokens[ti]] @ np.asarray(w1[e], dtype=np.float64).T
+        a = (silu(z[:, :F]) * z[:, F:]).astype(np.float32)
+        ah = dequant_row_blocks_pow2(*quantize_row_blocks_pow2(a))
+        o = ah @ np.asarray(w2[e], dtype=np.float64).T
+        contrib[ti, j] = p[tokens[ti], j][:, None] * o
+        if return_z:
+            zs[e] = (tokens[ti], j, z)
+    y = np.zeros((len(tokens), x.shape[1]))
+    for j in range(k):
+        y += contrib[:, j]
+    return (y, zs) if return_z else y
+
+
 def backward(x, w1, w2, topk_ids, gates, dy, tokens=None, experts=None):
     """Gradients of L = sum_t dy_t . y_t.
 

@@ -304,3 +304,72 @@ def test_fp8_backward_d_rows_are_token_axis_blocks_with_gates():
         j = np.nonzero(ids[t] == e)[1]                  # slot of expert e in each token
         d_exact = g[t, j].astype(np.float64)[:, None] * dy[t]     # D = p dy
         _check_token_blocks(b["dw2"][e][:, t].T / silu1, d_exact, beta)
+
+
+# ---- the fp8-operand forward (x and A quantized per row block of 128) ----------
+
+def _fp8act_identity_case():
+    """One token, one expert, d = d_ff = 128, where both quantizations are the
+    identity: x = 448 at feature 0 (a block maximum exactly 448 * 2^0) and
+    e4m3 values below it; G rows pick features so G = x[1..], U rows read
+    x[0] scaled so that A = SiLU(G) U lands exactly on chosen e4m3 values with
+    a block maximum of 448 * 2^-2."""
+    from oracle.fp8 import decode_e4m3
+    rng = np.random.default_rng(21)
+    grid = decode_e4m3(np.arange(0x08, 0x76, dtype=np.uint8))       # normal codes below 448
+    x = np.zeros((1, 128))
+    x[0, 0] = 448.0
+    x[0, 1:] = rng.choice(grid, 127) * rng.choice([-1, 1], 127)
+    w1 = np.zeros((1, 256, 128))
+    for jj in range(128):
+        w1[0, jj, 1 + jj % 127] = 1.0                               # G_j = x[1 + j % 127]
+    g = x[0, 1 + np.arange(128) % 127]
+    a_want = rng.choice(grid, 128) * 0.25
+    a_want[7] = 448.0 * 0.25                                        # the block maximum
+    sil = offn.silu(g)
+    for jj in range(128):
+        w1[0, 128 + jj, 0] = a_want[jj] / sil[jj] / 448.0           # U_j = a_j / SiLU(G_j)
+    w2 = rng.standard_normal((1, 128, 128))
+    return x, w1, w2, np.zeros((1, 1), dtype=np.int64), np.ones((1, 1)), a_want
+
+
+def test_forward_fp8act_is_forward_where_quantization_is_exact():
+    x, w1, w2, ids, gates, a_want = _fp8act_identity_case()
+    y8 = offn.forward_fp8act(x, w1, w2, ids, gates)
+    y = offn.forward(x, w1, w2, ids, gates)
+    np.testing.assert_allclose(y8, y, rtol=1e-12, atol=1e-9)
+    np.testing.assert_allclose(y8[0], w2[0] @ a_want, rtol=1e-12, atol=1e-9)
+
+
+def test_forward_fp8act_quantizes_a_per_block():
+    """Moving one A value off the e4m3 grid changes y by the rounding of that
+    value alone (its block's scale is unchanged), within half an e4m3 step;
+    the exact forward moves by the full offset."""
+    x, w1, w2, ids, gates, a_want = _fp8act_identity_case()
+    j = 40
+    v = a_want[j]
+    w1b = w1.copy()
+    off = abs(v) * 2.0 ** -6                                        # a sixteenth of v's own step
+    w1b[0, 128 + j, 0] *= (v + off) / v
+    y8 = offn.forward_fp8act(x, w1b, w2, ids, gates)
+    y = offn.forward(x, w1b, w2, ids, gates)
+    base = w2[0] @ a_want
+    np.testing.assert_allclose(y8[0], base, rtol=1e-12, atol=1e-9)   # rounded back onto the grid
+    np.testing.assert_allclose(y[0] - base, w2[0][:, j] * off, rtol=1e-6, atol=1e-9)
+
+
+def test_forward_fp8act_error_bound():
+    """On random data the fp8-operand forward stays within the e4m3
+    quantization bound of the exact one (two roundings of at most 2^-4
+    relative per value, plus one through SiLU)."""
+    rng = np.random.default_rng(22)
+    T, d, F, E, k = 40, 256, 128, 3, 2
+    x = rng.standard_normal((T, d))
+    w1 = rng.standard_normal((E, 2 * F, d)) / np.sqrt(d)
+    w2 = rng.standard_normal((E, d, F)) / np.sqrt(F)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    gates = rng.random((T, k))
+    y8 = offn.forward_fp8act(x, w1, w2, ids, gates)
+    y = offn.forward(x, w1, w2, ids, gates)
+    err = np.linalg.norm(y8 - y) / np.linalg.norm(y)
+    assert 1e-3 < err < 3 * 2.0 ** -4
