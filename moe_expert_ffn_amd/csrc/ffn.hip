@@ -246,8 +246,10 @@ struct ExecArgs {
   float* dqs;             //   its scales [slots / beta][d]
   uint8_t* zq;            //   dZ, e4m3 [slots][2 d_ff]
   float* zqs;             //   its scales [slots / beta][2 d_ff]
-  const void* xq;         // fp8 MFMA forward: x codes [T][d] and exponents [d/128][T]
-  const int32_t* xe;
+  const void* xq;         // fp8 MFMA forward: x codes [T][d] and exponents [d/128][T],
+  const int32_t* xe;      // A codes [slots][d_ff] and exponents [d_ff/128][slots]
+  void* hq;
+  int32_t* he;
   void* dhat;             // fp8 backward on the stream kernels: D requantized and
                           //   widened back to bf16, [slots][d]
   const int32_t* boff;    // block offsets [E + 1]: boff[E] blocks of beta slots are in use
@@ -657,38 +659,63 @@ int launch_quant_tok(const uint16_t* src, int ld, const int32_t* map, int gather
 // b of row r gets e = the smallest integer with amax <= 448 * 2^e (clamped to
 // [-127, 127]; -127 for a zero block) and codes e4m3(x * 2^-e).  With amax =
 // M * 2^E (M in [1, 2)) and 448 = 1.75 * 2^8 that is e = E - 8, or E - 7 when
-// M > 1.75 (mantissa field above 0x600000).  One wave per (row, block), two
-// values per lane; exps is block-major, exps[b * rows + r], so a GEMM step
-// (one block) reads the exponents of its rows from one array row.
+// M > 1.75 (mantissa field above 0x600000).  One wave per row and group of 4
+// blocks: 16 lanes per block, 8 values (16 bytes) per lane.  exps is
+// block-major, exps[b * rows + r], so a GEMM step (one block) reads the
+// exponents of its rows from one array row.
+MOE_DEV int e8_exponent(float amax) {
+  const uint32_t bits = __float_as_uint(amax);
+  const int E = (int)((bits >> 23) & 0xFF) - 127;
+  const int e = (bits & 0x7FFFFFFFu) == 0 ? -127 : E - 8 + ((bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
 __global__ __launch_bounds__(256) void k_quant_act(const uint16_t* __restrict__ x, int rows,
                                                    int cols, uint8_t* __restrict__ codes,
-                                                   int32_t* __restrict__ exps) {
-  const int nb = cols / 128;
+                                                   int32_t* __restrict__ exps,
+                                                   const int32_t* __restrict__ blk_end, int blk_rows) {
+  const int nb = cols / 128, ng = (nb + 3) / 4;
   const long long task = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (task >= (long long)rows * nb) return;                  // whole waves
-  const int r = (int)(task / nb), b = (int)(task % nb), lane = threadIdx.x & 63;
-  const size_t off = (size_t)r * cols + (size_t)b * 128 + 2 * lane;
-  const uint32_t w = *(const uint32_t*)(x + off);
-  const float v0 = __uint_as_float(w << 16), v1 = __uint_as_float(w & 0xFFFF0000u);
-  float m = fmaxf(fabsf(v0), fabsf(v1));
+  if (task >= (long long)rows * ng) return;                  // whole waves
+  const int r = (int)(task / ng), lane = threadIdx.x & 63;
+  // optional: only the rows of the blocks in use (*blk_end blocks of blk_rows)
+  if (blk_end && r >= (long long)*blk_end * blk_rows) return;
+  const int b = (int)(task % ng) * 4 + (lane >> 4);
+  const bool on = b < nb;
+  const size_t off = (size_t)r * cols + (size_t)b * 128 + 8 * (lane & 15);
+  uint4 q = make_uint4(0, 0, 0, 0);
+  if (on) q = *(const uint4*)(x + off);
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  float v[8];
 #pragma unroll
-  for (int sh = 32; sh >= 1; sh >>= 1) m = fmaxf(m, __shfl_xor(m, sh, 64));
-  const uint32_t bits = __float_as_uint(m);
-  const int E = (int)((bits >> 23) & 0xFF) - 127;
-  int e = (bits & 0x7FFFFFFFu) == 0 ? -127 : E - 8 + ((bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
-  e = e < -127 ? -127 : (e > 127 ? 127 : e);
-  const float s0 = ldexpf(v0, -e), s1 = ldexpf(v1, -e);     // exact: powers of two
-  const int p = __builtin_amdgcn_cvt_pk_fp8_f32(s0, s1, 0, false);
-  *(uint16_t*)(codes + off) = (uint16_t)(p & 0xFFFF);
-  if (lane == 0) exps[(size_t)b * rows + r] = e;
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+#pragma unroll
+  for (int sh = 8; sh >= 1; sh >>= 1) m = fmaxf(m, __shfl_xor(m, sh, 64));   // within 16 lanes
+  const int e = e8_exponent(m);
+  uint32_t c[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int p = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * h], -e), ldexpf(v[4 * h + 1], -e), 0, false);
+    p = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * h + 2], -e), ldexpf(v[4 * h + 3], -e), p, true);
+    c[h] = (uint32_t)p;
+  }
+  if (on) {
+    *(uint2*)(codes + off) = make_uint2(c[0], c[1]);
+    if ((lane & 15) == 0) exps[(size_t)b * rows + r] = e;
+  }
 }
 
 int launch_quant_act(const uint16_t* x, int rows, int cols, uint8_t* codes, int32_t* exps,
-                     hipStream_t st) {
-  const long long tasks = (long long)rows * (cols / 128);
+                     hipStream_t st, const int32_t* blk_end, int blk_rows) {
+  const long long tasks = (long long)rows * ((cols / 128 + 3) / 4);
   if (tasks > 0)
     hipLaunchKernelGGL(k_quant_act, dim3((unsigned)((tasks + 3) / 4)), dim3(256), 0, st, x, rows,
-                       cols, codes, exps);
+                       cols, codes, exps, blk_end, blk_rows);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -1262,6 +1289,34 @@ template <bool FP8> struct SrcFc2T : MSrcBase {
       });
     }
   }
+};
+
+// FC2 on the fp8 MFMA: A rows are the e4m3 codes SrcFc1F8 wrote (slot rows of
+// hq, exponents in he), B rows W2's codes; K steps of 128 over d_ff.  The
+// epilogue (gate, O rows) is FC2's.
+struct SrcFc2F8 : SrcFc2T<true> {
+  using OB = RowW8;
+  MOE_DEV RowA8 opA(const Item& it, int) const {
+    RowA8 x;
+    x.init((const uint16_t*)a.hq, (uint32_t)((size_t)a.slots * a.dff),
+           [&](int row) { return row < it.nrows ? (it.slot0 + row) * (a.dff / 2) : -1; });
+    const int w = wave_id(), row = w * 64 + (threadIdx.x & 63);
+    x.rsc = make_rsrc(a.he, (uint32_t)((size_t)(a.dff / 128) * a.slots * 4));
+    x.scs = (uint32_t)a.slots * 4u;
+    x.sco = (w < 4 && row < it.nrows) ? (uint32_t)(it.slot0 + row) * 4u : kOob;
+    return x;
+  }
+  MOE_DEV RowW8 opB(const Item& it, int) const {
+    RowW8 w;
+    const int nj = it.nj, dff = a.dff;
+    w.init((const uint16_t*)((const uint8_t*)a.w2 + (size_t)it.e * a.d * dff),
+           (uint32_t)((size_t)a.d * dff), [&](int rho) { return (nj * WC::BN + rho) * (dff / 2); });
+    const int kb = dff / 128, wn = wave_id() % WC::WAVES_N;
+    w.sp[0] = w.sp[1] = (const MOE_CONST float*)a.w2s + (size_t)it.e * (a.d / 128) * kb +
+                        (size_t)(2 * nj + wn / 2) * kb;
+    return w;
+  }
+  MOE_DEV int steps(const Item&) const { return a.dff / 128; }
 };
 
 // dA = p * dy W2 (W2 [d][d_ff] read K-major through transpose reads), then
@@ -1914,10 +1969,12 @@ WsLayout exec_layout(const Sizes& z, bool backward) {
   L.rslots = backward ? take(sizeof(float) * (size_t)z.P * z.s * 3 * z.d * z.dff) : o;
   L.bufP = backward ? take((size_t)z.act_bytes * z.max_slots * z.dff) : o;
   L.sgate = take(sizeof(float) * z.max_slots);
-  L.dq = L.dqs = L.zq = L.zqs = L.dhat = L.xq = L.xe = o;
+  L.dq = L.dqs = L.zq = L.zqs = L.dhat = L.xq = L.xe = L.hq = L.he = o;
   if (!backward && z.fp8 && use_stream(z)) {      // MOE_EXEC_FP8_ACT
     L.xq = take((size_t)z.T * z.d);
     L.xe = take(sizeof(int32_t) * (size_t)(z.d / 128) * z.T);
+    L.hq = take(z.max_slots * (size_t)z.dff);
+    L.he = take(sizeof(int32_t) * (size_t)(z.dff / 128) * z.max_slots);
   }
   if (backward && z.fp8 && use_stream(z)) {
     L.dhat = take((size_t)2 * z.max_slots * z.d);           // requantized D as bf16
@@ -2035,6 +2092,8 @@ static ExecArgs make_exec(const Sizes& z, const LayerPtrs& Lp, char* ws, const W
   if (z.fp8) {
     a.xq = ws + L.xq;
     a.xe = (const int32_t*)(ws + L.xe);
+    a.hq = ws + L.hq;
+    a.he = (int32_t*)(ws + L.he);
     a.dq = (uint8_t*)(ws + L.dq);
     a.dqs = (float*)(ws + L.dqs);
     a.zq = (uint8_t*)(ws + L.zq);
@@ -2125,9 +2184,12 @@ static void run_forward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_t
   if (FP8 && f8act) {                  // x quantized per row block, FC1 on the fp8 MFMA
     launch_quant_act((const uint16_t*)a.x, z.T, z.d, (uint8_t*)a.xq, (int32_t*)a.xe, st);
     launch_stream<SrcFc1F8, WC, RowA8, RowW8>(a, n1, kStreamLds8, st);
+    // A's slot rows in use, quantized the same way for FC2
+    launch_quant_act((const uint16_t*)a.bufA, (int)z.max_slots, z.dff, (uint8_t*)a.hq, a.he, st,
+                     a.boff + z.E, z.beta);
     rec(ev, 2, st);
     a.tl_phase = MOE_TL_FC2;
-    launch_stream<SrcFc2T<FP8>, WC, RowW, typename SrcFc2T<FP8>::OB>(a, n2, kStreamLds, st);
+    launch_stream<SrcFc2F8, WC, RowA8, RowW8>(a, n2, kStreamLds8, st);
   } else if (split) {
     launch_stream<SrcFc1T<FP8>, WC, RowW, typename SrcFc1T<FP8>::OB>(a, n1, kStreamLds, st);
     rec(ev, 2, st);
@@ -2164,6 +2226,7 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
   ExecArgs a = make_exec(z, Lp, ws, L);
   a.x = x; a.gates = gates; a.slot_to_row = slot_to_row; a.row_to_slot = row_to_slot;
   a.z_save = z_save;
+  a.boff = boff;
   a.timeline = timeline;
   a.status = status;
   const bool big = use_big_tiles(z);

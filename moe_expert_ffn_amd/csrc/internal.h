@@ -31,6 +31,7 @@ struct WsLayout {
   size_t dq, dqs, zq, zqs;   // fp8 backward: token-axis e4m3 codes and scales of D and dZ
   size_t dhat;               // fp8 backward on the stream kernels: requantized D as bf16
   size_t xq, xe;             // fp8 MFMA forward: x as e4m3 codes and row exponents
+  size_t hq, he;             // ... and A = SiLU(G) U as e4m3 codes and row exponents
   size_t total;
 };
 
@@ -53,7 +54,7 @@ int launch_plan(const int32_t* bcnt, const int32_t* boff, const int32_t* owner, 
 constexpr int kQtMaxCols = 65535 * 128;   // column tiles of the quantizer grid
 // map_lim: map values m >= map_lim read as zero rows (src rows * div)
 int launch_quant_act(const uint16_t* x, int rows, int cols, uint8_t* codes, int32_t* exps,
-                     hipStream_t st);
+                     hipStream_t st, const int32_t* blk_end = nullptr, int blk_rows = 0);
 int launch_quant_tok(const uint16_t* src, int ld, const int32_t* map, int gather, int div,
                      const float* rscale, int map_lim, int rows, int cols, int brows,
                      uint8_t* codes, float* scales, hipStream_t st,

@@ -67,14 +67,23 @@ def forward(x, w1, w2, topk_ids, gates, tokens=None, return_z=False):
     return (y, zs) if return_z else y
 
 
+def round_bf16(v) -> np.ndarray:
+    """fp32 values rounded to bfloat16 (8 significant bits, nearest, ties to
+    even), returned as fp32; finite inputs only."""
+    u = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
 def forward_fp8act(x, w1, w2, topk_ids, gates, tokens=None, return_z=False):
     """The forward of an e4m3-weight layer whose two products run on fp8
     operands (reading of "per-1x128 e4m3 activations"): each row of x and each
     row of A = SiLU(G) U is quantized in blocks of 128 features with
     power-of-two scales (oracle.fp8.quantize_row_blocks_pow2) before the
     product that reads it; the weights are as given (dequantized).  A is
-    formed from Z in fp64 and rounded to fp32 before its quantization (the
-    device quantizes its fp32 value).  The gated combine is forward's."""
+    formed from Z and stored in the activation dtype, bf16 (round to nearest
+    even from its fp32 value), before its quantization, as the layer keeps
+    A between the two products.  The gated combine is forward's."""
     from oracle.fp8 import dequant_row_blocks_pow2, quantize_row_blocks_pow2
     x = np.asarray(x, dtype=np.float64)
     xh = dequant_row_blocks_pow2(*quantize_row_blocks_pow2(x.astype(np.float32)))
@@ -87,7 +96,7 @@ def forward_fp8act(x, w1, w2, topk_ids, gates, tokens=None, return_z=False):
     zs = {}
     for e, (ti, j) in _pairs_by_expert(ids, tokens).items():
         z = xh[tokens[ti]] @ np.asarray(w1[e], dtype=np.float64).T
-        a = (silu(z[:, :F]) * z[:, F:]).astype(np.float32)
+        a = round_bf16((silu(z[:, :F]) * z[:, F:]).astype(np.float32))
         ah = dequant_row_blocks_pow2(*quantize_row_blocks_pow2(a))
         o = ah @ np.asarray(w2[e], dtype=np.float64).T
         contrib[ti, j] = p[tokens[ti], j][:, None] * o

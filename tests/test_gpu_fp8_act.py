@@ -3,10 +3,10 @@ quantizer.
 
 - The quantizer (moe_quantize_act_rows) is bit-exact against the oracle's
   power-of-two row blocks: codes and exponents.
-- The forward is checked two ways:
-  - against the oracle run on the quantized x (its dequantized values), where
-    only accumulation order and the bf16 roundings differ: saved [G, U] within
-    1e-2, y within 2e-2;
+- The forward (FC1 and FC2 on the fp8 MFMA) is checked two ways:
+  - against the oracle's fp8-operand forward (x and A quantized the same
+    way), where only accumulation order and the bf16 roundings differ: saved
+    [G, U] within 1e-2, y within 2e-2;
   - against the exact oracle (bf16 x, dequantized weights) within the e4m3
     bar of 6e-2.
 - Placement does not change a bit. A zero weight-scale block adds nothing.
@@ -18,14 +18,14 @@ import torch
 from moe_expert_ffn_amd import binding as B
 from moe_expert_ffn_amd.inputs import WORKLOADS, Workload
 from oracle import ffn as offn
-from oracle.fp8 import dequant_row_blocks_pow2, quantize_row_blocks_pow2
+from oracle.fp8 import quantize_row_blocks_pow2
 from oracle.route import route_stats as oracle_route
 from tests.conftest import rel_l2
 from tests.gpu_util import Case, say
 
 pytestmark = pytest.mark.gpu
 
-TOL_MODEL_Z = 1e-2      # [G, U] against the oracle on the quantized x (bf16 storage)
+TOL_MODEL_Z = 1e-2      # [G, U] against the fp8-operand oracle (bf16 storage)
 TOL_MODEL_Y = 2e-2      # y against the same
 TOL_EXACT = 6e-2        # y against the exact oracle (the e4m3 bar)
 
@@ -37,13 +37,6 @@ SMALL = {
     "stream_fp8": Workload("stream_fp8", "bf16", "fp8", T=700, k=4, E=8, d=512, d_ff=512,
                            beta=128, P=8, s=4, kappas=(0,), cfg_id=18),
 }
-
-
-def _xhat(x):
-    """The oracle's quantize-dequantize of x's rows (fp64)."""
-    xf = x.float().cpu().numpy()
-    codes, exps = quantize_row_blocks_pow2(xf)
-    return dequant_row_blocks_pow2(codes, exps)
 
 
 def _run(c, fp8_act=True, s=None):
@@ -78,10 +71,9 @@ def test_quantize_act_rows_matches_oracle():
 
 
 def _z_check(c, zg):
-    """Saved [G, U] of every routed row against the oracle on the quantized x."""
+    """Saved [G, U] of every routed row against the fp8-operand oracle."""
     x, w1, w2, ids, gates = c.oracle_inputs()
-    xh = _xhat(c.x)
-    _, zs = offn.forward(xh, w1, w2, ids, gates, return_z=True)
+    _, zs = offn.forward_fp8act(x, w1, w2, ids, gates, return_z=True)
     rs = oracle_route(ids, c.w.E, c.w.beta)
     got, ref = [], []
     for e, (toks, j, z) in zs.items():
@@ -99,10 +91,10 @@ def test_fp8_act_forward_parity(name):
     y = _run(c)
     x, w1, w2, ids, gates = c.oracle_inputs()
     ez = _z_check(c, c.runner.z.double().cpu().numpy())
-    ym = rel_l2(y.double().cpu().numpy(), offn.forward(_xhat(c.x), w1, w2, ids, gates))
+    ym = rel_l2(y.double().cpu().numpy(), offn.forward_fp8act(x, w1, w2, ids, gates))
     ye = rel_l2(y.double().cpu().numpy(), offn.forward(x, w1, w2, ids, gates))
     moved = rel_l2(y.double().cpu().numpy(), y0.double().cpu().numpy())
-    say(f"  z vs quantized-x oracle {ez:.3e}, y {ym:.3e}; y vs exact {ye:.3e}; "
+    say(f"  z vs fp8-operand oracle {ez:.3e}, y {ym:.3e}; y vs exact {ye:.3e}; "
         f"vs the bf16-x path {moved:.3e}")
     assert ez <= TOL_MODEL_Z and ym <= TOL_MODEL_Y and ye <= TOL_EXACT
     assert moved > 1e-4                    # the flag took the fp8 path
@@ -129,7 +121,7 @@ def test_fp8_act_zero_scale_block():
     c.w1s[3, 5, 1] = 0.0
     _run(c)
     ez = _z_check(c, c.runner.z.double().cpu().numpy())
-    say(f"  z vs quantized-x oracle {ez:.3e}")
+    say(f"  z vs fp8-operand oracle {ez:.3e}")
     assert ez <= TOL_MODEL_Z
 
 
@@ -143,9 +135,9 @@ def test_fp8_act_full_size_sampled(kappa):
     tok = np.sort(rng.choice(c.T, size=48, replace=False))
     x, w1, w2, ids, gates = c.oracle_inputs()
     yt = y[tok].double().cpu().numpy()
-    ym = rel_l2(yt, offn.forward(_xhat(c.x), w1, w2, ids, gates, tokens=tok))
+    ym = rel_l2(yt, offn.forward_fp8act(x, w1, w2, ids, gates, tokens=tok))
     ye = rel_l2(yt, offn.forward(x, w1, w2, ids, gates, tokens=tok))
-    say(f"  y vs quantized-x oracle {ym:.3e}; vs exact {ye:.3e}")
+    say(f"  y vs fp8-operand oracle {ym:.3e}; vs exact {ye:.3e}")
     assert ym <= TOL_MODEL_Y and ye <= TOL_EXACT
     assert torch.isfinite(y.float()).all()
 

@@ -373,3 +373,11 @@ def test_forward_fp8act_error_bound():
     y = offn.forward(x, w1, w2, ids, gates)
     err = np.linalg.norm(y8 - y) / np.linalg.norm(y)
     assert 1e-3 < err < 3 * 2.0 ** -4
+
+
+def test_round_bf16_matches_torch():
+    import torch
+    rng = np.random.default_rng(23)
+    v = (rng.standard_normal(200000) * 10.0 ** rng.uniform(-30, 30, 200000)).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).float().numpy()
+    np.testing.assert_array_equal(offn.round_bf16(v), ref)
