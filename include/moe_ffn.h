@@ -82,12 +82,18 @@ typedef enum {
 #define MOE_EXEC_SPLIT_SHIFT 8
 #define MOE_EXEC_SPLIT(n1) (((n1) & 0xff) << MOE_EXEC_SPLIT_SHIFT)
 /* moe_forward only, e4m3 weights on the persistent stream kernels (d and
- * d_ff multiples of 256), two launches: FC1 runs on the fp8 MFMA.  x is
- * quantized per token row and 128 features with power-of-two scales
- * (moe_quantize_act_rows) into the workspace, the weights' codes are used
- * as stored, and per 128-deep K block the weights' fp32 block scale is
- * applied to the accumulators.  The results differ from the default path by
- * x's quantization (relative error about 2^-5 per value). */
+ * d_ff multiples of 256), two launches: FC1 and FC2 run on the fp8 MFMA
+ * (v_mfma_scale_f32_32x32x64_f8f6f4).  x is quantized per token row and 128
+ * features with power-of-two scales (moe_quantize_act_rows) into the
+ * workspace; FC1's activations A = SiLU(G) * U, stored as bf16, are quantized
+ * the same way, only the rows of the blocks in use.  The row exponents ride
+ * in the MFMA's scale operand, the weights' codes are used as stored, and per
+ * 128-deep K block the weights' fp32 block scale is applied to the
+ * accumulators.  The results differ from the default path by the two
+ * quantizations (relative error about 2^-5 per value); the saved [G, U] of a
+ * backward-capable call come from the quantized x.  MOE_ERR_ARG for the flag
+ * with moe_backward, a two-phase launch, activations other than bf16,
+ * weights other than e4m3, or a layer off the stream kernels. */
 #define MOE_EXEC_FP8_ACT 2
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
@@ -404,7 +410,8 @@ int moe_quantize_token_blocks(const void* src, int ld, int src_rows, const int32
  * of row r gets the power-of-two scale 2^e, e the smallest integer with
  * amax <= 448 * 2^e, clamped to [-127, 127] (-127 for a zero block), and
  * codes[r][c] = e4m3(src[r][c] * 2^-e), round to nearest even (the product
- * is exact).  This is how MOE_EXEC_FP8_ACT quantizes x for FC1.
+ * is exact).  This is how MOE_EXEC_FP8_ACT quantizes x for FC1 and A for
+ * FC2.
  *   codes uint8 [rows][cols]; exps int32 [cols / 128][rows] (block-major:
  *   exps[b * rows + r] = e), all device memory owned by the caller.
  * Errors: MOE_ERR_ARG for rows < 0, cols not a positive multiple of 128, or

@@ -669,53 +669,77 @@ MOE_DEV int e8_exponent(float amax) {
   const int e = (bits & 0x7FFFFFFFu) == 0 ? -127 : E - 8 + ((bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
+// A task is one row and group of 4 blocks, one wave's work; waves walk the
+// tasks grid-stride, two tasks in flight each.  With blk_end only the rows of
+// the blocks in use (*blk_end blocks of blk_rows) are tasks.
 __global__ __launch_bounds__(256) void k_quant_act(const uint16_t* __restrict__ x, int rows,
                                                    int cols, uint8_t* __restrict__ codes,
                                                    int32_t* __restrict__ exps,
                                                    const int32_t* __restrict__ blk_end, int blk_rows) {
   const int nb = cols / 128, ng = (nb + 3) / 4;
-  const long long task = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (task >= (long long)rows * ng) return;                  // whole waves
-  const int r = (int)(task / ng), lane = threadIdx.x & 63;
-  // optional: only the rows of the blocks in use (*blk_end blocks of blk_rows)
-  if (blk_end && r >= (long long)*blk_end * blk_rows) return;
-  const int b = (int)(task % ng) * 4 + (lane >> 4);
-  const bool on = b < nb;
-  const size_t off = (size_t)r * cols + (size_t)b * 128 + 8 * (lane & 15);
-  uint4 q = make_uint4(0, 0, 0, 0);
-  if (on) q = *(const uint4*)(x + off);
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-  float v[8];
+  long long rl = rows;
+  if (blk_end) rl = min(rl, (long long)*blk_end * blk_rows);
+  const long long ntask = rl * ng, nw = (long long)gridDim.x * 4;
+  const int lane = threadIdx.x & 63;
+  for (long long t = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); t < ntask; t += 2 * nw) {
+    uint4 q[2];
+    size_t off[2];
+    int r[2], b[2];
+    bool on[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(w[i] << 16);
-    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-  }
-  float m = 0.f;
+    for (int u = 0; u < 2; ++u) {
+      const long long tu = t + u * nw;
+      r[u] = (int)(tu / ng);
+      b[u] = (int)(tu % ng) * 4 + (lane >> 4);
+      on[u] = tu < ntask && b[u] < nb;
+      off[u] = on[u] ? (size_t)r[u] * cols + (size_t)b[u] * 128 + 8 * (lane & 15) : 0;
+      q[u] = on[u] ? *(const uint4*)(x + off[u]) : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+      float v[8];
 #pragma unroll
-  for (int sh = 8; sh >= 1; sh >>= 1) m = fmaxf(m, __shfl_xor(m, sh, 64));   // within 16 lanes
-  const int e = e8_exponent(m);
-  uint32_t c[2];
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+      float m = 0.f;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    int p = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * h], -e), ldexpf(v[4 * h + 1], -e), 0, false);
-    p = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * h + 2], -e), ldexpf(v[4 * h + 3], -e), p, true);
-    c[h] = (uint32_t)p;
-  }
-  if (on) {
-    *(uint2*)(codes + off) = make_uint2(c[0], c[1]);
-    if ((lane & 15) == 0) exps[(size_t)b * rows + r] = e;
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+#pragma unroll
+      for (int sh = 8; sh >= 1; sh >>= 1) m = fmaxf(m, __shfl_xor(m, sh, 64));  // within 16 lanes
+      const int e = e8_exponent(m);
+      uint32_t c[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        int p = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * h], -e), ldexpf(v[4 * h + 1], -e), 0,
+                                                false);
+        p = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * h + 2], -e), ldexpf(v[4 * h + 3], -e), p,
+                                            true);
+        c[h] = (uint32_t)p;
+      }
+      if (on[u]) {
+        *(uint2*)(codes + off[u]) = make_uint2(c[0], c[1]);
+        if ((lane & 15) == 0) exps[(size_t)b[u] * rows + r[u]] = e;
+      }
+    }
   }
 }
+
+// Every task its own wave when all rows are tasks; when the rows in use are
+// known only on the device (blk_end), one resident round of workgroups (8 of
+// 4 waves per CU) walks them, so the capacity past them costs nothing.
+static constexpr long long kQuantActWG = 256 * 8;
 
 int launch_quant_act(const uint16_t* x, int rows, int cols, uint8_t* codes, int32_t* exps,
                      hipStream_t st, const int32_t* blk_end, int blk_rows) {
   const long long tasks = (long long)rows * ((cols / 128 + 3) / 4);
+  const long long all = (tasks + 3) / 4;
+  const long long wg = (blk_end || all > (1LL << 30)) ? std::min(all, kQuantActWG) : all;
   if (tasks > 0)
-    hipLaunchKernelGGL(k_quant_act, dim3((unsigned)((tasks + 3) / 4)), dim3(256), 0, st, x, rows,
-                       cols, codes, exps, blk_end, blk_rows);
+    hipLaunchKernelGGL(k_quant_act, dim3((unsigned)wg), dim3(256), 0, st, x, rows, cols, codes,
+                       exps, blk_end, blk_rows);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

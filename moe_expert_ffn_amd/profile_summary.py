@@ -13,8 +13,11 @@ WRITE_SIZE per dispatch (KiB), the calibration of both counters against a
 plain elementwise copy of `copy_bytes` bytes read and written (the copy's own
 dispatch is the one with the largest reading), and the calibrated HBM bytes
 per dispatch.  `mfma` takes a `--pmc MfmaUtil MfmaFlopsBF16` run and prints,
-per GEMM kernel, the mean MfmaUtil, the executed bf16 MFMA work and the
-dispatch duration (its own timestamps; counter runs serialise dispatches).
+per GEMM kernel, the mean MfmaUtil, the executed MFMA work and the dispatch
+duration (its own timestamps; counter runs serialise dispatches).  The work
+is `MfmaFlopsBF16`, priced against the bf16 peak, or, for kernels that run
+the fp8 MFMA, 512 · SQ_INSTS_VALU_MFMA_MOPS_F8 (the run then names that
+counter in place of MfmaFlopsBF16), priced against the fp8 peak.
 """
 from __future__ import annotations
 
@@ -35,6 +38,8 @@ STAGE_OF = {"k_stream<SrcFc1>": "fwd.fc1", "k_stream<SrcFc2>": "fwd.fc2",
             "k_bwd_dw": "bwd.dW", "k_bwd_reduce": "bwd.reduce",
             "k_combine": "fwd.combine + bwd.combine", "k_sched": "fwd.sched + bwd.sched",
             "k_slot_gate": "fwd.sched + bwd.sched", "k_plan": "plan (fwd + bwd)",
+            "k_stream<SrcFc1F8>": "fwd.fc1 (fp8 MFMA)", "k_stream<SrcFc2F8>": "fwd.fc2 (fp8 MFMA)",
+            "k_quant_act": "fwd.fc1 (x) + fwd.fc2 (A), fp8 MFMA",
             "k_route_count": "route", "k_route_scan": "route", "k_route_slot": "route"}
 
 
@@ -53,6 +58,9 @@ def short(name: str) -> str:
     m = re.search(r"k_stream<moe::Src(\w+?)T<(true|false)\b", name)
     if m:
         return f"k_stream<Src{m.group(1)}{fp8(m.group(2))}>"
+    m = re.search(r"k_stream<moe::Src(\w+F8),", name)
+    if m:
+        return f"k_stream<Src{m.group(1)}>"
     m = re.search(r"moe::(\w+)", name)
     return m.group(1) if m else name[:60]
 
@@ -77,10 +85,12 @@ def per_kernel(path: str):
 
 
 PEAK_BF16_TFLOPS = 2516.6
+PEAK_FP8_TFLOPS = 5033.2
 
 
 def mfma(path: str) -> str:
     util, flops, dur = (collections.defaultdict(list) for _ in range(3))
+    kind = {}
     for r in csv.DictReader(open(path)):
         if "moe::" not in r["Kernel_Name"]:
             continue
@@ -90,15 +100,20 @@ def mfma(path: str) -> str:
             dur[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
         elif r["Counter_Name"] == "MfmaFlopsBF16":
             flops[k].append(float(r["Counter_Value"]))
-    out = ["| kernel | dispatches | MfmaUtil % | executed bf16 MFMA GFLOP / launch | us / launch "
-           "| TFLOP/s | % of 2,516.6 TFLOP/s |", "|---|---|---|---|---|---|---|"]
+            kind[k] = "bf16"
+        elif r["Counter_Name"] == "SQ_INSTS_VALU_MFMA_MOPS_F8":
+            flops[k].append(512.0 * float(r["Counter_Value"]))
+            kind[k] = "fp8"
+    peak = {"bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS}
+    out = ["| kernel | dispatches | MfmaUtil % | MFMA | executed GFLOP / launch | us / launch "
+           "| TFLOP/s | % of that MFMA's peak |", "|---|---|---|---|---|---|---|---|"]
     for k in sorted(util, key=lambda k: -sum(dur[k]) / len(dur[k])):
         if not flops.get(k) or sum(flops[k]) == 0:
             continue
         u, f, t = (sum(v) / len(v) for v in (util[k], flops[k], dur[k]))
         tf = f / (t * 1e-6) / 1e12
-        out.append(f"| {k} | {len(util[k])} | {u:.1f} | {f / 1e9:.1f} | {t:.1f} | {tf:.1f} | "
-                   f"{100 * tf / PEAK_BF16_TFLOPS:.1f} |")
+        out.append(f"| {k} | {len(util[k])} | {u:.1f} | {kind[k]} | {f / 1e9:.1f} | {t:.1f} | "
+                   f"{tf:.1f} | {100 * tf / peak[kind[k]]:.1f} of {peak[kind[k]]:,.1f} |")
     return "\n".join(out)
 
 
