@@ -211,3 +211,81 @@ def backward_fp8(x, w1, w2, topk_ids, gates, dy, beta, tokens=None, experts=None
         out["dw2"][e] = Dq.T @ a
         out["dw1"][e] = dZq.T @ xe
     return out
+
+
+def backward_fp8act(x, w1, w2, topk_ids, gates, dy, beta, tokens=None, experts=None):
+    """The backward of an e4m3-weight layer whose products run on fp8 operands
+    in both directions (the reading of "per-1x128 e4m3 activations" that
+    forward_fp8act follows, carried to dA and dX):
+
+    * [G, U] are what the fp8-operand forward saves: Z = Q(x) W1 (Q: each row
+      in blocks of 128 features with power-of-two scales,
+      oracle.fp8.quantize_row_blocks_pow2);
+    * dA = p * (Q(dy_t) W2): the token's dy row is quantized, once for all of
+      its k slots, and the gate is applied to the product;
+    * dZ = [dG, dU] from dA, G and U as in backward; the layer stores dZ in
+      bf16 between the two products, so the row's dX contribution is
+      Q(bf16(dZ)) W1, and dx adds a token's k contributions in slot order;
+    * the weight gradients are backward_fp8's: dW2 = Dq^T A with D = p * dy
+      (dy as given) and A from this Z, dW1 = dZq^T X with dZ (fp32) from this
+      dA and X as given; Dq and dZq are the token-axis requantizations.
+    """
+    from oracle.fp8 import (dequant_row_blocks_pow2, dequant_token_blocks,
+                            quantize_row_blocks_pow2, quantize_token_blocks)
+
+    def q_rows(v):
+        return dequant_row_blocks_pow2(*quantize_row_blocks_pow2(np.asarray(v, dtype=np.float32)))
+
+    x = np.asarray(x, dtype=np.float64)
+    xh = q_rows(x)
+    dy32 = np.asarray(dy, dtype=np.float32)
+    dyh = q_rows(dy32)
+    ids = np.asarray(topk_ids)
+    p32 = np.asarray(gates, dtype=np.float32)
+    p = p32.astype(np.float64)
+    T, k = ids.shape
+    d = x.shape[1]
+    E = w1.shape[0]
+    F = w1.shape[1] // 2
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    experts = range(E) if experts is None else experts
+    tok_pos = {int(t): i for i, t in enumerate(tokens)}
+    all_pairs = _pairs_by_expert(ids, np.arange(T))
+
+    dx_contrib = np.zeros((len(tokens), k, d))
+    dw1, dw2 = {}, {}
+    want_w = set(int(e) for e in experts)
+    for e in range(E):
+        need_rows = e in want_w
+        ti, j = all_pairs.get(e, (np.zeros(0, int), np.zeros(0, int)))
+        if not need_rows:
+            keep = np.array([t in tok_pos for t in ti], dtype=bool)
+            ti, j = ti[keep], j[keep]
+        w1e = np.asarray(w1[e], dtype=np.float64)
+        w2e = np.asarray(w2[e], dtype=np.float64)
+        if len(ti) == 0:
+            if need_rows:
+                dw1[e] = np.zeros((2 * F, d))
+                dw2[e] = np.zeros((d, F))
+            continue
+        z = xh[ti] @ w1e.T
+        g, u = z[:, :F], z[:, F:]
+        sg = sigmoid(g)
+        a = g * sg * u
+        dA = p[ti, j][:, None] * (dyh[ti] @ w2e)
+        dZ = np.concatenate([dA * u * sg * (1.0 + g * (1.0 - sg)), dA * g * sg], axis=1)
+        dX = q_rows(round_bf16(dZ.astype(np.float32))) @ w1e
+        for r in range(len(ti)):
+            pos = tok_pos.get(int(ti[r]))
+            if pos is not None:
+                dx_contrib[pos, j[r]] = dX[r]
+        if need_rows:
+            D32 = (p32[ti, j][:, None] * dy32[ti]).astype(np.float32)
+            Dq = dequant_token_blocks(*quantize_token_blocks(D32, beta), beta)
+            dZq = dequant_token_blocks(*quantize_token_blocks(dZ.astype(np.float32), beta), beta)
+            dw2[e] = Dq.T @ a
+            dw1[e] = dZq.T @ x[ti]
+    dx = np.zeros((len(tokens), d))
+    for jj in range(k):
+        dx += dx_contrib[:, jj]
+    return {"dx": dx, "dw1": dw1, "dw2": dw2}

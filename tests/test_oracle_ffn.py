@@ -381,3 +381,121 @@ def test_round_bf16_matches_torch():
     v = (rng.standard_normal(200000) * 10.0 ** rng.uniform(-30, 30, 200000)).astype(np.float32)
     ref = torch.from_numpy(v).to(torch.bfloat16).float().numpy()
     np.testing.assert_array_equal(offn.round_bf16(v), ref)
+
+
+# ---- the fp8-operand backward (dy and dZ quantized per row block of 128) -------
+
+def _q_rows(v):
+    from oracle.fp8 import dequant_row_blocks_pow2, quantize_row_blocks_pow2
+    return dequant_row_blocks_pow2(*quantize_row_blocks_pow2(np.asarray(v, dtype=np.float32)))
+
+
+def _check_row_blocks_pow2(q, v):
+    """q holds v (bf16 values) quantized per row and block of 128 features with
+    a power-of-two scale 2^e, e the smallest integer with amax <= 448 * 2^e:
+    every value is an e4m3 value times 2^e, within half an e4m3 step of v."""
+    rows, cols = v.shape
+    for b0 in range(0, cols, 128):
+        vb, qb = v[:, b0:b0 + 128], q[:, b0:b0 + 128]
+        amax = np.abs(vb).max(axis=1)
+        m, E = np.frexp(amax / 448.0)
+        e = np.where(m == 0.5, E - 1, E)[:, None].astype(np.float64)
+        s = np.power(2.0, e)
+        assert np.all(amax[:, None] <= 448.0 * s) and np.all(amax[:, None] > 224.0 * s)
+        assert np.all(_grid_units(qb / s) <= 1e-6), "values off the row block's e4m3 grid"
+        assert np.all(np.abs(qb - vb) <= 2.0 ** -4 * np.abs(vb) + 2.0 ** -10 * s), \
+            "a value moved by more than half an e4m3 step"
+
+
+def _fp8act_bwd_case(seed, T=24, k=1, E=2, F=128):
+    """d = 2 F and W1 = I, so G and U are the two halves of the row and
+    dX = dZ: the exact backward's dx shows dZ itself."""
+    rng = np.random.default_rng(seed)
+    d = 2 * F
+    x = rng.standard_normal((T, d))
+    w1 = np.repeat(np.eye(d)[None], E, axis=0)
+    w2 = rng.standard_normal((E, d, F)) / np.sqrt(F)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    g = rng.uniform(0.2, 0.9, (T, k)).astype(np.float32)            # gates off powers of two
+    dy = rng.standard_normal((T, d)).astype(np.float32).astype(np.float64)
+    return x, w1, w2, ids, g, dy
+
+
+def test_backward_fp8act_dx_is_the_dz_rows_quantized():
+    """dX = Q(bf16(dZ)) W1 with dZ from dA = p Q(dy) W2 and Z = Q(x) W1: the
+    exact backward on Q(x) and Q(dy) gives that dZ (W1 = I exposes it in dx),
+    and the fp8-operand dx must be it, rounded to bf16 and quantized per row
+    block.  Quantizing D = p dy instead of dy, dA instead of dZ, blocks along
+    the wrong axis, or no dZ quantization, each fail it."""
+    x, w1, w2, ids, g, dy = _fp8act_bwd_case(31)
+    dz = offn.backward(_q_rows(x), w1, w2, ids, g, _q_rows(dy))["dx"]
+    got = offn.backward_fp8act(x, w1, w2, ids, g, dy, beta=8)["dx"]
+    v = offn.round_bf16(dz.astype(np.float32)).astype(np.float64)
+    _check_row_blocks_pow2(got, v)
+    assert np.abs(got - v).max() > 0                   # something was rounded
+
+
+def test_backward_fp8act_dw2_takes_z_of_the_quantized_x():
+    """dW2 = Dq^T A with A from the fp8-operand forward's Z = Q(x) W1 and D
+    from dy as given: it is backward_fp8's dW2 on Q(x)."""
+    rng = np.random.default_rng(32)
+    T, k, E, d, F = 40, 2, 3, 256, 128
+    x = rng.standard_normal((T, d))
+    w1 = rng.standard_normal((E, 2 * F, d)) / np.sqrt(d)
+    w2 = rng.standard_normal((E, d, F)) / np.sqrt(F)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    g = rng.uniform(0.2, 0.9, (T, k)).astype(np.float32)
+    dy = rng.standard_normal((T, d)).astype(np.float32).astype(np.float64)
+    b = offn.backward_fp8act(x, w1, w2, ids, g, dy, beta=16)
+    ref = offn.backward_fp8(_q_rows(x), w1, w2, ids, g, dy, beta=16)
+    plain = offn.backward_fp8(x, w1, w2, ids, g, dy, beta=16)
+    for e in range(E):
+        np.testing.assert_allclose(b["dw2"][e], ref["dw2"][e], rtol=1e-12, atol=1e-12)
+        assert np.abs(b["dw2"][e] - plain["dw2"][e]).max() > 1e-6
+
+
+def test_backward_fp8act_dw1_takes_dz_of_the_quantized_dy():
+    """With x_t = e_t (on the e4m3 grid, so Q(x) = x) column t of dW1_e is the
+    token-axis requantized dZ row of token t, whose dZ comes from dA =
+    p Q(dy) W2: each block of beta slots times one column keeps its maximum,
+    lies on that column's e4m3 grid and stays within half a step of the exact
+    backward's dZ on Q(dy)."""
+    beta = 8
+    rng, x, ids, g, dy = _onehot_case(33)
+    E, d, F = 3, x.shape[1], 64                        # dZ rows: one block of 128
+    assert np.array_equal(_q_rows(np.pad(x, ((0, 0), (0, 128 - d)))), np.pad(x, ((0, 0), (0, 128 - d))))
+    w1 = rng.standard_normal((E, 2 * F, d))
+    w2 = rng.standard_normal((E, d, F)) / np.sqrt(F)
+    dyp = np.pad(dy, ((0, 0), (0, 128 - d)))           # feature blocks of 128
+    w1p = np.pad(w1, ((0, 0), (0, 0), (0, 128 - d)))
+    w2p = np.pad(w2, ((0, 0), (0, 128 - d), (0, 0)))
+    xp = np.pad(x, ((0, 0), (0, 128 - d)))
+    a = offn.backward(xp, w1p, w2p, ids, g, _q_rows(dyp))
+    b = offn.backward_fp8act(xp, w1p, w2p, ids, g, dyp, beta=beta)
+    plain = offn.backward_fp8(xp, w1p, w2p, ids, g, dyp, beta=beta)
+    for e in range(E):
+        t = _tokens_of(ids, e)
+        _check_token_blocks(b["dw1"][e][:, t].T, a["dw1"][e][:, t].T, beta)
+        assert np.abs(b["dw1"][e] - plain["dw1"][e]).max() > 0
+
+
+def test_backward_fp8act_error_bound():
+    """dx and the weight gradients stay within the e4m3 bound of the exact
+    backward (a few roundings of at most 2^-4 relative per value)."""
+    rng = np.random.default_rng(34)
+    T, k, E, d, F = 40, 2, 3, 256, 128
+    x = rng.standard_normal((T, d))
+    w1 = rng.standard_normal((E, 2 * F, d)) / np.sqrt(d)
+    w2 = rng.standard_normal((E, d, F)) / np.sqrt(F)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    g = rng.uniform(0.2, 0.9, (T, k)).astype(np.float32)
+    dy = rng.standard_normal((T, d)).astype(np.float32).astype(np.float64)
+    a = offn.backward(x, w1, w2, ids, g, dy)
+    b = offn.backward_fp8act(x, w1, w2, ids, g, dy, beta=16)
+    err = np.linalg.norm(b["dx"] - a["dx"]) / np.linalg.norm(a["dx"])
+    assert 1e-3 < err < 3 * 2.0 ** -4, err
+    for key in ("dw1", "dw2"):
+        A = np.stack([a[key][e] for e in range(E)])
+        Bq = np.stack([b[key][e] for e in range(E)])
+        err = np.linalg.norm(Bq - A) / np.linalg.norm(A)
+        assert 1e-4 < err < 3 * 2.0 ** -4, (key, err)
