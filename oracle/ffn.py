@@ -218,23 +218,30 @@ def backward_fp8act(x, w1, w2, topk_ids, gates, dy, beta, tokens=None, experts=N
     in both directions (the reading of "per-1x128 e4m3 activations" that
     forward_fp8act follows, carried to dA and dX):
 
-    * [G, U] are what the fp8-operand forward saves: Z = Q(x) W1 (Q: each row
-      in blocks of 128 features with power-of-two scales,
+    * [G, U] are what the fp8-operand forward saves: Z = Q(x) W1 stored in
+      bf16 (Q: each row in blocks of 128 features with power-of-two scales,
       oracle.fp8.quantize_row_blocks_pow2);
     * dA = p * (Q(dy_t) W2): the token's dy row is quantized, once for all of
-      its k slots, and the gate is applied to the product;
-    * dZ = [dG, dU] from dA, G and U as in backward; the layer stores dZ in
-      bf16 between the two products, so the row's dX contribution is
-      Q(bf16(dZ)) W1, and dx adds a token's k contributions in slot order;
+      its k slots, the gate is applied to the product, and dA is stored in
+      bf16 before the SwiGLU gradient;
+    * dZ = [dG, dU] from dA, G and U as in backward, stored in bf16; the row's
+      dX contribution is Q(dZ) W1, and dx adds a token's k contributions in
+      slot order;
     * the weight gradients are backward_fp8's: dW2 = Dq^T A with D = p * dy
-      (dy as given) and A from this Z, dW1 = dZq^T X with dZ (fp32) from this
-      dA and X as given; Dq and dZq are the token-axis requantizations.
+      (dy as given) and A from the saved Z, dW1 = dZq^T X with this dZ and X
+      as given; Dq and dZq are the token-axis requantizations.
+    The e4m3 codes of dZ (both quantizations) are integers decided by floating
+    point, so they are decided on the values the layer stores (bf16 Z, dA and
+    dZ), as the layer decides them.
     """
     from oracle.fp8 import (dequant_row_blocks_pow2, dequant_token_blocks,
                             quantize_row_blocks_pow2, quantize_token_blocks)
 
     def q_rows(v):
         return dequant_row_blocks_pow2(*quantize_row_blocks_pow2(np.asarray(v, dtype=np.float32)))
+
+    def bf16(v):
+        return round_bf16(np.asarray(v, dtype=np.float32)).astype(np.float64)
 
     x = np.asarray(x, dtype=np.float64)
     xh = q_rows(x)
@@ -268,13 +275,13 @@ def backward_fp8act(x, w1, w2, topk_ids, gates, dy, beta, tokens=None, experts=N
                 dw1[e] = np.zeros((2 * F, d))
                 dw2[e] = np.zeros((d, F))
             continue
-        z = xh[ti] @ w1e.T
+        z = bf16(xh[ti] @ w1e.T)
         g, u = z[:, :F], z[:, F:]
         sg = sigmoid(g)
         a = g * sg * u
-        dA = p[ti, j][:, None] * (dyh[ti] @ w2e)
-        dZ = np.concatenate([dA * u * sg * (1.0 + g * (1.0 - sg)), dA * g * sg], axis=1)
-        dX = q_rows(round_bf16(dZ.astype(np.float32))) @ w1e
+        dA = bf16(p[ti, j][:, None] * (dyh[ti] @ w2e))
+        dZ = bf16(np.concatenate([dA * u * sg * (1.0 + g * (1.0 - sg)), dA * g * sg], axis=1))
+        dX = q_rows(dZ) @ w1e
         for r in range(len(ti)):
             pos = tok_pos.get(int(ti[r]))
             if pos is not None:

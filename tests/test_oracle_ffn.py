@@ -407,26 +407,33 @@ def _check_row_blocks_pow2(q, v):
             "a value moved by more than half an e4m3 step"
 
 
+# Gates with at most four significant bits, off powers of two: p times an e4m3
+# value is then exact in bf16.
+_GATES4 = np.array([0.375, 0.625, 0.75, 0.875, 0.3125, 0.5625, 0.6875, 0.8125], dtype=np.float32)
+
+
 def _fp8act_bwd_case(seed, T=24, k=1, E=2, F=128):
-    """d = 2 F and W1 = I, so G and U are the two halves of the row and
-    dX = dZ: the exact backward's dx shows dZ itself."""
+    """d = 2 F, W1 = I and W2 picking dy's first F features, so that
+    G, U = the halves of Q(x), dA = p Q(dy)[:F] and dX = dZ; Z and dA are then
+    exact in bf16 and the exact backward's dx is dZ itself."""
     rng = np.random.default_rng(seed)
     d = 2 * F
     x = rng.standard_normal((T, d))
     w1 = np.repeat(np.eye(d)[None], E, axis=0)
-    w2 = rng.standard_normal((E, d, F)) / np.sqrt(F)
+    w2 = np.repeat(np.eye(d, F)[None], E, axis=0)
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
-    g = rng.uniform(0.2, 0.9, (T, k)).astype(np.float32)            # gates off powers of two
+    g = rng.choice(_GATES4, (T, k))
     dy = rng.standard_normal((T, d)).astype(np.float32).astype(np.float64)
     return x, w1, w2, ids, g, dy
 
 
 def test_backward_fp8act_dx_is_the_dz_rows_quantized():
-    """dX = Q(bf16(dZ)) W1 with dZ from dA = p Q(dy) W2 and Z = Q(x) W1: the
-    exact backward on Q(x) and Q(dy) gives that dZ (W1 = I exposes it in dx),
-    and the fp8-operand dx must be it, rounded to bf16 and quantized per row
-    block.  Quantizing D = p dy instead of dy, dA instead of dZ, blocks along
-    the wrong axis, or no dZ quantization, each fail it."""
+    """dX = Q(dZ) W1 with dZ (bf16) from dA = p Q(dy) W2 and Z = Q(x) W1: the
+    exact backward on Q(x) and Q(dy) gives that dZ (W1 = I exposes it in dx;
+    Z and dA are exact in bf16 here), and the fp8-operand dx must be it,
+    rounded to bf16 and quantized per row block.  Quantizing D = p dy instead
+    of dy, dA instead of dZ, blocks along the wrong axis, or no dZ
+    quantization, each fail it."""
     x, w1, w2, ids, g, dy = _fp8act_bwd_case(31)
     dz = offn.backward(_q_rows(x), w1, w2, ids, g, _q_rows(dy))["dx"]
     got = offn.backward_fp8act(x, w1, w2, ids, g, dy, beta=8)["dx"]
@@ -436,12 +443,14 @@ def test_backward_fp8act_dx_is_the_dz_rows_quantized():
 
 
 def test_backward_fp8act_dw2_takes_z_of_the_quantized_x():
-    """dW2 = Dq^T A with A from the fp8-operand forward's Z = Q(x) W1 and D
-    from dy as given: it is backward_fp8's dW2 on Q(x)."""
+    """dW2 = Dq^T A with A from the fp8-operand forward's Z = Q(x) W1 (W1 = I:
+    Z exact in bf16) and D from dy as given: it is backward_fp8's dW2 on
+    Q(x), and not the one on x."""
     rng = np.random.default_rng(32)
-    T, k, E, d, F = 40, 2, 3, 256, 128
+    T, k, E, F = 40, 2, 3, 128
+    d = 2 * F
     x = rng.standard_normal((T, d))
-    w1 = rng.standard_normal((E, 2 * F, d)) / np.sqrt(d)
+    w1 = np.repeat(np.eye(d)[None], E, axis=0)
     w2 = rng.standard_normal((E, d, F)) / np.sqrt(F)
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
     g = rng.uniform(0.2, 0.9, (T, k)).astype(np.float32)
@@ -456,26 +465,27 @@ def test_backward_fp8act_dw2_takes_z_of_the_quantized_x():
 
 def test_backward_fp8act_dw1_takes_dz_of_the_quantized_dy():
     """With x_t = e_t (on the e4m3 grid, so Q(x) = x) column t of dW1_e is the
-    token-axis requantized dZ row of token t, whose dZ comes from dA =
-    p Q(dy) W2: each block of beta slots times one column keeps its maximum,
-    lies on that column's e4m3 grid and stays within half a step of the exact
-    backward's dZ on Q(dy)."""
+    token-axis requantized dZ row of token t, whose dZ (bf16) comes from
+    dA = p Q(dy) W2: each block of beta slots times one column keeps its
+    maximum, lies on that column's e4m3 grid and stays within half a step of
+    the exact backward's dZ on Q(dy), rounded to bf16 (W1 exact in bf16 and W2
+    picking features keep Z and dA exact in bf16)."""
     beta = 8
     rng, x, ids, g, dy = _onehot_case(33)
+    g = rng.choice(_GATES4, g.shape)
     E, d, F = 3, x.shape[1], 64                        # dZ rows: one block of 128
-    assert np.array_equal(_q_rows(np.pad(x, ((0, 0), (0, 128 - d)))), np.pad(x, ((0, 0), (0, 128 - d))))
-    w1 = rng.standard_normal((E, 2 * F, d))
-    w2 = rng.standard_normal((E, d, F)) / np.sqrt(F)
-    dyp = np.pad(dy, ((0, 0), (0, 128 - d)))           # feature blocks of 128
-    w1p = np.pad(w1, ((0, 0), (0, 0), (0, 128 - d)))
-    w2p = np.pad(w2, ((0, 0), (0, 128 - d), (0, 0)))
-    xp = np.pad(x, ((0, 0), (0, 128 - d)))
-    a = offn.backward(xp, w1p, w2p, ids, g, _q_rows(dyp))
-    b = offn.backward_fp8act(xp, w1p, w2p, ids, g, dyp, beta=beta)
-    plain = offn.backward_fp8(xp, w1p, w2p, ids, g, dyp, beta=beta)
+    pad = ((0, 0), (0, 128 - d))
+    xp, dyp = np.pad(x, pad), np.pad(dy, pad)          # feature blocks of 128
+    assert np.array_equal(_q_rows(xp), xp)
+    w1 = offn.round_bf16(rng.standard_normal((E, 2 * F, 128)).astype(np.float32)).astype(np.float64)
+    w2 = np.repeat(np.eye(128, F)[None], E, axis=0)
+    a = offn.backward(xp, w1, w2, ids, g, _q_rows(dyp))
+    b = offn.backward_fp8act(xp, w1, w2, ids, g, dyp, beta=beta)
+    plain = offn.backward_fp8(xp, w1, w2, ids, g, dyp, beta=beta)
     for e in range(E):
         t = _tokens_of(ids, e)
-        _check_token_blocks(b["dw1"][e][:, t].T, a["dw1"][e][:, t].T, beta)
+        ref = offn.round_bf16(a["dw1"][e][:, t].T.astype(np.float32)).astype(np.float64)
+        _check_token_blocks(b["dw1"][e][:, t].T, ref, beta)
         assert np.abs(b["dw1"][e] - plain["dw1"][e]).max() > 0
 
 
