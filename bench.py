@@ -620,20 +620,24 @@ def main():
         "kernels": per_kernel,
     }
     if w.wdt == "fp8":
-        # the same steps with FC1 and FC2 on the fp8 MFMA (MOE_EXEC_FP8_ACT: x
-        # and A quantized per row block of 128 features), each stage priced
-        # against the fp8 peak; the fc1 stage includes both quantization passes
+        # the same steps with FC1, FC2 (and with a backward dA, dX) on the fp8
+        # MFMA (MOE_EXEC_FP8_ACT: x, A, dy and dZ quantized per row block of
+        # 128 features), each of those stages priced against the fp8 peak; the
+        # fc1 stage includes the quantization of x and A, the dA stage that of
+        # dy, the requantization of D and the SwiGLU gradient pass that
+        # quantizes dZ
         case["runner"].fp8_act = True
         ms_f8, st_f8 = time_steps(case, args.steps, args.warmup)
         case["runner"].fp8_act = False
-        gemm = {"fc1": 4 * w.d * w.d_ff * R, "fc2": 2 * w.d * w.d_ff * R}
+        gemm = {"fwd.fc1": 4 * w.d * w.d_ff * R, "fwd.fc2": 2 * w.d * w.d_ff * R,
+                "bwd.dA": 2 * w.d * w.d_ff * R, "bwd.dX": 4 * w.d * w.d_ff * R}
         out["fp8_act"] = {
             "ms_per_step": round(ms_f8, 4),
             "tflops": round(useful / (ms_f8 * 1e-3) / 1e12, 3),
             "stages_us": {k: round(v * 1e3, 2) for k, v in st_f8.items()},
         }
         for k, fl in gemm.items():
-            us = st_f8.get("fwd." + k, 0.0) * 1e3
+            us = st_f8.get(k, 0.0) * 1e3
             if us:
                 tf = fl / (us * 1e-6) / 1e12
                 out["fp8_act"][k] = {"tflops": round(tf, 1),

@@ -81,19 +81,22 @@ typedef enum {
  * plan.  The results are the same bits in every mode. */
 #define MOE_EXEC_SPLIT_SHIFT 8
 #define MOE_EXEC_SPLIT(n1) (((n1) & 0xff) << MOE_EXEC_SPLIT_SHIFT)
-/* moe_forward only, e4m3 weights on the persistent stream kernels (d and
- * d_ff multiples of 256), two launches: FC1 and FC2 run on the fp8 MFMA
- * (v_mfma_scale_f32_32x32x64_f8f6f4).  x is quantized per token row and 128
- * features with power-of-two scales (moe_quantize_act_rows) into the
- * workspace; FC1's activations A = SiLU(G) * U, stored as bf16, are quantized
- * the same way, only the rows of the blocks in use.  The row exponents ride
- * in the MFMA's scale operand, the weights' codes are used as stored, and per
- * 128-deep K block the weights' fp32 block scale is applied to the
- * accumulators.  The results differ from the default path by the two
- * quantizations (relative error about 2^-5 per value); the saved [G, U] of a
- * backward-capable call come from the quantized x.  MOE_ERR_ARG for the flag
- * with moe_backward, a two-phase launch, activations other than bf16,
- * weights other than e4m3, or a layer off the stream kernels. */
+/* e4m3 weights on the persistent stream kernels (d and d_ff multiples of
+ * 256), two launches: every product except the weight gradients runs on the
+ * fp8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4), its activation operand
+ * quantized per row and 128 features with power-of-two scales
+ * (moe_quantize_act_rows), the weights' codes used as stored and their fp32
+ * block scales applied to the accumulators per 128-deep K block.
+ *   moe_forward: x, and A = SiLU(G) * U as stored in bf16 (only the rows of
+ *   the blocks in use), feed FC1 and FC2; the saved [G, U] come from the
+ *   quantized x.
+ *   moe_backward: dy feeds dA, and dZ, formed in bf16 from dA (stored in bf16)
+ *   and the saved [G, U], feeds dX; the weight gradients are the default
+ *   path's, with D and dZ requantized along the tokens.
+ * The results differ from the default path by these quantizations (relative
+ * error about 2^-5 per value).  MOE_ERR_ARG with the two-phase launch,
+ * activations other than bf16, weights other than e4m3, or a layer off the
+ * stream kernels. */
 #define MOE_EXEC_FP8_ACT 2
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
@@ -314,7 +317,8 @@ int moe_predict_split(const int32_t* counts, const int32_t* block_offsets,
  *   z_save (nullable) [moe_max_slots][2*d_ff] act dtype: receives [G, U] of
  *     every routed row, as needed by moe_backward.
  *   exec_flags: 0, or MOE_EXEC_TWO_PHASE (FC1 and FC2 in one launch), with
- *     an optional MOE_EXEC_SPLIT(n1) (FC1 producers and FC2 consumers).
+ *     an optional MOE_EXEC_SPLIT(n1) (FC1 producers and FC2 consumers); or
+ *     MOE_EXEC_FP8_ACT (e4m3 weights: FC1 and FC2 on the fp8 MFMA).
  *   stage_events (host, nullable): 5 hipEvent_t recorded on `stream` at
  *     start / after scheduling / after FC1 / after FC2 / after combine (with
  *     MOE_EXEC_TWO_PHASE the FC1 and FC2 events follow the one launch).
@@ -350,7 +354,8 @@ int moe_forward(const moe_layer* L, const void* x, const float* gates,
  *   dy [T][d], z_save from moe_forward on the same routing, owner [E] = h(e);
  *   dx [T][d] act dtype; dw1 [E][2*d_ff][d] fp32; dw2 [E][d][d_ff] fp32.
  *   exec_flags: 0, or MOE_EXEC_TWO_PHASE (dA and dX in one launch), with
- *     an optional MOE_EXEC_SPLIT(n1) (dA producers and dX consumers).
+ *     an optional MOE_EXEC_SPLIT(n1) (dA producers and dX consumers); or
+ *     MOE_EXEC_FP8_ACT (e4m3 weights: dA and dX on the fp8 MFMA).
  *   stage_events (host, nullable): 7 events: start / after scheduling /
  *     after dA / after dX / after dx combine / after weight gradients /
  *     after replica reduction (with MOE_EXEC_TWO_PHASE the dA and dX events
@@ -410,8 +415,8 @@ int moe_quantize_token_blocks(const void* src, int ld, int src_rows, const int32
  * of row r gets the power-of-two scale 2^e, e the smallest integer with
  * amax <= 448 * 2^e, clamped to [-127, 127] (-127 for a zero block), and
  * codes[r][c] = e4m3(src[r][c] * 2^-e), round to nearest even (the product
- * is exact).  This is how MOE_EXEC_FP8_ACT quantizes x for FC1 and A for
- * FC2.
+ * is exact).  This is how MOE_EXEC_FP8_ACT quantizes x, A and dy (dZ is
+ * quantized the same way where it is formed).
  *   codes uint8 [rows][cols]; exps int32 [cols / 128][rows] (block-major:
  *   exps[b * rows + r] = e), all device memory owned by the caller.
  * Errors: MOE_ERR_ARG for rows < 0, cols not a positive multiple of 128, or

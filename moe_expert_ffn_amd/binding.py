@@ -420,7 +420,8 @@ def forward(layer: Layer, x, gates, topk_ids, beta, P, rs, block_worker, y, z_sa
 
 
 def backward(layer: Layer, x, gates, dy, z_save, topk_ids, beta, P, s, rs, owner, block_worker,
-             dx, dw1, dw2, ws, status, events=None, timeline=None, two_phase=False, split=0):
+             dx, dw1, dw2, ws, status, events=None, timeline=None, two_phase=False, split=0,
+             fp8_act=False):
     _require_device(x, gates, dy, z_save, topk_ids, owner, block_worker, dx, dw1, dw2, ws, status,
                     timeline)
     _expect_timeline(timeline)
@@ -444,7 +445,7 @@ def backward(layer: Layer, x, gates, dy, z_save, topk_ids, beta, P, s, rs, owner
                                _ptr(rs["block_offsets"]), _ptr(rs["row_to_slot"]),
                                _ptr(rs["slot_to_row"]), _ptr(owner), _ptr(block_worker), _ptr(dx),
                                _ptr(dw1), _ptr(dw2), _ptr(status), wsp, wsn,
-                               exec_flags(two_phase, split), ev, _ptr(timeline),
+                               exec_flags(two_phase, split, fp8_act), ev, _ptr(timeline),
                                _stream()))
 
 

@@ -244,9 +244,9 @@ int moe_predict_split(const int32_t* counts, const int32_t* block_offsets,
 
 // known bits only; a producer/consumer split only with the two-phase launch
 // (its upper bound, the workgroups of one worker, is checked at launch)
-static bool exec_flags_ok(int f, bool backward) {
+static bool exec_flags_ok(int f) {
   const int split = (f >> MOE_EXEC_SPLIT_SHIFT) & 0xff;
-  const int known = MOE_EXEC_TWO_PHASE | MOE_EXEC_SPLIT(0xff) | (backward ? 0 : MOE_EXEC_FP8_ACT);
+  const int known = MOE_EXEC_TWO_PHASE | MOE_EXEC_SPLIT(0xff) | MOE_EXEC_FP8_ACT;
   if (f & ~known) return false;
   return split == 0 || (f & MOE_EXEC_TWO_PHASE);
 }
@@ -259,7 +259,7 @@ int moe_forward(const moe_layer* L, const void* x, const float* gates, const int
                 void* const* stage_events, uint64_t* timeline, void* stream) {
   (void)topk_ids;
   const int lc = check_layer(L, false);
-  if (!exec_flags_ok(exec_flags, false)) return MOE_ERR_ARG;
+  if (!exec_flags_ok(exec_flags)) return MOE_ERR_ARG;
   if (lc != MOE_OK) return lc;
   if (!sizes_ok(T, k, L->E, beta)) return MOE_ERR_ARG;
   if (!valid_P(P)) return MOE_ERR_UNSUPPORTED;
@@ -289,7 +289,7 @@ int moe_backward(const moe_layer* L, const void* x, const float* gates, const vo
                  void* const* stage_events, uint64_t* timeline, void* stream) {
   (void)topk_ids;
   const int lc = check_layer(L, true);
-  if (!exec_flags_ok(exec_flags, true)) return MOE_ERR_ARG;
+  if (!exec_flags_ok(exec_flags)) return MOE_ERR_ARG;
   if (lc != MOE_OK) return lc;
   if (!sizes_ok(T, k, L->E, beta) || s < 0) return MOE_ERR_ARG;
   if (!valid_P(P)) return MOE_ERR_UNSUPPORTED;
@@ -298,6 +298,11 @@ int moe_backward(const moe_layer* L, const void* x, const float* gates, const vo
     return MOE_ERR_ARG;
   const Sizes z = make_sizes(L, T, k, beta, P, s);
   if (!extents_ok(z)) return MOE_ERR_UNSUPPORTED;
+  // dA and dX on the fp8 MFMA: bf16 dy, e4m3 weights on the stream kernels, two launches
+  if ((exec_flags & MOE_EXEC_FP8_ACT) &&
+      (L->act_dtype != MOE_BF16 || L->w_dtype != MOE_FP8_E4M3 || !use_stream(z) ||
+       (exec_flags & MOE_EXEC_TWO_PHASE)))
+    return MOE_ERR_ARG;
   if (!ws_ok(ws, ws_bytes, exec_layout(z, true).total)) return MOE_ERR_WORKSPACE;
   LayerPtrs Lp{L->w1, L->w2, L->w1_scale, L->w2_scale, L->act_dtype, L->w_dtype};
   return launch_backward(z, Lp, x, gates, dy, z_save, counts, block_offsets, row_to_slot,

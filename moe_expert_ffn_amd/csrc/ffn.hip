@@ -246,8 +246,9 @@ struct ExecArgs {
   float* dqs;             //   its scales [slots / beta][d]
   uint8_t* zq;            //   dZ, e4m3 [slots][2 d_ff]
   float* zqs;             //   its scales [slots / beta][2 d_ff]
-  const void* xq;         // fp8 MFMA forward: x codes [T][d] and exponents [d/128][T],
-  const int32_t* xe;      // A codes [slots][d_ff] and exponents [d_ff/128][slots]
+  const void* xq;         // fp8 MFMA: x (dy in the backward) codes [T][d] and exponents
+  const int32_t* xe;      // [d/128][T]; A (dZ) codes [slots][d_ff (2 d_ff)] and exponents
+                          // [d_ff/128 (2 d_ff/128)][slots]
   void* hq;
   int32_t* he;
   void* dhat;             // fp8 backward on the stream kernels: D requantized and
@@ -743,6 +744,113 @@ int launch_quant_act(const uint16_t* x, int rows, int cols, uint8_t* codes, int3
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+MOE_DEV float sigm(float g) { return __builtin_amdgcn_rcpf(1.f + __expf(-g)); }
+
+// SwiGLU gradient and dZ's e4m3 rows for dX on the fp8 MFMA: for each slot
+// row s in use (s < *blk_end * beta, slot_to_row[s] >= 0) and feature f of
+// d_ff, from dA (bf16 [slots][d_ff], gate applied) and [G, U] (z_save
+// [slots][2 d_ff]): sg = sigmoid(G), dG = dA U sg (1 + G (1 - sg)),
+// dU = dA G sg, P = SiLU(G) U.  dZ = [dG, dU] is stored bf16 into dz
+// [slots][2 d_ff] and P into p [slots][d_ff]; dZ's bf16 values are
+// quantized per row and 128 features as k_quant_act quantizes rows (codes
+// [slots][2 d_ff], exps [2 d_ff / 128][slots]).  A task is one row and group
+// of 4 blocks of 128 features, one wave, 16 lanes a block, 8 features a
+// lane; waves walk the tasks grid-stride.  Padding slots are left alone.
+__global__ __launch_bounds__(256) void k_swiglu_bwd_q(
+    const uint16_t* __restrict__ dA, const uint16_t* __restrict__ Z,
+    const int32_t* __restrict__ slot_to_row, int slots, int dff, uint16_t* __restrict__ dz,
+    uint16_t* __restrict__ P, uint8_t* __restrict__ codes, int32_t* __restrict__ exps,
+    const int32_t* __restrict__ blk_end, int beta) {
+  const int nb = dff / 128, ng = (nb + 3) / 4;
+  const long long rl = min((long long)slots, (long long)*blk_end * beta);
+  const long long ntask = rl * ng, nw = (long long)gridDim.x * 4;
+  const int lane = threadIdx.x & 63;
+  for (long long t = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); t < ntask; t += nw) {
+    const int r = (int)(t / ng);
+    if (slot_to_row[r] < 0) continue;                       // wave-uniform
+    const int b = (int)(t % ng) * 4 + (lane >> 4);
+    const bool on = b < nb;
+    const int c = b * 128 + 8 * (lane & 15);
+    uint4 qa = make_uint4(0, 0, 0, 0), qg = qa, qu = qa;
+    if (on) {
+      qa = *(const uint4*)(dA + (size_t)r * dff + c);
+      qg = *(const uint4*)(Z + (size_t)r * 2 * dff + c);
+      qu = *(const uint4*)(Z + (size_t)r * 2 * dff + dff + c);
+    }
+    const uint32_t wa[4] = {qa.x, qa.y, qa.z, qa.w}, wg[4] = {qg.x, qg.y, qg.z, qg.w},
+                   wu[4] = {qu.x, qu.y, qu.z, qu.w};
+    float vg[8], vu[8];
+    uint32_t og[4], ou[4], op[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int sh = (i & 1) ? 16 : 0;
+      const float da = bf2f((uint16_t)(wa[i >> 1] >> sh)), g = bf2f((uint16_t)(wg[i >> 1] >> sh)),
+                  u = bf2f((uint16_t)(wu[i >> 1] >> sh));
+      const float sg = sigm(g);
+      const uint16_t hg = f2bf(da * u * sg * (1.f + g * (1.f - sg)));
+      const uint16_t hu = f2bf(da * g * sg);
+      const uint16_t hp = f2bf(g * sg * u);
+      vg[i] = bf2f(hg);
+      vu[i] = bf2f(hu);
+      if (i & 1) {
+        og[i >> 1] |= (uint32_t)hg << 16;
+        ou[i >> 1] |= (uint32_t)hu << 16;
+        op[i >> 1] |= (uint32_t)hp << 16;
+      } else {
+        og[i >> 1] = hg;
+        ou[i >> 1] = hu;
+        op[i >> 1] = hp;
+      }
+    }
+    float mg = 0.f, mu = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      mg = fmaxf(mg, fabsf(vg[i]));
+      mu = fmaxf(mu, fabsf(vu[i]));
+    }
+#pragma unroll
+    for (int sh = 8; sh >= 1; sh >>= 1) {                   // within 16 lanes
+      mg = fmaxf(mg, __shfl_xor(mg, sh, 64));
+      mu = fmaxf(mu, __shfl_xor(mu, sh, 64));
+    }
+    const int eg = e8_exponent(mg), eu = e8_exponent(mu);
+    uint32_t cg[2], cu[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int p = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(vg[4 * h], -eg), ldexpf(vg[4 * h + 1], -eg), 0,
+                                              false);
+      cg[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(vg[4 * h + 2], -eg),
+                                                        ldexpf(vg[4 * h + 3], -eg), p, true);
+      p = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(vu[4 * h], -eu), ldexpf(vu[4 * h + 1], -eu), 0,
+                                          false);
+      cu[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(vu[4 * h + 2], -eu),
+                                                        ldexpf(vu[4 * h + 3], -eu), p, true);
+    }
+    if (on) {
+      const size_t rz = (size_t)r * 2 * dff;
+      *(uint4*)(dz + rz + c) = make_uint4(og[0], og[1], og[2], og[3]);
+      *(uint4*)(dz + rz + dff + c) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+      *(uint4*)(P + (size_t)r * dff + c) = make_uint4(op[0], op[1], op[2], op[3]);
+      *(uint2*)(codes + rz + c) = make_uint2(cg[0], cg[1]);
+      *(uint2*)(codes + rz + dff + c) = make_uint2(cu[0], cu[1]);
+      if ((lane & 15) == 0) {
+        exps[(size_t)b * slots + r] = eg;
+        exps[(size_t)(nb + b) * slots + r] = eu;
+      }
+    }
+  }
+}
+
+static void launch_swiglu_bwd_q(const ExecArgs& a, int dff, const int32_t* blk_end, int beta,
+                                hipStream_t st) {
+  const long long tasks = (long long)a.slots * ((dff / 128 + 3) / 4);
+  if (tasks > 0)
+    hipLaunchKernelGGL(k_swiglu_bwd_q, dim3((unsigned)std::min((tasks + 3) / 4, kQuantActWG)),
+                       dim3(256), 0, st, (const uint16_t*)a.bufO, (const uint16_t*)a.z_save,
+                       a.slot_to_row, (int)a.slots, dff, (uint16_t*)a.bufA, (uint16_t*)a.bufP,
+                       (uint8_t*)a.hq, a.he, blk_end, beta);
+}
+
 // The same blocks, written back as bf16 code * scale into deq [rows][cols].
 static void launch_quant_dequant(const uint16_t* src, int ld, const int32_t* map, int gather,
                                  int div, const float* rscale, int map_lim, int rows, int cols,
@@ -941,7 +1049,6 @@ __global__ __launch_bounds__(C::NT) void k_bwd_dx(ExecArgs a) {
 // items (M tile x N tile) in a static sequence through WideStream.  Fast exp
 // and reciprocal in the SiLU terms: their error is far below the bf16
 // rounding of every value they feed.
-MOE_DEV float sigm(float g) { return __builtin_amdgcn_rcpf(1.f + __expf(-g)); }
 
 using WC = WideCfg;
 constexpr int kWNW = WC::NT / 64;
@@ -1233,24 +1340,43 @@ constexpr size_t kScOff8 = kStreamLds;           // two 1 KB exponent regions af
 constexpr size_t kStreamLds8 = kStreamLds + 2 * 1024;
 using RowA8 = RowK8A<256, kWNW, kScOff8>;
 using RowW8 = RowK8W<256, kWNW>;
+// The tile's rows as quantized token rows: codes [T][d] (read as element
+// offsets of code pairs, token * d / 2) and exponents [d / 128][T].
+MOE_DEV RowA8 gathered8(const ExecArgs& a, const MItem& it, const MOE_LDS int* rows,
+                        const void* codes, const int32_t* exps) {
+  using RB = typename RowA8::Base;
+  int o[RB::NI];
+#pragma unroll
+  for (int i = 0; i < RB::NI; ++i) {
+    const int row = RB::lane_row(i);
+    o[i] = row < it.nrows ? (int)token_of((uint32_t)rows[row], a.kmagic) * (a.d / 2) : -1;
+  }
+  RowA8 x;
+  x.init_offsets((const uint16_t*)codes, (uint32_t)((size_t)a.T * a.d), o);
+  const int w = wave_id(), row = w * 64 + (threadIdx.x & 63);
+  x.rsc = make_rsrc(exps, (uint32_t)((size_t)(a.d / 128) * a.T * 4));
+  x.scs = (uint32_t)a.T * 4u;
+  x.sco = (w < 4 && row < it.nrows) ? token_of((uint32_t)rows[row], a.kmagic) * 4u : kOob;
+  return x;
+}
+// The tile's slot rows of quantized codes [slots][ld] and exponents
+// [ld / 128][slots].
+MOE_DEV RowA8 slotrows8(const ExecArgs& a, const MItem& it, const void* codes,
+                        const int32_t* exps, int ld) {
+  RowA8 x;
+  x.init((const uint16_t*)codes, (uint32_t)((size_t)a.slots * ld),
+         [&](int row) { return row < it.nrows ? (it.slot0 + row) * (ld / 2) : -1; });
+  const int w = wave_id(), row = w * 64 + (threadIdx.x & 63);
+  x.rsc = make_rsrc(exps, (uint32_t)((size_t)(ld / 128) * a.slots * 4));
+  x.scs = (uint32_t)a.slots * 4u;
+  x.sco = (w < 4 && row < it.nrows) ? (uint32_t)(it.slot0 + row) * 4u : kOob;
+  return x;
+}
+
 struct SrcFc1F8 : SrcFc1T<true> {
   using OB = RowW8;
   MOE_DEV RowA8 opA(const Item& it, int slot) const {
-    const MOE_LDS int* rows = item_rows(smem, slot);
-    using RB = typename RowA8::Base;
-    int o[RB::NI];
-#pragma unroll
-    for (int i = 0; i < RB::NI; ++i) {
-      const int row = RB::lane_row(i);   // element offsets of bf16 pairs: token * d / 2
-      o[i] = row < it.nrows ? (int)token_of((uint32_t)rows[row], a.kmagic) * (a.d / 2) : -1;
-    }
-    RowA8 x;
-    x.init_offsets((const uint16_t*)a.xq, (uint32_t)((size_t)a.T * a.d), o);
-    const int w = wave_id(), row = w * 64 + (threadIdx.x & 63);
-    x.rsc = make_rsrc(a.xe, (uint32_t)((size_t)(a.d / 128) * a.T * 4));
-    x.scs = (uint32_t)a.T * 4u;
-    x.sco = (w < 4 && row < it.nrows) ? token_of((uint32_t)rows[row], a.kmagic) * 4u : kOob;
-    return x;
+    return gathered8(a, it, item_rows(smem, slot), a.xq, a.xe);
   }
   MOE_DEV RowW8 opB(const Item& it, int) const {
     RowW8 w;
@@ -1320,16 +1446,7 @@ template <bool FP8> struct SrcFc2T : MSrcBase {
 // epilogue (gate, O rows) is FC2's.
 struct SrcFc2F8 : SrcFc2T<true> {
   using OB = RowW8;
-  MOE_DEV RowA8 opA(const Item& it, int) const {
-    RowA8 x;
-    x.init((const uint16_t*)a.hq, (uint32_t)((size_t)a.slots * a.dff),
-           [&](int row) { return row < it.nrows ? (it.slot0 + row) * (a.dff / 2) : -1; });
-    const int w = wave_id(), row = w * 64 + (threadIdx.x & 63);
-    x.rsc = make_rsrc(a.he, (uint32_t)((size_t)(a.dff / 128) * a.slots * 4));
-    x.scs = (uint32_t)a.slots * 4u;
-    x.sco = (w < 4 && row < it.nrows) ? (uint32_t)(it.slot0 + row) * 4u : kOob;
-    return x;
-  }
+  MOE_DEV RowA8 opA(const Item& it, int) const { return slotrows8(a, it, a.hq, a.he, a.dff); }
   MOE_DEV RowW8 opB(const Item& it, int) const {
     RowW8 w;
     const int nj = it.nj, dff = a.dff;
@@ -1495,6 +1612,67 @@ template <bool FP8> struct SrcDxT : MSrcBase {
       });
     }
   }
+};
+
+// dA and dX on the fp8 MFMA (MOE_EXEC_FP8_ACT): the A rows are dy's token
+// rows (dA) or the bf16 dZ slot rows (dX) quantized per row and 128 features
+// with power-of-two scales (k_quant_act into xq / xe and hq / he), the B
+// operand the weights' codes read K-major into the fp8 MFMA's layout, a K step
+// of 128 codes; the epilogues are dA's and dX's.
+using MnK8W = MnK8<256, kWNW>;
+using MnK8Op = MnKOperand<MnK8W, MnFixed>;
+struct SrcDaF8 : SrcDaT<true> {
+  using OB = MnK8Op;
+  MOE_DEV RowA8 opA(const Item& it, int slot) const {
+    return gathered8(a, it, item_rows(smem, slot), a.xq, a.xe);
+  }
+  MOE_DEV MnK8Op opB(const Item& it, int) const {   // W2 [d][d_ff] codes; block (kt, 2 nj + wn / 2)
+    MnK8W m;
+    m.rs = make_rsrc((const uint8_t*)a.w2 + (size_t)it.e * a.d * a.dff, (uint32_t)((size_t)a.d * a.dff));
+    const int wn = wave_id() % WC::WAVES_N;
+    m.sp = (const MOE_CONST float*)a.w2s + (size_t)it.e * (a.d / 128) * (a.dff / 128) +
+           (2 * it.nj + wn / 2);
+    m.sld = a.dff / 128;
+    return {m, MnFixed{(uint32_t)a.dff, (uint32_t)it.nj * WC::BN}};
+  }
+  MOE_DEV int steps(const Item&) const { return a.d / 128; }
+  // p dA rows as bf16 into bufO [slots][d_ff]; dZ and P follow in
+  // k_swiglu_bwd_q (forming them here, with the [G, U] loads, takes the
+  // kernel past 256 VGPRs and spills inside its K loop)
+  static constexpr int kEpiVm = WC::MB * RowStore<uint16_t, 2>::STORES;
+  template <int B> MOE_DEV void relaxed_wait() const { wait_vm_lgkm0<vm_clamp(B + kEpiVm)>(); }
+  MOE_DEV void epilogue(const Item& it, int slot, const f32x16_t (&acc)[WC::MB][WC::NB]) const {
+    const int lane = threadIdx.x & 63, wm = wave_id() / WC::WAVES_N, wn = wave_id() % WC::WAVES_N;
+    const MOE_LDS float* gt = item_gates(smem, slot);
+    const BufRsrc ro = make_rsrc(a.bufO, (uint32_t)(a.slots * a.dff * 2));
+    const int colb = it.nj * WC::BN + wn * WC::WN;
+    MOE_LDS char* scr = epi_scratch(smem);
+#pragma unroll
+    for (int i = 0; i < WC::MB; ++i) {
+      const int rb = wm * WC::WM + i * 32;
+      const float pg = gt[rb + (lane & 31)];
+      RowStore<uint16_t, 2>::run(scr, [&](int jj, int g, float* v) {
+        for (int q = 0; q < 4; ++q) v[q] = pg * acc[i][jj][4 * g + q];
+      }, [&](int row, int c, const u32x4_t& d) {
+        st_row16(ro, it.slot0 + rb + row, a.dff, colb + c * 8, rb + row < it.nrows, d);
+      });
+    }
+  }
+};
+struct SrcDxF8 : SrcDxT<true> {
+  using OB = MnK8Op;
+  MOE_DEV RowA8 opA(const Item& it, int) const { return slotrows8(a, it, a.hq, a.he, 2 * a.dff); }
+  MOE_DEV MnK8Op opB(const Item& it, int) const {   // W1 [2 d_ff][d] codes; block (kt, 2 nj + wn / 2)
+    MnK8W m;
+    m.rs = make_rsrc((const uint8_t*)a.w1 + (size_t)it.e * 2 * a.dff * a.d,
+                     (uint32_t)((size_t)2 * a.dff * a.d));
+    const int wn = wave_id() % WC::WAVES_N;
+    m.sp = (const MOE_CONST float*)a.w1s + (size_t)it.e * (2 * a.dff / 128) * (a.d / 128) +
+           (2 * it.nj + wn / 2);
+    m.sld = a.d / 128;
+    return {m, MnFixed{(uint32_t)a.d, (uint32_t)it.nj * WC::BN}};
+  }
+  MOE_DEV int steps(const Item&) const { return 2 * a.dff / 128; }
 };
 
 // Two GEMM phases in one persistent launch (MegaFlux summary, Methodology
@@ -1994,11 +2172,12 @@ WsLayout exec_layout(const Sizes& z, bool backward) {
   L.bufP = backward ? take((size_t)z.act_bytes * z.max_slots * z.dff) : o;
   L.sgate = take(sizeof(float) * z.max_slots);
   L.dq = L.dqs = L.zq = L.zqs = L.dhat = L.xq = L.xe = L.hq = L.he = o;
-  if (!backward && z.fp8 && use_stream(z)) {      // MOE_EXEC_FP8_ACT
+  if (z.fp8 && use_stream(z)) {      // MOE_EXEC_FP8_ACT: x (dy) and A (dZ) as e4m3 rows
+    const size_t hc = (size_t)(backward ? 2 : 1) * z.dff;
     L.xq = take((size_t)z.T * z.d);
     L.xe = take(sizeof(int32_t) * (size_t)(z.d / 128) * z.T);
-    L.hq = take(z.max_slots * (size_t)z.dff);
-    L.he = take(sizeof(int32_t) * (size_t)(z.dff / 128) * z.max_slots);
+    L.hq = take(z.max_slots * hc);
+    L.he = take(sizeof(int32_t) * (hc / 128) * z.max_slots);
   }
   if (backward && z.fp8 && use_stream(z)) {
     L.dhat = take((size_t)2 * z.max_slots * z.d);           // requantized D as bf16
@@ -2273,10 +2452,14 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
 // With e4m3 weights (FP8): D = p dy per slot is requantized along the tokens
 // and widened back to bf16 (dhat) before dA; dZ is requantized in place in
 // bufA once dX has used it; the weight gradients then read both as bf16.
+// With f8act (FP8 only, MOE_EXEC_FP8_ACT) dA and dX run on the fp8 MFMA:
+// dy's rows are quantized per 128 features before dA; dA leaves as bf16 rows
+// (bufO), and k_swiglu_bwd_q forms dZ and P from them and quantizes dZ's rows
+// for dX.
 template <bool FP8>
 static void run_backward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* dx,
-                                float* dw1, float* dw2, bool split, int n1split, void* const* ev,
-                                hipStream_t st) {
+                                float* dw1, float* dw2, bool split, int n1split, bool f8act,
+                                void* const* ev, hipStream_t st) {
   const int rows = (int)z.max_slots;
   launch_slot_gate(z, a, st);
   if constexpr (FP8)
@@ -2284,7 +2467,14 @@ static void run_backward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_
                          rows, z.d, z.beta, (uint16_t*)a.dhat, a.boff + z.E, st);
   const int n1 = z.dff / WC::BN, n2 = z.d / WC::BN;
   a.tl_phase = MOE_TL_DA;
-  if (split) {
+  if (FP8 && f8act) {
+    launch_quant_act((const uint16_t*)a.dy, z.T, z.d, (uint8_t*)a.xq, (int32_t*)a.xe, st);
+    launch_stream<SrcDaF8, WC, RowA8, MnK8Op>(a, n1, kStreamLds8, st);
+    launch_swiglu_bwd_q(a, z.dff, a.boff + z.E, z.beta, st);
+    rec(ev, 2, st);
+    a.tl_phase = MOE_TL_DX;
+    launch_stream<SrcDxF8, WC, RowA8, MnK8Op>(a, n2, kStreamLds8, st);
+  } else if (split) {
     launch_stream<SrcDaT<FP8>, WC, RowW, typename SrcDaT<FP8>::OB>(a, n1, kStreamLds, st);
     rec(ev, 2, st);
     a.tl_phase = MOE_TL_DX;
@@ -2350,6 +2540,9 @@ int launch_backward(const Sizes& z, const LayerPtrs& Lp, const void* x, const fl
   bool split = true;
   const int n1split = exec_split(exec_flags, z.P, &split);
   if (n1split < 0) return MOE_ERR_ARG;
+  if ((exec_flags & MOE_EXEC_FP8_ACT) &&
+      (Lp.act_dtype != MOE_BF16 || Lp.w_dtype != MOE_FP8_E4M3 || !use_stream(z) || !split))
+    return MOE_ERR_ARG;
   const WsLayout L = exec_layout(z, true);
   rec(ev, 0, st);
   launch_sched(z, counts, boff, block_worker, owner, true, ws, L, status, st);
@@ -2363,11 +2556,12 @@ int launch_backward(const Sizes& z, const LayerPtrs& Lp, const void* x, const fl
   if (Lp.act_dtype == MOE_F32) run_backward<float, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else if (Lp.w_dtype == MOE_FP8_E4M3) {
     if (use_stream(z))
-      run_backward_stream<true>(z, a, row_to_slot, dx, dw1, dw2, split, n1split, ev, st);
+      run_backward_stream<true>(z, a, row_to_slot, dx, dw1, dw2, split, n1split,
+                                (exec_flags & MOE_EXEC_FP8_ACT) != 0, ev, st);
     else if (use_big_tiles(z)) run_backward<uint16_t, BigCfg, true>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
     else run_backward<uint16_t, SmallCfg, true>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   } else if (use_stream(z))
-    run_backward_stream<false>(z, a, row_to_slot, dx, dw1, dw2, split, n1split, ev, st);
+    run_backward_stream<false>(z, a, row_to_slot, dx, dw1, dw2, split, n1split, false, ev, st);
   else if (use_big_tiles(z)) run_backward<uint16_t, BigCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   else run_backward<uint16_t, SmallCfg>(z, a, row_to_slot, dx, dw1, dw2, ev, st);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;

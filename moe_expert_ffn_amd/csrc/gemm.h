@@ -910,6 +910,69 @@ template <int MN, int NWAVES, int BK_> struct MnKFp8 {
   }
 };
 
+// MN-contiguous e4m3 operand for the fp8 MFMA: 128 K rows x MN codes per
+// stage (a K step of 128 codes is one 128 x 128 scale block deep), laid out
+// and swizzled like MnKFp8.  BK = 64 in the stream's units (the bf16
+// elements a RowK8 row of 128 codes stands for); KROWS = 128 K rows.  Block j
+// of a wave, chunk C (K 64 C .. 64 C + 63): lane l holds column
+// wave_base + 32 j + l % 32 and needs K 16 h + 0..15 and 32 + 16 h + 0..15 of
+// the chunk (h = l / 32), four ds_read_b64_tr_b8 of 8 K rows each.  In
+// 16-lane group G (columns 16 (G & 1) + 0..15, h = G >> 1) lane j' addresses
+// row 64 C + 16 h + 8 (r & 1) + 32 (r >> 1) + j' / 2 for read r; the row
+// offsets are multiples of 8, so the swizzle 2 (j' / 2) depends on the lane
+// only and each read is the lane's base address plus an immediate.
+template <int MN, int NWAVES> struct MnK8 {
+  static constexpr bool kF8Mma = true;
+  static constexpr int BK = 64;
+  static constexpr int KROWS = 128;
+  static constexpr int ROWB = MN;
+  static constexpr int RPI = 1024 / ROWB;
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int NI = KROWS / RPI / NWAVES;
+  static constexpr int STAGE_BYTES = KROWS * ROWB;
+  static_assert(NI * RPI * NWAVES == KROWS, "K rows per stage");
+  static_assert(CPR == 16, "chunk swizzle spans 16 chunks");
+  BufRsrc rs;
+  const MOE_CONST float* sp;
+  int sld;
+  struct Offs { uint32_t o[NI]; };
+  static MOE_DEV int chunk_swz(int row) { return 2 * (row & 7); }
+  static MOE_DEV int row_of(int i) { return ((threadIdx.x >> 6) + NWAVES * i) * RPI + (threadIdx.x & 63) / CPR; }
+  static MOE_DEV int row_base(int i) { return (wave_id() + NWAVES * i) * RPI; }
+  MOE_DEV void issue(const Offs& p, MOE_LDS char* st) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      buf_load_lds16(rs, p.o[i], (MOE_LDS void*)(st + (w + NWAVES * i) * RPI * ROWB));
+  }
+  // a wave's 64 columns and a K step lie in one scale block
+  MOE_DEV float scale(int, int kt) const { return sp[(size_t)kt * sld]; }
+  struct Lane { uint32_t off[2]; };
+  static MOE_DEV Lane lane_info(int wave_base, int lane) {
+    const int G = lane >> 4, jl = lane & 15;
+    const int row = 16 * (G >> 1) + (jl >> 1);
+    Lane L;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = (wave_base + 32 * j) / 16 + (G & 1);
+      L.off[j] = (uint32_t)(row * ROWB + ((c ^ chunk_swz(row)) << 4) + 8 * (jl & 1));
+    }
+    return L;
+  }
+  // Issued from inline asm, like MnK::frag: every output is consumed, after
+  // an explicit lgkmcnt(0) wait.
+  template <int C> static MOE_DEV i32x8_t frag8(const MOE_LDS char* st, const Lane& L, int j) {
+    u32x2_t v0, v1, v2, v3;
+    const MOE_LDS char* p = st + L.off[j & 1];
+    asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(v0) : "v"(p), "i"((64 * C) * ROWB));
+    asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(v1) : "v"(p), "i"((64 * C + 8) * ROWB));
+    asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(v2) : "v"(p), "i"((64 * C + 32) * ROWB));
+    asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(v3) : "v"(p), "i"((64 * C + 40) * ROWB));
+    return i32x8_t{(int)v0[0], (int)v0[1], (int)v1[0], (int)v1[1],
+                   (int)v2[0], (int)v2[1], (int)v3[0], (int)v3[1]};
+  }
+};
+
 // MN-contiguous operand bound to its row function.  F::pre(k) gives a raw
 // value for K index k (an index, or a value loaded from memory, not yet
 // combined with anything, so no wait is needed until the loads are issued),
@@ -920,7 +983,9 @@ template <class OP, class F> struct MnKOperand {
   OP op;
   F f;
   static constexpr int BK = OP::BK, NI = OP::NI, STAGE_BYTES = OP::STAGE_BYTES;
+  static constexpr int KR = OP::STAGE_BYTES / OP::ROWB;   // K rows per step
   static constexpr bool kFp8 = op_fp8<OP>::value;
+  static constexpr bool kF8Mma = op_f8mma<OP>::value;
   using Lane = typename OP::Lane;
   // f.pre(kb, k): what post needs for the lane's K row k, where kb is the
   // wave-uniform first row of the same instruction
@@ -929,7 +994,7 @@ template <class OP, class F> struct MnKOperand {
     Offs p;
     p.kt = kt;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) p.raw[i] = f.pre(kt * BK + OP::row_base(i), kt * BK + OP::row_of(i));
+    for (int i = 0; i < NI; ++i) p.raw[i] = f.pre(kt * KR + OP::row_base(i), kt * KR + OP::row_of(i));
     return p;
   }
   MOE_DEV void issue(const Offs& p, MOE_LDS char* st) const {
@@ -937,7 +1002,7 @@ template <class OP, class F> struct MnKOperand {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int r = OP::row_of(i);
-      q.o[i] = f.post(p.raw[i], p.kt * BK + r) + (uint32_t)(((threadIdx.x & 63) % OP::CPR) ^ OP::chunk_swz(r)) * 16u;
+      q.o[i] = f.post(p.raw[i], p.kt * KR + r) + (uint32_t)(((threadIdx.x & 63) % OP::CPR) ^ OP::chunk_swz(r)) * 16u;
     }
     op.issue(q, st);
   }
@@ -947,6 +1012,9 @@ template <class OP, class F> struct MnKOperand {
   }
   template <int KC> static MOE_DEV u32x2_t codes(const MOE_LDS char* st, const Lane& L, int j) {
     return OP::template codes<KC>(st, L, j);
+  }
+  template <int C> static MOE_DEV i32x8_t frag8(const MOE_LDS char* st, const Lane& L, int j) {
+    return OP::template frag8<C>(st, L, j);
   }
   MOE_DEV float scale(int j, int kt) const { return op.scale(j, kt); }
 };

@@ -39,7 +39,9 @@ STAGE_OF = {"k_stream<SrcFc1>": "fwd.fc1", "k_stream<SrcFc2>": "fwd.fc2",
             "k_combine": "fwd.combine + bwd.combine", "k_sched": "fwd.sched + bwd.sched",
             "k_slot_gate": "fwd.sched + bwd.sched", "k_plan": "plan (fwd + bwd)",
             "k_stream<SrcFc1F8>": "fwd.fc1 (fp8 MFMA)", "k_stream<SrcFc2F8>": "fwd.fc2 (fp8 MFMA)",
-            "k_quant_act": "fwd.fc1 (x) + fwd.fc2 (A), fp8 MFMA",
+            "k_stream<SrcDaF8>": "bwd.dA (fp8 MFMA)", "k_stream<SrcDxF8>": "bwd.dX (fp8 MFMA)",
+            "k_quant_act": "fp8 MFMA: fwd.fc1 (x, A), bwd.dA (dy)",
+            "k_swiglu_bwd_q": "bwd.dA (dZ, P, dZ's e4m3 rows; fp8 MFMA)",
             "k_route_count": "route", "k_route_scan": "route", "k_route_slot": "route"}
 
 

@@ -33,7 +33,8 @@ class LayerRunner:
         # launch (0: every workgroup runs both phases)
         self.split_fwd = 0
         self.split_bwd = 0
-        # e4m3 weights: FC1 on the fp8 MFMA with x quantized per row block
+        # e4m3 weights: every product but the weight gradients on the fp8 MFMA
+        # (x, A, dy and dZ quantized per row block of 128 features)
         self.fp8_act = False
         self.owner = owner.to(device=dev, dtype=torch.int32).contiguous()
         self.with_backward = with_backward
@@ -80,7 +81,7 @@ class LayerRunner:
         bw = self.plan_b["block_worker"] if block_worker is None else block_worker
         B.backward(self.layer, x, gates, dy, self.z, topk_ids, self.beta, self.P, self.s, self.rs,
                    self.owner, bw, self.dx, self.dw1, self.dw2, self.ws, self.status, events,
-                   timeline, self.two_phase, self.split_bwd)
+                   timeline, self.two_phase, self.split_bwd, self.fp8_act)
         return self.dx, self.dw1, self.dw2
 
     def step(self, x, gates, topk_ids, dy=None, s=None, timeline=None):

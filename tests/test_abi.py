@@ -158,14 +158,16 @@ def test_host_validation_errors():
                            None, None) == B.MOE_ERR_ARG
     assert lib.moe_forward(ctypes.byref(ok), P, P, P, 4, 2, 16, 4, *([P] * 8), P, 1 << 30,
                            B.EXEC_FP8_ACT, None, None, None) == B.MOE_ERR_ARG
-    # ... on an e4m3 layer together with the two-phase launch, or off the 256 grid;
-    # and never for the backward
+    # ... on an e4m3 layer together with the two-phase launch, or off the 256 grid,
+    # in either direction; the backward refuses it on a bf16 layer too
     f8 = B.Layer(8, 256, 256, B.MOE_BF16, B.MOE_FP8_E4M3, 16, 32, 64, 64)
     f8small = B.Layer(8, 128, 128, B.MOE_BF16, B.MOE_FP8_E4M3, 16, 32, 64, 64)
     for lay, fl in ((f8, B.EXEC_FP8_ACT | B.EXEC_TWO_PHASE), (f8small, B.EXEC_FP8_ACT)):
         assert lib.moe_forward(ctypes.byref(lay), P, P, P, 4, 2, 16, 4, *([P] * 8), P, 1 << 30,
                                fl, None, None, None) == B.MOE_ERR_ARG
-    assert lib.moe_backward(ctypes.byref(f8), P, P, P, P, P, 4, 2, 16, 4, 1, *([P] * 10), P,
+        assert lib.moe_backward(ctypes.byref(lay), P, P, P, P, P, 4, 2, 16, 4, 1, *([P] * 10), P,
+                                1 << 30, fl, None, None, None) == B.MOE_ERR_ARG
+    assert lib.moe_backward(ctypes.byref(ok), P, P, P, P, P, 4, 2, 16, 4, 1, *([P] * 10), P,
                             1 << 30, B.EXEC_FP8_ACT, None, None, None) == B.MOE_ERR_ARG
     assert lib.moe_backward(ctypes.byref(ok), P, P, P, P, P, 4, 2, 16, 4, 1, *([P] * 10), P,
                             1 << 30, 4, None, None, None) == B.MOE_ERR_ARG

@@ -1,4 +1,4 @@
-"""GPU parity of the fp8 MFMA forward (MOE_EXEC_FP8_ACT) and its activation
+"""GPU parity of the fp8 MFMA path (MOE_EXEC_FP8_ACT) and its activation
 quantizer.
 
 - The quantizer (moe_quantize_act_rows) is bit-exact against the oracle's
@@ -10,6 +10,11 @@ quantizer.
   - against the exact oracle (bf16 x, dequantized weights) within the e4m3
     bar of 6e-2.
 - Placement does not change a bit. A zero weight-scale block adds nothing.
+- The backward (dA and dX on the fp8 MFMA, dy and dZ quantized per row
+  block) against the oracle's fp8-operand backward, which decides the e4m3
+  codes on the same bf16 values the layer stores: dx, dW1 and dW2 within
+  2e-2; against the exact backward within 3 * 2^-4, the bound the oracle's
+  own pin uses for three quantizations.
 """
 import numpy as np
 import pytest
@@ -28,6 +33,9 @@ pytestmark = pytest.mark.gpu
 TOL_MODEL_Z = 1e-2      # [G, U] against the fp8-operand oracle (bf16 storage)
 TOL_MODEL_Y = 2e-2      # y against the same
 TOL_EXACT = 6e-2        # y against the exact oracle (the e4m3 bar)
+TOL_MODEL_DX = 2e-2     # dx against the fp8-operand backward oracle
+TOL_MODEL_DW = 2e-2     # dW1, dW2 against the same
+TOL_EXACT_BWD = 3 * 2.0 ** -4   # dx, dW against the exact backward
 
 SMALL = {
     # one tile each way, ragged blocks
@@ -143,7 +151,8 @@ def test_fp8_act_full_size_sampled(kappa):
 
 
 def test_fp8_act_rejected_where_unsupported():
-    """bf16 weights, the two-phase launch and the backward refuse the flag."""
+    """bf16 weights and the two-phase launch refuse the flag, in the forward
+    and the backward."""
     say("[fp8-act] refusals")
     c = Case(SMALL["small_fp8"], 0)
     r = c.runner
@@ -159,3 +168,84 @@ def test_fp8_act_rejected_where_unsupported():
     with pytest.raises(B.MoeError):
         B.forward(rb.layer, cb.x, cb.gates, cb.ids, rb.beta, rb.P, rb.rs, rb.plan_f["block_worker"],
                   rb.y, rb.z, rb.ws, rb.status, fp8_act=True)
+    cw = Case(SMALL["small_fp8"], 0, backward=True)
+    rw = cw.runner
+    rw.step(cw.x, cw.gates, cw.ids)
+    rw.make_plan(B.PLAN_BWD, None, rw.plan_b)
+    with pytest.raises(B.MoeError):
+        B.backward(rw.layer, cw.x, cw.gates, cw.dy, rw.z, cw.ids, rw.beta, rw.P, rw.s, rw.rs,
+                   rw.owner, rw.plan_b["block_worker"], rw.dx, rw.dw1, rw.dw2, rw.ws, rw.status,
+                   two_phase=True, fp8_act=True)
+
+
+def _run_bwd(c, fp8_act=True, s=None):
+    r = c.runner
+    r.fp8_act = fp8_act
+    r.status.zero_()
+    r.step(c.x, c.gates, c.ids, dy=c.dy, s=s)
+    torch.cuda.synchronize()
+    assert c.status() == 0
+    return r.dx.clone(), r.dw1.clone(), r.dw2.clone()
+
+
+def _bwd_errs(dx, dw1, dw2, o, tokens=None, experts=None):
+    """rel-L2 of dx (the tokens given) and of the worst expert's dW1 and dW2,
+    each expert on its own."""
+    ex = range(dw1.shape[0]) if experts is None else experts
+    dxs = dx if tokens is None else dx[tokens]
+
+    def worst(dw, ref):
+        return max(rel_l2(dw[e].double().cpu().numpy(), ref[e]) for e in ex)
+    return rel_l2(dxs.double().cpu().numpy(), o["dx"]), worst(dw1, o["dw1"]), worst(dw2, o["dw2"])
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fp8_act_backward_parity(name):
+    w = SMALL[name]
+    say(f"[fp8-act-bwd] {name}")
+    c = Case(w, 0, backward=True)
+    dx0, _, _ = _run_bwd(c, fp8_act=False)
+    dx, dw1, dw2 = _run_bwd(c)
+    x, w1, w2, ids, gates = c.oracle_inputs()
+    dy = c.dy.double().cpu().numpy()
+    e8 = _bwd_errs(dx, dw1, dw2, offn.backward_fp8act(x, w1, w2, ids, gates, dy, w.beta))
+    e0 = _bwd_errs(dx, dw1, dw2, offn.backward(x, w1, w2, ids, gates, dy))
+    moved = rel_l2(dx.double().cpu().numpy(), dx0.double().cpu().numpy())
+    say(f"  vs fp8-operand oracle dx={e8[0]:.3e} dw1={e8[1]:.3e} dw2={e8[2]:.3e}; "
+        f"vs exact dx={e0[0]:.3e} dw1={e0[1]:.3e} dw2={e0[2]:.3e}; dx vs the bf16-operand path "
+        f"{moved:.3e}")
+    assert e8[0] <= TOL_MODEL_DX and max(e8[1:]) <= TOL_MODEL_DW
+    assert max(e0) <= TOL_EXACT_BWD
+    assert moved > 1e-4                    # the flag took the fp8 path
+
+
+def test_fp8_act_backward_plan_invariance():
+    w = SMALL["stream_fp8"]
+    say("[fp8-act-bwd] plan invariance")
+    c = Case(w, 0, backward=True)
+    dx_p, dw1_p, dw2_p = _run_bwd(c)
+    dx_f, dw1_f, dw2_f = _run_bwd(c, s=0)
+    assert torch.equal(dx_p, dx_f)
+    assert rel_l2(dw1_p.double().cpu().numpy(), dw1_f.double().cpu().numpy()) < 1e-6
+    assert rel_l2(dw2_p.double().cpu().numpy(), dw2_f.double().cpu().numpy()) < 1e-6
+
+
+@pytest.mark.parametrize("kappa", [1, 8])
+def test_fp8_act_backward_full_size_sampled(kappa):
+    w = WORKLOADS["dsv3_fp8_fwdbwd"]
+    say(f"[fp8-act-bwd] dsv3_fp8_fwdbwd kappa={kappa}")
+    c = Case(w, kappa, backward=True)
+    dx, dw1, dw2 = _run_bwd(c)
+    counts = np.bincount(c.ids_np[c.ids_np >= 0], minlength=w.E)
+    held = [e for e in range(w.E) if counts[e] > 0]
+    experts = sorted({int(np.argmax(counts)), min(held, key=lambda e: (counts[e], e))})
+    rng = np.random.default_rng(kappa + 200)
+    tok = np.sort(rng.choice(c.T, size=32, replace=False))
+    x, w1, w2, ids, gates = c.oracle_inputs()
+    o = offn.backward_fp8act(x, w1, w2, ids, gates, c.dy.double().cpu().numpy(), w.beta,
+                             tokens=tok, experts=experts)
+    e = _bwd_errs(dx, dw1, dw2, o, tokens=tok, experts=experts)
+    say(f"  experts={experts} rows={counts[experts].tolist()} dx={e[0]:.3e} dw1={e[1]:.3e} "
+        f"dw2={e[2]:.3e}")
+    assert e[0] <= TOL_MODEL_DX and max(e[1:]) <= TOL_MODEL_DW
+    assert torch.isfinite(dx.float()).all()
