@@ -199,12 +199,20 @@ def time_steps(case, steps, warmup, with_events=True):
     r = case["runner"]
     bwd = case["dy"] is not None
 
-    def one(evf=None, evb=None):
+    def one(evf=None, evb=None, es=None):
         r.route(case["ids"])
+        if es:
+            es.record(1)
         r.make_plan(B.PLAN_FWD)
+        if es:
+            es.record(2)
         r.forward(case["x"], case["gates"], case["ids"], events=evf)
         if bwd:
+            if es:
+                es.record(3)
             r.make_plan(B.PLAN_BWD, out=r.plan_b)
+            if es:
+                es.record(4)
             r.backward(case["x"], case["gates"], case["dy"], case["ids"], events=evb)
 
     for _ in range(warmup):
@@ -218,13 +226,13 @@ def time_steps(case, steps, warmup, with_events=True):
     evs = []
     if with_events:
         for _ in range(steps):
-            evs.append((B.Events(5), B.Events(7) if bwd else None, B.Events(2)))
+            evs.append((B.Events(5), B.Events(7) if bwd else None, B.Events(6)))
         torch.cuda.synchronize()
         for i in range(steps):
             ef, eb, es = evs[i]
             es.record(0)
-            one(ef.ev, eb.ev if eb else None)
-            es.record(1)
+            one(ef.ev, eb.ev if eb else None, es)
+            es.record(5)
         torch.cuda.synchronize()
     stages = {}
     if with_events:
@@ -238,7 +246,11 @@ def time_steps(case, steps, warmup, with_events=True):
                 for j, nm in enumerate(BWD_STAGES[two]):
                     if nm:
                         acc.setdefault("bwd." + nm, []).append(eb.elapsed_ms(j, j + 1))
-            acc.setdefault("step", []).append(es.elapsed_ms(0, 1))
+            acc.setdefault("route", []).append(es.elapsed_ms(0, 1))
+            acc.setdefault("plan.fwd", []).append(es.elapsed_ms(1, 2))
+            if eb:
+                acc.setdefault("plan.bwd", []).append(es.elapsed_ms(3, 4))
+            acc.setdefault("step", []).append(es.elapsed_ms(0, 5))
         stages = {k: sum(v) / len(v) for k, v in acc.items()}
         steps_sorted = sorted(acc["step"])
 
@@ -249,12 +261,14 @@ def time_steps(case, steps, warmup, with_events=True):
     return wall_ms, stages
 
 
-def kernel_model(w, R, T, e_act, replicas, red_bytes=0):
+def kernel_model(w, R, T, e_act, replicas, red_bytes=0, slots_used=0):
     """Algorithmic flops and HBM bytes of one launch of each kernel: every
     operand read once from HBM and every output written once (weights of the
     experts that have rows, gathered activations counted once per token, the
     fp32 weight gradients of owners and replicas; the replica reduction's
-    bytes come from the backward plan, see reduce_bytes)."""
+    bytes come from the backward plan, see reduce_bytes).  The routing
+    statistics (histogram, scan, slotting) read the T k ids and write
+    row_to_slot (T k) and slot_to_row over the slots in use, int32 each."""
     d, f, ab = w.d, w.d_ff, 2
     wb = 1 if w.wdt == "fp8" else 2
     w1 = 2 * f * d * wb * e_act
@@ -264,6 +278,7 @@ def kernel_model(w, R, T, e_act, replicas, red_bytes=0):
         "fwd.fc1": (4 * d * f * R, w1 + x + R * f * ab + (R * 2 * f * ab if w.backward else 0)),
         "fwd.fc2": (2 * d * f * R, w2 + R * f * ab + R * d * ab),
         "fwd.combine": (0, R * d * ab + x),
+        "route": (0, 4 * (2 * T * w.k + slots_used)),
     }
     if w.backward:
         m.update({
@@ -302,7 +317,7 @@ def reduce_bytes(case, w):
 # WRITE_SIZE per dispatch, scaled by the reading of a plain copy kernel of
 # known size), valid only for the kernel sources it was measured on.
 PROFILED_TRAFFIC = {"kernel": "bwd.dW", "workload": "qwen3_bf16_fwdbwd", "kappa": 1.0, "fixed": False,
-                    "source": "023c0a71c6a329c3", "bytes": 3338825914,
+                    "source": "4afd536b398886d7", "bytes": 3340247623,
                     "summary": "profiles/k_stream_SrcDwT_qwen3_bf16_fwdbwd_hbm_traffic.md"}
 
 
@@ -316,8 +331,8 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def roofline(w, stages, R, T, e_act, replicas, red_bytes=0, run=None):
-    model = kernel_model(w, R, T, e_act, replicas, red_bytes)
+def roofline(w, stages, R, T, e_act, replicas, red_bytes=0, run=None, slots_used=0):
+    model = kernel_model(w, R, T, e_act, replicas, red_bytes, slots_used)
     # every contraction runs on bf16 MFMA (e4m3 weights are widened to bf16
     # between LDS and the matrix cores), so the bf16 peak bounds it
     peak_f = PEAK_BF16_TFLOPS
@@ -345,7 +360,8 @@ def roofline(w, stages, R, T, e_act, replicas, red_bytes=0, run=None):
            "unit": r["unit"], "frac": round(r["frac"], 4), "traffic": traffic,
            "launch_us": round(r["launch_us"], 2), "algorithmic_flops": r["flops"],
            "algorithmic_bytes": r["bytes"]}
-    per = {k: {"bound": v["bound"], "frac": round(v["frac"], 4), "us": round(v["launch_us"], 1)}
+    per = {k: {"bound": v["bound"], "frac": round(v["frac"], 4), "us": round(v["launch_us"], 1),
+               "achieved": round(v["achieved"], 1), "unit": v["unit"]}
            for k, v in rows.items()}
     return out, per
 
@@ -587,9 +603,13 @@ def main():
     e_act = int((np.bincount(case["ids_np"][case["ids_np"] >= 0].ravel(), minlength=w.E) > 0).sum())
     replicas = int(case["runner"].plan_b["plan_info"][2].item()) if w.backward else 0
     red_bytes = reduce_bytes(case, w) if w.backward else 0
+    cnt = np.bincount(case["ids_np"][case["ids_np"] >= 0].ravel(), minlength=w.E)
+    slots_used = int((-(-cnt // w.beta)).sum() * w.beta)
     roof, per_kernel = roofline(w, stages, R, case["T"], e_act, replicas, red_bytes,
-                                run=(w.name, float(args.kappa), bool(args.fixed)))
-    _, per_two = roofline(w, stages_two, R, case["T"], e_act, replicas, red_bytes)
+                                run=(w.name, float(args.kappa), bool(args.fixed)),
+                                slots_used=slots_used)
+    _, per_two = roofline(w, stages_two, R, case["T"], e_act, replicas, red_bytes,
+                          slots_used=slots_used)
     for k in ("fwd.fc1+fc2", "bwd.dA+dX"):
         if k in per_two:
             per_kernel[k + " (two-phase launch)"] = per_two[k]

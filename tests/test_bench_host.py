@@ -50,6 +50,9 @@ def test_kernel_model_reduce_entry_only_with_bytes():
     for a, b in (("fwd.fc1", "fwd.fc2"), ("bwd.dA", "bwd.dX")):
         both = m1[a + "+" + b.split(".")[1]]
         assert both == (m1[a][0] + m1[b][0], m1[a][1] + m1[b][1])
+    # routing statistics: the ids read once, row_to_slot and the slots in use written
+    m2 = bench.kernel_model(w, R, T, w.E, 0, 0, slots_used=70000)
+    assert m2["route"] == (0, 4 * (2 * T * w.k + 70000))
 
 
 def test_worker_spread_from_a_hand_timeline():
