@@ -224,6 +224,57 @@ def test_quantize_rounding_ties():
     _check_exact(codes, scales, src.float().numpy(), rows)
 
 
+def _near_boundary_columns(n_cols, rows, rng):
+    """Columns of bf16 values whose quotients v / (amax / 448), in fp32, lie
+    within two ulps of an e4m3 rounding boundary (low 20 mantissa bits at
+    0x80000), or below 2^-6 (the subnormal range), with row 0 the column's
+    amax: the values for which the quantizer cannot use v times 1 / scale."""
+    bf = np.arange(0x3F80, 0x4000, dtype=np.uint32)        # bf16 mantissas of [1, 2)
+    amaxes = ((bf << 16).view(np.float32)[None, :] *
+              np.float32(2.0) ** rng.integers(-20, 20, 4096)[:, None].astype(np.float32))
+    amaxes = np.unique(amaxes.ravel().astype(np.float32))
+    rng.shuffle(amaxes)
+    cols = []
+    for amax in amaxes:
+        s = np.float32(amax / np.float32(448.0))
+        # bf16 candidates from amax down to 2^-6 of the scale
+        e = np.arange(-7, 9)
+        cand = ((bf << 16).view(np.float32)[None, :] * np.float32(2.0) ** e[:, None].astype(np.float32) * s)
+        cand = cand.ravel().astype(np.float32)
+        cand = torch.from_numpy(cand).to(torch.bfloat16).float().numpy()
+        cand = cand[(cand > 0) & (cand < amax)]
+        q = (cand / s).astype(np.float32)
+        b = q.view(np.uint32)
+        near = np.abs((b & 0xFFFFF).astype(np.int64) - 0x80000) <= 2
+        hits = np.unique(cand[near & (b >= 0x3C800000)])
+        if len(hits):
+            tiny = (amax * np.float32(2.0) ** -rng.uniform(15, 30, rows)).astype(np.float32)
+            tiny = torch.from_numpy(tiny).to(torch.bfloat16).float().numpy()
+            col = np.concatenate([[amax], hits, -hits, tiny.astype(np.float32)])[:rows]
+            cols.append((col, len(hits)))
+        if len(cols) == n_cols:
+            break
+    return cols
+
+
+def test_quantize_near_rounding_boundaries():
+    """The quantizer multiplies by the reciprocal scale and divides only where
+    that could change the code; values placed on both kinds of such spots
+    give the oracle's codes (correctly rounded division) bit for bit."""
+    say("[quant-boundaries]")
+    rng = np.random.default_rng(77)
+    rows, brows = 128, 128
+    cols = _near_boundary_columns(64, rows, rng)
+    assert len(cols) == 64 and sum(n for _, n in cols) >= 64
+    src = np.zeros((rows, len(cols)), dtype=np.float32)
+    for c, (col, _) in enumerate(cols):
+        src[:len(col), c] = col
+    s16 = torch.from_numpy(src).to(torch.bfloat16)
+    assert torch.equal(s16.float(), torch.from_numpy(src))    # every value exact in bf16
+    codes, scales = _quant_dev(s16, rows, len(cols), brows)
+    _check_exact(codes, scales, src, brows)
+
+
 def test_fp8_nothing_routed_writes_zeros():
     """e4m3 weights, every id -1: the requantization passes see no used block
     and the outputs and weight gradients are still written, as zeros."""
