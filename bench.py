@@ -666,11 +666,14 @@ def main():
         out["kappa_sweep"], out["skew"] = kappa_sweep(w, dev, lay, args.sweep_steps)
     if args.sweep:
         sweep, planners = [], []
+        arms = [("fixed", True, None, 12, False), ("planned", False, None, 12, False),
+                ("planned-lambda1", False, None, 1, False), ("planned-quota", False, 1, 12, False)]
+        if w.wdt == "fp8":      # the same quota plans with the products on the fp8 MFMA
+            arms.append(("planned-quota-fp8-mfma", False, 1, 12, True))
         for kap in w.kappas:
-            for arm, fixed, umin, lam in (("fixed", True, None, 12), ("planned", False, None, 12),
-                                          ("planned-lambda1", False, None, 1),
-                                          ("planned-quota", False, 1, 12)):
+            for arm, fixed, umin, lam, f8 in arms:
                 c = build_case(w, kap, fixed, dev, quota_umin=umin, lam=lam, lay=lay)
+                c["runner"].fp8_act = f8
                 Rk = int((c["ids_np"] >= 0).sum())
                 msk, st = time_steps(c, max(5, args.steps // 2), 2)
                 uk = (f_fwd + (f_bwd if w.backward else 0)) * Rk
