@@ -249,3 +249,22 @@ def test_fp8_act_backward_full_size_sampled(kappa):
         f"dw2={e[2]:.3e}")
     assert e[0] <= TOL_MODEL_DX and max(e[1:]) <= TOL_MODEL_DW
     assert torch.isfinite(dx.float()).all()
+
+
+def test_fp8_act_nothing_routed_writes_zeros():
+    """Every id -1: the quantizers see no rows in use and the fp8 MFMA
+    kernels no items; y, dx and the weight gradients are still written, as
+    zeros."""
+    w = SMALL["stream_fp8"]
+    say("[fp8-act] nothing routed")
+    T = 64
+    ids = np.full((T, w.k), -1, dtype=np.int32)
+    gates = np.zeros((T, w.k), dtype=np.float32)
+    c = Case(w, 0, backward=True, ids=ids, gates=gates)
+    r = c.runner
+    for t in (r.y, r.dx, r.dw1, r.dw2):
+        t.fill_(float("nan"))
+    dx, dw1, dw2 = _run_bwd(c)
+    for name, t in (("y", r.y), ("dx", dx), ("dw1", dw1), ("dw2", dw2)):
+        assert not torch.isnan(t).any(), f"{name} left unwritten"
+        assert torch.count_nonzero(t) == 0, f"{name} not zero"
