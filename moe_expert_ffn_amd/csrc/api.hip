@@ -196,6 +196,7 @@ int moe_quantize_act_rows(const void* src, int rows, int cols, uint8_t* codes, i
                           void* stream) {
   if (rows < 0 || cols < 128 || cols % 128) return MOE_ERR_ARG;
   if (rows > 0 && (!src || !codes || !exps)) return MOE_ERR_ARG;
+  if (rows == 0) return MOE_OK;
   return launch_quant_act((const uint16_t*)src, rows, cols, codes, exps, (hipStream_t)stream);
 }
 

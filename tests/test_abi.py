@@ -148,6 +148,15 @@ def test_host_validation_errors():
     assert q(P, 16, 3, P, 0, 1, None, 4, 16, 128, P, P, None) == B.MOE_ERR_ARG        # > src_rows
     big = 65535 * 128 + 8                                                            # > 65535 column tiles
     assert q(P, big, 4, None, 0, 1, None, 4, big, 128, P, P, None) == B.MOE_ERR_ARG
+    # activation rows for the fp8 MFMA: (src, rows, cols, codes, exps, stream)
+    qa = lib.moe_quantize_act_rows
+    assert qa(P, -1, 128, P, P, None) == B.MOE_ERR_ARG                               # rows
+    assert qa(P, 4, 192, P, P, None) == B.MOE_ERR_ARG                                # cols % 128
+    assert qa(P, 4, 0, P, P, None) == B.MOE_ERR_ARG                                  # cols
+    assert qa(None, 4, 128, P, P, None) == B.MOE_ERR_ARG                             # src
+    assert qa(P, 4, 128, None, P, None) == B.MOE_ERR_ARG                             # codes
+    assert qa(P, 4, 128, P, None, None) == B.MOE_ERR_ARG                             # exps
+    assert qa(None, 0, 128, None, None, None) == B.MOE_OK                            # nothing to do
     ok = _layer()
     assert lib.moe_forward(ctypes.byref(ok), P, P, P, 4, 2, 16, 4, *([P] * 8), P, 16, 0, None,
                            None, None) == B.MOE_ERR_WORKSPACE
