@@ -698,6 +698,7 @@ __global__ __launch_bounds__(256) void k_quant_act(const uint16_t* __restrict__ 
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
+      if (u == 1 && t + nw >= ntask) break;              // wave-uniform: no second task
       const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
       float v[8];
 #pragma unroll
