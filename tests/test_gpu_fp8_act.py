@@ -268,3 +268,22 @@ def test_fp8_act_nothing_routed_writes_zeros():
     for name, t in (("y", r.y), ("dx", dx), ("dw1", dw1), ("dw2", dw2)):
         assert not torch.isnan(t).any(), f"{name} left unwritten"
         assert torch.count_nonzero(t) == 0, f"{name} not zero"
+
+
+def test_fp8_act_backward_two_workers_quota_plans():
+    """Two workers with quota plans (the partition count the cost model picks
+    for the DeepSeek-V3 share at high kappa), replicas in both directions:
+    the same parity as with the default plans."""
+    w = SMALL["stream_fp8"]
+    say("[fp8-act-bwd] P=2, quota plans")
+    c = Case(w, 0, P=2, backward=True)
+    c.runner.quota_umin = 1
+    dx, dw1, dw2 = _run_bwd(c)
+    say(f"  plans fwd={c.runner.plan_f['plan_info'].cpu().numpy().tolist()} "
+        f"bwd={c.runner.plan_b['plan_info'].cpu().numpy().tolist()}")
+    x, w1, w2, ids, gates = c.oracle_inputs()
+    dy = c.dy.double().cpu().numpy()
+    e8 = _bwd_errs(dx, dw1, dw2, offn.backward_fp8act(x, w1, w2, ids, gates, dy, w.beta))
+    ym = rel_l2(c.runner.y.double().cpu().numpy(), offn.forward_fp8act(x, w1, w2, ids, gates))
+    say(f"  y {ym:.3e}; dx={e8[0]:.3e} dw1={e8[1]:.3e} dw2={e8[2]:.3e}")
+    assert ym <= TOL_MODEL_Y and e8[0] <= TOL_MODEL_DX and max(e8[1:]) <= TOL_MODEL_DW
