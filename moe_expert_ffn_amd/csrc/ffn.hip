@@ -516,9 +516,10 @@ static dim3 combine_grid(int T) { return dim3((unsigned)((T + 3) / 4)); }
 // columns (8 each) and 16 rows are read at once.  Pass 1 takes each column's
 // amax over the block's rows (exact in any order), reduced through LDS; pass
 // 2 encodes.  A thread keeps its first kQtKeep rows (a 128-row block) in
-// registers between the passes; rows beyond them are read again.  Row reads
-// are branchless (a masked row loads row 0 and selects +0), so a thread's
-// rows are all in flight at once.
+// registers between the passes, as their bf16 source words and multiplier
+// (the values are formed again, by the same product, in pass 2); rows beyond
+// them are read again.  Row reads are branchless (a masked row loads row 0
+// and keeps zero words), so a thread's rows are all in flight at once.
 // DEQ: instead of codes and scales, write code * scale as bf16 to deq
 // [rows][cols] (which may be src itself: pass 2 reads each value before the
 // same thread overwrites it, and workgroups cover disjoint tiles).
@@ -541,23 +542,34 @@ __global__ __launch_bounds__(256) void k_quant_tok(const uint16_t* src, int ld,
   if (blk_end && b >= *blk_end) return;                   // whole workgroup, before any barrier
   const bool colok = c0 < cols;
   const int r0 = b * brows, r1 = min(rows, r0 + brows);
-  auto value8 = [&](int r, float* v) {
+  // a row's 8 bf16 source words and its multiplier; a masked row keeps zero
+  // words (values +0) and multiplier 1
+  auto raw8 = [&](int r, uint4& q, float& f) {
     int srow = r;
     bool ok = true;
-    float f = 1.f;
+    f = 1.f;
     if (map) {
       const int m = map[r];
       ok = m >= 0 && m < map_lim;
       if (gather) srow = ok ? m / div : 0;
-      if (rscale) f = rscale[ok ? m : 0];
+      if (rscale) f = ok ? rscale[ok ? m : 0] : 1.f;
     }
-    const uint4 q = *(const uint4*)(src + (size_t)srow * ld + c0);
+    const uint4 l = *(const uint4*)(src + (size_t)srow * ld + c0);
+    q = ok ? l : make_uint4(0, 0, 0, 0);
+  };
+  auto expand8 = [&](const uint4& q, float f, float* v) {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      v[2 * i] = ok ? __uint_as_float(w[i] << 16) * f : 0.f;
-      v[2 * i + 1] = ok ? __uint_as_float(w[i] & 0xFFFF0000u) * f : 0.f;
+      v[2 * i] = __uint_as_float(w[i] << 16) * f;
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u) * f;
     }
+  };
+  auto value8 = [&](int r, float* v) {
+    uint4 q;
+    float f;
+    raw8(r, q, f);
+    expand8(q, f, v);
   };
   // v_cvt_pk_fp8_f32 rounds to nearest even on the OCP e4m3 grid: checked on
   // MI355X against a bit-level round-to-nearest-even encoder on every fp32
@@ -590,16 +602,20 @@ __global__ __launch_bounds__(256) void k_quant_tok(const uint16_t* src, int ld,
       *(uint2*)(codes + (size_t)r * cols + c0) = make_uint2(w[0], w[1]);
     }
   };
-  float keep[kQtKeep][8];
+  // 5 registers a kept row instead of 8 values: more waves fit a SIMD
+  uint4 kq[kQtKeep];
+  float kf[kQtKeep];
   float amax[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (colok) {
 #pragma unroll
     for (int u = 0; u < kQtKeep; ++u) {
       const int r = r0 + ty + kQtRowLanes * u;
       if (r < r1) {
-        value8(r, keep[u]);
+        raw8(r, kq[u], kf[u]);
+        float v[8];
+        expand8(kq[u], kf[u], v);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax[i] = fmaxf(amax[i], fabsf(keep[u][i]));
+        for (int i = 0; i < 8; ++i) amax[i] = fmaxf(amax[i], fabsf(v[i]));
       }
     }
     for (int r = r0 + ty + kQtRowLanes * kQtKeep; r < r1; r += kQtRowLanes) {
@@ -631,7 +647,11 @@ __global__ __launch_bounds__(256) void k_quant_tok(const uint16_t* src, int ld,
 #pragma unroll
   for (int u = 0; u < kQtKeep; ++u) {
     const int r = r0 + ty + kQtRowLanes * u;
-    if (r < r1) encode(r, keep[u], sc);
+    if (r < r1) {
+      float v[8];
+      expand8(kq[u], kf[u], v);
+      encode(r, v, sc);
+    }
   }
   for (int r = r0 + ty + kQtRowLanes * kQtKeep; r < r1; r += kQtRowLanes) {
     float v[8];
