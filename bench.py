@@ -317,7 +317,7 @@ def reduce_bytes(case, w):
 # WRITE_SIZE per dispatch, scaled by the reading of a plain copy kernel of
 # known size), valid only for the kernel sources it was measured on.
 PROFILED_TRAFFIC = {"kernel": "bwd.dW", "workload": "qwen3_bf16_fwdbwd", "kappa": 1.0, "fixed": False,
-                    "source": "9b5c9965437143f3", "bytes": 3339451729,
+                    "source": "4f034f21543a8303", "bytes": 3344891174,
                     "summary": "profiles/k_stream_SrcDwT_qwen3_bf16_fwdbwd_hbm_traffic.md"}
 
 
