@@ -199,20 +199,18 @@ def time_steps(case, steps, warmup, with_events=True):
     r = case["runner"]
     bwd = case["dy"] is not None
 
-    def one(evf=None, evb=None, es=None):
+    def one(evf=None, evb=None, es=None, ep=None):
         r.route(case["ids"])
         if es:
             es.record(1)
+        if bwd:               # the backward plan on the runner's side stream
+            r.plan_bwd_async(events=ep)
         r.make_plan(B.PLAN_FWD)
         if es:
             es.record(2)
         r.forward(case["x"], case["gates"], case["ids"], events=evf)
         if bwd:
-            if es:
-                es.record(3)
-            r.make_plan(B.PLAN_BWD, out=r.plan_b)
-            if es:
-                es.record(4)
+            r.join_bwd_plan()
             r.backward(case["x"], case["gates"], case["dy"], case["ids"], events=evb)
 
     for _ in range(warmup):
@@ -226,19 +224,20 @@ def time_steps(case, steps, warmup, with_events=True):
     evs = []
     if with_events:
         for _ in range(steps):
-            evs.append((B.Events(5), B.Events(7) if bwd else None, B.Events(6)))
+            evs.append((B.Events(5), B.Events(7) if bwd else None, B.Events(6),
+                        B.Events(2) if bwd else None))
         torch.cuda.synchronize()
         for i in range(steps):
-            ef, eb, es = evs[i]
+            ef, eb, es, ep = evs[i]
             es.record(0)
-            one(ef.ev, eb.ev if eb else None, es)
+            one(ef.ev, eb.ev if eb else None, es, ep)
             es.record(5)
         torch.cuda.synchronize()
     stages = {}
     if with_events:
         acc = {}
         two = r.two_phase
-        for ef, eb, es in evs:
+        for ef, eb, es, ep in evs:
             for j, nm in enumerate(FWD_STAGES[two]):
                 if nm:
                     acc.setdefault("fwd." + nm, []).append(ef.elapsed_ms(j, j + 1))
@@ -248,8 +247,8 @@ def time_steps(case, steps, warmup, with_events=True):
                         acc.setdefault("bwd." + nm, []).append(eb.elapsed_ms(j, j + 1))
             acc.setdefault("route", []).append(es.elapsed_ms(0, 1))
             acc.setdefault("plan.fwd", []).append(es.elapsed_ms(1, 2))
-            if eb:
-                acc.setdefault("plan.bwd", []).append(es.elapsed_ms(3, 4))
+            if ep:            # on the side stream, next to the forward plan
+                acc.setdefault("plan.bwd", []).append(ep.elapsed_ms(0, 1))
             acc.setdefault("step", []).append(es.elapsed_ms(0, 5))
         stages = {k: sum(v) / len(v) for k, v in acc.items()}
         steps_sorted = sorted(acc["step"])

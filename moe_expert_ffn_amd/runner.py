@@ -44,6 +44,9 @@ class LayerRunner:
         nbc = B.max_blocks(T, k, self.E, beta)
         self.plan_f = B.alloc_plan(self.E, P, nbc, dev)
         self.plan_b = B.alloc_plan(self.E, P, nbc, dev) if with_backward else None
+        # the backward plan needs only the routing statistics: it runs on this
+        # stream (default priority) while the forward plan and the forward run
+        self.side = torch.cuda.Stream(device=dev) if with_backward and dev.type == "cuda" else None
         self.y = torch.empty((T, self.d), dtype=act_dtype, device=dev)
         need_z = with_backward if save_z is None else save_z
         ms = max(B.max_slots(T, k, self.E, beta), 1)
@@ -92,9 +95,28 @@ class LayerRunner:
         if s is not None and s > self.s:
             raise B.MoeError(f"replica budget s={s} above the runner's s={self.s}")
         self.route(topk_ids)
+        if dy is not None:
+            self.plan_bwd_async(s)
         self.make_plan(B.PLAN_FWD, s)
         self.forward(x, gates, topk_ids, timeline=timeline)
         if dy is not None:
-            self.make_plan(B.PLAN_BWD, s, self.plan_b)
+            self.join_bwd_plan()
             self.backward(x, gates, dy, topk_ids, timeline=timeline)
         return self.y
+
+    def plan_bwd_async(self, s=None, events=None):
+        """The backward plan on the side stream, after the work already queued
+        on the current stream (the routing statistics); `events` (optional,
+        a B.Events of 2) brackets it there."""
+        main = torch.cuda.current_stream(self.dev)
+        self.side.wait_stream(main)
+        with torch.cuda.stream(self.side):
+            if events is not None:
+                events.record(0)
+            self.make_plan(B.PLAN_BWD, s, self.plan_b)
+            if events is not None:
+                events.record(1)
+
+    def join_bwd_plan(self):
+        """The current stream waits for the backward plan."""
+        torch.cuda.current_stream(self.dev).wait_stream(self.side)
