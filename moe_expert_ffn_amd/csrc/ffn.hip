@@ -39,6 +39,12 @@ struct SchedArgs {
   int32_t* owner_has;
   int32_t* flags;      // per (worker, row tile) readiness counters of the two-phase launches
   int32_t* status;
+  // per-slot gates p (0 for padding slots), written by the workgroups past
+  // the first: gate_out[i] = gate_src[gate_s2r[i]] for i < gate_n
+  const int32_t* gate_s2r;
+  const float* gate_src;
+  float* gate_out;
+  size_t gate_n;
 };
 
 MOE_DEV int expert_of(int g, const int* boff_s, int E) {
@@ -75,6 +81,14 @@ constexpr int kSchedThreads = 512;
 template <bool BWL>
 __global__ __launch_bounds__(kSchedThreads) void k_sched(SchedArgs a) {
   extern __shared__ int sm[];
+  if (blockIdx.x > 0) {          // the per-slot gates, beside the scheduling workgroup
+    const size_t stride = (size_t)(gridDim.x - 1) * kSchedThreads;
+    for (size_t i = (size_t)(blockIdx.x - 1) * kSchedThreads + threadIdx.x; i < a.gate_n; i += stride) {
+      const int row = a.gate_s2r[i];
+      a.gate_out[i] = row >= 0 ? a.gate_src[row] : 0.f;
+    }
+    return;
+  }
   const int E = a.E, P = a.P;
   int* boff_s = sm;
   int* cnt_s = boff_s + E + 1;
@@ -431,74 +445,67 @@ __global__ __launch_bounds__(C::NT) void k_fc2(ExecArgs a) {
 }
 
 // ---- combine: out_t = sum_{j: slot(t,j) >= 0} src[slot(t,j)], fp32, j order ---
-// One wave per token: the token's slot indices are read once (64 per load,
-// lane j holding slot j) and taken out of their lanes as wave-uniform values;
-// each lane covers 16-byte chunks c, c + 64, ... of the row, two at a time.
-// For every chunk the values of up to 8 slots are loaded together and then
-// added in slot order, starting from 0, in fp32, and the sum is rounded to the
-// output dtype.  The slot rows themselves arrive in that dtype (FC2 and dX
-// store them rounded), so a bf16 output is rounded twice in all.
+// One wave per (token, group of 64 16-byte chunks of the row): the token's
+// slot indices are read (64 per load, lane j holding slot j) and taken out of
+// their lanes as wave-uniform values; lane c covers chunk c of the group.  The
+// values of up to 8 slots are loaded together and then added in slot order,
+// starting from 0, in fp32, and the sum is rounded to the output dtype.  The
+// slot rows themselves arrive in that dtype (FC2 and dX store them rounded),
+// so a bf16 output is rounded twice in all.  Splitting a row into groups
+// makes the units small (d = 2048 in bf16: four per token), so the last
+// round of workgroups is short.
 template <typename T>
 __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ src,
                                                  const int32_t* __restrict__ row_to_slot,
                                                  int T_, int k, int d, T* __restrict__ out) {
-  constexpr int VE = Elem<T>::VE, U = 2, G = 8;
-  const int t = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (t >= T_) return;                                  // the whole wave
-  const int nch = d / VE;
+  constexpr int VE = Elem<T>::VE, G = 8;
+  const int nch = d / VE, ngrp = (nch + 63) / 64;
+  const size_t unit = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (unit >= (size_t)T_ * ngrp) return;                // the whole wave
+  const int t = (int)(unit / ngrp), c = (int)(unit % ngrp) * 64 + lane;
+  const bool live = c < nch;
   const int32_t* slots = row_to_slot + (size_t)t * k;
-  for (int c = lane; c < nch; c += 64 * U) {
-    float acc[U][VE];
+  float acc[VE];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+  for (int v = 0; v < VE; ++v) acc[v] = 0.f;
+  for (int j64 = 0; j64 < k; j64 += 64) {
+    const int sl = j64 + lane < k ? slots[j64 + lane] : -1;
+    const int nj = min(64, k - j64);
+    for (int j0 = 0; j0 < nj; j0 += G) {
+      V16 in[G];
+      int sj[G];
 #pragma unroll
-      for (int v = 0; v < VE; ++v) acc[u][v] = 0.f;
-    for (int j64 = 0; j64 < k; j64 += 64) {
-      const int sl = j64 + lane < k ? slots[j64 + lane] : -1;
-      const int nj = min(64, k - j64);
-      for (int j0 = 0; j0 < nj; j0 += G) {
-        V16 in[G][U];
-        int sj[G];
+      for (int g = 0; g < G; ++g) {
+        sj[g] = j0 + g < nj ? __builtin_amdgcn_readlane(sl, j0 + g) : -1;
+        in[g].u = (sj[g] >= 0 && live) ? ldg16(src + (size_t)sj[g] * d + (size_t)c * VE) : zero4();
+      }
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          sj[g] = j0 + g < nj ? __builtin_amdgcn_readlane(sl, j0 + g) : -1;
+      for (int g = 0; g < G; ++g) {
+        if (sj[g] < 0) continue;                        // wave-uniform
 #pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const int cc = c + 64 * u;
-            in[g][u].u = (sj[g] >= 0 && cc < nch) ? ldg16(src + (size_t)sj[g] * d + (size_t)cc * VE)
-                                                 : zero4();
-          }
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          if (sj[g] < 0) continue;                      // wave-uniform
-#pragma unroll
-          for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int v = 0; v < VE; ++v) {
-              if constexpr (sizeof(T) == 2) acc[u][v] += bf2f(in[g][u].h[v]);
-              else acc[u][v] += in[g][u].f[v];
-            }
+        for (int v = 0; v < VE; ++v) {
+          if constexpr (sizeof(T) == 2) acc[v] += bf2f(in[g].h[v]);
+          else acc[v] += in[g].f[v];
         }
       }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int cc = c + 64 * u;
-      if (cc >= nch) continue;
-      V16 o;
-#pragma unroll
-      for (int v = 0; v < VE; ++v) {
-        if constexpr (sizeof(T) == 2) o.h[v] = f2bf(acc[u][v]);
-        else o.f[v] = acc[u][v];
-      }
-      stg16(out + (size_t)t * d + (size_t)cc * VE, o.u);
     }
   }
+  if (!live) return;
+  V16 o;
+#pragma unroll
+  for (int v = 0; v < VE; ++v) {
+    if constexpr (sizeof(T) == 2) o.h[v] = f2bf(acc[v]);
+    else o.f[v] = acc[v];
+  }
+  stg16(out + (size_t)t * d + (size_t)c * VE, o.u);
 }
 
-// grid of the combine: one wave per token, four tokens per workgroup
-static dim3 combine_grid(int T) { return dim3((unsigned)((T + 3) / 4)); }
+// grid of the combine: four waves (units) per workgroup
+template <typename T> static dim3 combine_grid(int T_, int d) {
+  const size_t units = (size_t)T_ * ((d / Elem<T>::VE + 63) / 64);
+  return dim3((unsigned)((units + 3) / 4));
+}
 
 // ---- backward: dA -> dZ -------------------------------------------------------
 // dA[slot, n] = p * sum_c dy[t, c] W2[c, n]; W2 is read as a K-major (c) by
@@ -2116,16 +2123,6 @@ template <class C, bool FP8 = false> struct SrcDwT {
 };
 
 
-// per-slot gate p (0 for padding slots), read by FC2 and dA through LDS
-__global__ __launch_bounds__(256) void k_slot_gate(const int32_t* __restrict__ slot_to_row,
-                                                   const float* __restrict__ gates, size_t n,
-                                                   float* __restrict__ sgate) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
-    const int row = slot_to_row[i];
-    sgate[i] = row >= 0 ? gates[row] : 0.f;
-  }
-}
-
 // Owner slot <- (owner partial or 0) + replica partials in ascending worker
 // order, fp32.  Experts with an owner partial and no replica are untouched.
 // The per-expert table is staged in LDS once per workgroup.
@@ -2261,10 +2258,21 @@ static size_t sched_lds(const Sizes& z, bool bwd, bool bwl) {
                         (bwd ? (size_t)3 * z.E * z.P : 0));
 }
 
+// gates (optional, nullptr: none): the per-slot gates the stream kernels read
+// (sgate) are written by extra workgroups of the same launch
 static void launch_sched(const Sizes& z, const int32_t* counts, const int32_t* boff,
                          const int32_t* bw, const int32_t* owner, bool bwd, char* ws,
-                         const WsLayout& L, int32_t* status, hipStream_t st) {
+                         const WsLayout& L, int32_t* status, const int32_t* slot_to_row,
+                         const float* gates, hipStream_t st) {
   SchedArgs s{};
+  unsigned gate_wg = 0;
+  if (gates && z.max_slots > 0) {
+    s.gate_s2r = slot_to_row;
+    s.gate_src = gates;
+    s.gate_out = (float*)(ws + L.sgate);
+    s.gate_n = z.max_slots;
+    gate_wg = (unsigned)std::min<size_t>((z.max_slots + kSchedThreads - 1) / kSchedThreads, 2048);
+  }
   s.counts = counts; s.boff = boff; s.bw = bw; s.owner = owner;
   s.E = z.E; s.P = z.P; s.s = z.s; s.beta = z.beta; s.backward = bwd ? 1 : 0;
   s.bm = use_big_tiles(z) ? BigCfg::BM : SmallCfg::BM;
@@ -2285,11 +2293,11 @@ static void launch_sched(const Sizes& z, const int32_t* counts, const int32_t* b
   if (bwl) {
     (void)hipFuncSetAttribute((const void*)k_sched<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)sched_lds(z, true, true));
-    hipLaunchKernelGGL(k_sched<true>, dim3(1), dim3(kSchedThreads), lds, st, s);
+    hipLaunchKernelGGL(k_sched<true>, dim3(1 + gate_wg), dim3(kSchedThreads), lds, st, s);
   } else {
     (void)hipFuncSetAttribute((const void*)k_sched<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)sched_lds(z, true, false));
-    hipLaunchKernelGGL(k_sched<false>, dim3(1), dim3(kSchedThreads), lds, st, s);
+    hipLaunchKernelGGL(k_sched<false>, dim3(1 + gate_wg), dim3(kSchedThreads), lds, st, s);
   }
 }
 
@@ -2338,7 +2346,7 @@ static void run_forward(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot,
   hipLaunchKernelGGL((k_fc2<T, FP8, C>), dim3(g2), dim3(C::NT), lds, st, a);
   rec(ev, 3, st);
   if (z.T > 0)
-    hipLaunchKernelGGL(k_combine<T>, combine_grid(z.T), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_combine<T>, combine_grid<T>(z.T, z.d), dim3(256), 0, st,
                        (const T*)a.bufO, row_to_slot, z.T, z.k, z.d, (T*)y);
   rec(ev, 4, st);
 }
@@ -2374,14 +2382,6 @@ static void launch_stream2(ExecArgs& a, int ntiles, int split, size_t lds, hipSt
                      split);
 }
 
-static void launch_slot_gate(const Sizes& z, const ExecArgs& a, hipStream_t st) {
-  const size_t n = z.max_slots;
-  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
-  if (n > 0)
-    hipLaunchKernelGGL(k_slot_gate, dim3(blocks), dim3(256), 0, st, a.slot_to_row, a.gates, n,
-                       (float*)a.sgate);
-}
-
 // workgroups of one worker in the two-phase launches (one per CU)
 static int wide_workers_wg(int P) {
   static int g = persistent_grid(k_stream2<FlowProducer<SrcFc1T<false, true>>,
@@ -2402,7 +2402,6 @@ template <bool FP8>
 static void run_forward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot, void* y,
                                bool split, int n1split, bool f8act, void* const* ev,
                                hipStream_t st) {
-  launch_slot_gate(z, a, st);
   const int n1 = z.dff / (WC::BN / 2), n2 = z.d / WC::BN;
   a.tl_phase = MOE_TL_FC1;
   if (FP8 && f8act) {                  // x quantized per row block, FC1 on the fp8 MFMA
@@ -2426,7 +2425,7 @@ static void run_forward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_t
   }
   rec(ev, 3, st);
   if (z.T > 0)
-    hipLaunchKernelGGL(k_combine<uint16_t>, combine_grid(z.T), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_combine<uint16_t>, combine_grid<uint16_t>(z.T, z.d), dim3(256), 0, st,
                        (const uint16_t*)a.bufO, row_to_slot, z.T, z.k, z.d, (uint16_t*)y);
   rec(ev, 4, st);
 }
@@ -2445,7 +2444,11 @@ int launch_forward(const Sizes& z, const LayerPtrs& Lp, const void* x, const flo
     return MOE_ERR_ARG;
   const WsLayout L = exec_layout(z, false);
   rec(ev, 0, st);
-  launch_sched(z, counts, boff, block_worker, nullptr, false, ws, L, status, st);
+  // the stream kernels read the per-slot gates, written beside the schedule
+  const bool stream = Lp.act_dtype == MOE_BF16 &&
+                      (Lp.w_dtype == MOE_BF16 || Lp.w_dtype == MOE_FP8_E4M3) && use_stream(z);
+  launch_sched(z, counts, boff, block_worker, nullptr, false, ws, L, status,
+               stream ? slot_to_row : nullptr, stream ? gates : nullptr, st);
   rec(ev, 1, st);
   ExecArgs a = make_exec(z, Lp, ws, L);
   a.x = x; a.gates = gates; a.slot_to_row = slot_to_row; a.row_to_slot = row_to_slot;
@@ -2482,7 +2485,6 @@ static void run_backward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_
                                 float* dw1, float* dw2, bool split, int n1split, bool f8act,
                                 void* const* ev, hipStream_t st) {
   const int rows = (int)z.max_slots;
-  launch_slot_gate(z, a, st);
   if constexpr (FP8)
     launch_quant_dequant((const uint16_t*)a.dy, z.d, a.slot_to_row, 1, z.k, a.gates, z.T * z.k,
                          rows, z.d, z.beta, (uint16_t*)a.dhat, a.boff + z.E, st);
@@ -2507,7 +2509,7 @@ static void run_backward_stream(const Sizes& z, ExecArgs& a, const int32_t* row_
   }
   rec(ev, 3, st);
   if (z.T > 0)
-    hipLaunchKernelGGL(k_combine<uint16_t>, combine_grid(z.T), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_combine<uint16_t>, combine_grid<uint16_t>(z.T, z.d), dim3(256), 0, st,
                        (const uint16_t*)a.bufO, row_to_slot, z.T, z.k, z.d, (uint16_t*)dx);
   rec(ev, 4, st);
   if constexpr (FP8)
@@ -2541,7 +2543,7 @@ static void run_backward(const Sizes& z, ExecArgs& a, const int32_t* row_to_slot
   hipLaunchKernelGGL((k_bwd_dx<T, C, FP8>), dim3(gx), dim3(C::NT), lds, st, a);
   rec(ev, 3, st);
   if (z.T > 0)
-    hipLaunchKernelGGL(k_combine<T>, combine_grid(z.T), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_combine<T>, combine_grid<T>(z.T, z.d), dim3(256), 0, st,
                        (const T*)a.bufO, row_to_slot, z.T, z.k, z.d, (T*)dx);
   rec(ev, 4, st);
   hipLaunchKernelGGL((k_bwd_dw<T, C, FP8>), dim3(gw), dim3(C::NT), lds, st, a);
@@ -2566,7 +2568,9 @@ int launch_backward(const Sizes& z, const LayerPtrs& Lp, const void* x, const fl
     return MOE_ERR_ARG;
   const WsLayout L = exec_layout(z, true);
   rec(ev, 0, st);
-  launch_sched(z, counts, boff, block_worker, owner, true, ws, L, status, st);
+  const bool stream = Lp.act_dtype != MOE_F32 && use_stream(z);
+  launch_sched(z, counts, boff, block_worker, owner, true, ws, L, status,
+               stream ? slot_to_row : nullptr, stream ? gates : nullptr, st);
   rec(ev, 1, st);
   ExecArgs a = make_exec(z, Lp, ws, L);
   a.x = x; a.gates = gates; a.slot_to_row = slot_to_row; a.row_to_slot = row_to_slot;

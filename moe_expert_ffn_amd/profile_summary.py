@@ -37,7 +37,7 @@ STAGE_OF = {"k_stream<SrcFc1>": "fwd.fc1", "k_stream<SrcFc2>": "fwd.fc2",
             "k_fc1": "fwd.fc1", "k_fc2": "fwd.fc2", "k_bwd_da": "bwd.dA", "k_bwd_dx": "bwd.dX",
             "k_bwd_dw": "bwd.dW", "k_bwd_reduce": "bwd.reduce",
             "k_combine": "fwd.combine + bwd.combine", "k_sched": "fwd.sched + bwd.sched",
-            "k_slot_gate": "fwd.sched + bwd.sched", "k_plan": "plan (fwd + bwd)",
+            "k_plan": "plan (fwd + bwd)",
             "k_stream<SrcFc1F8>": "fwd.fc1 (fp8 MFMA)", "k_stream<SrcFc2F8>": "fwd.fc2 (fp8 MFMA)",
             "k_stream<SrcDaF8>": "bwd.dA (fp8 MFMA)", "k_stream<SrcDxF8>": "bwd.dX (fp8 MFMA)",
             "k_quant_act": "fp8 MFMA: fwd.fc1 (x, A), bwd.dA (dy)",
