@@ -316,7 +316,7 @@ def reduce_bytes(case, w):
 # WRITE_SIZE per dispatch, scaled by the reading of a plain copy kernel of
 # known size), valid only for the kernel sources it was measured on.
 PROFILED_TRAFFIC = {"kernel": "bwd.dW", "workload": "qwen3_bf16_fwdbwd", "kappa": 1.0, "fixed": False,
-                    "source": "ce7e7e78f1dfb817", "bytes": 3331610301,
+                    "source": "4928bdf5712c7e12", "bytes": 3335867346,
                     "summary": "profiles/k_stream_SrcDwT_qwen3_bf16_fwdbwd_hbm_traffic.md"}
 
 

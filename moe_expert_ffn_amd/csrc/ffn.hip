@@ -56,7 +56,7 @@ MOE_DEV int expert_of(int g, const int* boff_s, int E) {
   return lo;
 }
 
-// One workgroup.  M-tiles: a tile holds up to `bm` consecutive slots of one
+// The scheduling workgroup.  M-tiles: a tile holds up to `bm` consecutive slots of one
 // (expert, worker) run of blocks.  When bm is a multiple of beta, tiles start
 // every bm/beta blocks from the start of each run; otherwise every block is cut
 // into ceil(valid rows / bm) tiles of its own.  Tiles are listed per worker in
@@ -74,9 +74,10 @@ MOE_DEV int block_rows(int g, int e, int beta, const int* boff_s, const int* cnt
   return min(beta, beta * boff_s[e] + cnt_s[e] - beta * g);
 }
 
-// One workgroup, one wave per worker (P <= 8).  BWL: block_worker is first
-// copied to LDS (when max_blocks entries fit), so each worker's pass over the
-// blocks reads LDS instead of issuing a global load per 64 blocks.
+// Workgroup 0 schedules, one wave per worker (P <= 8); the workgroups past it
+// (if any) write the per-slot gates.  BWL: block_worker is first copied to LDS
+// (when max_blocks entries fit), so each worker's pass over the blocks reads
+// LDS instead of issuing a global load per 64 blocks.
 constexpr int kSchedThreads = 512;
 template <bool BWL>
 __global__ __launch_bounds__(kSchedThreads) void k_sched(SchedArgs a) {
